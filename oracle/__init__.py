@@ -1,0 +1,19 @@
+"""CPU oracle of one denoising step of a block text-diffusion MoE model.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call, link or execute anything
+under ``oracle/``.  The product path (the HIP library and its Python binding)
+never does, and shares no code with it: no kernels, headers, helpers, tables
+or constant generators.
+
+  model.py    float64 numpy forward: embedding + self-conditioning, causal and
+              bidirectional attention over a KV cache, top-k SwiGLU MoE,
+              tied head, prompt encode and block commit.
+  sampler.c   binary32 sampler (statistics, Philox draw, lock rules, renoise,
+              stop) with every floating-point operation fixed, so that
+              decisions can be compared bit for bit; sampler.py wraps it.
+  driver.py   the block loop: canvas init, denoise/sample rounds, commit.
+
+Parity pins live in tests/test_oracle_*.py.  Functions without a pin are
+marked "parity unpinned" in their docstring.
+"""

@@ -1,0 +1,47 @@
+"""Block-autoregressive driver of the oracle (TEST INFRASTRUCTURE ONLY).
+
+Report-summary page (animattoys.com), sections 1 and 4: a block starts as 256
+uniformly random tokens and is refined for at most 48 rounds, each round
+predicting every position, locking confident positions and re-randomising the
+rest, until the entropy stop fires.  akiraxclaw.com blog, "memory, not
+compute", and youleyou.com article, "Architecture basis": a finished block is
+encoded into the KV cache and the next block is conditioned on it.
+
+The block output is the most likely token sequence of the last round (the stop
+rule is defined on it).  Committing re-encodes that block causally.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import model, sampler
+
+
+def generate_block(W: dict, cfg: dict, cache: model.KVCache, params: dict, block_index: int,
+                   B: int, selfcond: bool = True, logits_hook=None):
+    """Runs one block; returns (block tokens [B, N] int32, steps [B] int32).
+    logits_hook(step, logits) may replace the float64 model logits (it must
+    return a [B, N, V] array) -- tests use it to feed identical logits to
+    two implementations."""
+    N, V = cfg["canvas"], cfg["vocab"]
+    canvas = sampler.canvas_init(params["seed"], block_index, B, N, V)
+    argmax = np.zeros((B, N), dtype=np.int32)
+    stop = np.zeros(B, dtype=np.int32)
+    steps = np.zeros(B, dtype=np.int32)
+    prev = None
+    for t in range(params["max_steps"]):
+        active = stop == 0
+        if not active.any():
+            break
+        logits = model.denoise_step(canvas, W, cfg, cache, prev if selfcond else None)
+        if logits_hook is not None:
+            logits = logits_hook(t, logits)
+        logits32 = np.ascontiguousarray(logits, dtype=np.float32)
+        sampler.sample_update(params, t, logits32, canvas, argmax, stop)
+        steps[active] = t + 1
+        # a stopped canvas keeps its last logits for self-conditioning
+        prev = logits32.astype(np.float64) if prev is None else np.where(
+            active[:, None, None], logits32.astype(np.float64), prev)
+    block = argmax.copy()
+    model.encode(block, W, cfg, cache)
+    return block, steps
