@@ -1,0 +1,781 @@
+// C ABI of the denoising step (include/dg.h): argument checks, workspace
+// layout, and the order of kernel launches for encode, denoise, sample,
+// commit and the block loop.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dg_status fail(dg_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define DG_HIP(expr)                                                                     \
+    do {                                                                                 \
+        hipError_t e_ = (expr);                                                          \
+        if (e_ != hipSuccess)                                                            \
+            return fail(DG_ERR_HIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_),      \
+                        __FILE__, __LINE__);                                             \
+    } while (0)
+
+#define DG_TRY(expr)                     \
+    do {                                 \
+        dg_status s_ = (expr);           \
+        if (s_ != DG_OK) return s_;      \
+    } while (0)
+
+constexpr int kEncodeTokens = 4096;    // tokens per encode chunk (all sequences)
+constexpr int kAttnPartRows = 8192;    // split-KV partial rows budget
+constexpr int kMaxSplitsSC = 64;       // self-conditioning split-K limit
+
+size_t elt_size(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carver {
+    char* base;
+    size_t size, off = 0;
+    bool ok = true;
+    Carver(void* b, size_t s) : base((char*)b), size(s) {}
+    template <typename T>
+    T* take(size_t n) {
+        off = (off + 255) & ~(size_t)255;
+        size_t bytes = n * sizeof(T);
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += bytes;
+        if (base && off > size) ok = false;
+        return p;
+    }
+    void* take_bytes(size_t n) { return take<char>(n); }
+};
+
+}  // namespace
+
+struct dg_model {
+    dg_config c;
+    const void* embed;
+    const void* embed_t;
+    const void* w_sc;
+    const float* final_norm;
+    std::vector<dg_layer_weights> layers;
+};
+
+struct dg_kv {
+    int B, cap, len;
+    void* buf;
+};
+
+namespace {
+
+// Per-call scratch, carved in a fixed order so a size query and a real call
+// agree.
+struct Scratch {
+    float* h;
+    void* u;
+    float* qkv;
+    void* q;
+    void* ao;
+    float* part_o;
+    float* part_ml;
+    float* z;
+    int32_t* route;
+    float* gates;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm_tok;
+    int32_t* slot_of;
+    void* act;
+    float* y;
+    float* sc_part;
+    void* sc_s;
+    int32_t* tok;
+    float* u32;       // bf16 models: fp32 normalised activations for the router
+    float* wr32;      // bf16 models: router weights widened to fp32
+};
+
+int token_budget(const dg_model* m, int B) {
+    return std::max(B * m->c.canvas, std::max(kEncodeTokens, B));
+}
+
+int sc_splits(const dg_model* m, int T) {
+    // enough workgroups for the chip on the [T x d] output tiles
+    const int tiles = cdiv(T, 256) * cdiv(m->c.d_model, 256);
+    return std::max(1, std::min(kMaxSplitsSC, 512 / std::max(tiles, 1)));
+}
+
+bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
+    const dg_config& c = m->c;
+    const size_t es = elt_size(c.dtype);
+    const size_t T = (size_t)token_budget(m, B);
+    const size_t Tc = (size_t)B * c.canvas;
+    const size_t qkvw = (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+    s.h = cv.take<float>(T * c.d_model);
+    s.u = cv.take_bytes(T * c.d_model * es);
+    s.qkv = cv.take<float>(T * qkvw);
+    s.q = cv.take_bytes(T * c.n_heads * c.head_dim * es);
+    s.ao = cv.take_bytes(T * c.n_heads * c.head_dim * es);
+    const size_t prow = std::max<size_t>(kAttnPartRows, Tc);
+    s.part_o = cv.take<float>(prow * c.n_heads * c.head_dim);
+    s.part_ml = cv.take<float>(prow * c.n_heads * 2);
+    s.z = cv.take<float>(T * c.n_experts);
+    s.route = cv.take<int32_t>(T * c.top_k);
+    s.gates = cv.take<float>(T * c.top_k);
+    s.counts = cv.take<int32_t>(c.n_experts);
+    s.offsets = cv.take<int32_t>(c.n_experts + 1);
+    s.perm_tok = cv.take<int32_t>(T * c.top_k);
+    s.slot_of = cv.take<int32_t>(T * c.top_k);
+    s.act = cv.take_bytes(T * c.top_k * c.d_ff * es);
+    s.y = cv.take<float>(T * c.top_k * c.d_model);
+    s.sc_part = cv.take<float>((size_t)sc_splits(m, (int)Tc) * Tc * c.d_model);
+    s.sc_s = cv.take_bytes(Tc * c.d_model * es);
+    s.tok = cv.take<int32_t>(T);
+    const bool wide = c.dtype == DG_BF16;
+    s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
+    s.wr32 = wide ? cv.take<float>((size_t)c.n_experts * c.d_model) : nullptr;
+    return cv.ok;
+}
+
+dg_status check_ws(const dg_model* m, int B, void* ws, size_t bytes, Scratch& s, Carver& cv) {
+    if (!ws) return fail(DG_ERR_ARG, "workspace is NULL");
+    if (!carve_scratch(cv, m, B, s))
+        return fail(DG_ERR_CAPACITY, "workspace of %zu bytes is too small (need %zu)", bytes,
+                    cv.off);
+    return DG_OK;
+}
+
+// layer pointers into the KV buffer
+void kv_layer(const dg_model* m, const dg_kv* kv, int layer, void** kc, void** vc) {
+    const dg_config& c = m->c;
+    const size_t es = elt_size(c.dtype);
+    const size_t per_layer = (size_t)kv->B * c.n_kv_heads * kv->cap * c.head_dim;
+    char* K = (char*)kv->buf;
+    char* V = K + per_layer * c.n_layers * es;
+    *kc = K + per_layer * layer * es;
+    *vc = V + per_layer * layer * es;
+}
+
+template <typename T>
+dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_t st) {
+    DG_HIP(dg::gemm_tn<T>(g, amode, epi, splits, st));
+    return DG_OK;
+}
+
+// y = x W^T helper: C fp32 [M][ldc] (+ column offset via C pointer)
+template <typename T>
+dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, long ldc, int epi,
+                 hipStream_t st) {
+    dg::GemmArgs g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = x;
+    g.lda = K;
+    g.B = W;
+    g.ldb = K;
+    g.C = C;
+    g.ldc = ldc;
+    g.k_split = K;
+    return gemm<T>(g, 0, epi, 1, st);
+}
+
+// ---- attention half-block: n new tokens per sequence at [pos0, pos0+n)
+template <typename T>
+dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, int causal,
+                    float* h, Scratch& s, hipStream_t st) {
+    const dg_config& c = m->c;
+    const dg_layer_weights& L = m->layers[layer];
+    const int Tn = B * n;
+    const int d = c.d_model, dh = c.head_dim;
+    const int qkvw = (c.n_heads + 2 * c.n_kv_heads) * dh;
+    DG_HIP(dg::rmsnorm<T>(h, L.attn_norm, (T*)s.u, Tn, d, c.rms_eps, st));
+    DG_TRY(linear<T>(s.u, Tn, d, L.wq, c.n_heads * dh, s.qkv, qkvw, dg::EPI_STORE_F32, st));
+    DG_TRY(linear<T>(s.u, Tn, d, L.wk, c.n_kv_heads * dh, s.qkv + c.n_heads * dh, qkvw,
+                     dg::EPI_STORE_F32, st));
+    DG_TRY(linear<T>(s.u, Tn, d, L.wv, c.n_kv_heads * dh, s.qkv + (c.n_heads + c.n_kv_heads) * dh,
+                     qkvw, dg::EPI_STORE_F32, st));
+    void *kc, *vc;
+    kv_layer(m, kv, layer, &kc, &vc);
+    DG_HIP(dg::rope_kv<T>(s.qkv, (T*)s.q, (T*)kc, (T*)vc, B, n, pos0, kv->cap, c.n_heads,
+                          c.n_kv_heads, dh, c.rope_on, c.rope_theta, st));
+    dg::AttnArgs a;
+    a.q = s.q;
+    a.kc = kc;
+    a.vc = vc;
+    a.out = s.ao;
+    a.part_o = s.part_o;
+    a.part_ml = s.part_ml;
+    a.B = B;
+    a.n = n;
+    a.pos0 = pos0;
+    a.cap = kv->cap;
+    a.Hq = c.n_heads;
+    a.Hkv = c.n_kv_heads;
+    a.dh = dh;
+    a.kv_len = pos0 + n;
+    a.causal = causal;
+    const int max_splits = std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
+    a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
+                                    &a.split_len);
+    DG_HIP(dg::attention<T>(a, st));
+    DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, st));
+    return DG_OK;
+}
+
+template <typename T>
+dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st) {
+    const dg_config& c = m->c;
+    const dg_layer_weights& L = m->layers[layer];
+    DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
+    if (sizeof(T) == 2) {
+        // The route is an integer decision taken from float logits: compute
+        // them from the fp32 normalised activations and fp32-widened router
+        // weights, so bf16 rounding of the activations cannot flip it.
+        DG_HIP(dg::rmsnorm<float>(h, L.moe_norm, s.u32, Tn, c.d_model, c.rms_eps, st));
+        DG_HIP(dg::widen_bf16((const uint16_t*)L.w_router, s.wr32,
+                              (long)c.n_experts * c.d_model, st));
+        DG_TRY(linear<float>(s.u32, Tn, c.d_model, s.wr32, c.n_experts, s.z, c.n_experts,
+                             dg::EPI_STORE_F32, st));
+    } else {
+        DG_TRY(linear<T>(s.u, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
+                         dg::EPI_STORE_F32, st));
+    }
+    dg::MoeArgs a;
+    a.T = Tn;
+    a.d = c.d_model;
+    a.E = c.n_experts;
+    a.k = c.top_k;
+    a.F = c.d_ff;
+    a.z = s.z;
+    a.route = s.route;
+    a.gates = s.gates;
+    a.counts = s.counts;
+    a.offsets = s.offsets;
+    a.perm_tok = s.perm_tok;
+    a.slot_of = s.slot_of;
+    a.u = s.u;
+    a.w_gate = L.w_gate;
+    a.w_up = L.w_up;
+    a.w_down = L.w_down;
+    a.act = s.act;
+    a.y = s.y;
+    a.h = h;
+    DG_HIP(dg::moe_forward<T>(a, st));
+    return DG_OK;
+}
+
+// h[B*N][d] = E[canvas] + (softmax(prev) E) W_sc^T
+template <typename T>
+dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* prev_logits,
+                      const float* prev_stats, float* h, Scratch& s, hipStream_t st) {
+    const dg_config& c = m->c;
+    const int Tn = B * c.canvas;
+    if (!prev_logits) {
+        DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, canvas, c.canvas, c.canvas, B, h, c.d_model,
+                                 st));
+        return DG_OK;
+    }
+    if (!m->embed_t) return fail(DG_ERR_ARG, "self-conditioning needs weights.embed_t");
+    const int splits = sc_splits(m, Tn);
+    dg::GemmArgs g;
+    g.M = Tn;
+    g.N = c.d_model;
+    g.K = c.vocab;
+    g.A = prev_logits;
+    g.lda = c.vocab;
+    g.a_stats = prev_stats;
+    g.B = m->embed_t;
+    g.ldb = c.vocab;
+    g.C = s.sc_part;
+    g.ldc = c.d_model;
+    g.k_split = cdiv(cdiv(c.vocab, splits), 64) * 64;
+    const int used = cdiv(c.vocab, g.k_split);
+    DG_TRY(gemm<T>(g, 1, dg::EPI_SPLITK, used, st));
+    DG_HIP(dg::splitk_reduce<T>(s.sc_part, (T*)s.sc_s, used, Tn, c.d_model, st));
+    dg::GemmArgs p;
+    p.M = Tn;
+    p.N = c.d_model;
+    p.K = c.d_model;
+    p.A = s.sc_s;
+    p.lda = c.d_model;
+    p.B = m->w_sc;
+    p.ldb = c.d_model;
+    p.C = h;
+    p.ldc = c.d_model;
+    p.k_split = c.d_model;
+    p.E = m->embed;
+    p.lde = c.d_model;
+    p.vocab = c.vocab;
+    p.tokens = canvas;
+    DG_TRY(gemm<T>(p, 0, dg::EPI_EMBED_ADD, 1, st));
+    return DG_OK;
+}
+
+template <typename T>
+dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch& s,
+                     hipStream_t st) {
+    const dg_config& c = m->c;
+    DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
+    DG_TRY(linear<T>(s.u, Tn, c.d_model, m->embed, c.vocab, logits, c.vocab, dg::EPI_STORE_F32,
+                     st));
+    return DG_OK;
+}
+
+template <typename T>
+dg_status denoise(dg_model* m, dg_kv* kv, int B, const int32_t* canvas, const float* prev,
+                  const float* prev_stats, float* logits, Scratch& s, hipStream_t st) {
+    const dg_config& c = m->c;
+    const int Tn = B * c.canvas;
+    DG_TRY(stage_input<T>(m, B, canvas, prev, prev_stats, s.h, s, st));
+    for (int l = 0; l < c.n_layers; ++l) {
+        DG_TRY(attn_half<T>(m, kv, l, B, c.canvas, kv->len, 0, s.h, s, st));
+        DG_TRY(moe_half<T>(m, l, Tn, s.h, s, st));
+    }
+    return stage_head<T>(m, Tn, s.h, logits, s, st);
+}
+
+template <typename T>
+dg_status encode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int P, Scratch& s,
+                 hipStream_t st) {
+    const dg_config& c = m->c;
+    const int chunk = std::max(1, token_budget(m, B) / B);
+    for (int c0 = 0; c0 < P; c0 += chunk) {
+        const int n = std::min(chunk, P - c0);
+        const int pos0 = kv->len + c0;
+        DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens + c0, P, n, B, s.h, c.d_model, st));
+        for (int l = 0; l < c.n_layers; ++l) {
+            DG_TRY(attn_half<T>(m, kv, l, B, n, pos0, 1, s.h, s, st));
+            if (l + 1 < c.n_layers) DG_TRY(moe_half<T>(m, l, B * n, s.h, s, st));
+        }
+    }
+    kv->len += P;
+    return DG_OK;
+}
+
+dg_status check_model(const dg_model* m) {
+    if (!m) return fail(DG_ERR_ARG, "model is NULL");
+    return DG_OK;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+// ======================================================================= API
+
+extern "C" {
+
+const char* dg_status_string(dg_status s) {
+    switch (s) {
+        case DG_OK: return "ok";
+        case DG_ERR_ARG: return "invalid argument";
+        case DG_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case DG_ERR_DTYPE: return "unknown dtype";
+        case DG_ERR_CAPACITY: return "capacity exceeded";
+        case DG_ERR_NONFINITE: return "non-finite values";
+        case DG_ERR_HIP: return "HIP runtime error";
+        case DG_ERR_UNSUPPORTED: return "unsupported";
+    }
+    return "unknown status";
+}
+
+const char* dg_last_error(void) { return g_err.c_str(); }
+
+dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** out) {
+    if (!cfg || !w || !out) return fail(DG_ERR_ARG, "NULL argument");
+    *out = nullptr;
+    const dg_config& c = *cfg;
+    if (c.dtype != DG_F32 && c.dtype != DG_BF16) return fail(DG_ERR_DTYPE, "dtype %d", c.dtype);
+    if (c.n_layers < 1 || c.d_model < 64 || c.d_model % 64 != 0)
+        return fail(DG_ERR_SHAPE, "n_layers >= 1 and d_model a multiple of 64 required");
+    if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads != 0)
+        return fail(DG_ERR_SHAPE, "n_heads must be a positive multiple of n_kv_heads");
+    const bool dh_ok = c.head_dim == 64 || c.head_dim == 128 ||
+                       (c.head_dim == 256 && c.dtype == DG_BF16);
+    if (!dh_ok) return fail(DG_ERR_SHAPE, "head_dim %d unsupported (64, 128; 256 in bf16)",
+                            c.head_dim);
+    if (c.n_experts < 1 || c.n_experts > 256 || c.top_k < 1 || c.top_k > 16 ||
+        c.top_k > c.n_experts)
+        return fail(DG_ERR_SHAPE, "need 1 <= top_k <= min(n_experts, 16), n_experts <= 256");
+    if (c.d_ff < 32 || c.d_ff % 32 != 0) return fail(DG_ERR_SHAPE, "d_ff must be a multiple of 32");
+    if (c.vocab < 8 || c.vocab > 524288 || c.vocab % 8 != 0)
+        return fail(DG_ERR_SHAPE, "vocab must be a multiple of 8 in [8, 524288]");
+    if (c.canvas < 1 || c.canvas > 1024) return fail(DG_ERR_SHAPE, "canvas must be in [1, 1024]");
+    if (!(c.rms_eps >= 0.f) || (c.rope_on && !(c.rope_theta > 0.f)))
+        return fail(DG_ERR_ARG, "rms_eps >= 0 and rope_theta > 0 required");
+    if (!w->embed || !w->w_sc || !w->layers) return fail(DG_ERR_ARG, "missing weights");
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dg_layer_weights& L = w->layers[l];
+        if (!L.wq || !L.wk || !L.wv || !L.wo || !L.w_router || !L.w_gate || !L.w_up || !L.w_down)
+            return fail(DG_ERR_ARG, "missing weights in layer %d", l);
+    }
+    dg_model* m = new dg_model;
+    m->c = c;
+    m->embed = w->embed;
+    m->embed_t = w->embed_t;
+    m->w_sc = w->w_sc;
+    m->final_norm = w->final_norm;
+    m->layers.assign(w->layers, w->layers + c.n_layers);
+    *out = m;
+    return DG_OK;
+}
+
+void dg_model_destroy(dg_model* m) { delete m; }
+
+dg_status dg_embed_transpose(const dg_model* m, const void* d_embed, void* d_out, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_embed || !d_out) return fail(DG_ERR_ARG, "NULL pointer");
+    if (m->c.dtype == DG_BF16)
+        DG_HIP(dg::transpose<bf16_t>((const bf16_t*)d_embed, (bf16_t*)d_out,
+                                         m->c.vocab, m->c.d_model, as_stream(stream)));
+    else
+        DG_HIP(dg::transpose<float>((const float*)d_embed, (float*)d_out, m->c.vocab,
+                                    m->c.d_model, as_stream(stream)));
+    return DG_OK;
+}
+
+dg_status dg_kv_bytes(const dg_model* m, int32_t batch, int32_t capacity, size_t* bytes) {
+    DG_TRY(check_model(m));
+    if (!bytes || batch < 1 || capacity < 1) return fail(DG_ERR_ARG, "bad kv size request");
+    const dg_config& c = m->c;
+    *bytes = 2 * (size_t)c.n_layers * batch * c.n_kv_heads * capacity * c.head_dim *
+             elt_size(c.dtype);
+    return DG_OK;
+}
+
+dg_status dg_kv_create(const dg_model* m, int32_t batch, int32_t capacity, void* d_buf,
+                       dg_kv** out) {
+    DG_TRY(check_model(m));
+    if (!d_buf || !out || batch < 1 || capacity < 1) return fail(DG_ERR_ARG, "bad kv arguments");
+    dg_kv* kv = new dg_kv;
+    kv->B = batch;
+    kv->cap = capacity;
+    kv->len = 0;
+    kv->buf = d_buf;
+    *out = kv;
+    return DG_OK;
+}
+
+void dg_kv_destroy(dg_kv* kv) { delete kv; }
+
+dg_status dg_kv_length(const dg_kv* kv, int32_t* len) {
+    if (!kv || !len) return fail(DG_ERR_ARG, "NULL argument");
+    *len = kv->len;
+    return DG_OK;
+}
+
+dg_status dg_kv_set_length(dg_kv* kv, int32_t len) {
+    if (!kv) return fail(DG_ERR_ARG, "NULL argument");
+    if (len < 0 || len > kv->cap) return fail(DG_ERR_CAPACITY, "length %d outside [0, %d]", len,
+                                              kv->cap);
+    kv->len = len;
+    return DG_OK;
+}
+
+dg_status dg_workspace_bytes(const dg_model* m, int32_t batch, size_t* bytes) {
+    DG_TRY(check_model(m));
+    if (!bytes || batch < 1) return fail(DG_ERR_ARG, "bad workspace request");
+    Carver cv(nullptr, 0);
+    Scratch s;
+    carve_scratch(cv, m, batch, s);
+    *bytes = cv.off + 256;
+    return DG_OK;
+}
+
+dg_status dg_sampler_workspace_bytes(int32_t batch, int32_t canvas, size_t* bytes) {
+    if (!bytes || batch < 1 || canvas < 1) return fail(DG_ERR_ARG, "bad sampler workspace request");
+    *bytes = 3 * (((size_t)batch * canvas * 4 + 255) & ~(size_t)255) + 256;
+    return DG_OK;
+}
+
+dg_status dg_encode_prompt(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_tokens,
+                           int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_tokens || n_tokens < 0) return fail(DG_ERR_ARG, "bad encode arguments");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + n_tokens > kv->cap)
+        return fail(DG_ERR_CAPACITY, "len %d + %d tokens exceeds capacity %d", kv->len, n_tokens,
+                    kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    if (n_tokens == 0) return DG_OK;
+    if (m->c.dtype == DG_BF16)
+        return encode<bf16_t>(m, kv, batch, d_tokens, n_tokens, s, as_stream(stream));
+    return encode<float>(m, kv, batch, d_tokens, n_tokens, s, as_stream(stream));
+}
+
+dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_block,
+                          void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    return dg_encode_prompt(m, kv, batch, d_block, m->c.canvas, d_ws, ws_bytes, stream);
+}
+
+dg_status dg_denoise_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
+                          const float* d_prev_logits, const float* d_prev_stats, float* d_logits,
+                          void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_canvas || !d_logits) return fail(DG_ERR_ARG, "NULL argument");
+    if ((d_prev_logits == nullptr) != (d_prev_stats == nullptr))
+        return fail(DG_ERR_ARG, "prev_logits and prev_stats must both be set or both NULL");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + m->c.canvas > kv->cap)
+        return fail(DG_ERR_CAPACITY, "cache needs len %d + canvas %d <= capacity %d", kv->len,
+                    m->c.canvas, kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    if (m->c.dtype == DG_BF16)
+        return denoise<bf16_t>(m, kv, batch, d_canvas, d_prev_logits, d_prev_stats, d_logits,
+                                   s, as_stream(stream));
+    return denoise<float>(m, kv, batch, d_canvas, d_prev_logits, d_prev_stats, d_logits, s,
+                          as_stream(stream));
+}
+
+static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t batch,
+                             int32_t canvas, int32_t vocab, const float* d_logits,
+                             int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                             float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
+                             hipStream_t st) {
+    if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
+        return fail(DG_ERR_ARG, "NULL argument");
+    if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
+        return fail(DG_ERR_SHAPE, "need batch >= 1, 1 <= canvas <= 1024, 1 <= vocab <= 524288");
+    if (p->max_steps < 1 || step < 0) return fail(DG_ERR_ARG, "bad step / max_steps");
+    if (p->lock_rule != DG_LOCK_MAXPROB && p->lock_rule != DG_LOCK_CUMENT)
+        return fail(DG_ERR_ARG, "lock_rule %d", p->lock_rule);
+    if (!(p->temp_start > 0.f) || !(p->temp_end > 0.f))
+        return fail(DG_ERR_ARG, "temperatures must be positive");
+    size_t need;
+    dg_sampler_workspace_bytes(batch, canvas, &need);
+    if (ws_bytes < need) return fail(DG_ERR_CAPACITY, "sampler workspace needs %zu bytes", need);
+    // temperature of this step: linear from temp_start to temp_end over the budget
+    double T = (double)p->temp_start;
+    if (p->max_steps > 1)
+        T = (double)p->temp_start + ((double)p->temp_end - (double)p->temp_start) * (double)step /
+                                        (double)(p->max_steps - 1);
+    const float Tf = (float)T;
+    Carver cv(d_ws, ws_bytes);
+    dg::SampleArgs a;
+    a.B = batch;
+    a.N = canvas;
+    a.V = vocab;
+    a.step = step;
+    a.lock_rule = p->lock_rule;
+    a.theta = p->lock_theta;
+    a.tau = p->stop_tau;
+    a.inv_t = 1.0f / Tf;
+    a.require_stable = p->require_stable;
+    a.max_steps = p->max_steps;
+    a.seed = p->seed;
+    a.logits = d_logits;
+    a.canvas = d_canvas;
+    a.argmax = d_argmax;
+    a.lock = d_lock;
+    a.stats = d_stats;
+    a.stop = d_stop;
+    a.y = cv.take<int32_t>((size_t)batch * canvas);
+    a.r = cv.take<int32_t>((size_t)batch * canvas);
+    a.newmax = cv.take<int32_t>((size_t)batch * canvas);
+    DG_HIP(dg::sample_update(a, st));
+    return DG_OK;
+}
+
+dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t batch,
+                           int32_t canvas, int32_t vocab, const float* d_logits,
+                           int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                           float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
+                           void* stream) {
+    return sample_impl(p, step, batch, canvas, vocab, d_logits, d_canvas, d_argmax, d_lock,
+                       d_stats, d_stop, d_ws, ws_bytes, as_stream(stream));
+}
+
+dg_status dg_canvas_init(uint64_t seed, int32_t block_index, int32_t batch, int32_t canvas,
+                         int32_t vocab, int32_t* d_canvas, void* stream) {
+    if (!d_canvas || batch < 1 || canvas < 1 || vocab < 1)
+        return fail(DG_ERR_ARG, "bad canvas_init arguments");
+    DG_HIP(dg::canvas_init(seed, block_index, batch, canvas, vocab, d_canvas, as_stream(stream)));
+    return DG_OK;
+}
+
+// generate workspace: model scratch, then the loop's own buffers
+static void carve_generate(Carver& cv, const dg_model* m, int B, Scratch& s, float** logits,
+                           float** stats, int32_t** canvas, int32_t** argmax, uint8_t** lock,
+                           int32_t** stop, void** sws, size_t* sws_bytes) {
+    carve_scratch(cv, m, B, s);
+    const size_t Tc = (size_t)B * m->c.canvas;
+    logits[0] = cv.take<float>(Tc * m->c.vocab);
+    logits[1] = cv.take<float>(Tc * m->c.vocab);
+    stats[0] = cv.take<float>(Tc * 4);
+    stats[1] = cv.take<float>(Tc * 4);
+    *canvas = cv.take<int32_t>(Tc);
+    *argmax = cv.take<int32_t>(Tc);
+    *lock = cv.take<uint8_t>(Tc);
+    *stop = cv.take<int32_t>(B);
+    dg_sampler_workspace_bytes(B, m->c.canvas, sws_bytes);
+    *sws = cv.take_bytes(*sws_bytes);
+}
+
+dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* bytes) {
+    DG_TRY(check_model(m));
+    if (!bytes || batch < 1) return fail(DG_ERR_ARG, "bad workspace request");
+    Carver cv(nullptr, 0);
+    Scratch s;
+    float *lg[2], *stt[2];
+    int32_t *cv_, *am, *sp;
+    uint8_t* lk;
+    void* sws;
+    size_t sb;
+    carve_generate(cv, m, batch, s, lg, stt, &cv_, &am, &lk, &sp, &sws, &sb);
+    *bytes = cv.off + 256;
+    return DG_OK;
+}
+
+dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
+                            int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
+                            void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !p || !d_block_out || !h_steps_out || !d_ws) return fail(DG_ERR_ARG, "NULL argument");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    const dg_config& c = m->c;
+    if (kv->len + c.canvas > kv->cap)
+        return fail(DG_ERR_CAPACITY, "cache needs len %d + canvas %d <= capacity %d", kv->len,
+                    c.canvas, kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    float *lg[2], *stt[2];
+    int32_t *canvas, *argmax, *stop;
+    uint8_t* lock;
+    void* sws;
+    size_t sws_bytes;
+    carve_generate(cv, m, batch, s, lg, stt, &canvas, &argmax, &lock, &stop, &sws, &sws_bytes);
+    if (!cv.ok) return fail(DG_ERR_CAPACITY, "workspace of %zu bytes too small (need %zu)",
+                            ws_bytes, cv.off);
+    hipStream_t st = as_stream(stream);
+    const size_t Tc = (size_t)batch * c.canvas;
+    DG_HIP(dg::canvas_init(p->seed, block_index, batch, c.canvas, c.vocab, canvas, st));
+    DG_HIP(hipMemsetAsync(argmax, 0, Tc * sizeof(int32_t), st));
+    DG_HIP(hipMemsetAsync(stop, 0, batch * sizeof(int32_t), st));
+    std::vector<int32_t> hstop(batch, 0);
+    for (int b = 0; b < batch; ++b) h_steps_out[b] = 0;
+    const float* prev = nullptr;
+    const float* prev_stats = nullptr;
+    for (int t = 0; t < p->max_steps; ++t) {
+        float* logits = lg[t & 1];
+        float* stats = stt[t & 1];
+        if (c.dtype == DG_BF16)
+            DG_TRY(denoise<bf16_t>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
+        else
+            DG_TRY(denoise<float>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
+        DG_TRY(sample_impl(p, t, batch, c.canvas, c.vocab, logits, canvas, argmax, lock, stats,
+                           stop, sws, sws_bytes, st));
+        DG_HIP(hipMemcpyAsync(hstop.data(), stop, batch * sizeof(int32_t), hipMemcpyDeviceToHost,
+                              st));
+        DG_HIP(hipStreamSynchronize(st));
+        bool all = true;
+        for (int b = 0; b < batch; ++b) {
+            if (h_steps_out[b] == 0 && hstop[b]) h_steps_out[b] = t + 1;
+            all = all && hstop[b];
+        }
+        if (all) break;
+        if (p->selfcond_on) {
+            prev = logits;
+            prev_stats = stats;
+        }
+    }
+    for (int b = 0; b < batch; ++b)
+        if (h_steps_out[b] == 0) h_steps_out[b] = p->max_steps;
+    DG_HIP(hipMemcpyAsync(d_block_out, argmax, Tc * sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+    const size_t model_ws = ws_bytes;  // the model scratch is the prefix of d_ws
+    return dg_commit_block(m, kv, batch, d_block_out, d_ws, model_ws, stream);
+}
+
+// ------------------------------------------------------------------ stages
+dg_status dg_stage_input(dg_model* m, int32_t batch, const int32_t* d_canvas,
+                         const float* d_prev_logits, const float* d_prev_stats, float* d_h,
+                         void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_canvas || !d_h || batch < 1) return fail(DG_ERR_ARG, "bad arguments");
+    if ((d_prev_logits == nullptr) != (d_prev_stats == nullptr))
+        return fail(DG_ERR_ARG, "prev_logits and prev_stats must both be set or both NULL");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    if (m->c.dtype == DG_BF16)
+        return stage_input<bf16_t>(m, batch, d_canvas, d_prev_logits, d_prev_stats, d_h, s,
+                                       as_stream(stream));
+    return stage_input<float>(m, batch, d_canvas, d_prev_logits, d_prev_stats, d_h, s,
+                              as_stream(stream));
+}
+
+dg_status dg_stage_attention(dg_model* m, dg_kv* kv, int32_t layer, int32_t batch, int32_t n,
+                             int32_t causal, float* d_h, void* d_ws, size_t ws_bytes,
+                             void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_h || layer < 0 || layer >= m->c.n_layers || n < 1)
+        return fail(DG_ERR_ARG, "bad arguments");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + n > kv->cap) return fail(DG_ERR_CAPACITY, "len + n exceeds capacity");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    if (batch * n > token_budget(m, batch))
+        return fail(DG_ERR_CAPACITY, "batch*n exceeds the workspace token budget");
+    if (m->c.dtype == DG_BF16)
+        return attn_half<bf16_t>(m, kv, layer, batch, n, kv->len, causal != 0, d_h, s,
+                                     as_stream(stream));
+    return attn_half<float>(m, kv, layer, batch, n, kv->len, causal != 0, d_h, s,
+                            as_stream(stream));
+}
+
+dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_t* d_route,
+                       float* d_gates, void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_h || layer < 0 || layer >= m->c.n_layers || T < 1) return fail(DG_ERR_ARG, "bad arguments");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
+    if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
+    hipStream_t st = as_stream(stream);
+    if (m->c.dtype == DG_BF16) DG_TRY(moe_half<bf16_t>(m, layer, T, d_h, s, st));
+    else DG_TRY(moe_half<float>(m, layer, T, d_h, s, st));
+    if (d_route)
+        DG_HIP(hipMemcpyAsync(d_route, s.route, (size_t)T * m->c.top_k * sizeof(int32_t),
+                              hipMemcpyDeviceToDevice, st));
+    if (d_gates)
+        DG_HIP(hipMemcpyAsync(d_gates, s.gates, (size_t)T * m->c.top_k * sizeof(float),
+                              hipMemcpyDeviceToDevice, st));
+    return DG_OK;
+}
+
+dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,
+                        size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_h || !d_logits || T < 1) return fail(DG_ERR_ARG, "bad arguments");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
+    if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
+    if (m->c.dtype == DG_BF16)
+        return stage_head<bf16_t>(m, T, d_h, d_logits, s, as_stream(stream));
+    return stage_head<float>(m, T, d_h, d_logits, s, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Bandwidth-bound helpers of the step: RMSNorm, embedding gather, split-K
+// reduction, transpose, and RoPE with the KV-cache write.
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+namespace {
+
+// One workgroup per row: sum of squares in fp32, then scale.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h,
+                                                      const float* __restrict__ w,
+                                                      T* __restrict__ u, int d, float eps) {
+    const long row = blockIdx.x;
+    const float* x = h + row * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        float4 v = *reinterpret_cast<const float4*>(x + i);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+    T* o = u + row * d;
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        float4 v = *reinterpret_cast<const float4*>(x + i);
+        float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+        o[i + 0] = Elt<T>::from_f(v.x * scale * s.x);
+        o[i + 1] = Elt<T>::from_f(v.y * scale * s.y);
+        o[i + 2] = Elt<T>::from_f(v.z * scale * s.z);
+        o[i + 3] = Elt<T>::from_f(v.w * scale * s.w);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E,
+                                                    const int32_t* __restrict__ tok, int ld,
+                                                    int n, int V, float* __restrict__ h, int d) {
+    const long row = blockIdx.x;   // b*n + i
+    const long b = row / n, i = row % n;
+    const int id = min(max(tok[b * ld + i], 0), V - 1);   // ids outside [0, V) never index past E
+    const T* e = E + (long)id * d;
+    for (int i = threadIdx.x; i < d; i += 256) h[row * d + i] = Elt<T>::to_f(e[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            T* __restrict__ out, int splits,
+                                                            long total) {
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += part[(long)z * total + i];
+    out[i] = Elt<T>::from_f(s);
+}
+
+__global__ __launch_bounds__(256) void widen_kernel(const bf16_t* __restrict__ in,
+                                                   float* __restrict__ out, long n) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = bf2f(in[i]);
+}
+
+// 64x64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in,
+                                                        T* __restrict__ out, int rows,
+                                                        int cols) {
+    __shared__ T tile[64][65];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        int r = i / 64, c = i % 64;
+        if (r0 + r < rows && c0 + c < cols) tile[r][c] = in[(long)(r0 + r) * cols + c0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        int c = i / 64, r = i % 64;
+        if (r0 + r < rows && c0 + c < cols) out[(long)(c0 + c) * rows + r0 + r] = tile[r][c];
+    }
+}
+
+// One thread per (token, rotation pair j < dh/2); angles in double.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv,
+                                                      T* __restrict__ q_out, T* __restrict__ kc,
+                                                      T* __restrict__ vc, int n, int pos0,
+                                                      int cap, int Hq, int Hkv, int dh,
+                                                      int rope_on, double log_theta,
+                                                      long total) {
+    long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int half = dh / 2;
+    const int j = (int)(idx % half);
+    const long t = idx / half;          // token index b*n + i
+    const int b = (int)(t / n), i = (int)(t % n);
+    const long pos = pos0 + i;
+    float c = 1.f, s = 0.f;
+    if (rope_on) {
+        double inv_freq = exp(-2.0 * (double)j / (double)dh * log_theta);
+        double ang = (double)pos * inv_freq;
+        c = (float)cos(ang);
+        s = (float)sin(ang);
+    }
+    const int width = (Hq + 2 * Hkv) * dh;
+    const float* row = qkv + t * width;
+    for (int h = 0; h < Hq; ++h) {
+        float x1 = row[h * dh + j], x2 = row[h * dh + j + half];
+        T* o = q_out + t * (long)Hq * dh + (long)h * dh;
+        o[j] = Elt<T>::from_f(x1 * c - x2 * s);
+        o[j + half] = Elt<T>::from_f(x2 * c + x1 * s);
+    }
+    for (int h = 0; h < Hkv; ++h) {
+        const float* kr = row + (Hq + h) * dh;
+        const float* vr = row + (Hq + Hkv + h) * dh;
+        long slot = (((long)b * Hkv + h) * cap + pos) * dh;
+        float x1 = kr[j], x2 = kr[j + half];
+        kc[slot + j] = Elt<T>::from_f(x1 * c - x2 * s);
+        kc[slot + j + half] = Elt<T>::from_f(x2 * c + x1 * s);
+        vc[slot + j] = Elt<T>::from_f(vr[j]);
+        vc[slot + j + half] = Elt<T>::from_f(vr[j + half]);
+    }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
+                   hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, st, h, w, u, d, eps);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int B, float* h, int d,
+                      hipStream_t st) {
+    if (n <= 0 || B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(embed_kernel<T>, dim3(B * n), dim3(256), 0, st, E, tok, ld, n, V, h, d);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int cols,
+                         hipStream_t st) {
+    long total = (long)rows * cols;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)cdiv((int)total, 256)), dim3(256),
+                       0, st, part, out, splits, total);
+    return hipGetLastError();
+}
+
+hipError_t widen_bf16(const bf16_t* in, float* out, long n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, in, out, n);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t transpose(const T* in, T* out, int rows, int cols, hipStream_t st) {
+    dim3 grid(cdiv(cols, 64), cdiv(rows, 64));
+    hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, st, in, out, rows, cols);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int pos0, int cap,
+                   int Hq, int Hkv, int dh, int rope_on, float theta, hipStream_t st) {
+    long total = (long)B * n * (dh / 2);
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_kv_kernel<T>, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0,
+                       st, qkv, q_out, kc, vc, n, pos0, cap, Hq, Hkv, dh, rope_on,
+                       log((double)theta), total);
+    return hipGetLastError();
+}
+
+#define DG_INST(T)                                                                        \
+    template hipError_t rmsnorm<T>(const float*, const float*, T*, int, int, float,        \
+                                   hipStream_t);                                           \
+    template hipError_t embed_rows<T>(const T*, int, const int32_t*, int, int, int, float*, int, \
+                                      hipStream_t);                                        \
+    template hipError_t splitk_reduce<T>(const float*, T*, int, int, int, hipStream_t);    \
+    template hipError_t transpose<T>(const T*, T*, int, int, hipStream_t);                 \
+    template hipError_t rope_kv<T>(const float*, T*, T*, T*, int, int, int, int, int, int, \
+                                   int, int, float, hipStream_t);
+DG_INST(bf16_t)
+DG_INST(float)
+#undef DG_INST
+
+}  // namespace dg

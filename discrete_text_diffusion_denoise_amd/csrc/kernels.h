@@ -1,0 +1,122 @@
+// Host-side launchers of the gfx950 kernels (internal to libdg.so).
+// Every launcher enqueues on `st` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// ------------------------------------------------------------------ GEMM
+enum { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SPLITK = 2, EPI_EMBED_ADD = 3 };
+
+struct GemmArgs {
+    int M = 0, N = 0, K = 0;
+    const void* A = nullptr;        // [M][lda] of T (amode 0) or fp32 logits (amode 1)
+    long lda = 0;
+    const int32_t* a_rows = nullptr;  // optional row gather for A (amode 0)
+    const float* a_stats = nullptr;   // amode 1: per-row {max, sum, ...}, stride 4
+    const void* B = nullptr;        // [N][ldb] of T
+    long ldb = 0;
+    void* C = nullptr;              // fp32 [M][ldc] (split-K: [splits][M][ldc])
+    long ldc = 0;
+    int k_split = 0;                // K elements per split (multiple of 64)
+    const void* E = nullptr;        // EPI_EMBED_ADD: embedding [vocab][lde] of T
+    long lde = 0;
+    int vocab = 0;
+    const int32_t* tokens = nullptr;  // EPI_EMBED_ADD: token per row
+};
+
+// C (op)= A * B^T.  amode 1 reads A as softmax of fp32 logits (only with
+// EPI_SPLITK).  T = bf16_t (uint16_t) or float.
+template <typename T>
+hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_t st);
+
+// ------------------------------------------------------------------ elementwise
+// u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T)
+template <typename T>
+hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
+                   hipStream_t st);
+// h[b*n + i] = E[tok[b*ld + i]] (fp32), b < B, i < n; E has V rows
+template <typename T>
+hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int B, float* h, int d,
+                      hipStream_t st);
+// out[t][j] = sum_s part[s][t][j]  (T)
+template <typename T>
+hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int cols,
+                         hipStream_t st);
+// out[i] = float(in[i])
+hipError_t widen_bf16(const uint16_t* in, float* out, long n, hipStream_t st);
+// out[j][v] = E[v][j]
+template <typename T>
+hipError_t transpose(const T* in, T* out, int rows, int cols, hipStream_t st);
+
+// RoPE on q and k (fp32 qkv [B*n][(Hq+2Hkv)*dh]); q -> q_out [B*n][Hq*dh] (T);
+// k, v -> cache slots [pos0, pos0+n) of kc/vc [B][Hkv][cap][dh] (T, one layer).
+template <typename T>
+hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int pos0, int cap,
+                   int Hq, int Hkv, int dh, int rope_on, float theta, hipStream_t st);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+    const void* q = nullptr;   // [B*n][Hq*dh] (T)
+    const void* kc = nullptr;  // [B][Hkv][cap][dh] (T)
+    const void* vc = nullptr;
+    void* out = nullptr;       // [B*n][Hq*dh] (T)
+    float* part_o = nullptr;   // [splits][B*n][Hq][dh]   (splits > 1)
+    float* part_ml = nullptr;  // [splits][B*n][Hq][2]
+    int B = 0, n = 0, pos0 = 0, cap = 0, Hq = 0, Hkv = 0, dh = 0;
+    int kv_len = 0;            // keys [0, kv_len)
+    int causal = 0;            // query i (position pos0+i) sees keys <= pos0+i
+    int splits = 1;
+    int split_len = 0;         // keys per split (multiple of 32)
+};
+template <typename T>
+hipError_t attention(const AttnArgs& a, hipStream_t st);
+// Number of key splits the launcher would use for this shape.
+int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int max_splits,
+                     int* split_len);
+
+// ------------------------------------------------------------------ MoE
+struct MoeArgs {
+    int T = 0, d = 0, E = 0, k = 0, F = 0;
+    const float* z = nullptr;        // router logits [T][E]
+    int32_t* route = nullptr;        // [T][k] experts, selection order
+    float* gates = nullptr;          // [T][k]
+    int32_t* counts = nullptr;       // [E]
+    int32_t* offsets = nullptr;      // [E+1]
+    int32_t* perm_tok = nullptr;     // [T*k] token of each sorted slot
+    int32_t* slot_of = nullptr;      // [T*k] sorted slot of (t, j)
+    const void* u = nullptr;         // normalised tokens [T][d] (T)
+    const void* w_gate = nullptr;    // [E][F][d]
+    const void* w_up = nullptr;      // [E][F][d]
+    const void* w_down = nullptr;    // [E][d][F]
+    void* act = nullptr;             // [T*k][F] (T)
+    float* y = nullptr;              // [T*k][d]
+    float* h = nullptr;              // residual [T][d]
+};
+template <typename T>
+hipError_t moe_forward(const MoeArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------------ sampler
+struct SampleArgs {
+    int B = 0, N = 0, V = 0, step = 0;
+    int lock_rule = 1;
+    float theta = 0.1f, tau = 0.005f, inv_t = 1.0f;
+    int require_stable = 1, max_steps = 48;
+    uint64_t seed = 0;
+    const float* logits = nullptr;   // [B][N][V]
+    int32_t* canvas = nullptr;
+    int32_t* argmax = nullptr;
+    uint8_t* lock = nullptr;
+    float* stats = nullptr;          // [B][N][4]
+    int32_t* stop = nullptr;         // [B]
+    int32_t* y = nullptr;            // scratch [B][N] drawn tokens
+    int32_t* r = nullptr;            // scratch [B][N] renoise tokens
+    int32_t* newmax = nullptr;       // scratch [B][N] argmax of this step
+};
+hipError_t sample_update(const SampleArgs& a, hipStream_t st);
+hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,
+                       hipStream_t st);
+
+}  // namespace dg

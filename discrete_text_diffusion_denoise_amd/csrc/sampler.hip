@@ -1,0 +1,440 @@
+// Multinomial-diffusion sampler on gfx950.
+//
+// Report-summary page (animattoys.com), section 1: uncertain positions are
+// replaced by any vocabulary token, and locked tokens can still change in a
+// later round; section 4: order positions by entropy and lock from the most
+// certain while the running entropy stays within the budget, re-randomise the
+// rest, temperature falls linearly, stop once the mean entropy is small and
+// the most likely sequence is unchanged, within a round budget.
+//
+// The arithmetic is fixed exactly (the pages leave it open) so that decisions
+// are bit-reproducible:
+//   E(x)  e^x for x <= 0: Cody-Waite reduction with a two-part ln2, Taylor
+//         polynomial of degree 6 in Horner form with fma, 2^k from exponent
+//         bits; x < -87 gives 0 (never subnormal).
+//   L(x)  ln x for x >= 1: mantissa in (sqrt(1/2), sqrt(2)], 2*atanh series
+//         to f^13 with fma, two-part ln2.
+//   Row layout: 65536-entry tiles; chunk c = t*1024 + lam holds entries
+//         4*(t*16384 + d*1024 + lam) + q, d < 16, q < 4, in increasing order.
+//   Chunk record: max, first argmax, sequential sums of E(z), E(z)*z and
+//         E(z/T) with z = l - max.  Records merge by a symmetric rule; the row
+//         record folds each lane's tiles in order and then reduces over the
+//         1024 lanes by a pairwise tree (adjacent pairs first).
+//   Draw: three inverse-CDF picks (64-chunk superchunks, chunks, entries),
+//         each "first running sum > u * total, else last positive", with
+//         u = (2r+1)/2^24 from Philox4x64-10 words 0, 2 and 3; word 1 gives
+//         the renoise token mulhi(word, V).
+// Every float operation below is one IEEE binary32 operation in the order
+// written; contraction into fma is disabled for this file.
+#pragma clang fp contract(off)
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+namespace {
+
+constexpr int NLANE = 1024;
+constexpr int NDEPTH = 16;
+constexpr int TILE = 4 * NLANE * NDEPTH;
+constexpr int SUPER = 64;
+
+__device__ __forceinline__ float dexp(float x) {
+    if (!(x >= -87.0f)) return 0.0f;
+    const float LOG2E = 1.44269504088896341f;
+    const float LN2_HI = 0.693145751953125f;
+    const float LN2_LO = 1.42860682030941723e-06f;
+    float kf = __builtin_rintf(x * LOG2E);
+    float r = __builtin_fmaf(-kf, LN2_HI, x);
+    r = __builtin_fmaf(-kf, LN2_LO, r);
+    float p = 1.0f / 720.0f;
+    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const int k = (int)kf;
+    return p * __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+__device__ __forceinline__ float dlog(float x) {
+    const float LN2_HI = 0.693145751953125f;
+    const float LN2_LO = 1.42860682030941723e-06f;
+    const uint32_t b = __float_as_uint(x);
+    int e = (int)((b >> 23) & 0xffu) - 127;
+    float m = __uint_as_float((b & 0x7fffffu) | 0x3f800000u);
+    if (m > 1.41421356f) {
+        m = m * 0.5f;
+        e = e + 1;
+    }
+    const float f = (m - 1.0f) / (m + 1.0f);
+    const float f2 = f * f;
+    float q = 1.0f / 13.0f;
+    q = __builtin_fmaf(q, f2, 1.0f / 11.0f);
+    q = __builtin_fmaf(q, f2, 1.0f / 9.0f);
+    q = __builtin_fmaf(q, f2, 1.0f / 7.0f);
+    q = __builtin_fmaf(q, f2, 1.0f / 5.0f);
+    q = __builtin_fmaf(q, f2, 1.0f / 3.0f);
+    q = __builtin_fmaf(q, f2, 1.0f);
+    const float lm = (2.0f * f) * q;
+    const float ef = (float)e;
+    return __builtin_fmaf(ef, LN2_HI, __builtin_fmaf(ef, LN2_LO, lm));
+}
+
+// Philox4x64-10 (Salmon et al., SC'11).
+__device__ __forceinline__ void philox(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                       uint64_t k0, uint64_t k1, uint64_t o[4]) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    o[0] = c0;
+    o[1] = c1;
+    o[2] = c2;
+    o[3] = c3;
+}
+
+__device__ __forceinline__ float uniform01(uint64_t w) {
+    const uint32_t r = (uint32_t)(w >> 41);
+    return (float)(2u * r + 1u) * 5.9604644775390625e-08f;
+}
+__device__ __forceinline__ int32_t uniform_token(uint64_t w, int V) {
+    return (int32_t)__umul64hi(w, (uint64_t)(uint32_t)V);
+}
+
+struct Rec {
+    float m;
+    int j;
+    float s, a;
+};
+
+__device__ __forceinline__ Rec merge(const Rec& x, const Rec& y) {
+    if (x.s == 0.0f) return y;
+    if (y.s == 0.0f) return x;
+    Rec r;
+    r.m = x.m > y.m ? x.m : y.m;
+    r.j = x.m > y.m ? x.j : (y.m > x.m ? y.j : (x.j < y.j ? x.j : y.j));
+    const float dx = x.m - r.m, dy = y.m - r.m;
+    const float fx = dexp(dx), fy = dexp(dy);
+    const float sx = x.s * fx, sy = y.s * fy;
+    r.s = sx + sy;
+    const float ax = fx * (x.a + dx * x.s);
+    const float ay = fy * (y.a + dy * y.s);
+    r.a = ax + ay;
+    return r;
+}
+
+__device__ __forceinline__ Rec shfl_rec(const Rec& x, int mask) {
+    Rec o;
+    o.m = __shfl_xor(x.m, mask, 64);
+    o.j = __shfl_xor(x.j, mask, 64);
+    o.s = __shfl_xor(x.s, mask, 64);
+    o.a = __shfl_xor(x.a, mask, 64);
+    return o;
+}
+
+// First index whose running sum exceeds u * total, else the last positive.
+__device__ int pick_seq(const float* w, int n, float u) {
+    float total = 0.0f;
+    for (int i = 0; i < n; ++i) total = total + w[i];
+    const float target = u * total;
+    float acc = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        acc = acc + w[i];
+        if (acc > target) return i;
+    }
+    for (int i = n - 1; i >= 0; --i)
+        if (w[i] > 0.0f) return i;
+    return 0;
+}
+
+// One workgroup of 1024 threads per logit row.
+template <bool VEC>
+__global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
+    extern __shared__ __align__(16) float sm[];
+    const int nt = cdiv(a.V, TILE);
+    float* Gs = sm;                       // [nt*1024] chunk weights at temperature T
+    float* Ms = sm + nt * NLANE;          // [nt*1024] chunk maxima
+    __shared__ Rec wrec[16];
+    __shared__ float Wsup[8 * 16];
+    __shared__ float wk[4 * NDEPTH];
+    __shared__ int kk[4 * NDEPTH];
+
+    const long rowid = blockIdx.x;        // b*N + i
+    const int b = (int)(rowid / a.N), i = (int)(rowid % a.N);
+    if (a.stop[b]) return;
+    const float* row = a.logits + rowid * (long)a.V;
+    const int lam = threadIdx.x, lane = lam & 63, wave = lam >> 6;
+    const float invT = a.inv_t;
+
+    Rec F = {-INFINITY, -1, 0.0f, 0.0f};
+    for (int t = 0; t < nt; ++t) {
+        float x[4 * NDEPTH];
+        const long g0 = (long)t * (NLANE * NDEPTH) + lam;
+#pragma unroll
+        for (int d = 0; d < NDEPTH; ++d) {
+            const long k = 4 * (g0 + (long)d * NLANE);
+            if (VEC && k + 3 < a.V) {
+                const float4 v = *reinterpret_cast<const float4*>(row + k);
+                x[4 * d + 0] = v.x;
+                x[4 * d + 1] = v.y;
+                x[4 * d + 2] = v.z;
+                x[4 * d + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[4 * d + q] = (k + q < a.V) ? row[k + q] : -INFINITY;
+            }
+        }
+        // chunk max and first argmax, in member order
+        float m = -INFINITY;
+        int j = -1;
+#pragma unroll
+        for (int d = 0; d < NDEPTH; ++d)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const long k = 4 * (g0 + (long)d * NLANE) + q;
+                if (k < a.V && (x[4 * d + q] > m || j < 0)) {
+                    m = x[4 * d + q];
+                    j = (int)k;
+                }
+            }
+        Rec rc = {-INFINITY, -1, 0.0f, 0.0f};
+        float s2 = 0.0f;
+        if (j >= 0) {
+            float s = 0.0f, ac = 0.0f;
+#pragma unroll
+            for (int d = 0; d < NDEPTH; ++d)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const long k = 4 * (g0 + (long)d * NLANE) + q;
+                    if (k < a.V) {
+                        const float z = x[4 * d + q] - m;
+                        const float e = dexp(z);
+                        s = s + e;
+                        const float ez = e * z;
+                        ac = ac + ez;
+                        if (invT != 1.0f) s2 = s2 + dexp(z * invT);
+                    }
+                }
+            if (invT == 1.0f) s2 = s;
+            rc.m = m;
+            rc.j = j;
+            rc.s = s;
+            rc.a = ac;
+        }
+        Gs[t * NLANE + lam] = s2;
+        Ms[t * NLANE + lam] = m;
+        F = (t == 0) ? rc : merge(F, rc);
+    }
+    // pairwise tree over lanes: within the wave, then over the 16 waves
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) F = merge(F, shfl_rec(F, o));
+    if (lane == 0) wrec[wave] = F;
+    __syncthreads();
+    __shared__ Rec rowrec;
+    if (lam == 0) {
+        Rec lv[16];
+        for (int w = 0; w < 16; ++w) lv[w] = wrec[w];
+        for (int n = 16; n > 1; n >>= 1)
+            for (int w = 0; w < n / 2; ++w) lv[w] = merge(lv[2 * w], lv[2 * w + 1]);
+        rowrec = lv[0];
+    }
+    __syncthreads();
+    const Rec R = rowrec;
+
+    // chunk weights at temperature T, relative to the row max
+    for (int c = lam; c < nt * NLANE; c += NLANE) {
+        const float s2 = Gs[c];
+        Gs[c] = s2 == 0.0f ? 0.0f : s2 * dexp((Ms[c] - R.m) * invT);
+    }
+    __syncthreads();
+    const int nsup = nt * (NLANE / SUPER);
+    if (lam < nsup) {
+        float acc = 0.0f;
+        for (int l = 0; l < SUPER; ++l) acc = acc + Gs[lam * SUPER + l];
+        Wsup[lam] = acc;
+    }
+    __syncthreads();
+    __shared__ int cstar_s;
+    __shared__ uint64_t words[4];
+    if (lam == 0) {
+        uint64_t o[4];
+        philox((uint64_t)a.step, (uint64_t)b, (uint64_t)i, 0ull, a.seed, 0ull, o);
+        words[0] = o[0];
+        words[1] = o[1];
+        words[2] = o[2];
+        words[3] = o[3];
+        const int sstar = pick_seq(Wsup, nsup, uniform01(o[0]));
+        cstar_s = sstar * SUPER + pick_seq(Gs + sstar * SUPER, SUPER, uniform01(o[2]));
+    }
+    __syncthreads();
+    // entries of the chosen chunk, in member order
+    const int cstar = cstar_s;
+    if (lam < 4 * NDEPTH) {
+        const int t = cstar / NLANE, l = cstar % NLANE;
+        const int d = lam / 4, q = lam % 4;
+        const long k = 4 * ((long)t * NLANE * NDEPTH + (long)d * NLANE + l) + q;
+        wk[lam] = k < a.V ? dexp((row[k] - Ms[cstar]) * invT) : 0.0f;
+        kk[lam] = k < a.V ? (int)k : -1;
+    }
+    __syncthreads();
+    if (lam == 0) {
+        // compact the members (entries past V are not members)
+        float w[4 * NDEPTH];
+        int ks[4 * NDEPTH];
+        int n = 0;
+        for (int u = 0; u < 4 * NDEPTH; ++u)
+            if (kk[u] >= 0) {
+                w[n] = wk[u];
+                ks[n] = kk[u];
+                ++n;
+            }
+        const int yv = n > 0 ? ks[pick_seq(w, n, uniform01(words[3]))] : 0;
+        float H = dlog(R.s) - R.a / R.s;
+        H = H > 0.0f ? H : 0.0f;
+        const float pmax = 1.0f / R.s;
+        float* st = a.stats + rowid * 4;
+        st[0] = R.m;
+        st[1] = R.s;
+        st[2] = H;
+        st[3] = pmax;
+        a.newmax[rowid] = R.j;
+        a.y[rowid] = yv;
+        a.r[rowid] = uniform_token(words[1], a.V);
+    }
+}
+
+// One workgroup per canvas: lock rule, renoise, stability and stop.
+__global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
+    const int b = blockIdx.x;
+    if (a.stop[b]) return;
+    __shared__ uint64_t keys[1024];
+    __shared__ float Hs[1024];
+    __shared__ uint8_t lk[1024];
+    const int tid = threadIdx.x;
+    const int N = a.N;
+    const long base = (long)b * N;
+    int npow = 1;
+    while (npow < N) npow <<= 1;
+    for (int i = tid; i < npow; i += blockDim.x) {
+        if (i < N) {
+            const float H = a.stats[(base + i) * 4 + 2];
+            Hs[i] = H;
+            keys[i] = ((uint64_t)__float_as_uint(H) << 32) | (uint32_t)i;
+            lk[i] = a.lock_rule == 0 ? (a.stats[(base + i) * 4 + 3] > a.theta ? 1 : 0) : 0;
+        } else {
+            keys[i] = ~0ull;
+        }
+    }
+    __syncthreads();
+    if (a.lock_rule == 1) {
+        // bitonic sort of (H, index); H >= 0 so its bits order like the value
+        for (int size = 2; size <= npow; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < npow; i += blockDim.x) {
+                    const int p = i ^ stride;
+                    if (p > i) {
+                        const bool up = (i & size) == 0;
+                        const uint64_t ki = keys[i], kp = keys[p];
+                        if ((ki > kp) == up) {
+                            keys[i] = kp;
+                            keys[p] = ki;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (tid == 0) {
+            float acc = 0.0f;
+            for (int n = 0; n < N; ++n) {
+                const int i = (int)(uint32_t)keys[n];
+                const float H = Hs[i];
+                if (acc + H <= a.theta) {
+                    lk[i] = 1;
+                    acc = acc + H;
+                } else {
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    int same = 1;
+    for (int i = tid; i < N; i += blockDim.x) {
+        const int am = a.newmax[base + i];
+        if (a.argmax[base + i] != am) same = 0;
+        a.argmax[base + i] = am;
+        a.lock[base + i] = lk[i];
+        a.canvas[base + i] = lk[i] ? a.y[base + i] : a.r[base + i];
+    }
+    const int stable = __syncthreads_and(same) && a.step > 0;
+    if (tid == 0) {
+        float sumH = 0.0f;
+        for (int i = 0; i < N; ++i) sumH = sumH + Hs[i];
+        const float meanH = sumH / (float)N;
+        int st = (meanH < a.tau) && (!a.require_stable || stable);
+        if (a.step + 1 >= a.max_steps) st = 1;
+        a.stop[b] = st;
+    }
+}
+
+__global__ __launch_bounds__(256) void canvas_init_kernel(uint64_t seed, int block, int N, int V,
+                                                          int32_t* canvas, long total) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int b = (int)(idx / N), i = (int)(idx % N);
+    uint64_t o[4];
+    philox((uint64_t)block, (uint64_t)b, (uint64_t)i, 1ull, seed, 0ull, o);
+    canvas[idx] = uniform_token(o[0], V);
+}
+
+}  // namespace
+
+hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
+    if (a.B <= 0 || a.N <= 0) return hipSuccess;
+    const int nt = cdiv(a.V, TILE);
+    const size_t lds = (size_t)2 * nt * NLANE * sizeof(float);
+    static bool attr_set[2] = {false, false};
+    const bool vec = (a.V % 4) == 0;
+    const void* kern = vec ? (const void*)sample_row_kernel<true> : (const void*)sample_row_kernel<false>;
+    if (!attr_set[vec]) {
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(2 * 8 * NLANE * sizeof(float)));
+        if (e != hipSuccess) return e;
+        attr_set[vec] = true;
+    }
+    if (vec)
+        hipLaunchKernelGGL(sample_row_kernel<true>, dim3(a.B * a.N), dim3(NLANE), lds, st, a);
+    else
+        hipLaunchKernelGGL(sample_row_kernel<false>, dim3(a.B * a.N), dim3(NLANE), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sample_canvas_kernel, dim3(a.B), dim3(1024), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,
+                       hipStream_t st) {
+    const long total = (long)B * N;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(canvas_init_kernel, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, st,
+                       seed, block, N, V, canvas, total);
+    return hipGetLastError();
+}
+
+}  // namespace dg

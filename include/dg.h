@@ -1,0 +1,254 @@
+/*
+ * dg.h -- C ABI of an MI355X-native denoising step for a block text-diffusion
+ * mixture-of-experts language model.
+ *
+ * The method (pages on DiffusionGemma; citations name the page and section):
+ *   - report-summary page (animattoys.com), section 1: a block of 256 tokens
+ *     starts as uniformly random vocabulary tokens and is refined in
+ *     parallel over rounds; uncertain positions are replaced by any
+ *     vocabulary token (multinomial diffusion);
+ *   - same page, section 2: one set of weights runs causal attention over
+ *     the prompt and bidirectional attention over the canvas; 128 experts,
+ *     8 active per token; a self-conditioning input from the previous round;
+ *   - same page, section 4: entropy-ordered locking within a 0.1 entropy
+ *     budget, re-randomisation of the rest, temperature 0.8 -> 0.4, stop on
+ *     mean entropy < 0.005 with an unchanged most likely sequence, <= 48
+ *     rounds;
+ *   - youleyou.com article, "Architecture basis": the causal encoder fills a
+ *     KV cache that every canvas position attends to; finished blocks are
+ *     handed to the KV cache and the next canvas is conditioned on them
+ *     (also akiraxclaw.com blog, "memory, not compute").
+ *
+ * Conventions for every call:
+ *   - Device pointers ("d_" prefix) point to GPU memory owned by the caller;
+ *     host pointers ("h_" prefix, or structs passed by pointer) are read
+ *     during the call only.  The library never allocates device memory: all
+ *     scratch space comes from a caller-supplied workspace.
+ *   - Work is enqueued asynchronously on the given stream (a hipStream_t
+ *     passed as void*; NULL = the default stream).  Only dg_generate_block
+ *     waits on the stream (to read stop flags).
+ *   - Every function returns a dg_status; on failure nothing has been
+ *     enqueued (argument errors) or the HIP error is reported as DG_ERR_HIP.
+ *     dg_last_error() gives a human-readable detail for the calling thread.
+ *   - Token ids are int32 in [0, vocab).  Canvas length N is 256 in the
+ *     pages' method; the library accepts any N in [1, 1024].
+ *   - Weight layout: every linear map is [out_features][in_features],
+ *     row-major, applied as y = x W^T, in the model dtype (fp32 or bf16).
+ *     RMSNorm scales are fp32.  Weights are borrowed: they must stay valid
+ *     while the model handle lives.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_ARG = 1,         /* NULL pointer or out-of-range argument            */
+    DG_ERR_SHAPE = 2,       /* shapes inconsistent or outside supported limits  */
+    DG_ERR_DTYPE = 3,       /* unknown dtype                                    */
+    DG_ERR_CAPACITY = 4,    /* KV cache or workspace too small                  */
+    DG_ERR_NONFINITE = 5,   /* reserved: non-finite values detected             */
+    DG_ERR_HIP = 6,         /* a HIP runtime call failed                        */
+    DG_ERR_UNSUPPORTED = 7  /* valid request this build does not implement      */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+typedef enum {
+    DG_LOCK_MAXPROB = 0,    /* lock i  <=>  max-probability(i) > theta                      */
+    DG_LOCK_CUMENT = 1      /* entropy order, lock while running entropy <= theta (pages) */
+} dg_lock_rule;
+
+typedef struct {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_heads;        /* query heads                                    */
+    int32_t n_kv_heads;     /* key/value heads (n_heads % n_kv_heads == 0)    */
+    int32_t head_dim;       /* even, <= 256, multiple of 32                   */
+    int32_t n_experts;      /* <= 256                                         */
+    int32_t top_k;          /* <= min(n_experts, 16)                          */
+    int32_t d_ff;           /* expert hidden width (multiple of 32)           */
+    int32_t vocab;          /* <= 524288                                      */
+    int32_t canvas;         /* N, tokens per canvas                           */
+    int32_t dtype;          /* dg_dtype of weights, KV cache, matmul operands */
+    int32_t rope_on;        /* 1: rotate-half RoPE on q and k                 */
+    float rope_theta;       /* RoPE base                                      */
+    float rms_eps;          /* RMSNorm epsilon                                */
+} dg_config;
+
+typedef struct {
+    const float* attn_norm;  /* [d]                 */
+    const void* wq;          /* [Hq*dh][d]          */
+    const void* wk;          /* [Hkv*dh][d]         */
+    const void* wv;          /* [Hkv*dh][d]         */
+    const void* wo;          /* [d][Hq*dh]          */
+    const float* moe_norm;   /* [d]                 */
+    const void* w_router;    /* [E][d]              */
+    const void* w_gate;      /* [E][F][d]           */
+    const void* w_up;        /* [E][F][d]           */
+    const void* w_down;      /* [E][d][F]           */
+} dg_layer_weights;
+
+typedef struct {
+    const void* embed;       /* [V][d] tied embedding / output head                    */
+    const void* embed_t;     /* [d][V] the same matrix transposed (dg_embed_transpose); */
+                             /* required for self-conditioning, else may be NULL       */
+    const void* w_sc;        /* [d][d] self-conditioning projection                    */
+    const float* final_norm; /* [d]                                                    */
+    const dg_layer_weights* layers; /* host array [n_layers], copied at create        */
+} dg_weights;
+
+typedef struct {
+    int32_t lock_rule;       /* dg_lock_rule                                   */
+    float lock_theta;        /* entropy budget (CUMENT) or probability (MAXPROB) */
+    float temp_start;        /* temperature at step 0                          */
+    float temp_end;          /* temperature at step max_steps-1 (linear)       */
+    float stop_tau;          /* mean-entropy stop threshold (nats)             */
+    int32_t require_stable;  /* 1: also require argmax unchanged from previous step */
+    int32_t max_steps;       /* round budget (>= 1)                            */
+    uint64_t seed;           /* Philox key                                     */
+    int32_t selfcond_on;     /* dg_generate_block: feed previous logits back   */
+} dg_sampler_params;
+
+typedef struct dg_model dg_model;
+typedef struct dg_kv dg_kv;
+
+/* ---------------------------------------------------------------- errors */
+const char* dg_status_string(dg_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dg_last_error(void);
+
+/* ---------------------------------------------------------------- model */
+/* Validates the configuration and copies the weight pointer table.
+ * DG_ERR_SHAPE on unsupported shapes (limits listed in dg_config). */
+dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** out);
+void dg_model_destroy(dg_model* m);
+
+/* Writes d_out [d][V] = embed^T (the layout the self-conditioning product
+ * streams).  d_out must hold vocab*d_model elements of the model dtype. */
+dg_status dg_embed_transpose(const dg_model* m, const void* d_embed, void* d_out, void* stream);
+
+/* ---------------------------------------------------------------- KV cache */
+/* Bytes of a KV cache for `batch` sequences of up to `capacity` positions:
+ * K then V, each [n_layers][batch][n_kv_heads][capacity][head_dim] in the
+ * model dtype, K after RoPE.  A denoising step needs capacity >= len + N
+ * (the canvas K/V are staged in slots [len, len+N) without advancing len). */
+dg_status dg_kv_bytes(const dg_model* m, int32_t batch, int32_t capacity, size_t* bytes);
+/* Wraps caller memory (d_buf, >= dg_kv_bytes) as an empty cache (len = 0). */
+dg_status dg_kv_create(const dg_model* m, int32_t batch, int32_t capacity, void* d_buf,
+                       dg_kv** out);
+void dg_kv_destroy(dg_kv* kv);
+dg_status dg_kv_length(const dg_kv* kv, int32_t* len);
+/* Rewinds (or advances) the valid length, e.g. to reuse an encoded prompt. */
+dg_status dg_kv_set_length(dg_kv* kv, int32_t len);
+
+/* ---------------------------------------------------------------- workspace */
+/* Bytes of scratch for every model call with up to `batch` sequences.
+ * Prompts of any length are encoded in chunks that fit this workspace. */
+dg_status dg_workspace_bytes(const dg_model* m, int32_t batch, size_t* bytes);
+/* Bytes of scratch for dg_sample_update alone (no model needed). */
+dg_status dg_sampler_workspace_bytes(int32_t batch, int32_t canvas, size_t* bytes);
+
+/* ---------------------------------------------------------------- the path */
+
+/* Causal encode of d_tokens [batch][n_tokens] (report-summary page, section 2;
+ * youleyou.com article, "Architecture basis"): embeddings run through every
+ * layer with causal attention over the cache plus the new tokens; K (after
+ * RoPE) and V of every layer are appended at [len, len+n_tokens) and len
+ * advances.  The last layer's MoE feeds no K/V and is skipped.
+ * DG_ERR_CAPACITY if len + n_tokens > capacity. */
+dg_status dg_encode_prompt(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_tokens,
+                           int32_t n_tokens, void* d_ws, size_t ws_bytes, void* stream);
+
+/* One denoiser forward over canvases d_canvas [batch][N] (report-summary
+ * page, sections 2 and 5): h0 = E[x] + s W_sc^T with s = softmax(prev) E
+ * (s = 0 when d_prev_logits is NULL); per layer pre-norm bidirectional
+ * attention over [cache ; canvas] and top-k SwiGLU MoE; logits =
+ * RMSNorm(h) E^T written to d_logits [batch][N][V] (fp32).
+ * d_prev_stats [batch][N][4] are the per-position statistics dg_sample_update
+ * wrote for d_prev_logits ({max, sum of exp(l - max), entropy, max-prob});
+ * both are NULL or both are set.  The cache length is unchanged (canvas K/V
+ * use slots [len, len+N), so capacity >= len + N is required). */
+dg_status dg_denoise_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
+                          const float* d_prev_logits, const float* d_prev_stats,
+                          float* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Sampler update of step `step` (report-summary page, sections 1 and 4).
+ * Model-free: reads fp32 logits [batch][N][V]; for every canvas b with
+ * d_stop[b] == 0 it writes, per position,
+ *   d_stats [b][i][4] = {max logit, sum exp(l - max), entropy H, max-prob}
+ *   d_argmax[b][i]    = first index of the max logit (in: previous step's)
+ *   d_lock[b][i]      = lock decision (rule in params)
+ *   d_canvas[b][i]    = lock ? token drawn from softmax(l / T_step)
+ *                            : uniform renoise token
+ *   d_stop[b]         = 1 if the stop rule fires (or the budget is used up).
+ * Canvases with d_stop[b] == 1 on entry are left untouched.  The binary32
+ * arithmetic (statistics, draw, lock and stop) is fixed exactly, so results
+ * are bit-reproducible and match the reference definition bit for bit.
+ * Random numbers: Philox4x64-10, key (seed, 0), counter (step, b, i, 0).
+ * d_ws needs dg_sampler_workspace_bytes.  N <= 1024, vocab <= 524288. */
+dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t batch,
+                           int32_t canvas, int32_t vocab, const float* d_logits,
+                           int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                           float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
+                           void* stream);
+
+/* Canvas initialisation: d_canvas [batch][N] = uniform tokens from Philox
+ * counter (block_index, b, i, 1), key (seed, 0) (report-summary page,
+ * section 1: the block starts as random tokens). */
+dg_status dg_canvas_init(uint64_t seed, int32_t block_index, int32_t batch, int32_t canvas,
+                         int32_t vocab, int32_t* d_canvas, void* stream);
+
+/* Block commit (akiraxclaw.com blog, "memory, not compute"): causal encode of
+ * the finished block d_block [batch][N] appended to the cache; len += N. */
+dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_block,
+                          void* d_ws, size_t ws_bytes, void* stream);
+
+/* One block of block-autoregressive generation: canvas init, up to
+ * params->max_steps rounds of dg_denoise_step + dg_sample_update (self-
+ * conditioned on the previous round if params->selfcond_on), stop per
+ * canvas, block = the last round's argmax, then dg_commit_block.
+ * d_block_out [batch][N]; h_steps_out [batch] receives the rounds each canvas
+ * ran.  Waits on the stream once per round to read the stop flags.
+ * d_ws needs dg_generate_workspace_bytes. */
+dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* bytes);
+dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
+                            int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
+                            void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- stages */
+/* The step's stages, exposed so each can be driven and checked on its own.
+ * T = number of tokens; h buffers are fp32 [T][d] residual streams. */
+
+/* Denoiser input: d_h [batch*N][d] = E[canvas] + (softmax(prev) E) W_sc^T. */
+dg_status dg_stage_input(dg_model* m, int32_t batch, const int32_t* d_canvas,
+                         const float* d_prev_logits, const float* d_prev_stats, float* d_h,
+                         void* d_ws, size_t ws_bytes, void* stream);
+/* Attention half-block of `layer` for n new tokens per sequence at positions
+ * [len, len+n): RMSNorm, Q/K/V, RoPE, K/V written to cache slots [len, len+n),
+ * attention (causal != 0: each query sees keys <= its position; causal == 0:
+ * every query sees all len+n keys), output projection, residual into d_h
+ * [batch*n][d].  The cache length is not changed. */
+dg_status dg_stage_attention(dg_model* m, dg_kv* kv, int32_t layer, int32_t batch, int32_t n,
+                             int32_t causal, float* d_h, void* d_ws, size_t ws_bytes,
+                             void* stream);
+/* MoE half-block of `layer` over T tokens: RMSNorm, router, top-k, SwiGLU
+ * experts, gate-weighted sum, residual into d_h [T][d].  If d_route is not
+ * NULL it receives the chosen experts [T][top_k] (selection order) and
+ * d_gates [T][top_k] the gates. */
+dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_t* d_route,
+                       float* d_gates, void* d_ws, size_t ws_bytes, void* stream);
+/* Head: d_logits [T][V] = RMSNorm(d_h) E^T (fp32). */
+dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,138 @@
+"""GPU sampler (dg_sample_update, dg_canvas_init) against the C oracle:
+bit-exact canvas, argmax, lock, statistics and stop flags on identical fp32
+logits and seed."""
+import numpy as np
+import pytest
+import torch
+
+from discrete_text_diffusion_denoise_amd import binding, synthetic
+from oracle import sampler as osampler
+
+from helpers import DEV, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_update(params, step, logits, canvas, argmax, stop):
+    B, N, V = logits.shape
+    lg = to_dev(logits)
+    cv = to_dev(canvas)
+    am = to_dev(argmax)
+    st = to_dev(stop)
+    lock = torch.zeros((B, N), dtype=torch.uint8, device=DEV)
+    stats = torch.zeros((B, N, 4), dtype=torch.float32, device=DEV)
+    ws = binding.sampler_workspace(B, N)
+    binding.sample_update(params, step, lg, cv, am, lock, stats, st, ws)
+    torch.cuda.synchronize()
+    return (cv.cpu().numpy(), am.cpu().numpy(), lock.cpu().numpy(), stats.cpu().numpy(),
+            st.cpu().numpy())
+
+
+def oracle_update(params, step, logits, canvas, argmax, stop):
+    c, a, s = canvas.copy(), argmax.copy(), stop.copy()
+    lock, stats = osampler.sample_update(params, step, logits, c, a, s)
+    return c, a, lock, stats, s
+
+
+def assert_same(g, r, what=""):
+    names = ("canvas", "argmax", "lock", "stats", "stop")
+    for name, x, y in zip(names, g, r):
+        if name == "stats":
+            bad = x.view(np.uint32) != y.view(np.uint32)
+            assert not bad.any(), f"{what} stats differ at {np.argwhere(bad)[:5].tolist()}"
+        else:
+            bad = x != y
+            assert not bad.any(), f"{what} {name} differs at {np.argwhere(bad)[:5].tolist()}"
+
+
+CASES = [
+    # B, N, V, sigma, lock rule, step, max_steps, T0, T1
+    (1, 256, 1024, 0.9, 1, 0, 4, 0.8, 0.4),
+    (2, 256, 1024, 4.0, 1, 1, 48, 0.8, 0.4),
+    (1, 256, 262144, 0.9, 0, 0, 48, 1.0, 1.0),      # full vocabulary, lock if pmax > 0.9
+    (2, 64, 1001, 2.0, 1, 5, 48, 0.8, 0.4),         # vocabulary not a multiple of 4
+    (1, 16, 70001, 1.5, 0, 3, 10, 0.8, 0.4),        # two tiles, ragged tail
+    (3, 100, 4096, 12.0, 1, 2, 48, 0.8, 0.4),       # peaked rows: many locks
+    (1, 1, 8, 1.0, 1, 0, 1, 0.8, 0.4),              # degenerate: one position, budget 1
+]
+
+
+@pytest.mark.parametrize("B,N,V,sigma,rule,step,max_steps,T0,T1", CASES)
+def test_sample_update_bit_exact(B, N, V, sigma, rule, step, max_steps, T0, T1):
+    print(f"sampler case B={B} N={N} V={V} sigma={sigma} rule={rule} step={step}", flush=True)
+    theta = 0.1 if rule == 1 else 0.9
+    params = synthetic.default_sampler_params(lock_rule=rule, lock_theta=theta, temp_start=T0,
+                                              temp_end=T1, max_steps=max_steps, seed=1234 + step)
+    logits = synthetic.make_logits((B, N, V), seed=V + B, sigma=sigma)
+    canvas = synthetic.make_tokens(V, (B, N), seed=5)
+    argmax = synthetic.make_tokens(V, (B, N), seed=6)
+    stop = np.zeros(B, dtype=np.int32)
+    g = gpu_update(params, step, logits, canvas, argmax, stop)
+    r = oracle_update(params, step, logits, canvas, argmax, stop)
+    assert_same(g, r, f"B={B} N={N} V={V}")
+
+
+def test_sampler_edge_rows_bit_exact():
+    """Rows that stress the arithmetic: ties for the max, a single finite
+    dominant entry with the rest far below (tiny chunk weights), all-equal
+    rows and huge logit values."""
+    B, N, V = 1, 8, 5000
+    L = np.zeros((B, N, V), dtype=np.float32)
+    L[0, 0, [7, 4000, 77]] = 3.0                  # ties: lowest index wins
+    L[0, 1] = -80.0
+    L[0, 1, 123] = 0.0                            # one entry dominates
+    L[0, 2] = 5.5                                 # all equal
+    L[0, 3] = np.linspace(-100, 100, V, dtype=np.float32)
+    L[0, 4] = 1e30
+    L[0, 4, 9] = 2e30
+    L[0, 5] = synthetic.make_logits((V,), seed=3, sigma=30.0)
+    L[0, 6] = -1e4
+    L[0, 6, ::97] = 0.0
+    L[0, 7] = synthetic.make_logits((V,), seed=4, sigma=0.01)
+    for rule in (0, 1):
+        params = synthetic.default_sampler_params(lock_rule=rule, max_steps=48, seed=9)
+        canvas = np.zeros((B, N), dtype=np.int32)
+        argmax = np.zeros((B, N), dtype=np.int32)
+        stop = np.zeros(B, dtype=np.int32)
+        g = gpu_update(params, 3, L, canvas, argmax, stop)
+        r = oracle_update(params, 3, L, canvas, argmax, stop)
+        assert_same(g, r, f"edge rows rule={rule}")
+
+
+def test_stop_sequence_and_untouched_stopped_canvas():
+    B, N, V = 2, 256, 1024
+    tok = synthetic.make_tokens(V, (B, N), seed=8)
+    logits = np.full((B, N, V), -60.0, dtype=np.float32)
+    np.put_along_axis(logits, tok[..., None].astype(np.int64), 40.0, axis=2)
+    params = synthetic.default_sampler_params(require_stable=1)
+    canvas = synthetic.make_tokens(V, (B, N), seed=9)
+    argmax = np.zeros((B, N), dtype=np.int32)
+    stop = np.array([0, 1], dtype=np.int32)          # canvas 1 already stopped
+    gs = (canvas, argmax, None, None, stop)
+    rs = gs
+    for t in range(2):
+        gs = gpu_update(params, t, logits, gs[0], gs[1], gs[4])
+        rs = oracle_update(params, t, logits, rs[0], rs[1], rs[4])
+        assert_same(gs, rs, f"step {t}")
+    assert gs[4].tolist() == [1, 1]
+    assert (gs[0][1] == canvas[1]).all() and (gs[1][1] == 0).all()
+    assert (gs[0][0] == tok[0]).all()
+
+
+def test_canvas_init_bit_exact():
+    B, N, V = 3, 256, 262144
+    g = torch.zeros((B, N), dtype=torch.int32, device=DEV)
+    binding.canvas_init(77, 5, g, V)
+    torch.cuda.synchronize()
+    assert (g.cpu().numpy() == osampler.canvas_init(77, 5, B, N, V)).all()
+
+
+def test_sampler_is_deterministic():
+    params = synthetic.default_sampler_params(seed=3)
+    logits = synthetic.make_logits((2, 256, 4096), seed=1, sigma=1.0)
+    canvas = synthetic.make_tokens(4096, (2, 256), seed=2)
+    argmax = np.zeros((2, 256), dtype=np.int32)
+    stop = np.zeros(2, dtype=np.int32)
+    a = gpu_update(params, 4, logits, canvas, argmax, stop)
+    b = gpu_update(params, 4, logits, canvas, argmax, stop)
+    assert_same(a, b, "rerun")

@@ -1,0 +1,138 @@
+"""CPU checks of the HIP library: it loads, exports every symbol include/dg.h
+declares, and its host-side validation (no GPU work) behaves as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from discrete_text_diffusion_denoise_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libdg.so not built: run `python -m discrete_text_diffusion_denoise_amd.build`")
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = declared_symbols()
+    assert len(syms) >= 20
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in dg.h but not exported"
+    assert set(syms) == set(binding.EXPORTED), "binding and header disagree"
+
+
+def _cfg(**over):
+    c = dict(n_layers=1, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, n_experts=8, top_k=2,
+             d_ff=512, vocab=1024, canvas=256, dtype=binding.DG_F32, rope_on=1, rope_theta=1e4,
+             rms_eps=1e-6)
+    c.update(over)
+    return binding.Config(**c)
+
+
+def _create(L, cfg):
+    lw = (binding.LayerWeights * cfg.n_layers)()
+    for i in range(cfg.n_layers):
+        for f, _ in binding.LayerWeights._fields_:
+            setattr(lw[i], f, 0x1000)      # never dereferenced on the host
+    w = binding.Weights(0x1000, 0x1000, 0x1000, 0x1000, lw)
+    h = ctypes.c_void_p()
+    st = L.dg_model_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, 0),
+    ({"dtype": 7}, 3),
+    ({"d_model": 250}, 2),
+    ({"n_heads": 6, "n_kv_heads": 4}, 2),
+    ({"head_dim": 96}, 2),
+    ({"head_dim": 256}, 2),                       # fp32 supports 64 and 128
+    ({"head_dim": 256, "dtype": binding.DG_BF16}, 0),
+    ({"top_k": 9}, 2),
+    ({"n_experts": 300}, 2),
+    ({"d_ff": 100}, 2),
+    ({"vocab": 1001}, 2),
+    ({"canvas": 2048}, 2),
+])
+def test_model_create_validation(L, over, status):
+    st, h = _create(L, _cfg(**over))
+    assert st == status, L.dg_last_error().decode()
+    if st == 0:
+        L.dg_model_destroy(h)
+    else:
+        assert L.dg_last_error().decode() != ""
+
+
+def test_kv_and_workspace_sizes(L):
+    st, h = _create(L, _cfg(n_layers=3, dtype=binding.DG_BF16))
+    assert st == 0
+    n = ctypes.c_size_t()
+    assert L.dg_kv_bytes(h, 2, 1000, ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * 2 * 4 * 1000 * 64 * 2
+    assert L.dg_kv_bytes(h, 0, 1000, ctypes.byref(n)) == 1
+    assert L.dg_workspace_bytes(h, 1, ctypes.byref(n)) == 0 and n.value > 0
+    w1 = n.value
+    assert L.dg_workspace_bytes(h, 4, ctypes.byref(n)) == 0 and n.value >= w1
+    assert L.dg_generate_workspace_bytes(h, 1, ctypes.byref(n)) == 0
+    assert n.value > w1 + 2 * 256 * 1024 * 4
+    assert L.dg_sampler_workspace_bytes(2, 256, ctypes.byref(n)) == 0 and n.value >= 3 * 2048
+    L.dg_model_destroy(h)
+
+
+def test_kv_length_bookkeeping_and_capacity_errors(L):
+    st, h = _create(L, _cfg())
+    kv = ctypes.c_void_p()
+    assert L.dg_kv_create(h, 1, 300, ctypes.c_void_p(0x1000), ctypes.byref(kv)) == 0
+    n = ctypes.c_int32()
+    assert L.dg_kv_length(kv, ctypes.byref(n)) == 0 and n.value == 0
+    assert L.dg_kv_set_length(kv, 40) == 0
+    assert L.dg_kv_length(kv, ctypes.byref(n)) == 0 and n.value == 40
+    assert L.dg_kv_set_length(kv, 301) == 4
+    # 40 + 256 canvas <= 300 is fine, 45 + 256 is not: checked before any GPU work
+    assert L.dg_kv_set_length(kv, 45) == 0
+    ws = ctypes.c_void_p(0x1000)
+    st = L.dg_denoise_step(h, kv, 1, ws, None, None, ws, ws, 1 << 40, None)
+    assert st == 4 and "capacity" in L.dg_last_error().decode()
+    st = L.dg_encode_prompt(h, kv, 1, ws, 256, ws, 1 << 40, None)
+    assert st == 4
+    # batch must match the cache
+    st = L.dg_denoise_step(h, kv, 2, ws, None, None, ws, ws, 1 << 40, None)
+    assert st == 2
+    # prev logits without stats
+    assert L.dg_kv_set_length(kv, 0) == 0
+    st = L.dg_denoise_step(h, kv, 1, ws, ws, None, ws, ws, 1 << 40, None)
+    assert st == 1
+    # workspace too small
+    st = L.dg_denoise_step(h, kv, 1, ws, None, None, ws, ws, 16, None)
+    assert st == 4
+    L.dg_kv_destroy(kv)
+    L.dg_model_destroy(h)
+
+
+def test_sampler_argument_errors(L):
+    p = binding.SamplerParams(1, 0.1, 0.8, 0.4, 0.005, 1, 48, 0, 1)
+    P = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    assert L.dg_sample_update(ctypes.byref(p), 0, 1, 2048, 1024, P, P, P, P, P, P, P, big,
+                              None) == 2
+    assert L.dg_sample_update(ctypes.byref(p), 0, 1, 256, 600000, P, P, P, P, P, P, P, big,
+                              None) == 2
+    assert L.dg_sample_update(None, 0, 1, 256, 1024, P, P, P, P, P, P, P, big, None) == 1
+    bad = binding.SamplerParams(5, 0.1, 0.8, 0.4, 0.005, 1, 48, 0, 1)
+    assert L.dg_sample_update(ctypes.byref(bad), 0, 1, 256, 1024, P, P, P, P, P, P, P, big,
+                              None) == 1
+    assert L.dg_sample_update(ctypes.byref(p), 0, 1, 256, 1024, P, P, P, P, P, P, P, 8,
+                              None) == 4
+    assert L.dg_status_string(4) == b"capacity exceeded"
