@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the block text-diffusion denoising path on one MI355X.
+
+One benchmark step = one block of block-autoregressive generation through
+the whole hot path (dg_generate_block): canvas initialisation, up to 48
+rounds of [self-conditioning + embedding, the denoiser layer stack with
+bidirectional attention over the cached prompt, top-8-of-128 MoE, tied
+vocabulary head, sampler with lock / renoise / entropy stop], then the
+causal commit of the block into the KV cache.  The cache is rewound to the
+prompt after each block so every step does identical work.
+
+Prints one JSON line.  value = canvas tokens per second (finished block
+tokens / wall time); ms_per_step = one block.  With random-init weights the
+entropy stop never fires, so each block runs the full 48 rounds.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config layer|stack]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="layer", choices=["layer", "stack"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def device_weights(cfg, seed, torch):
+    """Random-init weights N(0, 0.02^2) drawn on the GPU (torch's generator),
+    rounded once to bf16; RMSNorm scales are ones."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    d, V = cfg["d_model"], cfg["vocab"]
+    Hq, Hkv, dh, E, F = (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["n_experts"],
+                         cfg["d_ff"])
+
+    def draw(*shape):
+        return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * 0.02).to(dt)
+
+    def ones():
+        return torch.ones(d, device="cuda", dtype=torch.float32)
+
+    W = {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": []}
+    for _ in range(cfg["n_layers"]):
+        W["layers"].append({"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
+                            "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
+                            "w_router": draw(E, d), "w_gate": draw(E, F, d),
+                            "w_up": draw(E, F, d), "w_down": draw(E, d, F)})
+    return W
+
+
+def kernel_work(name, cfg, B, P, sc_splits):
+    """Algorithmic (flops, bytes) of one launch of a timed kernel: every
+    weight read once, activations read/written once."""
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    N, V, d = cfg["canvas"], cfg["vocab"], cfg["d_model"]
+    Hq, Hkv, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    E, k, F = cfg["n_experts"], cfg["top_k"], cfg["d_ff"]
+    T = B * N
+    # expected number of experts that receive at least one of T*k assignments
+    hit = E * (1.0 - (1.0 - k / E) ** T)
+    if name == "head_gemm":
+        return 2.0 * T * V * d, V * d * es + T * d * es + T * V * 4.0
+    if name == "selfcond_gemm":
+        return 2.0 * T * d * V, T * V * 4.0 + d * V * es + sc_splits * T * d * 4.0
+    if name == "moe_gateup":
+        return 2.0 * T * k * 2 * F * d, hit * 2 * F * d * es + T * d * es + T * k * F * es
+    if name == "moe_down":
+        return 2.0 * T * k * F * d, hit * d * F * es + T * k * F * es + T * k * d * 4.0
+    if name == "attention":
+        L = P + N
+        return (4.0 * T * L * Hq * dh,
+                T * Hq * dh * es + B * L * Hkv * dh * 2 * es + T * Hq * dh * es)
+    if name == "sampler":
+        return 0.0, T * V * 4.0 + T * 16.0
+    raise KeyError(name)
+
+
+def roofline(name, ms, cfg, B, P, sc_splits):
+    flops, nbytes = kernel_work(name, cfg, B, P, sc_splits)
+    ai = flops / nbytes if nbytes else 0.0
+    s = ms * 1e-3
+    if flops and ai >= RIDGE:
+        ach = flops / s / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": name, "flop_per_launch": flops, "bytes_per_launch": nbytes,
+                "avg_launch_ms": round(ms, 5)}
+    ach = nbytes / s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name,
+            "flop_per_launch": flops, "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
+
+
+def cpu_baseline(cfg, W, prompt, canvas, params, torch):
+    """The CPU oracle (float64 numpy model + C sampler), timed on this host on
+    a bounded sample: one self-conditioned denoising step and one sampler
+    update over the full canvas, plus the commit encode; a block is 48 such
+    rounds + a commit, so tokens/s = B*N / (48 * (step + sampler) + commit)."""
+    import numpy as np
+    from oracle import model as om
+    from oracle import sampler as osampler
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    host = {"embed": W["embed"].float().cpu().numpy(), "w_sc": W["w_sc"].float().cpu().numpy(),
+            "final_norm": W["final_norm"].cpu().numpy().astype(np.float64), "layers": []}
+    for lw in W["layers"]:
+        host["layers"].append({k: v.float().cpu().numpy() for k, v in lw.items()})
+    B, N, V = canvas.shape[0], cfg["canvas"], cfg["vocab"]
+    P = prompt.shape[1]
+    cache = om.KVCache(cfg, B)
+    om.encode(prompt, host, cfg, cache)                 # prompt encode: not timed
+    rng = np.random.default_rng(0)
+    prev = (rng.standard_normal((B, N, V), dtype=np.float32) * 2.0)
+    t0 = time.perf_counter()
+    logits = om.denoise_step(canvas, host, cfg, cache, prev)
+    t1 = time.perf_counter()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    cv = canvas.astype(np.int32).copy()
+    am = np.zeros((B, N), np.int32)
+    stop = np.zeros(B, np.int32)
+    osampler.sample_update(params, 0, lg, cv, am, stop)
+    t2 = time.perf_counter()
+    om.encode(cv, host, cfg, cache)                     # commit of one block
+    t3 = time.perf_counter()
+    block_s = 48 * ((t1 - t0) + (t2 - t1)) + (t3 - t2)
+    return {"value": round(B * N / block_s, 4), "unit": "canvas tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one self-conditioned denoise step ({(t1 - t0):.2f} s, float64 numpy, "
+                       f"{threads} BLAS threads) + one sampler update over {B}x{N} rows of "
+                       f"{V} logits ({(t2 - t1):.2f} s, C, 1 thread) + one {N}-token commit "
+                       f"({(t3 - t2):.2f} s) at prompt {P}; block = 48 rounds + commit, "
+                       f"extrapolated"),
+            "step_s": round(t1 - t0, 3), "sampler_s": round(t2 - t1, 3),
+            "commit_s": round(t3 - t2, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the step would shard).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from discrete_text_diffusion_denoise_amd import binding, synthetic
+
+    shape = synthetic.SHAPES[args.config]
+    cfg = synthetic.model_config(args.config)
+    B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
+    torch.cuda.init()
+    W = device_weights(cfg, args.seed, torch)
+    m = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
+    m.encode_prompt(prompt)
+    params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1)
+    block = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+
+    for w in range(args.warmup):
+        m.generate_block(params, w, block)
+        m.set_kv_length(P)
+    torch.cuda.synchronize()
+
+    names = list(binding.TIMERS)
+    binding.timer_enable(names)
+    rounds = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        rounds += m.generate_block(params, args.warmup + s, block)
+        m.set_kv_length(P)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    kern = {}
+    for n in names:
+        ms, cnt = binding.timer_read(n)
+        kern[n] = {"total_ms": round(ms, 3), "launches": cnt,
+                   "avg_ms": round(ms / cnt, 5) if cnt else None}
+    binding.timer_enable([])
+
+    # denoise-step latency: one self-conditioned dg_denoise_step + dg_sample_update
+    logits = [torch.empty((B, N, V), dtype=torch.float32, device="cuda") for _ in range(2)]
+    stats = [torch.zeros((B, N, 4), dtype=torch.float32, device="cuda") for _ in range(2)]
+    canvas = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+    binding.canvas_init(params["seed"], 0, canvas, V)
+    argmax = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+    lock = torch.zeros((B, N), dtype=torch.uint8, device="cuda")
+    stop = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sws = binding.sampler_workspace(B, N)
+    m.denoise_step(canvas, logits[0])
+    binding.sample_update(params, 0, logits[0], canvas, argmax, lock, stats[0], stop, sws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 10
+    ev[0].record()
+    for j in range(1, reps + 1):
+        stop.zero_()
+        m.denoise_step(canvas, logits[j % 2], logits[(j - 1) % 2], stats[(j - 1) % 2])
+        binding.sample_update(params, j, logits[j % 2], canvas, argmax, lock, stats[j % 2], stop,
+                              sws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    step_ms = ev[0].elapsed_time(ev[1]) / reps
+
+    sc_tiles = -(-B * N // 256) * -(-cfg["d_model"] // 256)
+    sc_splits = max(1, min(64, 512 // max(sc_tiles, 1)))
+    sc_splits = -(-V // (-(-(-(-V // sc_splits)) // 64) * 64))
+    dominant = max((n for n in names if kern[n]["launches"]), key=lambda n: kern[n]["total_ms"])
+    roof = roofline(dominant, kern[dominant]["avg_ms"], cfg, B, P, sc_splits)
+    per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], cfg, B, P,
+                                                                  sc_splits).items()
+                                       if k in ("bound", "achieved", "unit", "frac")}
+                                      if kern[n]["launches"] else {}))
+                  for n in names}
+
+    value = B * N * args.steps / wall
+    out = {
+        "metric": "canvas tokens/s at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt tokens)",
+        "config": {"workload": (f"{args.config}: {cfg['n_layers']} denoiser layer(s) d{cfg['d_model']} "
+                                f"{cfg['n_heads']}q/{cfg['n_kv_heads']}kv x{cfg['head_dim']}, "
+                                f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}, "
+                                f"vocab {V}, prompt {P}, canvas {N}, batch {B}; one step = one "
+                                f"block (<=48 self-conditioned rounds + commit)"),
+                   "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
+                   "rounds_per_block": float(np.mean(rounds)) if rounds else None,
+                   "sampler": "cumulative-entropy lock 0.1, T 0.8->0.4, stop 0.005 + stable"},
+        "denoise_step_ms": round(step_ms, 4),
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        cpu_canvas = np.asarray(canvas.cpu().numpy(), dtype=np.int64)
+        out["cpu_baseline"] = cpu_baseline(cfg, W, prompt.cpu().numpy().astype(np.int64),
+                                           cpu_canvas, params, torch)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -85,7 +85,12 @@ _SIGS = {
     "dg_stage_attention": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "dg_stage_moe": (_I, [_P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_stage_head": (_I, [_P, _I, _P, _P, _P, _SZ, _P]),
+    "dg_timer_enable": (_I, [ctypes.c_uint32]),
+    "dg_timer_read": (_I, [_I, _P, _P]),
 }
+
+TIMERS = {"head_gemm": 0, "selfcond_gemm": 1, "moe_gateup": 2, "moe_down": 3, "attention": 4,
+          "sampler": 5}
 EXPORTED = tuple(_SIGS)
 
 
@@ -282,6 +287,22 @@ def sample_update(params: dict, step: int, logits, canvas, argmax, lock, stats, 
     _check(lib().dg_sample_update(ctypes.byref(sp), int(step), B, N, V, _ptr(logits),
                                   _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats), _ptr(stop),
                                   _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def timer_enable(names) -> None:
+    """Start the library's kernel timers for the given names (see TIMERS)."""
+    mask = 0
+    for n in names:
+        mask |= 1 << TIMERS[n]
+    _check(lib().dg_timer_enable(mask))
+
+
+def timer_read(name: str):
+    """(total ms, launches) recorded for a timer since timer_enable."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().dg_timer_read(TIMERS[name], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def canvas_init(seed: int, block_index: int, canvas, vocab: int, stream=None):

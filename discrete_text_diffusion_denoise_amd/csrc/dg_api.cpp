@@ -43,6 +43,41 @@ dg_status fail(dg_status s, const char* fmt, ...) {
         if (s_ != DG_OK) return s_;      \
     } while (0)
 
+// ---- kernel timers (dg_timer_enable / dg_timer_read)
+struct Timers {
+    uint32_t mask = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[DG_TIMER_COUNT];
+    void clear() {
+        for (auto& v : ev) {
+            for (auto& p : v) {
+                (void)hipEventDestroy(p.first);
+                (void)hipEventDestroy(p.second);
+            }
+            v.clear();
+        }
+    }
+};
+Timers g_timers;
+
+// Runs `launch` (returning hipError_t) between two events on `st` if timer
+// `id` is enabled.
+template <typename F>
+hipError_t timed(int id, hipStream_t st, F&& launch) {
+    if (!(g_timers.mask & (1u << id))) return launch();
+    hipEvent_t a, b;
+    hipError_t e = hipEventCreate(&a);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&b);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(a, st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, st);
+    g_timers.ev[id].push_back({a, b});
+    return e;
+}
+
 constexpr int kEncodeTokens = 4096;    // tokens per encode chunk (all sequences)
 constexpr int kAttnPartRows = 8192;    // split-KV partial rows budget
 constexpr int kMaxSplitsSC = 64;       // self-conditioning split-K limit
@@ -234,7 +269,7 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     const int max_splits = std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len);
-    DG_HIP(dg::attention<T>(a, st));
+    DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
     DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, st));
     return DG_OK;
 }
@@ -277,7 +312,10 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.act = s.act;
     a.y = s.y;
     a.h = h;
-    DG_HIP(dg::moe_forward<T>(a, st));
+    DG_HIP(dg::moe_route(a, st));
+    DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
+    DG_HIP(timed(DG_TIMER_MOE_DOWN, st, [&] { return dg::moe_down<T>(a, st); }));
+    DG_HIP(dg::moe_combine(a, st));
     return DG_OK;
 }
 
@@ -307,7 +345,8 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
     g.ldc = c.d_model;
     g.k_split = cdiv(cdiv(c.vocab, splits), 64) * 64;
     const int used = cdiv(c.vocab, g.k_split);
-    DG_TRY(gemm<T>(g, 1, dg::EPI_SPLITK, used, st));
+    DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
+                 [&] { return dg::gemm_tn<T>(g, 1, dg::EPI_SPLITK, used, st); }));
     DG_HIP(dg::splitk_reduce<T>(s.sc_part, (T*)s.sc_s, used, Tn, c.d_model, st));
     dg::GemmArgs p;
     p.M = Tn;
@@ -333,8 +372,19 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
                      hipStream_t st) {
     const dg_config& c = m->c;
     DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
-    DG_TRY(linear<T>(s.u, Tn, c.d_model, m->embed, c.vocab, logits, c.vocab, dg::EPI_STORE_F32,
-                     st));
+    dg::GemmArgs g;
+    g.M = Tn;
+    g.N = c.vocab;
+    g.K = c.d_model;
+    g.A = s.u;
+    g.lda = c.d_model;
+    g.B = m->embed;
+    g.ldb = c.d_model;
+    g.C = logits;
+    g.ldc = c.vocab;
+    g.k_split = c.d_model;
+    DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
+                 [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_STORE_F32, 1, st); }));
     return DG_OK;
 }
 
@@ -594,7 +644,7 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
     a.y = cv.take<int32_t>((size_t)batch * canvas);
     a.r = cv.take<int32_t>((size_t)batch * canvas);
     a.newmax = cv.take<int32_t>((size_t)batch * canvas);
-    DG_HIP(dg::sample_update(a, st));
+    DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
     return DG_OK;
 }
 
@@ -776,6 +826,27 @@ dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logit
     if (m->c.dtype == DG_BF16)
         return stage_head<bf16_t>(m, T, d_h, d_logits, s, as_stream(stream));
     return stage_head<float>(m, T, d_h, d_logits, s, as_stream(stream));
+}
+
+dg_status dg_timer_enable(uint32_t mask) {
+    g_timers.clear();
+    g_timers.mask = mask & ((1u << DG_TIMER_COUNT) - 1);
+    return DG_OK;
+}
+
+dg_status dg_timer_read(int32_t id, double* total_ms, int64_t* launches) {
+    if (id < 0 || id >= DG_TIMER_COUNT || !total_ms || !launches)
+        return fail(DG_ERR_ARG, "bad timer read");
+    double tot = 0.0;
+    for (auto& p : g_timers.ev[id]) {
+        DG_HIP(hipEventSynchronize(p.second));
+        float ms = 0.f;
+        DG_HIP(hipEventElapsedTime(&ms, p.first, p.second));
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int64_t)g_timers.ev[id].size();
+    return DG_OK;
 }
 
 }  // extern "C"

@@ -95,8 +95,13 @@ struct MoeArgs {
     float* y = nullptr;              // [T*k][d]
     float* h = nullptr;              // residual [T][d]
 };
+// routing, counts and the stable permutation
+hipError_t moe_route(const MoeArgs& a, hipStream_t st);
 template <typename T>
-hipError_t moe_forward(const MoeArgs& a, hipStream_t st);
+hipError_t moe_gateup(const MoeArgs& a, hipStream_t st);
+template <typename T>
+hipError_t moe_down(const MoeArgs& a, hipStream_t st);
+hipError_t moe_combine(const MoeArgs& a, hipStream_t st);
 
 // ------------------------------------------------------------------ sampler
 struct SampleArgs {

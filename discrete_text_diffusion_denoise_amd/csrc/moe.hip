@@ -251,19 +251,37 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 
 }  // namespace
 
-template <typename T>
-hipError_t moe_forward(const MoeArgs& a, hipStream_t st) {
+hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     hipLaunchKernelGGL(route_kernel, dim3(cdiv(a.T, 4)), dim3(256), 0, st, a);
     hipLaunchKernelGGL(count_kernel, dim3(a.E), dim3(256), 0, st, a);
     hipLaunchKernelGGL(place_kernel, dim3(a.E), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
     hipLaunchKernelGGL(gateup_kernel<T>, dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
     hipLaunchKernelGGL(down_kernel<T>, dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t moe_combine(const MoeArgs& a, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
     hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-template hipError_t moe_forward<bf16_t>(const MoeArgs&, hipStream_t);
-template hipError_t moe_forward<float>(const MoeArgs&, hipStream_t);
+template hipError_t moe_gateup<bf16_t>(const MoeArgs&, hipStream_t);
+template hipError_t moe_gateup<float>(const MoeArgs&, hipStream_t);
+template hipError_t moe_down<bf16_t>(const MoeArgs&, hipStream_t);
+template hipError_t moe_down<float>(const MoeArgs&, hipStream_t);
 
 }  // namespace dg

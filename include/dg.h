@@ -248,6 +248,26 @@ dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_
 dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,
                         size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- timers */
+/* Kernel timers: when enabled, the library records a pair of HIP events on
+ * the launch stream around every launch of the selected kernels, so a caller
+ * can measure each kernel's average duration inside its own timed region.
+ * Process-wide state; enable/read from one thread. */
+typedef enum {
+    DG_TIMER_HEAD_GEMM = 0,      /* logits = RMSNorm(h) E^T (the GEMM launch)        */
+    DG_TIMER_SELFCOND_GEMM = 1,  /* softmax(prev) E split-K product                 */
+    DG_TIMER_MOE_GATEUP = 2,     /* grouped SwiGLU gate/up expert GEMM               */
+    DG_TIMER_MOE_DOWN = 3,       /* grouped down-projection expert GEMM              */
+    DG_TIMER_ATTENTION = 4,      /* attention (+ split merge)                        */
+    DG_TIMER_SAMPLER = 5,        /* per-row sampler kernel + per-canvas kernel       */
+    DG_TIMER_COUNT = 6
+} dg_timer_id;
+/* Bit i of mask enables timer i; clears all recorded events.  0 disables. */
+dg_status dg_timer_enable(uint32_t mask);
+/* Waits for the recorded events of timer `id` and returns the summed
+ * duration (ms) and number of launches since the last dg_timer_enable. */
+dg_status dg_timer_read(int32_t id, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif
