@@ -80,7 +80,8 @@ def kernel_work(name, cfg, B, P, sc_splits):
     if name == "head_gemm":
         return 2.0 * T * V * d, V * d * es + T * d * es + T * V * 4.0
     if name == "selfcond_gemm":
-        return 2.0 * T * d * V, T * V * 4.0 + d * V * es + sc_splits * T * d * 4.0
+        # bf16 models read the softmax probabilities in bf16 (written by a pre-pass)
+        return 2.0 * T * d * V, T * V * es + d * V * es + sc_splits * T * d * 4.0
     if name == "moe_gateup":
         return 2.0 * T * k * 2 * F * d, hit * 2 * F * d * es + T * d * es + T * k * F * es
     if name == "moe_down":
@@ -227,8 +228,10 @@ def main():
     step_ms = ev[0].elapsed_time(ev[1]) / reps
 
     sc_tiles = -(-B * N // 256) * -(-cfg["d_model"] // 256)
-    sc_splits = max(1, min(64, 512 // max(sc_tiles, 1)))
-    sc_splits = -(-V // (-(-(-(-V // sc_splits)) // 64) * 64))
+    sc_splits = max(1, min(64, 256 // max(sc_tiles, 1)))
+    sc_splits = (sc_splits // 8) * 8 if sc_splits >= 8 else sc_splits
+    k_split = -(-(-(-V // sc_splits)) // 64) * 64
+    sc_splits = -(-V // k_split)
     dominant = max((n for n in names if kern[n]["launches"]), key=lambda n: kern[n]["total_ms"])
     roof = roofline(dominant, kern[dominant]["avg_ms"], cfg, B, P, sc_splits)
     per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], cfg, B, P,

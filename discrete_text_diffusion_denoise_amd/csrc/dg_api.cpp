@@ -142,6 +142,8 @@ struct Scratch {
     float* sc_part;
     void* sc_s;
     int32_t* tok;
+    float* gp;        // split-K partials of the small projections
+    void* probs;      // bf16 models: softmax(prev logits) in bf16 for self-conditioning
     float* u32;       // bf16 models: fp32 normalised activations for the router
     float* wr32;      // bf16 models: router weights widened to fp32
 };
@@ -151,10 +153,16 @@ int token_budget(const dg_model* m, int B) {
 }
 
 int sc_splits(const dg_model* m, int T) {
-    // enough workgroups for the chip on the [T x d] output tiles
+    // enough workgroups for the chip on the [T x d] output tiles; a multiple
+    // of 8 so the column tiles of one split can share an XCD
     const int tiles = cdiv(T, 256) * cdiv(m->c.d_model, 256);
-    return std::max(1, std::min(kMaxSplitsSC, 512 / std::max(tiles, 1)));
+    int s = std::max(1, std::min(kMaxSplitsSC, 256 / std::max(tiles, 1)));
+    return s >= 8 ? (s / 8) * 8 : s;
 }
+
+// Split-K partial budget of the small projections (floats): splits are chosen
+// so that splits * tiles stays below ~640 workgroups of 64 columns x 256 rows.
+constexpr size_t kSplitPartFloats = (size_t)640 * 64 * 256;
 
 bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     const dg_config& c = m->c;
@@ -181,6 +189,8 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.y = cv.take<float>(T * c.top_k * c.d_model);
     s.sc_part = cv.take<float>((size_t)sc_splits(m, (int)Tc) * Tc * c.d_model);
     s.sc_s = cv.take_bytes(Tc * c.d_model * es);
+    s.gp = cv.take<float>(kSplitPartFloats);
+    s.probs = c.dtype == DG_BF16 ? cv.take_bytes(Tc * c.vocab * 2) : nullptr;
     s.tok = cv.take<int32_t>(T);
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
@@ -213,10 +223,25 @@ dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_
     return DG_OK;
 }
 
-// y = x W^T helper: C fp32 [M][ldc] (+ column offset via C pointer)
+// The vocabulary-sized products use the LDS-tiled GEMM unless DG_WIDE_TILE
+// selects one of the streaming shapes (values 0-4, for tile sweeps).
+bool use_stream_wide() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("DG_WIDE_TILE");
+        v = (e && atoi(e) <= 4) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+// C (epi)= x W^T for x [M][K] (model dtype, or fp32 when T = float) and
+// W [N][K]: C fp32 [M][ldc].  bf16 uses the streaming GEMM, fp32 the LDS-tiled
+// one.  When the output has too few tiles to fill the chip, K is split and a
+// second pass sums the partials in a fixed order (deterministic).
 template <typename T>
 dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, long ldc, int epi,
-                 hipStream_t st) {
+                 Scratch& s, hipStream_t st, const void* E = nullptr,
+                 const int32_t* tokens = nullptr, int vocab = 0) {
     dg::GemmArgs g;
     g.M = M;
     g.N = N;
@@ -228,7 +253,35 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
     g.C = C;
     g.ldc = ldc;
     g.k_split = K;
-    return gemm<T>(g, 0, epi, 1, st);
+    g.E = E;
+    g.lde = N;
+    g.tokens = tokens;
+    g.vocab = vocab;
+    g.E_is_f32 = sizeof(T) == 4;
+    const bool bf = sizeof(T) == 2;
+    const int mt = bf ? cdiv(M, 16 * dg::stream_tm_for(M)) : cdiv(M, 64);
+    long tiles_wide = (long)cdiv(N, 256) * mt;
+    if (bf && tiles_wide >= 200) {
+        DG_HIP(dg::gemm_stream(g, epi, 4, 1, st));
+        return DG_OK;
+    }
+    const long tiles = (long)cdiv(N, 64) * mt;
+    int splits = (int)std::min<long>(std::max<long>(1, cdiv(320, (int)tiles)), std::max(1, K / 256));
+    while (splits > 1 && (size_t)splits * M * N > kSplitPartFloats) --splits;
+    if (splits <= 1) {
+        if (bf) DG_HIP(dg::gemm_stream(g, epi, 1, 1, st));
+        else DG_HIP(dg::gemm_tn<T>(g, 0, epi, 1, st));
+        return DG_OK;
+    }
+    dg::GemmArgs p = g;
+    p.C = s.gp;
+    p.ldc = N;
+    p.k_split = cdiv(cdiv(K, splits), 64) * 64;
+    const int used = cdiv(K, p.k_split);
+    if (bf) DG_HIP(dg::gemm_stream(p, dg::EPI_SPLITK, 1, used, st));
+    else DG_HIP(dg::gemm_tn<T>(p, 0, dg::EPI_SPLITK, used, st));
+    DG_HIP(dg::splitk_epilogue(g, s.gp, used, epi, st));
+    return DG_OK;
 }
 
 // ---- attention half-block: n new tokens per sequence at [pos0, pos0+n)
@@ -241,11 +294,11 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     const int d = c.d_model, dh = c.head_dim;
     const int qkvw = (c.n_heads + 2 * c.n_kv_heads) * dh;
     DG_HIP(dg::rmsnorm<T>(h, L.attn_norm, (T*)s.u, Tn, d, c.rms_eps, st));
-    DG_TRY(linear<T>(s.u, Tn, d, L.wq, c.n_heads * dh, s.qkv, qkvw, dg::EPI_STORE_F32, st));
+    DG_TRY(linear<T>(s.u, Tn, d, L.wq, c.n_heads * dh, s.qkv, qkvw, dg::EPI_STORE_F32, s, st));
     DG_TRY(linear<T>(s.u, Tn, d, L.wk, c.n_kv_heads * dh, s.qkv + c.n_heads * dh, qkvw,
-                     dg::EPI_STORE_F32, st));
+                     dg::EPI_STORE_F32, s, st));
     DG_TRY(linear<T>(s.u, Tn, d, L.wv, c.n_kv_heads * dh, s.qkv + (c.n_heads + c.n_kv_heads) * dh,
-                     qkvw, dg::EPI_STORE_F32, st));
+                     qkvw, dg::EPI_STORE_F32, s, st));
     void *kc, *vc;
     kv_layer(m, kv, layer, &kc, &vc);
     DG_HIP(dg::rope_kv<T>(s.qkv, (T*)s.q, (T*)kc, (T*)vc, B, n, pos0, kv->cap, c.n_heads,
@@ -270,7 +323,7 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len);
     DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
-    DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, st));
+    DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, s, st));
     return DG_OK;
 }
 
@@ -287,10 +340,10 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
         DG_HIP(dg::widen_bf16((const uint16_t*)L.w_router, s.wr32,
                               (long)c.n_experts * c.d_model, st));
         DG_TRY(linear<float>(s.u32, Tn, c.d_model, s.wr32, c.n_experts, s.z, c.n_experts,
-                             dg::EPI_STORE_F32, st));
+                             dg::EPI_STORE_F32, s, st));
     } else {
         DG_TRY(linear<T>(s.u, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
-                         dg::EPI_STORE_F32, st));
+                         dg::EPI_STORE_F32, s, st));
     }
     dg::MoeArgs a;
     a.T = Tn;
@@ -345,25 +398,26 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
     g.ldc = c.d_model;
     g.k_split = cdiv(cdiv(c.vocab, splits), 64) * 64;
     const int used = cdiv(c.vocab, g.k_split);
-    DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
-                 [&] { return dg::gemm_tn<T>(g, 1, dg::EPI_SPLITK, used, st); }));
+    if (sizeof(T) == 2) {
+        // probabilities once in bf16, then the streaming product over the
+        // vocabulary split into `used` k-ranges (column tiles of a range on
+        // one XCD)
+        DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, st));
+        g.A = s.probs;
+        g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
+        if (use_stream_wide())
+            DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
+                         [&] { return dg::gemm_stream(g, dg::EPI_SPLITK, 4, used, st); }));
+        else
+            DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
+                         [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_SPLITK, used, st); }));
+    } else {
+        DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
+                     [&] { return dg::gemm_tn<T>(g, 1, dg::EPI_SPLITK, used, st); }));
+    }
     DG_HIP(dg::splitk_reduce<T>(s.sc_part, (T*)s.sc_s, used, Tn, c.d_model, st));
-    dg::GemmArgs p;
-    p.M = Tn;
-    p.N = c.d_model;
-    p.K = c.d_model;
-    p.A = s.sc_s;
-    p.lda = c.d_model;
-    p.B = m->w_sc;
-    p.ldb = c.d_model;
-    p.C = h;
-    p.ldc = c.d_model;
-    p.k_split = c.d_model;
-    p.E = m->embed;
-    p.lde = c.d_model;
-    p.vocab = c.vocab;
-    p.tokens = canvas;
-    DG_TRY(gemm<T>(p, 0, dg::EPI_EMBED_ADD, 1, st));
+    DG_TRY(linear<T>(s.sc_s, Tn, c.d_model, m->w_sc, c.d_model, h, c.d_model, dg::EPI_EMBED_ADD, s,
+                     st, m->embed, canvas, c.vocab));
     return DG_OK;
 }
 
@@ -383,8 +437,12 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.C = logits;
     g.ldc = c.vocab;
     g.k_split = c.d_model;
-    DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
-                 [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_STORE_F32, 1, st); }));
+    if (sizeof(T) == 2 && use_stream_wide())
+        DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
+                     [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));
+    else
+        DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
+                     [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_STORE_F32, 1, st); }));
     return DG_OK;
 }
 

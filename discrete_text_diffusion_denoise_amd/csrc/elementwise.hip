@@ -64,6 +64,24 @@ __global__ __launch_bounds__(256) void widen_kernel(const bf16_t* __restrict__ i
     if (i < n) out[i] = bf2f(in[i]);
 }
 
+// p = exp(l - max) / sum, written as bf16; blockIdx.y = row, blockIdx.x = a
+// 4096-entry segment of it (enough workgroups to keep HBM busy).
+__global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ stats,
+                                                           bf16_t* __restrict__ out, int V) {
+    const long row = blockIdx.y;
+    const float m = stats[row * 4 + 0];
+    const float inv = 1.0f / stats[row * 4 + 1];
+    const float4* L = reinterpret_cast<const float4*>(logits + row * V);
+    uint2* O = reinterpret_cast<uint2*>(out + row * V);
+    const int end = min(V / 4, (int)(blockIdx.x + 1) * 1024);
+    for (int i = blockIdx.x * 1024 + threadIdx.x; i < end; i += 256) {
+        const float4 x = L[i];
+        O[i] = make_uint2(pack_bf2(__expf(x.x - m) * inv, __expf(x.y - m) * inv),
+                          pack_bf2(__expf(x.z - m) * inv, __expf(x.w - m) * inv));
+    }
+}
+
 // 64x64 tiles through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in,
@@ -149,6 +167,14 @@ hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int co
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)cdiv((int)total, 256)), dim3(256),
                        0, st, part, out, splits, total);
+    return hipGetLastError();
+}
+
+hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
+                             int V, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(softmax_rows_kernel, dim3(cdiv(V / 4, 1024), rows), dim3(256), 0, st, logits,
+                       stats, out, V);
     return hipGetLastError();
 }
 

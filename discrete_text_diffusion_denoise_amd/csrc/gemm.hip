@@ -12,6 +12,8 @@
 // (64 bf16 or 32 fp32), staging both operands in LDS with double buffering.
 // Waves are arranged WM x WN; each wave owns (BM/WM) x (BN/WN) as 16x16
 // MFMA tiles.  fp32 models use the same code with the 16x16x4 fp32 MFMA.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -96,9 +98,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tn_kernel(GemmArgs g) {
     const int wm = wave / WN, wn = wave % WN;
     const int r16 = lane & 15, g4 = lane >> 4;
 
-    const int n0 = blockIdx.x * BN;
+    // With xcd_group, the column tiles of one k-split are placed on one XCD
+    // (workgroups are dealt to the 8 XCDs round-robin) so they share its L2.
+    int nt = blockIdx.x, kz = blockIdx.z;
+    if (g.xcd_group) {
+        const int nx = gridDim.x;
+        const int lin = blockIdx.x + nx * blockIdx.z;
+        nt = (lin >> 3) % nx;
+        kz = ((lin >> 3) / nx) * 8 + (lin & 7);
+    }
+    const int n0 = nt * BN;
     const int m0 = blockIdx.y * BM;
-    const int kbeg = blockIdx.z * g.k_split;
+    const int kbeg = kz * g.k_split;
     const int kend = min(g.K, kbeg + g.k_split);
     const int nslices = cdiv(kend - kbeg, ST::BK);
 
@@ -197,7 +208,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tn_kernel(GemmArgs g) {
                 } else if constexpr (EPI == EPI_ADD_F32) {
                     reinterpret_cast<float*>(g.C)[(long)row * g.ldc + col] += v;
                 } else if constexpr (EPI == EPI_SPLITK) {
-                    reinterpret_cast<float*>(g.C)[((long)blockIdx.z * g.M + row) * g.ldc + col] = v;
+                    reinterpret_cast<float*>(g.C)[((long)kz * g.M + row) * g.ldc + col] = v;
                 } else if constexpr (EPI == EPI_EMBED_ADD) {
                     const T* E = reinterpret_cast<const T*>(g.E);
                     const long tok = min(max(g.tokens[row], 0), g.vocab - 1);
@@ -226,12 +237,27 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
+int wide_choice() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("DG_WIDE_TILE");
+        v = e ? atoi(e) : 6;
+    }
+    return v;
+}
+
 template <typename T, int AMODE, int EPI>
 hipError_t launch_sized(const GemmArgs& g, int splits, hipStream_t st) {
     // Pick the largest tile that still gives the chip enough workgroups.
     long big = (long)cdiv(g.M, 256) * cdiv(g.N, 256) * splits;
     long med = (long)cdiv(g.M, 128) * cdiv(g.N, 128) * splits;
-    if (big >= 240) return launch_cfg<T, 256, 256, 2, 4, AMODE, EPI>(g, splits, st);
+    if (big >= 240) {
+        // 256 x 256: eight waves of 128 x 64 (measured faster than four waves of
+        // 128 x 128, which halve LDS reads but have half the loads in flight);
+        // DG_WIDE_TILE=5 selects the four-wave shape for sweeps
+        if (wide_choice() == 5) return launch_cfg<T, 256, 256, 2, 2, AMODE, EPI>(g, splits, st);
+        return launch_cfg<T, 256, 256, 2, 4, AMODE, EPI>(g, splits, st);
+    }
     if (med >= 200) return launch_cfg<T, 128, 128, 2, 2, AMODE, EPI>(g, splits, st);
     return launch_cfg<T, 64, 64, 2, 2, AMODE, EPI>(g, splits, st);
 }

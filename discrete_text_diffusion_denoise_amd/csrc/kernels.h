@@ -25,6 +25,8 @@ struct GemmArgs {
     long lde = 0;
     int vocab = 0;
     const int32_t* tokens = nullptr;  // EPI_EMBED_ADD: token per row
+    int E_is_f32 = 0;               // split-K epilogue: E element type
+    int xcd_group = 0;              // stream GEMM: put a k-split's column tiles on one XCD
 };
 
 // C (op)= A * B^T.  amode 1 reads A as softmax of fp32 logits (only with
@@ -32,7 +34,18 @@ struct GemmArgs {
 template <typename T>
 hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_t st);
 
+// Streaming bf16 GEMM (M <= 256 per row tile): all rows of a tile share the A
+// slice in LDS, each wave streams 16*tn columns of B (tn = 1 or 4).
+hipError_t gemm_stream(const GemmArgs& g, int epi, int tn, int splits, hipStream_t st);
+int stream_tm_for(int M);
+// C[m][n] (epi)= sum_z part[z][m][n]  (part is [splits][M][N])
+hipError_t splitk_epilogue(const GemmArgs& g, const float* part, int splits, int epi,
+                           hipStream_t st);
+
 // ------------------------------------------------------------------ elementwise
+// out[r][v] = exp(logits[r][v] - stats[r][0]) / stats[r][1] as bf16 (V % 4 == 0)
+hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
+                             int V, hipStream_t st);
 // u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T)
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,

@@ -110,131 +110,163 @@ __global__ __launch_bounds__(64) void place_kernel(MoeArgs a) {
     }
 }
 
-constexpr int MT = 4;     // 16-row token tiles per group (64 routed tokens)
-constexpr int KB = 128;   // K elements per lane-contiguous block (4 fragments of 8)
+// Grouped expert GEMMs, weight streaming.  A workgroup owns a block of weight
+// rows of one expert -- MODE 0: 32 rows of W_gate and the same 32 rows of
+// W_up (SwiGLU epilogue into act); MODE 1: 32 rows of W_down (fp32 out) --
+// and walks K in 64-wide stages.  Each stage's weight rows are read as full
+// 128-byte row segments (8 threads per row, coalesced), two stages ahead of
+// use through registers, and staged in LDS together with the stage's token
+// rows (gathered through the permutation for MODE 0).  Waves: column tile
+// ct = w & 1 (16 rows each), token tiles {w >> 1, (w >> 1) + 2} of the
+// 64-token group.  Token groups beyond 64 re-read the block's weights (L2).
+constexpr int XK = 64;             // k per stage
+constexpr int XROW = XK + 8;       // LDS row stride (elements)
+constexpr int XG = 64;             // tokens per group
 
-// act[slot][f] = silu(u W_gate^T)[f] * (u W_up^T)[f] for the tokens of expert
-// blockIdx.y, f in a 64-wide block.  Wave w owns 16 f-columns; lane (g4, r16)
-// streams 32 consecutive k of weight row f0 + r16 per block (the same 32 k of
-// each token row), so every weight byte is read once per token group.
-template <typename T>
-__global__ __launch_bounds__(256) void gateup_kernel(MoeArgs a) {
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
+    constexpr int RW = MODE == 0 ? 64 : 32;           // weight rows in LDS
+    constexpr int CE = 16 / (int)sizeof(T);           // elements per 16-byte chunk
+    constexpr int CPR = XK / CE;                      // chunks per row per stage
+    constexpr int WCH = RW * CPR / 256;               // weight chunks per thread
+    constexpr int XCH = XG * CPR / 256;               // token chunks per thread
+    __shared__ __align__(16) T Ws[2][RW * XROW];
+    __shared__ __align__(16) T Xs[2][XG * XROW];
+
     const int e = blockIdx.y;
     const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
     if (cnt == 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int f = blockIdx.x * 64 + wave * 16 + r16;
-    const bool fvalid = f < a.F;
-    const T* Wg = reinterpret_cast<const T*>(a.w_gate) + ((long)e * a.F + (fvalid ? f : 0)) * a.d;
-    const T* Wu = reinterpret_cast<const T*>(a.w_up) + ((long)e * a.F + (fvalid ? f : 0)) * a.d;
-    const T* U = reinterpret_cast<const T*>(a.u);
-    T* act = reinterpret_cast<T*>(a.act);
+    const int ct = wave & 1, mp = wave >> 1;
+    const int K = MODE == 0 ? a.d : a.F;
+    const int NOUT = MODE == 0 ? a.F : a.d;            // output columns of this expert
+    const int c0 = blockIdx.x * 32;                    // first output column of the block
+    const T* Wg = reinterpret_cast<const T*>(MODE == 0 ? a.w_gate : a.w_down);
+    const T* Wu = reinterpret_cast<const T*>(a.w_up);
+    const T* X = reinterpret_cast<const T*>(MODE == 0 ? a.u : a.act);
+    const int nst = cdiv(K, XK);
 
-    for (int mg = 0; mg < cnt; mg += 16 * MT) {
-        long tok[MT];
-        bool tv[MT];
+    // this thread's weight chunks: (row, k chunk) -> global row pointer
+    const T* wsrc[WCH];
+    int wrow[WCH], wkc[WCH];
+    bool wval[WCH];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int row = mg + 16 * mt + r16;
-            tv[mt] = row < cnt;
-            tok[mt] = tv[mt] ? a.perm_tok[off + row] : 0;
-        }
-        f32x4_t ag[MT], au[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            ag[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            au[mt] = ag[mt];
-        }
-        for (int k0 = 0; k0 < a.d; k0 += KB) {
-            Frag<T> bg[4], bu[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = k0 + g4 * 32 + s * 8;
-                if (fvalid && k < a.d) {
-                    load_frag(bg[s], Wg + k);
-                    load_frag(bu[s], Wu + k);
-                } else {
-                    zero_frag(bg[s]);
-                    zero_frag(bu[s]);
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (mg + 16 * mt >= cnt) break;   // uniform across the wave
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int k = k0 + g4 * 32 + s * 8;
-                    Frag<T> fa;
-                    if (tv[mt] && k < a.d) load_frag(fa, U + tok[mt] * a.d + k);
-                    else zero_frag(fa);
-                    mma(ag[mt], fa, bg[s]);
-                    mma(au[mt], fa, bu[s]);
-                }
-            }
-        }
-        if (!fvalid) continue;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = mg + 16 * mt + 4 * g4 + i;
-                if (row >= cnt) continue;
-                const float gv = ag[mt][i], uv = au[mt][i];
-                const float sv = gv / (1.0f + __expf(-gv));
-                act[(long)(off + row) * a.F + f] = Elt<T>::from_f(sv * uv);
-            }
+    for (int c = 0; c < WCH; ++c) {
+        const int ch = tid + c * 256;
+        wrow[c] = ch / CPR;
+        wkc[c] = (ch % CPR) * CE;
+        const int r = wrow[c] % 32;                     // row within the gate / up half
+        const int col = c0 + r;
+        wval[c] = col < NOUT;
+        const T* base = (MODE == 0 && wrow[c] >= 32) ? Wu : Wg;
+        wsrc[c] = base + ((long)e * NOUT + (wval[c] ? col : 0)) * K;
     }
-}
 
-// y[slot][c] = act[slot] . W_down[e][c] for a 64-wide block of output
-// columns c (fp32 out).
-template <typename T>
-__global__ __launch_bounds__(256) void down_kernel(MoeArgs a) {
-    const int e = blockIdx.y;
-    const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
-    if (cnt == 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const int c = blockIdx.x * 64 + wave * 16 + r16;
-    const bool cvalid = c < a.d;
-    const T* Wd = reinterpret_cast<const T*>(a.w_down) + ((long)e * a.d + (cvalid ? c : 0)) * a.F;
-    const T* act = reinterpret_cast<const T*>(a.act);
+    for (int mg = 0; mg < cnt; mg += XG) {
+        // this thread's token chunks for the group
+        const T* xsrc[XCH];
+        int xrow[XCH], xkc[XCH];
+        bool xval[XCH];
+#pragma unroll
+        for (int c = 0; c < XCH; ++c) {
+            const int ch = tid + c * 256;
+            xrow[c] = ch / CPR;
+            xkc[c] = (ch % CPR) * CE;
+            xval[c] = mg + xrow[c] < cnt;
+            long src = 0;
+            if (xval[c]) src = MODE == 0 ? (long)a.perm_tok[off + mg + xrow[c]] : (long)(off + mg + xrow[c]);
+            xsrc[c] = X + src * K;
+        }
+        f32x4_t ag[2], au[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            ag[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            au[q] = ag[q];
+        }
+        uint4 wA[WCH], xA[XCH], wB[WCH], xB[XCH];
 
-    for (int mg = 0; mg < cnt; mg += 16 * MT) {
-        f32x4_t acc[MT];
+#define DG_XLOAD(ST, WR, XR)                                                                  \
+        {                                                                                     \
+            const int kb_ = (ST) * XK;                                                        \
+            _Pragma("unroll") for (int c = 0; c < WCH; ++c) {                                 \
+                const int k_ = kb_ + wkc[c];                                                  \
+                WR[c] = (wval[c] && k_ < K) ? *reinterpret_cast<const uint4*>(wsrc[c] + k_)   \
+                                            : make_uint4(0, 0, 0, 0);                         \
+            }                                                                                 \
+            _Pragma("unroll") for (int c = 0; c < XCH; ++c) {                                 \
+                const int k_ = kb_ + xkc[c];                                                  \
+                XR[c] = (xval[c] && k_ < K) ? *reinterpret_cast<const uint4*>(xsrc[c] + k_)   \
+                                            : make_uint4(0, 0, 0, 0);                         \
+            }                                                                                 \
+        }
+#define DG_XSTORE(BUF, WR, XR)                                                                \
+        {                                                                                     \
+            _Pragma("unroll") for (int c = 0; c < WCH; ++c)                                   \
+                *reinterpret_cast<uint4*>(&Ws[BUF][wrow[c] * XROW + wkc[c]]) = WR[c];         \
+            _Pragma("unroll") for (int c = 0; c < XCH; ++c)                                   \
+                *reinterpret_cast<uint4*>(&Xs[BUF][xrow[c] * XROW + xkc[c]]) = XR[c];         \
+        }
+#define DG_XCOMPUTE(BUF)                                                                      \
+        _Pragma("unroll") for (int s_ = 0; s_ < XK / 32; ++s_) {                              \
+            Frag<T> fg, fu;                                                                   \
+            load_frag(fg, &Ws[BUF][(ct * 16 + r16) * XROW + s_ * 32 + g4 * 8]);               \
+            if (MODE == 0) load_frag(fu, &Ws[BUF][(32 + ct * 16 + r16) * XROW + s_ * 32 + g4 * 8]); \
+            _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                   \
+                const int mt = mp + 2 * q;                                                    \
+                if (mg + 16 * mt < cnt) {                                                     \
+                    Frag<T> fx;                                                               \
+                    load_frag(fx, &Xs[BUF][(16 * mt + r16) * XROW + s_ * 32 + g4 * 8]);       \
+                    mma(ag[q], fx, fg);                                                       \
+                    if (MODE == 0) mma(au[q], fx, fu);                                        \
+                }                                                                             \
+            }                                                                                 \
+        }
+
+        DG_XLOAD(0, wA, xA)
+        DG_XSTORE(0, wA, xA)
+        if (nst > 1) DG_XLOAD(1, wB, xB)
+        if (nst > 2) DG_XLOAD(2, wA, xA)
+        __syncthreads();
+        // stage st: LDS buffer st & 1; register set of stage st+1 is stored at
+        // the end of the iteration, stage st+2 is in flight in the other set
+        for (int st = 0; st < nst; st += 2) {
+            DG_XCOMPUTE(0)
+            if (st + 1 < nst) DG_XSTORE(1, wB, xB)
+            __syncthreads();
+            if (st + 3 < nst) DG_XLOAD(st + 3, wB, xB)
+            if (st + 1 >= nst) break;
+            DG_XCOMPUTE(1)
+            if (st + 2 < nst) DG_XSTORE(0, wA, xA)
+            __syncthreads();
+            if (st + 4 < nst) DG_XLOAD(st + 4, wA, xA)
+        }
+#undef DG_XLOAD
+#undef DG_XSTORE
+#undef DG_XCOMPUTE
+
+        // lane holds tokens 4*g4 + i of tile mt, output column c0 + ct*16 + r16
+        const int col = c0 + ct * 16 + r16;
+        if (col < NOUT) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < a.F; k0 += KB) {
-            Frag<T> bw[4];
+            for (int q = 0; q < 2; ++q) {
+                const int mt = mp + 2 * q;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = k0 + g4 * 32 + s * 8;
-                if (cvalid && k < a.F) load_frag(bw[s], Wd + k);
-                else zero_frag(bw[s]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (mg + 16 * mt >= cnt) break;
-                const int row = mg + 16 * mt + r16;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int k = k0 + g4 * 32 + s * 8;
-                    Frag<T> fa;
-                    if (row < cnt && k < a.F) load_frag(fa, act + (long)(off + row) * a.F + k);
-                    else zero_frag(fa);
-                    mma(acc[mt], fa, bw[s]);
+                for (int i = 0; i < 4; ++i) {
+                    const int row = mg + 16 * mt + 4 * g4 + i;
+                    if (row >= cnt) continue;
+                    if constexpr (MODE == 0) {
+                        const float gv = ag[q][i], uv = au[q][i];
+                        const float sv = gv / (1.0f + __expf(-gv));
+                        reinterpret_cast<T*>(a.act)[(long)(off + row) * a.F + col] =
+                            Elt<T>::from_f(sv * uv);
+                    } else {
+                        a.y[(long)(off + row) * a.d + col] = ag[q][i];
+                    }
                 }
             }
         }
-        if (!cvalid) continue;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = mg + 16 * mt + 4 * g4 + i;
-                if (row < cnt) a.y[(long)(off + row) * a.d + c] = acc[mt][i];
-            }
+        __syncthreads();   // LDS reuse by the next token group
     }
 }
 
@@ -262,14 +294,14 @@ hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gateup_kernel<T>, dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(down_kernel<T>, dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
