@@ -223,6 +223,12 @@ dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_
     return DG_OK;
 }
 
+// Integer environment knob (read once per name) for tile and schedule sweeps.
+int env_flag(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
 // The vocabulary-sized products use the LDS-tiled GEMM unless DG_WIDE_TILE
 // selects one of the streaming shapes (values 0-4, for tile sweeps).
 bool use_stream_wide() {
@@ -365,6 +371,7 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.act = s.act;
     a.y = s.y;
     a.h = h;
+    a.k_rotate = env_flag("DG_KROT", 1);
     DG_HIP(dg::moe_route(a, st));
     DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
     DG_HIP(timed(DG_TIMER_MOE_DOWN, st, [&] { return dg::moe_down<T>(a, st); }));
@@ -405,6 +412,7 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, st));
         g.A = s.probs;
         g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
+        g.k_rotate = env_flag("DG_KROT", 1);
         if (use_stream_wide())
             DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
                          [&] { return dg::gemm_stream(g, dg::EPI_SPLITK, 4, used, st); }));
@@ -437,6 +445,7 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.C = logits;
     g.ldc = c.vocab;
     g.k_split = c.d_model;
+    g.k_rotate = env_flag("DG_KROT", 1);
     if (sizeof(T) == 2 && use_stream_wide())
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
                      [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));

@@ -115,8 +115,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tn_kernel(GemmArgs g) {
 
     uint4 ra[A_CHUNKS], rb[B_CHUNKS];
 
+    // Workgroups start their K walk at different slices (rotation by tile),
+    // so concurrent workgroups read different offsets within their rows.
+    const int rot = g.k_rotate && nslices > 0 ? (int)((nt + (long)blockIdx.y * 7) % nslices) : 0;
     auto gload = [&](int s) {
-        const int kb = kbeg + s * ST::BK;
+        int sr = s + rot;
+        if (sr >= nslices) sr -= nslices;
+        const int kb = kbeg + sr * ST::BK;
 #pragma unroll
         for (int c = 0; c < A_CHUNKS; ++c) {
             int ch = tid + c * NT;

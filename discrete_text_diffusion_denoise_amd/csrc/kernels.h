@@ -26,7 +26,8 @@ struct GemmArgs {
     int vocab = 0;
     const int32_t* tokens = nullptr;  // EPI_EMBED_ADD: token per row
     int E_is_f32 = 0;               // split-K epilogue: E element type
-    int xcd_group = 0;              // stream GEMM: put a k-split's column tiles on one XCD
+    int xcd_group = 0;              // put a k-split's column tiles on one XCD
+    int k_rotate = 0;               // rotate each tile's starting k-slice
 };
 
 // C (op)= A * B^T.  amode 1 reads A as softmax of fp32 logits (only with
@@ -107,6 +108,7 @@ struct MoeArgs {
     void* act = nullptr;             // [T*k][F] (T)
     float* y = nullptr;              // [T*k][d]
     float* h = nullptr;              // residual [T][d]
+    int k_rotate = 0;                // rotate each block's starting k-stage
 };
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);

@@ -146,6 +146,9 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
     const T* Wu = reinterpret_cast<const T*>(a.w_up);
     const T* X = reinterpret_cast<const T*>(MODE == 0 ? a.u : a.act);
     const int nst = cdiv(K, XK);
+    // blocks start their K walk at different stages so concurrent blocks read
+    // different offsets within their weight rows
+    const int rot = a.k_rotate ? (int)((blockIdx.x + (long)blockIdx.y * 5) % nst) : 0;
 
     // this thread's weight chunks: (row, k chunk) -> global row pointer
     const T* wsrc[WCH];
@@ -188,7 +191,9 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
 
 #define DG_XLOAD(ST, WR, XR)                                                                  \
         {                                                                                     \
-            const int kb_ = (ST) * XK;                                                        \
+            int sr_ = (ST) + rot;                                                             \
+            if (sr_ >= nst) sr_ -= nst;                                                       \
+            const int kb_ = sr_ * XK;                                                         \
             _Pragma("unroll") for (int c = 0; c < WCH; ++c) {                                 \
                 const int k_ = kb_ + wkc[c];                                                  \
                 WR[c] = (wval[c] && k_ < K) ? *reinterpret_cast<const uint4*>(wsrc[c] + k_)   \
