@@ -230,7 +230,7 @@ def main():
     sc_tiles = -(-B * N // 256) * -(-cfg["d_model"] // 256)
     sc_splits = max(1, min(64, 256 // max(sc_tiles, 1)))
     sc_splits = (sc_splits // 8) * 8 if sc_splits >= 8 else sc_splits
-    k_split = -(-(-(-V // sc_splits)) // 64) * 64
+    k_split = -(-(-(-V // sc_splits)) // 128) * 128
     sc_splits = -(-V // k_split)
     dominant = max((n for n in names if kern[n]["launches"]), key=lambda n: kern[n]["total_ms"])
     roof = roofline(dominant, kern[dominant]["avg_ms"], cfg, B, P, sc_splits)

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libdg.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "gemm_stream.hip", "attention.hip", "moe.hip", "elementwise.hip", "sampler.hip",
+SOURCES = ["gemm.hip", "gemm_dma.hip", "gemm_stream.hip", "attention.hip", "moe.hip", "elementwise.hip", "sampler.hip",
            "dg_api.cpp"]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -403,7 +403,9 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
     g.ldb = c.vocab;
     g.C = s.sc_part;
     g.ldc = c.d_model;
-    g.k_split = cdiv(cdiv(c.vocab, splits), 64) * 64;
+    // k-ranges in whole 128-element steps (the bf16 ring kernel walks four
+    // 32-element stages at a time)
+    g.k_split = cdiv(cdiv(c.vocab, splits), 128) * 128;
     const int used = cdiv(c.vocab, g.k_split);
     if (sizeof(T) == 2) {
         // probabilities once in bf16, then the streaming product over the

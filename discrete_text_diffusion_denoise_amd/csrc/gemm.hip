@@ -256,6 +256,11 @@ hipError_t launch_sized(const GemmArgs& g, int splits, hipStream_t st) {
     // Pick the largest tile that still gives the chip enough workgroups.
     long big = (long)cdiv(g.M, 256) * cdiv(g.N, 256) * splits;
     long med = (long)cdiv(g.M, 128) * cdiv(g.N, 128) * splits;
+    // bf16 products with enough 256 x 256 tiles for every CU: the
+    // direct-to-LDS ring kernel
+    if constexpr (sizeof(T) == 2 && AMODE == 0 && (EPI == EPI_STORE_F32 || EPI == EPI_SPLITK)) {
+        if (big >= 128 && gemm_dma_ok(g, EPI)) return gemm_dma_bf16(g, EPI, splits, st);
+    }
     if (big >= 240) {
         // 256 x 256: eight waves of 128 x 64 (measured faster than four waves of
         // 128 x 128, which halve LDS reads but have half the loads in flight);

@@ -1,0 +1,234 @@
+// The two vocabulary-sized bf16 GEMMs of the denoising step on gfx950:
+//
+//   logits[T, V]        = norm(h)[T, d] * E[V, d]^T        (tied head)
+//   part_z[T, d]        = softmax(L_prev)[T, Vz] * E^T[d, Vz]^T   (self-
+//                          conditioning, one vocabulary range Vz per k-split)
+//
+// (report-summary page, sections 2 and 5: the denoiser reuses the
+// autoregressive model's tied embedding; self-conditioning feeds the previous
+// step's distribution back through it.)  Both stream a 1 GiB weight once per
+// call while the other operand (256 canvas rows) stays in L2, so the kernel
+// is built around keeping many bytes of the streamed operand in flight:
+//
+//   * a 256 x 256 output tile per workgroup, eight waves of 128 x 64;
+//   * K walked in 32-element stages (64 bytes per row) that go straight from
+//     global memory into LDS with global_load_lds (no register staging);
+//   * a ring of four stages in four separately declared LDS buffers, three of
+//     them in flight while the fourth is multiplied; each wave waits only for
+//     its own oldest loads (vmcnt) and the barrier orders the LDS reads;
+//   * an XOR swizzle of the 16-byte chunks inside every 64-byte row so that
+//     the fragment reads (16 rows x one chunk per lane group) hit distinct
+//     banks, chosen by which global chunk each lane fetches.
+//
+// Rows past M or N are clamped to the last valid row (their results are
+// never stored), so every load stays inside the operands.
+#include <cstdlib>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 32;                 // bf16 per row per stage (64 bytes)
+constexpr int WAVES = 8;               // arranged 2 (rows) x 4 (columns)
+constexpr int STAGE_BYTES = BM * BK * 2;   // one operand's stage: 16 KiB
+
+// chunk slot of (row r, chunk c) within its 64-byte LDS row
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// vmcnt(n): wait until at most n vector-memory operations of this wave are
+// outstanding; lgkm and exp counters are left alone.
+#define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+
+// Barrier that only waits for this wave's LDS traffic: the direct-to-LDS
+// loads of later stages stay in flight across it.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+}
+
+template <int EPI>
+__global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
+    __shared__ __align__(1024) unsigned char a0[STAGE_BYTES], b0[STAGE_BYTES];
+    __shared__ __align__(1024) unsigned char a1[STAGE_BYTES], b1[STAGE_BYTES];
+    __shared__ __align__(1024) unsigned char a2[STAGE_BYTES], b2[STAGE_BYTES];
+    __shared__ __align__(1024) unsigned char a3[STAGE_BYTES], b3[STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    int nt = blockIdx.x, kz = blockIdx.z;
+    if (g.xcd_group) {
+        // the column tiles of one k-split land on one XCD and share its L2
+        const int nx = gridDim.x;
+        const int lin = blockIdx.x + nx * blockIdx.z;
+        nt = (lin >> 3) % nx;
+        kz = ((lin >> 3) / nx) * 8 + (lin & 7);
+    }
+    const int n0 = nt * BN;
+    const int m0 = blockIdx.y * BM;
+    const int kbeg = kz * g.k_split;
+    const int kend = min(g.K, kbeg + g.k_split);
+    // n and rot are the same in every lane; saying so keeps the stage
+    // branches scalar
+    const int n = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg) / BK : 0);
+    const int rot = __builtin_amdgcn_readfirstlane(g.k_rotate && n > 0 ? (int)((nt + blockIdx.y * 7) % n) : 0);
+
+    // This wave fills blocks 2*wave and 2*wave+1 of both operands; lane p
+    // writes LDS slot p of a block: row p/4, slot p%4, which holds chunk
+    // (p%4) ^ swz(row).
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
+    const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
+    const int pr = lane >> 2;
+    const int pc = ((lane & 3) ^ swz(pr)) * 8;
+    const long ar0 = min(m0 + 32 * wave + pr, g.M - 1), ar1 = min(m0 + 32 * wave + 16 + pr, g.M - 1);
+    const long br0 = min(n0 + 32 * wave + pr, g.N - 1), br1 = min(n0 + 32 * wave + 16 + pr, g.N - 1);
+    const bf16_t* pa0 = A + ar0 * g.lda + kbeg + pc;
+    const bf16_t* pa1 = A + ar1 * g.lda + kbeg + pc;
+    const bf16_t* pb0 = B + br0 * g.ldb + kbeg + pc;
+    const bf16_t* pb1 = B + br1 * g.ldb + kbeg + pc;
+    const int blk0 = 2 * wave * 1024;
+
+#define DG_ISSUE(s, SA, SB)                                                                       \
+    {                                                                                             \
+        int sr_ = (s) + rot;                                                                      \
+        if (sr_ >= n) sr_ -= n;                                                                   \
+        const int ko_ = sr_ * BK;                                                                 \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pa0 + ko_), (lds_void*)((SA) + blk0), 16, 0, 0);        \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pb0 + ko_), (lds_void*)((SB) + blk0), 16, 0, 0);        \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pa1 + ko_), (lds_void*)((SA) + blk0 + 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pb1 + ko_), (lds_void*)((SB) + blk0 + 1024), 16, 0, 0); \
+    }
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int roff = r16 * 64 + ((g4 ^ swz(r16)) << 4);
+    // The twelve fragment reads of a stage are one asm block that ends with
+    // its own lgkmcnt(0): written as ordinary loads, the compiler cannot
+    // tell at the top of the loop which ring buffer a pending direct-to-LDS
+    // load targets and drains all of them (vmcnt(0)) once per pass.  The
+    // ring discipline above already orders every read after the loads it
+    // needs.  Operands enter the MFMA swapped (B rows as the 16-row side), so
+    // a lane ends up holding four consecutive columns of one output row.
+#define DG_COMPUTE(SA, SB)                                                                        \
+    {                                                                                             \
+        u32x4 f0, f1, f2, f3, f4, f5, f6, f7, e0, e1, e2, e3;                                     \
+        const uint32_t qa_ = lds_addr(SA) + wm * 8192 + roff, qb_ = lds_addr(SB) + wn * 4096 + roff; \
+        asm volatile(                                                                             \
+            "ds_read_b128 %0, %12 offset:0\n ds_read_b128 %1, %12 offset:1024\n"                   \
+            "ds_read_b128 %2, %12 offset:2048\n ds_read_b128 %3, %12 offset:3072\n"                \
+            "ds_read_b128 %4, %12 offset:4096\n ds_read_b128 %5, %12 offset:5120\n"                \
+            "ds_read_b128 %6, %12 offset:6144\n ds_read_b128 %7, %12 offset:7168\n"                \
+            "ds_read_b128 %8, %13 offset:0\n ds_read_b128 %9, %13 offset:1024\n"                   \
+            "ds_read_b128 %10, %13 offset:2048\n ds_read_b128 %11, %13 offset:3072\n"              \
+            "s_waitcnt lgkmcnt(0)"                                                                 \
+            : "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(f4), "=&v"(f5), "=&v"(f6),         \
+              "=&v"(f7), "=&v"(e0), "=&v"(e1), "=&v"(e2), "=&v"(e3)                               \
+            : "v"(qa_), "v"(qb_)                                                                  \
+            : "memory");                                                                          \
+        const u32x4 fa_[8] = {f0, f1, f2, f3, f4, f5, f6, f7};                                    \
+        const u32x4 fb_[4] = {e0, e1, e2, e3};                                                    \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                             \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                         \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+                    __builtin_bit_cast(bf16x8_t, fb_[j]), __builtin_bit_cast(bf16x8_t, fa_[i]),   \
+                    acc[i][j], 0, 0, 0);                                                          \
+    }
+
+    // Stage t: wait for its loads (later stages may stay outstanding: four
+    // loads per wave per stage), let every wave pass the barrier, refill the
+    // buffer freed one stage earlier, multiply.
+#define DG_STAGE(t, CA, CB, NA, NB)          \
+    {                                        \
+        if ((t) + 2 < n)                     \
+            DG_WAIT_VM(8);                   \
+        else if ((t) + 1 < n)                \
+            DG_WAIT_VM(4);                   \
+        else                                 \
+            DG_WAIT_VM(0);                   \
+        barrier_lds();                       \
+        if ((t) + 3 < n) DG_ISSUE((t) + 3, NA, NB); \
+        DG_COMPUTE(CA, CB);                  \
+    }
+
+    if (n > 0) DG_ISSUE(0, a0, b0);
+    if (n > 1) DG_ISSUE(1, a1, b1);
+    if (n > 2) DG_ISSUE(2, a2, b2);
+    // n is a multiple of four (checked on the host), so every pass of the
+    // loop runs all four stages and the accumulators never leave the loop
+    // early
+    for (int t = 0; t < n; t += 4) {
+        DG_STAGE(t, a0, b0, a3, b3);
+        DG_STAGE(t + 1, a1, b1, a0, b0);
+        DG_STAGE(t + 2, a2, b2, a1, b1);
+        DG_STAGE(t + 3, a3, b3, a2, b2);
+    }
+#undef DG_STAGE
+#undef DG_COMPUTE
+#undef DG_ISSUE
+
+    // epilogue: lane holds row r16, columns 4*g4 .. 4*g4+3 of each 16x16 tile
+    float* C = reinterpret_cast<float*>(g.C) + (EPI == EPI_SPLITK ? (long)kz * g.M * g.ldc : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = m0 + wm * 128 + 16 * i + r16;
+        if (row >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 64 + 16 * j + 4 * g4;
+            if (col < g.N) *reinterpret_cast<f32x4_t*>(C + (long)row * g.ldc + col) = acc[i][j];
+        }
+    }
+}
+
+}  // namespace
+
+bool gemm_dma_ok(const GemmArgs& g, int epi) {
+    static int enabled = -1;
+    if (enabled < 0) {
+        const char* e = getenv("DG_DMA");
+        enabled = e ? atoi(e) : 1;
+    }
+    if (!enabled) return false;
+    if (epi != EPI_STORE_F32 && epi != EPI_SPLITK) return false;
+    if (g.a_rows || g.M <= 0 || g.N <= 0) return false;
+    // whole rings of four stages in every k-range
+    if (g.K % (4 * BK) || g.k_split % (4 * BK)) return false;
+    if (g.lda % 8 || g.ldb % 8) return false;
+    // four-column stores of the output
+    if (g.N % 4 || g.ldc % 4 || ((uintptr_t)g.C & 15)) return false;
+    if (((uintptr_t)g.A | (uintptr_t)g.B) & 15) return false;
+    return true;
+}
+
+hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st) {
+    if (!gemm_dma_ok(g, epi)) return hipErrorInvalidValue;
+    dim3 grid(cdiv(g.N, BN), cdiv(g.M, BM), splits);
+    if (epi == EPI_STORE_F32)
+        hipLaunchKernelGGL(gemm_dma_kernel<EPI_STORE_F32>, grid, dim3(WAVES * 64), 0, st, g);
+    else
+        hipLaunchKernelGGL(gemm_dma_kernel<EPI_SPLITK>, grid, dim3(WAVES * 64), 0, st, g);
+    return hipGetLastError();
+}
+
+}  // namespace dg

@@ -35,6 +35,13 @@ struct GemmArgs {
 template <typename T>
 hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_t st);
 
+// bf16 C (STORE_F32 or SPLITK) = A * B^T with direct-to-LDS loads and a
+// four-stage ring (256 x 256 tiles).  gemm_dma_ok says whether the operands
+// meet its conditions: K and k_split multiples of 128, 16-byte aligned rows,
+// no row gather.
+bool gemm_dma_ok(const GemmArgs& g, int epi);
+hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st);
+
 // Streaming bf16 GEMM (M <= 256 per row tile): all rows of a tile share the A
 // slice in LDS, each wave streams 16*tn columns of B (tn = 1 or 4).
 hipError_t gemm_stream(const GemmArgs& g, int epi, int tn, int splits, hipStream_t st);

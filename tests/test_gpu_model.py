@@ -25,7 +25,16 @@ SMALL_BF16 = dict(n_layers=2, d_model=512, n_heads=8, n_kv_heads=2, head_dim=64,
 F32_GQA = dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128, n_experts=8,
                top_k=2, d_ff=96, vocab=2048, canvas=100, dtype="f32")
 
-MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA}
+# bf16 with enough 256 x 256 tiles in the two vocabulary products to take
+# the direct-to-LDS ring kernel; the ragged variant (canvas 200, vocabulary
+# not a multiple of 256 or 128) clamps rows in the head and falls back to the
+# double-buffered kernel for self-conditioning
+VOCAB_BF16 = dict(n_layers=1, d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, n_experts=16,
+                  top_k=2, d_ff=256, vocab=32768, canvas=256, dtype="bf16")
+VOCAB_RAGGED = dict(VOCAB_BF16, vocab=32768 + 96, canvas=200)
+
+MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
+          "vocab_ragged": VOCAB_RAGGED}
 
 
 def setup(name, prompt_len, batch=1, std=0.05, seed=0, capacity_extra=0, **over):
@@ -220,7 +229,7 @@ def test_stage_moe(name, T):
     assert normwise(hd.cpu().numpy()[ok], ref[ok]) <= tol_for(cfg)
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "vocab_bf16", "vocab_ragged"])
 def test_stage_head_and_input(name):
     cfg, W, m = setup(name, 0)
     N, V, d = cfg["canvas"], cfg["vocab"], cfg["d_model"]
