@@ -40,8 +40,9 @@ constexpr int NDEPTH = 16;
 constexpr int TILE = 4 * NLANE * NDEPTH;
 constexpr int SUPER = 64;
 
+// Computed for every x and selected at the end (no branch): the value for
+// x >= -87 is the same sequence of operations either way.
 __device__ __forceinline__ float dexp(float x) {
-    if (!(x >= -87.0f)) return 0.0f;
     const float LOG2E = 1.44269504088896341f;
     const float LN2_HI = 0.693145751953125f;
     const float LN2_LO = 1.42860682030941723e-06f;
@@ -56,7 +57,8 @@ __device__ __forceinline__ float dexp(float x) {
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     const int k = (int)kf;
-    return p * __uint_as_float((uint32_t)(k + 127) << 23);
+    const float v = p * __uint_as_float((uint32_t)(k + 127) << 23);
+    return x >= -87.0f ? v : 0.0f;
 }
 
 __device__ __forceinline__ float dlog(float x) {
@@ -182,8 +184,65 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
     const float invT = a.inv_t;
 
     Rec F = {-INFINITY, -1, 0.0f, 0.0f};
-    for (int t = 0; t < nt; ++t) {
+    // whole tiles first (every entry a member), then the ragged last tile
+    const int nfull = VEC ? a.V / TILE : 0;
+    for (int t = 0; t < nfull; ++t) {
         float x[4 * NDEPTH];
+        Rec rc;
+        float s2 = 0.0f;
+        const int k0 = 4 * (t * (NLANE * NDEPTH) + lam);
+#pragma unroll
+        for (int d = 0; d < NDEPTH; ++d) {
+            const float4 v = *reinterpret_cast<const float4*>(row + k0 + 4 * NLANE * d);
+            x[4 * d + 0] = v.x;
+            x[4 * d + 1] = v.y;
+            x[4 * d + 2] = v.z;
+            x[4 * d + 3] = v.w;
+        }
+        // chunk max and first argmax, in member order
+        float m = x[0];
+        int j = k0;
+#pragma unroll
+        for (int u = 1; u < 4 * NDEPTH; ++u) {
+            const int k = k0 + 4 * NLANE * (u / 4) + (u % 4);
+            const bool gt = x[u] > m;
+            m = gt ? x[u] : m;
+            j = gt ? k : j;
+        }
+        float sum = 0.0f, ac = 0.0f;
+        if (invT != 1.0f) {
+#pragma unroll
+            for (int u = 0; u < 4 * NDEPTH; ++u) {
+                const float z = x[u] - m;
+                const float e = dexp(z);
+                sum = sum + e;
+                const float ez = e * z;
+                ac = ac + ez;
+                s2 = s2 + dexp(z * invT);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4 * NDEPTH; ++u) {
+                const float z = x[u] - m;
+                const float e = dexp(z);
+                sum = sum + e;
+                const float ez = e * z;
+                ac = ac + ez;
+            }
+            s2 = sum;
+        }
+        rc.m = m;
+        rc.j = j;
+        rc.s = sum;
+        rc.a = ac;
+        Gs[t * NLANE + lam] = s2;
+        Ms[t * NLANE + lam] = rc.m;
+        F = (t == 0) ? rc : merge(F, rc);
+    }
+    for (int t = nfull; t < nt; ++t) {
+        float x[4 * NDEPTH];
+        Rec rc = {-INFINITY, -1, 0.0f, 0.0f};
+        float s2 = 0.0f;
         const long g0 = (long)t * (NLANE * NDEPTH) + lam;
 #pragma unroll
         for (int d = 0; d < NDEPTH; ++d) {
@@ -199,7 +258,6 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
                 for (int q = 0; q < 4; ++q) x[4 * d + q] = (k + q < a.V) ? row[k + q] : -INFINITY;
             }
         }
-        // chunk max and first argmax, in member order
         float m = -INFINITY;
         int j = -1;
 #pragma unroll
@@ -212,10 +270,8 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
                     j = (int)k;
                 }
             }
-        Rec rc = {-INFINITY, -1, 0.0f, 0.0f};
-        float s2 = 0.0f;
         if (j >= 0) {
-            float s = 0.0f, ac = 0.0f;
+            float sum = 0.0f, ac = 0.0f;
 #pragma unroll
             for (int d = 0; d < NDEPTH; ++d)
 #pragma unroll
@@ -224,34 +280,36 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
                     if (k < a.V) {
                         const float z = x[4 * d + q] - m;
                         const float e = dexp(z);
-                        s = s + e;
+                        sum = sum + e;
                         const float ez = e * z;
                         ac = ac + ez;
                         if (invT != 1.0f) s2 = s2 + dexp(z * invT);
                     }
                 }
-            if (invT == 1.0f) s2 = s;
+            if (invT == 1.0f) s2 = sum;
             rc.m = m;
             rc.j = j;
-            rc.s = s;
+            rc.s = sum;
             rc.a = ac;
         }
-        Gs[t * NLANE + lam] = s2;
-        Ms[t * NLANE + lam] = m;
+            Gs[t * NLANE + lam] = s2;
+        Ms[t * NLANE + lam] = rc.m;
         F = (t == 0) ? rc : merge(F, rc);
     }
-    // pairwise tree over lanes: within the wave, then over the 16 waves
+    // pairwise tree over lanes: within the wave, then over the 16 waves.
+    // merge is symmetric, so the butterfly leaves every lane of a pair with
+    // the record of the pair: level by level the same tree as merging
+    // adjacent pairs first.
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) F = merge(F, shfl_rec(F, o));
     if (lane == 0) wrec[wave] = F;
     __syncthreads();
     __shared__ Rec rowrec;
-    if (lam == 0) {
-        Rec lv[16];
-        for (int w = 0; w < 16; ++w) lv[w] = wrec[w];
-        for (int n = 16; n > 1; n >>= 1)
-            for (int w = 0; w < n / 2; ++w) lv[w] = merge(lv[2 * w], lv[2 * w + 1]);
-        rowrec = lv[0];
+    if (wave == 0) {
+        Rec W = wrec[lane & 15];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) W = merge(W, shfl_rec(W, o));
+        if (lane == 0) rowrec = W;
     }
     __syncthreads();
     const Rec R = rowrec;
@@ -293,17 +351,15 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
     }
     __syncthreads();
     if (lam == 0) {
-        // compact the members (entries past V are not members)
-        float w[4 * NDEPTH];
-        int ks[4 * NDEPTH];
+        // compact the members in place (entries past V are not members)
         int n = 0;
         for (int u = 0; u < 4 * NDEPTH; ++u)
             if (kk[u] >= 0) {
-                w[n] = wk[u];
-                ks[n] = kk[u];
+                wk[n] = wk[u];
+                kk[n] = kk[u];
                 ++n;
             }
-        const int yv = n > 0 ? ks[pick_seq(w, n, uniform01(words[3]))] : 0;
+        const int yv = n > 0 ? kk[pick_seq(wk, n, uniform01(words[3]))] : 0;
         float H = dlog(R.s) - R.a / R.s;
         H = H > 0.0f ? H : 0.0f;
         const float pmax = 1.0f / R.s;
