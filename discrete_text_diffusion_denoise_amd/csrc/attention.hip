@@ -43,6 +43,7 @@ __device__ __forceinline__ void load_vt(Frag<float>& f, const float* row, int g4
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+    if (a.halt && *a.halt) return;
     using L = AttnLds<T>;
     constexpr int KROW = DH + L::KPAD;
     constexpr int VROW = KT + L::VPAD;
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // Merge of split partials: one workgroup of DH threads per (token, head).
 template <typename T>
 __global__ void attn_merge_kernel(AttnArgs a) {
+    if (a.halt && *a.halt) return;
     const long th = blockIdx.x;            // token * Hq + head
     const int d = threadIdx.x;
     const long stride = (long)a.B * a.n * a.Hq;

@@ -111,6 +111,16 @@ struct dg_model {
     const void* w_sc;
     const float* final_norm;
     std::vector<dg_layer_weights> layers;
+    // block loop: pinned host copies of the stop flags of two rounds, and
+    // the events that say they have arrived (created on first use)
+    int32_t* hflags = nullptr;
+    int hflags_cap = 0;
+    hipEvent_t flag_ev[2] = {nullptr, nullptr};
+    ~dg_model() {
+        if (hflags) (void)hipHostFree(hflags);
+        for (hipEvent_t e : flag_ev)
+            if (e) (void)hipEventDestroy(e);
+    }
 };
 
 struct dg_kv {
@@ -146,6 +156,9 @@ struct Scratch {
     void* probs;      // bf16 models: softmax(prev logits) in bf16 for self-conditioning
     float* u32;       // bf16 models: fp32 normalised activations for the router
     float* wr32;      // bf16 models: router weights widened to fp32
+    // set by the block loop (not carved): when *halt != 0 every sequence of
+    // the batch has stopped and the heavy kernels of a round skip their work
+    const int32_t* halt = nullptr;
 };
 
 int token_budget(const dg_model* m, int B) {
@@ -325,6 +338,7 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     a.dh = dh;
     a.kv_len = pos0 + n;
     a.causal = causal;
+    a.halt = s.halt;
     const int max_splits = std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len);
@@ -372,6 +386,7 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.y = s.y;
     a.h = h;
     a.k_rotate = env_flag("DG_KROT", 1);
+    a.halt = s.halt;
     DG_HIP(dg::moe_route(a, st));
     DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
     DG_HIP(timed(DG_TIMER_MOE_DOWN, st, [&] { return dg::moe_down<T>(a, st); }));
@@ -411,10 +426,12 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         // probabilities once in bf16, then the streaming product over the
         // vocabulary split into `used` k-ranges (column tiles of a range on
         // one XCD)
-        DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, st));
+        DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, s.halt,
+                                     st));
         g.A = s.probs;
         g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
         g.k_rotate = env_flag("DG_KROT", 1);
+        g.halt = s.halt;
         if (use_stream_wide())
             DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
                          [&] { return dg::gemm_stream(g, dg::EPI_SPLITK, 4, used, st); }));
@@ -448,6 +465,7 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.ldc = c.vocab;
     g.k_split = c.d_model;
     g.k_rotate = env_flag("DG_KROT", 1);
+    g.halt = s.halt;
     if (sizeof(T) == 2 && use_stream_wide())
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
                      [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));
@@ -672,7 +690,8 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              int32_t canvas, int32_t vocab, const float* d_logits,
                              int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
                              float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
-                             hipStream_t st) {
+                             hipStream_t st, int32_t* nstop = nullptr,
+                             int32_t* halt = nullptr) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
@@ -713,6 +732,8 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
     a.y = cv.take<int32_t>((size_t)batch * canvas);
     a.r = cv.take<int32_t>((size_t)batch * canvas);
     a.newmax = cv.take<int32_t>((size_t)batch * canvas);
+    a.nstop = nstop;
+    a.halt = halt;
     DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
     return DG_OK;
 }
@@ -747,7 +768,7 @@ static void carve_generate(Carver& cv, const dg_model* m, int B, Scratch& s, flo
     *canvas = cv.take<int32_t>(Tc);
     *argmax = cv.take<int32_t>(Tc);
     *lock = cv.take<uint8_t>(Tc);
-    *stop = cv.take<int32_t>(B);
+    *stop = cv.take<int32_t>(B + 2);   // flags, then count of stopped and the halt flag
     dg_sampler_workspace_bytes(B, m->c.canvas, sws_bytes);
     *sws = cv.take_bytes(*sws_bytes);
 }
@@ -764,6 +785,19 @@ dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* 
     size_t sb;
     carve_generate(cv, m, batch, s, lg, stt, &cv_, &am, &lk, &sp, &sws, &sb);
     *bytes = cv.off + 256;
+    return DG_OK;
+}
+
+static dg_status ensure_host_flags(dg_model* m, int batch) {
+    if (!m->flag_ev[0]) {
+        for (hipEvent_t& e : m->flag_ev) DG_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    }
+    if (m->hflags_cap < batch) {
+        if (m->hflags) DG_HIP(hipHostFree(m->hflags));
+        m->hflags = nullptr;
+        DG_HIP(hipHostMalloc((void**)&m->hflags, 2 * (size_t)batch * sizeof(int32_t)));
+        m->hflags_cap = batch;
+    }
     return DG_OK;
 }
 
@@ -789,14 +823,34 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
                             ws_bytes, cv.off);
     hipStream_t st = as_stream(stream);
     const size_t Tc = (size_t)batch * c.canvas;
+    DG_TRY(ensure_host_flags(m, batch));
     DG_HIP(dg::canvas_init(p->seed, block_index, batch, c.canvas, c.vocab, canvas, st));
-    DG_HIP(hipMemsetAsync(argmax, 0, Tc * sizeof(int32_t), st));
-    DG_HIP(hipMemsetAsync(stop, 0, batch * sizeof(int32_t), st));
-    std::vector<int32_t> hstop(batch, 0);
+    DG_HIP(dg::fill_i32(argmax, 0, (long)Tc, st));
+    DG_HIP(dg::fill_i32(stop, 0, batch + 2, st));
+    int32_t* nstop = stop + batch;
+    int32_t* halt = stop + batch + 1;
+    s.halt = halt;
     for (int b = 0; b < batch; ++b) h_steps_out[b] = 0;
+    // The stop flags of round t are read on the host while round t+1 is
+    // already queued (one round of look-ahead hides the host round trip).
+    // Once every sequence has stopped the sampler raises `halt` on the
+    // device, so a look-ahead round after the last stop skips its heavy
+    // kernels and leaves canvas, argmax and locks untouched.
+    auto flags_of = [&](int t, bool* all) -> dg_status {   // round t's flags; all stopped?
+        DG_HIP(hipEventSynchronize(m->flag_ev[t & 1]));
+        const int32_t* hs = m->hflags + (size_t)(t & 1) * m->hflags_cap;
+        *all = true;
+        for (int b = 0; b < batch; ++b) {
+            if (h_steps_out[b] == 0 && hs[b]) h_steps_out[b] = t + 1;
+            *all = *all && hs[b];
+        }
+        return DG_OK;
+    };
     const float* prev = nullptr;
     const float* prev_stats = nullptr;
-    for (int t = 0; t < p->max_steps; ++t) {
+    int t = 0;
+    bool done = false;
+    for (; t < p->max_steps && !done; ++t) {
         float* logits = lg[t & 1];
         float* stats = stt[t & 1];
         if (c.dtype == DG_BF16)
@@ -804,20 +858,21 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
         else
             DG_TRY(denoise<float>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         DG_TRY(sample_impl(p, t, batch, c.canvas, c.vocab, logits, canvas, argmax, lock, stats,
-                           stop, sws, sws_bytes, st));
-        DG_HIP(hipMemcpyAsync(hstop.data(), stop, batch * sizeof(int32_t), hipMemcpyDeviceToHost,
-                              st));
-        DG_HIP(hipStreamSynchronize(st));
-        bool all = true;
-        for (int b = 0; b < batch; ++b) {
-            if (h_steps_out[b] == 0 && hstop[b]) h_steps_out[b] = t + 1;
-            all = all && hstop[b];
-        }
-        if (all) break;
+                           stop, sws, sws_bytes, st, nstop, halt));
+        DG_HIP(hipMemcpyAsync(m->hflags + (size_t)(t & 1) * m->hflags_cap, stop,
+                              batch * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+        DG_HIP(hipEventRecord(m->flag_ev[t & 1], st));
+        if (t > 0) DG_TRY(flags_of(t - 1, &done));
         if (p->selfcond_on) {
             prev = logits;
             prev_stats = stats;
         }
+    }
+    // the last round queued: its flags (a look-ahead round after the final
+    // stop changes nothing)
+    if (!done && t > 0) {
+        bool all;
+        DG_TRY(flags_of(t - 1, &all));
     }
     for (int b = 0; b < batch; ++b)
         if (h_steps_out[b] == 0) h_steps_out[b] = p->max_steps;

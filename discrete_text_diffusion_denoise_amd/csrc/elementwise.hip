@@ -66,9 +66,16 @@ __global__ __launch_bounds__(256) void widen_kernel(const bf16_t* __restrict__ i
 
 // p = exp(l - max) / sum, written as bf16; blockIdx.y = row, blockIdx.x = a
 // 4096-entry segment of it (enough workgroups to keep HBM busy).
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int32_t v, long n) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
 __global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ stats,
-                                                           bf16_t* __restrict__ out, int V) {
+                                                           bf16_t* __restrict__ out, int V,
+                                                           const int32_t* halt) {
+    if (halt && *halt) return;
     const long row = blockIdx.y;
     const float m = stats[row * 4 + 0];
     const float inv = 1.0f / stats[row * 4 + 1];
@@ -171,10 +178,16 @@ hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int co
 }
 
 hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, hipStream_t st) {
+                             int V, const int32_t* halt, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(softmax_rows_kernel, dim3(cdiv(V / 4, 1024), rows), dim3(256), 0, st, logits,
-                       stats, out, V);
+                       stats, out, V, halt);
+    return hipGetLastError();
+}
+
+hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, v, n);
     return hipGetLastError();
 }
 

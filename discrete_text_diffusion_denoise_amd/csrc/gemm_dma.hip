@@ -62,6 +62,7 @@ __device__ __forceinline__ void barrier_lds() {
 
 template <int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
+    if (g.halt && *g.halt) return;
     __shared__ __align__(1024) unsigned char a0[STAGE_BYTES], b0[STAGE_BYTES];
     __shared__ __align__(1024) unsigned char a1[STAGE_BYTES], b1[STAGE_BYTES];
     __shared__ __align__(1024) unsigned char a2[STAGE_BYTES], b2[STAGE_BYTES];

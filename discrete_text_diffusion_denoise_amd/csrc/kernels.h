@@ -28,6 +28,7 @@ struct GemmArgs {
     int E_is_f32 = 0;               // split-K epilogue: E element type
     int xcd_group = 0;              // put a k-split's column tiles on one XCD
     int k_rotate = 0;               // rotate each tile's starting k-slice
+    const int32_t* halt = nullptr;  // vocabulary GEMMs: skip all work when *halt != 0
 };
 
 // C (op)= A * B^T.  amode 1 reads A as softmax of fp32 logits (only with
@@ -52,8 +53,10 @@ hipError_t splitk_epilogue(const GemmArgs& g, const float* part, int splits, int
 
 // ------------------------------------------------------------------ elementwise
 // out[r][v] = exp(logits[r][v] - stats[r][0]) / stats[r][1] as bf16 (V % 4 == 0)
+hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t st);
+// halt: when non-null and *halt != 0 the kernel does nothing
 hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, hipStream_t st);
+                             int V, const int32_t* halt, hipStream_t st);
 // u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T)
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
@@ -91,6 +94,7 @@ struct AttnArgs {
     int causal = 0;            // query i (position pos0+i) sees keys <= pos0+i
     int splits = 1;
     int split_len = 0;         // keys per split (multiple of 32)
+    const int32_t* halt = nullptr;   // skip all work when *halt != 0
 };
 template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t st);
@@ -116,6 +120,7 @@ struct MoeArgs {
     float* y = nullptr;              // [T*k][d]
     float* h = nullptr;              // residual [T][d]
     int k_rotate = 0;                // rotate each block's starting k-stage
+    const int32_t* halt = nullptr;   // expert kernels: skip all work when *halt != 0
 };
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);
@@ -141,6 +146,8 @@ struct SampleArgs {
     int32_t* y = nullptr;            // scratch [B][N] drawn tokens
     int32_t* r = nullptr;            // scratch [B][N] renoise tokens
     int32_t* newmax = nullptr;       // scratch [B][N] argmax of this step
+    int32_t* nstop = nullptr;        // optional: count of stopped sequences
+    int32_t* halt = nullptr;         // optional: set to 1 once all B have stopped
 };
 hipError_t sample_update(const SampleArgs& a, hipStream_t st);
 hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,

@@ -125,6 +125,7 @@ constexpr int XG = 64;             // tokens per group
 
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
+    if (a.halt && *a.halt) return;
     constexpr int RW = MODE == 0 ? 64 : 32;           // weight rows in LDS
     constexpr int CE = 16 / (int)sizeof(T);           // elements per 16-byte chunk
     constexpr int CPR = XK / CE;                      // chunks per row per stage

@@ -446,6 +446,8 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
         int st = (meanH < a.tau) && (!a.require_stable || stable);
         if (a.step + 1 >= a.max_steps) st = 1;
         a.stop[b] = st;
+        // the last sequence to stop raises the halt flag
+        if (st && a.nstop && atomicAdd(a.nstop, 1) + 1 == a.B) *a.halt = 1;
     }
 }
 

@@ -270,16 +270,25 @@ def test_commit_equals_encode_of_concatenation():
     assert normwise(V1[..., :L, :].float().cpu().numpy(), V2[..., :L, :].float().cpu().numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("name,B,selfcond", [("tiny", 1, True), ("small_bf16", 2, True),
-                                             ("small_bf16", 2, False)])
-def test_generate_block_is_its_composition(name, B, selfcond):
+@pytest.mark.parametrize("name,B,selfcond,early", [("tiny", 1, True, False),
+                                                   ("small_bf16", 2, True, False),
+                                                   ("small_bf16", 2, False, False),
+                                                   ("small_bf16", 2, True, True)])
+def test_generate_block_is_its_composition(name, B, selfcond, early):
     """dg_generate_block == canvas init + (denoise, sample) rounds + commit,
-    driven call by call; bitwise identical block, round counts and cache."""
+    driven call by call; bitwise identical block, round counts and cache.
+    early: every sequence stops after its first round (entropy threshold
+    above any entropy, no stability condition), so the loop's look-ahead
+    round runs after the stop and must leave the block untouched."""
     P = 40
     cfg, W, m = setup(name, P, batch=B, capacity_extra=0)
     N, V = cfg["canvas"], cfg["vocab"]
     prompt = synthetic.make_tokens(V, (B, P), seed=30)
-    params = synthetic.default_sampler_params(max_steps=3, seed=5, selfcond_on=int(selfcond))
+    if early:
+        params = synthetic.default_sampler_params(max_steps=5, seed=5, selfcond_on=int(selfcond),
+                                                  stop_tau=1e9, require_stable=0)
+    else:
+        params = synthetic.default_sampler_params(max_steps=3, seed=5, selfcond_on=int(selfcond))
     # library loop
     mg = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(to_dev(prompt))
@@ -312,7 +321,7 @@ def test_generate_block_is_its_composition(name, B, selfcond):
             prev, prev_st = lg[t % 2], st[t % 2]
     mc.commit_block(argmax)
     torch.cuda.synchronize()
-    assert steps == my_steps == [3] * B
+    assert steps == my_steps == ([1] * B if early else [3] * B)
     assert (block.cpu().numpy() == argmax.cpu().numpy()).all()
     assert mg.kv_length == mc.kv_length == P + N
     K1, V1 = mg.kv_tensors()
