@@ -155,7 +155,6 @@ struct Scratch {
     float* gp;        // split-K partials of the small projections
     void* probs;      // bf16 models: softmax(prev logits) in bf16 for self-conditioning
     float* u32;       // bf16 models: fp32 normalised activations for the router
-    float* wr32;      // bf16 models: router weights widened to fp32
     // set by the block loop (not carved): when *halt != 0 every sequence of
     // the batch has stopped and the heavy kernels of a round skip their work
     const int32_t* halt = nullptr;
@@ -207,7 +206,6 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.tok = cv.take<int32_t>(T);
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
-    s.wr32 = wide ? cv.take<float>((size_t)c.n_experts * c.d_model) : nullptr;
     return cv.ok;
 }
 
@@ -260,7 +258,8 @@ bool use_stream_wide() {
 template <typename T>
 dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, long ldc, int epi,
                  Scratch& s, hipStream_t st, const void* E = nullptr,
-                 const int32_t* tokens = nullptr, int vocab = 0) {
+                 const int32_t* tokens = nullptr, int vocab = 0, int b_bf16 = 0,
+                 const void* B2 = nullptr, int n_b2 = 0, const void* B3 = nullptr, int n_b3 = 0) {
     dg::GemmArgs g;
     g.M = M;
     g.N = N;
@@ -277,6 +276,11 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
     g.tokens = tokens;
     g.vocab = vocab;
     g.E_is_f32 = sizeof(T) == 4;
+    g.b_bf16 = b_bf16;
+    g.B2 = B2;
+    g.n_b2 = n_b2;
+    g.B3 = B3;
+    g.n_b3 = n_b3;
     const bool bf = sizeof(T) == 2;
     const int mt = bf ? cdiv(M, 16 * dg::stream_tm_for(M)) : cdiv(M, 64);
     long tiles_wide = (long)cdiv(N, 256) * mt;
@@ -313,11 +317,9 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     const int d = c.d_model, dh = c.head_dim;
     const int qkvw = (c.n_heads + 2 * c.n_kv_heads) * dh;
     DG_HIP(dg::rmsnorm<T>(h, L.attn_norm, (T*)s.u, Tn, d, c.rms_eps, st));
-    DG_TRY(linear<T>(s.u, Tn, d, L.wq, c.n_heads * dh, s.qkv, qkvw, dg::EPI_STORE_F32, s, st));
-    DG_TRY(linear<T>(s.u, Tn, d, L.wk, c.n_kv_heads * dh, s.qkv + c.n_heads * dh, qkvw,
-                     dg::EPI_STORE_F32, s, st));
-    DG_TRY(linear<T>(s.u, Tn, d, L.wv, c.n_kv_heads * dh, s.qkv + (c.n_heads + c.n_kv_heads) * dh,
-                     qkvw, dg::EPI_STORE_F32, s, st));
+    // q, k and v in one product: the columns of W_k and W_v follow those of W_q
+    DG_TRY(linear<T>(s.u, Tn, d, L.wq, qkvw, s.qkv, qkvw, dg::EPI_STORE_F32, s, st, nullptr,
+                     nullptr, 0, 0, L.wk, c.n_heads * dh, L.wv, (c.n_heads + c.n_kv_heads) * dh));
     void *kc, *vc;
     kv_layer(m, kv, layer, &kc, &vc);
     DG_HIP(dg::rope_kv<T>(s.qkv, (T*)s.q, (T*)kc, (T*)vc, B, n, pos0, kv->cap, c.n_heads,
@@ -351,17 +353,16 @@ template <typename T>
 dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
-    DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
     if (sizeof(T) == 2) {
         // The route is an integer decision taken from float logits: compute
-        // them from the fp32 normalised activations and fp32-widened router
-        // weights, so bf16 rounding of the activations cannot flip it.
-        DG_HIP(dg::rmsnorm<float>(h, L.moe_norm, s.u32, Tn, c.d_model, c.rms_eps, st));
-        DG_HIP(dg::widen_bf16((const uint16_t*)L.w_router, s.wr32,
-                              (long)c.n_experts * c.d_model, st));
-        DG_TRY(linear<float>(s.u32, Tn, c.d_model, s.wr32, c.n_experts, s.z, c.n_experts,
-                             dg::EPI_STORE_F32, s, st));
+        // them from the fp32 normalised activations (written by the same
+        // kernel as the bf16 ones) and the bf16 router weights widened to
+        // fp32 on load, so bf16 rounding of the activations cannot flip it.
+        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32));
+        DG_TRY(linear<float>(s.u32, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
+                             dg::EPI_STORE_F32, s, st, nullptr, nullptr, 0, 1));
     } else {
+        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
         DG_TRY(linear<T>(s.u, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
                          dg::EPI_STORE_F32, s, st));
     }

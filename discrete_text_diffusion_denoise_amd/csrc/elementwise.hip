@@ -11,7 +11,8 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h,
                                                       const float* __restrict__ w,
-                                                      T* __restrict__ u, int d, float eps) {
+                                                      T* __restrict__ u, int d, float eps,
+                                                      float* __restrict__ u32) {
     const long row = blockIdx.x;
     const float* x = h + row * d;
     float ss = 0.f;
@@ -29,10 +30,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
         float4 v = *reinterpret_cast<const float4*>(x + i);
         float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
-        o[i + 0] = Elt<T>::from_f(v.x * scale * s.x);
-        o[i + 1] = Elt<T>::from_f(v.y * scale * s.y);
-        o[i + 2] = Elt<T>::from_f(v.z * scale * s.z);
-        o[i + 3] = Elt<T>::from_f(v.w * scale * s.w);
+        const float4 r = make_float4(v.x * scale * s.x, v.y * scale * s.y, v.z * scale * s.z,
+                                     v.w * scale * s.w);
+        o[i + 0] = Elt<T>::from_f(r.x);
+        o[i + 1] = Elt<T>::from_f(r.y);
+        o[i + 2] = Elt<T>::from_f(r.z);
+        o[i + 3] = Elt<T>::from_f(r.w);
+        if (u32) *reinterpret_cast<float4*>(u32 + row * d + i) = r;
     }
 }
 
@@ -153,9 +157,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
-                   hipStream_t st) {
+                   hipStream_t st, float* u32) {
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, st, h, w, u, d, eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, st, h, w, u, d, eps, u32);
     return hipGetLastError();
 }
 
@@ -217,7 +221,7 @@ hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int p
 
 #define DG_INST(T)                                                                        \
     template hipError_t rmsnorm<T>(const float*, const float*, T*, int, int, float,        \
-                                   hipStream_t);                                           \
+                                   hipStream_t, float*);                                   \
     template hipError_t embed_rows<T>(const T*, int, const int32_t*, int, int, int, float*, int, \
                                       hipStream_t);                                        \
     template hipError_t splitk_reduce<T>(const float*, T*, int, int, int, hipStream_t);    \

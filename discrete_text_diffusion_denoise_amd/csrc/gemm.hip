@@ -132,16 +132,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tn_kernel(GemmArgs g) {
             else
                 ra[c] = make_uint4(0, 0, 0, 0);
         }
-        const T* B = reinterpret_cast<const T*>(g.B);
 #pragma unroll
         for (int c = 0; c < B_CHUNKS; ++c) {
             int ch = tid + c * NT;
             int row = ch >> 3, kc = (ch & 7) * ST::CE;
             int gn = n0 + row, gk = kb + kc;
-            if (gn < g.N && gk < kend)
-                rb[c] = *reinterpret_cast<const uint4*>(B + (long)gn * g.ldb + gk);
-            else
+            if (gn < g.N && gk < kend) {
+                if (sizeof(T) == 4 && g.b_bf16) {
+                    // bf16 weights widened on load (exact)
+                    const uint2 h = *reinterpret_cast<const uint2*>(b_row<bf16_t>(g, gn) + gk);
+                    rb[c] = make_uint4(h.x << 16, h.x & 0xffff0000u, h.y << 16, h.y & 0xffff0000u);
+                } else {
+                    rb[c] = *reinterpret_cast<const uint4*>(b_row<T>(g, gn) + gk);
+                }
+            } else {
                 rb[c] = make_uint4(0, 0, 0, 0);
+            }
         }
     };
     auto sstore = [&](int buf) {

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(256 * WM) void gemm_stream_kernel(GemmArgs g) {
     const int kend = min(g.K, kbeg + g.k_split);
     const int nst = kend > kbeg ? cdiv(kend - kbeg, SKB) : 0;
     const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
-    const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
 
     const bf16_t* brow[TN];
     bool bval[TN];
@@ -66,7 +65,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_stream_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) {
         const int col = n0 + 16 * j + r16;
         bval[j] = col < g.N;
-        brow[j] = B + (long)(bval[j] ? col : 0) * g.ldb;
+        brow[j] = b_row<bf16_t>(g, bval[j] ? col : 0);
     }
 
     f32x4_t acc[TM][TN];

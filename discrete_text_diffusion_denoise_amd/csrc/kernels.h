@@ -29,7 +29,21 @@ struct GemmArgs {
     int xcd_group = 0;              // put a k-split's column tiles on one XCD
     int k_rotate = 0;               // rotate each tile's starting k-slice
     const int32_t* halt = nullptr;  // vocabulary GEMMs: skip all work when *halt != 0
+    int b_bf16 = 0;                 // fp32 GEMM: B is bf16, widened on load
+    // column segments: columns [n_b2, n_b3) are rows of B2, [n_b3, N) rows
+    // of B3 (0 = no segment); the stacked Q/K/V projection in one product
+    const void* B2 = nullptr;
+    const void* B3 = nullptr;
+    int n_b2 = 0, n_b3 = 0;
 };
+
+// Row n of the (segmented) B operand, in elements of type E.
+template <typename E>
+__device__ __forceinline__ const E* b_row(const GemmArgs& g, int n) {
+    if (g.n_b3 && n >= g.n_b3) return reinterpret_cast<const E*>(g.B3) + (long)(n - g.n_b3) * g.ldb;
+    if (g.n_b2 && n >= g.n_b2) return reinterpret_cast<const E*>(g.B2) + (long)(n - g.n_b2) * g.ldb;
+    return reinterpret_cast<const E*>(g.B) + (long)n * g.ldb;
+}
 
 // C (op)= A * B^T.  amode 1 reads A as softmax of fp32 logits (only with
 // EPI_SPLITK).  T = bf16_t (uint16_t) or float.
@@ -57,10 +71,10 @@ hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t st);
 // halt: when non-null and *halt != 0 the kernel does nothing
 hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
                              int V, const int32_t* halt, hipStream_t st);
-// u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T)
+// u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T; also fp32 into u32 if set)
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
-                   hipStream_t st);
+                   hipStream_t st, float* u32 = nullptr);
 // h[b*n + i] = E[tok[b*ld + i]] (fp32), b < B, i < n; E has V rows
 template <typename T>
 hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int B, float* h, int d,

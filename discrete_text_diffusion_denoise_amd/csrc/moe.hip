@@ -276,14 +276,94 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
     }
 }
 
+// Counts, offsets and the stable placement in one workgroup: counts by LDS
+// atomics, an exclusive prefix in one wave, then one wave walks the
+// assignments in order, 64 at a time.  Lanes holding the same expert find
+// each other by ballots over the expert's bits; a lane's slot is the
+// expert's running offset plus the number of lower lanes in its group, and
+// the group's highest lane advances the offset.  Same permutation as the
+// per-expert scan (assignments of an expert in increasing order).
+__global__ __launch_bounds__(1024) void place_all_kernel(MoeArgs a) {
+    __shared__ int cnt[256], off[256];
+    const int tid = threadIdx.x;
+    const int total = a.T * a.k;
+    for (int e = tid; e < a.E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < total; i += 1024) atomicAdd(&cnt[a.route[i]], 1);
+    __syncthreads();
+    if (tid < 64) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            v[q] = e < a.E ? cnt[e] : 0;
+            sum += v[q];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += y;
+        }
+        int ex = incl - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid * 4 + q;
+            if (e < a.E) {
+                off[e] = ex;
+                a.offsets[e] = ex;
+                a.counts[e] = v[q];
+            }
+            ex += v[q];
+        }
+        if (tid == 63) a.offsets[a.E] = incl;
+        const uint64_t lt = tid == 0 ? 0ull : (~0ull >> (64 - tid));
+        for (int base = 0; base < total; base += 64) {
+            const int i = base + tid;
+            const bool valid = i < total;
+            const int e = valid ? a.route[i] : 0x1FF;   // 9 bits: never a real expert
+            uint64_t same = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 9; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t bal = __ballot(bit);
+                same &= bit ? bal : ~bal;
+            }
+            if (valid) {
+                const int slot = off[e] + __popcll(same & lt);
+                a.perm_tok[slot] = i / a.k;
+                a.slot_of[i] = slot;
+                const uint64_t higher = tid == 63 ? 0ull : (same >> (tid + 1));
+                if (higher == 0) off[e] += __popcll(same);
+            }
+        }
+    }
+}
+
 // h[t] += sum_j gate[t][j] * y[slot_of[t][j]]  (j in selection order)
 __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
     const long t = blockIdx.x;
-    for (int c = threadIdx.x; c < a.d; c += 256) {
-        float acc = a.h[t * a.d + c];
-        for (int j = 0; j < a.k; ++j)
-            acc += a.gates[t * a.k + j] * a.y[(long)a.slot_of[t * a.k + j] * a.d + c];
-        a.h[t * a.d + c] = acc;
+    float gt[16];
+    long yo[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        gt[j] = j < a.k ? a.gates[t * a.k + j] : 0.f;
+        yo[j] = j < a.k ? (long)a.slot_of[t * a.k + j] * a.d : 0;
+    }
+    float* hr = a.h + t * a.d;
+    for (int c = threadIdx.x * 4; c < a.d; c += 1024) {
+        float4 acc = *reinterpret_cast<const float4*>(hr + c);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < a.k) {
+                const float4 y = *reinterpret_cast<const float4*>(a.y + yo[j] + c);
+                acc.x += gt[j] * y.x;
+                acc.y += gt[j] * y.y;
+                acc.z += gt[j] * y.z;
+                acc.w += gt[j] * y.w;
+            }
+        }
+        *reinterpret_cast<float4*>(hr + c) = acc;
     }
 }
 
@@ -292,8 +372,13 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
 hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     hipLaunchKernelGGL(route_kernel, dim3(cdiv(a.T, 4)), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(count_kernel, dim3(a.E), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(place_kernel, dim3(a.E), dim3(64), 0, st, a);
+    if ((long)a.T * a.k <= 8192) {
+        // few assignments (a canvas): one workgroup places them all
+        hipLaunchKernelGGL(place_all_kernel, dim3(1), dim3(1024), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(count_kernel, dim3(a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(place_kernel, dim3(a.E), dim3(64), 0, st, a);
+    }
     return hipGetLastError();
 }
 
