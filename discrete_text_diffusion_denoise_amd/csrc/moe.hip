@@ -7,6 +7,8 @@
 // grouped GEMMs therefore stream each expert's weights exactly once per
 // group of 64 routed tokens, straight from HBM into MFMA operands, while the
 // (small, reused) token rows come through the caches.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -276,6 +278,206 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
     }
 }
 
+// bf16 expert GEMMs with direct-to-LDS loads.  Same work split and epilogue
+// as expert_kernel, but weight and token rows go from memory straight into
+// a ring of four LDS stages (64-wide k) with global_load_lds, three stages in
+// flight while one is multiplied, so the weight stream is not throttled by
+// register staging.  Rows are 128 bytes per stage; chunk c of row r sits in
+// slot c ^ (r & 7), which keeps the fragment reads free of bank conflicts.
+// Fragment reads are one asm block per stage ending in its own
+// lgkmcnt(0) (the ring order already guarantees their loads have landed).
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+#define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
+    if (a.halt && *a.halt) return;
+    constexpr int WR = MODE == 0 ? 64 : 32;            // weight rows per stage
+    constexpr int WQ = WR / 32;                        // weight DMAs per wave per stage
+    constexpr int PER = WQ + 2;                        // DMAs per wave per stage
+    __shared__ __align__(1024) unsigned char w0[WR * 128], x0[8192];
+    __shared__ __align__(1024) unsigned char w1[WR * 128], x1[8192];
+    __shared__ __align__(1024) unsigned char w2[WR * 128], x2[8192];
+    __shared__ __align__(1024) unsigned char w3[WR * 128], x3[8192];
+
+    const int e = blockIdx.y;
+    const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
+    if (cnt == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int ct = wave & 1, mp = wave >> 1;
+    const int K = MODE == 0 ? a.d : a.F;
+    const int NOUT = MODE == 0 ? a.F : a.d;
+    const int c0 = blockIdx.x * 32;
+    const int n = __builtin_amdgcn_readfirstlane(K / 64);   // stages, a multiple of 4
+    const int rot = __builtin_amdgcn_readfirstlane(
+        a.k_rotate ? (int)((blockIdx.x + blockIdx.y * 5) % n) : 0);
+    const bf16_t* Wg = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.w_gate : a.w_down);
+    const bf16_t* Wu = reinterpret_cast<const bf16_t*>(a.w_up);
+    const bf16_t* X = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.u : a.act);
+
+    // DMA lanes: an instruction fills 8 rows x 128 bytes; lane l takes row
+    // l / 8 of them and global chunk (l % 8) ^ (row & 7)
+    const int lr = lane >> 3;
+    const int lc = ((lane & 7) ^ lr) * 8;             // element offset (rows are 8-aligned)
+    const bf16_t* wsrc[WQ];
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+        const int r = (wave * WQ + q) * 8 + lr;        // weight row within the block
+        const int rr = MODE == 0 ? (r & 31) : r;
+        const int col = min(c0 + rr, NOUT - 1);
+        const bf16_t* base = (MODE == 0 && r >= 32) ? Wu : Wg;
+        wsrc[q] = base + ((long)e * NOUT + col) * K + lc;
+    }
+    const int wblk = wave * WQ * 1024;
+    const int xblk = wave * 2 * 1024;
+    const int roff = r16 * 128;
+
+    for (int mg = 0; mg < cnt; mg += 64) {
+        const bf16_t* xsrc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tok = min(mg + (wave * 2 + q) * 8 + lr, cnt - 1);
+            const long src = MODE == 0 ? (long)a.perm_tok[off + tok] : (long)(off + tok);
+            xsrc[q] = X + src * K + lc;
+        }
+        f32x4_t ag[2], au[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            ag[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            au[q] = ag[q];
+        }
+        const bool t0 = mg + 16 * mp < cnt, t1 = mg + 16 * (mp + 2) < cnt;
+
+#define XD_ISSUE(ST, WB, XB)                                                                      \
+        {                                                                                         \
+            int sr_ = (ST) + rot;                                                                 \
+            if (sr_ >= n) sr_ -= n;                                                               \
+            const int k_ = sr_ * 64;                                                              \
+            _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                        \
+                __builtin_amdgcn_global_load_lds((glb_void*)(wsrc[q] + k_),                       \
+                                                 (lds_void*)((WB) + wblk + q * 1024), 16, 0, 0);  \
+            _Pragma("unroll") for (int q = 0; q < 2; ++q)                                         \
+                __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
+                                                 (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
+        }
+        // fragments: token rows 16*mt + r16 (two tiles), weight rows ct*16 + r16
+        // (and 32 + ct*16 + r16 for the up half); chunk 4*s + g4 of k-step s
+#define XD_COMPUTE(WB, XB)                                                                        \
+        {                                                                                         \
+            u32x4 fx0a, fx0b, fx1a, fx1b, fga, fgb, fua, fub;                                     \
+            const uint32_t xa0 = lds_addr(XB) + (16 * mp) * 128 + roff;                           \
+            const uint32_t xa1 = xa0 + 32 * 128;                                                  \
+            const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                            \
+            const uint32_t sa = ((g4 ^ (r16 & 7)) << 4), sb = (((4 + g4) ^ (r16 & 7)) << 4);      \
+            if (MODE == 0) {                                                                      \
+                asm volatile(                                                                     \
+                    "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                                  \
+                    "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                                \
+                    "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                                \
+                    "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                                \
+                    "s_waitcnt lgkmcnt(0)"                                                         \
+                    : "=&v"(fx0a), "=&v"(fx0b), "=&v"(fx1a), "=&v"(fx1b), "=&v"(fga), "=&v"(fgb), \
+                      "=&v"(fua), "=&v"(fub)                                                      \
+                    : "v"(xa0 + sa), "v"(xa0 + sb), "v"(xa1 + sa), "v"(xa1 + sb), "v"(wa + sa),   \
+                      "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb)              \
+                    : "memory");                                                                  \
+            } else {                                                                              \
+                asm volatile(                                                                     \
+                    "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                                  \
+                    "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                                  \
+                    "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                                \
+                    "s_waitcnt lgkmcnt(0)"                                                         \
+                    : "=&v"(fx0a), "=&v"(fx0b), "=&v"(fx1a), "=&v"(fx1b), "=&v"(fga), "=&v"(fgb)  \
+                    : "v"(xa0 + sa), "v"(xa0 + sb), "v"(xa1 + sa), "v"(xa1 + sb), "v"(wa + sa),   \
+                      "v"(wa + sb)                                                                \
+                    : "memory");                                                                  \
+            }                                                                                     \
+            if (t0) {                                                                             \
+                ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0a), \
+                    __builtin_bit_cast(bf16x8_t, fga), ag[0], 0, 0, 0);                           \
+                ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0b), \
+                    __builtin_bit_cast(bf16x8_t, fgb), ag[0], 0, 0, 0);                           \
+                if (MODE == 0) {                                                                  \
+                    au[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0a), \
+                        __builtin_bit_cast(bf16x8_t, fua), au[0], 0, 0, 0);                       \
+                    au[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0b), \
+                        __builtin_bit_cast(bf16x8_t, fub), au[0], 0, 0, 0);                       \
+                }                                                                                 \
+            }                                                                                     \
+            if (t1) {                                                                             \
+                ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1a), \
+                    __builtin_bit_cast(bf16x8_t, fga), ag[1], 0, 0, 0);                           \
+                ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1b), \
+                    __builtin_bit_cast(bf16x8_t, fgb), ag[1], 0, 0, 0);                           \
+                if (MODE == 0) {                                                                  \
+                    au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1a), \
+                        __builtin_bit_cast(bf16x8_t, fua), au[1], 0, 0, 0);                       \
+                    au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1b), \
+                        __builtin_bit_cast(bf16x8_t, fub), au[1], 0, 0, 0);                       \
+                }                                                                                 \
+            }                                                                                     \
+        }
+#define XD_STAGE(t, CW, CX, NW, NX)                          \
+        {                                                    \
+            if ((t) + 2 < n)                                 \
+                DG_WAIT_VM(2 * PER);                         \
+            else if ((t) + 1 < n)                            \
+                DG_WAIT_VM(PER);                             \
+            else                                             \
+                DG_WAIT_VM(0);                               \
+            barrier_lds();                                   \
+            if ((t) + 3 < n) XD_ISSUE((t) + 3, NW, NX);      \
+            XD_COMPUTE(CW, CX);                              \
+        }
+        XD_ISSUE(0, w0, x0);
+        XD_ISSUE(1, w1, x1);
+        XD_ISSUE(2, w2, x2);
+        for (int t = 0; t < n; t += 4) {
+            XD_STAGE(t, w0, x0, w3, x3);
+            XD_STAGE(t + 1, w1, x1, w0, x0);
+            XD_STAGE(t + 2, w2, x2, w1, x1);
+            XD_STAGE(t + 3, w3, x3, w2, x2);
+        }
+#undef XD_STAGE
+#undef XD_COMPUTE
+#undef XD_ISSUE
+
+        // lane holds tokens 4*g4 + i of tile mt, output column c0 + ct*16 + r16
+        const int col = c0 + ct * 16 + r16;
+        if (col < NOUT) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int mt = mp + 2 * q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = mg + 16 * mt + 4 * g4 + i;
+                    if (row >= cnt) continue;
+                    if constexpr (MODE == 0) {
+                        const float gv = ag[q][i], uv = au[q][i];
+                        const float sv = gv / (1.0f + __expf(-gv));
+                        reinterpret_cast<bf16_t*>(a.act)[(long)(off + row) * a.F + col] = f2bf(sv * uv);
+                    } else {
+                        a.y[(long)(off + row) * a.d + col] = ag[q][i];
+                    }
+                }
+            }
+        }
+        // the next group's loads refill the ring only after every wave is done
+        barrier_lds();
+    }
+}
+
 // Counts, offsets and the stable placement in one workgroup: counts by LDS
 // atomics, an exclusive prefix in one wave, then one wave walks the
 // assignments in order, 64 at a time.  Lanes holding the same expert find
@@ -382,17 +584,33 @@ hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// the ring kernel needs whole rings of four 64-wide stages in both products
+bool expert_dma_ok(const MoeArgs& a) {
+    static int enabled = -1;
+    if (enabled < 0) {
+        const char* e = getenv("DG_DMA");
+        enabled = e ? atoi(e) : 1;
+    }
+    return enabled && a.d % 256 == 0 && a.F % 256 == 0;
+}
+
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+    if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL(expert_dma_kernel<0>, dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
+    if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL(expert_dma_kernel<1>, dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
