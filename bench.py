@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="layer", choices=["layer", "stack"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the measurement, two 1 GiB device copies (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
 
@@ -111,6 +113,34 @@ def roofline(name, ms, cfg, B, P, sc_splits):
             "flop_per_launch": flops, "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 5)}
 
 
+# kernel timer -> the source file its kernel is built from
+KERNEL_SOURCE = {"head_gemm": "gemm_dma.hip", "selfcond_gemm": "gemm_dma.hip",
+                 "moe_gateup": "moe.hip", "moe_down": "moe.hip", "attention": "attention.hip",
+                 "sampler": "sampler.hip"}
+
+
+def measured_traffic(name, config):
+    """HBM bytes per launch of `name` from the committed counter summary
+    profiles/traffic_<name>_<config>.txt (FETCH_SIZE and WRITE_SIZE runs,
+    each scaled by the same counter on a 1 GiB copy), or None when there is
+    no summary or the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{config}.txt")
+    src = os.path.join(ROOT, "discrete_text_diffusion_denoise_amd", "csrc",
+                       KERNEL_SOURCE.get(name, ""))
+    if not os.path.exists(path) or not os.path.isfile(src):
+        return None, None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != digest or "traffic_bytes" not in vals:
+        return None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
+    return float(vals["traffic_bytes"]), os.path.relpath(path, ROOT)
+
+
 def cpu_baseline(cfg, W, prompt, canvas, params, torch):
     """The CPU oracle (float64 numpy model + C sampler), timed on this host on
     a bounded sample: one self-conditioned denoising step and one sampler
@@ -181,12 +211,21 @@ def main():
     params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1)
     block = torch.zeros((B, N), dtype=torch.int32, device="cuda")
 
+    names = list(binding.TIMERS)
+    # warmup, with every kernel timer on: picks the dominant kernel
+    binding.timer_enable(names)
     for w in range(args.warmup):
         m.generate_block(params, w, block)
         m.set_kv_length(P)
     torch.cuda.synchronize()
+    warm = {n: binding.timer_read(n) for n in names}
+    binding.timer_enable([])
+    dominant = max(names, key=lambda n: warm[n][0]) if args.warmup else "head_gemm"
 
-    # timed blocks: no kernel timers (their events sit between kernels)
+    # timed blocks: only the dominant kernel is bracketed by the library's
+    # HIP events (on the stream it runs on); every other timer is off, since
+    # each recorded event sits between two kernels
+    binding.timer_enable([dominant])
     rounds = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -196,9 +235,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    dom_ms, dom_n = binding.timer_read(dominant)
+    binding.timer_enable([])
 
-    # per-kernel breakdown: one more block with the library's HIP-event timers
-    names = list(binding.TIMERS)
+    # per-kernel breakdown: one more block with every timer on
     binding.timer_enable(names)
     m.generate_block(params, args.warmup + args.steps, block)
     m.set_kv_length(P)
@@ -238,8 +278,9 @@ def main():
     sc_splits = (sc_splits // 8) * 8 if sc_splits >= 8 else sc_splits
     k_split = -(-(-(-V // sc_splits)) // 128) * 128
     sc_splits = -(-V // k_split)
-    dominant = max((n for n in names if kern[n]["launches"]), key=lambda n: kern[n]["total_ms"])
-    roof = roofline(dominant, kern[dominant]["avg_ms"], cfg, B, P, sc_splits)
+    roof = roofline(dominant, dom_ms / dom_n, cfg, B, P, sc_splits)
+    roof["timed_launches"] = dom_n
+    roof["traffic"], roof["traffic_source"] = measured_traffic(dominant, args.config)
     per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], cfg, B, P,
                                                                   sc_splits).items()
                                        if k in ("bound", "achieved", "unit", "frac")}
@@ -272,6 +313,13 @@ def main():
         "kernels": per_kernel,
         "roofline": roof,
     }
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         cpu_canvas = np.asarray(canvas.cpu().numpy(), dtype=np.int64)
         out["cpu_baseline"] = cpu_baseline(cfg, W, prompt.cpu().numpy().astype(np.int64),

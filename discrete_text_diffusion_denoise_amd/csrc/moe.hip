@@ -478,27 +478,39 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     }
 }
 
-// Counts, offsets and the stable placement in one workgroup: counts by LDS
-// atomics, an exclusive prefix in one wave, then one wave walks the
-// assignments in order, 64 at a time.  Lanes holding the same expert find
-// each other by ballots over the expert's bits; a lane's slot is the
-// expert's running offset plus the number of lower lanes in its group, and
-// the group's highest lane advances the offset.  Same permutation as the
-// per-expert scan (assignments of an expert in increasing order).
-__global__ __launch_bounds__(1024) void place_all_kernel(MoeArgs a) {
-    __shared__ int cnt[256], off[256];
-    const int tid = threadIdx.x;
+// Counts, offsets and the stable placement in one workgroup.  The
+// assignments are cut into PW contiguous ranges, one per wave: per-range
+// expert counts (LDS atomics), an exclusive prefix over (expert, range),
+// then each wave walks its range 64 assignments at a time.  Lanes holding
+// the same expert find each other by ballots over the expert's bits; a
+// lane's slot is its range's running offset for the expert plus the number
+// of lower lanes in its group, and the group's highest lane advances the
+// offset.  Same permutation as the per-expert scan (assignments of an
+// expert in increasing order).
+constexpr int PW = 16;             // waves of the placement workgroup
+
+__global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
+    __shared__ int cw[PW][256];    // per-range counts, then per-range running offsets
+    __shared__ int tot[256];       // per-expert totals, then expert offsets
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int total = a.T * a.k;
-    for (int e = tid; e < a.E; e += 1024) cnt[e] = 0;
+    const int per = cdiv(cdiv(total, 64), PW) * 64;    // assignments per range
+    const int i0 = min(total, wave * per), i1 = min(total, (wave + 1) * per);
+    for (int x = tid; x < PW * 256; x += 64 * PW) (&cw[0][0])[x] = 0;
     __syncthreads();
-    for (int i = tid; i < total; i += 1024) atomicAdd(&cnt[a.route[i]], 1);
+    for (int i = i0 + lane; i < i1; i += 64) atomicAdd(&cw[wave][a.route[i]], 1);
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 256) {
+        int c = 0;
+        for (int w = 0; w < PW; ++w) c += cw[w][tid];
+        tot[tid] = c;
+    }
+    __syncthreads();
+    if (tid < 64) {                                    // exclusive scan of the totals
         int v[4], sum = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = tid * 4 + q;
-            v[q] = e < a.E ? cnt[e] : 0;
+            v[q] = tot[tid * 4 + q];
             sum += v[q];
         }
         int incl = sum;
@@ -512,32 +524,43 @@ __global__ __launch_bounds__(1024) void place_all_kernel(MoeArgs a) {
         for (int q = 0; q < 4; ++q) {
             const int e = tid * 4 + q;
             if (e < a.E) {
-                off[e] = ex;
                 a.offsets[e] = ex;
                 a.counts[e] = v[q];
             }
+            tot[e] = ex;
             ex += v[q];
         }
         if (tid == 63) a.offsets[a.E] = incl;
-        const uint64_t lt = tid == 0 ? 0ull : (~0ull >> (64 - tid));
-        for (int base = 0; base < total; base += 64) {
-            const int i = base + tid;
-            const bool valid = i < total;
-            const int e = valid ? a.route[i] : 0x1FF;   // 9 bits: never a real expert
-            uint64_t same = ~0ull;
+    }
+    __syncthreads();
+    if (tid < 256) {                                   // range offsets: expert offset + earlier ranges
+        int run = tot[tid];
+        for (int w = 0; w < PW; ++w) {
+            const int c = cw[w][tid];
+            cw[w][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int* off = cw[wave];
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int base = i0; base < i1; base += 64) {
+        const int i = base + lane;
+        const bool valid = i < i1;
+        const int e = valid ? a.route[i] : 0x1FF;       // 9 bits: never a real expert
+        uint64_t same = ~0ull;
 #pragma unroll
-            for (int b = 0; b < 9; ++b) {
-                const bool bit = (e >> b) & 1;
-                const uint64_t bal = __ballot(bit);
-                same &= bit ? bal : ~bal;
-            }
-            if (valid) {
-                const int slot = off[e] + __popcll(same & lt);
-                a.perm_tok[slot] = i / a.k;
-                a.slot_of[i] = slot;
-                const uint64_t higher = tid == 63 ? 0ull : (same >> (tid + 1));
-                if (higher == 0) off[e] += __popcll(same);
-            }
+        for (int b = 0; b < 9; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        if (valid) {
+            const int slot = off[e] + __popcll(same & lt);
+            a.perm_tok[slot] = i / a.k;
+            a.slot_of[i] = slot;
+            const uint64_t higher = lane == 63 ? 0ull : (same >> (lane + 1));
+            if (higher == 0) off[e] += __popcll(same);
         }
     }
 }
@@ -576,7 +599,7 @@ hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(route_kernel, dim3(cdiv(a.T, 4)), dim3(256), 0, st, a);
     if ((long)a.T * a.k <= 8192) {
         // few assignments (a canvas): one workgroup places them all
-        hipLaunchKernelGGL(place_all_kernel, dim3(1), dim3(1024), 0, st, a);
+        hipLaunchKernelGGL(place_all_kernel, dim3(1), dim3(64 * PW), 0, st, a);
     } else {
         hipLaunchKernelGGL(count_kernel, dim3(a.E), dim3(256), 0, st, a);
         hipLaunchKernelGGL(place_kernel, dim3(a.E), dim3(64), 0, st, a);
