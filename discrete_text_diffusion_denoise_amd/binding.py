@@ -48,7 +48,7 @@ class LayerWeights(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("embed_t", ctypes.c_void_p),
                 ("w_sc", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(LayerWeights))]
+                ("layers", ctypes.POINTER(LayerWeights)), ("embed_head", ctypes.c_void_p)]
 
 
 class SamplerParams(ctypes.Structure):
@@ -67,6 +67,8 @@ _SIGS = {
     "dg_model_create": (_I, [_P, _P, _P]),
     "dg_model_destroy": (None, [_P]),
     "dg_embed_transpose": (_I, [_P, _P, _P, _P]),
+    "dg_embed_head_bytes": (_I, [_P, _P]),
+    "dg_embed_head": (_I, [_P, _P, _P, _P]),
     "dg_kv_bytes": (_I, [_P, _I, _I, _P]),
     "dg_kv_create": (_I, [_P, _I, _I, _P, _P]),
     "dg_kv_destroy": (None, [_P]),
@@ -177,10 +179,22 @@ class Model:
         self.w["embed_t"] = torch.empty((cfg["d_model"], cfg["vocab"]), dtype=self.dtype,
                                         device=self.device)
         w = Weights(self.w["embed"].data_ptr(), self.w["embed_t"].data_ptr(),
-                    self.w["w_sc"].data_ptr(), self.w["final_norm"].data_ptr(), layer_arr)
-        self._w_struct = w
+                    self.w["w_sc"].data_ptr(), self.w["final_norm"].data_ptr(), layer_arr, None)
         h = ctypes.c_void_p()
         _check(L.dg_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)))
+        # blocked models take the head's operand prepared once (the weight
+        # table is copied at create, so the model is created again with it)
+        nb = ctypes.c_size_t()
+        _check(L.dg_embed_head_bytes(h, ctypes.byref(nb)))
+        if nb.value:
+            self.w["embed_head"] = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+            w.embed_head = self.w["embed_head"].data_ptr()
+            L.dg_model_destroy(h)
+            h = ctypes.c_void_p()
+            _check(L.dg_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)))
+            _check(L.dg_embed_head(h, _ptr(self.w["embed"]), _ptr(self.w["embed_head"]),
+                                   _stream()))
+        self._w_struct = w
         self.handle = h
         _check(L.dg_embed_transpose(h, _ptr(self.w["embed"]), _ptr(self.w["embed_t"]),
                                     _stream()))

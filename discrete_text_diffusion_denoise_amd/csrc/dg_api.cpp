@@ -108,6 +108,11 @@ struct dg_model {
     dg_config c;
     const void* embed;
     const void* embed_t;
+    const void* embed_head;   // optional: E in the blocked layout (dg_embed_head)
+    // bf16, d % 256 == 0, V % 128 == 0: the vocabulary products run on the
+    // ring kernel with both operands in the blocked layout (embed_t is E^T
+    // blocked; the activations are written blocked)
+    bool blocked = false;
     const void* w_sc;
     const float* final_norm;
     std::vector<dg_layer_weights> layers;
@@ -154,6 +159,7 @@ struct Scratch {
     int32_t* tok;
     float* gp;        // split-K partials of the small projections
     void* probs;      // bf16 models: softmax(prev logits) in bf16 for self-conditioning
+    void* ut;         // blocked models: final-normed rows for the head, blocked layout
     float* u32;       // bf16 models: fp32 normalised activations for the router
     // set by the block loop (not carved): when *halt != 0 every sequence of
     // the batch has stopped and the heavy kernels of a round skip their work
@@ -202,7 +208,10 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.sc_part = cv.take<float>((size_t)sc_splits(m, (int)Tc) * Tc * c.d_model);
     s.sc_s = cv.take_bytes(Tc * c.d_model * es);
     s.gp = cv.take<float>(kSplitPartFloats);
-    s.probs = c.dtype == DG_BF16 ? cv.take_bytes(Tc * c.vocab * 2) : nullptr;
+    // rows padded to 256 for the blocked layout
+    const size_t Tp = (size_t)cdiv((int)Tc, 256) * 256;
+    s.probs = c.dtype == DG_BF16 ? cv.take_bytes(Tp * c.vocab * 2) : nullptr;
+    s.ut = m->blocked ? cv.take_bytes(Tp * c.d_model * 2) : nullptr;
     s.tok = cv.take<int32_t>(T);
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
@@ -428,12 +437,13 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         // vocabulary split into `used` k-ranges (column tiles of a range on
         // one XCD)
         DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, s.halt,
-                                     st));
+                                     m->blocked ? 1 : 0, st));
         g.A = s.probs;
+        g.a_tiled = g.b_tiled = m->blocked ? 1 : 0;
         g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
         g.k_rotate = env_flag("DG_KROT", 1);
         g.halt = s.halt;
-        if (use_stream_wide())
+        if (use_stream_wide() && !g.a_tiled)
             DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
                          [&] { return dg::gemm_stream(g, dg::EPI_SPLITK, 4, used, st); }));
         else
@@ -453,13 +463,10 @@ template <typename T>
 dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch& s,
                      hipStream_t st) {
     const dg_config& c = m->c;
-    DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
     dg::GemmArgs g;
     g.M = Tn;
     g.N = c.vocab;
     g.K = c.d_model;
-    g.A = s.u;
-    g.lda = c.d_model;
     g.B = m->embed;
     g.ldb = c.d_model;
     g.C = logits;
@@ -467,7 +474,19 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.k_split = c.d_model;
     g.k_rotate = env_flag("DG_KROT", 1);
     g.halt = s.halt;
-    if (sizeof(T) == 2 && use_stream_wide())
+    if (m->blocked && m->embed_head) {
+        // both operands in the blocked layout: each stage of a tile is one
+        // contiguous 16 KiB block of E and of the normalised rows
+        DG_HIP(dg::rmsnorm_tiled(h, m->final_norm, (uint16_t*)s.ut, Tn, c.d_model, c.rms_eps, st));
+        g.A = s.ut;
+        g.B = m->embed_head;
+        g.a_tiled = g.b_tiled = 1;
+    } else {
+        DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
+        g.A = s.u;
+        g.lda = c.d_model;
+    }
+    if (sizeof(T) == 2 && use_stream_wide() && !g.a_tiled)
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
                      [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));
     else
@@ -568,6 +587,8 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
     m->c = c;
     m->embed = w->embed;
     m->embed_t = w->embed_t;
+    m->embed_head = w->embed_head;
+    m->blocked = c.dtype == DG_BF16 && c.d_model % 256 == 0 && c.vocab % 128 == 0;
     m->w_sc = w->w_sc;
     m->final_norm = w->final_norm;
     m->layers.assign(w->layers, w->layers + c.n_layers);
@@ -580,12 +601,31 @@ void dg_model_destroy(dg_model* m) { delete m; }
 dg_status dg_embed_transpose(const dg_model* m, const void* d_embed, void* d_out, void* stream) {
     DG_TRY(check_model(m));
     if (!d_embed || !d_out) return fail(DG_ERR_ARG, "NULL pointer");
-    if (m->c.dtype == DG_BF16)
+    if (m->blocked)
+        DG_HIP(dg::embed_tile((const uint16_t*)d_embed, m->c.vocab, m->c.d_model, 1,
+                              (uint16_t*)d_out, as_stream(stream)));
+    else if (m->c.dtype == DG_BF16)
         DG_HIP(dg::transpose<bf16_t>((const bf16_t*)d_embed, (bf16_t*)d_out,
                                          m->c.vocab, m->c.d_model, as_stream(stream)));
     else
         DG_HIP(dg::transpose<float>((const float*)d_embed, (float*)d_out, m->c.vocab,
                                     m->c.d_model, as_stream(stream)));
+    return DG_OK;
+}
+
+dg_status dg_embed_head_bytes(const dg_model* m, size_t* bytes) {
+    DG_TRY(check_model(m));
+    if (!bytes) return fail(DG_ERR_ARG, "NULL pointer");
+    *bytes = m->blocked ? (size_t)cdiv(m->c.vocab, 256) * 256 * m->c.d_model * 2 : 0;
+    return DG_OK;
+}
+
+dg_status dg_embed_head(const dg_model* m, const void* d_embed, void* d_out, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_embed || !d_out) return fail(DG_ERR_ARG, "NULL pointer");
+    if (!m->blocked) return fail(DG_ERR_UNSUPPORTED, "this model's head reads embed directly");
+    DG_HIP(dg::embed_tile((const uint16_t*)d_embed, m->c.vocab, m->c.d_model, 0, (uint16_t*)d_out,
+                          as_stream(stream)));
     return DG_OK;
 }
 

@@ -68,29 +68,102 @@ __global__ __launch_bounds__(256) void widen_kernel(const bf16_t* __restrict__ i
     if (i < n) out[i] = bf2f(in[i]);
 }
 
-// p = exp(l - max) / sum, written as bf16; blockIdx.y = row, blockIdx.x = a
-// 4096-entry segment of it (enough workgroups to keep HBM busy).
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int32_t v, long n) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = v;
 }
 
+// p = exp(l - max) / sum, written as bf16 (row-major, or in the 256 x 32
+// blocked layout when `tiled`); blockIdx.y = row, blockIdx.x = a 4096-entry
+// segment of it (enough workgroups to keep HBM busy).
 __global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ stats,
                                                            bf16_t* __restrict__ out, int V,
-                                                           const int32_t* halt) {
+                                                           const int32_t* halt, int tiled) {
     if (halt && *halt) return;
     const long row = blockIdx.y;
     const float m = stats[row * 4 + 0];
     const float inv = 1.0f / stats[row * 4 + 1];
     const float4* L = reinterpret_cast<const float4*>(logits + row * V);
-    uint2* O = reinterpret_cast<uint2*>(out + row * V);
     const int end = min(V / 4, (int)(blockIdx.x + 1) * 1024);
     for (int i = blockIdx.x * 1024 + threadIdx.x; i < end; i += 256) {
         const float4 x = L[i];
-        O[i] = make_uint2(pack_bf2(__expf(x.x - m) * inv, __expf(x.y - m) * inv),
-                          pack_bf2(__expf(x.z - m) * inv, __expf(x.w - m) * inv));
+        const uint2 p = make_uint2(pack_bf2(__expf(x.x - m) * inv, __expf(x.y - m) * inv),
+                                   pack_bf2(__expf(x.z - m) * inv, __expf(x.w - m) * inv));
+        const long o = tiled ? tiled_index(row, 4L * i, V) : row * V + 4L * i;
+        *reinterpret_cast<uint2*>(out + o) = p;
     }
+}
+
+// RMSNorm of fp32 rows into the blocked bf16 layout (rows padded to 256 are
+// not written).
+__global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float* __restrict__ h,
+                                                            const float* __restrict__ w,
+                                                            bf16_t* __restrict__ u, int d,
+                                                            float eps) {
+    const long row = blockIdx.x;
+    const float* x = h + row * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        float4 v = *reinterpret_cast<const float4*>(x + i);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        float4 v = *reinterpret_cast<const float4*>(x + i);
+        float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+        *reinterpret_cast<uint2*>(u + tiled_index(row, i, d)) =
+            make_uint2(pack_bf2(v.x * scale * s.x, v.y * scale * s.y),
+                       pack_bf2(v.z * scale * s.z, v.w * scale * s.w));
+    }
+}
+
+// E [V][d] (bf16) into the blocked layout of E (rows V, padded with zeros to
+// a multiple of 256; K = d).  One thread per 16-byte chunk of the output.
+__global__ __launch_bounds__(256) void embed_tile_kernel(const bf16_t* __restrict__ E, int V,
+                                                         int d, bf16_t* __restrict__ out,
+                                                         long chunks) {
+    const long q = (long)blockIdx.x * 256 + threadIdx.x;
+    if (q >= chunks) return;
+    const long o = q * 8;                       // output element
+    const int c = (int)(o & 31);
+    const long i = (o >> 5) & 255;
+    const long blk = o >> 13;                   // (row tile, k stage)
+    const long ks = blk % (d / 32), rt = blk / (d / 32);
+    const long r = rt * 256 + i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < V) v = *reinterpret_cast<const uint4*>(E + r * d + ks * 32 + c);
+    *reinterpret_cast<uint4*>(out + o) = v;
+}
+
+// E^T in the blocked layout (rows d, a multiple of 256; K = V): one
+// workgroup per 16 KiB output block, 32 rows of E through LDS.
+__global__ __launch_bounds__(256) void embed_t_tile_kernel(const bf16_t* __restrict__ E, int V,
+                                                           int d, bf16_t* __restrict__ out) {
+    __shared__ bf16_t t[32][256 + 8];
+    const int vs = blockIdx.x, dt = blockIdx.y;         // v stage (32 entries), d tile (256)
+    for (int x = threadIdx.x; x < 32 * 32; x += 256) {  // 32 rows x 32 chunks of 8
+        const int j = x / 32, c = (x % 32) * 8;
+        const long v = (long)vs * 32 + j;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (v < V) val = *reinterpret_cast<const uint4*>(E + v * d + (long)dt * 256 + c);
+        const bf16_t* p = reinterpret_cast<const bf16_t*>(&val);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[j][c + e] = p[e];
+    }
+    __syncthreads();
+    const int i = threadIdx.x;                          // row dt*256 + i of E^T
+    bf16_t row[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) row[j] = t[j][i];
+    bf16_t* o = out + tiled_index((long)dt * 256 + i, (long)vs * 32, V);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(o + 8 * q) = *reinterpret_cast<const uint4*>(row + 8 * q);
 }
 
 // 64x64 tiles through LDS.
@@ -182,10 +255,31 @@ hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int co
 }
 
 hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, const int32_t* halt, hipStream_t st) {
+                             int V, const int32_t* halt, int tiled, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(softmax_rows_kernel, dim3(cdiv(V / 4, 1024), rows), dim3(256), 0, st, logits,
-                       stats, out, V, halt);
+                       stats, out, V, halt, tiled);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm_tiled(const float* h, const float* w, uint16_t* u, int rows, int d, float eps,
+                         hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_tiled_kernel, dim3(rows), dim3(256), 0, st, h, w, u, d, eps);
+    return hipGetLastError();
+}
+
+hipError_t embed_tile(const uint16_t* E, int V, int d, int transpose, uint16_t* out,
+                      hipStream_t st) {
+    if (transpose) {
+        if (d % 256 || V % 32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(embed_t_tile_kernel, dim3(V / 32, d / 256), dim3(256), 0, st, E, V, d, out);
+    } else {
+        if (d % 32) return hipErrorInvalidValue;
+        const long chunks = (long)cdiv(V, 256) * 256 * d / 8;
+        hipLaunchKernelGGL(embed_tile_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                           E, V, d, out, chunks);
+    }
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_barrier();
 }
 
-template <int EPI>
+template <int EPI, int TA, int TB>
 __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
     if (g.halt && *g.halt) return;
     __shared__ __align__(1024) unsigned char a0[STAGE_BYTES], b0[STAGE_BYTES];
@@ -98,23 +98,38 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
     const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
     const int pr = lane >> 2;
     const int pc = ((lane & 3) ^ swz(pr)) * 8;
-    const long ar0 = min(m0 + 32 * wave + pr, g.M - 1), ar1 = min(m0 + 32 * wave + 16 + pr, g.M - 1);
-    const long br0 = min(n0 + 32 * wave + pr, g.N - 1), br1 = min(n0 + 32 * wave + 16 + pr, g.N - 1);
-    const bf16_t* pa0 = A + ar0 * g.lda + kbeg + pc;
-    const bf16_t* pa1 = A + ar1 * g.lda + kbeg + pc;
-    const bf16_t* pb0 = B + br0 * g.ldb + kbeg + pc;
-    const bf16_t* pb1 = B + br1 * g.ldb + kbeg + pc;
+    // row-major: rows clamped to the last valid row; tiled: the padded
+    // rows exist, and a stage of a 256-row tile is one 16 KiB block
+    const bf16_t *pa0, *pa1, *pb0, *pb1;
+    if (TA) {
+        pa0 = A + tiled_index(m0 + 32 * wave + pr, kbeg, g.K) + pc;
+        pa1 = pa0 + 16 * 32;
+    } else {
+        const long ar0 = min(m0 + 32 * wave + pr, g.M - 1), ar1 = min(m0 + 32 * wave + 16 + pr, g.M - 1);
+        pa0 = A + ar0 * g.lda + kbeg + pc;
+        pa1 = A + ar1 * g.lda + kbeg + pc;
+    }
+    if (TB) {
+        pb0 = B + tiled_index(n0 + 32 * wave + pr, kbeg, g.K) + pc;
+        pb1 = pb0 + 16 * 32;
+    } else {
+        const long br0 = min(n0 + 32 * wave + pr, g.N - 1), br1 = min(n0 + 32 * wave + 16 + pr, g.N - 1);
+        pb0 = B + br0 * g.ldb + kbeg + pc;
+        pb1 = B + br1 * g.ldb + kbeg + pc;
+    }
+    constexpr int SA_STRIDE = TA ? 256 * BK : BK;      // elements from one stage to the next
+    constexpr int SB_STRIDE = TB ? 256 * BK : BK;
     const int blk0 = 2 * wave * 1024;
 
 #define DG_ISSUE(s, SA, SB)                                                                       \
     {                                                                                             \
         int sr_ = (s) + rot;                                                                      \
         if (sr_ >= n) sr_ -= n;                                                                   \
-        const int ko_ = sr_ * BK;                                                                 \
-        __builtin_amdgcn_global_load_lds((glb_void*)(pa0 + ko_), (lds_void*)((SA) + blk0), 16, 0, 0);        \
-        __builtin_amdgcn_global_load_lds((glb_void*)(pb0 + ko_), (lds_void*)((SB) + blk0), 16, 0, 0);        \
-        __builtin_amdgcn_global_load_lds((glb_void*)(pa1 + ko_), (lds_void*)((SA) + blk0 + 1024), 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds((glb_void*)(pb1 + ko_), (lds_void*)((SB) + blk0 + 1024), 16, 0, 0); \
+        const long ka_ = (long)sr_ * SA_STRIDE, kb_ = (long)sr_ * SB_STRIDE;                      \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pa0 + ka_), (lds_void*)((SA) + blk0), 16, 0, 0);        \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pb0 + kb_), (lds_void*)((SB) + blk0), 16, 0, 0);        \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pa1 + ka_), (lds_void*)((SA) + blk0 + 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pb1 + kb_), (lds_void*)((SB) + blk0 + 1024), 16, 0, 0); \
     }
 
     f32x4_t acc[8][4];
@@ -215,7 +230,8 @@ bool gemm_dma_ok(const GemmArgs& g, int epi) {
     if (g.a_rows || g.M <= 0 || g.N <= 0) return false;
     // whole rings of four stages in every k-range
     if (g.K % (4 * BK) || g.k_split % (4 * BK)) return false;
-    if (g.lda % 8 || g.ldb % 8) return false;
+    if ((!g.a_tiled && g.lda % 8) || (!g.b_tiled && g.ldb % 8)) return false;
+    if ((g.a_tiled || g.b_tiled) && g.K % 32) return false;
     // four-column stores of the output
     if (g.N % 4 || g.ldc % 4 || ((uintptr_t)g.C & 15)) return false;
     if (((uintptr_t)g.A | (uintptr_t)g.B) & 15) return false;
@@ -225,10 +241,18 @@ bool gemm_dma_ok(const GemmArgs& g, int epi) {
 hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st) {
     if (!gemm_dma_ok(g, epi)) return hipErrorInvalidValue;
     dim3 grid(cdiv(g.N, BN), cdiv(g.M, BM), splits);
-    if (epi == EPI_STORE_F32)
-        hipLaunchKernelGGL(gemm_dma_kernel<EPI_STORE_F32>, grid, dim3(WAVES * 64), 0, st, g);
-    else
-        hipLaunchKernelGGL(gemm_dma_kernel<EPI_SPLITK>, grid, dim3(WAVES * 64), 0, st, g);
+#define DG_LAUNCH(E, TA_, TB_) hipLaunchKernelGGL((gemm_dma_kernel<E, TA_, TB_>), grid, dim3(WAVES * 64), 0, st, g)
+    const int t = (g.a_tiled ? 1 : 0) | (g.b_tiled ? 2 : 0);
+    if (epi == EPI_STORE_F32) {
+        if (t == 3) DG_LAUNCH(EPI_STORE_F32, 1, 1);
+        else if (t == 0) DG_LAUNCH(EPI_STORE_F32, 0, 0);
+        else return hipErrorInvalidValue;
+    } else {
+        if (t == 3) DG_LAUNCH(EPI_SPLITK, 1, 1);
+        else if (t == 0) DG_LAUNCH(EPI_SPLITK, 0, 0);
+        else return hipErrorInvalidValue;
+    }
+#undef DG_LAUNCH
     return hipGetLastError();
 }
 

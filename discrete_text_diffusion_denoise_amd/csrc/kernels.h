@@ -35,7 +35,18 @@ struct GemmArgs {
     const void* B2 = nullptr;
     const void* B3 = nullptr;
     int n_b2 = 0, n_b3 = 0;
+    // bf16 ring kernel: operand stored in 256 x 32 blocks (see tiled_index);
+    // lda / ldb are then ignored and the row count is padded to 256
+    int a_tiled = 0, b_tiled = 0;
 };
+
+// Blocked layout of a bf16 matrix [R][K] (K a multiple of 32, R padded to a
+// multiple of 256): rows in tiles of 256, each tile's K in stages of 32, one
+// stage of one tile = 256 rows x 32 values = 16 KiB, contiguous.  Element
+// (r, k) sits at ((r / 256 * (K / 32) + k / 32) * 256 + r % 256) * 32 + k % 32.
+__host__ __device__ __forceinline__ long tiled_index(long r, long k, long K) {
+    return (((r >> 8) * (K >> 5) + (k >> 5)) * 256 + (r & 255)) * 32 + (k & 31);
+}
 
 // Row n of the (segmented) B operand, in elements of type E.
 template <typename E>
@@ -70,7 +81,14 @@ hipError_t splitk_epilogue(const GemmArgs& g, const float* part, int splits, int
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t st);
 // halt: when non-null and *halt != 0 the kernel does nothing
 hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, const int32_t* halt, hipStream_t st);
+                             int V, const int32_t* halt, int tiled, hipStream_t st);
+// RMSNorm into the blocked bf16 layout (tiled_index over [rows][d])
+hipError_t rmsnorm_tiled(const float* h, const float* w, uint16_t* u, int rows, int d, float eps,
+                         hipStream_t st);
+// E [V][d] (bf16) into the blocked layout of E (transpose 0: rows V padded to
+// 256, K = d) or of E^T (transpose 1: rows d, K = V; d % 256 == 0, V % 32 == 0)
+hipError_t embed_tile(const uint16_t* E, int V, int d, int transpose, uint16_t* out,
+                      hipStream_t st);
 // u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T; also fp32 into u32 if set)
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,

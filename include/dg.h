@@ -97,11 +97,13 @@ typedef struct {
 
 typedef struct {
     const void* embed;       /* [V][d] tied embedding / output head                    */
-    const void* embed_t;     /* [d][V] the same matrix transposed (dg_embed_transpose); */
-                             /* required for self-conditioning, else may be NULL       */
+    const void* embed_t;     /* E^T for self-conditioning, written by dg_embed_transpose */
+                             /* (layout below); required for it, else may be NULL      */
     const void* w_sc;        /* [d][d] self-conditioning projection                    */
     const float* final_norm; /* [d]                                                    */
     const dg_layer_weights* layers; /* host array [n_layers], copied at create        */
+    const void* embed_head;  /* optional: E in the blocked layout (dg_embed_head); NULL */
+                             /* = the head reads `embed`                              */
 } dg_weights;
 
 typedef struct {
@@ -130,9 +132,26 @@ const char* dg_last_error(void);
 dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** out);
 void dg_model_destroy(dg_model* m);
 
-/* Writes d_out [d][V] = embed^T (the layout the self-conditioning product
- * streams).  d_out must hold vocab*d_model elements of the model dtype. */
+/* Blocked layout (bf16 models with d_model % 256 == 0 and vocab % 128 == 0):
+ * a matrix [R][K] is stored as tiles of 256 rows, each tile's K in stages of
+ * 32 values; one stage of one tile (256 x 32 values, 16 KiB) is contiguous,
+ * element (r, k) at ((r/256 * K/32 + k/32) * 256 + r%256) * 32 + k%32, with R
+ * padded to a multiple of 256.  The vocabulary products stream their weight
+ * one contiguous block per stage (youleyou.com article, "Deployment": the
+ * step is bound by memory traffic, not arithmetic).
+ *
+ * Writes the self-conditioning operand E^T [d][V] from d_embed [V][d]: in the
+ * blocked layout for blocked models, else row-major.  d_out holds
+ * vocab*d_model elements of the model dtype.  Errors: DG_ERR_ARG on NULL. */
 dg_status dg_embed_transpose(const dg_model* m, const void* d_embed, void* d_out, void* stream);
+/* Bytes of the blocked head operand of this model (E [V][d] in the blocked
+ * layout, V padded to a multiple of 256), or 0 when the model's head reads
+ * `embed` directly (not a blocked model). */
+dg_status dg_embed_head_bytes(const dg_model* m, size_t* bytes);
+/* Writes that operand from d_embed [V][d] into d_out (dg_embed_head_bytes
+ * bytes); pass it as weights.embed_head.  DG_ERR_UNSUPPORTED for models that
+ * are not blocked, DG_ERR_ARG on NULL. */
+dg_status dg_embed_head(const dg_model* m, const void* d_embed, void* d_out, void* stream);
 
 /* ---------------------------------------------------------------- KV cache */
 /* Bytes of a KV cache for `batch` sequences of up to `capacity` positions:
