@@ -56,8 +56,9 @@ __device__ __forceinline__ float dexp(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    const int k = (int)kf;
-    const float v = p * __uint_as_float((uint32_t)(k + 127) << 23);
+    // p * 2^k: for x >= -87, k >= -126 and p > 1, so the product is a normal
+    // number and scaling the exponent (ldexp) is the same exact result
+    const float v = __builtin_amdgcn_ldexpf(p, (int)kf);
     return x >= -87.0f ? v : 0.0f;
 }
 
@@ -199,16 +200,18 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
             x[4 * d + 2] = v.z;
             x[4 * d + 3] = v.w;
         }
-        // chunk max and first argmax, in member order
+        // chunk max (each entry replaces it only if strictly greater, in
+        // member order), then the first member equal to it: the same first
+        // argmax as tracking both in one pass, since the max is attained
+        // first there (+0 and -0 compare equal in both passes; NaN is never
+        // taken, and a NaN first entry leaves the max NaN and the argmax 0)
         float m = x[0];
-        int j = k0;
 #pragma unroll
-        for (int u = 1; u < 4 * NDEPTH; ++u) {
-            const int k = k0 + 4 * NLANE * (u / 4) + (u % 4);
-            const bool gt = x[u] > m;
-            m = gt ? x[u] : m;
-            j = gt ? k : j;
-        }
+        for (int u = 1; u < 4 * NDEPTH; ++u) m = x[u] > m ? x[u] : m;
+        int ju = 0;
+#pragma unroll
+        for (int u = 4 * NDEPTH - 1; u > 0; --u) ju = x[u] == m ? u : ju;
+        const int j = k0 + 4 * NLANE * (ju / 4) + (ju % 4);
         float sum = 0.0f, ac = 0.0f;
         if (invT != 1.0f) {
 #pragma unroll
