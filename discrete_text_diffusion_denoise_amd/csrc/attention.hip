@@ -30,6 +30,15 @@ template <typename T> struct AttnLds {
     static constexpr int CE = 16 / (int)sizeof(T);    // elements per 16-byte chunk
 };
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that waits only for this wave's LDS traffic (global
+// loads in flight stay in flight).
+__device__ __forceinline__ void attn_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+}
+
 // V^T fragment: row d, keys {4g..4g+3} and {16+4g..16+4g+3}.
 __device__ __forceinline__ void load_vt(Frag<bf16_t>& f, const bf16_t* row, int g4) {
     uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * g4);
@@ -50,7 +59,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     constexpr int NQF = DH / 32;   // Q fragments (k-steps over dh)
     constexpr int NOT = DH / 16;   // O^T tiles over dh
     __shared__ __align__(16) T Ks[KT * KROW];
-    __shared__ __align__(16) T Vt[DH * VROW];
+    // bf16: V kept as it is in the cache, [key][dh] with rows padded to
+    // DH + 16 (the four key rows one transposed read touches fall in
+    // distinct banks), read transposed by ds_read_b64_tr_b16; fp32: V^T
+    // written element by element
+    constexpr bool TRV = sizeof(T) == 2;
+    constexpr int VRROW = DH + 16;
+    __shared__ __align__(16) T Vt[TRV ? KT * VRROW : DH * VROW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -97,23 +112,46 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const T* Kc = reinterpret_cast<const T*>(a.kc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
     const T* Vc = reinterpret_cast<const T*>(a.vc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
     constexpr int CHUNKS = KT * DH / L::CE;   // 16-byte chunks per K (or V) tile
+    constexpr int NC = CHUNKS / 256;          // per thread
+    static_assert(NC >= 1 && CHUNKS % 256 == 0, "tile chunks must split over the workgroup");
 
+    // This thread's chunks of a tile are loaded one tile ahead into
+    // registers (kr, vr): the loads of tile t+1 are in flight while tile t
+    // is multiplied.  The barriers wait only for LDS traffic, so those loads
+    // stay outstanding across them; their first use (the LDS store of the
+    // next pass) waits for them.
+    uint4 kr[NC], vr[NC];
+#define ATT_GLOAD(K0)                                                                         \
+    _Pragma("unroll") for (int c = 0; c < NC; ++c) {                                          \
+        const int ch = tid + c * 256;                                                         \
+        const int key = ch / (DH / L::CE);                                                    \
+        const int d0 = (ch % (DH / L::CE)) * L::CE;                                           \
+        kr[c] = make_uint4(0, 0, 0, 0);                                                       \
+        vr[c] = kr[c];                                                                        \
+        if ((K0) + key < ke) {                                                                \
+            kr[c] = *reinterpret_cast<const uint4*>(Kc + (long)((K0) + key) * DH + d0);       \
+            vr[c] = *reinterpret_cast<const uint4*>(Vc + (long)((K0) + key) * DH + d0);       \
+        }                                                                                     \
+    }
+    if (kb < ke) ATT_GLOAD(kb);
     for (int k0 = kb; k0 < ke; k0 += KT) {
-        __syncthreads();
-        for (int c = tid; c < CHUNKS; c += 256) {
-            const int key = c / (DH / L::CE);
-            const int d0 = (c % (DH / L::CE)) * L::CE;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (k0 + key < ke) {
-                kv = *reinterpret_cast<const uint4*>(Kc + (long)(k0 + key) * DH + d0);
-                vv = *reinterpret_cast<const uint4*>(Vc + (long)(k0 + key) * DH + d0);
-            }
-            *reinterpret_cast<uint4*>(&Ks[key * KROW + d0]) = kv;
-            const T* vp = reinterpret_cast<const T*>(&vv);
+        attn_barrier();
 #pragma unroll
-            for (int i = 0; i < L::CE; ++i) Vt[(d0 + i) * VROW + key] = vp[i];
+        for (int c = 0; c < NC; ++c) {
+            const int ch = tid + c * 256;
+            const int key = ch / (DH / L::CE);
+            const int d0 = (ch % (DH / L::CE)) * L::CE;
+            *reinterpret_cast<uint4*>(&Ks[key * KROW + d0]) = kr[c];
+            if constexpr (TRV) {
+                *reinterpret_cast<uint4*>(&Vt[key * VRROW + d0]) = vr[c];
+            } else {
+                const T* vp = reinterpret_cast<const T*>(&vr[c]);
+#pragma unroll
+                for (int i = 0; i < L::CE; ++i) Vt[(d0 + i) * VROW + key] = vp[i];
+            }
         }
-        __syncthreads();
+        attn_barrier();
+        if (k0 + KT < ke) ATT_GLOAD(k0 + KT);
 
         // S^T for 32 keys: lane holds keys kt*16 + 4*g4 + e of query r16
         f32x4_t sc[2];
@@ -159,10 +197,25 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[dt][e] *= corr;
             Frag<T> vf;
-            load_vt(vf, &Vt[(dt * 16 + r16) * VROW], g4);
+            if constexpr (TRV) {
+                // lane j of a 16-lane group gives the address of keys
+                // 4*g4 + j/4 (+16), dh dt*16 + 4*(j%4) .. +3; lane 4a+b then
+                // receives dh dt*16 + 4a+b of keys 4*g4 + 0..3 (+16): row r16,
+                // the same keys as its probabilities
+                typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+                const T* vb = &Vt[(4 * g4 + (r16 >> 2)) * VRROW + dt * 16 + 4 * (r16 & 3)];
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 16 * VRROW));
+                vf.v = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                  __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+            } else {
+                load_vt(vf, &Vt[(dt * 16 + r16) * VROW], g4);
+            }
             mma(o[dt], vf, pf);
         }
     }
+
+#undef ATT_GLOAD
 
     // lane holds O^T[d = dt*16 + 4*g4 + e][query r16]
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
