@@ -13,6 +13,7 @@
 // already sit in the B-operand layout of O^T = V^T P^T.  Long key ranges are
 // split across workgroups and merged by a second kernel.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
@@ -268,8 +269,12 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
     const int G = Hq / Hkv;
     const long base = (long)cdiv(G * cdiv(n, 16), 4) * Hkv * B;
     int splits = 1;
+    static const int target = [] {
+        const char* e = getenv("DG_ATTN_WG");   // sweeps: workgroups to aim for
+        return e ? std::max(1, atoi(e)) : 640;
+    }();
     if (!causal && kv_len > 256) {
-        splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(640, (int)base)));
+        splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(target, (int)base)));
         splits = std::min(splits, std::min(32, std::max(1, max_splits)));
     }
     int len = cdiv(cdiv(kv_len, splits), KT) * KT;
