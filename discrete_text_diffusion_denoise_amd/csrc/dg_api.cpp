@@ -297,6 +297,31 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
         DG_HIP(dg::gemm_stream(g, epi, 4, 1, st));
         return DG_OK;
     }
+    if (bf) {
+        // canvas-size bf16 projection: skinny ring kernel over 256 x 64 tiles,
+        // split over K into 128-multiples, then the ordered split-K pass
+        static const int target = [] {
+            const char* e = getenv("DG_SKINNY_WG");   // sweeps: workgroups to aim for
+            return e ? std::max(1, atoi(e)) : 192;
+        }();
+        dg::GemmArgs p = g;
+        const long stiles = (long)cdiv(N, 64) * cdiv(M, 256);
+        int sp = (int)std::min<long>(std::max<long>(1, cdiv(target, (int)stiles)),
+                                     std::max(1, K / 128));
+        p.k_split = cdiv(cdiv(K, sp), 128) * 128;
+        int used = cdiv(K, p.k_split);
+        while (used > 1 && (size_t)used * M * N > kSplitPartFloats) {
+            p.k_split += 128;
+            used = cdiv(K, p.k_split);
+        }
+        p.C = s.gp;
+        p.ldc = N;
+        if ((size_t)used * M * N <= kSplitPartFloats && dg::gemm_skinny_ok(p)) {
+            DG_HIP(dg::gemm_skinny_splitk(p, used, st));
+            DG_HIP(dg::splitk_epilogue(g, s.gp, used, epi, st));
+            return DG_OK;
+        }
+    }
     const long tiles = (long)cdiv(N, 64) * mt;
     int splits = (int)std::min<long>(std::max<long>(1, cdiv(320, (int)tiles)), std::max(1, K / 256));
     while (splits > 1 && (size_t)splits * M * N > kSplitPartFloats) --splits;

@@ -217,6 +217,124 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
     }
 }
 
+// Skinny variant for the canvas-size projections (Q/K/V, O, W_sc): a
+// 256 x 64 output tile per workgroup, four waves of 64 x 64, the same
+// four-stage direct-to-LDS ring over row-major operands, split-K partials
+// out (the split-K pass applies the projection's epilogue).  Two workgroups
+// fit per CU (80 KiB of LDS each).
+constexpr int SBN = 64;
+constexpr int SA_BYTES = BM * BK * 2;    // 16 KiB
+constexpr int SB_BYTES = SBN * BK * 2;   // 4 KiB
+
+__global__ __launch_bounds__(256) void gemm_dma_skinny_kernel(GemmArgs g) {
+    __shared__ __align__(1024) unsigned char a0[SA_BYTES], b0[SB_BYTES];
+    __shared__ __align__(1024) unsigned char a1[SA_BYTES], b1[SB_BYTES];
+    __shared__ __align__(1024) unsigned char a2[SA_BYTES], b2[SB_BYTES];
+    __shared__ __align__(1024) unsigned char a3[SA_BYTES], b3[SB_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;                 // 64-row band of the tile
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int n0 = blockIdx.x * SBN;
+    const int m0 = blockIdx.y * BM;
+    const int kz = blockIdx.z;
+    const int kbeg = kz * g.k_split;
+    const int kend = min(g.K, kbeg + g.k_split);
+    const int n = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg) / BK : 0);
+
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
+    const int pr = lane >> 2;
+    const int pc = ((lane & 3) ^ swz(pr)) * 8;
+    // this wave fills A blocks 4*wave .. 4*wave+3 and B block `wave`
+    const bf16_t* pa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const long r = min(m0 + (4 * wave + q) * 16 + pr, g.M - 1);
+        pa[q] = A + r * g.lda + kbeg + pc;
+    }
+    const long brow = min(n0 + wave * 16 + pr, g.N - 1);
+    const bf16_t* pb = b_row<bf16_t>(g, (int)brow) + kbeg + pc;
+
+#define SK_ISSUE(s, SA, SB)                                                                      \
+    {                                                                                            \
+        const int k_ = (s) * BK;                                                                 \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                            \
+            __builtin_amdgcn_global_load_lds((glb_void*)(pa[q] + k_),                            \
+                                             (lds_void*)((SA) + (4 * wave + q) * 1024), 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds((glb_void*)(pb + k_), (lds_void*)((SB) + wave * 1024),  \
+                                         16, 0, 0);                                              \
+    }
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int roff = r16 * 64 + ((g4 ^ swz(r16)) << 4);
+#define SK_COMPUTE(SA, SB)                                                                       \
+    {                                                                                            \
+        u32x4 f0, f1, f2, f3, e0, e1, e2, e3;                                                    \
+        const uint32_t qa_ = lds_addr(SA) + wave * 4096 + roff, qb_ = lds_addr(SB) + roff;       \
+        asm volatile(                                                                            \
+            "ds_read_b128 %0, %8 offset:0\n ds_read_b128 %1, %8 offset:1024\n"                    \
+            "ds_read_b128 %2, %8 offset:2048\n ds_read_b128 %3, %8 offset:3072\n"                 \
+            "ds_read_b128 %4, %9 offset:0\n ds_read_b128 %5, %9 offset:1024\n"                    \
+            "ds_read_b128 %6, %9 offset:2048\n ds_read_b128 %7, %9 offset:3072\n"                 \
+            "s_waitcnt lgkmcnt(0)"                                                                \
+            : "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(e0), "=&v"(e1), "=&v"(e2),        \
+              "=&v"(e3)                                                                          \
+            : "v"(qa_), "v"(qb_)                                                                 \
+            : "memory");                                                                         \
+        const u32x4 fa_[4] = {f0, f1, f2, f3};                                                   \
+        const u32x4 fb_[4] = {e0, e1, e2, e3};                                                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                        \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                             \
+                    __builtin_bit_cast(bf16x8_t, fb_[j]), __builtin_bit_cast(bf16x8_t, fa_[i]),  \
+                    acc[i][j], 0, 0, 0);                                                         \
+    }
+#define SK_STAGE(t, CA, CB, NA, NB)          \
+    {                                        \
+        if ((t) + 2 < n)                     \
+            DG_WAIT_VM(10);                  \
+        else if ((t) + 1 < n)                \
+            DG_WAIT_VM(5);                   \
+        else                                 \
+            DG_WAIT_VM(0);                   \
+        barrier_lds();                       \
+        if ((t) + 3 < n) SK_ISSUE((t) + 3, NA, NB); \
+        SK_COMPUTE(CA, CB);                  \
+    }
+
+    if (n > 0) SK_ISSUE(0, a0, b0);
+    if (n > 1) SK_ISSUE(1, a1, b1);
+    if (n > 2) SK_ISSUE(2, a2, b2);
+    for (int t = 0; t < n; t += 4) {
+        SK_STAGE(t, a0, b0, a3, b3);
+        SK_STAGE(t + 1, a1, b1, a0, b0);
+        SK_STAGE(t + 2, a2, b2, a1, b1);
+        SK_STAGE(t + 3, a3, b3, a2, b2);
+    }
+#undef SK_STAGE
+#undef SK_COMPUTE
+#undef SK_ISSUE
+
+    // split-K partial: lane holds row 16i + r16, columns 16j + 4*g4 .. +3
+    float* C = reinterpret_cast<float*>(g.C) + (long)kz * g.M * g.ldc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wave * 64 + 16 * i + r16;
+        if (row >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 16 * j + 4 * g4;
+            if (col < g.N) *reinterpret_cast<f32x4_t*>(C + (long)row * g.ldc + col) = acc[i][j];
+        }
+    }
+}
+
 }  // namespace
 
 bool gemm_dma_ok(const GemmArgs& g, int epi) {
@@ -225,7 +343,9 @@ bool gemm_dma_ok(const GemmArgs& g, int epi) {
         const char* e = getenv("DG_DMA");
         enabled = e ? atoi(e) : 1;
     }
-    if (!enabled) return false;
+    // DG_DMA=0 (sweeps) only turns the ring off for row-major operands:
+    // blocked operands exist for this kernel alone
+    if (!enabled && !g.a_tiled && !g.b_tiled) return false;
     if (epi != EPI_STORE_F32 && epi != EPI_SPLITK) return false;
     if (g.a_rows || g.M <= 0 || g.N <= 0) return false;
     // whole rings of four stages in every k-range
@@ -253,6 +373,27 @@ hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st)
         else return hipErrorInvalidValue;
     }
 #undef DG_LAUNCH
+    return hipGetLastError();
+}
+
+bool gemm_skinny_ok(const GemmArgs& g) {
+    static int enabled = -1;
+    if (enabled < 0) {
+        const char* e = getenv("DG_DMA");
+        enabled = e ? atoi(e) : 1;
+    }
+    if (!enabled || g.a_rows || g.M <= 0 || g.N <= 0 || g.a_tiled || g.b_tiled) return false;
+    if (g.K % (4 * BK) || g.k_split % (4 * BK)) return false;
+    if (g.lda % 8 || g.ldb % 8 || g.N % 4 || g.ldc % 4) return false;
+    if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return false;
+    if ((g.B2 && ((uintptr_t)g.B2 & 15)) || (g.B3 && ((uintptr_t)g.B3 & 15))) return false;
+    return true;
+}
+
+hipError_t gemm_skinny_splitk(const GemmArgs& g, int splits, hipStream_t st) {
+    if (!gemm_skinny_ok(g)) return hipErrorInvalidValue;
+    dim3 grid(cdiv(g.N, SBN), cdiv(g.M, BM), splits);
+    hipLaunchKernelGGL(gemm_dma_skinny_kernel, grid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
 

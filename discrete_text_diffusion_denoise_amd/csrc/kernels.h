@@ -67,6 +67,11 @@ hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_
 // no row gather.
 bool gemm_dma_ok(const GemmArgs& g, int epi);
 hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st);
+// Skinny ring kernel (256 x 64 tiles, row-major bf16 operands, segmented B
+// allowed): writes split-K partials C[kz][M][ldc]; K and k_split multiples
+// of 128.
+bool gemm_skinny_ok(const GemmArgs& g);
+hipError_t gemm_skinny_splitk(const GemmArgs& g, int splits, hipStream_t st);
 
 // Streaming bf16 GEMM (M <= 256 per row tile): all rows of a tile share the A
 // slice in LDS, each wave streams 16*tn columns of B (tn = 1 or 4).
