@@ -79,6 +79,9 @@ _SIGS = {
     "dg_encode_prompt": (_I, [_P, _P, _I, _P, _I, _P, _SZ, _P]),
     "dg_denoise_step": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_sample_update": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_sample_update_probs": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                    _SZ, _P]),
+    "dg_stage_probs": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "dg_canvas_init": (_I, [_U64, _I, _I, _I, _I, _P, _P]),
     "dg_commit_block": (_I, [_P, _P, _I, _P, _P, _SZ, _P]),
     "dg_generate_workspace_bytes": (_I, [_P, _I, _P]),
@@ -87,6 +90,7 @@ _SIGS = {
     "dg_stage_attention": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "dg_stage_moe": (_I, [_P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_stage_head": (_I, [_P, _I, _P, _P, _P, _SZ, _P]),
+    "dg_stage_head_rowmax": (_I, [_P, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_timer_enable": (_I, [ctypes.c_uint32]),
     "dg_timer_read": (_I, [_I, _P, _P]),
 }
@@ -283,6 +287,12 @@ class Model:
         _check(lib().dg_stage_head(self.handle, h.shape[0], _ptr(h), _ptr(logits), _ptr(self.ws),
                                    self.ws.numel(), _stream(stream)))
 
+    def stage_head_rowmax(self, h, logits, rowmax, stream=None):
+        """dg_stage_head_rowmax: also rowmax [T, V/64] f32 (slab maxima)."""
+        _check(lib().dg_stage_head_rowmax(self.handle, h.shape[0], _ptr(h), _ptr(logits),
+                                          _ptr(rowmax), _ptr(self.ws), self.ws.numel(),
+                                          _stream(stream)))
+
 
 # ------------------------------------------------------------------ model-free calls
 
@@ -301,6 +311,25 @@ def sample_update(params: dict, step: int, logits, canvas, argmax, lock, stats, 
     _check(lib().dg_sample_update(ctypes.byref(sp), int(step), B, N, V, _ptr(logits),
                                   _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats), _ptr(stop),
                                   _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def sample_update_probs(params: dict, step: int, logits, canvas, argmax, lock, stats, stop,
+                        rowmax, probs, ws, blocked: bool = True, stream=None):
+    """dg_sample_update_probs: sample_update, and probs (bf16 storage; blocked
+    layout over B*N rows padded to 256, or row-major) from rowmax [B*N, V/64] f32."""
+    B, N, V = logits.shape
+    sp = sampler_params(params)
+    _check(lib().dg_sample_update_probs(ctypes.byref(sp), int(step), B, N, V, _ptr(logits),
+                                        _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats),
+                                        _ptr(stop), _ptr(rowmax), 1 if blocked else 0, _ptr(probs),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def stage_probs(logits, stats, probs, blocked: bool, stream=None):
+    """dg_stage_probs: logits [T, V] f32, stats [T, 4] f32 -> probs (bf16 storage)."""
+    T, V = logits.shape
+    _check(lib().dg_stage_probs(T, V, 1 if blocked else 0, _ptr(logits), _ptr(stats), _ptr(probs),
+                                _stream(stream)))
 
 
 def timer_enable(names) -> None:

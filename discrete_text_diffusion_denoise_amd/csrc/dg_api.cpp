@@ -160,7 +160,15 @@ struct Scratch {
     float* gp;        // split-K partials of the small projections
     void* probs;      // bf16 models: softmax(prev logits) in bf16 for self-conditioning
     void* ut;         // blocked models: final-normed rows for the head, blocked layout
+    int ut_rows = 0;  // rows `ut` holds (the canvas tokens, padded to 256)
+    int probs_tiled = 0;  // `probs` in the 64-wide blocked layout (else row-major)
     float* u32;       // bf16 models: fp32 normalised activations for the router
+    float* tmax;      // blocked models: head GEMM row maxima per 64-column slab
+    // set by the block loop (not carved): the head GEMM writes its slab
+    // maxima (fuse), and the probabilities of the previous round's logits are
+    // already in `probs`, written by the sampler (probs_ready)
+    bool fuse = false;
+    bool probs_ready = false;
     // set by the block loop (not carved): when *halt != 0 every sequence of
     // the batch has stopped and the heavy kernels of a round skip their work
     const int32_t* halt = nullptr;
@@ -211,10 +219,13 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     // rows padded to 256 for the blocked layout
     const size_t Tp = (size_t)cdiv((int)Tc, 256) * 256;
     s.probs = c.dtype == DG_BF16 ? cv.take_bytes(Tp * c.vocab * 2) : nullptr;
+    s.probs_tiled = m->blocked ? 1 : 0;
     s.ut = m->blocked ? cv.take_bytes(Tp * c.d_model * 2) : nullptr;
+    s.ut_rows = m->blocked ? (int)Tp : 0;
     s.tok = cv.take<int32_t>(T);
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
+    s.tmax = m->blocked ? cv.take<float>(Tc * (size_t)(c.vocab / 64)) : nullptr;
     return cv.ok;
 }
 
@@ -247,6 +258,13 @@ dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_
 int env_flag(const char* name, int dflt) {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
+}
+
+// DG_FUSE_PROBS=0 (for comparisons) keeps the separate probability pass in
+// the block loop.
+bool fuse_probs() {
+    static const int v = env_flag("DG_FUSE_PROBS", 1);
+    return v != 0;
 }
 
 // The vocabulary-sized products use the LDS-tiled GEMM unless DG_WIDE_TILE
@@ -461,10 +479,15 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         // probabilities once in bf16, then the streaming product over the
         // vocabulary split into `used` k-ranges (column tiles of a range on
         // one XCD)
-        DG_HIP(dg::softmax_rows_bf16(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab, s.halt,
-                                     m->blocked ? 1 : 0, st));
+        // unnormalised probabilities once in bf16 (the 1 / sum factor is
+        // applied in the split-K reduction); in the block loop the sampler
+        // has already written them
+        if (!s.probs_ready)
+            DG_HIP(dg::selfcond_probs(prev_logits, prev_stats, (uint16_t*)s.probs, Tn, c.vocab,
+                                      s.halt, s.probs_tiled, st));
         g.A = s.probs;
-        g.a_tiled = g.b_tiled = m->blocked ? 1 : 0;
+        g.a_tiled = s.probs_tiled ? 2 : 0;
+        g.b_tiled = m->blocked ? 1 : 0;
         g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
         g.k_rotate = env_flag("DG_KROT", 1);
         g.halt = s.halt;
@@ -478,7 +501,8 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
                      [&] { return dg::gemm_tn<T>(g, 1, dg::EPI_SPLITK, used, st); }));
     }
-    DG_HIP(dg::splitk_reduce<T>(s.sc_part, (T*)s.sc_s, used, Tn, c.d_model, st));
+    DG_HIP(dg::splitk_reduce<T>(s.sc_part, (T*)s.sc_s, used, Tn, c.d_model, st,
+                                sizeof(T) == 2 ? prev_stats : nullptr));
     DG_TRY(linear<T>(s.sc_s, Tn, c.d_model, m->w_sc, c.d_model, h, c.d_model, dg::EPI_EMBED_ADD, s,
                      st, m->embed, canvas, c.vocab));
     return DG_OK;
@@ -499,13 +523,14 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.k_split = c.d_model;
     g.k_rotate = env_flag("DG_KROT", 1);
     g.halt = s.halt;
-    if (m->blocked && m->embed_head) {
+    if (m->blocked && m->embed_head && Tn <= s.ut_rows) {
         // both operands in the blocked layout: each stage of a tile is one
         // contiguous 16 KiB block of E and of the normalised rows
         DG_HIP(dg::rmsnorm_tiled(h, m->final_norm, (uint16_t*)s.ut, Tn, c.d_model, c.rms_eps, st));
         g.A = s.ut;
         g.B = m->embed_head;
         g.a_tiled = g.b_tiled = 1;
+        if (s.fuse) g.rowmax = s.tmax;
     } else {
         DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
         g.A = s.u;
@@ -757,7 +782,8 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
                              float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
                              hipStream_t st, int32_t* nstop = nullptr,
-                             int32_t* halt = nullptr) {
+                             int32_t* halt = nullptr, const float* rowmax = nullptr,
+                             void* probs = nullptr, int probs_tiled = 1) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
@@ -800,6 +826,14 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
     a.newmax = cv.take<int32_t>((size_t)batch * canvas);
     a.nstop = nstop;
     a.halt = halt;
+    if (probs) {
+        // also write the next round's self-conditioning operand
+        if (!rowmax || vocab % 128) return fail(DG_ERR_SHAPE, "probabilities need row maxima and vocab %% 128 == 0");
+        a.rowmax = rowmax;
+        a.rowmax_n = vocab / 64;
+        a.probs = (uint16_t*)probs;
+        a.probs_tiled = probs_tiled;
+    }
     DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
     return DG_OK;
 }
@@ -811,6 +845,28 @@ dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t bat
                            void* stream) {
     return sample_impl(p, step, batch, canvas, vocab, d_logits, d_canvas, d_argmax, d_lock,
                        d_stats, d_stop, d_ws, ws_bytes, as_stream(stream));
+}
+
+dg_status dg_sample_update_probs(const dg_sampler_params* p, int32_t step, int32_t batch,
+                                 int32_t canvas, int32_t vocab, const float* d_logits,
+                                 int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                                 float* d_stats, int32_t* d_stop, const float* d_rowmax,
+                                 int32_t blocked, void* d_probs, void* d_ws, size_t ws_bytes,
+                                 void* stream) {
+    if (!d_rowmax || !d_probs) return fail(DG_ERR_ARG, "NULL argument");
+    return sample_impl(p, step, batch, canvas, vocab, d_logits, d_canvas, d_argmax, d_lock,
+                       d_stats, d_stop, d_ws, ws_bytes, as_stream(stream), nullptr, nullptr,
+                       d_rowmax, d_probs, blocked ? 1 : 0);
+}
+
+dg_status dg_stage_probs(int32_t T, int32_t vocab, int32_t blocked, const float* d_logits,
+                         const float* d_stats, void* d_probs, void* stream) {
+    if (!d_logits || !d_stats || !d_probs) return fail(DG_ERR_ARG, "NULL argument");
+    if (T < 1 || vocab < 4 || vocab % 4) return fail(DG_ERR_SHAPE, "need T >= 1 and vocab %% 4 == 0");
+    if (blocked && vocab % 64) return fail(DG_ERR_SHAPE, "the blocked layout needs vocab %% 64 == 0");
+    DG_HIP(dg::selfcond_probs(d_logits, d_stats, (uint16_t*)d_probs, T, vocab, nullptr,
+                                 blocked ? 1 : 0, as_stream(stream)));
+    return DG_OK;
 }
 
 dg_status dg_canvas_init(uint64_t seed, int32_t block_index, int32_t batch, int32_t canvas,
@@ -912,6 +968,11 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
         }
         return DG_OK;
     };
+    // Blocked models: the sampler writes the self-conditioning probabilities
+    // of round t while it reads round t's logits (the head GEMM supplies the
+    // row maxima), so round t+1 skips the separate probability pass.  The
+    // values are the same bits that pass would write.
+    s.fuse = p->selfcond_on && m->blocked && m->embed_head && fuse_probs();
     const float* prev = nullptr;
     const float* prev_stats = nullptr;
     int t = 0;
@@ -919,12 +980,14 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     for (; t < p->max_steps && !done; ++t) {
         float* logits = lg[t & 1];
         float* stats = stt[t & 1];
+        s.probs_ready = s.fuse && t > 0;
         if (c.dtype == DG_BF16)
             DG_TRY(denoise<bf16_t>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         else
             DG_TRY(denoise<float>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         DG_TRY(sample_impl(p, t, batch, c.canvas, c.vocab, logits, canvas, argmax, lock, stats,
-                           stop, sws, sws_bytes, st, nstop, halt));
+                           stop, sws, sws_bytes, st, nstop, halt, s.fuse ? s.tmax : nullptr,
+                           s.fuse ? s.probs : nullptr, s.probs_tiled));
         DG_HIP(hipMemcpyAsync(m->hflags + (size_t)(t & 1) * m->hflags_cap, stop,
                               batch * sizeof(int32_t), hipMemcpyDeviceToHost, st));
         DG_HIP(hipEventRecord(m->flag_ev[t & 1], st));
@@ -1003,6 +1066,22 @@ dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_
         DG_HIP(hipMemcpyAsync(d_gates, s.gates, (size_t)T * m->c.top_k * sizeof(float),
                               hipMemcpyDeviceToDevice, st));
     return DG_OK;
+}
+
+dg_status dg_stage_head_rowmax(dg_model* m, int32_t T, const float* d_h, float* d_logits,
+                               float* d_rowmax, void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_h || !d_logits || !d_rowmax || T < 1) return fail(DG_ERR_ARG, "bad arguments");
+    if (!m->blocked || !m->embed_head)
+        return fail(DG_ERR_UNSUPPORTED, "row maxima come from the blocked head (embed_head)");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
+    if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
+    if (T > s.ut_rows) return fail(DG_ERR_CAPACITY, "T exceeds the head's blocked row budget %d", s.ut_rows);
+    s.fuse = true;
+    s.tmax = d_rowmax;
+    return stage_head<bf16_t>(m, T, d_h, d_logits, s, as_stream(stream));
 }
 
 dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,

@@ -54,11 +54,13 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E,
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             T* __restrict__ out, int splits,
-                                                            long total) {
+                                                            long total, int cols,
+                                                            const float* __restrict__ row_stats) {
     long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     float s = 0.f;
     for (int z = 0; z < splits; ++z) s += part[(long)z * total + i];
+    if (row_stats) s = s * (1.0f / row_stats[(i / cols) * 4 + 1]);
     out[i] = Elt<T>::from_f(s);
 }
 
@@ -71,28 +73,6 @@ __global__ __launch_bounds__(256) void widen_kernel(const bf16_t* __restrict__ i
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int32_t v, long n) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = v;
-}
-
-// p = exp(l - max) / sum, written as bf16 (row-major, or in the 256 x 32
-// blocked layout when `tiled`); blockIdx.y = row, blockIdx.x = a 4096-entry
-// segment of it (enough workgroups to keep HBM busy).
-__global__ __launch_bounds__(256) void softmax_rows_kernel(const float* __restrict__ logits,
-                                                           const float* __restrict__ stats,
-                                                           bf16_t* __restrict__ out, int V,
-                                                           const int32_t* halt, int tiled) {
-    if (halt && *halt) return;
-    const long row = blockIdx.y;
-    const float m = stats[row * 4 + 0];
-    const float inv = 1.0f / stats[row * 4 + 1];
-    const float4* L = reinterpret_cast<const float4*>(logits + row * V);
-    const int end = min(V / 4, (int)(blockIdx.x + 1) * 1024);
-    for (int i = blockIdx.x * 1024 + threadIdx.x; i < end; i += 256) {
-        const float4 x = L[i];
-        const uint2 p = make_uint2(pack_bf2(__expf(x.x - m) * inv, __expf(x.y - m) * inv),
-                                   pack_bf2(__expf(x.z - m) * inv, __expf(x.w - m) * inv));
-        const long o = tiled ? tiled_index(row, 4L * i, V) : row * V + 4L * i;
-        *reinterpret_cast<uint2*>(out + o) = p;
-    }
 }
 
 // RMSNorm of fp32 rows into the blocked bf16 layout (rows padded to 256 are
@@ -246,19 +226,11 @@ hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int 
 
 template <typename T>
 hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int cols,
-                         hipStream_t st) {
+                         hipStream_t st, const float* row_stats) {
     long total = (long)rows * cols;
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)cdiv((int)total, 256)), dim3(256),
-                       0, st, part, out, splits, total);
-    return hipGetLastError();
-}
-
-hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, const int32_t* halt, int tiled, hipStream_t st) {
-    if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(softmax_rows_kernel, dim3(cdiv(V / 4, 1024), rows), dim3(256), 0, st, logits,
-                       stats, out, V, halt, tiled);
+                       0, st, part, out, splits, total, cols, row_stats);
     return hipGetLastError();
 }
 
@@ -318,7 +290,8 @@ hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int p
                                    hipStream_t, float*);                                   \
     template hipError_t embed_rows<T>(const T*, int, const int32_t*, int, int, int, float*, int, \
                                       hipStream_t);                                        \
-    template hipError_t splitk_reduce<T>(const float*, T*, int, int, int, hipStream_t);    \
+    template hipError_t splitk_reduce<T>(const float*, T*, int, int, int, hipStream_t,     \
+                                         const float*);                                    \
     template hipError_t transpose<T>(const T*, T*, int, int, hipStream_t);                 \
     template hipError_t rope_kv<T>(const float*, T*, T*, T*, int, int, int, int, int, int, \
                                    int, int, float, hipStream_t);

@@ -283,8 +283,8 @@ hipError_t launch_sized(const GemmArgs& g, int splits, hipStream_t st) {
 template <typename T>
 hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    // blocked operands exist only for the bf16 ring kernel
-    if (g.a_tiled || g.b_tiled) {
+    // blocked operands and slab maxima exist only for the bf16 ring kernel
+    if (g.a_tiled || g.b_tiled || g.rowmax) {
         if (sizeof(T) != 2 || amode != 0) return hipErrorInvalidValue;
         return gemm_dma_bf16(g, epi, splits, st);
     }

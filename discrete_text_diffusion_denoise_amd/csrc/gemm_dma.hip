@@ -101,9 +101,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
     // row-major: rows clamped to the last valid row; tiled: the padded
     // rows exist, and a stage of a 256-row tile is one 16 KiB block
     const bf16_t *pa0, *pa1, *pb0, *pb1;
-    if (TA) {
+    if (TA == 1) {
         pa0 = A + tiled_index(m0 + 32 * wave + pr, kbeg, g.K) + pc;
         pa1 = pa0 + 16 * 32;
+    } else if (TA == 2) {
+        pa0 = A + tiled64_index(m0 + 32 * wave + pr, kbeg, g.K) + pc;
+        pa1 = pa0 + 16 * 64;
     } else {
         const long ar0 = min(m0 + 32 * wave + pr, g.M - 1), ar1 = min(m0 + 32 * wave + 16 + pr, g.M - 1);
         pa0 = A + ar0 * g.lda + kbeg + pc;
@@ -125,7 +128,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
     {                                                                                             \
         int sr_ = (s) + rot;                                                                      \
         if (sr_ >= n) sr_ -= n;                                                                   \
-        const long ka_ = (long)sr_ * SA_STRIDE, kb_ = (long)sr_ * SB_STRIDE;                      \
+        const long ka_ = TA == 2 ? (long)(sr_ >> 1) * (256 * 64) + (sr_ & 1) * 32                 \
+                                 : (long)sr_ * SA_STRIDE;                                         \
+        const long kb_ = (long)sr_ * SB_STRIDE;                                                   \
         __builtin_amdgcn_global_load_lds((glb_void*)(pa0 + ka_), (lds_void*)((SA) + blk0), 16, 0, 0);        \
         __builtin_amdgcn_global_load_lds((glb_void*)(pb0 + kb_), (lds_void*)((SB) + blk0), 16, 0, 0);        \
         __builtin_amdgcn_global_load_lds((glb_void*)(pa1 + ka_), (lds_void*)((SA) + blk0 + 1024), 16, 0, 0); \
@@ -213,6 +218,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
         for (int j = 0; j < 4; ++j) {
             const int col = n0 + wn * 64 + 16 * j + 4 * g4;
             if (col < g.N) *reinterpret_cast<f32x4_t*>(C + (long)row * g.ldc + col) = acc[i][j];
+        }
+    }
+    if (EPI == EPI_STORE_F32 && g.rowmax) {
+        // maximum of each row over this wave's 64 columns: the four columns
+        // of each of the four 16-column tiles in the lane, then the four
+        // lanes (g4) that hold the same row
+        const int nslab = g.N >> 6, slab = nt * 4 + wn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float mx = acc[i][0][0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) mx = fmaxf(mx, acc[i][j][q]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const int row = m0 + wm * 128 + 16 * i + r16;
+            if (g4 == 0 && row < g.M && slab < nslab) g.rowmax[(long)row * nslab + slab] = mx;
         }
     }
 }
@@ -348,10 +371,12 @@ bool gemm_dma_ok(const GemmArgs& g, int epi) {
     if (!enabled && !g.a_tiled && !g.b_tiled) return false;
     if (epi != EPI_STORE_F32 && epi != EPI_SPLITK) return false;
     if (g.a_rows || g.M <= 0 || g.N <= 0) return false;
+    if (g.rowmax && (epi != EPI_STORE_F32 || g.N % 64)) return false;
     // whole rings of four stages in every k-range
     if (g.K % (4 * BK) || g.k_split % (4 * BK)) return false;
     if ((!g.a_tiled && g.lda % 8) || (!g.b_tiled && g.ldb % 8)) return false;
     if ((g.a_tiled || g.b_tiled) && g.K % 32) return false;
+    if (g.a_tiled == 2 && (g.K % 64 || g.k_split % 64)) return false;
     // four-column stores of the output
     if (g.N % 4 || g.ldc % 4 || ((uintptr_t)g.C & 15)) return false;
     if (((uintptr_t)g.A | (uintptr_t)g.B) & 15) return false;
@@ -362,6 +387,11 @@ hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st)
     if (!gemm_dma_ok(g, epi)) return hipErrorInvalidValue;
     dim3 grid(cdiv(g.N, BN), cdiv(g.M, BM), splits);
 #define DG_LAUNCH(E, TA_, TB_) hipLaunchKernelGGL((gemm_dma_kernel<E, TA_, TB_>), grid, dim3(WAVES * 64), 0, st, g)
+    if (g.a_tiled == 2) {   // 64-wide blocked A (the self-conditioning operand)
+        if (epi != EPI_SPLITK || !g.b_tiled) return hipErrorInvalidValue;
+        DG_LAUNCH(EPI_SPLITK, 2, 1);
+        return hipGetLastError();
+    }
     const int t = (g.a_tiled ? 1 : 0) | (g.b_tiled ? 2 : 0);
     if (epi == EPI_STORE_F32) {
         if (t == 3) DG_LAUNCH(EPI_STORE_F32, 1, 1);

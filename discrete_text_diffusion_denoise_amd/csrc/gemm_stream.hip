@@ -252,6 +252,7 @@ int stream_tm_for(int M) { return M <= 64 ? 4 : (M <= 128 ? 8 : 16); }
 hipError_t gemm_stream(const GemmArgs& g, int epi, int tn, int splits, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (g.K % 16 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0) return hipErrorInvalidValue;
+    if (g.a_tiled || g.b_tiled || g.rowmax) return hipErrorInvalidValue;
     const int tm = stream_tm_for(g.M);
     switch (epi) {
         case EPI_STORE_F32: return launch_tiles<EPI_STORE_F32>(g, tm, tn, splits, st);

@@ -35,9 +35,14 @@ struct GemmArgs {
     const void* B2 = nullptr;
     const void* B3 = nullptr;
     int n_b2 = 0, n_b3 = 0;
-    // bf16 ring kernel: operand stored in 256 x 32 blocks (see tiled_index);
-    // lda / ldb are then ignored and the row count is padded to 256
+    // bf16 ring kernel: operand stored in 256 x 32 blocks (1, see
+    // tiled_index) or, for A, 256 x 64 blocks (2, tiled64_index); lda / ldb
+    // are then ignored and the row count is padded to 256
     int a_tiled = 0, b_tiled = 0;
+    // bf16 ring kernel, EPI_STORE_F32 with N % 64 == 0: per-row maxima of
+    // each 64-column slab, rowmax[m * (N / 64) + n / 64] (the row maxima of
+    // the logits, before they are read again)
+    float* rowmax = nullptr;
 };
 
 // Blocked layout of a bf16 matrix [R][K] (K a multiple of 32, R padded to a
@@ -46,6 +51,13 @@ struct GemmArgs {
 // (r, k) sits at ((r / 256 * (K / 32) + k / 32) * 256 + r % 256) * 32 + k % 32.
 __host__ __device__ __forceinline__ long tiled_index(long r, long k, long K) {
     return (((r >> 8) * (K >> 5) + (k >> 5)) * 256 + (r & 255)) * 32 + (k & 31);
+}
+
+// The same with 64-value stages (256 rows x 64 values = 32 KiB, contiguous;
+// K a multiple of 64): one row's stage is a whole 128-byte line, which the
+// sampler's row pass writes at once.
+__host__ __device__ __forceinline__ long tiled64_index(long r, long k, long K) {
+    return (((r >> 8) * (K >> 6) + (k >> 6)) * 256 + (r & 255)) * 64 + (k & 63);
 }
 
 // Row n of the (segmented) B operand, in elements of type E.
@@ -82,11 +94,7 @@ hipError_t splitk_epilogue(const GemmArgs& g, const float* part, int splits, int
                            hipStream_t st);
 
 // ------------------------------------------------------------------ elementwise
-// out[r][v] = exp(logits[r][v] - stats[r][0]) / stats[r][1] as bf16 (V % 4 == 0)
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t st);
-// halt: when non-null and *halt != 0 the kernel does nothing
-hipError_t softmax_rows_bf16(const float* logits, const float* stats, uint16_t* out, int rows,
-                             int V, const int32_t* halt, int tiled, hipStream_t st);
 // RMSNorm into the blocked bf16 layout (tiled_index over [rows][d])
 hipError_t rmsnorm_tiled(const float* h, const float* w, uint16_t* u, int rows, int d, float eps,
                          hipStream_t st);
@@ -102,10 +110,10 @@ hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float 
 template <typename T>
 hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int B, float* h, int d,
                       hipStream_t st);
-// out[t][j] = sum_s part[s][t][j]  (T)
+// out[t][j] = sum_s part[s][t][j]  (T); with row_stats, times 1 / row_stats[t][1]
 template <typename T>
 hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int cols,
-                         hipStream_t st);
+                         hipStream_t st, const float* row_stats = nullptr);
 // out[i] = float(in[i])
 hipError_t widen_bf16(const uint16_t* in, float* out, long n, hipStream_t st);
 // out[j][v] = E[v][j]
@@ -185,8 +193,25 @@ struct SampleArgs {
     int32_t* newmax = nullptr;       // scratch [B][N] argmax of this step
     int32_t* nstop = nullptr;        // optional: count of stopped sequences
     int32_t* halt = nullptr;         // optional: set to 1 once all B have stopped
+    // optional (V % 128 == 0): also write the self-conditioning weights of
+    // the logits (selfcond_probs) as bf16 [B*N][V], 64-wide blocked
+    // (probs_tiled, tiled64_index) or row-major, the operand of the next
+    // round; the row maximum is taken from rowmax [B*N][rowmax_n] (the head
+    // GEMM's slab maxima)
+    const float* rowmax = nullptr;
+    int rowmax_n = 0;
+    uint16_t* probs = nullptr;
+    int probs_tiled = 1;
 };
 hipError_t sample_update(const SampleArgs& a, hipStream_t st);
+// Self-conditioning weights of logit rows [rows][V] with their statistics
+// (stats[r][0] = row max): bf16, row-major or 64-wide blocked (`tiled`,
+// tiled64_index, V % 64 == 0),
+// the same bits the row pass writes through SampleArgs::probs; the division
+// by stats[r][1] follows the product (splitk_reduce with row_stats).
+// V % 4 == 0.  halt: when non-null and *halt != 0 the kernel does nothing.
+hipError_t selfcond_probs(const float* logits, const float* stats, uint16_t* out, int rows, int V,
+                          const int32_t* halt, int tiled, hipStream_t st);
 hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,
                        hipStream_t st);
 

@@ -35,6 +35,8 @@ namespace dg {
 
 namespace {
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int NLANE = 1024;
 constexpr int NDEPTH = 16;
 constexpr int TILE = 4 * NLANE * NDEPTH;
@@ -61,6 +63,13 @@ __device__ __forceinline__ float dexp(float x) {
     const float v = __builtin_amdgcn_ldexpf(p, (int)kf);
     return x >= -87.0f ? v : 0.0f;
 }
+
+// Self-conditioning weight of an entry: e = E(l - m_c) against its chunk's
+// max, f = E(m_c - M) the chunk's factor against the row max; e * f is
+// exp(l - M) to within a few binary32 roundings.  The sampler's row pass and
+// the stand-alone probability pass both compute it this way, chunk by chunk,
+// so their outputs are the same bits.
+__device__ __forceinline__ float chunk_weight(float e, float f) { return e * f; }
 
 __device__ __forceinline__ float dlog(float x) {
     const float LN2_HI = 0.693145751953125f;
@@ -165,9 +174,171 @@ __device__ int pick_seq(const float* w, int n, float u) {
     return 0;
 }
 
-// One workgroup of 1024 threads per logit row.
-template <bool VEC>
-__global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
+// Raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data,
+// no swizzle).  A buffer access takes one 32-bit lane offset plus a uniform
+// offset, so the sixteen loads and stores of a tile share one address
+// register instead of a 64-bit address each.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Where a row's self-conditioning weights go: a buffer over the row's span
+// of the output, 64-wide blocked (entry k at (k / 64) * 16384 + k % 64
+// elements from the row's first one, tiled64_index) or row-major, and the
+// row max M.
+struct ProbOut {
+    __amdgpu_buffer_rsrc_t rs;
+    int tiled;
+    float M;
+    __device__ uint32_t off(uint32_t k) const {   // byte offset of entry k
+        return tiled ? 2u * (((k >> 6) << 14) + (k & 63)) : 2u * k;
+    }
+    __device__ int step() const { return tiled ? (2 << 20) : 8192; }   // entries k -> k + 4096
+};
+
+// Weights of four consecutive entries k..k+3 (k % 4 == 0): lane part and
+// uniform part of the byte offset.  Non-temporal (the operand is read once,
+// by the next round's product): measured faster for whole 128-byte lines.
+__device__ __forceinline__ void put4(const ProbOut& po, uint32_t voff, int soff, const float (&w)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(u32x2_t, make_uint2(pack_bf2(w[0], w[1]), pack_bf2(w[2], w[3]))), po.rs,
+        voff, soff, 2 /* nt */);
+}
+
+// Record of a whole chunk (all 64 entries members; x in member order, k0 its
+// first entry); *s2 receives its weight sum at temperature T.  With PROBS,
+// also the self-conditioning weights of its entries.
+template <bool PROBS>
+__device__ __forceinline__ Rec chunk_full(const float (&x)[4 * NDEPTH], int k0, float invT,
+                                          float* s2out, const ProbOut& po) {
+    // chunk max (each entry replaces it only if strictly greater, in member
+    // order), then the first member equal to it: the same first argmax as
+    // tracking both in one pass, since the max is attained first there (+0
+    // and -0 compare equal in both passes; NaN is never taken, and a NaN
+    // first entry leaves the max NaN and the argmax 0)
+    float m = x[0];
+#pragma unroll
+    for (int u = 1; u < 4 * NDEPTH; ++u) m = x[u] > m ? x[u] : m;
+    int ju = 0;
+#pragma unroll
+    for (int u = 4 * NDEPTH - 1; u > 0; --u) ju = x[u] == m ? u : ju;
+    // byte offset of entry k0 in the output; entry k0 + 4096 d adds step d
+    const uint32_t o0 = PROBS ? po.off((uint32_t)k0) : 0u;
+    const int ds = PROBS ? po.step() : 0;
+    const float f = PROBS ? dexp(m - po.M) : 0.0f;
+    float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sum = 0.0f, ac = 0.0f, s2 = 0.0f;
+    if (invT != 1.0f) {
+#pragma unroll
+        for (int u = 0; u < 4 * NDEPTH; ++u) {
+            const float z = x[u] - m;
+            const float e = dexp(z);
+            sum = sum + e;
+            const float ez = e * z;
+            ac = ac + ez;
+            s2 = s2 + dexp(z * invT);
+            if (PROBS) {
+                w[u % 4] = chunk_weight(e, f);
+                if (u % 4 == 3) put4(po, o0, ds * (u / 4), w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4 * NDEPTH; ++u) {
+            const float z = x[u] - m;
+            const float e = dexp(z);
+            sum = sum + e;
+            const float ez = e * z;
+            ac = ac + ez;
+            if (PROBS) {
+                w[u % 4] = chunk_weight(e, f);
+                if (u % 4 == 3) put4(po, o0, ds * (u / 4), w);
+            }
+        }
+        s2 = sum;
+    }
+    *s2out = s2;
+    Rec r;
+    r.m = m;
+    r.j = k0 + 4 * NLANE * (ju / 4) + (ju % 4);
+    r.s = sum;
+    r.a = ac;
+    return r;
+}
+
+// Chunk lam of the ragged last tile t: members are the entries below V.
+template <bool VEC, bool PROBS>
+__device__ __forceinline__ Rec chunk_ragged(const float* row, int V, int t, int lam, float invT,
+                                            float* s2out, const ProbOut& po) {
+    float x[4 * NDEPTH];
+    Rec rc = {-INFINITY, -1, 0.0f, 0.0f};
+    float s2 = 0.0f;
+    const long g0 = (long)t * (NLANE * NDEPTH) + lam;
+#pragma unroll
+    for (int d = 0; d < NDEPTH; ++d) {
+        const long k = 4 * (g0 + (long)d * NLANE);
+        if (VEC && k + 3 < V) {
+            const float4 v = *reinterpret_cast<const float4*>(row + k);
+            x[4 * d + 0] = v.x;
+            x[4 * d + 1] = v.y;
+            x[4 * d + 2] = v.z;
+            x[4 * d + 3] = v.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[4 * d + q] = (k + q < V) ? row[k + q] : -INFINITY;
+        }
+    }
+    float m = -INFINITY;
+    int j = -1;
+#pragma unroll
+    for (int d = 0; d < NDEPTH; ++d)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const long k = 4 * (g0 + (long)d * NLANE) + q;
+            if (k < V && (x[4 * d + q] > m || j < 0)) {
+                m = x[4 * d + q];
+                j = (int)k;
+            }
+        }
+    if (j >= 0) {
+        const float f = PROBS ? dexp(m - po.M) : 0.0f;
+        float sum = 0.0f, ac = 0.0f;
+#pragma unroll
+        for (int d = 0; d < NDEPTH; ++d) {
+            float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const long k = 4 * (g0 + (long)d * NLANE) + q;
+                if (k < V) {
+                    const float z = x[4 * d + q] - m;
+                    const float e = dexp(z);
+                    sum = sum + e;
+                    const float ez = e * z;
+                    ac = ac + ez;
+                    if (invT != 1.0f) s2 = s2 + dexp(z * invT);
+                    if (PROBS) w[q] = chunk_weight(e, f);
+                }
+            }
+            const uint32_t k = 4u * (uint32_t)(g0 + (long)d * NLANE);
+            if (PROBS && k + 3 < (uint32_t)V) put4(po, po.off(k), 0, w);
+        }
+        if (invT == 1.0f) s2 = sum;
+        rc.m = m;
+        rc.j = j;
+        rc.s = sum;
+        rc.a = ac;
+    }
+    *s2out = s2;
+    return rc;
+}
+
+// One workgroup of 512 threads per logit row; thread p owns chunks p and
+// p + 512 of every tile (256 registers a lane at this size, where 1024
+// threads of 128 spill).
+constexpr int NTHR = 512;
+
+template <bool VEC, bool PROBS>
+__global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
     extern __shared__ __align__(16) float sm[];
     const int nt = cdiv(a.V, TILE);
     float* Gs = sm;                       // [nt*1024] chunk weights at temperature T
@@ -181,131 +352,106 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
     const int b = (int)(rowid / a.N), i = (int)(rowid % a.N);
     if (a.stop[b]) return;
     const float* row = a.logits + rowid * (long)a.V;
-    const int lam = threadIdx.x, lane = lam & 63, wave = lam >> 6;
+    const __amdgpu_buffer_rsrc_t lrs = buf_rsrc(row, 4u * (uint32_t)a.V);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float invT = a.inv_t;
 
-    Rec F = {-INFINITY, -1, 0.0f, 0.0f};
-    // whole tiles first (every entry a member), then the ragged last tile
+    // Optional output for the next round's self-conditioning: the weight
+    // chunk_weight(E(l - m_c), E(m_c - M)) of every logit, m_c its chunk's
+    // max and M the row max (the largest of the head GEMM's slab maxima), as
+    // bf16, blocked or row-major.  E(l - m_c) is the value the statistics
+    // below sum anyway.  It takes no part in the decisions.
+    __shared__ float wmx[NTHR / 64];
+    ProbOut po;
+    po.rs = buf_rsrc(a.probs, 0);   // an empty resource when unused
+    po.tiled = a.probs_tiled;
+    po.M = 0.0f;
+    if (PROBS) {
+        const float* rm = a.rowmax + rowid * (long)a.rowmax_n;
+        float mm = -INFINITY;
+        for (int c = tid; c < a.rowmax_n; c += NTHR) mm = fmaxf(mm, rm[c]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+        if (lane == 0) wmx[wave] = mm;
+        __syncthreads();
+        float Mp = wmx[0];
+#pragma unroll
+        for (int w = 1; w < NTHR / 64; ++w) Mp = fmaxf(Mp, wmx[w]);
+        po.M = Mp;
+        // the row's span fits 32 bits (V <= 2^19)
+        if (po.tiled)
+            po.rs = buf_rsrc(a.probs + tiled64_index(rowid, 0, a.V),
+                             2u * ((((uint32_t)a.V / 64 - 1) << 14) + 64));
+        else
+            po.rs = buf_rsrc(a.probs + rowid * (long)a.V, 2u * (uint32_t)a.V);
+    }
+
+    // lane records of chunks tid (F0) and tid + 512 (F1), folded over the
+    // tiles in order: whole tiles first (every entry a member), then the
+    // ragged last tile
+    Rec F0 = {-INFINITY, -1, 0.0f, 0.0f}, F1 = F0;
     const int nfull = VEC ? a.V / TILE : 0;
     for (int t = 0; t < nfull; ++t) {
-        float x[4 * NDEPTH];
-        Rec rc;
-        float s2 = 0.0f;
-        const int k0 = 4 * (t * (NLANE * NDEPTH) + lam);
+        float x0[4 * NDEPTH], x1[4 * NDEPTH];
+        const int k0 = 4 * (t * (NLANE * NDEPTH) + tid), k1 = k0 + 4 * NTHR;
+        // entry k0 + 4096 d is 16 KiB d after entry k0
 #pragma unroll
         for (int d = 0; d < NDEPTH; ++d) {
-            const float4 v = *reinterpret_cast<const float4*>(row + k0 + 4 * NLANE * d);
-            x[4 * d + 0] = v.x;
-            x[4 * d + 1] = v.y;
-            x[4 * d + 2] = v.z;
-            x[4 * d + 3] = v.w;
+            const f32x4_t v = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lrs, 4u * (uint32_t)k0, 16384 * d, 0));
+            x0[4 * d + 0] = v[0];
+            x0[4 * d + 1] = v[1];
+            x0[4 * d + 2] = v[2];
+            x0[4 * d + 3] = v[3];
         }
-        // chunk max (each entry replaces it only if strictly greater, in
-        // member order), then the first member equal to it: the same first
-        // argmax as tracking both in one pass, since the max is attained
-        // first there (+0 and -0 compare equal in both passes; NaN is never
-        // taken, and a NaN first entry leaves the max NaN and the argmax 0)
-        float m = x[0];
+        float s0, s1;
+        const Rec r0 = chunk_full<PROBS>(x0, k0, invT, &s0, po);
+        // the second chunk's loads go out after the first chunk's work
+        // (measured: fewer loads in flight beside the first chunk's stores,
+        // and the other wave of the SIMD covers their latency)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 1; u < 4 * NDEPTH; ++u) m = x[u] > m ? x[u] : m;
-        int ju = 0;
-#pragma unroll
-        for (int u = 4 * NDEPTH - 1; u > 0; --u) ju = x[u] == m ? u : ju;
-        const int j = k0 + 4 * NLANE * (ju / 4) + (ju % 4);
-        float sum = 0.0f, ac = 0.0f;
-        if (invT != 1.0f) {
-#pragma unroll
-            for (int u = 0; u < 4 * NDEPTH; ++u) {
-                const float z = x[u] - m;
-                const float e = dexp(z);
-                sum = sum + e;
-                const float ez = e * z;
-                ac = ac + ez;
-                s2 = s2 + dexp(z * invT);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4 * NDEPTH; ++u) {
-                const float z = x[u] - m;
-                const float e = dexp(z);
-                sum = sum + e;
-                const float ez = e * z;
-                ac = ac + ez;
-            }
-            s2 = sum;
+        for (int d = 0; d < NDEPTH; ++d) {
+            const f32x4_t v = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lrs, 4u * (uint32_t)k1, 16384 * d, 0));
+            x1[4 * d + 0] = v[0];
+            x1[4 * d + 1] = v[1];
+            x1[4 * d + 2] = v[2];
+            x1[4 * d + 3] = v[3];
         }
-        rc.m = m;
-        rc.j = j;
-        rc.s = sum;
-        rc.a = ac;
-        Gs[t * NLANE + lam] = s2;
-        Ms[t * NLANE + lam] = rc.m;
-        F = (t == 0) ? rc : merge(F, rc);
+        const Rec r1 = chunk_full<PROBS>(x1, k1, invT, &s1, po);
+        Gs[t * NLANE + tid] = s0;
+        Ms[t * NLANE + tid] = r0.m;
+        Gs[t * NLANE + tid + NTHR] = s1;
+        Ms[t * NLANE + tid + NTHR] = r1.m;
+        F0 = (t == 0) ? r0 : merge(F0, r0);
+        F1 = (t == 0) ? r1 : merge(F1, r1);
     }
     for (int t = nfull; t < nt; ++t) {
-        float x[4 * NDEPTH];
-        Rec rc = {-INFINITY, -1, 0.0f, 0.0f};
-        float s2 = 0.0f;
-        const long g0 = (long)t * (NLANE * NDEPTH) + lam;
-#pragma unroll
-        for (int d = 0; d < NDEPTH; ++d) {
-            const long k = 4 * (g0 + (long)d * NLANE);
-            if (VEC && k + 3 < a.V) {
-                const float4 v = *reinterpret_cast<const float4*>(row + k);
-                x[4 * d + 0] = v.x;
-                x[4 * d + 1] = v.y;
-                x[4 * d + 2] = v.z;
-                x[4 * d + 3] = v.w;
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) x[4 * d + q] = (k + q < a.V) ? row[k + q] : -INFINITY;
-            }
-        }
-        float m = -INFINITY;
-        int j = -1;
-#pragma unroll
-        for (int d = 0; d < NDEPTH; ++d)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const long k = 4 * (g0 + (long)d * NLANE) + q;
-                if (k < a.V && (x[4 * d + q] > m || j < 0)) {
-                    m = x[4 * d + q];
-                    j = (int)k;
-                }
-            }
-        if (j >= 0) {
-            float sum = 0.0f, ac = 0.0f;
-#pragma unroll
-            for (int d = 0; d < NDEPTH; ++d)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const long k = 4 * (g0 + (long)d * NLANE) + q;
-                    if (k < a.V) {
-                        const float z = x[4 * d + q] - m;
-                        const float e = dexp(z);
-                        sum = sum + e;
-                        const float ez = e * z;
-                        ac = ac + ez;
-                        if (invT != 1.0f) s2 = s2 + dexp(z * invT);
-                    }
-                }
-            if (invT == 1.0f) s2 = sum;
-            rc.m = m;
-            rc.j = j;
-            rc.s = sum;
-            rc.a = ac;
-        }
-            Gs[t * NLANE + lam] = s2;
-        Ms[t * NLANE + lam] = rc.m;
-        F = (t == 0) ? rc : merge(F, rc);
+        float s0, s1;
+        const Rec r0 = chunk_ragged<VEC, PROBS>(row, a.V, t, tid, invT, &s0, po);
+        const Rec r1 = chunk_ragged<VEC, PROBS>(row, a.V, t, tid + NTHR, invT, &s1, po);
+        Gs[t * NLANE + tid] = s0;
+        Ms[t * NLANE + tid] = r0.m;
+        Gs[t * NLANE + tid + NTHR] = s1;
+        Ms[t * NLANE + tid + NTHR] = r1.m;
+        F0 = (t == 0) ? r0 : merge(F0, r0);
+        F1 = (t == 0) ? r1 : merge(F1, r1);
     }
-    // pairwise tree over lanes: within the wave, then over the 16 waves.
+    // pairwise tree over the 1024 chunk lanes: within each group of 64
+    // (F0 of wave w is group w, F1 group w + 8), then over the 16 groups.
     // merge is symmetric, so the butterfly leaves every lane of a pair with
     // the record of the pair: level by level the same tree as merging
     // adjacent pairs first.
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) F = merge(F, shfl_rec(F, o));
-    if (lane == 0) wrec[wave] = F;
+    for (int o = 1; o < 64; o <<= 1) {
+        F0 = merge(F0, shfl_rec(F0, o));
+        F1 = merge(F1, shfl_rec(F1, o));
+    }
+    if (lane == 0) {
+        wrec[wave] = F0;
+        wrec[wave + NTHR / 64] = F1;
+    }
     __syncthreads();
     __shared__ Rec rowrec;
     if (wave == 0) {
@@ -318,21 +464,21 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
     const Rec R = rowrec;
 
     // chunk weights at temperature T, relative to the row max
-    for (int c = lam; c < nt * NLANE; c += NLANE) {
+    for (int c = tid; c < nt * NLANE; c += NTHR) {
         const float s2 = Gs[c];
         Gs[c] = s2 == 0.0f ? 0.0f : s2 * dexp((Ms[c] - R.m) * invT);
     }
     __syncthreads();
     const int nsup = nt * (NLANE / SUPER);
-    if (lam < nsup) {
+    if (tid < nsup) {
         float acc = 0.0f;
-        for (int l = 0; l < SUPER; ++l) acc = acc + Gs[lam * SUPER + l];
-        Wsup[lam] = acc;
+        for (int l = 0; l < SUPER; ++l) acc = acc + Gs[tid * SUPER + l];
+        Wsup[tid] = acc;
     }
     __syncthreads();
     __shared__ int cstar_s;
     __shared__ uint64_t words[4];
-    if (lam == 0) {
+    if (tid == 0) {
         uint64_t o[4];
         philox((uint64_t)a.step, (uint64_t)b, (uint64_t)i, 0ull, a.seed, 0ull, o);
         words[0] = o[0];
@@ -345,15 +491,15 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
     __syncthreads();
     // entries of the chosen chunk, in member order
     const int cstar = cstar_s;
-    if (lam < 4 * NDEPTH) {
+    if (tid < 4 * NDEPTH) {
         const int t = cstar / NLANE, l = cstar % NLANE;
-        const int d = lam / 4, q = lam % 4;
+        const int d = tid / 4, q = tid % 4;
         const long k = 4 * ((long)t * NLANE * NDEPTH + (long)d * NLANE + l) + q;
-        wk[lam] = k < a.V ? dexp((row[k] - Ms[cstar]) * invT) : 0.0f;
-        kk[lam] = k < a.V ? (int)k : -1;
+        wk[tid] = k < a.V ? dexp((row[k] - Ms[cstar]) * invT) : 0.0f;
+        kk[tid] = k < a.V ? (int)k : -1;
     }
     __syncthreads();
-    if (lam == 0) {
+    if (tid == 0) {
         // compact the members in place (entries past V are not members)
         int n = 0;
         for (int u = 0; u < 4 * NDEPTH; ++u)
@@ -374,6 +520,59 @@ __global__ __launch_bounds__(1024) void sample_row_kernel(SampleArgs a) {
         a.newmax[rowid] = R.j;
         a.y[rowid] = yv;
         a.r[rowid] = uniform_token(words[1], a.V);
+    }
+}
+
+// Stand-alone pass: the self-conditioning weights of whole rows from their
+// statistics (M = stats[0], the row max the statistics hold), chunk by chunk
+// exactly as the row pass computes them.  blockIdx.x = row, blockIdx.y = a
+// quarter of one tile's 1024 chunks.  V % 4 == 0.
+__global__ __launch_bounds__(256) void selfcond_probs_kernel(const float* __restrict__ logits,
+                                                            const float* __restrict__ stats,
+                                                            bf16_t* __restrict__ out, int V,
+                                                            const int32_t* halt, int tiled) {
+    if (halt && *halt) return;
+    const long rowid = blockIdx.x;
+    const int t = blockIdx.y >> 2;
+    const int lam = ((blockIdx.y & 3) << 8) + threadIdx.x;
+    const float M = stats[rowid * 4];
+    const float* row = logits + rowid * (long)V;
+    const long g0 = (long)t * (NLANE * NDEPTH) + lam;
+    float x[4 * NDEPTH];
+#pragma unroll
+    for (int d = 0; d < NDEPTH; ++d) {
+        const long k = 4 * (g0 + (long)d * NLANE);
+        const float4 v = k + 3 < V ? *reinterpret_cast<const float4*>(row + k)
+                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        x[4 * d + 0] = v.x;
+        x[4 * d + 1] = v.y;
+        x[4 * d + 2] = v.z;
+        x[4 * d + 3] = v.w;
+    }
+    // the chunk max as the row pass takes it: the first member, then every
+    // member that is strictly greater, in member order
+    float m = -INFINITY;
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < 4 * NDEPTH; ++u) {
+        const long k = 4 * (g0 + (long)(u / 4) * NLANE) + u % 4;
+        if (k < V && (!any || x[u] > m)) {
+            m = x[u];
+            any = true;
+        }
+    }
+    if (!any) return;
+    const float f = dexp(m - M);
+#pragma unroll
+    for (int d = 0; d < NDEPTH; ++d) {
+        const long k = 4 * (g0 + (long)d * NLANE);
+        if (k + 3 < V) {
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = chunk_weight(dexp(x[4 * d + q] - m), f);
+            const long o = tiled ? tiled64_index(rowid, k, V) : rowid * (long)V + k;
+            *reinterpret_cast<uint2*>(out + o) = make_uint2(pack_bf2(w[0], w[1]), pack_bf2(w[2], w[3]));
+        }
     }
 }
 
@@ -468,24 +667,41 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(uint64_t seed, int blo
 
 hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
     if (a.B <= 0 || a.N <= 0) return hipSuccess;
+    if (a.probs && (a.V % 128 || !a.rowmax || a.rowmax_n < 1 || ((uintptr_t)a.logits & 15) ||
+                    ((uintptr_t)a.probs & 7)))
+        return hipErrorInvalidValue;
     const int nt = cdiv(a.V, TILE);
     const size_t lds = (size_t)2 * nt * NLANE * sizeof(float);
-    static bool attr_set[2] = {false, false};
+    static bool attr_set[3] = {false, false, false};
     const bool vec = (a.V % 4) == 0;
-    const void* kern = vec ? (const void*)sample_row_kernel<true> : (const void*)sample_row_kernel<false>;
-    if (!attr_set[vec]) {
-        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+    const int which = a.probs ? 2 : (vec ? 1 : 0);
+    const void* kerns[3] = {(const void*)sample_row_kernel<false, false>,
+                            (const void*)sample_row_kernel<true, false>,
+                            (const void*)sample_row_kernel<true, true>};
+    if (!attr_set[which]) {
+        hipError_t e = hipFuncSetAttribute(kerns[which], hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(2 * 8 * NLANE * sizeof(float)));
         if (e != hipSuccess) return e;
-        attr_set[vec] = true;
+        attr_set[which] = true;
     }
-    if (vec)
-        hipLaunchKernelGGL(sample_row_kernel<true>, dim3(a.B * a.N), dim3(NLANE), lds, st, a);
+    if (a.probs)
+        hipLaunchKernelGGL((sample_row_kernel<true, true>), dim3(a.B * a.N), dim3(NTHR), lds, st, a);
+    else if (vec)
+        hipLaunchKernelGGL((sample_row_kernel<true, false>), dim3(a.B * a.N), dim3(NTHR), lds, st, a);
     else
-        hipLaunchKernelGGL(sample_row_kernel<false>, dim3(a.B * a.N), dim3(NLANE), lds, st, a);
+        hipLaunchKernelGGL((sample_row_kernel<false, false>), dim3(a.B * a.N), dim3(NTHR), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sample_canvas_kernel, dim3(a.B), dim3(1024), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t selfcond_probs(const float* logits, const float* stats, uint16_t* out, int rows, int V,
+                          const int32_t* halt, int tiled, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (V % 4 || (tiled && V % 64)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(selfcond_probs_kernel, dim3(rows, 4 * cdiv(V, TILE)), dim3(256), 0, st, logits,
+                       stats, out, V, halt, tiled);
     return hipGetLastError();
 }
 

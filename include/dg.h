@@ -218,6 +218,39 @@ dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t bat
                            float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
                            void* stream);
 
+/* dg_sample_update that also writes the next round's self-conditioning
+ * operand (report-summary page, section 2: the model sees its previous
+ * round's prediction; section 5: that costs a pass over the full
+ * distributions), while it reads the logits anyway.  For every sampled row r
+ * = b*N + i, d_probs receives the softmax numerators exp(l - M_r) exactly as
+ * dg_stage_probs computes them, M_r = the largest of d_rowmax[r][0 ..
+ * vocab/64) (dg_stage_head_rowmax writes them; it equals the statistics'
+ * max), in the layout `blocked` selects as for dg_stage_probs: the same
+ * bits dg_stage_probs writes.  All other
+ * outputs are those of dg_sample_update.  vocab % 128 == 0 (DG_ERR_SHAPE
+ * otherwise). */
+dg_status dg_sample_update_probs(const dg_sampler_params* p, int32_t step, int32_t batch,
+                                 int32_t canvas, int32_t vocab, const float* d_logits,
+                                 int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                                 float* d_stats, int32_t* d_stop, const float* d_rowmax,
+                                 int32_t blocked, void* d_probs, void* d_ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Self-conditioning operand of T logit rows d_logits [T][vocab] with their
+ * statistics d_stats [T][4] (as dg_sample_update writes them): d_probs =
+ * the softmax numerators exp(l - stats[0]) as bf16; the division by
+ * stats[1] follows the product with E inside the denoiser (report-summary
+ * page, sections 2 and 5).  Computed in the sampler's row layout: for each
+ * chunk with max m_c, E(l - m_c) * E(m_c - stats[0]) in binary32, E the
+ * sampler's exp (so the row pass of dg_sample_update_probs, which already
+ * holds E(l - m_c), writes the same bits).  blocked != 0: 64-wide blocks,
+ * element (r, v) at ((r/256 * vocab/64 + v/64) * 256 + r%256) * 64 + v%64
+ * over T rows padded to 256 (vocab % 64 == 0; one row's 64 values are one
+ * 128-byte line), else row-major [T][vocab].  vocab % 4 == 0.  Model-free;
+ * d_probs is caller-owned device memory. */
+dg_status dg_stage_probs(int32_t T, int32_t vocab, int32_t blocked, const float* d_logits,
+                         const float* d_stats, void* d_probs, void* stream);
+
 /* Canvas initialisation: d_canvas [batch][N] = uniform tokens from Philox
  * counter (block_index, b, i, 1), key (seed, 0) (report-summary page,
  * section 1: the block starts as random tokens). */
@@ -234,7 +267,11 @@ dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
  * conditioned on the previous round if params->selfcond_on), stop per
  * canvas, block = the last round's argmax, then dg_commit_block.
  * d_block_out [batch][N]; h_steps_out [batch] receives the rounds each canvas
- * ran.  Waits on the stream once per round to read the stop flags.
+ * ran.  Waits on the stream once per round to read the stop flags.  For
+ * blocked models with weights.embed_head the rounds run as
+ * dg_stage_head_rowmax + dg_sample_update_probs, so the next round's
+ * self-conditioning operand comes out of the sampler's pass over the logits
+ * (the same bits as the separate pass dg_denoise_step makes).
  * d_ws needs dg_generate_workspace_bytes. */
 dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* bytes);
 dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
@@ -266,6 +303,13 @@ dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_
 /* Head: d_logits [T][V] = RMSNorm(d_h) E^T (fp32). */
 dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,
                         size_t ws_bytes, void* stream);
+/* The head as the block loop runs it: dg_stage_head, and d_rowmax [T][V/64]
+ * = the largest logit of each row in each 64-column slab, taken from the
+ * product's registers before the logits are read again.  Blocked models with
+ * weights.embed_head only (DG_ERR_UNSUPPORTED otherwise); T up to the canvas
+ * tokens of the workspace's batch rounded up to 256 (DG_ERR_CAPACITY). */
+dg_status dg_stage_head_rowmax(dg_model* m, int32_t T, const float* d_h, float* d_logits,
+                               float* d_rowmax, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- timers */
 /* Kernel timers: when enabled, the library records a pair of HIP events on

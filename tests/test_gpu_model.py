@@ -252,6 +252,29 @@ def test_stage_head_and_input(name):
     assert normwise(hd.cpu().numpy(), ref_in) <= tol_for(cfg)
 
 
+@pytest.mark.parametrize("T", [256, 200])
+def test_stage_head_rowmax(T):
+    """The blocked head's slab maxima: the same logits as dg_stage_head, and
+    rowmax[t][j] == max(logits[t][64 j : 64 j + 64]) exactly; also with a
+    ragged row count.  Models without the blocked head refuse the call."""
+    cfg, W, m = setup("vocab_bf16", 0)
+    V, d = cfg["vocab"], cfg["d_model"]
+    h = to_dev(np.random.default_rng(15).standard_normal((T, d)).astype(np.float32))
+    a = torch.empty((T, V), dtype=torch.float32, device=DEV)
+    b = torch.empty_like(a)
+    rowmax = torch.full((T, V // 64), float("nan"), dtype=torch.float32, device=DEV)
+    m.stage_head(h, a)
+    m.stage_head_rowmax(h, b, rowmax)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(rowmax, b.view(T, V // 64, 64).amax(dim=-1))
+    cr, _, mr = setup("vocab_ragged", 0)
+    lr = torch.empty((200, cr["vocab"]), dtype=torch.float32, device=DEV)
+    rr = torch.empty((200, cr["vocab"] // 64 + 1), dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.DGError):
+        mr.stage_head_rowmax(h[:200].contiguous(), lr, rr)
+
+
 def test_commit_equals_encode_of_concatenation():
     cfg, W, m1 = setup("small_bf16", 50, batch=1)
     N, V = cfg["canvas"], cfg["vocab"]
@@ -272,6 +295,7 @@ def test_commit_equals_encode_of_concatenation():
 
 @pytest.mark.parametrize("name,B,selfcond,early", [("tiny", 1, True, False),
                                                    ("small_bf16", 2, True, False),
+                                                   ("vocab_bf16", 1, True, False),
                                                    ("small_bf16", 2, False, False),
                                                    ("small_bf16", 2, True, True)])
 def test_generate_block_is_its_composition(name, B, selfcond, early):

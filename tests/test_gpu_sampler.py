@@ -136,3 +136,96 @@ def test_sampler_is_deterministic():
     a = gpu_update(params, 4, logits, canvas, argmax, stop)
     b = gpu_update(params, 4, logits, canvas, argmax, stop)
     assert_same(a, b, "rerun")
+
+
+def unblock_bf16(buf: np.ndarray, rows: int, V: int) -> np.ndarray:
+    """float32 values of a bf16 [rows][V] matrix stored in the 256 x 64
+    blocked layout of the self-conditioning operand (rows padded to 256)."""
+    rp = -(-rows // 256) * 256
+    b = buf.view(np.uint16)[: rp * V].reshape(rp // 256, V // 64, 256, 64)
+    b = b.transpose(0, 2, 1, 3).reshape(rp, V)[:rows]
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+PROB_CASES = [
+    # B, N, V, sigma, blocked: rows padded to 256 and only the ragged tile
+    # loop; two whole 65536-entry tiles and a ragged tail
+    (2, 100, 4096, 3.0, True),
+    (1, 256, 2 * 65536 + 384, 3.0, True),
+    (2, 100, 4096, 3.0, False),
+    (1, 256, 2 * 65536 + 384, 3.0, False),
+]
+
+
+@pytest.mark.parametrize("B,N,V,sigma,blocked", PROB_CASES)
+def test_sampler_writes_selfcond_operand(B, N, V, sigma, blocked):
+    """dg_sample_update_probs: every sampler output bit-identical to
+    dg_sample_update; the probabilities bit-identical to the stand-alone pass
+    dg_stage_probs (the operand dg_denoise_step builds); both within bf16
+    rounding of the T = 1 distribution; padded rows untouched."""
+    print(f"selfcond operand case B={B} N={N} V={V} blocked={blocked}", flush=True)
+    T = B * N
+    params = synthetic.default_sampler_params(seed=21)
+    logits = synthetic.make_logits((B, N, V), seed=V + 7, sigma=sigma)
+    canvas = synthetic.make_tokens(V, (B, N), seed=22)
+    argmax = synthetic.make_tokens(V, (B, N), seed=23)
+    lg = to_dev(logits)
+    rowmax = lg.view(T, V // 64, 64).amax(dim=-1).contiguous()
+    outs = []
+    rp = -(-T // 256) * 256
+    sentinel = torch.full((rp * V,), 0x7f81, dtype=torch.int16, device=DEV)
+    probs = sentinel.clone()
+    for fused in (False, True):
+        cv, am = to_dev(canvas), to_dev(argmax)
+        st = torch.zeros(B, dtype=torch.int32, device=DEV)
+        lock = torch.zeros((B, N), dtype=torch.uint8, device=DEV)
+        stats = torch.zeros((B, N, 4), dtype=torch.float32, device=DEV)
+        ws = binding.sampler_workspace(B, N)
+        if fused:
+            binding.sample_update_probs(params, 2, lg, cv, am, lock, stats, st, rowmax, probs, ws,
+                                        blocked=blocked)
+        else:
+            binding.sample_update(params, 2, lg, cv, am, lock, stats, st, ws)
+        torch.cuda.synchronize()
+        outs.append(tuple(x.cpu().numpy() for x in (cv, am, lock, stats, st)))
+    assert_same(outs[1], outs[0], "fused sampler")
+    stats = to_dev(outs[1][3])
+    alone = sentinel.clone()
+    binding.stage_probs(lg.view(T, V), stats.view(T, 4), alone, blocked=blocked)
+    torch.cuda.synchronize()
+    p_fused, p_alone = probs.cpu().numpy(), alone.cpu().numpy()
+    bad = p_fused != p_alone
+    assert not bad.any(), f"operands differ at {np.argwhere(bad)[:5].ravel().tolist()}"
+    if blocked:
+        e = unblock_bf16(p_fused, T, V).astype(np.float64)
+    else:
+        e = ((p_fused.view(np.uint16)[: T * V].astype(np.uint32) << 16).view(np.float32)
+             .reshape(T, V).astype(np.float64))
+    L = logits.reshape(T, V).astype(np.float64)
+    ref = np.exp(L - L.max(axis=1, keepdims=True))
+    # bf16 keeps 8 significant bits (relative rounding <= 2^-9); the
+    # hardware exp2 and the fp32 argument add ~1e-6
+    assert (np.abs(e - ref) <= 2.0 ** -8 * ref + 1e-30).all()
+    # divided by the statistics' sum: the T = 1 distribution
+    S = outs[1][3].reshape(T, 4)[:, 1].astype(np.float64)
+    p = e / S[:, None]
+    pref = ref / ref.sum(axis=1, keepdims=True)
+    assert np.abs(p - pref).max() <= 2.0 ** -8 * pref.max()
+    if blocked and rp > T:   # padded rows are not written
+        pad = p_fused.reshape(rp // 256, V // 64, 256, 64)[-1, :, T % 256:, :]
+        assert (pad == 0x7f81).all()
+
+
+def test_stage_probs_row_major_matches_blocked():
+    T, V = 37, 4096
+    logits = synthetic.make_logits((T, V), seed=31, sigma=2.0)
+    stats = np.stack([osampler.row_stats(logits[i])[0] for i in range(T)]).astype(np.float32)
+    lg, st = to_dev(logits), to_dev(stats)
+    rm = torch.zeros((T * V,), dtype=torch.int16, device=DEV)
+    bl = torch.zeros((256 * V,), dtype=torch.int16, device=DEV)
+    binding.stage_probs(lg, st, rm, blocked=False)
+    binding.stage_probs(lg, st, bl, blocked=True)
+    torch.cuda.synchronize()
+    a = (rm.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(T, V)
+    b = unblock_bf16(bl.cpu().numpy(), T, V)
+    assert (a.view(np.uint32) == b.view(np.uint32)).all()
