@@ -250,14 +250,24 @@ __global__ void attn_merge_kernel(AttnArgs a) {
     const long th = blockIdx.x;            // token * Hq + head
     const int d = threadIdx.x;
     const long stride = (long)a.B * a.n * a.Hq;
-    float m = -1e30f;
-    for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_ml[(s * stride + th) * 2]);
-    float lsum = 0.f, acc = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-        const float w = exp2f(a.part_ml[(s * stride + th) * 2] - m);
-        lsum += w * a.part_ml[(s * stride + th) * 2 + 1];
-        acc += w * a.part_o[(s * stride + th) * a.dh + d];
+    // the first wave reads every split's (max, sum) at once (splits <= 32)
+    // and leaves the split weights and the total in LDS
+    __shared__ float wts[32];
+    __shared__ float ltot;
+    if (d < 64) {
+        const bool on = d < a.splits;
+        const float ms = on ? a.part_ml[(d * stride + th) * 2] : -1e30f;
+        const float ls = on ? a.part_ml[(d * stride + th) * 2 + 1] : 0.f;
+        const float m = wave_max(ms);
+        const float w = on ? exp2f(ms - m) : 0.f;
+        const float l = wave_sum(w * ls);
+        if (on) wts[d] = w;
+        if (d == 0) ltot = l;
     }
+    __syncthreads();
+    float acc = 0.f;
+    for (int s = 0; s < a.splits; ++s) acc += wts[s] * a.part_o[(s * stride + th) * a.dh + d];
+    const float lsum = ltot;
     T* out = reinterpret_cast<T*>(a.out);
     out[th * a.dh + d] = Elt<T>::from_f(lsum > 0.f ? acc / lsum : 0.f);
 }
@@ -286,6 +296,8 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
 template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t st) {
     if (a.n <= 0 || a.B <= 0) return hipSuccess;
+    // the merge keeps the split weights in one wave
+    if (a.splits > 1 && (a.splits > 32 || a.dh < 64)) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     dim3 grid(cdiv(G * cdiv(a.n, 16), 4), a.Hkv, a.B * a.splits);
     switch (a.dh) {

@@ -116,8 +116,9 @@ struct dg_model {
     const void* w_sc;
     const float* final_norm;
     std::vector<dg_layer_weights> layers;
-    // block loop: pinned host copies of the stop flags of two rounds, and
-    // the events that say they have arrived (created on first use)
+    // block loop: pinned host memory that the sampler's canvas kernel writes
+    // the stop flags of two rounds into, and the events that say they have
+    // arrived (created on first use)
     int32_t* hflags = nullptr;
     int hflags_cap = 0;
     hipEvent_t flag_ev[2] = {nullptr, nullptr};
@@ -341,7 +342,7 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
         }
     }
     const long tiles = (long)cdiv(N, 64) * mt;
-    int splits = (int)std::min<long>(std::max<long>(1, cdiv(320, (int)tiles)), std::max(1, K / 256));
+    int splits = (int)std::min<long>(std::max<long>(1, cdiv(320, (int)tiles)), std::max(1, K / 64));
     while (splits > 1 && (size_t)splits * M * N > kSplitPartFloats) --splits;
     if (splits <= 1) {
         if (bf) DG_HIP(dg::gemm_stream(g, epi, 1, 1, st));
@@ -783,7 +784,8 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
                              hipStream_t st, int32_t* nstop = nullptr,
                              int32_t* halt = nullptr, const float* rowmax = nullptr,
-                             void* probs = nullptr, int probs_tiled = 1) {
+                             void* probs = nullptr, int probs_tiled = 1,
+                             int32_t* host_stop = nullptr) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
@@ -826,6 +828,7 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
     a.newmax = cv.take<int32_t>((size_t)batch * canvas);
     a.nstop = nstop;
     a.halt = halt;
+    a.host_stop = host_stop;
     if (probs) {
         // also write the next round's self-conditioning operand
         if (!rowmax || vocab % 128) return fail(DG_ERR_SHAPE, "probabilities need row maxima and vocab %% 128 == 0");
@@ -953,8 +956,9 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     int32_t* halt = stop + batch + 1;
     s.halt = halt;
     for (int b = 0; b < batch; ++b) h_steps_out[b] = 0;
-    // The stop flags of round t are read on the host while round t+1 is
-    // already queued (one round of look-ahead hides the host round trip).
+    // The stop flags of round t (written by the canvas kernel straight into
+    // pinned host memory, slot t & 1) are read on the host while round t+1
+    // is already queued (one round of look-ahead hides the host round trip).
     // Once every sequence has stopped the sampler raises `halt` on the
     // device, so a look-ahead round after the last stop skips its heavy
     // kernels and leaves canvas, argmax and locks untouched.
@@ -987,9 +991,8 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
             DG_TRY(denoise<float>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         DG_TRY(sample_impl(p, t, batch, c.canvas, c.vocab, logits, canvas, argmax, lock, stats,
                            stop, sws, sws_bytes, st, nstop, halt, s.fuse ? s.tmax : nullptr,
-                           s.fuse ? s.probs : nullptr, s.probs_tiled));
-        DG_HIP(hipMemcpyAsync(m->hflags + (size_t)(t & 1) * m->hflags_cap, stop,
-                              batch * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+                           s.fuse ? s.probs : nullptr, s.probs_tiled,
+                           m->hflags + (size_t)(t & 1) * m->hflags_cap));
         DG_HIP(hipEventRecord(m->flag_ev[t & 1], st));
         if (t > 0) DG_TRY(flags_of(t - 1, &done));
         if (p->selfcond_on) {

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     }
 }
 
-// One thread per (token, rotation pair j < dh/2); angles in double.
+// RoPE of q and k and the K/V cache write; angles in double.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv,
                                                       T* __restrict__ q_out, T* __restrict__ kc,
@@ -172,11 +172,15 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       int cap, int Hq, int Hkv, int dh,
                                                       int rope_on, double log_theta,
                                                       long total) {
+    // one thread per (token, head, rotation pair): heads [0, Hq) are query
+    // heads, [Hq, Hq + Hkv) key heads (whose value row is copied alongside)
     long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
     const int half = dh / 2;
     const int j = (int)(idx % half);
-    const long t = idx / half;          // token index b*n + i
+    const long r = idx / half;
+    const int hh = (int)(r % (Hq + Hkv));
+    const long t = r / (Hq + Hkv);      // token index b*n + i
     const int b = (int)(t / n), i = (int)(t % n);
     const long pos = pos0 + i;
     float c = 1.f, s = 0.f;
@@ -188,17 +192,17 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     const int width = (Hq + 2 * Hkv) * dh;
     const float* row = qkv + t * width;
-    for (int h = 0; h < Hq; ++h) {
-        float x1 = row[h * dh + j], x2 = row[h * dh + j + half];
-        T* o = q_out + t * (long)Hq * dh + (long)h * dh;
+    if (hh < Hq) {
+        const float x1 = row[hh * dh + j], x2 = row[hh * dh + j + half];
+        T* o = q_out + t * (long)Hq * dh + (long)hh * dh;
         o[j] = Elt<T>::from_f(x1 * c - x2 * s);
         o[j + half] = Elt<T>::from_f(x2 * c + x1 * s);
-    }
-    for (int h = 0; h < Hkv; ++h) {
+    } else {
+        const int h = hh - Hq;
         const float* kr = row + (Hq + h) * dh;
         const float* vr = row + (Hq + Hkv + h) * dh;
-        long slot = (((long)b * Hkv + h) * cap + pos) * dh;
-        float x1 = kr[j], x2 = kr[j + half];
+        const long slot = (((long)b * Hkv + h) * cap + pos) * dh;
+        const float x1 = kr[j], x2 = kr[j + half];
         kc[slot + j] = Elt<T>::from_f(x1 * c - x2 * s);
         kc[slot + j + half] = Elt<T>::from_f(x2 * c + x1 * s);
         vc[slot + j] = Elt<T>::from_f(vr[j]);
@@ -277,9 +281,9 @@ hipError_t transpose(const T* in, T* out, int rows, int cols, hipStream_t st) {
 template <typename T>
 hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int pos0, int cap,
                    int Hq, int Hkv, int dh, int rope_on, float theta, hipStream_t st) {
-    long total = (long)B * n * (dh / 2);
+    long total = (long)B * n * (Hq + Hkv) * (dh / 2);
     if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rope_kv_kernel<T>, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0,
+    hipLaunchKernelGGL(rope_kv_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        st, qkv, q_out, kc, vc, n, pos0, cap, Hq, Hkv, dh, rope_on,
                        log((double)theta), total);
     return hipGetLastError();

@@ -193,6 +193,7 @@ struct SampleArgs {
     int32_t* newmax = nullptr;       // scratch [B][N] argmax of this step
     int32_t* nstop = nullptr;        // optional: count of stopped sequences
     int32_t* halt = nullptr;         // optional: set to 1 once all B have stopped
+    int32_t* host_stop = nullptr;    // optional: the stop flags also go here (pinned host memory)
     // optional (V % 128 == 0): also write the self-conditioning weights of
     // the logits (selfcond_probs) as bf16 [B*N][V], 64-wide blocked
     // (probs_tiled, tiled64_index) or row-major, the operand of the next

@@ -576,7 +576,9 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
         yo[j] = j < a.k ? (long)a.slot_of[t * a.k + j] * a.d : 0;
     }
     float* hr = a.h + t * a.d;
-    for (int c = threadIdx.x * 4; c < a.d; c += 1024) {
+    // blockIdx.y: a 1024-column slice of the row, one float4 per thread
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < min(a.d, (int)(blockIdx.y + 1) * 1024);
+         c += 1024) {
         float4 acc = *reinterpret_cast<const float4*>(hr + c);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -639,7 +641,7 @@ hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
 
 hipError_t moe_combine(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.T, cdiv(a.d, 1024)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

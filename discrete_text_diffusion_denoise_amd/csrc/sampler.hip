@@ -579,7 +579,10 @@ __global__ __launch_bounds__(256) void selfcond_probs_kernel(const float* __rest
 // One workgroup per canvas: lock rule, renoise, stability and stop.
 __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
     const int b = blockIdx.x;
-    if (a.stop[b]) return;
+    if (a.stop[b]) {
+        if (threadIdx.x == 0 && a.host_stop) a.host_stop[b] = 1;
+        return;
+    }
     __shared__ uint64_t keys[1024];
     __shared__ float Hs[1024];
     __shared__ uint8_t lk[1024];
@@ -648,6 +651,7 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
         int st = (meanH < a.tau) && (!a.require_stable || stable);
         if (a.step + 1 >= a.max_steps) st = 1;
         a.stop[b] = st;
+        if (a.host_stop) a.host_stop[b] = st;
         // the last sequence to stop raises the halt flag
         if (st && a.nstop && atomicAdd(a.nstop, 1) + 1 == a.B) *a.halt = 1;
     }
