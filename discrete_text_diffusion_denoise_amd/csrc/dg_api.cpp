@@ -151,6 +151,7 @@ struct Scratch {
     float* gates;
     int32_t* counts;
     int32_t* offsets;
+    int32_t* order;
     int32_t* perm_tok;
     int32_t* slot_of;
     void* act;
@@ -209,6 +210,7 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.route = cv.take<int32_t>(T * c.top_k);
     s.gates = cv.take<float>(T * c.top_k);
     s.counts = cv.take<int32_t>(c.n_experts);
+    s.order = cv.take<int32_t>(c.n_experts);
     s.offsets = cv.take<int32_t>(c.n_experts + 1);
     s.perm_tok = cv.take<int32_t>(T * c.top_k);
     s.slot_of = cv.take<int32_t>(T * c.top_k);
@@ -430,6 +432,7 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.gates = s.gates;
     a.counts = s.counts;
     a.offsets = s.offsets;
+    a.order = s.order;
     a.perm_tok = s.perm_tok;
     a.slot_of = s.slot_of;
     a.u = s.u;

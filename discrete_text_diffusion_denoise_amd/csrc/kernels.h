@@ -155,6 +155,7 @@ struct MoeArgs {
     float* gates = nullptr;          // [T][k]
     int32_t* counts = nullptr;       // [E]
     int32_t* offsets = nullptr;      // [E+1]
+    int32_t* order = nullptr;        // optional [E]: experts by falling count (ties: lower id)
     int32_t* perm_tok = nullptr;     // [T*k] token of each sorted slot
     int32_t* slot_of = nullptr;      // [T*k] sorted slot of (t, j)
     const void* u = nullptr;         // normalised tokens [T][d] (T)

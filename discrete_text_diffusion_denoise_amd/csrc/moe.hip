@@ -83,6 +83,19 @@ __global__ __launch_bounds__(256) void count_kernel(MoeArgs a) {
     if (threadIdx.x == 0) a.counts[e] = part[0];
 }
 
+// Experts by falling count (ties: lower id) from the counts.
+__global__ __launch_bounds__(256) void order_kernel(MoeArgs a) {
+    const int e = threadIdx.x;
+    if (e >= a.E) return;
+    const int me = a.counts[e];
+    int rank = 0;
+    for (int e2 = 0; e2 < a.E; ++e2) {
+        const int o = a.counts[e2];
+        rank += (o > me) || (o == me && e2 < e);
+    }
+    a.order[rank] = e;
+}
+
 // One wave per expert: exclusive prefix of counts, then a stable, ordered
 // placement of the pairs routed to e (ballot + popcount), so the permutation
 // is deterministic.
@@ -299,65 +312,45 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_barrier();
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
-    if (a.halt && *a.halt) return;
-    constexpr int WR = MODE == 0 ? 64 : 32;            // weight rows per stage
-    constexpr int WQ = WR / 32;                        // weight DMAs per wave per stage
-    constexpr int PER = WQ + 2;                        // DMAs per wave per stage
-    __shared__ __align__(1024) unsigned char w0[WR * 128], x0[8192];
-    __shared__ __align__(1024) unsigned char w1[WR * 128], x1[8192];
-    __shared__ __align__(1024) unsigned char w2[WR * 128], x2[8192];
-    __shared__ __align__(1024) unsigned char w3[WR * 128], x3[8192];
+// One expert's token groups against one block of weight rows: a four-stage
+// ring of direct-to-LDS loads (64 weight rows x 64 k and 32 * G token rows x
+// 64 k per stage), G = 1 or 2 groups of 32 tokens per pass over the weights.
+struct XdCtx {
+    int e, off, cnt, K, NOUT, c0, n, rot;
+    int lane, wave, r16, g4, ct, mp, lr, lc;
+    const bf16_t* wsrc[2];
+    const bf16_t* X;
+};
 
-    const int e = blockIdx.y;
-    const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
-    if (cnt == 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const int ct = wave & 1, mp = wave >> 1;
-    const int K = MODE == 0 ? a.d : a.F;
-    const int NOUT = MODE == 0 ? a.F : a.d;
-    const int c0 = blockIdx.x * 32;
-    const int n = __builtin_amdgcn_readfirstlane(K / 64);   // stages, a multiple of 4
-    const int rot = __builtin_amdgcn_readfirstlane(
-        a.k_rotate ? (int)((blockIdx.x + blockIdx.y * 5) % n) : 0);
-    const bf16_t* Wg = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.w_gate : a.w_down);
-    const bf16_t* Wu = reinterpret_cast<const bf16_t*>(a.w_up);
-    const bf16_t* X = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.u : a.act);
-
-    // DMA lanes: an instruction fills 8 rows x 128 bytes; lane l takes row
-    // l / 8 of them and global chunk (l % 8) ^ (row & 7)
-    const int lr = lane >> 3;
-    const int lc = ((lane & 7) ^ lr) * 8;             // element offset (rows are 8-aligned)
-    const bf16_t* wsrc[WQ];
-#pragma unroll
-    for (int q = 0; q < WQ; ++q) {
-        const int r = (wave * WQ + q) * 8 + lr;        // weight row within the block
-        const int rr = MODE == 0 ? (r & 31) : r;
-        const int col = min(c0 + rr, NOUT - 1);
-        const bf16_t* base = (MODE == 0 && r >= 32) ? Wu : Wg;
-        wsrc[q] = base + ((long)e * NOUT + col) * K + lc;
-    }
-    const int wblk = wave * WQ * 1024;
-    const int xblk = wave * 2 * 1024;
+template <int MODE, int G>
+__device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, unsigned char* w0,
+                                              unsigned char* w1, unsigned char* w2, unsigned char* w3,
+                                              unsigned char* x0, unsigned char* x1, unsigned char* x2,
+                                              unsigned char* x3) {
+    constexpr int WQ = 2;                              // weight DMAs per wave per stage
+    constexpr int PER = WQ + G;                        // DMAs per wave per stage
+    const int n = c.n, rot = c.rot, mp = c.mp, ct = c.ct, r16 = c.r16, g4 = c.g4;
+    const int wblk = c.wave * WQ * 1024;
+    const int xblk = c.wave * G * 1024;
     const int roff = r16 * 128;
-
-    for (int mg = 0; mg < cnt; mg += 64) {
-        const bf16_t* xsrc[2];
+    for (int mg = 0; mg < c.cnt; mg += 32 * G) {
+        const bf16_t* xsrc[G];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int tok = min(mg + (wave * 2 + q) * 8 + lr, cnt - 1);
-            const long src = MODE == 0 ? (long)a.perm_tok[off + tok] : (long)(off + tok);
-            xsrc[q] = X + src * K + lc;
+        for (int q = 0; q < G; ++q) {
+            const int tok = min(mg + (c.wave * G + q) * 8 + c.lr, c.cnt - 1);
+            const long src = MODE == 0 ? (long)a.perm_tok[c.off + tok] : (long)(c.off + tok);
+            xsrc[q] = c.X + src * c.K + c.lc;
         }
-        f32x4_t ag[2], au[2];
+        // wave: token tiles mp (and mp + 2 when G = 2), column tile ct of
+        // both halves of the weight block
+        f32x4_t ag[G], au[G];
+        bool tv[G];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < G; ++q) {
             ag[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             au[q] = ag[q];
+            tv[q] = mg + 16 * (mp + 2 * q) < c.cnt;
         }
-        const bool t0 = mg + 16 * mp < cnt, t1 = mg + 16 * (mp + 2) < cnt;
 
 #define XD_ISSUE(ST, WB, XB)                                                                      \
         {                                                                                         \
@@ -365,66 +358,54 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
             if (sr_ >= n) sr_ -= n;                                                               \
             const int k_ = sr_ * 64;                                                              \
             _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                        \
-                __builtin_amdgcn_global_load_lds((glb_void*)(wsrc[q] + k_),                       \
+                __builtin_amdgcn_global_load_lds((glb_void*)(c.wsrc[q] + k_),                     \
                                                  (lds_void*)((WB) + wblk + q * 1024), 16, 0, 0);  \
-            _Pragma("unroll") for (int q = 0; q < 2; ++q)                                         \
+            _Pragma("unroll") for (int q = 0; q < G; ++q)                                         \
                 __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
                                                  (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
         }
-        // fragments: token rows 16*mt + r16 (two tiles), weight rows ct*16 + r16
-        // (and 32 + ct*16 + r16 for the up half); chunk 4*s + g4 of k-step s
+        // fragments: token rows 16*(mp + 2q) + r16, weight rows ct*16 + r16 and
+        // 32 + ct*16 + r16 (up half, or down columns 32..63); chunk 4*s + g4 of
+        // k-step s
 #define XD_COMPUTE(WB, XB)                                                                        \
         {                                                                                         \
-            u32x4 fx0a, fx0b, fx1a, fx1b, fga, fgb, fua, fub;                                     \
-            const uint32_t xa0 = lds_addr(XB) + (16 * mp) * 128 + roff;                           \
-            const uint32_t xa1 = xa0 + 32 * 128;                                                  \
+            u32x4 fga, fgb, fua, fub, fxa[G], fxb[G];                                             \
+            const uint32_t xa = lds_addr(XB) + (16 * mp) * 128 + roff;                            \
             const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                            \
             const uint32_t sa = ((g4 ^ (r16 & 7)) << 4), sb = (((4 + g4) ^ (r16 & 7)) << 4);      \
-            if (MODE == 0) {                                                                      \
+            if (G == 1) {                                                                         \
+                asm volatile(                                                                     \
+                    "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                                  \
+                    "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                                  \
+                    "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                                \
+                    "s_waitcnt lgkmcnt(0)"                                                         \
+                    : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub) \
+                    : "v"(xa + sa), "v"(xa + sb), "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), \
+                      "v"(wa + 32 * 128 + sb)                                                     \
+                    : "memory");                                                                  \
+            } else {                                                                              \
                 asm volatile(                                                                     \
                     "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                                  \
                     "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                                \
                     "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                                \
                     "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                                \
                     "s_waitcnt lgkmcnt(0)"                                                         \
-                    : "=&v"(fx0a), "=&v"(fx0b), "=&v"(fx1a), "=&v"(fx1b), "=&v"(fga), "=&v"(fgb), \
-                      "=&v"(fua), "=&v"(fub)                                                      \
-                    : "v"(xa0 + sa), "v"(xa0 + sb), "v"(xa1 + sa), "v"(xa1 + sb), "v"(wa + sa),   \
-                      "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb)              \
-                    : "memory");                                                                  \
-            } else {                                                                              \
-                asm volatile(                                                                     \
-                    "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                                  \
-                    "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                                  \
-                    "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                                \
-                    "s_waitcnt lgkmcnt(0)"                                                         \
-                    : "=&v"(fx0a), "=&v"(fx0b), "=&v"(fx1a), "=&v"(fx1b), "=&v"(fga), "=&v"(fgb)  \
-                    : "v"(xa0 + sa), "v"(xa0 + sb), "v"(xa1 + sa), "v"(xa1 + sb), "v"(wa + sa),   \
-                      "v"(wa + sb)                                                                \
+                    : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),          \
+                      "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub)                              \
+                    : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa), "v"(xa + 32 * 128 + sb), \
+                      "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb) \
                     : "memory");                                                                  \
             }                                                                                     \
-            if (t0) {                                                                             \
-                ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0a), \
-                    __builtin_bit_cast(bf16x8_t, fga), ag[0], 0, 0, 0);                           \
-                ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0b), \
-                    __builtin_bit_cast(bf16x8_t, fgb), ag[0], 0, 0, 0);                           \
-                if (MODE == 0) {                                                                  \
-                    au[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0a), \
-                        __builtin_bit_cast(bf16x8_t, fua), au[0], 0, 0, 0);                       \
-                    au[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx0b), \
-                        __builtin_bit_cast(bf16x8_t, fub), au[0], 0, 0, 0);                       \
-                }                                                                                 \
-            }                                                                                     \
-            if (t1) {                                                                             \
-                ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1a), \
-                    __builtin_bit_cast(bf16x8_t, fga), ag[1], 0, 0, 0);                           \
-                ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1b), \
-                    __builtin_bit_cast(bf16x8_t, fgb), ag[1], 0, 0, 0);                           \
-                if (MODE == 0) {                                                                  \
-                    au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1a), \
-                        __builtin_bit_cast(bf16x8_t, fua), au[1], 0, 0, 0);                       \
-                    au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fx1b), \
-                        __builtin_bit_cast(bf16x8_t, fub), au[1], 0, 0, 0);                       \
+            _Pragma("unroll") for (int q = 0; q < G; ++q) {                                       \
+                if (tv[q]) {                                                                      \
+                    ag[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+                        __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fga), ag[q], 0, 0, 0); \
+                    ag[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+                        __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fgb), ag[q], 0, 0, 0); \
+                    au[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+                        __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fua), au[q], 0, 0, 0); \
+                    au[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
+                        __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fub), au[q], 0, 0, 0); \
                 }                                                                                 \
             }                                                                                     \
         }
@@ -453,22 +434,24 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
 #undef XD_COMPUTE
 #undef XD_ISSUE
 
-        // lane holds tokens 4*g4 + i of tile mt, output column c0 + ct*16 + r16
-        const int col = c0 + ct * 16 + r16;
-        if (col < NOUT) {
+        // lane holds tokens 4*g4 + i of tile mp + 2q, output column
+        // c0 + ct*16 + r16 (and c0 + 32 + ct*16 + r16 for the second half of
+        // the down projection)
+        const int col = c.c0 + ct * 16 + r16;
+        if (col < c.NOUT) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int mt = mp + 2 * q;
+            for (int q = 0; q < G; ++q) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = mg + 16 * mt + 4 * g4 + i;
-                    if (row >= cnt) continue;
+                    const int row = mg + 16 * (mp + 2 * q) + 4 * g4 + i;
+                    if (row >= c.cnt) continue;
                     if constexpr (MODE == 0) {
                         const float gv = ag[q][i], uv = au[q][i];
                         const float sv = gv / (1.0f + __expf(-gv));
-                        reinterpret_cast<bf16_t*>(a.act)[(long)(off + row) * a.F + col] = f2bf(sv * uv);
+                        reinterpret_cast<bf16_t*>(a.act)[(long)(c.off + row) * a.F + col] = f2bf(sv * uv);
                     } else {
-                        a.y[(long)(off + row) * a.d + col] = ag[q][i];
+                        a.y[(long)(c.off + row) * a.d + col] = ag[q][i];
+                        if (col + 32 < c.NOUT) a.y[(long)(c.off + row) * a.d + col + 32] = au[q][i];
                     }
                 }
             }
@@ -476,6 +459,61 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
         // the next group's loads refill the ring only after every wave is done
         barrier_lds();
     }
+}
+
+// 64 weight rows per block: gate and up rows of 32 columns (MODE 0), or 64
+// columns of the down projection (MODE 1); blockIdx.y walks the experts in
+// `order` when it is set.  An expert with at most 32
+// tokens (most of them: a 256-token canvas makes 2048 assignments over 128
+// experts) runs groups of 32, a busier one groups of 64, so its weights are
+// streamed fewer times.
+template <int MODE>
+__global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
+    if (a.halt && *a.halt) return;
+    __shared__ __align__(1024) unsigned char w0[64 * 128], x0[8192];
+    __shared__ __align__(1024) unsigned char w1[64 * 128], x1[8192];
+    __shared__ __align__(1024) unsigned char w2[64 * 128], x2[8192];
+    __shared__ __align__(1024) unsigned char w3[64 * 128], x3[8192];
+
+    XdCtx c;
+    // the busiest experts first, so their longer blocks do not form the tail
+    c.e = a.order ? a.order[blockIdx.y] : (int)blockIdx.y;
+    c.off = a.offsets[c.e];
+    c.cnt = a.offsets[c.e + 1] - c.off;
+    if (c.cnt == 0) return;
+    const int tid = threadIdx.x;
+    c.lane = tid & 63;
+    c.wave = tid >> 6;
+    c.r16 = c.lane & 15;
+    c.g4 = c.lane >> 4;
+    c.ct = c.wave & 1;
+    c.mp = c.wave >> 1;
+    c.K = MODE == 0 ? a.d : a.F;
+    c.NOUT = MODE == 0 ? a.F : a.d;
+    c.c0 = blockIdx.x * (MODE == 0 ? 32 : 64);
+    c.n = __builtin_amdgcn_readfirstlane(c.K / 64);   // stages, a multiple of 4
+    // the starting stage depends on (column block, expert) only, so a token's
+    // sum runs in the same order whatever the other tokens of the batch are
+    c.rot = __builtin_amdgcn_readfirstlane(a.k_rotate ? (int)((blockIdx.x + c.e * 5) % c.n) : 0);
+    const bf16_t* Wg = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.w_gate : a.w_down);
+    const bf16_t* Wu = reinterpret_cast<const bf16_t*>(a.w_up);
+    c.X = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.u : a.act);
+    // DMA lanes: an instruction fills 8 rows x 128 bytes; lane l takes row
+    // l / 8 of them and global chunk (l % 8) ^ (row & 7)
+    c.lr = c.lane >> 3;
+    c.lc = ((c.lane & 7) ^ c.lr) * 8;                 // element offset (rows are 8-aligned)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (c.wave * 2 + q) * 8 + c.lr;     // weight row within the block
+        const int rr = MODE == 0 ? (r & 31) : r;
+        const int col = min(c.c0 + rr, c.NOUT - 1);
+        const bf16_t* base = (MODE == 0 && r >= 32) ? Wu : Wg;
+        c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + c.lc;
+    }
+    if (__builtin_amdgcn_readfirstlane(c.cnt) <= 32)
+        expert_groups<MODE, 1>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
+    else
+        expert_groups<MODE, 2>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
 }
 
 // Counts, offsets and the stable placement in one workgroup.  The
@@ -504,6 +542,16 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
         int c = 0;
         for (int w = 0; w < PW; ++w) c += cw[w][tid];
         tot[tid] = c;
+    }
+    __syncthreads();
+    if (a.order && tid < a.E) {                        // rank by falling count
+        const int me = tot[tid];
+        int rank = 0;
+        for (int e2 = 0; e2 < a.E; ++e2) {
+            const int o = tot[e2];
+            rank += (o > me) || (o == me && e2 < tid);
+        }
+        a.order[rank] = tid;
     }
     __syncthreads();
     if (tid < 64) {                                    // exclusive scan of the totals
@@ -605,6 +653,7 @@ hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     } else {
         hipLaunchKernelGGL(count_kernel, dim3(a.E), dim3(256), 0, st, a);
         hipLaunchKernelGGL(place_kernel, dim3(a.E), dim3(64), 0, st, a);
+        if (a.order) hipLaunchKernelGGL(order_kernel, dim3(1), dim3(256), 0, st, a);
     }
     return hipGetLastError();
 }
@@ -633,7 +682,7 @@ template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL(expert_dma_kernel<1>, dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(expert_dma_kernel<1>, dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
