@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="layer", choices=["layer", "stack"])
+    ap.add_argument("--config", default="layer", choices=["layer", "layer_fp8", "stack"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the measurement, two 1 GiB device copies (counter calibration)")
@@ -62,10 +62,22 @@ def device_weights(cfg, seed, torch):
 
     W = {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": []}
     for _ in range(cfg["n_layers"]):
-        W["layers"].append({"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
-                            "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
-                            "w_router": draw(E, d), "w_gate": draw(E, F, d),
-                            "w_up": draw(E, F, d), "w_down": draw(E, d, F)})
+        lw = {"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
+              "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
+              "w_router": draw(E, d), "w_gate": draw(E, F, d), "w_up": draw(E, F, d),
+              "w_down": draw(E, d, F)}
+        if cfg.get("expert_dtype") == "fp8":
+            # 8-bit experts: the same draws, quantised on the GPU by the
+            # library (E4M3 codes, one scale per weight row)
+            from discrete_text_diffusion_denoise_amd import binding
+            for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+                w = lw[k]
+                q = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+                sc = torch.empty(w.shape[:-1], dtype=torch.float32, device="cuda")
+                binding.quantize_fp8(w, q, sc)
+                lw[k], lw[sk] = q, sc
+            torch.cuda.synchronize()
+        W["layers"].append(lw)
     return W
 
 
@@ -73,6 +85,10 @@ def kernel_work(name, cfg, B, P, sc_splits):
     """Algorithmic (flops, bytes) of one launch of a timed kernel: every
     weight read once, activations read/written once."""
     es = 2 if cfg["dtype"] == "bf16" else 4
+    # expert weight bytes per element (8-bit experts also read one fp32
+    # scale per weight row)
+    fp8 = cfg.get("expert_dtype") == "fp8"
+    ew = 1 if fp8 else es
     N, V, d = cfg["canvas"], cfg["vocab"], cfg["d_model"]
     Hq, Hkv, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     E, k, F = cfg["n_experts"], cfg["top_k"], cfg["d_ff"]
@@ -85,9 +101,11 @@ def kernel_work(name, cfg, B, P, sc_splits):
         # bf16 models read the softmax probabilities in bf16 (written by a pre-pass)
         return 2.0 * T * d * V, T * V * es + d * V * es + sc_splits * T * d * 4.0
     if name == "moe_gateup":
-        return 2.0 * T * k * 2 * F * d, hit * 2 * F * d * es + T * d * es + T * k * F * es
+        return (2.0 * T * k * 2 * F * d,
+                hit * 2 * F * (d * ew + (4 if fp8 else 0)) + T * d * es + T * k * F * es)
     if name == "moe_down":
-        return 2.0 * T * k * F * d, hit * d * F * es + T * k * F * es + T * k * d * 4.0
+        return (2.0 * T * k * F * d,
+                hit * d * (F * ew + (4 if fp8 else 0)) + T * k * F * es + T * k * d * 4.0)
     if name == "attention":
         L = P + N
         return (4.0 * T * L * Hq * dh,
@@ -157,7 +175,16 @@ def cpu_baseline(cfg, W, prompt, canvas, params, torch):
     host = {"embed": W["embed"].float().cpu().numpy(), "w_sc": W["w_sc"].float().cpu().numpy(),
             "final_norm": W["final_norm"].cpu().numpy().astype(np.float64), "layers": []}
     for lw in W["layers"]:
-        host["layers"].append({k: v.float().cpu().numpy() for k, v in lw.items()})
+        hl = {k: v.float().cpu().numpy() for k, v in lw.items() if not k.startswith("s_")}
+        if cfg.get("expert_dtype") == "fp8":
+            # the oracle's experts are the dequantised codes
+            from oracle import quant as oq
+            for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+                q = lw[k].cpu().numpy()
+                sc = lw[sk].cpu().numpy()
+                hl[k] = oq.dequantize_rows(q.reshape(-1, q.shape[-1]),
+                                           sc.reshape(-1)).reshape(q.shape)
+        host["layers"].append(hl)
     B, N, V = canvas.shape[0], cfg["canvas"], cfg["vocab"]
     P = prompt.shape[1]
     cache = om.KVCache(cfg, B)
@@ -299,11 +326,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg["dtype"],
+        "dtype": cfg["dtype"] + ("+fp8-experts" if cfg.get("expert_dtype") == "fp8" else ""),
         "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt tokens)",
         "config": {"workload": (f"{args.config}: {cfg['n_layers']} denoiser layer(s) d{cfg['d_model']} "
                                 f"{cfg['n_heads']}q/{cfg['n_kv_heads']}kv x{cfg['head_dim']}, "
-                                f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}, "
+                                f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}"
+                                f"{' (E4M3 weights, per-row scales)' if cfg.get('expert_dtype') == 'fp8' else ''}, "
                                 f"vocab {V}, prompt {P}, canvas {N}, batch {B}; one step = one "
                                 f"block (<=48 self-conditioned rounds + commit)"),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdg.so")
 _lib = None
 
-DG_F32, DG_BF16 = 0, 1
+DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 LOCK_MAXPROB, LOCK_CUMENT = 0, 1
 STATUS = {0: "DG_OK", 1: "DG_ERR_ARG", 2: "DG_ERR_SHAPE", 3: "DG_ERR_DTYPE",
           4: "DG_ERR_CAPACITY", 5: "DG_ERR_NONFINITE", 6: "DG_ERR_HIP", 7: "DG_ERR_UNSUPPORTED"}
@@ -36,13 +36,13 @@ class Config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("canvas", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rope_on", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("expert_dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("attn_norm", "wq", "wk", "wv", "wo", "moe_norm", "w_router", "w_gate", "w_up",
-                 "w_down")]
+                 "w_down", "s_gate", "s_up", "s_down")]
 
 
 class Weights(ctypes.Structure):
@@ -69,6 +69,7 @@ _SIGS = {
     "dg_embed_transpose": (_I, [_P, _P, _P, _P]),
     "dg_embed_head_bytes": (_I, [_P, _P]),
     "dg_embed_head": (_I, [_P, _P, _P, _P]),
+    "dg_quantize_fp8": (_I, [_P, _I, ctypes.c_int64, _I, _P, _P, _P]),
     "dg_kv_bytes": (_I, [_P, _I, _I, _P]),
     "dg_kv_create": (_I, [_P, _I, _I, _P, _P]),
     "dg_kv_destroy": (None, [_P]),
@@ -165,20 +166,35 @@ class Model:
 
         self.w = {"embed": dev(weights["embed"]), "w_sc": dev(weights["w_sc"]),
                   "final_norm": dev(weights["final_norm"], torch.float32)}
+        # 8-bit experts: w_gate / w_up / w_down hold E4M3 codes (uint8) and
+        # s_gate / s_up / s_down their per-row fp32 scales
+        fp8 = cfg.get("expert_dtype") == "fp8"
+
+        def ldtype(k):
+            if k.endswith("norm") or k.startswith("s_"):
+                return torch.float32
+            if fp8 and k in ("w_gate", "w_up", "w_down"):
+                return torch.uint8
+            return None
+
         self.lw = []
         for lw in weights["layers"]:
-            d = {k: dev(v, torch.float32 if k.endswith("norm") else None) for k, v in lw.items()}
+            d = {k: dev(v, ldtype(k)) for k, v in lw.items()}
             self.lw.append(d)
         c = Config(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"],
                    cfg["head_dim"], cfg["n_experts"], cfg["top_k"], cfg["d_ff"], cfg["vocab"],
                    cfg["canvas"], DG_BF16 if cfg["dtype"] == "bf16" else DG_F32,
-                   int(cfg["rope_on"]), float(cfg["rope_theta"]), float(cfg["rms_eps"]))
+                   int(cfg["rope_on"]), float(cfg["rope_theta"]), float(cfg["rms_eps"]),
+                   DG_FP8_E4M3 if fp8 else 0)
         self._cfg_struct = c
         layer_arr = (LayerWeights * cfg["n_layers"])()
         for i, d in enumerate(self.lw):
             for k in ("attn_norm", "wq", "wk", "wv", "wo", "moe_norm", "w_router", "w_gate",
                       "w_up", "w_down"):
                 setattr(layer_arr[i], k, d[k].data_ptr())
+            if fp8:
+                for k in ("s_gate", "s_up", "s_down"):
+                    setattr(layer_arr[i], k, d[k].data_ptr())
         self._layer_arr = layer_arr
         self.w["embed_t"] = torch.empty((cfg["d_model"], cfg["vocab"]), dtype=self.dtype,
                                         device=self.device)
@@ -330,6 +346,15 @@ def stage_probs(logits, stats, probs, blocked: bool, stream=None):
     T, V = logits.shape
     _check(lib().dg_stage_probs(T, V, 1 if blocked else 0, _ptr(logits), _ptr(stats), _ptr(probs),
                                 _stream(stream)))
+
+
+def quantize_fp8(src, q, scale, stream=None):
+    """dg_quantize_fp8: src [..., cols] (f32 or bf16) -> q (uint8, same shape)
+    and scale (f32, one per row)."""
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    dt = DG_BF16 if src.dtype == torch.bfloat16 else DG_F32
+    _check(lib().dg_quantize_fp8(_ptr(src), dt, rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
 
 
 def timer_enable(names) -> None:

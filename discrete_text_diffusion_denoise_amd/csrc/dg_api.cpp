@@ -433,6 +433,12 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.counts = s.counts;
     a.offsets = s.offsets;
     a.order = s.order;
+    if (c.expert_dtype == DG_FP8_E4M3) {
+        a.f8 = 1;
+        a.s_gate = L.s_gate;
+        a.s_up = L.s_up;
+        a.s_down = L.s_down;
+    }
     a.perm_tok = s.perm_tok;
     a.slot_of = s.slot_of;
     a.u = s.u;
@@ -637,6 +643,23 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
         if (!L.wq || !L.wk || !L.wv || !L.wo || !L.w_router || !L.w_gate || !L.w_up || !L.w_down)
             return fail(DG_ERR_ARG, "missing weights in layer %d", l);
     }
+    if (c.expert_dtype != 0 && c.expert_dtype != c.dtype && c.expert_dtype != DG_FP8_E4M3)
+        return fail(DG_ERR_DTYPE, "expert_dtype %d", c.expert_dtype);
+    if (c.expert_dtype == DG_FP8_E4M3) {
+        // the 8-bit experts run on the direct-to-LDS ring kernels only
+        dg::MoeArgs probe;
+        probe.d = c.d_model;
+        probe.F = c.d_ff;
+        probe.f8 = 1;
+        if (c.dtype != DG_BF16 || !dg::expert_dma_ok(probe))
+            return fail(DG_ERR_UNSUPPORTED,
+                        "FP8 experts need a bf16 model with d_model and d_ff multiples of 256");
+        for (int l = 0; l < c.n_layers; ++l) {
+            const dg_layer_weights& L = w->layers[l];
+            if (!L.s_gate || !L.s_up || !L.s_down)
+                return fail(DG_ERR_ARG, "FP8 experts need s_gate, s_up and s_down (layer %d)", l);
+        }
+    }
     dg_model* m = new dg_model;
     m->c = c;
     m->embed = w->embed;
@@ -651,6 +674,21 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
 }
 
 void dg_model_destroy(dg_model* m) { delete m; }
+
+dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
+                          void* d_q, float* d_scale, void* stream) {
+    if (!d_src || !d_q || !d_scale) return fail(DG_ERR_ARG, "NULL pointer");
+    if (rows < 1 || cols < 1 || rows > 0x7FFFFFFF) return fail(DG_ERR_ARG, "bad sizes");
+    if (src_dtype == DG_BF16)
+        DG_HIP(dg::quantize_fp8<bf16_t>((const bf16_t*)d_src, (long)rows, cols, (uint8_t*)d_q,
+                                        d_scale, as_stream(stream)));
+    else if (src_dtype == DG_F32)
+        DG_HIP(dg::quantize_fp8<float>((const float*)d_src, (long)rows, cols, (uint8_t*)d_q,
+                                       d_scale, as_stream(stream)));
+    else
+        return fail(DG_ERR_DTYPE, "src_dtype %d", src_dtype);
+    return DG_OK;
+}
 
 dg_status dg_embed_transpose(const dg_model* m, const void* d_embed, void* d_out, void* stream) {
     DG_TRY(check_model(m));

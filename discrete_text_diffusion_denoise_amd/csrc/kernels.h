@@ -167,6 +167,12 @@ struct MoeArgs {
     float* h = nullptr;              // residual [T][d]
     int k_rotate = 0;                // rotate each block's starting k-stage
     const int32_t* halt = nullptr;   // expert kernels: skip all work when *halt != 0
+    // 8-bit experts: w_gate / w_up / w_down hold E4M3 codes, one fp32 scale
+    // per weight row (s_gate, s_up [E][F]; s_down [E][d])
+    int f8 = 0;
+    const float* s_gate = nullptr;
+    const float* s_up = nullptr;
+    const float* s_down = nullptr;
 };
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);
@@ -175,6 +181,16 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st);
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st);
 hipError_t moe_combine(const MoeArgs& a, hipStream_t st);
+// the ring kernels' shape limits (d and F multiples of 256); 8-bit experts
+// run on them only
+bool expert_dma_ok(const MoeArgs& a);
+
+// E4M3 codes and per-row scales of src [rows][cols] (T = float or bf16_t):
+// scale = max|x| / 448 (1 for a zero row), code = round-to-nearest-even of
+// x / scale, saturating at 448
+template <typename T>
+hipError_t quantize_fp8(const T* src, long rows, int cols, uint8_t* q, float* scale,
+                        hipStream_t st);
 
 // ------------------------------------------------------------------ sampler
 struct SampleArgs {

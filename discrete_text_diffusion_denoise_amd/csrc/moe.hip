@@ -315,24 +315,55 @@ __device__ __forceinline__ void barrier_lds() {
 // One expert's token groups against one block of weight rows: a four-stage
 // ring of direct-to-LDS loads (64 weight rows x 64 k and 32 * G token rows x
 // 64 k per stage), G = 1 or 2 groups of 32 tokens per pass over the weights.
+// F8: the weight rows hold E4M3 codes (64 bytes per row and stage), widened
+// to bf16 in registers (exactly: E4M3 values are bf16 values) and scaled per
+// output column after the sum.
 struct XdCtx {
     int e, off, cnt, K, NOUT, c0, n, rot;
     int lane, wave, r16, g4, ct, mp, lr, lc;
-    const bf16_t* wsrc[2];
+    const char* wsrc[2];     // byte addresses of this lane's weight chunks at k = 0
     const bf16_t* X;
 };
 
-template <int MODE, int G>
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (two words, increasing k) -> 8 bf16 values
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    return u32x4{pack_bf2(a.x, a.y), pack_bf2(b.x, b.y), pack_bf2(c.x, c.y), pack_bf2(d.x, d.y)};
+}
+
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int MODE, int G, bool F8>
 __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, unsigned char* w0,
                                               unsigned char* w1, unsigned char* w2, unsigned char* w3,
                                               unsigned char* x0, unsigned char* x1, unsigned char* x2,
                                               unsigned char* x3) {
-    constexpr int WQ = 2;                              // weight DMAs per wave per stage
+    constexpr int WQ = F8 ? 1 : 2;                     // weight DMAs per wave per stage
     constexpr int PER = WQ + G;                        // DMAs per wave per stage
+    constexpr int WSTAGE = F8 ? 64 : 128;              // weight bytes per row and stage
     const int n = c.n, rot = c.rot, mp = c.mp, ct = c.ct, r16 = c.r16, g4 = c.g4;
     const int wblk = c.wave * WQ * 1024;
     const int xblk = c.wave * G * 1024;
     const int roff = r16 * 128;
+    // per-column scales of the 8-bit weights (column col, and col + 32 for
+    // the down projection's second half)
+    const int col = c.c0 + ct * 16 + r16;
+    float sc0 = 1.0f, sc1 = 1.0f;
+    if (F8 && col < c.NOUT) {
+        if (MODE == 0) {
+            sc0 = a.s_gate[(long)c.e * c.NOUT + col];
+            sc1 = a.s_up[(long)c.e * c.NOUT + col];
+        } else {
+            sc0 = a.s_down[(long)c.e * c.NOUT + col];
+            sc1 = col + 32 < c.NOUT ? a.s_down[(long)c.e * c.NOUT + col + 32] : 1.0f;
+        }
+    }
     for (int mg = 0; mg < c.cnt; mg += 32 * G) {
         const bf16_t* xsrc[G];
 #pragma unroll
@@ -358,43 +389,80 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             if (sr_ >= n) sr_ -= n;                                                               \
             const int k_ = sr_ * 64;                                                              \
             _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                        \
-                __builtin_amdgcn_global_load_lds((glb_void*)(c.wsrc[q] + k_),                     \
+                __builtin_amdgcn_global_load_lds((glb_void*)(c.wsrc[q] + (long)sr_ * WSTAGE),     \
                                                  (lds_void*)((WB) + wblk + q * 1024), 16, 0, 0);  \
             _Pragma("unroll") for (int q = 0; q < G; ++q)                                         \
                 __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
                                                  (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
         }
         // fragments: token rows 16*(mp + 2q) + r16, weight rows ct*16 + r16 and
-        // 32 + ct*16 + r16 (up half, or down columns 32..63); chunk 4*s + g4 of
-        // k-step s
+        // 32 + ct*16 + r16 (up half, or down columns 32..63).  bf16 weights:
+        // k-step s of a lane is chunk 4*s + g4 of both operands; 8-bit
+        // weights: the lane's 16 codes are chunk g4 of the 64-byte row (k
+        // 16*g4 .. 16*g4+15), so its token chunks are 2*g4 (k-step 0) and
+        // 2*g4 + 1 (k-step 1): every k of the stage is in exactly one k-step
+        // of one lane group, as the sum needs
 #define XD_COMPUTE(WB, XB)                                                                        \
         {                                                                                         \
             u32x4 fga, fgb, fua, fub, fxa[G], fxb[G];                                             \
             const uint32_t xa = lds_addr(XB) + (16 * mp) * 128 + roff;                            \
-            const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                            \
-            const uint32_t sa = ((g4 ^ (r16 & 7)) << 4), sb = (((4 + g4) ^ (r16 & 7)) << 4);      \
-            if (G == 1) {                                                                         \
-                asm volatile(                                                                     \
-                    "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                                  \
-                    "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                                  \
-                    "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                                \
-                    "s_waitcnt lgkmcnt(0)"                                                         \
-                    : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub) \
-                    : "v"(xa + sa), "v"(xa + sb), "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), \
-                      "v"(wa + 32 * 128 + sb)                                                     \
-                    : "memory");                                                                  \
+            const int xs = r16 & 7;                                                               \
+            const uint32_t sa = F8 ? ((2 * g4) ^ xs) << 4 : (g4 ^ xs) << 4;                       \
+            const uint32_t sb = F8 ? ((2 * g4 + 1) ^ xs) << 4 : ((4 + g4) ^ xs) << 4;             \
+            if (F8) {                                                                             \
+                const int wr = ct * 16 + r16;                                                     \
+                const uint32_t wg_ = lds_addr(WB) + wr * 64 + ((g4 ^ swz4(wr)) << 4);             \
+                const uint32_t wu_ = lds_addr(WB) + (wr + 32) * 64 + ((g4 ^ swz4(wr + 32)) << 4); \
+                u32x4 cg, cu;                                                                     \
+                if (G == 1) {                                                                     \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %4\n ds_read_b128 %1, %5\n"                              \
+                        "ds_read_b128 %2, %6\n ds_read_b128 %3, %7\n"                              \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cg), "=&v"(cu)                      \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(wg_), "v"(wu_)                          \
+                        : "memory");                                                              \
+                } else {                                                                          \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                              \
+                        "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                              \
+                        "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                            \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
+                          "=&v"(cg), "=&v"(cu)                                                    \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa),                    \
+                          "v"(xa + 32 * 128 + sb), "v"(wg_), "v"(wu_)                             \
+                        : "memory");                                                              \
+                }                                                                                 \
+                fga = e4m3x8_to_bf16(cg[0], cg[1]);                                               \
+                fgb = e4m3x8_to_bf16(cg[2], cg[3]);                                               \
+                fua = e4m3x8_to_bf16(cu[0], cu[1]);                                               \
+                fub = e4m3x8_to_bf16(cu[2], cu[3]);                                               \
             } else {                                                                              \
-                asm volatile(                                                                     \
-                    "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                                  \
-                    "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                                \
-                    "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                                \
-                    "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                                \
-                    "s_waitcnt lgkmcnt(0)"                                                         \
-                    : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),          \
-                      "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub)                              \
-                    : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa), "v"(xa + 32 * 128 + sb), \
-                      "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb) \
-                    : "memory");                                                                  \
+                const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                        \
+                if (G == 1) {                                                                     \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                              \
+                        "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                              \
+                        "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                            \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub) \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), \
+                          "v"(wa + 32 * 128 + sb)                                                 \
+                        : "memory");                                                              \
+                } else {                                                                          \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                              \
+                        "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                            \
+                        "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                            \
+                        "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                            \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
+                          "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub)                          \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa), "v"(xa + 32 * 128 + sb), \
+                          "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb) \
+                        : "memory");                                                              \
+                }                                                                                 \
             }                                                                                     \
             _Pragma("unroll") for (int q = 0; q < G; ++q) {                                       \
                 if (tv[q]) {                                                                      \
@@ -434,10 +502,8 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
 #undef XD_COMPUTE
 #undef XD_ISSUE
 
-        // lane holds tokens 4*g4 + i of tile mp + 2q, output column
-        // c0 + ct*16 + r16 (and c0 + 32 + ct*16 + r16 for the second half of
-        // the down projection)
-        const int col = c.c0 + ct * 16 + r16;
+        // lane holds tokens 4*g4 + i of tile mp + 2q, output column col
+        // (and col + 32 for the second half of the down projection)
         if (col < c.NOUT) {
 #pragma unroll
             for (int q = 0; q < G; ++q) {
@@ -446,12 +512,14 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                     const int row = mg + 16 * (mp + 2 * q) + 4 * g4 + i;
                     if (row >= c.cnt) continue;
                     if constexpr (MODE == 0) {
-                        const float gv = ag[q][i], uv = au[q][i];
+                        const float gv = F8 ? ag[q][i] * sc0 : ag[q][i];
+                        const float uv = F8 ? au[q][i] * sc1 : au[q][i];
                         const float sv = gv / (1.0f + __expf(-gv));
                         reinterpret_cast<bf16_t*>(a.act)[(long)(c.off + row) * a.F + col] = f2bf(sv * uv);
                     } else {
-                        a.y[(long)(c.off + row) * a.d + col] = ag[q][i];
-                        if (col + 32 < c.NOUT) a.y[(long)(c.off + row) * a.d + col + 32] = au[q][i];
+                        a.y[(long)(c.off + row) * a.d + col] = F8 ? ag[q][i] * sc0 : ag[q][i];
+                        if (col + 32 < c.NOUT)
+                            a.y[(long)(c.off + row) * a.d + col + 32] = F8 ? au[q][i] * sc1 : au[q][i];
                     }
                 }
             }
@@ -463,11 +531,10 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
 
 // 64 weight rows per block: gate and up rows of 32 columns (MODE 0), or 64
 // columns of the down projection (MODE 1); blockIdx.y walks the experts in
-// `order` when it is set.  An expert with at most 32
-// tokens (most of them: a 256-token canvas makes 2048 assignments over 128
-// experts) runs groups of 32, a busier one groups of 64, so its weights are
-// streamed fewer times.
-template <int MODE>
+// `order` when it is set.  An expert with at most 32 tokens (most of them: a
+// 256-token canvas makes 2048 assignments over 128 experts) runs groups of
+// 32, a busier one groups of 64, so its weights are streamed fewer times.
+template <int MODE, bool F8>
 __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.halt && *a.halt) return;
     __shared__ __align__(1024) unsigned char w0[64 * 128], x0[8192];
@@ -495,25 +562,36 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     // the starting stage depends on (column block, expert) only, so a token's
     // sum runs in the same order whatever the other tokens of the batch are
     c.rot = __builtin_amdgcn_readfirstlane(a.k_rotate ? (int)((blockIdx.x + c.e * 5) % c.n) : 0);
-    const bf16_t* Wg = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.w_gate : a.w_down);
-    const bf16_t* Wu = reinterpret_cast<const bf16_t*>(a.w_up);
+    const char* Wg = reinterpret_cast<const char*>(MODE == 0 ? a.w_gate : a.w_down);
+    const char* Wu = reinterpret_cast<const char*>(a.w_up);
     c.X = reinterpret_cast<const bf16_t*>(MODE == 0 ? a.u : a.act);
-    // DMA lanes: an instruction fills 8 rows x 128 bytes; lane l takes row
-    // l / 8 of them and global chunk (l % 8) ^ (row & 7)
+    // token DMA lanes: an instruction fills 8 rows x 128 bytes; lane l takes
+    // row l / 8 of them and global chunk (l % 8) ^ (row & 7)
     c.lr = c.lane >> 3;
     c.lc = ((c.lane & 7) ^ c.lr) * 8;                 // element offset (rows are 8-aligned)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = (c.wave * 2 + q) * 8 + c.lr;     // weight row within the block
+    if (F8) {
+        // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
+        // takes row l / 4 and global chunk (l % 4) ^ swz4(row)
+        const int r = c.wave * 16 + (c.lane >> 2);     // weight row within the block
         const int rr = MODE == 0 ? (r & 31) : r;
         const int col = min(c.c0 + rr, c.NOUT - 1);
-        const bf16_t* base = (MODE == 0 && r >= 32) ? Wu : Wg;
-        c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + c.lc;
+        const char* base = (MODE == 0 && r >= 32) ? Wu : Wg;
+        c.wsrc[0] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz4(r)) << 4);
+        c.wsrc[1] = c.wsrc[0];
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int r = (c.wave * 2 + q) * 8 + c.lr;     // weight row within the block
+            const int rr = MODE == 0 ? (r & 31) : r;
+            const int col = min(c.c0 + rr, c.NOUT - 1);
+            const char* base = (MODE == 0 && r >= 32) ? Wu : Wg;
+            c.wsrc[q] = base + (((long)c.e * c.NOUT + col) * c.K + c.lc) * 2;
+        }
     }
     if (__builtin_amdgcn_readfirstlane(c.cnt) <= 32)
-        expert_groups<MODE, 1>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
+        expert_groups<MODE, 1, F8>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
     else
-        expert_groups<MODE, 2>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
+        expert_groups<MODE, 2, F8>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
 }
 
 // Counts, offsets and the stable placement in one workgroup.  The
@@ -665,14 +743,19 @@ bool expert_dma_ok(const MoeArgs& a) {
         const char* e = getenv("DG_DMA");
         enabled = e ? atoi(e) : 1;
     }
-    return enabled && a.d % 256 == 0 && a.F % 256 == 0;
+    // DG_DMA=0 (sweeps) turns off the bf16 ring only: 8-bit experts run on
+    // the ring alone
+    return (enabled || a.f8) && a.d % 256 == 0 && a.F % 256 == 0;
 }
 
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL(expert_dma_kernel<0>, dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+    if (a.f8) {
+        if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((expert_dma_kernel<0, true>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+    } else if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL((expert_dma_kernel<0, false>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -681,8 +764,11 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL(expert_dma_kernel<1>, dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+    if (a.f8) {
+        if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((expert_dma_kernel<1, true>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+    } else if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL((expert_dma_kernel<1, false>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();

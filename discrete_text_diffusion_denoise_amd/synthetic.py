@@ -27,6 +27,10 @@ SHAPES = {
     "layer": dict(n_layers=1, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                   n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
                   prompt=2048, batch=1, max_steps=48),
+    # the same layer with 8-bit (E4M3, per-row scale) expert weights
+    "layer_fp8": dict(n_layers=1, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+                      n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
+                      expert_dtype="fp8", prompt=2048, batch=1, max_steps=48),
     # 30 such layers, prompt 4096
     "stack": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                   n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
@@ -51,6 +55,8 @@ def model_config(name_or_shape, **over) -> dict:
     cfg = {k: base[k] for k in MODEL_KEYS}
     cfg.update(dtype=base.get("dtype", "bf16"), rope_on=1, rope_theta=10000.0, rms_eps=1e-6,
                selfcond_on=1)
+    if base.get("expert_dtype"):
+        cfg["expert_dtype"] = base["expert_dtype"]
     cfg.update(over)
     # the oracle's names
     cfg["d"] = cfg["d_model"]

@@ -58,7 +58,11 @@ typedef enum {
     DG_ERR_UNSUPPORTED = 7  /* valid request this build does not implement      */
 } dg_status;
 
-typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+typedef enum {
+    DG_F32 = 0,
+    DG_BF16 = 1,
+    DG_FP8_E4M3 = 2   /* OCP 8-bit float E4M3 ("e4m3fn"), expert weights only */
+} dg_dtype;
 
 typedef enum {
     DG_LOCK_MAXPROB = 0,    /* lock i  <=>  max-probability(i) > theta                      */
@@ -80,6 +84,9 @@ typedef struct {
     int32_t rope_on;        /* 1: rotate-half RoPE on q and k                 */
     float rope_theta;       /* RoPE base                                      */
     float rms_eps;          /* RMSNorm epsilon                                */
+    int32_t expert_dtype;   /* 0: experts in `dtype`; DG_FP8_E4M3: expert     */
+                            /* weights as E4M3 codes with per-row fp32 scales */
+                            /* (bf16 models, d_model and d_ff multiples of 256) */
 } dg_config;
 
 typedef struct {
@@ -93,6 +100,11 @@ typedef struct {
     const void* w_gate;      /* [E][F][d]           */
     const void* w_up;        /* [E][F][d]           */
     const void* w_down;      /* [E][d][F]           */
+    /* FP8 experts only (else NULL): one fp32 scale per weight row, so that   */
+    /* weight[e][r][k] = decode(w[e][r][k]) * s[e][r] (dg_quantize_fp8)        */
+    const float* s_gate;     /* [E][F]              */
+    const float* s_up;       /* [E][F]              */
+    const float* s_down;     /* [E][d]              */
 } dg_layer_weights;
 
 typedef struct {
@@ -128,7 +140,10 @@ const char* dg_last_error(void);
 
 /* ---------------------------------------------------------------- model */
 /* Validates the configuration and copies the weight pointer table.
- * DG_ERR_SHAPE on unsupported shapes (limits listed in dg_config). */
+ * DG_ERR_SHAPE on unsupported shapes (limits listed in dg_config);
+ * DG_ERR_DTYPE on an unknown dtype or expert_dtype, DG_ERR_UNSUPPORTED for
+ * FP8 experts outside their limits, DG_ERR_ARG when their scales are
+ * missing. */
 dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** out);
 void dg_model_destroy(dg_model* m);
 
@@ -166,6 +181,19 @@ void dg_kv_destroy(dg_kv* kv);
 dg_status dg_kv_length(const dg_kv* kv, int32_t* len);
 /* Rewinds (or advances) the valid length, e.g. to reuse an encoded prompt. */
 dg_status dg_kv_set_length(dg_kv* kv, int32_t len);
+
+/* 8-bit expert weights (youleyou.com article, "Deployment": the model ships
+ * tuned for a 4-bit floating-point weight format on NVIDIA parts, to move
+ * fewer bytes through the memory-bound experts; the CDNA4 analogue here is
+ * OCP E4M3 with one scale per row).  Quantises d_src [rows][cols] (src_dtype
+ * DG_F32 or DG_BF16) row by row: amax = max |x|, scale = amax / 448 in fp32
+ * (1 for an all-zero row), code = E4M3 of the fp32 quotient x / scale, round
+ * to nearest with ties to the even code, saturating at 448.  Writes d_q
+ * [rows][cols] (one byte per code) and d_scale [rows] (fp32).  An expert
+ * matrix [E][R][K] is rows = E*R, cols = K.  DG_ERR_ARG on NULL or
+ * non-positive sizes, DG_ERR_DTYPE on another src_dtype. */
+dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
+                          void* d_q, float* d_scale, void* stream);
 
 /* ---------------------------------------------------------------- workspace */
 /* Bytes of scratch for every model call with up to `batch` sequences.

@@ -90,16 +90,11 @@ def quantize_rows(w: np.ndarray):
     """Rows of w [R, K] (rounded to binary32) -> (codes uint8 [R, K], scales
     float32 [R]) by the definition in the module docstring."""
     w = np.asarray(w, dtype=np.float32)
-    R, K = w.shape
-    q = np.zeros((R, K), dtype=np.uint8)
-    s = np.zeros(R, dtype=np.float32)
-    for r in range(R):
-        amax = np.float32(np.max(np.abs(w[r]))) if K else np.float32(0.0)
-        scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
-        s[r] = scale
-        quo = (w[r] / scale).astype(np.float32)    # binary32 division per entry
-        q[r] = e4m3_encode_array(quo)
-    return q, s
+    amax = np.max(np.abs(w), axis=1).astype(np.float32)
+    # binary32 scale per row (1 for an all-zero row), binary32 quotients
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    quo = (w / s[:, None]).astype(np.float32)
+    return e4m3_encode_array(quo), s
 
 
 def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:

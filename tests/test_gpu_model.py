@@ -9,6 +9,7 @@ import torch
 
 from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import model as om
+from oracle import quant as oq
 from oracle import sampler as osampler
 
 from helpers import (DEV, normwise, round_model_dtype, route_ambiguous, route_is_valid, to_dev,
@@ -33,15 +34,39 @@ VOCAB_BF16 = dict(n_layers=1, d_model=1024, n_heads=8, n_kv_heads=2, head_dim=12
                   top_k=2, d_ff=256, vocab=32768, canvas=256, dtype="bf16")
 VOCAB_RAGGED = dict(VOCAB_BF16, vocab=32768 + 96, canvas=200)
 
+# the bf16 model with 8-bit (E4M3, per-row scale) expert weights; the oracle
+# runs the dequantised weights
+SMALL_FP8 = dict(SMALL_BF16, expert_dtype="fp8")
+
 MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
-          "vocab_ragged": VOCAB_RAGGED}
+          "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8}
+
+
+def device_form(cfg, W):
+    """(weights for the library, weights for the oracle).  8-bit experts: the
+    oracle's quantiser gives the codes and scales the library runs on, and
+    the oracle runs their dequantised values."""
+    if cfg.get("expert_dtype") != "fp8":
+        return W, W
+    Wg = dict(W, layers=[dict(lw) for lw in W["layers"]])
+    Wo = dict(W, layers=[dict(lw) for lw in W["layers"]])
+    for lg, lo in zip(Wg["layers"], Wo["layers"]):
+        for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+            w = lg[k]
+            q, sc = oq.quantize_rows(w.reshape(-1, w.shape[-1]))
+            lg[k] = q.reshape(w.shape)
+            lg[sk] = sc.reshape(w.shape[:-1])
+            lo[k] = oq.dequantize_rows(q, sc).reshape(w.shape)
+    return Wg, Wo
 
 
 def setup(name, prompt_len, batch=1, std=0.05, seed=0, capacity_extra=0, **over):
     cfg = synthetic.model_config(MODELS[name], **over)
     W = synthetic.make_weights(cfg, seed=seed, std=std, random_norms=True)
+    Wg, W = device_form(cfg, W)
     N = cfg["canvas"]
-    m = binding.Model(cfg, W, batch=batch, capacity=prompt_len + N + capacity_extra)
+    m = binding.Model(cfg, Wg, batch=batch, capacity=prompt_len + N + capacity_extra)
+    m.src_weights = Wg
     return cfg, W, m
 
 
@@ -78,7 +103,8 @@ def oracle_encode_with_gaps(prompt, W64, cfg, gap):
     return cache, amb
 
 
-@pytest.mark.parametrize("name,P,B", [("tiny", 32, 1), ("small_bf16", 300, 2), ("f32_gqa", 77, 2)])
+@pytest.mark.parametrize("name,P,B", [("tiny", 32, 1), ("small_bf16", 300, 2), ("f32_gqa", 77, 2),
+                                      ("small_fp8", 300, 2)])
 def test_encode_prompt_kv_cache(name, P, B):
     print(f"encode {name} P={P} B={B}", flush=True)
     cfg, W, m = setup(name, P, batch=B)
@@ -117,7 +143,8 @@ def test_encode_prompt_kv_cache(name, P, B):
                                                       ("small_bf16", 200, 2, False, 1),
                                                       ("small_bf16", 200, 2, True, 1),
                                                       ("f32_gqa", 64, 2, True, 2),
-                                                      ("f32_gqa", 64, 1, False, 3)])
+                                                      ("f32_gqa", 64, 1, False, 3),
+                                                      ("small_fp8", 200, 2, True, 1)])
 def test_denoise_step(name, P, B, selfcond, layers):
     print(f"denoise {name} P={P} B={B} selfcond={selfcond} layers={layers}", flush=True)
     cfg, W, m = setup(name, P, batch=B, n_layers=layers)
@@ -198,7 +225,7 @@ def test_stage_attention_on_synthetic_cache(name, causal):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 256), ("small_bf16", 512), ("small_bf16", 37),
-                                    ("f32_gqa", 1000)])
+                                    ("f32_gqa", 1000), ("small_fp8", 512), ("small_fp8", 37)])
 def test_stage_moe(name, T):
     cfg, W, m = setup(name, 0)
     rng = np.random.default_rng(11)
@@ -282,7 +309,7 @@ def test_commit_equals_encode_of_concatenation():
     block = synthetic.make_tokens(V, (1, N), seed=21)
     m1.encode_prompt(to_dev(prompt))
     m1.commit_block(to_dev(block))
-    m2 = binding.Model(cfg, W, batch=1, capacity=50 + 2 * N)
+    m2 = binding.Model(cfg, m1.src_weights, batch=1, capacity=50 + 2 * N)
     m2.encode_prompt(to_dev(np.concatenate([prompt, block], axis=1)))
     torch.cuda.synchronize()
     assert m1.kv_length == m2.kv_length == 50 + N
@@ -296,6 +323,7 @@ def test_commit_equals_encode_of_concatenation():
 @pytest.mark.parametrize("name,B,selfcond,early", [("tiny", 1, True, False),
                                                    ("small_bf16", 2, True, False),
                                                    ("vocab_bf16", 1, True, False),
+                                                   ("small_fp8", 2, True, False),
                                                    ("small_bf16", 2, False, False),
                                                    ("small_bf16", 2, True, True)])
 def test_generate_block_is_its_composition(name, B, selfcond, early):
@@ -314,13 +342,13 @@ def test_generate_block_is_its_composition(name, B, selfcond, early):
     else:
         params = synthetic.default_sampler_params(max_steps=3, seed=5, selfcond_on=int(selfcond))
     # library loop
-    mg = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
+    mg = binding.Model(cfg, m.src_weights, batch=B, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(to_dev(prompt))
     block = torch.zeros((B, N), dtype=torch.int32, device=DEV)
     steps = mg.generate_block(params, 0, block)
     torch.cuda.synchronize()
     # the same rounds, one call at a time
-    mc = binding.Model(cfg, W, batch=B, capacity=P + 2 * N)
+    mc = binding.Model(cfg, m.src_weights, batch=B, capacity=P + 2 * N)
     mc.encode_prompt(to_dev(prompt))
     canvas = torch.zeros((B, N), dtype=torch.int32, device=DEV)
     binding.canvas_init(params["seed"], 0, canvas, V)
