@@ -313,11 +313,12 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // One expert's token groups against one block of weight rows: a four-stage
-// ring of direct-to-LDS loads (64 weight rows x 64 k and 32 * G token rows x
-// 64 k per stage), G = 1 or 2 groups of 32 tokens per pass over the weights.
-// F8: the weight rows hold E4M3 codes (64 bytes per row and stage), widened
-// to bf16 in registers (exactly: E4M3 values are bf16 values) and scaled per
-// output column after the sum.
+// ring of direct-to-LDS loads (8 KiB of weight rows x 64 k and 32 * G token
+// rows x 64 k per stage), G = 1 or 2 groups of 32 tokens per pass over the
+// weights.  bf16 weights: 64 rows (two halves of 32 columns) per block.
+// F8: 128 rows of E4M3 codes (two halves of 64 columns; 64 bytes per row and
+// stage), widened to bf16 in registers (exactly: E4M3 values are bf16
+// values) and scaled per output column after the sum.
 struct XdCtx {
     int e, off, cnt, K, NOUT, c0, n, rot;
     int lane, wave, r16, g4, ct, mp, lr, lc;
@@ -344,24 +345,33 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                                               unsigned char* w1, unsigned char* w2, unsigned char* w3,
                                               unsigned char* x0, unsigned char* x1, unsigned char* x2,
                                               unsigned char* x3) {
-    constexpr int WQ = F8 ? 1 : 2;                     // weight DMAs per wave per stage
+    constexpr int WQ = 2;                              // weight DMAs per wave per stage
     constexpr int PER = WQ + G;                        // DMAs per wave per stage
     constexpr int WSTAGE = F8 ? 64 : 128;              // weight bytes per row and stage
+    constexpr int J = F8 ? 2 : 1;                      // 16-column tiles per half and wave
+    constexpr int HALF = 32 * J;                       // columns per half of the block
     const int n = c.n, rot = c.rot, mp = c.mp, ct = c.ct, r16 = c.r16, g4 = c.g4;
     const int wblk = c.wave * WQ * 1024;
     const int xblk = c.wave * G * 1024;
     const int roff = r16 * 128;
-    // per-column scales of the 8-bit weights (column col, and col + 32 for
-    // the down projection's second half)
-    const int col = c.c0 + ct * 16 + r16;
-    float sc0 = 1.0f, sc1 = 1.0f;
-    if (F8 && col < c.NOUT) {
-        if (MODE == 0) {
-            sc0 = a.s_gate[(long)c.e * c.NOUT + col];
-            sc1 = a.s_up[(long)c.e * c.NOUT + col];
-        } else {
-            sc0 = a.s_down[(long)c.e * c.NOUT + col];
-            sc1 = col + 32 < c.NOUT ? a.s_down[(long)c.e * c.NOUT + col + 32] : 1.0f;
+    // output columns of the lane (tile ct + 2j of the first half; the
+    // second half is the up projection, or the down columns HALF later)
+    // and, for 8-bit weights, their scales
+    int col[J];
+    float sc0[J], sc1[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        col[j] = c.c0 + (ct + 2 * j) * 16 + r16;
+        sc0[j] = 1.0f;
+        sc1[j] = 1.0f;
+        if (F8 && col[j] < c.NOUT) {
+            if (MODE == 0) {
+                sc0[j] = a.s_gate[(long)c.e * c.NOUT + col[j]];
+                sc1[j] = a.s_up[(long)c.e * c.NOUT + col[j]];
+            } else {
+                sc0[j] = a.s_down[(long)c.e * c.NOUT + col[j]];
+                sc1[j] = col[j] + HALF < c.NOUT ? a.s_down[(long)c.e * c.NOUT + col[j] + HALF] : 1.0f;
+            }
         }
     }
     for (int mg = 0; mg < c.cnt; mg += 32 * G) {
@@ -372,14 +382,17 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             const long src = MODE == 0 ? (long)a.perm_tok[c.off + tok] : (long)(c.off + tok);
             xsrc[q] = c.X + src * c.K + c.lc;
         }
-        // wave: token tiles mp (and mp + 2 when G = 2), column tile ct of
-        // both halves of the weight block
-        f32x4_t ag[G], au[G];
+        // wave: token tiles mp (and mp + 2 when G = 2), column tiles ct + 2j
+        // of both halves of the weight block
+        f32x4_t ag[G][J], au[G][J];
         bool tv[G];
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            ag[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            au[q] = ag[q];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                ag[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                au[q][j] = ag[q][j];
+            }
             tv[q] = mg + 16 * (mp + 2 * q) < c.cnt;
         }
 
@@ -395,49 +408,57 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                 __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
                                                  (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
         }
-        // fragments: token rows 16*(mp + 2q) + r16, weight rows ct*16 + r16 and
-        // 32 + ct*16 + r16 (up half, or down columns 32..63).  bf16 weights:
-        // k-step s of a lane is chunk 4*s + g4 of both operands; 8-bit
-        // weights: the lane's 16 codes are chunk g4 of the 64-byte row (k
-        // 16*g4 .. 16*g4+15), so its token chunks are 2*g4 (k-step 0) and
-        // 2*g4 + 1 (k-step 1): every k of the stage is in exactly one k-step
-        // of one lane group, as the sum needs
+        // fragments: token rows 16*(mp + 2q) + r16; weight rows (ct + 2j)*16
+        // + r16 of each half.  bf16 weights: k-step s of a lane is chunk
+        // 4*s + g4 of both operands; 8-bit weights: the lane's 16 codes are
+        // chunk g4 of the 64-byte row (k 16*g4 .. 16*g4+15), so its token
+        // chunks are 2*g4 (k-step 0) and 2*g4 + 1 (k-step 1): every k of the
+        // stage is in exactly one k-step of one lane group, as the sum needs
 #define XD_COMPUTE(WB, XB)                                                                        \
         {                                                                                         \
-            u32x4 fga, fgb, fua, fub, fxa[G], fxb[G];                                             \
+            u32x4 fga[J], fgb[J], fua[J], fub[J], fxa[G], fxb[G];                                 \
             const uint32_t xa = lds_addr(XB) + (16 * mp) * 128 + roff;                            \
             const int xs = r16 & 7;                                                               \
             const uint32_t sa = F8 ? ((2 * g4) ^ xs) << 4 : (g4 ^ xs) << 4;                       \
             const uint32_t sb = F8 ? ((2 * g4 + 1) ^ xs) << 4 : ((4 + g4) ^ xs) << 4;             \
             if (F8) {                                                                             \
-                const int wr = ct * 16 + r16;                                                     \
-                const uint32_t wg_ = lds_addr(WB) + wr * 64 + ((g4 ^ swz4(wr)) << 4);             \
-                const uint32_t wu_ = lds_addr(WB) + (wr + 32) * 64 + ((g4 ^ swz4(wr + 32)) << 4); \
-                u32x4 cg, cu;                                                                     \
+                const int wr0 = ct * 16 + r16, wr1 = wr0 + 32;                                    \
+                const uint32_t wb_ = lds_addr(WB);                                                \
+                const uint32_t g0_ = wb_ + wr0 * 64 + ((g4 ^ swz4(wr0)) << 4);                    \
+                const uint32_t g1_ = wb_ + wr1 * 64 + ((g4 ^ swz4(wr1)) << 4);                    \
+                const uint32_t u0_ = wb_ + (wr0 + 64) * 64 + ((g4 ^ swz4(wr0 + 64)) << 4);        \
+                const uint32_t u1_ = wb_ + (wr1 + 64) * 64 + ((g4 ^ swz4(wr1 + 64)) << 4);        \
+                u32x4 cg0, cg1, cu0, cu1;                                                         \
                 if (G == 1) {                                                                     \
-                    asm volatile(                                                                 \
-                        "ds_read_b128 %0, %4\n ds_read_b128 %1, %5\n"                              \
-                        "ds_read_b128 %2, %6\n ds_read_b128 %3, %7\n"                              \
-                        "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cg), "=&v"(cu)                      \
-                        : "v"(xa + sa), "v"(xa + sb), "v"(wg_), "v"(wu_)                          \
-                        : "memory");                                                              \
-                } else {                                                                          \
                     asm volatile(                                                                 \
                         "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                              \
                         "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                              \
                         "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                            \
                         "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cg0), "=&v"(cg1), "=&v"(cu0), "=&v"(cu1) \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(g0_), "v"(g1_), "v"(u0_), "v"(u1_)      \
+                        : "memory");                                                              \
+                } else {                                                                          \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                              \
+                        "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                            \
+                        "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                            \
+                        "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                            \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
                         : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
-                          "=&v"(cg), "=&v"(cu)                                                    \
+                          "=&v"(cg0), "=&v"(cg1), "=&v"(cu0), "=&v"(cu1)                          \
                         : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa),                    \
-                          "v"(xa + 32 * 128 + sb), "v"(wg_), "v"(wu_)                             \
+                          "v"(xa + 32 * 128 + sb), "v"(g0_), "v"(g1_), "v"(u0_), "v"(u1_)         \
                         : "memory");                                                              \
                 }                                                                                 \
-                fga = e4m3x8_to_bf16(cg[0], cg[1]);                                               \
-                fgb = e4m3x8_to_bf16(cg[2], cg[3]);                                               \
-                fua = e4m3x8_to_bf16(cu[0], cu[1]);                                               \
-                fub = e4m3x8_to_bf16(cu[2], cu[3]);                                               \
+                fga[0] = e4m3x8_to_bf16(cg0[0], cg0[1]);                                          \
+                fgb[0] = e4m3x8_to_bf16(cg0[2], cg0[3]);                                          \
+                fua[0] = e4m3x8_to_bf16(cu0[0], cu0[1]);                                          \
+                fub[0] = e4m3x8_to_bf16(cu0[2], cu0[3]);                                          \
+                fga[J - 1] = e4m3x8_to_bf16(cg1[0], cg1[1]);                                      \
+                fgb[J - 1] = e4m3x8_to_bf16(cg1[2], cg1[3]);                                      \
+                fua[J - 1] = e4m3x8_to_bf16(cu1[0], cu1[1]);                                      \
+                fub[J - 1] = e4m3x8_to_bf16(cu1[2], cu1[3]);                                      \
             } else {                                                                              \
                 const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                        \
                 if (G == 1) {                                                                     \
@@ -446,7 +467,8 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                         "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                              \
                         "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                            \
                         "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub) \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fga[0]), "=&v"(fgb[0]), "=&v"(fua[0]), \
+                          "=&v"(fub[0])                                                           \
                         : "v"(xa + sa), "v"(xa + sb), "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), \
                           "v"(wa + 32 * 128 + sb)                                                 \
                         : "memory");                                                              \
@@ -458,7 +480,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                         "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                            \
                         "s_waitcnt lgkmcnt(0)"                                                     \
                         : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
-                          "=&v"(fga), "=&v"(fgb), "=&v"(fua), "=&v"(fub)                          \
+                          "=&v"(fga[0]), "=&v"(fgb[0]), "=&v"(fua[0]), "=&v"(fub[0])              \
                         : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa), "v"(xa + 32 * 128 + sb), \
                           "v"(wa + sa), "v"(wa + sb), "v"(wa + 32 * 128 + sa), "v"(wa + 32 * 128 + sb) \
                         : "memory");                                                              \
@@ -466,14 +488,16 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             }                                                                                     \
             _Pragma("unroll") for (int q = 0; q < G; ++q) {                                       \
                 if (tv[q]) {                                                                      \
-                    ag[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
-                        __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fga), ag[q], 0, 0, 0); \
-                    ag[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
-                        __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fgb), ag[q], 0, 0, 0); \
-                    au[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
-                        __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fua), au[q], 0, 0, 0); \
-                    au[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                              \
-                        __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fub), au[q], 0, 0, 0); \
+                    _Pragma("unroll") for (int j = 0; j < J; ++j) {                               \
+                        ag[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                       \
+                            __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fga[j]), ag[q][j], 0, 0, 0); \
+                        ag[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                       \
+                            __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fgb[j]), ag[q][j], 0, 0, 0); \
+                        au[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                       \
+                            __builtin_bit_cast(bf16x8_t, fxa[q]), __builtin_bit_cast(bf16x8_t, fua[j]), au[q][j], 0, 0, 0); \
+                        au[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                       \
+                            __builtin_bit_cast(bf16x8_t, fxb[q]), __builtin_bit_cast(bf16x8_t, fub[j]), au[q][j], 0, 0, 0); \
+                    }                                                                             \
                 }                                                                                 \
             }                                                                                     \
         }
@@ -502,9 +526,11 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
 #undef XD_COMPUTE
 #undef XD_ISSUE
 
-        // lane holds tokens 4*g4 + i of tile mp + 2q, output column col
-        // (and col + 32 for the second half of the down projection)
-        if (col < c.NOUT) {
+        // lane holds tokens 4*g4 + i of tile mp + 2q, output columns col[j]
+        // (and col[j] + HALF for the second half of the down projection)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (col[j] >= c.NOUT) continue;
 #pragma unroll
             for (int q = 0; q < G; ++q) {
 #pragma unroll
@@ -512,14 +538,16 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                     const int row = mg + 16 * (mp + 2 * q) + 4 * g4 + i;
                     if (row >= c.cnt) continue;
                     if constexpr (MODE == 0) {
-                        const float gv = F8 ? ag[q][i] * sc0 : ag[q][i];
-                        const float uv = F8 ? au[q][i] * sc1 : au[q][i];
+                        const float gv = F8 ? ag[q][j][i] * sc0[j] : ag[q][j][i];
+                        const float uv = F8 ? au[q][j][i] * sc1[j] : au[q][j][i];
                         const float sv = gv / (1.0f + __expf(-gv));
-                        reinterpret_cast<bf16_t*>(a.act)[(long)(c.off + row) * a.F + col] = f2bf(sv * uv);
+                        reinterpret_cast<bf16_t*>(a.act)[(long)(c.off + row) * a.F + col[j]] =
+                            f2bf(sv * uv);
                     } else {
-                        a.y[(long)(c.off + row) * a.d + col] = F8 ? ag[q][i] * sc0 : ag[q][i];
-                        if (col + 32 < c.NOUT)
-                            a.y[(long)(c.off + row) * a.d + col + 32] = F8 ? au[q][i] * sc1 : au[q][i];
+                        a.y[(long)(c.off + row) * a.d + col[j]] = F8 ? ag[q][j][i] * sc0[j] : ag[q][j][i];
+                        if (col[j] + HALF < c.NOUT)
+                            a.y[(long)(c.off + row) * a.d + col[j] + HALF] =
+                                F8 ? au[q][j][i] * sc1[j] : au[q][j][i];
                     }
                 }
             }
@@ -529,11 +557,12 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
     }
 }
 
-// 64 weight rows per block: gate and up rows of 32 columns (MODE 0), or 64
-// columns of the down projection (MODE 1); blockIdx.y walks the experts in
-// `order` when it is set.  An expert with at most 32 tokens (most of them: a
-// 256-token canvas makes 2048 assignments over 128 experts) runs groups of
-// 32, a busier one groups of 64, so its weights are streamed fewer times.
+// Blocks of weight rows (bf16: 64 rows = gate and up rows of 32 columns
+// (MODE 0) or 64 columns of the down projection (MODE 1); 8-bit: 128 rows,
+// twice the columns); blockIdx.y walks the experts in `order` when it is
+// set.  An expert with at most 32 tokens (most of them: a 256-token canvas
+// makes 2048 assignments over 128 experts) runs groups of 32, a busier one
+// groups of 64, so its weights are streamed fewer times.
 template <int MODE, bool F8>
 __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.halt && *a.halt) return;
@@ -541,6 +570,7 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     __shared__ __align__(1024) unsigned char w1[64 * 128], x1[8192];
     __shared__ __align__(1024) unsigned char w2[64 * 128], x2[8192];
     __shared__ __align__(1024) unsigned char w3[64 * 128], x3[8192];
+    constexpr int HALF = F8 ? 64 : 32;                 // columns per half of a block
 
     XdCtx c;
     // the busiest experts first, so their longer blocks do not form the tail
@@ -557,7 +587,7 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     c.mp = c.wave >> 1;
     c.K = MODE == 0 ? a.d : a.F;
     c.NOUT = MODE == 0 ? a.F : a.d;
-    c.c0 = blockIdx.x * (MODE == 0 ? 32 : 64);
+    c.c0 = blockIdx.x * (MODE == 0 ? HALF : 2 * HALF);
     c.n = __builtin_amdgcn_readfirstlane(c.K / 64);   // stages, a multiple of 4
     // the starting stage depends on (column block, expert) only, so a token's
     // sum runs in the same order whatever the other tokens of the batch are
@@ -569,22 +599,21 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     // row l / 8 of them and global chunk (l % 8) ^ (row & 7)
     c.lr = c.lane >> 3;
     c.lc = ((c.lane & 7) ^ c.lr) * 8;                 // element offset (rows are 8-aligned)
-    if (F8) {
-        // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
-        // takes row l / 4 and global chunk (l % 4) ^ swz4(row)
-        const int r = c.wave * 16 + (c.lane >> 2);     // weight row within the block
-        const int rr = MODE == 0 ? (r & 31) : r;
-        const int col = min(c.c0 + rr, c.NOUT - 1);
-        const char* base = (MODE == 0 && r >= 32) ? Wu : Wg;
-        c.wsrc[0] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz4(r)) << 4);
-        c.wsrc[1] = c.wsrc[0];
-    } else {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int r = (c.wave * 2 + q) * 8 + c.lr;     // weight row within the block
-            const int rr = MODE == 0 ? (r & 31) : r;
+    for (int q = 0; q < 2; ++q) {
+        if (F8) {
+            // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
+            // takes row l / 4 and global chunk (l % 4) ^ swz4(row)
+            const int r = (c.wave * 2 + q) * 16 + (c.lane >> 2);   // row within the block
+            const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
             const int col = min(c.c0 + rr, c.NOUT - 1);
-            const char* base = (MODE == 0 && r >= 32) ? Wu : Wg;
+            const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
+            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz4(r)) << 4);
+        } else {
+            const int r = (c.wave * 2 + q) * 8 + c.lr;             // row within the block
+            const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
+            const int col = min(c.c0 + rr, c.NOUT - 1);
+            const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
             c.wsrc[q] = base + (((long)c.e * c.NOUT + col) * c.K + c.lc) * 2;
         }
     }
@@ -753,7 +782,7 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.f8) {
         if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<0, true>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<0, true>), dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
     } else if (sizeof(T) == 2 && expert_dma_ok(a))
         hipLaunchKernelGGL((expert_dma_kernel<0, false>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     else
@@ -766,7 +795,7 @@ hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.f8) {
         if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<1, true>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<1, true>), dim3(cdiv(a.d, 128), a.E), dim3(256), 0, st, a);
     } else if (sizeof(T) == 2 && expert_dma_ok(a))
         hipLaunchKernelGGL((expert_dma_kernel<1, false>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
     else
