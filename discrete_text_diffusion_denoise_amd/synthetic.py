@@ -134,6 +134,6 @@ def default_sampler_params(**over) -> dict:
     0.8 -> 0.4, stop at mean entropy < 0.005 with an unchanged most likely
     sequence, at most 48 rounds."""
     p = dict(lock_rule=1, lock_theta=0.1, temp_start=0.8, temp_end=0.4, stop_tau=0.005,
-             require_stable=1, max_steps=48, seed=0, selfcond_on=1)
+             require_stable=1, max_steps=48, seed=0, selfcond_on=1, top_k=0)
     p.update(over)
     return p

@@ -186,20 +186,39 @@ def embed(tokens: np.ndarray, W: dict) -> np.ndarray:
     return W["embed"][np.asarray(tokens)]
 
 
-def selfcond_vector(prev_logits: np.ndarray, W: dict) -> np.ndarray:
+def topk_candidates(row: np.ndarray, K: int) -> np.ndarray:
+    """Indices of the K largest entries of a logit row, by value descending,
+    ties to the lower index (the sampler's top-k truncation)."""
+    row = np.asarray(row, dtype=np.float64)
+    order = np.lexsort((np.arange(row.size), -row))
+    return order[:min(K, row.size)]
+
+
+def selfcond_vector(prev_logits: np.ndarray, W: dict, top_k: int = 0) -> np.ndarray:
     """Expected embedding under the previous round's T = 1 distribution:
-    s = softmax(L_prev) E, per position.  prev_logits [..., V]."""
+    s = softmax(L_prev) E, per position.  prev_logits [..., V].  With top_k
+    > 0 the distribution is truncated to each position's top_k logits and
+    renormalised (report-summary page, section 8: top-k truncation)."""
     L = np.asarray(prev_logits, dtype=np.float64)
-    p = np.exp(L - L.max(axis=-1, keepdims=True))
-    p = p / p.sum(axis=-1, keepdims=True)
-    return p @ W["embed"]
+    if top_k <= 0:
+        p = np.exp(L - L.max(axis=-1, keepdims=True))
+        p = p / p.sum(axis=-1, keepdims=True)
+        return p @ W["embed"]
+    flat = L.reshape(-1, L.shape[-1])
+    out = np.zeros((flat.shape[0], W["embed"].shape[1]))
+    for r in range(flat.shape[0]):
+        c = topk_candidates(flat[r], top_k)
+        p = np.exp(flat[r, c] - flat[r, c[0]])
+        out[r] = (p / p.sum()) @ W["embed"][c]
+    return out.reshape(L.shape[:-1] + (W["embed"].shape[1],))
 
 
-def denoiser_input(canvas: np.ndarray, W: dict, prev_logits: np.ndarray | None) -> np.ndarray:
+def denoiser_input(canvas: np.ndarray, W: dict, prev_logits: np.ndarray | None,
+                   top_k: int = 0) -> np.ndarray:
     """h0 = E[x] + s W_sc^T, with s = 0 when there is no previous prediction."""
     h = embed(canvas, W)
     if prev_logits is not None:
-        s = selfcond_vector(prev_logits, W)
+        s = selfcond_vector(prev_logits, W, top_k)
         h = h + s @ W["w_sc"].T
     return h
 
@@ -234,7 +253,7 @@ def encode(tokens: np.ndarray, W: dict, cfg: dict, cache: KVCache) -> None:
 
 
 def denoise_step(canvas: np.ndarray, W: dict, cfg: dict, cache: KVCache,
-                 prev_logits: np.ndarray | None = None) -> np.ndarray:
+                 prev_logits: np.ndarray | None = None, top_k: int = 0) -> np.ndarray:
     """One denoiser forward over canvases [B, N] with bidirectional attention
     over [cached context ; canvas].  The cache is not modified.  Returns
     float64 logits [B, N, V]."""
@@ -242,7 +261,7 @@ def denoise_step(canvas: np.ndarray, W: dict, cfg: dict, cache: KVCache,
     B, N = canvas.shape
     out = []
     for b in range(B):
-        h = denoiser_input(canvas[b], W, None if prev_logits is None else prev_logits[b])
+        h = denoiser_input(canvas[b], W, None if prev_logits is None else prev_logits[b], top_k)
         for li, lw in enumerate(W["layers"]):
             h, _, _ = attn_half(h, lw, cfg, cache.k[li][b], cache.v[li][b], cache.length,
                                 causal=False)

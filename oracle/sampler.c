@@ -378,6 +378,108 @@ int ora_stop_flag(int N, const float* H, int stable, float tau, int require_stab
     return st;
 }
 
+/* ------------------------------------------------------------------ */
+/* Top-k truncation (report-summary page, section 8: at large batches a */
+/* top-k truncation of the distribution is the named missing            */
+/* throughput optimisation).  With K > 0 a position's statistics, draw  */
+/* and self-conditioning use only its K largest logits.                 */
+/*   candidates c_0..c_{K-1}: the K largest entries, ordered by value    */
+/*     descending, ties to the lower index (a total order);             */
+/*   m = l[c_0] (the argmax); z_i = l[c_i] - m; e_i = ora_exp(z_i);      */
+/*   S = e_0 + e_1 + ... (in candidate order), A likewise of e_i * z_i;  */
+/*   H = max(0, ora_log(S) - A / S), pmax = 1 / S;                       */
+/*   draw: w_i = ora_exp(z_i * invT), y = c_pick(w, K, u) with u from    */
+/*     Philox word 0 (one level; words 2 and 3 are not used);           */
+/*   self-conditioning weights p_i = e_i / S.                            */
+/* ------------------------------------------------------------------ */
+static const float* g_row;   /* qsort has no context argument */
+static int cmp_desc(const void* pa, const void* pb)
+{
+    int a = *(const int*)pa, b = *(const int*)pb;
+    float x = g_row[a], y = g_row[b];
+    if (x > y) return -1;
+    if (x < y) return 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* One row: out4 = {m, S, H, pmax}; idx[K], p[K] the candidates and their
+ * self-conditioning weights; returns the drawn token. */
+int32_t ora_topk_row(const float* row, int V, int K, float invT, float u, float* out4,
+                     int32_t* idx, float* p)
+{
+    int* ord = (int*)malloc(sizeof(int) * V);
+    for (int v = 0; v < V; ++v) ord[v] = v;
+    g_row = row;
+    qsort(ord, V, sizeof(int), cmp_desc);
+    if (K > V) K = V;
+    float m = row[ord[0]];
+    float S = 0.0f, A = 0.0f;
+    float* e = (float*)malloc(sizeof(float) * K);
+    float* w = (float*)malloc(sizeof(float) * K);
+    for (int i = 0; i < K; ++i) {
+        float z = row[ord[i]] - m;
+        e[i] = ora_exp(z);
+        S = S + e[i];
+        float ez = e[i] * z;
+        A = A + ez;
+        w[i] = ora_exp(z * invT);
+    }
+    float h = ora_log(S) - A / S;
+    out4[0] = m;
+    out4[1] = S;
+    out4[2] = h > 0.0f ? h : 0.0f;
+    out4[3] = 1.0f / S;
+    for (int i = 0; i < K; ++i) {
+        idx[i] = ord[i];
+        p[i] = e[i] / S;
+    }
+    int32_t y = ord[pick(w, K, u)];
+    free(ord); free(e); free(w);
+    return y;
+}
+
+/* ora_sample_update with top-k truncation (K >= 1); argmax = c_0. */
+void ora_sample_update_topk(int lock_rule, float theta, float T0, float T1, float tau,
+                            int require_stable, int max_steps, uint64_t seed, int step, int K,
+                            int B, int N, int V, const float* logits, int32_t* canvas,
+                            int32_t* argmax, uint8_t* lock, float* stats, int32_t* stop)
+{
+    float invT = ora_inv_temperature(T0, T1, step, max_steps);
+    float* H = (float*)malloc(sizeof(float) * N);
+    float* P = (float*)malloc(sizeof(float) * N);
+    int32_t* y = (int32_t*)malloc(sizeof(int32_t) * N);
+    int32_t* r = (int32_t*)malloc(sizeof(int32_t) * N);
+    int32_t* am = (int32_t*)malloc(sizeof(int32_t) * N);
+    int Ke = K < V ? K : V;
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * Ke);
+    float* pp = (float*)malloc(sizeof(float) * Ke);
+    for (int b = 0; b < B; ++b) {
+        if (stop[b]) continue;
+        for (int i = 0; i < N; ++i) {
+            const float* row = logits + ((size_t)b * N + i) * (size_t)V;
+            uint64_t o[4];
+            draw_block(seed, (uint64_t)step, (uint64_t)b, (uint64_t)i, 0, o);
+            float* st = stats + ((size_t)b * N + i) * 4;
+            y[i] = ora_topk_row(row, V, K, invT, ora_uniform(o[0]), st, idx, pp);
+            H[i] = st[2];
+            P[i] = st[3];
+            am[i] = idx[0];
+            r[i] = ora_uniform_token(o[1], V);
+        }
+        ora_lock_set(lock_rule, theta, N, H, P, lock + (size_t)b * N);
+        uint8_t* lk = lock + (size_t)b * N;
+        int stable = step > 0;
+        for (int i = 0; i < N; ++i) {
+            size_t bi = (size_t)b * N + i;
+            canvas[bi] = lk[i] ? y[i] : r[i];
+            if (argmax[bi] != am[i]) stable = 0;
+            argmax[bi] = am[i];
+        }
+        stop[b] = ora_stop_flag(N, H, stable, tau, require_stable, step, max_steps);
+    }
+    free(H); free(P); free(y); free(r); free(am); free(idx); free(pp);
+}
+
 /*
  * One sampler update over B canvases of N positions each.
  *   logits   [B,N,V] float

@@ -64,6 +64,13 @@ def lib():
         L.ora_sample_update.argtypes = [ctypes.c_int, f32, f32, f32, f32, ctypes.c_int,
                                         ctypes.c_int, u64, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, P, P, P, P, P, P]
+        L.ora_topk_row.restype = i32
+        L.ora_topk_row.argtypes = [P, ctypes.c_int, ctypes.c_int, f32, f32, P, P, P]
+        L.ora_sample_update_topk.restype = None
+        L.ora_sample_update_topk.argtypes = [ctypes.c_int, f32, f32, f32, f32, ctypes.c_int,
+                                             ctypes.c_int, u64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
+                                             P, P, P]
         _lib = L
     return _lib
 
@@ -122,18 +129,37 @@ def canvas_init(seed: int, block: int, B: int, N: int, V: int) -> np.ndarray:
     return out
 
 
+def topk_row(row: np.ndarray, K: int, inv_t: float, u: float):
+    """Top-k truncated statistics of one float32 row: (stats [m, S, H, pmax],
+    candidates idx [K], self-conditioning weights p [K], drawn token)."""
+    row = np.ascontiguousarray(row, dtype=np.float32)
+    Ke = min(K, row.size)
+    out = np.zeros(4, dtype=np.float32)
+    idx = np.zeros(Ke, dtype=np.int32)
+    p = np.zeros(Ke, dtype=np.float32)
+    y = int(lib().ora_topk_row(_ptr(row), row.size, int(K), float(np.float32(inv_t)),
+                               float(np.float32(u)), _ptr(out), _ptr(idx), _ptr(p)))
+    return out, idx, p, y
+
+
 def sample_update(params: dict, step: int, logits: np.ndarray, canvas: np.ndarray,
                   argmax: np.ndarray, stop: np.ndarray):
     """One sampler update.  logits [B,N,V] float32; canvas/argmax [B,N] int32 and
-    stop [B] int32 are updated in place; returns (lock [B,N] uint8, stats [B,N,4])."""
+    stop [B] int32 are updated in place; returns (lock [B,N] uint8, stats [B,N,4]).
+    params["top_k"] > 0 selects top-k truncation."""
     B, N, V = logits.shape
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     assert canvas.dtype == np.int32 and argmax.dtype == np.int32 and stop.dtype == np.int32
     lock = np.zeros((B, N), dtype=np.uint8)
     stats = np.zeros((B, N, 4), dtype=np.float32)
-    lib().ora_sample_update(
-        int(params["lock_rule"]), float(params["lock_theta"]), float(params["temp_start"]),
-        float(params["temp_end"]), float(params["stop_tau"]), int(params["require_stable"]),
-        int(params["max_steps"]), int(params["seed"]), int(step), B, N, V, _ptr(logits),
-        _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats), _ptr(stop))
+    common = (int(params["lock_rule"]), float(params["lock_theta"]), float(params["temp_start"]),
+              float(params["temp_end"]), float(params["stop_tau"]), int(params["require_stable"]),
+              int(params["max_steps"]), int(params["seed"]), int(step))
+    K = int(params.get("top_k", 0))
+    if K > 0:
+        lib().ora_sample_update_topk(*common, K, B, N, V, _ptr(logits), _ptr(canvas),
+                                     _ptr(argmax), _ptr(lock), _ptr(stats), _ptr(stop))
+    else:
+        lib().ora_sample_update(*common, B, N, V, _ptr(logits), _ptr(canvas), _ptr(argmax),
+                                _ptr(lock), _ptr(stats), _ptr(stop))
     return lock, stats
