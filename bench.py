@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the measurement, two 1 GiB device copies (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="sampler top-k truncation (0: the full distribution)")
     return ap.parse_args()
 
 
@@ -111,6 +113,10 @@ def kernel_work(name, cfg, B, P, sc_splits):
         return (4.0 * T * L * Hq * dh,
                 T * Hq * dh * es + B * L * Hkv * dh * 2 * es + T * Hq * dh * es)
     if name == "sampler":
+        if cfg.get("sampler_top_k"):
+            # slab maxima, then about K candidate slabs of 64 logits per row
+            K = cfg["sampler_top_k"]
+            return 0.0, T * (V / 64) * 4.0 + T * K * 64 * 4.0 + T * 16.0
         return 0.0, T * V * 4.0 + T * 16.0
     raise KeyError(name)
 
@@ -227,6 +233,7 @@ def main():
 
     shape = synthetic.SHAPES[args.config]
     cfg = synthetic.model_config(args.config)
+    cfg["sampler_top_k"] = args.top_k
     B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
     torch.cuda.init()
     W = device_weights(cfg, args.seed, torch)
@@ -235,7 +242,8 @@ def main():
     g.manual_seed(args.seed + 1)
     prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
     m.encode_prompt(prompt)
-    params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1)
+    params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1,
+                                              top_k=args.top_k)
     block = torch.zeros((B, N), dtype=torch.int32, device="cuda")
 
     names = list(binding.TIMERS)
@@ -293,7 +301,8 @@ def main():
     ev[0].record()
     for j in range(1, reps + 1):
         stop.zero_()
-        m.denoise_step(canvas, logits[j % 2], logits[(j - 1) % 2], stats[(j - 1) % 2])
+        m.denoise_step(canvas, logits[j % 2], logits[(j - 1) % 2], stats[(j - 1) % 2],
+                       top_k=args.top_k)
         binding.sample_update(params, j, logits[j % 2], canvas, argmax, lock, stats[j % 2], stop,
                               sws)
     ev[1].record()
@@ -336,7 +345,8 @@ def main():
                                 f"block (<=48 self-conditioned rounds + commit)"),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
                    "rounds_per_block": float(np.mean(rounds)) if rounds else None,
-                   "sampler": "cumulative-entropy lock 0.1, T 0.8->0.4, stop 0.005 + stable"},
+                   "sampler": ("cumulative-entropy lock 0.1, T 0.8->0.4, stop 0.005 + stable"
+                               + (f", top-{args.top_k} truncation" if args.top_k else ""))},
         "denoise_step_ms": round(step_ms, 4),
         "kernels": per_kernel,
         "roofline": roof,

@@ -56,7 +56,7 @@ class SamplerParams(ctypes.Structure):
                 ("temp_start", ctypes.c_float), ("temp_end", ctypes.c_float),
                 ("stop_tau", ctypes.c_float), ("require_stable", ctypes.c_int32),
                 ("max_steps", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("selfcond_on", ctypes.c_int32)]
+                ("selfcond_on", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
 
 # exported symbol -> (restype, argtypes)
@@ -79,6 +79,7 @@ _SIGS = {
     "dg_sampler_workspace_bytes": (_I, [_I, _I, _P]),
     "dg_encode_prompt": (_I, [_P, _P, _I, _P, _I, _P, _SZ, _P]),
     "dg_denoise_step": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_denoise_step_topk": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "dg_sample_update": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_sample_update_probs": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                     _SZ, _P]),
@@ -139,7 +140,8 @@ def _stream(stream=None):
 def sampler_params(p: dict) -> SamplerParams:
     return SamplerParams(int(p["lock_rule"]), float(p["lock_theta"]), float(p["temp_start"]),
                          float(p["temp_end"]), float(p["stop_tau"]), int(p["require_stable"]),
-                         int(p["max_steps"]), int(p["seed"]), int(p.get("selfcond_on", 1)))
+                         int(p["max_steps"]), int(p["seed"]), int(p.get("selfcond_on", 1)),
+                         int(p.get("top_k", 0)))
 
 
 # ------------------------------------------------------------------ model handle
@@ -267,7 +269,16 @@ class Model:
         _check(lib().dg_encode_prompt(self.handle, self.kv, B, _ptr(tokens), P, _ptr(self.ws),
                                       self.ws.numel(), _stream(stream)))
 
-    def denoise_step(self, canvas, logits, prev_logits=None, prev_stats=None, stream=None):
+    def denoise_step(self, canvas, logits, prev_logits=None, prev_stats=None, stream=None,
+                     top_k: int = 0):
+        """dg_denoise_step (top_k > 0: dg_denoise_step_topk, the self-conditioning
+        truncated to each position's top_k previous logits)."""
+        if top_k:
+            _check(lib().dg_denoise_step_topk(self.handle, self.kv, canvas.shape[0], _ptr(canvas),
+                                              _ptr(prev_logits), _ptr(prev_stats), int(top_k),
+                                              _ptr(logits), _ptr(self.ws), self.ws.numel(),
+                                              _stream(stream)))
+            return
         _check(lib().dg_denoise_step(self.handle, self.kv, canvas.shape[0], _ptr(canvas),
                                      _ptr(prev_logits), _ptr(prev_stats), _ptr(logits),
                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))

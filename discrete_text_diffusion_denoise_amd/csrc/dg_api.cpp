@@ -171,6 +171,15 @@ struct Scratch {
     // already in `probs`, written by the sampler (probs_ready)
     bool fuse = false;
     bool probs_ready = false;
+    // top-k self-conditioning: the previous round's candidates and weights
+    // (written by the sampler in the block loop: topk_ready), and whether
+    // the head writes its slab maxima for the sampler
+    int topk = 0;
+    bool topk_ready = false;
+    bool want_rowmax = false;
+    int32_t* tk_idx;  // [canvas tokens][kTopKMax]
+    float* tk_p;
+    int32_t* zero;    // one int32 kept at 0 (the stop flag of a list-only pass)
     // set by the block loop (not carved): when *halt != 0 every sequence of
     // the batch has stopped and the heavy kernels of a round skip their work
     const int32_t* halt = nullptr;
@@ -229,6 +238,9 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
     s.tmax = m->blocked ? cv.take<float>(Tc * (size_t)(c.vocab / 64)) : nullptr;
+    s.tk_idx = cv.take<int32_t>(Tc * dg::kTopKMax);
+    s.tk_p = cv.take<float>(Tc * dg::kTopKMax);
+    s.zero = cv.take<int32_t>(64);
     return cv.ok;
 }
 
@@ -468,6 +480,30 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
                                  st));
         return DG_OK;
     }
+    if (s.topk > 0) {
+        // the previous distribution truncated to each position's top-k:
+        // candidates and weights from the sampler (block loop) or from the
+        // same selection run on the previous logits, then the gathered sum
+        if (!s.topk_ready) {
+            dg::SampleArgs a;
+            a.B = 1;
+            a.N = Tn;
+            a.V = c.vocab;
+            a.top_k = s.topk;
+            a.logits = prev_logits;
+            a.stop = s.zero;
+            a.tk_idx = s.tk_idx;
+            a.tk_p = s.tk_p;
+            a.list_only = 1;
+            DG_HIP(dg::fill_i32(s.zero, 0, 1, st));
+            DG_HIP(dg::sample_update(a, st));
+        }
+        DG_HIP(dg::selfcond_topk<T>((const T*)m->embed, c.d_model, s.tk_idx, s.tk_p, s.topk, Tn,
+                                    (T*)s.sc_s, st));
+        DG_TRY(linear<T>(s.sc_s, Tn, c.d_model, m->w_sc, c.d_model, h, c.d_model,
+                         dg::EPI_EMBED_ADD, s, st, m->embed, canvas, c.vocab));
+        return DG_OK;
+    }
     if (!m->embed_t) return fail(DG_ERR_ARG, "self-conditioning needs weights.embed_t");
     const int splits = sc_splits(m, Tn);
     dg::GemmArgs g;
@@ -540,7 +576,7 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
         g.A = s.ut;
         g.B = m->embed_head;
         g.a_tiled = g.b_tiled = 1;
-        if (s.fuse) g.rowmax = s.tmax;
+        if (s.want_rowmax) g.rowmax = s.tmax;
     } else {
         DG_HIP(dg::rmsnorm<T>(h, m->final_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
         g.A = s.u;
@@ -798,6 +834,32 @@ dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
     return dg_encode_prompt(m, kv, batch, d_block, m->c.canvas, d_ws, ws_bytes, stream);
 }
 
+dg_status dg_denoise_step_topk(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
+                               const float* d_prev_logits, const float* d_prev_stats,
+                               int32_t top_k, float* d_logits, void* d_ws, size_t ws_bytes,
+                               void* stream) {
+    if (top_k == 0)
+        return dg_denoise_step(m, kv, batch, d_canvas, d_prev_logits, d_prev_stats, d_logits,
+                               d_ws, ws_bytes, stream);
+    DG_TRY(check_model(m));
+    if (!kv || !d_canvas || !d_logits || !d_prev_logits) return fail(DG_ERR_ARG, "NULL argument");
+    if (top_k < 0 || top_k > dg::kTopKMax || top_k > m->c.vocab)
+        return fail(DG_ERR_ARG, "top_k %d outside [0, min(64, vocab)]", top_k);
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + m->c.canvas > kv->cap)
+        return fail(DG_ERR_CAPACITY, "cache needs len %d + canvas %d <= capacity %d", kv->len,
+                    m->c.canvas, kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    s.topk = top_k;
+    if (m->c.dtype == DG_BF16)
+        return denoise<bf16_t>(m, kv, batch, d_canvas, d_prev_logits, d_prev_stats, d_logits,
+                               s, as_stream(stream));
+    return denoise<float>(m, kv, batch, d_canvas, d_prev_logits, d_prev_stats, d_logits, s,
+                          as_stream(stream));
+}
+
 dg_status dg_denoise_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
                           const float* d_prev_logits, const float* d_prev_stats, float* d_logits,
                           void* d_ws, size_t ws_bytes, void* stream) {
@@ -826,12 +888,15 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              hipStream_t st, int32_t* nstop = nullptr,
                              int32_t* halt = nullptr, const float* rowmax = nullptr,
                              void* probs = nullptr, int probs_tiled = 1,
-                             int32_t* host_stop = nullptr) {
+                             int32_t* host_stop = nullptr, int32_t* tk_idx = nullptr,
+                             float* tk_p = nullptr) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
         return fail(DG_ERR_SHAPE, "need batch >= 1, 1 <= canvas <= 1024, 1 <= vocab <= 524288");
     if (p->max_steps < 1 || step < 0) return fail(DG_ERR_ARG, "bad step / max_steps");
+    if (p->top_k < 0 || p->top_k > dg::kTopKMax || p->top_k > vocab)
+        return fail(DG_ERR_ARG, "top_k %d outside [0, min(64, vocab)]", p->top_k);
     if (p->lock_rule != DG_LOCK_MAXPROB && p->lock_rule != DG_LOCK_CUMENT)
         return fail(DG_ERR_ARG, "lock_rule %d", p->lock_rule);
     if (!(p->temp_start > 0.f) || !(p->temp_end > 0.f))
@@ -877,6 +942,16 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
         a.rowmax_n = vocab / 64;
         a.probs = (uint16_t*)probs;
         a.probs_tiled = probs_tiled;
+    }
+    if (p->top_k > 0) {
+        // top-k truncation; the block loop passes the head's slab maxima and
+        // keeps the candidates for the next round's self-conditioning
+        a.top_k = p->top_k;
+        a.rowmax = rowmax;
+        a.rowmax_n = rowmax ? cdiv(vocab, 64) : 0;
+        a.probs = nullptr;
+        a.tk_idx = tk_idx;
+        a.tk_p = tk_p;
     }
     DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
     return DG_OK;
@@ -1017,7 +1092,9 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     // of round t while it reads round t's logits (the head GEMM supplies the
     // row maxima), so round t+1 skips the separate probability pass.  The
     // values are the same bits that pass would write.
-    s.fuse = p->selfcond_on && m->blocked && m->embed_head && fuse_probs();
+    s.fuse = p->selfcond_on && p->top_k == 0 && m->blocked && m->embed_head && fuse_probs();
+    s.topk = p->selfcond_on ? p->top_k : 0;
+    s.want_rowmax = (s.fuse || p->top_k > 0) && m->blocked && m->embed_head;
     const float* prev = nullptr;
     const float* prev_stats = nullptr;
     int t = 0;
@@ -1026,14 +1103,16 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
         float* logits = lg[t & 1];
         float* stats = stt[t & 1];
         s.probs_ready = s.fuse && t > 0;
+        s.topk_ready = s.topk > 0 && t > 0;
         if (c.dtype == DG_BF16)
             DG_TRY(denoise<bf16_t>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         else
             DG_TRY(denoise<float>(m, kv, batch, canvas, prev, prev_stats, logits, s, st));
         DG_TRY(sample_impl(p, t, batch, c.canvas, c.vocab, logits, canvas, argmax, lock, stats,
-                           stop, sws, sws_bytes, st, nstop, halt, s.fuse ? s.tmax : nullptr,
-                           s.fuse ? s.probs : nullptr, s.probs_tiled,
-                           m->hflags + (size_t)(t & 1) * m->hflags_cap));
+                           stop, sws, sws_bytes, st, nstop, halt,
+                           s.want_rowmax ? s.tmax : nullptr, s.fuse ? s.probs : nullptr,
+                           s.probs_tiled, m->hflags + (size_t)(t & 1) * m->hflags_cap,
+                           s.topk > 0 ? s.tk_idx : nullptr, s.topk > 0 ? s.tk_p : nullptr));
         DG_HIP(hipEventRecord(m->flag_ev[t & 1], st));
         if (t > 0) DG_TRY(flags_of(t - 1, &done));
         if (p->selfcond_on) {

@@ -75,6 +75,43 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int32_t v, lo
     if (i < n) p[i] = v;
 }
 
+// Top-k self-conditioning: s[row] = sum_i p_i E[idx_i] over the row's K
+// candidates, in candidate order (fp32).  A thread owns 8 consecutive
+// columns (16 bytes of a bf16 row); the candidates' rows are loaded eight at
+// a time, so eight loads per thread are in flight.
+template <typename T>
+__global__ __launch_bounds__(256) void selfcond_topk_kernel(const T* __restrict__ E, int d,
+                                                            const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ p, int K,
+                                                            T* __restrict__ out) {
+    const long row = blockIdx.x;
+    const int32_t* ri = idx + row * K;
+    const float* rp = p + row * K;
+    for (int c0 = threadIdx.x * 8; c0 < d; c0 += 256 * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i0 = 0; i0 < K; i0 += 8) {
+            float v[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + u, K - 1);
+                const T* src = E + (long)ri[i] * d + c0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[u][q] = Elt<T>::to_f(src[q]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (i0 + u < K) {
+                    const float w = rp[i0 + u];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[q] += w * v[u][q];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[row * d + c0 + q] = Elt<T>::from_f(acc[q]);
+    }
+}
+
 // RMSNorm of fp32 rows into the blocked bf16 layout (rows padded to 256 are
 // not written).
 __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float* __restrict__ h,
@@ -237,6 +274,19 @@ hipError_t splitk_reduce(const float* part, T* out, int splits, int rows, int co
                        0, st, part, out, splits, total, cols, row_stats);
     return hipGetLastError();
 }
+
+template <typename T>
+hipError_t selfcond_topk(const T* E, int d, const int32_t* idx, const float* p, int K, int rows,
+                         T* out, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (d % 8 || K < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(selfcond_topk_kernel<T>, dim3(rows), dim3(256), 0, st, E, d, idx, p, K, out);
+    return hipGetLastError();
+}
+template hipError_t selfcond_topk<bf16_t>(const bf16_t*, int, const int32_t*, const float*, int, int,
+                                          bf16_t*, hipStream_t);
+template hipError_t selfcond_topk<float>(const float*, int, const int32_t*, const float*, int, int,
+                                         float*, hipStream_t);
 
 hipError_t rmsnorm_tiled(const float* h, const float* w, uint16_t* u, int rows, int d, float eps,
                          hipStream_t st) {

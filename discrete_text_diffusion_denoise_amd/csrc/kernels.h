@@ -220,8 +220,24 @@ struct SampleArgs {
     int rowmax_n = 0;
     uint16_t* probs = nullptr;
     int probs_tiled = 1;
+    // top-k truncation (1 <= top_k <= 64; 0 = the full distribution): the
+    // statistics, draw and argmax come from each row's top_k logits; the
+    // slab maxima are read from rowmax when set (rowmax_n = V / 64), else
+    // computed from the row.  tk_idx / tk_p (optional, [B*N][top_k]) receive
+    // the candidates and their self-conditioning weights; list_only skips
+    // everything else (the self-conditioning of a stand-alone step).
+    int top_k = 0;
+    int32_t* tk_idx = nullptr;
+    float* tk_p = nullptr;
+    int list_only = 0;
 };
+constexpr int kTopKMax = 64;
 hipError_t sample_update(const SampleArgs& a, hipStream_t st);
+// s[t][:] = sum_i p[t][i] * E[idx[t][i]][:] over i < K in order (fp32), stored
+// in T; E [V][d] of T
+template <typename T>
+hipError_t selfcond_topk(const T* E, int d, const int32_t* idx, const float* p, int K, int rows,
+                         T* out, hipStream_t st);
 // Self-conditioning weights of logit rows [rows][V] with their statistics
 // (stats[r][0] = row max): bf16, row-major or 64-wide blocked (`tiled`,
 // tiled64_index, V % 64 == 0),

@@ -576,6 +576,274 @@ __global__ __launch_bounds__(256) void selfcond_probs_kernel(const float* __rest
     }
 }
 
+// ---------------------------------------------------------------- top-k
+// Report-summary page, section 8: at large batches a top-k truncation of
+// the distribution is the named missing throughput optimisation.  With K > 0
+// a row's statistics, draw and self-conditioning use its K largest logits,
+// c_0..c_{K-1} by value descending, ties to the lower index:
+//   m = l[c_0] (the argmax), z_i = l[c_i] - m, e_i = E(z_i), S and A the
+//   sums of e_i and e_i * z_i in candidate order, H = max(0, L(S) - A / S),
+//   pmax = 1 / S, draw: first running sum of w_i = E(z_i / T) above u * total
+//   (u from Philox word 0), else the last positive; weights p_i = e_i / S.
+// Finding the K largest without a full pass: with t the K-th largest of the
+// row's 64-entry slab maxima, at least K entries are >= t, so every top-K
+// entry is >= t and lies in a slab whose maximum is >= t.  The candidates
+// are the slabs above t and the lowest-index K slabs whose maximum equals t
+// (entries equal to t rank by index); their entries >= t are sorted.
+
+constexpr int TK_THR = 256;
+constexpr int TK_KEYS = 8192;      // >= (2 * kTopKMax - 1) * 64, a power of two
+
+// Order-preserving unsigned key of a finite float (-0 taken as +0, so keys
+// are equal exactly when the values compare equal).
+__device__ __forceinline__ uint32_t okey(float v) {
+    const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(TK_THR) void sample_topk_kernel(SampleArgs a) {
+    extern __shared__ __align__(16) unsigned char tk_sm[];
+    const int nslab = cdiv(a.V, 64);
+    uint64_t* keys = reinterpret_cast<uint64_t*>(tk_sm);                 // [TK_KEYS]
+    float* cval = reinterpret_cast<float*>(keys + TK_KEYS);              // [2 kTopKMax][64]
+    uint32_t* skey = reinterpret_cast<uint32_t*>(cval + 2 * kTopKMax * 64);   // [nslab]
+    __shared__ uint32_t hist[TK_THR / 64][256];   // one histogram per wave
+    __shared__ int gt_list[kTopKMax], eq_list[kTopKMax];
+    __shared__ int ctl[4];               // selected digit, remaining rank, #gt, #eq (capped)
+    __shared__ uint32_t red[2][TK_THR / 64];
+    __shared__ unsigned int nf;
+    __shared__ int cidx[kTopKMax];
+    __shared__ float cz[kTopKMax], ce[kTopKMax], cw[kTopKMax];
+    __shared__ float sS;
+
+    const long rowid = blockIdx.x;
+    const int b = (int)(rowid / a.N), i = (int)(rowid % a.N);
+    if (a.stop[b]) return;
+    const float* row = a.logits + rowid * (long)a.V;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = min(a.top_k, a.V);
+
+    // 1. slab maxima as keys, and their smallest and largest key
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+    if (a.rowmax) {
+        const float* rm = a.rowmax + rowid * (long)nslab;
+        for (int sl = tid; sl < nslab; sl += TK_THR) {
+            const uint32_t k = okey(rm[sl]);
+            skey[sl] = k;
+            lmin = min(lmin, k);
+            lmax = max(lmax, k);
+        }
+    } else {
+        for (int sl = tid; sl < nslab; sl += TK_THR) {
+            const int k0 = sl * 64, k1 = min(a.V, k0 + 64);
+            float mx = row[k0];
+            for (int k = k0 + 1; k < k1; ++k) mx = fmaxf(mx, row[k]);
+            const uint32_t k = okey(mx);
+            skey[sl] = k;
+            lmin = min(lmin, k);
+            lmax = max(lmax, k);
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lmin = min(lmin, (uint32_t)__shfl_xor((int)lmin, o, 64));
+        lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, o, 64));
+    }
+    if (lane == 0) {
+        red[0][wave] = lmin;
+        red[1][wave] = lmax;
+    }
+    __syncthreads();
+    uint32_t kmin = red[0][0], kmax = red[1][0];
+#pragma unroll
+    for (int w = 1; w < TK_THR / 64; ++w) {
+        kmin = min(kmin, red[0][w]);
+        kmax = max(kmax, red[1][w]);
+    }
+
+    // 2. t = the K-th largest slab key: radix select over the bits below the
+    // keys' common prefix, 8 at a time (fewer slabs than K: every slab is a
+    // candidate, t below every key)
+    uint32_t prefix = 0, pmask = 0;
+    int hi = 0;
+    if (K <= nslab) {
+        const uint32_t diff = kmin ^ kmax;
+        hi = diff ? 32 - __builtin_clz(diff) : 0;       // bits still to decide
+        pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+        prefix = kmax & pmask;
+    }
+    int need = K;
+#pragma unroll 1
+    while (hi > 0) {
+        const int w = hi < 8 ? hi : 8;
+        const int shift = hi - w;
+        const uint32_t dmask = (1u << w) - 1u;
+        for (int x = tid; x < (TK_THR / 64) * 256; x += TK_THR) (&hist[0][0])[x] = 0u;
+        __syncthreads();
+        for (int sl = tid; sl < nslab; sl += TK_THR) {
+            const uint32_t k = skey[sl];
+            if ((k & pmask) == prefix) atomicAdd(&hist[wave][(k >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds digits 4l .. 4l+3; counts from the top digit down
+            uint32_t cnt[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cnt[q] = 0;
+#pragma unroll
+                for (int ww = 0; ww < TK_THR / 64; ++ww) cnt[q] += hist[ww][4 * lane + q];
+                tot += cnt[q];
+            }
+            uint32_t suf = tot;                       // lanes >= l
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = (uint32_t)__shfl_down((int)suf, o, 64);
+                if (lane + o < 64) suf += t;
+            }
+            uint32_t acc = suf - tot;                 // lanes > l: larger digits
+#pragma unroll
+            for (int q = 3; q >= 0; --q) {
+                if (acc < (uint32_t)need && acc + cnt[q] >= (uint32_t)need) {
+                    ctl[0] = 4 * lane + q;
+                    ctl[1] = need - (int)acc;
+                }
+                acc += cnt[q];
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)ctl[0] << shift;
+        pmask |= dmask << shift;
+        need = ctl[1];
+        hi = shift;
+        __syncthreads();
+    }
+
+    // 3. candidate slabs, in slab order: all above t, the first K equal to t
+    if (wave == 0) {
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        int ngt = 0, neq = 0;
+        for (int base = 0; base < nslab; base += 64) {
+            const int sl = base + lane;
+            const uint32_t k = sl < nslab ? skey[sl] : 0u;
+            const bool gt = sl < nslab && k > prefix, eq = sl < nslab && k == prefix;
+            const uint64_t mg = __ballot(gt), me = __ballot(eq);
+            const int rg = __popcll(mg & below), re = __popcll(me & below);
+            if (gt && ngt + rg < kTopKMax) gt_list[ngt + rg] = sl;
+            if (eq && neq + re < K) eq_list[neq + re] = sl;
+            ngt += __popcll(mg);
+            neq += __popcll(me);
+        }
+        if (lane == 0) {
+            ctl[2] = min(ngt, kTopKMax);    // at most K - 1 slabs exceed t
+            ctl[3] = min(neq, K);
+            nf = 0;
+        }
+    }
+    __syncthreads();
+    const int ngt = ctl[2], ncand = ctl[2] + ctl[3];
+
+    // 4. the candidate slabs' logits into LDS (16 threads a slab, all loads
+    // issued before any is used), then their entries >= t as (key, reversed
+    // index) pairs
+    const bool vec = (a.V & 3) == 0;
+#pragma unroll 8
+    for (int base = 0; base < 2 * kTopKMax; base += TK_THR / 16) {
+        const int j = base + (tid >> 4);
+        if (j < ncand) {
+            const int sl = j < ngt ? gt_list[j] : eq_list[j - ngt];
+            const int q = (tid & 15) * 4;
+            const int k = sl * 64 + q;
+            float4 v;
+            if (vec && k + 3 < a.V) {
+                v = *reinterpret_cast<const float4*>(row + k);
+            } else {
+                v.x = k < a.V ? row[k] : 0.0f;
+                v.y = k + 1 < a.V ? row[k + 1] : 0.0f;
+                v.z = k + 2 < a.V ? row[k + 2] : 0.0f;
+                v.w = k + 3 < a.V ? row[k + 3] : 0.0f;
+            }
+            *reinterpret_cast<float4*>(cval + j * 64 + q) = v;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < ncand * 64; e += TK_THR) {
+        const int j = e >> 6;
+        const int sl = j < ngt ? gt_list[j] : eq_list[j - ngt];
+        const int k = sl * 64 + (e & 63);
+        if (k < a.V) {
+            const uint32_t kv = okey(cval[e]);
+            if (kv >= prefix) {
+                const unsigned int pos = atomicAdd(&nf, 1u);
+                keys[pos] = ((uint64_t)kv << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)k);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. bitonic sort, descending (larger value first, then lower index)
+    int P = 64;
+    while (P < (int)nf) P <<= 1;
+    for (int e = (int)nf + tid; e < P; e += TK_THR) keys[e] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int x = tid; x < P; x += TK_THR) {
+                const int y = x ^ stride;
+                if (y > x) {
+                    const bool desc = (x & size) == 0;
+                    const uint64_t kx = keys[x], ky = keys[y];
+                    if ((kx < ky) == desc) {
+                        keys[x] = ky;
+                        keys[y] = kx;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 6. the K candidates: weights in parallel, the sums in order
+    if (tid < K) cidx[tid] = (int)(0xFFFFFFFFu - (uint32_t)keys[tid]);
+    __syncthreads();
+    const float m = row[cidx[0]];
+    if (tid < K) {
+        const float z = row[cidx[tid]] - m;
+        cz[tid] = z;
+        ce[tid] = dexp(z);
+        cw[tid] = dexp(z * a.inv_t);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float S = 0.0f, A = 0.0f;
+        for (int c = 0; c < K; ++c) {
+            S = S + ce[c];
+            const float ez = ce[c] * cz[c];
+            A = A + ez;
+        }
+        sS = S;
+        if (!a.list_only) {
+            uint64_t o[4];
+            philox((uint64_t)a.step, (uint64_t)b, (uint64_t)i, 0ull, a.seed, 0ull, o);
+            float H = dlog(S) - A / S;
+            H = H > 0.0f ? H : 0.0f;
+            float* st = a.stats + rowid * 4;
+            st[0] = m;
+            st[1] = S;
+            st[2] = H;
+            st[3] = 1.0f / S;
+            a.newmax[rowid] = cidx[0];
+            a.y[rowid] = cidx[pick_seq(cw, K, uniform01(o[0]))];
+            a.r[rowid] = uniform_token(o[1], a.V);
+        }
+    }
+    __syncthreads();
+    if (a.tk_idx && tid < K) {
+        a.tk_idx[rowid * K + tid] = cidx[tid];
+        a.tk_p[rowid * K + tid] = ce[tid] / sS;
+    }
+}
+
 // One workgroup per canvas: lock rule, renoise, stability and stop.
 __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
     const int b = blockIdx.x;
@@ -671,6 +939,26 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(uint64_t seed, int blo
 
 hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
     if (a.B <= 0 || a.N <= 0) return hipSuccess;
+    if (a.top_k > 0) {
+        const int nslab = cdiv(a.V, 64);
+        if (a.top_k > kTopKMax || a.top_k > a.V || (a.rowmax && a.rowmax_n != nslab) ||
+            (a.tk_idx == nullptr) != (a.tk_p == nullptr) || (a.list_only && !a.tk_idx))
+            return hipErrorInvalidValue;
+        const size_t lds = (size_t)TK_KEYS * 8 + (size_t)2 * kTopKMax * 64 * 4 + (size_t)nslab * 4;
+        static bool tk_attr = false;
+        if (!tk_attr) {
+            hipError_t e = hipFuncSetAttribute((const void*)sample_topk_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(TK_KEYS * 8 + 2 * kTopKMax * 64 * 4 + 8192 * 4));
+            if (e != hipSuccess) return e;
+            tk_attr = true;
+        }
+        hipLaunchKernelGGL(sample_topk_kernel, dim3(a.B * a.N), dim3(TK_THR), lds, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.list_only) return e;
+        hipLaunchKernelGGL(sample_canvas_kernel, dim3(a.B), dim3(1024), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.probs && (a.V % 128 || !a.rowmax || a.rowmax_n < 1 || ((uintptr_t)a.logits & 15) ||
                     ((uintptr_t)a.probs & 7)))
         return hipErrorInvalidValue;

@@ -128,6 +128,10 @@ typedef struct {
     int32_t max_steps;       /* round budget (>= 1)                            */
     uint64_t seed;           /* Philox key                                     */
     int32_t selfcond_on;     /* dg_generate_block: feed previous logits back   */
+    int32_t top_k;           /* 0: the full distribution; 1..64: top-k         */
+                             /* truncation (report-summary page, section 8):  */
+                             /* statistics, draw and self-conditioning use     */
+                             /* each position's top_k logits only              */
 } dg_sampler_params;
 
 typedef struct dg_model dg_model;
@@ -226,6 +230,18 @@ dg_status dg_denoise_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
                           const float* d_prev_logits, const float* d_prev_stats,
                           float* d_logits, void* d_ws, size_t ws_bytes, void* stream);
 
+/* dg_denoise_step whose self-conditioning uses the previous round's
+ * distribution truncated to each position's top_k logits (what the sampler
+ * used with params->top_k = top_k): s = sum_i p_i E[c_i] over the top_k
+ * candidates c_i (value descending, ties to the lower index) with
+ * p_i = e_i / S as the sampler defines them.  top_k = 0 is dg_denoise_step;
+ * 1 <= top_k <= min(64, vocab) (DG_ERR_ARG otherwise).  d_prev_stats may be
+ * NULL when top_k > 0. */
+dg_status dg_denoise_step_topk(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
+                               const float* d_prev_logits, const float* d_prev_stats,
+                               int32_t top_k, float* d_logits, void* d_ws, size_t ws_bytes,
+                               void* stream);
+
 /* Sampler update of step `step` (report-summary page, sections 1 and 4).
  * Model-free: reads fp32 logits [batch][N][V]; for every canvas b with
  * d_stop[b] == 0 it writes, per position,
@@ -239,6 +255,9 @@ dg_status dg_denoise_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
  * arithmetic (statistics, draw, lock and stop) is fixed exactly, so results
  * are bit-reproducible and match the reference definition bit for bit.
  * Random numbers: Philox4x64-10, key (seed, 0), counter (step, b, i, 0).
+ * params->top_k > 0 (<= 64, <= vocab): the statistics, argmax and draw use
+ * each position's top_k logits only (value descending, ties to the lower
+ * index; sums in that order; one inverse-CDF draw with word 0).
  * d_ws needs dg_sampler_workspace_bytes.  N <= 1024, vocab <= 524288. */
 dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t batch,
                            int32_t canvas, int32_t vocab, const float* d_logits,

@@ -138,15 +138,20 @@ def test_encode_prompt_kv_cache(name, P, B):
 # random-init MoE layers.  bf16 runs end to end on one layer (the shape of the
 # single-layer benchmark configuration); multi-layer bf16 is covered stage by
 # stage with identical inputs.
-@pytest.mark.parametrize("name,P,B,selfcond,layers", [("tiny", 32, 1, False, 1),
-                                                      ("tiny", 32, 1, True, 1),
-                                                      ("small_bf16", 200, 2, False, 1),
-                                                      ("small_bf16", 200, 2, True, 1),
-                                                      ("f32_gqa", 64, 2, True, 2),
-                                                      ("f32_gqa", 64, 1, False, 3),
-                                                      ("small_fp8", 200, 2, True, 1)])
-def test_denoise_step(name, P, B, selfcond, layers):
-    print(f"denoise {name} P={P} B={B} selfcond={selfcond} layers={layers}", flush=True)
+@pytest.mark.parametrize("name,P,B,selfcond,layers,top_k", [("tiny", 32, 1, False, 1, 0),
+                                                             ("tiny", 32, 1, True, 1, 0),
+                                                             ("small_bf16", 200, 2, False, 1, 0),
+                                                             ("small_bf16", 200, 2, True, 1, 0),
+                                                             ("f32_gqa", 64, 2, True, 2, 0),
+                                                             ("f32_gqa", 64, 1, False, 3, 0),
+                                                             ("small_fp8", 200, 2, True, 1, 0),
+                                                             ("tiny", 32, 1, True, 1, 64),
+                                                             ("small_bf16", 200, 2, True, 1, 8)])
+def test_denoise_step(name, P, B, selfcond, layers, top_k):
+    """top_k > 0: the self-conditioning truncated to each position's top_k
+    previous logits (dg_denoise_step_topk)."""
+    print(f"denoise {name} P={P} B={B} selfcond={selfcond} layers={layers} top_k={top_k}",
+          flush=True)
     cfg, W, m = setup(name, P, batch=B, n_layers=layers)
     N, V = cfg["canvas"], cfg["vocab"]
     prompt = synthetic.make_tokens(V, (B, P), seed=2)
@@ -160,7 +165,7 @@ def test_denoise_step(name, P, B, selfcond, layers):
         for b in range(B):
             for i in range(N):
                 stats[b, i], _ = osampler.row_stats(prev[b, i])
-        m.denoise_step(to_dev(canvas), logits, to_dev(prev), to_dev(stats))
+        m.denoise_step(to_dev(canvas), logits, to_dev(prev), to_dev(stats), top_k=top_k)
     else:
         m.denoise_step(to_dev(canvas), logits)
     torch.cuda.synchronize()
@@ -174,7 +179,7 @@ def test_denoise_step(name, P, B, selfcond, layers):
     keep = np.ones((B, N), dtype=bool)
     refs = []
     for b in range(B):
-        h = om.denoiser_input(canvas[b], W64, None if prev is None else prev[b])
+        h = om.denoiser_input(canvas[b], W64, None if prev is None else prev[b], top_k)
         for li, lw in enumerate(W64["layers"]):
             h, _, _ = om.attn_half(h, lw, cfg, cache.k[li][b], cache.v[li][b], P, causal=False)
             u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
@@ -320,13 +325,16 @@ def test_commit_equals_encode_of_concatenation():
     assert normwise(V1[..., :L, :].float().cpu().numpy(), V2[..., :L, :].float().cpu().numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("name,B,selfcond,early", [("tiny", 1, True, False),
-                                                   ("small_bf16", 2, True, False),
-                                                   ("vocab_bf16", 1, True, False),
-                                                   ("small_fp8", 2, True, False),
-                                                   ("small_bf16", 2, False, False),
-                                                   ("small_bf16", 2, True, True)])
-def test_generate_block_is_its_composition(name, B, selfcond, early):
+@pytest.mark.parametrize("name,B,selfcond,early,top_k", [("tiny", 1, True, False, 0),
+                                                         ("small_bf16", 2, True, False, 0),
+                                                         ("vocab_bf16", 1, True, False, 0),
+                                                         ("small_fp8", 2, True, False, 0),
+                                                         ("small_bf16", 2, False, False, 0),
+                                                         ("small_bf16", 2, True, True, 0),
+                                                         ("tiny", 1, True, False, 16),
+                                                         ("small_bf16", 2, True, False, 64),
+                                                         ("vocab_bf16", 1, True, False, 32)])
+def test_generate_block_is_its_composition(name, B, selfcond, early, top_k):
     """dg_generate_block == canvas init + (denoise, sample) rounds + commit,
     driven call by call; bitwise identical block, round counts and cache.
     early: every sequence stops after its first round (entropy threshold
@@ -338,9 +346,10 @@ def test_generate_block_is_its_composition(name, B, selfcond, early):
     prompt = synthetic.make_tokens(V, (B, P), seed=30)
     if early:
         params = synthetic.default_sampler_params(max_steps=5, seed=5, selfcond_on=int(selfcond),
-                                                  stop_tau=1e9, require_stable=0)
+                                                  stop_tau=1e9, require_stable=0, top_k=top_k)
     else:
-        params = synthetic.default_sampler_params(max_steps=3, seed=5, selfcond_on=int(selfcond))
+        params = synthetic.default_sampler_params(max_steps=3, seed=5, selfcond_on=int(selfcond),
+                                                  top_k=top_k)
     # library loop
     mg = binding.Model(cfg, m.src_weights, batch=B, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(to_dev(prompt))
@@ -361,7 +370,7 @@ def test_generate_block_is_its_composition(name, B, selfcond, early):
     prev = prev_st = None
     my_steps = [0] * B
     for t in range(params["max_steps"]):
-        mc.denoise_step(canvas, lg[t % 2], prev, prev_st)
+        mc.denoise_step(canvas, lg[t % 2], prev, prev_st, top_k=top_k if prev is not None else 0)
         binding.sample_update(params, t, lg[t % 2], canvas, argmax, lock, st[t % 2], stop, ws)
         s = stop.cpu().tolist()
         for b in range(B):

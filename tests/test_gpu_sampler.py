@@ -229,3 +229,54 @@ def test_stage_probs_row_major_matches_blocked():
     a = (rm.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(T, V)
     b = unblock_bf16(bl.cpu().numpy(), T, V)
     assert (a.view(np.uint32) == b.view(np.uint32)).all()
+
+
+TOPK_CASES = [
+    # B, N, V, K, sigma, pattern
+    (1, 256, 262144, 64, 0.9, "normal"),         # the full vocabulary
+    (2, 64, 4096, 8, 2.0, "normal"),
+    (1, 16, 70001, 16, 1.5, "normal"),          # partial last slab, V % 4 != 0
+    (1, 8, 1000, 64, 1.0, "normal"),            # fewer slabs (16) than K
+    (1, 4, 5000, 1, 1.0, "normal"),
+    (1, 8, 8192, 32, 1.0, "equal"),             # every logit equal: slabs tie at t
+    (1, 8, 8192, 32, 1.0, "coarse"),            # logits on a 0.5 grid: many ties
+    (1, 8, 8192, 64, 1.0, "top_repeated"),      # the maximum in 300 slabs
+]
+
+
+def topk_logits(B, N, V, sigma, pattern, seed):
+    L = synthetic.make_logits((B, N, V), seed=seed, sigma=sigma)
+    if pattern == "equal":
+        L[:] = 1.25
+    elif pattern == "coarse":
+        L = (np.round(L * 2) / 2).astype(np.float32)
+    elif pattern == "top_repeated":
+        rng = np.random.default_rng(seed)
+        for b in range(B):
+            for i in range(N):
+                L[b, i, rng.choice(V, 300, replace=False)] = L[b, i].max() + 1.0
+    return L
+
+
+@pytest.mark.parametrize("B,N,V,K,sigma,pattern", TOPK_CASES)
+def test_topk_sample_update_bit_exact(B, N, V, K, sigma, pattern):
+    """Top-k truncation: candidates, statistics, draw, locks and stop flags
+    bit-identical to the C oracle (slab maxima computed by the kernel)."""
+    print(f"top-k sampler case B={B} N={N} V={V} K={K} {pattern}", flush=True)
+    params = synthetic.default_sampler_params(top_k=K, seed=77)
+    logits = topk_logits(B, N, V, sigma, pattern, seed=V + K)
+    canvas = synthetic.make_tokens(V, (B, N), seed=5)
+    argmax = synthetic.make_tokens(V, (B, N), seed=6)
+    stop = np.zeros(B, dtype=np.int32)
+    for step in (0, 3):
+        g = gpu_update(params, step, logits, canvas, argmax, stop)
+        r = oracle_update(params, step, logits, canvas, argmax, stop)
+        assert_same(g, r, f"top-k B={B} N={N} V={V} K={K} {pattern} step {step}")
+
+
+def test_topk_rejects_bad_k():
+    params = synthetic.default_sampler_params(top_k=65)
+    logits = synthetic.make_logits((1, 4, 1000), seed=1)
+    with pytest.raises(binding.DGError):
+        gpu_update(params, 0, logits, np.zeros((1, 4), np.int32), np.zeros((1, 4), np.int32),
+                   np.zeros(1, np.int32))
