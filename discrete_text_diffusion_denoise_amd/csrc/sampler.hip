@@ -577,7 +577,7 @@ __global__ __launch_bounds__(256) void selfcond_probs_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------- top-k
-// Report-summary page, section 8: at large batches a top-k truncation of
+// Report-summary page, section 9 (known limitations): at large batches a top-k truncation of
 // the distribution is the named missing throughput optimisation.  With K > 0
 // a row's statistics, draw and self-conditioning use its K largest logits,
 // c_0..c_{K-1} by value descending, ties to the lower index:

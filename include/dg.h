@@ -129,7 +129,7 @@ typedef struct {
     uint64_t seed;           /* Philox key                                     */
     int32_t selfcond_on;     /* dg_generate_block: feed previous logits back   */
     int32_t top_k;           /* 0: the full distribution; 1..64: top-k         */
-                             /* truncation (report-summary page, section 8):  */
+                             /* truncation (report-summary page, section 9):  */
                              /* statistics, draw and self-conditioning use     */
                              /* each position's top_k logits only              */
 } dg_sampler_params;

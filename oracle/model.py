@@ -198,7 +198,7 @@ def selfcond_vector(prev_logits: np.ndarray, W: dict, top_k: int = 0) -> np.ndar
     """Expected embedding under the previous round's T = 1 distribution:
     s = softmax(L_prev) E, per position.  prev_logits [..., V].  With top_k
     > 0 the distribution is truncated to each position's top_k logits and
-    renormalised (report-summary page, section 8: top-k truncation)."""
+    renormalised (report-summary page, section 9 (known limitations): top-k truncation)."""
     L = np.asarray(prev_logits, dtype=np.float64)
     if top_k <= 0:
         p = np.exp(L - L.max(axis=-1, keepdims=True))

@@ -379,7 +379,7 @@ int ora_stop_flag(int N, const float* H, int stable, float tau, int require_stab
 }
 
 /* ------------------------------------------------------------------ */
-/* Top-k truncation (report-summary page, section 8: at large batches a */
+/* Top-k truncation (report-summary page, section 9, known limitations:  */
 /* top-k truncation of the distribution is the named missing            */
 /* throughput optimisation).  With K > 0 a position's statistics, draw  */
 /* and self-conditioning use only its K largest logits.                 */
