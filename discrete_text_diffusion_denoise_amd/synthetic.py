@@ -38,7 +38,7 @@ SHAPES = {
     # 8 canvases with 8192-token prompts each
     "batched": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                     n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
-                    prompt=8192, batch=8, max_steps=48),
+                    prompt=8192, batch=8, max_steps=48, stop_tau=0.05),
     # long prompt, 8 consecutive blocks committed to the cache
     "long": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                  n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
