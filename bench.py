@@ -227,8 +227,8 @@ def cpu_baseline(cfg, W, prompt, canvas, params, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the step would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the kernels run on one GPU's share at full shape).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

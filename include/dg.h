@@ -55,7 +55,7 @@ typedef enum {
     DG_ERR_CAPACITY = 4,    /* KV cache or workspace too small                  */
     DG_ERR_NONFINITE = 5,   /* reserved: non-finite values detected             */
     DG_ERR_HIP = 6,         /* a HIP runtime call failed                        */
-    DG_ERR_UNSUPPORTED = 7  /* valid request this build does not implement      */
+    DG_ERR_UNSUPPORTED = 7  /* valid request the library does not implement     */
 } dg_status;
 
 typedef enum {

@@ -22,7 +22,7 @@ What the pages fix, and where:
 Everything else (pre-norm RMSNorm, rotate-half RoPE, SwiGLU experts, softmax
 over the selected router logits, a single d x d self-conditioning projection
 of the expected embedding, tied output head) is the plainest reading the pages
-support; each is listed in DESIGN.md.
+support; each is named where it is used below.
 
 Weight layout (all float64 here): every linear map is stored as
 [out_features, in_features] and applied as x @ W.T.

@@ -20,8 +20,8 @@
  * this file fixes the arithmetic completely -- every operation is an IEEE
  * binary32 operation in the order written here, with fma only where written --
  * and the GPU sampler implements the same definition independently.  The
- * definition (chunk layout, merge rule, three-level draw) is the build's own
- * reading of the pages and is written out in the design doc.
+ * definition (chunk layout, merge rule, three-level draw) is this library's
+ * own reading of the pages, written out in the functions below.
  *
  * Build: gcc -O2 -std=gnu11 -ffp-contract=off -fno-fast-math -shared -fPIC
  * (contraction off: a*b+c must stay two roundings unless fmaf is written).
