@@ -252,6 +252,80 @@ def encode(tokens: np.ndarray, W: dict, cfg: dict, cache: KVCache) -> None:
     cache.length = pos0 + n
 
 
+# ---------------------------------------------------------------- AR mode
+# Report-summary page, section 7: the diffusion model keeps its autoregressive
+# starting point's architecture, so the same weights also run as an ordinary
+# causal language model.  Section 5 describes that mode's step: one new token
+# per step, attending over the cached history.  Plainest reading: the same
+# stack with causal attention for every layer, every layer's MoE, the final
+# norm and the tied head on the new token; greedy decoding takes the largest
+# logit.
+
+def causal_logits(tokens: np.ndarray, W: dict, cfg: dict) -> np.ndarray:
+    """Causal language-model forward of one sequence tokens [n] from an empty
+    context: every layer with causal attention and its MoE, then the head.
+    Returns float64 logits [n, V]; row t scores the token after position t."""
+    tokens = np.asarray(tokens).reshape(-1)
+    h = embed(tokens, W)
+    empty = np.zeros((cfg["n_kv_heads"], 0, cfg["head_dim"]))
+    for lw in W["layers"]:
+        h, _, _ = attn_half(h, lw, cfg, empty, empty, 0, causal=True)
+        h, _, _, _ = moe_half(h, lw, cfg)
+    return head(h, W, cfg)
+
+
+def ar_decode_step(tokens: np.ndarray, W: dict, cfg: dict, cache: KVCache) -> np.ndarray:
+    """One decode step of B sequences: tokens [B] at position cache.length.
+    Each layer appends the token's K/V to the cache, and every layer's MoE
+    runs (the token's hidden state feeds the head).  Returns float64 logits
+    [B, V]; the cache grows by one position."""
+    tokens = np.asarray(tokens).reshape(-1)
+    B = tokens.size
+    pos0 = cache.length
+    dh = cfg["head_dim"]
+    for li in range(len(W["layers"])):
+        cache.k[li] = np.concatenate([cache.k[li], np.zeros(cache.k[li].shape[:2] + (1, dh))],
+                                     axis=2)
+        cache.v[li] = np.concatenate([cache.v[li], np.zeros(cache.v[li].shape[:2] + (1, dh))],
+                                     axis=2)
+    out = np.zeros((B, W["embed"].shape[0]))
+    for b in range(B):
+        h = embed(tokens[b:b + 1], W)
+        for li, lw in enumerate(W["layers"]):
+            h, kn, vn = attn_half(h, lw, cfg, cache.k[li][b][:, :pos0], cache.v[li][b][:, :pos0],
+                                  pos0, causal=True)
+            cache.k[li][b, :, pos0:pos0 + 1] = kn
+            cache.v[li][b, :, pos0:pos0 + 1] = vn
+            h, _, _, _ = moe_half(h, lw, cfg)
+        out[b] = head(h, W, cfg)[0]
+    cache.length = pos0 + 1
+    return out
+
+
+def greedy_token(logits: np.ndarray) -> np.ndarray:
+    """Greedy choice per row: the index of the largest logit, ties to the
+    lower index."""
+    return np.argmax(np.asarray(logits), axis=-1).astype(np.int32)
+
+
+def ar_generate(first: np.ndarray, n_new: int, W: dict, cfg: dict, cache: KVCache,
+                logits_of=None) -> np.ndarray:
+    """Greedy decoding of n_new tokens per sequence: step t decodes the
+    previous token (first [B] at t = 0) and takes the greedy token of its
+    logits.  logits_of(t, logits) may replace a step's logits (tests feed
+    the device's own logits here so both sides take identical decisions).
+    Returns int32 tokens [B, n_new]."""
+    tok = np.asarray(first).reshape(-1).astype(np.int32)
+    out = np.zeros((tok.size, n_new), dtype=np.int32)
+    for t in range(n_new):
+        lg = ar_decode_step(tok, W, cfg, cache)
+        if logits_of is not None:
+            lg = logits_of(t, lg)
+        tok = greedy_token(lg)
+        out[:, t] = tok
+    return out
+
+
 def denoise_step(canvas: np.ndarray, W: dict, cfg: dict, cache: KVCache,
                  prev_logits: np.ndarray | None = None, top_k: int = 0) -> np.ndarray:
     """One denoiser forward over canvases [B, N] with bidirectional attention
