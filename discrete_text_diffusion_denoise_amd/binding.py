@@ -86,6 +86,9 @@ _SIGS = {
     "dg_stage_probs": (_I, [_I, _I, _I, _P, _P, _P, _P]),
     "dg_canvas_init": (_I, [_U64, _I, _I, _I, _I, _P, _P]),
     "dg_commit_block": (_I, [_P, _P, _I, _P, _P, _SZ, _P]),
+    "dg_ar_decode_step": (_I, [_P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "dg_argmax_rows": (_I, [_I, _I, _P, _P, _P]),
+    "dg_ar_generate": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "dg_generate_workspace_bytes": (_I, [_P, _I, _P]),
     "dg_generate_block": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "dg_stage_input": (_I, [_P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -283,6 +286,19 @@ class Model:
                                      _ptr(prev_logits), _ptr(prev_stats), _ptr(logits),
                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))
 
+    def ar_decode_step(self, tokens, logits, stream=None):
+        """dg_ar_decode_step: tokens [B] int32 -> logits [B, V] f32; len += 1."""
+        _check(lib().dg_ar_decode_step(self.handle, self.kv, tokens.shape[0], _ptr(tokens),
+                                       _ptr(logits), _ptr(self.ws), self.ws.numel(),
+                                       _stream(stream)))
+
+    def ar_generate(self, first, n_new: int, out, logits, stream=None):
+        """dg_ar_generate: greedy decoding of n_new tokens per sequence from
+        first [B] into out [B, n_new] int32; logits [B, V] f32 scratch."""
+        _check(lib().dg_ar_generate(self.handle, self.kv, first.shape[0], _ptr(first), int(n_new),
+                                    _ptr(out), _ptr(logits), _ptr(self.ws), self.ws.numel(),
+                                    _stream(stream)))
+
     def commit_block(self, block, stream=None):
         _check(lib().dg_commit_block(self.handle, self.kv, block.shape[0], _ptr(block),
                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))
@@ -350,6 +366,12 @@ def sample_update_probs(params: dict, step: int, logits, canvas, argmax, lock, s
                                         _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats),
                                         _ptr(stop), _ptr(rowmax), 1 if blocked else 0, _ptr(probs),
                                         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def argmax_rows(logits, out, stream=None):
+    """dg_argmax_rows: logits [R, V] f32 -> out [R] int32 (ties to the lower index)."""
+    R, V = logits.shape
+    _check(lib().dg_argmax_rows(R, V, _ptr(logits), _ptr(out), _stream(stream)))
 
 
 def stage_probs(logits, stats, probs, blocked: bool, stream=None):

@@ -622,6 +622,23 @@ dg_status encode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int P, Sc
     return DG_OK;
 }
 
+// Retained autoregressive mode: one token per sequence at position kv->len
+// (token b at tokens[b * ld]), causal attention over the cache in every
+// layer, every layer's MoE, then the head on the new tokens.
+template <typename T>
+dg_status ar_decode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int ld, float* logits,
+                    Scratch& s, hipStream_t st) {
+    const dg_config& c = m->c;
+    const int pos0 = kv->len;
+    DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens, ld, 1, B, s.h, c.d_model, st));
+    for (int l = 0; l < c.n_layers; ++l) {
+        DG_TRY(attn_half<T>(m, kv, l, B, 1, pos0, 1, s.h, s, st));
+        DG_TRY(moe_half<T>(m, l, B, s.h, s, st));
+    }
+    kv->len += 1;
+    return stage_head<T>(m, B, s.h, logits, s, st);
+}
+
 dg_status check_model(const dg_model* m) {
     if (!m) return fail(DG_ERR_ARG, "model is NULL");
     return DG_OK;
@@ -832,6 +849,65 @@ dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
                           void* d_ws, size_t ws_bytes, void* stream) {
     DG_TRY(check_model(m));
     return dg_encode_prompt(m, kv, batch, d_block, m->c.canvas, d_ws, ws_bytes, stream);
+}
+
+dg_status dg_ar_decode_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_tokens,
+                            float* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_tokens || !d_logits) return fail(DG_ERR_ARG, "NULL argument");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + 1 > kv->cap)
+        return fail(DG_ERR_CAPACITY, "cache of capacity %d is full", kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    if (m->c.dtype == DG_BF16)
+        return ar_decode<bf16_t>(m, kv, batch, d_tokens, 1, d_logits, s, as_stream(stream));
+    return ar_decode<float>(m, kv, batch, d_tokens, 1, d_logits, s, as_stream(stream));
+}
+
+dg_status dg_argmax_rows(int32_t rows, int32_t vocab, const float* d_logits, int32_t* d_out,
+                         void* stream) {
+    if (rows < 0 || vocab < 1 || (rows > 0 && (!d_logits || !d_out)))
+        return fail(DG_ERR_ARG, "bad argmax arguments");
+    if ((uintptr_t)d_logits & 15) return fail(DG_ERR_ARG, "logits must be 16-byte aligned");
+    DG_HIP(dg::argmax_rows(d_logits, rows, vocab, d_out, 1, as_stream(stream)));
+    return DG_OK;
+}
+
+dg_status dg_ar_generate(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_first,
+                         int32_t n_new, int32_t* d_out, float* d_logits, void* d_ws,
+                         size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_first || !d_out || !d_logits || n_new < 0)
+        return fail(DG_ERR_ARG, "bad generate arguments");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + n_new > kv->cap)
+        return fail(DG_ERR_CAPACITY, "len %d + %d tokens exceeds capacity %d", kv->len, n_new,
+                    kv->cap);
+    if ((uintptr_t)d_logits & 15) return fail(DG_ERR_ARG, "logits must be 16-byte aligned");
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    const dg_config& c = m->c;
+    hipStream_t st = as_stream(stream);
+    // the head's slab maxima make the greedy choice a read of 16 KB + one
+    // slab per row (blocked bf16 models); otherwise one pass over the row
+    const bool slabs = m->blocked && m->embed_head && batch <= s.ut_rows && c.vocab % 64 == 0;
+    s.want_rowmax = slabs;
+    for (int t = 0; t < n_new; ++t) {
+        const int32_t* tok = t == 0 ? d_first : d_out + (t - 1);
+        const int ld = t == 0 ? 1 : n_new;
+        if (c.dtype == DG_BF16)
+            DG_TRY(ar_decode<bf16_t>(m, kv, batch, tok, ld, d_logits, s, st));
+        else
+            DG_TRY(ar_decode<float>(m, kv, batch, tok, ld, d_logits, s, st));
+        if (slabs)
+            DG_HIP(dg::argmax_slabs(d_logits, s.tmax, batch, c.vocab, d_out + t, n_new, st));
+        else
+            DG_HIP(dg::argmax_rows(d_logits, batch, c.vocab, d_out + t, n_new, st));
+    }
+    return DG_OK;
 }
 
 dg_status dg_denoise_step_topk(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,

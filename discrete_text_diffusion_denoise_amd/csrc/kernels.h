@@ -248,5 +248,14 @@ hipError_t selfcond_probs(const float* logits, const float* stats, uint16_t* out
                           const int32_t* halt, int tiled, hipStream_t st);
 hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,
                        hipStream_t st);
+// Greedy decoding: out[r * out_stride] = the index of row r's largest value,
+// ties to the lower index (NaNs never win; an all-NaN row gives 0).
+// logits [rows][V], 16-byte aligned.
+hipError_t argmax_rows(const float* logits, int rows, int V, int32_t* out, long out_stride,
+                       hipStream_t st);
+// The same from the head's 64-column slab maxima rowmax [rows][V / 64]
+// (V % 64 == 0), reading one slab of the logits per row.
+hipError_t argmax_slabs(const float* logits, const float* rowmax, int rows, int V, int32_t* out,
+                        long out_stride, hipStream_t st);
 
 }  // namespace dg

@@ -935,7 +935,121 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(uint64_t seed, int blo
     canvas[idx] = uniform_token(o[0], V);
 }
 
+// ------------------------------------------------------- greedy (AR mode)
+// Greedy decoding takes each row's largest logit, ties to the lower index.
+// A candidate (v, i) beats (bv, bi) when v > bv, or v == bv and i < bi; NaN
+// entries never win (a row of NaNs gives 0).
+
+__device__ __forceinline__ void amax_take(float v, int i, float& bv, int& bi) {
+    if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
+    }
+}
+
+// Block-wide (value, index) reduction of AM_THR threads; the result in
+// every thread.
+template <int NT>
+__device__ __forceinline__ void amax_block(float& bv, int& bi) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        amax_take(ov, oi, bv, bi);
+    }
+    __shared__ float wv[NT / 64];
+    __shared__ int wi[NT / 64];
+    if ((threadIdx.x & 63) == 0) {
+        wv[threadIdx.x >> 6] = bv;
+        wi[threadIdx.x >> 6] = bi;
+    }
+    __syncthreads();
+    bv = wv[0];
+    bi = wi[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) amax_take(wv[w], wi[w], bv, bi);
+}
+
+// One workgroup per row: four float4 loads in flight per thread.
+constexpr int AM_THR = 1024;
+__global__ __launch_bounds__(AM_THR) void argmax_rows_kernel(const float* __restrict__ x, int V,
+                                                             int32_t* __restrict__ out,
+                                                             long out_stride) {
+    const long row = blockIdx.x;
+    const float* r = x + row * (long)V;
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    if ((V & 3) == 0) {
+        const float4* r4 = reinterpret_cast<const float4*>(r);
+        const int n4 = V >> 2;
+        for (int j0 = threadIdx.x; j0 < n4; j0 += 4 * AM_THR) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * AM_THR;
+                v[u] = j < n4 ? r4[j] : make_float4(NAN, NAN, NAN, NAN);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * (j0 + u * AM_THR);
+                amax_take(v[u].x, i, bv, bi);
+                amax_take(v[u].y, i + 1, bv, bi);
+                amax_take(v[u].z, i + 2, bv, bi);
+                amax_take(v[u].w, i + 3, bv, bi);
+            }
+        }
+    } else {
+        for (int j = threadIdx.x; j < V; j += AM_THR) amax_take(r[j], j, bv, bi);
+    }
+    amax_block<AM_THR>(bv, bi);
+    if (threadIdx.x == 0) out[row * out_stride] = bi == 0x7FFFFFFF ? 0 : bi;
+}
+
+// From the head's 64-column slab maxima (V % 64 == 0): the first slab whose
+// maximum is the row's largest, then the first entry of that slab equal to
+// it.  Every earlier slab's maximum is smaller, so this is the first index
+// of the row's maximum.
+__global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ rowmax, int V,
+                                                           int32_t* __restrict__ out,
+                                                           long out_stride) {
+    const long row = blockIdx.x;
+    const int nslab = V >> 6;
+    const float* rm = rowmax + row * (long)nslab;
+    float bv = -INFINITY;
+    int bs = 0x7FFFFFFF;
+    for (int sl = threadIdx.x; sl < nslab; sl += 256) amax_take(rm[sl], sl, bv, bs);
+    amax_block<256>(bv, bs);
+    if (threadIdx.x < 64) {
+        int idx = 0;
+        if (bs != 0x7FFFFFFF) {
+            const float v = x[row * (long)V + (long)bs * 64 + threadIdx.x];
+            const uint64_t hit = __ballot(v == bv);
+            idx = bs * 64 + (hit ? __builtin_ctzll(hit) : 0);
+        }
+        if (threadIdx.x == 0) out[row * out_stride] = idx;
+    }
+}
+
 }  // namespace
+
+hipError_t argmax_rows(const float* logits, int rows, int V, int32_t* out, long out_stride,
+                       hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (V <= 0 || ((uintptr_t)logits & 15)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(argmax_rows_kernel, dim3(rows), dim3(AM_THR), 0, st, logits, V, out,
+                       out_stride);
+    return hipGetLastError();
+}
+
+hipError_t argmax_slabs(const float* logits, const float* rowmax, int rows, int V, int32_t* out,
+                        long out_stride, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (V <= 0 || V % 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(argmax_slabs_kernel, dim3(rows), dim3(256), 0, st, logits, rowmax, V, out,
+                       out_stride);
+    return hipGetLastError();
+}
 
 hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
     if (a.B <= 0 || a.N <= 0) return hipSuccess;

@@ -325,6 +325,37 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
                             int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
                             void* d_ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- retained AR mode */
+/* Report-summary page, section 7: the diffusion model keeps its
+ * autoregressive starting point's architecture, so the same weights run as an
+ * ordinary causal language model; section 5 describes that mode's step (one
+ * new token per step over the cached history).
+ *
+ * One decode step: d_tokens [batch] (ids in [0, vocab)) at position len of
+ * every sequence.  Every layer runs causal attention over the cache [0, len]
+ * (the token's K/V written to slot len) and its MoE; then the final norm and
+ * the tied head: d_logits [batch][vocab] fp32, 16-byte aligned.  len += 1.
+ * To continue a prompt of P tokens, encode its first P - 1 with
+ * dg_encode_prompt and decode the last one.  d_ws needs
+ * dg_workspace_bytes(batch).  Errors: DG_ERR_SHAPE if batch != the cache's,
+ * DG_ERR_CAPACITY if the cache is full (nothing launched). */
+dg_status dg_ar_decode_step(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_tokens,
+                            float* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+/* Greedy choice: d_out[r] = the index of row r's largest logit, ties to the
+ * lower index (NaN entries never win; an all-NaN row gives 0).
+ * d_logits [rows][vocab] fp32, 16-byte aligned. */
+dg_status dg_argmax_rows(int32_t rows, int32_t vocab, const float* d_logits, int32_t* d_out,
+                         void* stream);
+/* Greedy decoding of n_new tokens per sequence: step t decodes the previous
+ * token (d_first [batch] at t = 0, else d_out[b][t-1]) with
+ * dg_ar_decode_step and writes the greedy choice of its logits to
+ * d_out [batch][n_new] (row-major).  d_logits [batch][vocab] is scratch that
+ * holds the last step's logits on return.  len += n_new.  Errors as
+ * dg_ar_decode_step; DG_ERR_CAPACITY if len + n_new exceeds the capacity. */
+dg_status dg_ar_generate(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_first,
+                         int32_t n_new, int32_t* d_out, float* d_logits, void* d_ws,
+                         size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- stages */
 /* The step's stages, exposed so each can be driven and checked on its own.
  * T = number of tokens; h buffers are fp32 [T][d] residual streams. */

@@ -1,0 +1,210 @@
+"""Retained autoregressive mode on the GPU through the C ABI: the greedy
+choice bit-exact against numpy's argmax (ties to the lower index); decode
+steps after a prompt encode against the float64 oracle (logits and the KV
+cache, fp32 1e-4, bf16 2e-2; steps whose routing is within the GPU's
+precision of a tie are not compared); greedy generation bitwise equal to its
+own composition of decode steps and greedy choices; one decode step of the
+full-size layer (vocabulary 262144, prompt 2048) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from discrete_text_diffusion_denoise_amd import binding, synthetic
+from oracle import model as om
+
+from helpers import DEV, TOL_BF16, normwise, route_ambiguous, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+from test_gpu_model import MODELS, device_form, route_gap  # noqa: E402
+
+
+def setup(name, capacity, batch, std=0.05, seed=0, **over):
+    cfg = synthetic.model_config(MODELS[name], **over)
+    W = synthetic.make_weights(cfg, seed=seed, std=std, random_norms=True)
+    Wg, W = device_form(cfg, W)
+    m = binding.Model(cfg, Wg, batch=batch, capacity=capacity)
+    m.src_weights = Wg
+    return cfg, W, m
+
+
+# ------------------------------------------------------------------ greedy
+
+
+def argmax_case(kind, R, V, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, V), dtype=np.float32)
+    if kind == "ties":
+        # the maximum planted twice (and three times in the last row)
+        for r in range(R):
+            a, b = sorted(rng.choice(V, 2, replace=False))
+            x[r, a] = x[r, b] = 9.0
+        x[-1, V - 1] = 9.0
+    elif kind == "flat":
+        x[:] = 0.5
+        x[0, :] = -np.inf
+        x[1, :] = 0.0
+        x[1, ::2] = -0.0
+    elif kind == "edges":
+        x[0, 0] = 50.0
+        x[1, V - 1] = 50.0
+        x[2, 63] = x[2, 64] = 50.0
+    return x
+
+
+ARGMAX_CASES = [("normal", 4, 262144), ("ties", 5, 262144), ("flat", 3, 4096),
+                ("edges", 3, 1001), ("ties", 3, 4099), ("normal", 1, 1)]
+
+
+@pytest.mark.parametrize("kind,R,V", ARGMAX_CASES)
+def test_argmax_rows_bit_exact(kind, R, V):
+    print(f"argmax {kind} R={R} V={V}", flush=True)
+    x = argmax_case(kind, R, V, seed=R * 7 + V)
+    out = torch.full((R,), -1, dtype=torch.int32, device=DEV)
+    binding.argmax_rows(to_dev(x), out)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tolist() == np.argmax(x, axis=1).tolist()
+
+
+# ------------------------------------------------------------------ decode
+
+
+def oracle_decode_with_gaps(tokens, W, cfg, cache, gap):
+    """om.ar_decode_step, also returning per sequence whether any layer's
+    route of this token is ambiguous at `gap`."""
+    B = tokens.size
+    amb = np.zeros(B, dtype=bool)
+    # the route check on a copy of the cache, layer by layer, mirrors the
+    # step itself
+    c2 = cache.copy()
+    for b in range(B):
+        h = om.embed(tokens[b:b + 1], W)
+        for li, lw in enumerate(W["layers"]):
+            h, _, _ = om.attn_half(h, lw, cfg, c2.k[li][b][:, :c2.length],
+                                   c2.v[li][b][:, :c2.length], c2.length, causal=True)
+            u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
+            amb[b] |= bool(route_ambiguous(u @ np.asarray(lw["w_router"]).T, cfg["top_k"], gap)[0])
+            h, _, _, _ = om.moe_half(h, lw, cfg)
+    return om.ar_decode_step(tokens, W, cfg, cache), amb
+
+
+# bf16 models decode through one layer here: with more, a prompt token whose
+# route the GPU's rounding flips (a near-tie) changes its later layers' K/V,
+# which every decoded token then reads; the last layer's K/V never depend on
+# a route.  Deeper bf16 stacks are covered by generate == composition.
+@pytest.mark.parametrize("name,P,B,layers", [("tiny", 20, 2, 2), ("small_bf16", 150, 3, 1),
+                                             ("f32_gqa", 33, 3, 2), ("small_fp8", 150, 3, 1),
+                                             ("vocab_bf16", 64, 2, 1)])
+def test_ar_decode_steps_match_oracle(name, P, B, layers):
+    print(f"ar decode {name} P={P} B={B} layers={layers}", flush=True)
+    steps = 5
+    cfg, W, m = setup(name, P + steps, B, n_layers=layers)
+    W = synthetic.to_float64(W)
+    V = cfg["vocab"]
+    toks = synthetic.make_tokens(V, (B, P + steps - 1), seed=11)
+    m.encode_prompt(to_dev(toks[:, :P - 1]))
+    cache = om.KVCache(cfg, B)
+    om.encode(toks[:, :P - 1], W, cfg, cache)
+    gap = route_gap(cfg, chained=True)
+    logits = torch.empty((B, V), dtype=torch.float32, device=DEV)
+    checked = 0
+    for t in range(steps):
+        tok = toks[:, P - 1 + t].copy()
+        m.ar_decode_step(to_dev(tok), logits)
+        # a token whose route is within the GPU's precision of a tie is not
+        # compared (with one layer its route feeds no K/V)
+        ref, amb = oracle_decode_with_gaps(tok, W, cfg, cache, gap)
+        got = logits.cpu().numpy()
+        for b in np.flatnonzero(~amb):
+            err = normwise(got[b], ref[b])
+            assert err <= tol_for(cfg), f"step {t} seq {b}: {err:.3e}"
+            checked += 1
+    print(f"compared {checked} of {steps * B} decoded tokens", flush=True)
+    assert checked >= (steps * B) // 4
+    # the cache holds every decoded token's K/V
+    K, Vc = m.kv_tensors()
+    L = P - 1 + steps
+    for li in range(layers):
+        for b in range(B):
+            assert normwise(K[li, b, :, :L].float().cpu().numpy(), cache.k[li][b]) <= tol_for(cfg)
+            assert normwise(Vc[li, b, :, :L].float().cpu().numpy(), cache.v[li][b]) <= tol_for(cfg)
+
+
+def test_ar_decode_rejects_full_cache():
+    cfg, W, m = setup("tiny", 8, 1)
+    toks = synthetic.make_tokens(cfg["vocab"], (1, 8), seed=3)
+    m.encode_prompt(to_dev(toks))
+    logits = torch.empty((1, cfg["vocab"]), dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.DGError):
+        m.ar_decode_step(to_dev(toks[:, 0]), logits)
+    out = torch.empty((1, 1), dtype=torch.int32, device=DEV)
+    with pytest.raises(binding.DGError):
+        m.ar_generate(to_dev(toks[:, 0]), 1, out, logits)
+
+
+@pytest.mark.parametrize("name,P,B,n_new", [("tiny", 12, 2, 6), ("small_bf16", 100, 2, 5),
+                                            ("vocab_bf16", 40, 1, 4), ("small_fp8", 100, 1, 4)])
+def test_ar_generate_equals_composition(name, P, B, n_new):
+    print(f"ar generate {name} P={P} B={B} n={n_new}", flush=True)
+    cfg, W, m1 = setup(name, P + n_new, B)
+    m2 = binding.Model(cfg, m1.src_weights, batch=B, capacity=P + n_new)
+    V = cfg["vocab"]
+    prompt = to_dev(synthetic.make_tokens(V, (B, P), seed=5))
+    for m in (m1, m2):
+        m.encode_prompt(prompt[:, :P - 1].contiguous())
+    first = prompt[:, P - 1].contiguous()
+    out = torch.full((B, n_new), -1, dtype=torch.int32, device=DEV)
+    lg1 = torch.empty((B, V), dtype=torch.float32, device=DEV)
+    m1.ar_generate(first, n_new, out, lg1)
+    lg2 = torch.empty((B, V), dtype=torch.float32, device=DEV)
+    tok = first.clone()
+    ref = torch.empty((B, n_new), dtype=torch.int32, device=DEV)
+    for t in range(n_new):
+        m2.ar_decode_step(tok, lg2)
+        nxt = torch.empty((B,), dtype=torch.int32, device=DEV)
+        binding.argmax_rows(lg2, nxt)
+        ref[:, t] = nxt
+        tok = nxt
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(lg1, lg2)
+    K1, V1 = m1.kv_tensors()
+    K2, V2 = m2.kv_tensors()
+    assert torch.equal(K1[:, :, :, :P - 1 + n_new], K2[:, :, :, :P - 1 + n_new])
+    assert torch.equal(V1[:, :, :, :P - 1 + n_new], V2[:, :, :, :P - 1 + n_new])
+    # the greedy tokens of the last step's logits continue the sequence
+    assert out[:, -1].cpu().numpy().tolist() == np.argmax(lg1.cpu().numpy(), axis=1).tolist()
+
+
+# ------------------------------------------------------------------ full size
+
+
+def test_ar_decode_full_layer():
+    cfg = synthetic.model_config("layer")
+    P, V = synthetic.SHAPES["layer"]["prompt"], cfg["vocab"]
+    B = 4
+    print("generating full-size layer weights", flush=True)
+    W = synthetic.make_weights(cfg, seed=0)
+    toks = synthetic.make_tokens(V, (B, P + 1), seed=1)
+    m = binding.Model(cfg, W, batch=B, capacity=P + 2)
+    m.encode_prompt(to_dev(toks[:, :P]))
+    logits = torch.empty((B, V), dtype=torch.float32, device=DEV)
+    m.ar_decode_step(to_dev(toks[:, P].copy()), logits)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    del m
+    torch.cuda.empty_cache()
+    print("oracle encode + decode", flush=True)
+    lw = {k: np.asarray(v, dtype=np.float64) if k.endswith("norm") or k in ("wq", "wk", "wv", "wo")
+          else v for k, v in W["layers"][0].items()}
+    Wk = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"], "layers": [lw]}
+    cache = om.KVCache(cfg, B)
+    om.encode(toks[:, :P], Wk, cfg, cache)
+    ref, amb = oracle_decode_with_gaps(toks[:, P].copy(), Wk, cfg, cache,
+                                       route_gap(cfg, chained=True))
+    # a token whose route is within bf16 precision of a tie is not compared
+    assert (~amb).any()
+    for b in np.flatnonzero(~amb):
+        err = normwise(got[b], ref[b])
+        print(f"full-layer decode, sequence {b}: normwise error {err:.3e}", flush=True)
+        assert err <= TOL_BF16
