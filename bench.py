@@ -15,6 +15,9 @@ entropy stop never fires, so each block runs the full 48 rounds.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
                   [--config layer|layer_fp8|stack|batched] [--layers L] [--top-k K]
+  python bench.py --mode ar [--ar-tokens n] [--ar-batch B] [--config ...]
+      the retained autoregressive mode: value = decoded tokens/s (greedy
+      decoding of n tokens per sequence after the prompt, B sequences)
 """
 from __future__ import annotations
 
@@ -47,6 +50,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--top-k", type=int, default=0,
                     help="sampler top-k truncation (0: the full distribution)")
+    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar"],
+                    help="ar: the retained autoregressive mode (greedy decoding); one step "
+                         "= --ar-tokens tokens per sequence after the prompt")
+    ap.add_argument("--ar-tokens", type=int, default=64)
+    ap.add_argument("--ar-batch", type=int, default=1)
     return ap.parse_args()
 
 
@@ -89,7 +97,8 @@ def device_weights(cfg, seed, torch):
 
 def kernel_work(name, cfg, B, P, sc_splits):
     """Algorithmic (flops, bytes) of one launch of a timed kernel: every
-    weight read once, activations read/written once."""
+    weight read once, activations read/written once.  cfg["canvas"] is the
+    number of new tokens per sequence (1 in the autoregressive mode)."""
     es = 2 if cfg["dtype"] == "bf16" else 4
     # expert weight bytes per element (8-bit experts also read one fp32
     # scale per weight row)
@@ -224,12 +233,142 @@ def cpu_baseline(cfg, W, prompt, canvas, params, torch):
             "commit_s": round(t3 - t2, 3)}
 
 
+def cpu_baseline_ar(cfg, W, prompt, B):
+    """The CPU oracle's autoregressive decode step (float64 numpy), timed on
+    this host: the prompt encode is not timed, then one decode step of the B
+    sequences; tokens/s = B / step time (the oracle runs the sequences one
+    after another, so one sequence gives the rate of any batch)."""
+    import numpy as np
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    host = {"embed": W["embed"].float().cpu().numpy(), "w_sc": W["w_sc"].float().cpu().numpy(),
+            "final_norm": W["final_norm"].cpu().numpy().astype(np.float64), "layers": []}
+    for lw in W["layers"]:
+        host["layers"].append({k: v.float().cpu().numpy() for k, v in lw.items()
+                               if not k.startswith("s_")})
+    P = prompt.shape[1]
+    cache = om.KVCache(cfg, B)
+    om.encode(prompt[:, :P - 1], host, cfg, cache)
+    t0 = time.perf_counter()
+    om.ar_decode_step(prompt[:, P - 1], host, cfg, cache)
+    t1 = time.perf_counter()
+    return {"value": round(B / (t1 - t0), 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one decode step of {B} sequence(s) after a {P - 1}-token prompt "
+                       f"({(t1 - t0):.2f} s, float64 numpy, {threads} BLAS threads)")}
+
+
+def bench_ar(args):
+    """The retained autoregressive mode: one step = greedy decoding of
+    --ar-tokens tokens for each of --ar-batch sequences after the prompt
+    (dg_ar_generate); the cache is rewound to the prompt after each step."""
+    import numpy as np
+    import torch
+
+    from discrete_text_diffusion_denoise_amd import binding, synthetic
+
+    shape = synthetic.SHAPES[args.config]
+    over = {"n_layers": args.layers} if args.layers else {}
+    cfg = synthetic.model_config(args.config, **over)
+    if cfg.get("expert_dtype") == "fp8":
+        raise SystemExit("--mode ar runs the bf16 configurations")
+    B, P, V, n_new = args.ar_batch, shape["prompt"], cfg["vocab"], args.ar_tokens
+    torch.cuda.init()
+    W = device_weights(cfg, args.seed, torch)
+    m = binding.Model(cfg, W, batch=B, capacity=P + n_new)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
+    m.encode_prompt(prompt[:, :P - 1].contiguous())
+    first = prompt[:, P - 1].contiguous()
+    out = torch.empty((B, n_new), dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
+    names = list(binding.TIMERS)
+    binding.timer_enable(names)
+    for _ in range(args.warmup):
+        m.ar_generate(first, n_new, out, logits)
+        m.set_kv_length(P - 1)
+    torch.cuda.synchronize()
+    warm = {n: binding.timer_read(n) for n in names}
+    binding.timer_enable([])
+    dominant = max(names, key=lambda n: warm[n][0]) if args.warmup else "head_gemm"
+    binding.timer_enable([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.ar_generate(first, n_new, out, logits)
+        m.set_kv_length(P - 1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms, dom_n = binding.timer_read(dominant)
+    binding.timer_enable(names)
+    m.ar_generate(first, n_new, out, logits)
+    m.set_kv_length(P - 1)
+    torch.cuda.synchronize()
+    kern = {}
+    for n in names:
+        ms, cnt = binding.timer_read(n)
+        kern[n] = {"total_ms": round(ms, 3), "launches": cnt,
+                   "avg_ms": round(ms / cnt, 5) if cnt else None}
+    binding.timer_enable([])
+    # one new token per sequence per launch; attention over the mean context
+    acfg = dict(cfg, canvas=1)
+    P_mean = P - 1 + n_new // 2
+    roof = roofline(dominant, dom_ms / dom_n, acfg, B, P_mean, 1)
+    roof["timed_launches"] = dom_n
+    roof["traffic"], roof["traffic_source"] = None, None
+    per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], acfg, B,
+                                                                  P_mean, 1).items()
+                                       if k in ("bound", "achieved", "unit", "frac")}
+                                      if kern[n]["launches"] and n != "sampler" else {}))
+                  for n in names}
+    value = B * n_new * args.steps / wall
+    out_json = {
+        "metric": "AR decode tokens/s at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "ms_per_token": round(wall / (args.steps * n_new) * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt tokens)",
+        "config": {"workload": (f"ar-{args.config}: {cfg['n_layers']} layer(s) d{cfg['d_model']} "
+                                f"{cfg['n_heads']}q/{cfg['n_kv_heads']}kv x{cfg['head_dim']}, "
+                                f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}, "
+                                f"vocab {V}; greedy decoding of {n_new} tokens per sequence after "
+                                f"a {P}-token prompt, batch {B}"),
+                   "global_batch": B, "seq_len": P + n_new, "parallelism": "none (1 GPU)"},
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+    oracle_fits = cfg["n_layers"] == 1 and P <= 4096
+    if args.no_cpu_baseline or not oracle_fits:
+        out_json["cpu_baseline"] = None
+    else:
+        # the oracle decodes sequences one by one: one sequence is the sample
+        out_json["cpu_baseline"] = cpu_baseline_ar(cfg, W, prompt[:1].cpu().numpy().astype(np.int64),
+                                                   1)
+    print(json.dumps(out_json), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the kernels run on one GPU's share at full shape).", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "ar":
+        bench_ar(args)
+        return
     import numpy as np
     import torch
 

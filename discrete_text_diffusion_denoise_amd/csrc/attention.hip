@@ -286,6 +286,13 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
     if (!causal && kv_len > 256) {
         splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(target, (int)base)));
         splits = std::min(splits, std::min(32, std::max(1, max_splits)));
+    } else if (causal && n <= 16 && kv_len > 2 * KT) {
+        // a decode step: a handful of queries over a long cache, so the
+        // keys split into ranges of at least two tiles; a query's keys past
+        // its position are masked in every range, and a range with no
+        // visible key merges with weight 0
+        splits = (int)std::min<long>(cdiv(kv_len, 2 * KT), std::max<long>(1, cdiv(target, (int)base)));
+        splits = std::min(splits, std::min(32, std::max(1, max_splits)));
     }
     int len = cdiv(cdiv(kv_len, splits), KT) * KT;
     if (len <= 0) len = KT;

@@ -408,7 +408,9 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     a.kv_len = pos0 + n;
     a.causal = causal;
     a.halt = s.halt;
-    const int max_splits = std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
+    // the split merge handles heads of 64 or more dimensions
+    const int max_splits =
+        dh < 64 ? 1 : std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len);
     DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
