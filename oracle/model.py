@@ -326,6 +326,40 @@ def ar_generate(first: np.ndarray, n_new: int, W: dict, cfg: dict, cache: KVCach
     return out
 
 
+# ---------------------------------------------------------------- training forward
+# Report-summary page, section 1: training replaces a random share of a
+# sentence's tokens (from none to all) by junk and asks the model for the
+# originals; section 3: the supervised stage does this at varying degrees
+# and learns from the gap between prediction and original.  Plainest
+# reading: multinomial corruption at a per-canvas rate (sampler.c,
+# ora_corrupt), one denoiser forward of the corrupted canvas over the cached
+# context with no self-conditioning input (there is no previous round), and
+# the cross-entropy of each position's prediction at its clean token.
+
+def xent_rows(logits: np.ndarray, target: np.ndarray) -> np.ndarray:
+    """-log softmax(l)[x] per row of float64 logits [..., V] (the textbook
+    log-sum-exp), target [...] int."""
+    lg = np.asarray(logits, dtype=np.float64)
+    m = lg.max(axis=-1, keepdims=True)
+    lse = m[..., 0] + np.log(np.exp(lg - m).sum(axis=-1))
+    lt = np.take_along_axis(lg, np.asarray(target)[..., None].astype(np.int64), axis=-1)[..., 0]
+    return lse - lt
+
+
+def train_forward(clean: np.ndarray, rate: np.ndarray, seed: int, step: int, W: dict, cfg: dict,
+                  cache: KVCache):
+    """Training-side forward of canvases clean [B, N] at corruption rates
+    rate [B] over the cached context (not modified).  Returns (corrupted
+    canvas int32 [B, N], float64 logits [B, N, V], float64 losses [B, N],
+    their mean)."""
+    from oracle import sampler as osampler
+    clean = np.asarray(clean, dtype=np.int32)
+    x = osampler.corrupt(seed, step, W["embed"].shape[0], np.asarray(rate, np.float32), clean)
+    logits = denoise_step(x, W, cfg, cache)
+    loss = xent_rows(logits, clean)
+    return x, logits, loss, float(loss.mean())
+
+
 def denoise_step(canvas: np.ndarray, W: dict, cfg: dict, cache: KVCache,
                  prev_logits: np.ndarray | None = None, top_k: int = 0) -> np.ndarray:
     """One denoiser forward over canvases [B, N] with bidirectional attention

@@ -332,6 +332,53 @@ void ora_canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* can
         }
 }
 
+/* ------------------------------------------------------------------ */
+/* Training-side forward (report-summary page, section 1: training     */
+/* replaces a random share of a sentence's tokens, from 0 % to 100 %,  */
+/* by junk and asks for the original; section 3: the supervised stage  */
+/* does this at varying degrees and trains on the gap between the       */
+/* prediction and the original).  Plainest reading, written out:        */
+/*   corruption: position (b, i) of canvas b with rate r_b draws the    */
+/*     Philox block of counter (step, b, i, 2), key (seed, 0); it is    */
+/*     replaced iff uniform(word 0) < r_b, by uniform_token(word 1, V)  */
+/*     (the multinomial kind of section 1: any token, possibly the      */
+/*     original one);                                                   */
+/*   loss of a position: the cross-entropy of softmax(l) at the clean  */
+/*     token x, -ln p(x) = ln S - (l[x] - m), with m and S the row's    */
+/*     max and sum of E(l - m) as the sampler defines them, so         */
+/*     loss = L(S) - (l[x] - m) in binary32 (both steps as written);    */
+/*   mean loss: the sequential binary32 sum over positions in order,    */
+/*     divided by their count (converted to binary32).                  */
+/* ------------------------------------------------------------------ */
+
+void ora_corrupt(uint64_t seed, int step, int B, int N, int V, const float* rate,
+                 const int32_t* clean, int32_t* out)
+{
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < N; ++i) {
+            uint64_t o[4];
+            draw_block(seed, (uint64_t)step, (uint64_t)b, (uint64_t)i, 2, o);
+            size_t bi = (size_t)b * N + i;
+            out[bi] = ora_uniform(o[0]) < rate[b] ? ora_uniform_token(o[1], V) : clean[bi];
+        }
+}
+
+/* Cross-entropy of each row [rows][V] at target[r]; returns the mean. */
+float ora_xent(const float* logits, int rows, int V, const int32_t* target, float* loss)
+{
+    chunk_t* chunks = (chunk_t*)malloc(sizeof(chunk_t) * n_tiles(V) * NLANE);
+    float sum = 0.0f;
+    for (int r = 0; r < rows; ++r) {
+        const float* row = logits + (size_t)r * V;
+        chunk_t st = row_stats(row, V, 1.0f, chunks);
+        float z = row[target[r]] - st.m;
+        loss[r] = ora_log(st.s) - z;
+        sum = sum + loss[r];
+    }
+    free(chunks);
+    return sum / (float)rows;
+}
+
 /* Lock set of one canvas from per-position entropy H and max-probability P.
  * rule 0 (max-probability): lock i  <=>  P[i] > theta.
  * rule 1 (cumulative entropy, report-summary page section 4): visit positions

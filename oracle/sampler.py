@@ -71,6 +71,11 @@ def lib():
                                              ctypes.c_int, u64, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                              P, P, P]
+        L.ora_corrupt.restype = None
+        L.ora_corrupt.argtypes = [u64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  P, P, P]
+        L.ora_xent.restype = f32
+        L.ora_xent.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
         _lib = L
     return _lib
 
@@ -127,6 +132,30 @@ def canvas_init(seed: int, block: int, B: int, N: int, V: int) -> np.ndarray:
     out = np.zeros((B, N), dtype=np.int32)
     lib().ora_canvas_init(int(seed), int(block), int(B), int(N), int(V), _ptr(out))
     return out
+
+
+def corrupt(seed: int, step: int, V: int, rate: np.ndarray, clean: np.ndarray) -> np.ndarray:
+    """Multinomial corruption of clean [B, N] int32 at per-canvas rates [B]
+    (float32) over a vocabulary of V: the training-side forward's input, as
+    sampler.c defines it."""
+    clean = np.ascontiguousarray(clean, dtype=np.int32)
+    rate = np.ascontiguousarray(rate, dtype=np.float32)
+    B, N = clean.shape
+    out = np.zeros_like(clean)
+    lib().ora_corrupt(int(seed), int(step), B, N, int(V), _ptr(rate), _ptr(clean), _ptr(out))
+    return out
+
+
+def xent(logits: np.ndarray, target: np.ndarray):
+    """Cross-entropy of float32 logit rows [R, V] at target [R]:
+    (per-row losses float32 [R], mean float32)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    R, V = lg.shape
+    t = np.ascontiguousarray(target, dtype=np.int32).reshape(-1)
+    assert t.size == R and (t >= 0).all() and (t < V).all()
+    loss = np.zeros(R, dtype=np.float32)
+    mean = np.float32(lib().ora_xent(_ptr(lg), R, V, _ptr(t), _ptr(loss)))
+    return loss, mean
 
 
 def topk_row(row: np.ndarray, K: int, inv_t: float, u: float):
