@@ -89,6 +89,10 @@ _SIGS = {
     "dg_ar_decode_step": (_I, [_P, _P, _I, _P, _P, _P, _SZ, _P]),
     "dg_argmax_rows": (_I, [_I, _I, _P, _P, _P]),
     "dg_ar_generate": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    "dg_corrupt": (_I, [ctypes.c_uint64, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "dg_xent": (_I, [_I, _I, _P, _P, _P, _P, _P]),
+    "dg_train_forward": (_I, [_P, _P, _I, _P, _P, ctypes.c_uint64, _I, _P, _P, _P, _P, _P, _SZ,
+                              _P]),
     "dg_generate_workspace_bytes": (_I, [_P, _I, _P]),
     "dg_generate_block": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "dg_stage_input": (_I, [_P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -299,6 +303,16 @@ class Model:
                                     _ptr(out), _ptr(logits), _ptr(self.ws), self.ws.numel(),
                                     _stream(stream)))
 
+    def train_forward(self, clean, rate, seed: int, step: int, corrupted, logits, loss,
+                      mean=None, stream=None):
+        """dg_train_forward: clean [B, N] int32, rate [B] f32 -> corrupted [B, N],
+        logits [B, N, V], loss [B, N] f32, mean [1] f32 (optional)."""
+        _check(lib().dg_train_forward(self.handle, self.kv, clean.shape[0], _ptr(clean),
+                                      _ptr(rate), int(seed), int(step), _ptr(corrupted),
+                                      _ptr(logits), _ptr(loss),
+                                      _ptr(mean) if mean is not None else None,
+                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))
+
     def commit_block(self, block, stream=None):
         _check(lib().dg_commit_block(self.handle, self.kv, block.shape[0], _ptr(block),
                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))
@@ -366,6 +380,20 @@ def sample_update_probs(params: dict, step: int, logits, canvas, argmax, lock, s
                                         _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats),
                                         _ptr(stop), _ptr(rowmax), 1 if blocked else 0, _ptr(probs),
                                         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def corrupt(seed: int, step: int, vocab: int, rate, clean, out, stream=None):
+    """dg_corrupt: clean [B, N] int32, rate [B] f32 -> out [B, N] int32."""
+    B, N = clean.shape
+    _check(lib().dg_corrupt(int(seed), int(step), B, N, int(vocab), _ptr(rate), _ptr(clean),
+                            _ptr(out), _stream(stream)))
+
+
+def xent(logits, target, loss, mean=None, stream=None):
+    """dg_xent: logits [R, V] f32, target [R] int32 -> loss [R] f32, mean [1] f32."""
+    R, V = logits.shape
+    _check(lib().dg_xent(R, V, _ptr(logits), _ptr(target), _ptr(loss),
+                         _ptr(mean) if mean is not None else None, _stream(stream)))
 
 
 def argmax_rows(logits, out, stream=None):

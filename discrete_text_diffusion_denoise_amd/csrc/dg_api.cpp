@@ -912,6 +912,65 @@ dg_status dg_ar_generate(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d
     return DG_OK;
 }
 
+dg_status dg_corrupt(uint64_t seed, int32_t step, int32_t batch, int32_t canvas, int32_t vocab,
+                     const float* d_rate, const int32_t* d_clean, int32_t* d_out, void* stream) {
+    if (batch < 0 || canvas < 0 || vocab < 1 ||
+        ((long)batch * canvas > 0 && (!d_rate || !d_clean || !d_out)))
+        return fail(DG_ERR_ARG, "bad corruption arguments");
+    DG_HIP(dg::corrupt(seed, step, batch, canvas, vocab, d_rate, d_clean, d_out,
+                       as_stream(stream)));
+    return DG_OK;
+}
+
+static dg_status xent_impl(int32_t rows, int32_t vocab, const float* d_logits,
+                           const int32_t* d_target, float* d_loss, float* d_mean,
+                           hipStream_t st) {
+    dg::SampleArgs a;
+    a.B = 1;
+    a.N = rows;
+    a.V = vocab;
+    a.inv_t = 1.0f;
+    a.logits = d_logits;
+    a.stats_only = 1;
+    a.target = d_target;
+    a.loss = d_loss;
+    DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
+    if (d_mean) DG_HIP(dg::mean_seq(d_loss, rows, d_mean, st));
+    return DG_OK;
+}
+
+dg_status dg_xent(int32_t rows, int32_t vocab, const float* d_logits, const int32_t* d_target,
+                  float* d_loss, float* d_mean, void* stream) {
+    if (rows < 1 || vocab < 1 || !d_logits || !d_target || !d_loss)
+        return fail(DG_ERR_ARG, "bad cross-entropy arguments");
+    if (vocab > (1 << 19)) return fail(DG_ERR_ARG, "vocab %d above 2^19", vocab);
+    return xent_impl(rows, vocab, d_logits, d_target, d_loss, d_mean, as_stream(stream));
+}
+
+dg_status dg_train_forward(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_clean,
+                           const float* d_rate, uint64_t seed, int32_t step, int32_t* d_corrupted,
+                           float* d_logits, float* d_loss, float* d_mean, void* d_ws,
+                           size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!kv || !d_clean || !d_rate || !d_corrupted || !d_logits || !d_loss)
+        return fail(DG_ERR_ARG, "NULL argument");
+    if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
+    if (kv->len + m->c.canvas > kv->cap)
+        return fail(DG_ERR_CAPACITY, "cache needs len %d + canvas %d <= capacity %d", kv->len,
+                    m->c.canvas, kv->cap);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    const dg_config& c = m->c;
+    hipStream_t st = as_stream(stream);
+    DG_HIP(dg::corrupt(seed, step, batch, c.canvas, c.vocab, d_rate, d_clean, d_corrupted, st));
+    if (c.dtype == DG_BF16)
+        DG_TRY(denoise<bf16_t>(m, kv, batch, d_corrupted, nullptr, nullptr, d_logits, s, st));
+    else
+        DG_TRY(denoise<float>(m, kv, batch, d_corrupted, nullptr, nullptr, d_logits, s, st));
+    return xent_impl(batch * c.canvas, c.vocab, d_logits, d_clean, d_loss, d_mean, st);
+}
+
 dg_status dg_denoise_step_topk(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_canvas,
                                const float* d_prev_logits, const float* d_prev_stats,
                                int32_t top_k, float* d_logits, void* d_ws, size_t ws_bytes,

@@ -230,6 +230,13 @@ struct SampleArgs {
     int32_t* tk_idx = nullptr;
     float* tk_p = nullptr;
     int list_only = 0;
+    // statistics only (the full distribution at T = 1): per row the
+    // optional stats and newmax, and, when loss is set, the cross-entropy at
+    // target[row]: L(S) - (l[target] - m), NaN for a target outside [0, V);
+    // no draw, no canvas update, stop may be null
+    int stats_only = 0;
+    const int32_t* target = nullptr;
+    float* loss = nullptr;
 };
 constexpr int kTopKMax = 64;
 hipError_t sample_update(const SampleArgs& a, hipStream_t st);
@@ -248,6 +255,13 @@ hipError_t selfcond_probs(const float* logits, const float* stats, uint16_t* out
                           const int32_t* halt, int tiled, hipStream_t st);
 hipError_t canvas_init(uint64_t seed, int block, int B, int N, int V, int32_t* canvas,
                        hipStream_t st);
+// Multinomial corruption of the training-side forward: position (b, i)
+// draws Philox counter (step, b, i, 2), key (seed, 0); it takes
+// uniform_token(word 1, V) when uniform(word 0) < rate[b], else clean[b][i].
+hipError_t corrupt(uint64_t seed, int step, int B, int N, int V, const float* rate,
+                   const int32_t* clean, int32_t* out, hipStream_t st);
+// mean = (sequential binary32 sum of loss[0 .. rows)) / rows, one thread
+hipError_t mean_seq(const float* loss, int rows, float* mean, hipStream_t st);
 // Greedy decoding: out[r * out_stride] = the index of row r's largest value,
 // ties to the lower index (NaNs never win; an all-NaN row gives 0).
 // logits [rows][V], 16-byte aligned.

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
 
     const long rowid = blockIdx.x;        // b*N + i
     const int b = (int)(rowid / a.N), i = (int)(rowid % a.N);
-    if (a.stop[b]) return;
+    if (a.stop && a.stop[b]) return;
     const float* row = a.logits + rowid * (long)a.V;
     const __amdgpu_buffer_rsrc_t lrs = buf_rsrc(row, 4u * (uint32_t)a.V);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -462,6 +462,26 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
     }
     __syncthreads();
     const Rec R = rowrec;
+
+    if (a.stats_only) {
+        if (tid == 0) {
+            if (a.stats) {
+                float H = dlog(R.s) - R.a / R.s;
+                H = H > 0.0f ? H : 0.0f;
+                float* st = a.stats + rowid * 4;
+                st[0] = R.m;
+                st[1] = R.s;
+                st[2] = H;
+                st[3] = 1.0f / R.s;
+            }
+            if (a.newmax) a.newmax[rowid] = R.j;
+            if (a.loss) {
+                const int x = a.target[rowid];
+                a.loss[rowid] = (x >= 0 && x < a.V) ? dlog(R.s) - (row[x] - R.m) : NAN;
+            }
+        }
+        return;
+    }
 
     // chunk weights at temperature T, relative to the row max
     for (int c = tid; c < nt * NLANE; c += NTHR) {
@@ -935,6 +955,34 @@ __global__ __launch_bounds__(256) void canvas_init_kernel(uint64_t seed, int blo
     canvas[idx] = uniform_token(o[0], V);
 }
 
+// ------------------------------------------------- training-side forward
+// Report-summary page, sections 1 and 3: training replaces a random share
+// of a text's tokens (0 to 100 %) and scores the prediction at the
+// originals.  Position (b, i) is replaced when the uniform of Philox word 0
+// (counter (step, b, i, 2)) is below its canvas's rate, by the uniform
+// token of word 1.
+__global__ __launch_bounds__(256) void corrupt_kernel(uint64_t seed, int step, int N, int V,
+                                                      const float* __restrict__ rate,
+                                                      const int32_t* __restrict__ clean,
+                                                      int32_t* __restrict__ out, long total) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int b = (int)(idx / N), i = (int)(idx % N);
+    uint64_t o[4];
+    philox((uint64_t)step, (uint64_t)b, (uint64_t)i, 2ull, seed, 0ull, o);
+    out[idx] = uniform01(o[0]) < rate[b] ? uniform_token(o[1], V) : clean[idx];
+}
+
+// The mean loss: one lane adds the rows in order (the definition is a
+// sequential binary32 sum), the other lanes prefetch nothing; rows are few.
+__global__ __launch_bounds__(64) void mean_seq_kernel(const float* __restrict__ loss, int rows,
+                                                      float* __restrict__ mean) {
+    if (threadIdx.x != 0) return;
+    float acc = 0.0f;
+    for (int r = 0; r < rows; ++r) acc = acc + loss[r];
+    mean[0] = acc / (float)rows;
+}
+
 // ------------------------------------------------------- greedy (AR mode)
 // Greedy decoding takes each row's largest logit, ties to the lower index.
 // A candidate (v, i) beats (bv, bi) when v > bv, or v == bv and i < bi; NaN
@@ -1033,6 +1081,21 @@ __global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restri
 
 }  // namespace
 
+hipError_t corrupt(uint64_t seed, int step, int B, int N, int V, const float* rate,
+                   const int32_t* clean, int32_t* out, hipStream_t st) {
+    const long total = (long)B * N;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(corrupt_kernel, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, st,
+                       seed, step, N, V, rate, clean, out, total);
+    return hipGetLastError();
+}
+
+hipError_t mean_seq(const float* loss, int rows, float* mean, hipStream_t st) {
+    if (rows <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mean_seq_kernel, dim3(1), dim3(64), 0, st, loss, rows, mean);
+    return hipGetLastError();
+}
+
 hipError_t argmax_rows(const float* logits, int rows, int V, int32_t* out, long out_stride,
                        hipStream_t st) {
     if (rows <= 0) return hipSuccess;
@@ -1053,6 +1116,7 @@ hipError_t argmax_slabs(const float* logits, const float* rowmax, int rows, int 
 
 hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
     if (a.B <= 0 || a.N <= 0) return hipSuccess;
+    if (a.stats_only && (a.top_k || a.probs || (a.loss && !a.target))) return hipErrorInvalidValue;
     if (a.top_k > 0) {
         const int nslab = cdiv(a.V, 64);
         if (a.top_k > kTopKMax || a.top_k > a.V || (a.rowmax && a.rowmax_n != nslab) ||
@@ -1097,7 +1161,7 @@ hipError_t sample_update(const SampleArgs& a, hipStream_t st) {
     else
         hipLaunchKernelGGL((sample_row_kernel<false, false>), dim3(a.B * a.N), dim3(NTHR), lds, st, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.stats_only) return e;
     hipLaunchKernelGGL(sample_canvas_kernel, dim3(a.B), dim3(1024), 0, st, a);
     return hipGetLastError();
 }

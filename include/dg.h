@@ -356,6 +356,40 @@ dg_status dg_ar_generate(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d
                          int32_t n_new, int32_t* d_out, float* d_logits, void* d_ws,
                          size_t ws_bytes, void* stream);
 
+/* -------------------------------------------------- training-side forward */
+/* Report-summary page, section 1: training replaces a random share of a
+ * text's tokens (from none to all) by junk and asks for the originals;
+ * section 3: the supervised stage does this at varying degrees and learns
+ * from the gap between prediction and original.  The forward pass only (no
+ * gradients).
+ *
+ * Multinomial corruption: d_out[b][i] = uniform_token(word 1, vocab) if
+ * uniform(word 0) < d_rate[b], else d_clean[b][i], with the Philox4x64-10
+ * block of counter (step, b, i, 2), key (seed, 0) (the sampler's uniform and
+ * uniform_token).  d_rate [batch] fp32 in [0, 1]; d_clean, d_out
+ * [batch][canvas] int32 (may not alias). */
+dg_status dg_corrupt(uint64_t seed, int32_t step, int32_t batch, int32_t canvas, int32_t vocab,
+                     const float* d_rate, const int32_t* d_clean, int32_t* d_out, void* stream);
+/* Cross-entropy of each row of d_logits [rows][vocab] fp32 at d_target[row]:
+ * d_loss[row] = L(S) - (l[target] - m), m and S the row's max and sum of
+ * E(l - m) as the sampler computes them (binary32, bit-exact with its
+ * statistics); NaN for a target outside [0, vocab).  d_mean (optional, one
+ * float) = the sequential binary32 sum of the losses in row order / rows.
+ * vocab <= 2^19. */
+dg_status dg_xent(int32_t rows, int32_t vocab, const float* d_logits, const int32_t* d_target,
+                  float* d_loss, float* d_mean, void* stream);
+/* Training-side forward of the canvases d_clean [batch][N] over the cached
+ * context (which is not modified): dg_corrupt into d_corrupted [batch][N],
+ * one denoiser forward of the corrupted canvases with no self-conditioning
+ * input (d_logits [batch][N][vocab] fp32), and dg_xent at the clean tokens
+ * (d_loss [batch][N], d_mean optional).  d_ws needs dg_workspace_bytes(batch).
+ * Errors: DG_ERR_SHAPE if batch != the cache's; DG_ERR_CAPACITY if
+ * len + N exceeds the capacity (nothing launched). */
+dg_status dg_train_forward(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* d_clean,
+                           const float* d_rate, uint64_t seed, int32_t step, int32_t* d_corrupted,
+                           float* d_logits, float* d_loss, float* d_mean, void* d_ws,
+                           size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- stages */
 /* The step's stages, exposed so each can be driven and checked on its own.
  * T = number of tokens; h buffers are fp32 [T][d] residual streams. */
