@@ -15,6 +15,9 @@ entropy stop never fires, so each block runs the full 48 rounds.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
                   [--config layer|layer_fp8|stack|batched] [--layers L] [--top-k K]
+  python bench.py --mode train [--rate r] [--config ...]
+      the training-side forward: value = canvas tokens/s through corruption,
+      the denoiser forward and the cross-entropy at the clean tokens
   python bench.py --mode ar [--ar-tokens n] [--ar-batch B] [--config ...]
       the retained autoregressive mode: value = decoded tokens/s (greedy
       decoding of n tokens per sequence after the prompt, B sequences)
@@ -50,9 +53,13 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--top-k", type=int, default=0,
                     help="sampler top-k truncation (0: the full distribution)")
-    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar"],
+    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar", "train"],
                     help="ar: the retained autoregressive mode (greedy decoding); one step "
-                         "= --ar-tokens tokens per sequence after the prompt")
+                         "= --ar-tokens tokens per sequence after the prompt.  train: the "
+                         "training-side forward; one step = corruption + denoiser forward + "
+                         "cross-entropy of every canvas")
+    ap.add_argument("--rate", type=float, default=0.5,
+                    help="train: corruption rate of every canvas")
     ap.add_argument("--ar-tokens", type=int, default=64)
     ap.add_argument("--ar-batch", type=int, default=1)
     return ap.parse_args()
@@ -360,6 +367,125 @@ def bench_ar(args):
     print(json.dumps(out_json), flush=True)
 
 
+def cpu_baseline_train(cfg, W, prompt, clean, rate, seed):
+    """The CPU oracle's training-side forward (float64 numpy model, C
+    corruption), timed on this host after an untimed prompt encode."""
+    import numpy as np
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    host = {"embed": W["embed"].float().cpu().numpy(), "w_sc": W["w_sc"].float().cpu().numpy(),
+            "final_norm": W["final_norm"].cpu().numpy().astype(np.float64), "layers": []}
+    for lw in W["layers"]:
+        host["layers"].append({k: v.float().cpu().numpy() for k, v in lw.items()
+                               if not k.startswith("s_")})
+    B, N = clean.shape
+    cache = om.KVCache(cfg, B)
+    om.encode(prompt, host, cfg, cache)
+    t0 = time.perf_counter()
+    om.train_forward(clean, rate, seed, 0, host, cfg, cache)
+    t1 = time.perf_counter()
+    return {"value": round(B * N / (t1 - t0), 4), "unit": "canvas tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"one training-side forward of {B}x{N} canvas tokens after a "
+                       f"{prompt.shape[1]}-token prompt ({(t1 - t0):.2f} s, float64 numpy, "
+                       f"{threads} BLAS threads)")}
+
+
+def bench_train(args):
+    """The training-side forward: one step = dg_train_forward of every canvas
+    of the batch at corruption rate --rate over the encoded prompt."""
+    import numpy as np
+    import torch
+
+    from discrete_text_diffusion_denoise_amd import binding, synthetic
+
+    shape = synthetic.SHAPES[args.config]
+    over = {"n_layers": args.layers} if args.layers else {}
+    cfg = synthetic.model_config(args.config, **over)
+    B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
+    torch.cuda.init()
+    W = device_weights(cfg, args.seed, torch)
+    m = binding.Model(cfg, W, batch=B, capacity=P + N)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
+    clean = torch.randint(0, V, (B, N), generator=g, device="cuda", dtype=torch.int32)
+    rate = torch.full((B,), float(args.rate), dtype=torch.float32, device="cuda")
+    m.encode_prompt(prompt)
+    x = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, N, V), dtype=torch.float32, device="cuda")
+    loss = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    names = list(binding.TIMERS)
+    binding.timer_enable(names)
+    for w in range(args.warmup):
+        m.train_forward(clean, rate, args.seed, w, x, logits, loss, mean)
+    torch.cuda.synchronize()
+    warm = {n: binding.timer_read(n) for n in names}
+    binding.timer_enable([])
+    dominant = max(names, key=lambda n: warm[n][0]) if args.warmup else "head_gemm"
+    binding.timer_enable([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        m.train_forward(clean, rate, args.seed, args.warmup + s_, x, logits, loss, mean)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms, dom_n = binding.timer_read(dominant)
+    binding.timer_enable(names)
+    m.train_forward(clean, rate, args.seed, 0, x, logits, loss, mean)
+    torch.cuda.synchronize()
+    kern = {}
+    for n in names:
+        ms, cnt = binding.timer_read(n)
+        kern[n] = {"total_ms": round(ms, 3), "launches": cnt,
+                   "avg_ms": round(ms / cnt, 5) if cnt else None}
+    binding.timer_enable([])
+    roof = roofline(dominant, dom_ms / dom_n, cfg, B, P, 1)
+    roof["timed_launches"] = dom_n
+    roof["traffic"], roof["traffic_source"] = measured_traffic(dominant, args.config)
+    per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], cfg, B, P,
+                                                                  1).items()
+                                       if k in ("bound", "achieved", "unit", "frac")}
+                                      if kern[n]["launches"] else {}))
+                  for n in names}
+    value = B * N * args.steps / wall
+    out = {
+        "metric": "training-forward canvas tokens/s at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"] + ("+fp8-experts" if cfg.get("expert_dtype") == "fp8" else ""),
+        "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt and clean tokens)",
+        "config": {"workload": (f"train-{args.config}: {cfg['n_layers']} layer(s) "
+                                f"d{cfg['d_model']}, vocab {V}, prompt {P}, canvas {N}, batch {B}; "
+                                f"one step = corruption at rate {args.rate:g} + denoiser forward "
+                                f"+ cross-entropy at the clean tokens"),
+                   "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
+                   "mean_loss": float(mean.cpu().numpy()[0])},
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+    oracle_fits = cfg["n_layers"] == 1 and B == 1 and P <= 4096
+    if args.no_cpu_baseline or not oracle_fits:
+        out["cpu_baseline"] = None
+    else:
+        out["cpu_baseline"] = cpu_baseline_train(
+            cfg, W, prompt.cpu().numpy().astype(np.int64), clean.cpu().numpy().astype(np.int32),
+            np.full(B, args.rate, np.float32), args.seed)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -368,6 +494,9 @@ def main():
         sys.exit(2)
     if args.mode == "ar":
         bench_ar(args)
+        return
+    if args.mode == "train":
+        bench_train(args)
         return
     import numpy as np
     import torch
