@@ -1339,7 +1339,7 @@ dg_status dg_stage_head_rowmax(dg_model* m, int32_t T, const float* d_h, float* 
     DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
     if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
     if (T > s.ut_rows) return fail(DG_ERR_CAPACITY, "T exceeds the head's blocked row budget %d", s.ut_rows);
-    s.fuse = true;
+    s.want_rowmax = true;
     s.tmax = d_rowmax;
     return stage_head<bf16_t>(m, T, d_h, d_logits, s, as_stream(stream));
 }
