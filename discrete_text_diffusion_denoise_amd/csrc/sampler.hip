@@ -174,6 +174,50 @@ __device__ int pick_seq(const float* w, int n, float u) {
     return 0;
 }
 
+// pick_seq over an array in LDS, read 16 values at a time (4 x 16 bytes,
+// one wait) instead of one wait per value: the same sums in the same order.
+// w is 16-byte aligned and readable up to n rounded up to 16.
+__device__ int pick_lds(const float* w, int n, float u) {
+    float total = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 t = reinterpret_cast<const float4*>(w + i0)[q];
+            v[4 * q + 0] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (i0 + j < n) total = total + v[j];
+    }
+    const float target = u * total;
+    float acc = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 t = reinterpret_cast<const float4*>(w + i0)[q];
+            v[4 * q + 0] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (i0 + j < n) {
+                acc = acc + v[j];
+                if (acc > target) return i0 + j;
+            }
+        }
+    }
+    for (int i = n - 1; i >= 0; --i)
+        if (w[i] > 0.0f) return i;
+    return 0;
+}
+
 // Raw buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data,
 // no swizzle).  A buffer access takes one 32-bit lane offset plus a uniform
 // offset, so the sixteen loads and stores of a tile share one address
@@ -344,9 +388,10 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
     float* Gs = sm;                       // [nt*1024] chunk weights at temperature T
     float* Ms = sm + nt * NLANE;          // [nt*1024] chunk maxima
     __shared__ Rec wrec[16];
-    __shared__ float Wsup[8 * 16];
-    __shared__ float wk[4 * NDEPTH];
+    __shared__ __align__(16) float Wsup[8 * 16];
+    __shared__ __align__(16) float wk[4 * NDEPTH];
     __shared__ int kk[4 * NDEPTH];
+    __shared__ int nmem;
 
     const long rowid = blockIdx.x;        // b*N + i
     const int b = (int)(rowid / a.N), i = (int)(rowid % a.N);
@@ -491,8 +536,21 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
     __syncthreads();
     const int nsup = nt * (NLANE / SUPER);
     if (tid < nsup) {
+        // sequential sum of the superchunk's 64 chunk weights, read 16 at a time
+        const float4* g4p = reinterpret_cast<const float4*>(Gs + tid * SUPER);
         float acc = 0.0f;
-        for (int l = 0; l < SUPER; ++l) acc = acc + Gs[tid * SUPER + l];
+        for (int l0 = 0; l0 < SUPER / 4; l0 += 4) {
+            float4 t[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t[q] = g4p[l0 + q];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = acc + t[q].x;
+                acc = acc + t[q].y;
+                acc = acc + t[q].z;
+                acc = acc + t[q].w;
+            }
+        }
         Wsup[tid] = acc;
     }
     __syncthreads();
@@ -505,8 +563,8 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
         words[1] = o[1];
         words[2] = o[2];
         words[3] = o[3];
-        const int sstar = pick_seq(Wsup, nsup, uniform01(o[0]));
-        cstar_s = sstar * SUPER + pick_seq(Gs + sstar * SUPER, SUPER, uniform01(o[2]));
+        const int sstar = pick_lds(Wsup, nsup, uniform01(o[0]));
+        cstar_s = sstar * SUPER + pick_lds(Gs + sstar * SUPER, SUPER, uniform01(o[2]));
     }
     __syncthreads();
     // entries of the chosen chunk, in member order
@@ -517,18 +575,15 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
         const long k = 4 * ((long)t * NLANE * NDEPTH + (long)d * NLANE + l) + q;
         wk[tid] = k < a.V ? dexp((row[k] - Ms[cstar]) * invT) : 0.0f;
         kk[tid] = k < a.V ? (int)k : -1;
+        // k grows with tid, so the members (k < V) are the first popcount
+        // slots, already in member order
+        const uint64_t mem = __ballot(k < a.V);
+        if (tid == 0) nmem = __popcll(mem);
     }
     __syncthreads();
     if (tid == 0) {
-        // compact the members in place (entries past V are not members)
-        int n = 0;
-        for (int u = 0; u < 4 * NDEPTH; ++u)
-            if (kk[u] >= 0) {
-                wk[n] = wk[u];
-                kk[n] = kk[u];
-                ++n;
-            }
-        const int yv = n > 0 ? kk[pick_seq(wk, n, uniform01(words[3]))] : 0;
+        const int n = nmem;
+        const int yv = n > 0 ? kk[pick_lds(wk, n, uniform01(words[3]))] : 0;
         float H = dlog(R.s) - R.a / R.s;
         H = H > 0.0f ? H : 0.0f;
         const float pmax = 1.0f / R.s;
@@ -909,15 +964,25 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
             }
         }
         if (tid == 0) {
+            // the sorted keys carry H in their high word; 16 keys are read
+            // before the running sum walks them (the LDS reads overlap)
             float acc = 0.0f;
-            for (int n = 0; n < N; ++n) {
-                const int i = (int)(uint32_t)keys[n];
-                const float H = Hs[i];
-                if (acc + H <= a.theta) {
-                    lk[i] = 1;
-                    acc = acc + H;
-                } else {
-                    break;
+            bool go = true;
+            for (int n0 = 0; n0 < N && go; n0 += 16) {
+                uint64_t kv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) kv[u] = keys[min(n0 + u, npow - 1)];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    if (go && n0 + u < N) {
+                        const float H = __uint_as_float((uint32_t)(kv[u] >> 32));
+                        if (acc + H <= a.theta) {
+                            lk[(uint32_t)kv[u]] = 1;
+                            acc = acc + H;
+                        } else {
+                            go = false;
+                        }
+                    }
                 }
             }
         }
@@ -933,8 +998,16 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
     }
     const int stable = __syncthreads_and(same) && a.step > 0;
     if (tid == 0) {
+        // sequential sum in position order, 16 values read ahead at a time
         float sumH = 0.0f;
-        for (int i = 0; i < N; ++i) sumH = sumH + Hs[i];
+        for (int i0 = 0; i0 < N; i0 += 16) {
+            float hv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) hv[u] = Hs[min(i0 + u, N - 1)];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (i0 + u < N) sumH = sumH + hv[u];
+        }
         const float meanH = sumH / (float)N;
         int st = (meanH < a.tau) && (!a.require_stable || stable);
         if (a.step + 1 >= a.max_steps) st = 1;
