@@ -36,6 +36,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
+# fp32 vector ALU without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# binary32 operations per second (an fma counts as one operation here)
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+ALU_RIDGE = ALU_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # operations per byte
+# binary32 operations per logit of the sampler's row pass, from its
+# definition: chunk max 1, z = l - m 1, E(z) 14, three sums and e*z 4,
+# z*invT 1, E(z*invT) 14, plus 2 when it also writes the self-conditioning
+# weight (e*f and the bf16 conversion)
+SAMPLER_OPS = 36
 
 
 def parse():
@@ -133,6 +142,11 @@ def kernel_work(name, cfg, B, P, sc_splits):
         return (4.0 * T * L * Hq * dh,
                 T * Hq * dh * es + B * L * Hkv * dh * 2 * es + T * Hq * dh * es)
     if name == "sampler":
+        if cfg.get("sampler_alu"):
+            # ALU work of the full-distribution row pass (see SAMPLER_OPS)
+            ops = T * V * (SAMPLER_OPS + (2 if cfg.get("sampler_probs") else 0))
+            nbytes = T * V * 4.0 + T * 16.0 + (T * V * 2.0 if cfg.get("sampler_probs") else 0.0)
+            return ops, nbytes
         if cfg.get("sampler_top_k"):
             # slab maxima, then about K candidate slabs of 64 logits per row
             K = cfg["sampler_top_k"]
@@ -143,6 +157,12 @@ def kernel_work(name, cfg, B, P, sc_splits):
 
 def roofline(name, ms, cfg, B, P, sc_splits):
     flops, nbytes = kernel_work(name, cfg, B, P, sc_splits)
+    if name == "sampler" and cfg.get("sampler_alu") and flops / nbytes >= ALU_RIDGE:
+        ach = flops / (ms * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": round(ach, 2), "peak": round(ALU_PEAK_TOPS, 1),
+                "unit": "Top/s", "frac": round(ach / ALU_PEAK_TOPS, 4), "traffic": None,
+                "kernel": name, "op_per_launch": flops, "bytes_per_launch": nbytes,
+                "avg_launch_ms": round(ms, 5)}
     ai = flops / nbytes if nbytes else 0.0
     s = ms * 1e-3
     if flops and ai >= RIDGE:
@@ -507,6 +527,11 @@ def main():
     over = {"n_layers": args.layers} if args.layers else {}
     cfg = synthetic.model_config(args.config, **over)
     cfg["sampler_top_k"] = args.top_k
+    # the full-distribution sampler is bound by its binary32 arithmetic; in
+    # the block loop of bf16 models it also writes the next round's
+    # self-conditioning weights
+    cfg["sampler_alu"] = args.top_k == 0
+    cfg["sampler_probs"] = args.top_k == 0 and cfg["dtype"] == "bf16"
     B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
     torch.cuda.init()
     W = device_weights(cfg, args.seed, torch)
