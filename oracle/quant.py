@@ -26,6 +26,17 @@ Quantisation of a row w[0..K) (this library's definition, written out):
   dequantised weight = decode(q_k) * scale.
 Every function below follows that text; the encoder is the plain
 definition (nearest entry of the value table), not a bit trick.
+
+MXFP4 (OCP Microscaling Formats specification, v1.0): blocks of 32
+consecutive elements of a row share one E8M0 scale (an 8-bit biased
+exponent, X = 2^(code - 127)); each element is an FP4 E2M1 value (1 sign, 2
+exponent bits with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6).  The
+specification's scale is X = 2^(floor(log2(max |v|)) - emax), emax = 2 for
+E2M1 (6 = 1.5 * 2^2), and each element is v / X rounded to the nearest E2M1
+value with ties to the even code, magnitudes above 6 clamped to 6.  Readings
+of this library: an all-zero block takes code 0 (X = 2^-127) and zero
+elements; the scale exponent is clamped to [-127, 127]; two elements per byte,
+the even-indexed one in the low nibble.
 """
 from __future__ import annotations
 
@@ -101,3 +112,95 @@ def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """decode(q) * scale per row, in float64 (exact)."""
     table = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
     return table[np.asarray(q, dtype=np.uint8)] * np.asarray(s, dtype=np.float64)[:, None]
+
+
+# ---------------------------------------------------------------- MXFP4
+
+FP4_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+FP4_MAX = 6.0
+MX_BLOCK = 32
+
+
+def fp4_decode(code: int) -> float:
+    """Value of a 4-bit E2M1 code."""
+    code = int(code) & 0xF
+    return (-1.0 if code & 8 else 1.0) * FP4_MAG[code & 7]
+
+
+def fp4_encode(x: float) -> int:
+    """E2M1 code of the nearest value to x (ties to the even code), magnitudes
+    above 6 giving 6; the sign is kept (-0 gives code 8)."""
+    neg = bool(np.signbit(x))
+    a = abs(float(x))
+    if a >= FP4_MAX:
+        c = 7
+    else:
+        d = np.abs(FP4_MAG - a)
+        best = d.min()
+        cands = np.nonzero(d == best)[0]
+        c = int(cands[0])
+        if len(cands) > 1:
+            c = int(cands[0] if cands[0] % 2 == 0 else cands[1])
+    return c | (8 if neg else 0)
+
+
+def fp4_encode_array(x: np.ndarray) -> np.ndarray:
+    """fp4_encode of every entry (the two table neighbours, the nearer one,
+    ties to the even code)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(FP4_MAG, a), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    d_lo = a - FP4_MAG[lo]
+    d_hi = FP4_MAG[hi] - a
+    c = np.where(d_hi < d_lo, hi, lo)
+    c = np.where(d_hi == d_lo, np.where(lo % 2 == 0, lo, hi), c)
+    c = np.where(a >= FP4_MAX, 7, c)
+    return (c | np.where(neg, 8, 0)).astype(np.uint8)
+
+
+def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """floor(log2(amax)) - 2 per block, clamped to [-127, 127]; -127 for an
+    all-zero block."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)                  # amax = m 2^e, m in [0.5, 1)
+    ex = (e - 1) - 2
+    ex = np.where(amax > 0, ex, -127)
+    return np.clip(ex, -127, 127).astype(np.int64)
+
+
+def mx_quantize_rows(w: np.ndarray):
+    """Rows of w [R, K] (K % 32 == 0, values rounded to binary32) -> (codes
+    uint8 [R, K], one E2M1 code per element; scale codes uint8 [R, K/32])."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    R, K = w.shape
+    blocks = w.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    ex = mx_scale_exponent(np.abs(blocks).max(axis=2))
+    quo = blocks * np.ldexp(1.0, -ex)[..., None]         # exact: a power of two
+    codes = fp4_encode_array(quo).reshape(R, K)
+    return codes, (ex + 127).astype(np.uint8)
+
+
+def mx_pack(codes: np.ndarray) -> np.ndarray:
+    """Two E2M1 codes per byte along the last axis, the even one in the low
+    nibble."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def mx_unpack(packed: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def mx_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """decode(code) * 2^(scale - 127) per element, in float64 (exact)."""
+    table = np.array([fp4_decode(c) for c in range(16)], dtype=np.float64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, K = codes.shape
+    x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (table[codes].reshape(R, K // MX_BLOCK, MX_BLOCK) * x[..., None]).reshape(R, K)
