@@ -14,7 +14,7 @@ tokens / wall time); ms_per_step = one block.  With random-init weights the
 entropy stop never fires, so each block runs the full 48 rounds.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--config layer|layer_fp8|stack|batched] [--layers L] [--top-k K]
+                  [--config layer|layer_fp8|layer_mxfp4|stack|batched] [--layers L] [--top-k K]
   python bench.py --mode train [--rate r] [--config ...]
       the training-side forward: value = canvas tokens/s through corruption,
       the denoiser forward and the cross-entropy at the clean tokens
@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="layer",
-                    choices=["layer", "layer_fp8", "stack", "batched"])
+                    choices=["layer", "layer_fp8", "layer_mxfp4", "stack", "batched"])
     ap.add_argument("--layers", type=int, default=None,
                     help="override the configuration's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,6 +107,17 @@ def device_weights(cfg, seed, torch):
                 binding.quantize_fp8(w, q, sc)
                 lw[k], lw[sk] = q, sc
             torch.cuda.synchronize()
+        if cfg.get("expert_dtype") == "mxfp4":
+            # MXFP4 experts: the same draws, quantised on the GPU by the
+            # library (packed E2M1 codes, an E8M0 scale per 32 weights)
+            from discrete_text_diffusion_denoise_amd import binding
+            for k, xk in (("w_gate", "x_gate"), ("w_up", "x_up"), ("w_down", "x_down")):
+                w = lw[k]
+                q = torch.empty(w.shape[:-1] + (w.shape[-1] // 2,), dtype=torch.uint8, device="cuda")
+                sc = torch.empty(w.numel() // 32, dtype=torch.uint8, device="cuda")
+                binding.quantize_mxfp4(w, q, sc)
+                lw[k], lw[xk] = q, sc
+            torch.cuda.synchronize()
         W["layers"].append(lw)
     return W
 
@@ -119,7 +130,9 @@ def kernel_work(name, cfg, B, P, sc_splits):
     # expert weight bytes per element (8-bit experts also read one fp32
     # scale per weight row)
     fp8 = cfg.get("expert_dtype") == "fp8"
-    ew = 1 if fp8 else es
+    fp4 = cfg.get("expert_dtype") == "mxfp4"
+    # MXFP4: half a byte per weight plus one scale byte per 32
+    ew = 1 if fp8 else (0.5 + 1.0 / 32 if fp4 else es)
     N, V, d = cfg["canvas"], cfg["vocab"], cfg["d_model"]
     Hq, Hkv, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     E, k, F = cfg["n_experts"], cfg["top_k"], cfg["d_ff"]
@@ -221,7 +234,18 @@ def cpu_baseline(cfg, W, prompt, canvas, params, torch):
     host = {"embed": W["embed"].float().cpu().numpy(), "w_sc": W["w_sc"].float().cpu().numpy(),
             "final_norm": W["final_norm"].cpu().numpy().astype(np.float64), "layers": []}
     for lw in W["layers"]:
-        hl = {k: v.float().cpu().numpy() for k, v in lw.items() if not k.startswith("s_")}
+        hl = {k: v.float().cpu().numpy() for k, v in lw.items()
+              if not k.startswith("s_") and not k.startswith("x_")}
+        if cfg.get("expert_dtype") == "mxfp4":
+            # the oracle's experts are the dequantised MXFP4 weights
+            from oracle import quant as oq
+            for k, xk in (("w_gate", "x_gate"), ("w_up", "x_up"), ("w_down", "x_down")):
+                q = lw[k].cpu().numpy()
+                K = 2 * q.shape[-1]
+                R = q.size // q.shape[-1]
+                codes = oq.mx_unpack(q.reshape(R, K // 2))
+                sc = lw[xk].cpu().numpy().reshape(K // 64, R, 2).transpose(1, 0, 2).reshape(R, K // 32)
+                hl[k] = oq.mx_dequantize_rows(codes, sc).reshape(q.shape[:-1] + (K,))
         if cfg.get("expert_dtype") == "fp8":
             # the oracle's experts are the dequantised codes
             from oracle import quant as oq
@@ -301,7 +325,7 @@ def bench_ar(args):
     shape = synthetic.SHAPES[args.config]
     over = {"n_layers": args.layers} if args.layers else {}
     cfg = synthetic.model_config(args.config, **over)
-    if cfg.get("expert_dtype") == "fp8":
+    if cfg.get("expert_dtype"):
         raise SystemExit("--mode ar runs the bf16 configurations")
     B, P, V, n_new = args.ar_batch, shape["prompt"], cfg["vocab"], args.ar_tokens
     torch.cuda.init()
@@ -426,6 +450,8 @@ def bench_train(args):
     shape = synthetic.SHAPES[args.config]
     over = {"n_layers": args.layers} if args.layers else {}
     cfg = synthetic.model_config(args.config, **over)
+    if cfg.get("expert_dtype"):
+        raise SystemExit("--mode train runs the bf16 configurations")
     B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
     torch.cuda.init()
     W = device_weights(cfg, args.seed, torch)
@@ -634,12 +660,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg["dtype"] + ("+fp8-experts" if cfg.get("expert_dtype") == "fp8" else ""),
+        "dtype": cfg["dtype"] + {"fp8": "+fp8-experts", "mxfp4": "+mxfp4-experts"}.get(
+            cfg.get("expert_dtype"), ""),
         "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt tokens)",
         "config": {"workload": (f"{args.config}: {cfg['n_layers']} denoiser layer(s) d{cfg['d_model']} "
                                 f"{cfg['n_heads']}q/{cfg['n_kv_heads']}kv x{cfg['head_dim']}, "
                                 f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}"
-                                f"{' (E4M3 weights, per-row scales)' if cfg.get('expert_dtype') == 'fp8' else ''}, "
+                                f"{ {'fp8': ' (E4M3 weights, per-row scales)', 'mxfp4': ' (MXFP4 weights)'}.get(cfg.get('expert_dtype'), '')}, "
                                 f"vocab {V}, prompt {P}, canvas {N}, batch {B}; one step = one "
                                 f"block (<=48 self-conditioned rounds + commit)"),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",

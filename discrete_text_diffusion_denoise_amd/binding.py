@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdg.so")
 _lib = None
 
-DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
+DG_F32, DG_BF16, DG_FP8_E4M3, DG_MXFP4 = 0, 1, 2, 3
 LOCK_MAXPROB, LOCK_CUMENT = 0, 1
 STATUS = {0: "DG_OK", 1: "DG_ERR_ARG", 2: "DG_ERR_SHAPE", 3: "DG_ERR_DTYPE",
           4: "DG_ERR_CAPACITY", 5: "DG_ERR_NONFINITE", 6: "DG_ERR_HIP", 7: "DG_ERR_UNSUPPORTED"}
@@ -42,7 +42,7 @@ class Config(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("attn_norm", "wq", "wk", "wv", "wo", "moe_norm", "w_router", "w_gate", "w_up",
-                 "w_down", "s_gate", "s_up", "s_down")]
+                 "w_down", "s_gate", "s_up", "s_down", "x_gate", "x_up", "x_down")]
 
 
 class Weights(ctypes.Structure):
@@ -70,6 +70,7 @@ _SIGS = {
     "dg_embed_head_bytes": (_I, [_P, _P]),
     "dg_embed_head": (_I, [_P, _P, _P, _P]),
     "dg_quantize_fp8": (_I, [_P, _I, ctypes.c_int64, _I, _P, _P, _P]),
+    "dg_quantize_mxfp4": (_I, [_P, _I, ctypes.c_int64, _I, _P, _P, _P]),
     "dg_kv_bytes": (_I, [_P, _I, _I, _P]),
     "dg_kv_create": (_I, [_P, _I, _I, _P, _P]),
     "dg_kv_destroy": (None, [_P]),
@@ -177,12 +178,17 @@ class Model:
                   "final_norm": dev(weights["final_norm"], torch.float32)}
         # 8-bit experts: w_gate / w_up / w_down hold E4M3 codes (uint8) and
         # s_gate / s_up / s_down their per-row fp32 scales
+        # MXFP4 experts: w_* hold packed E2M1 codes (uint8 [E][R][K/2]) and
+        # x_gate / x_up / x_down the E8M0 scale codes ([K/64][E*R][2], uint8)
         fp8 = cfg.get("expert_dtype") == "fp8"
+        fp4 = cfg.get("expert_dtype") == "mxfp4"
 
         def ldtype(k):
             if k.endswith("norm") or k.startswith("s_"):
                 return torch.float32
-            if fp8 and k in ("w_gate", "w_up", "w_down"):
+            if (fp8 or fp4) and k in ("w_gate", "w_up", "w_down"):
+                return torch.uint8
+            if k.startswith("x_"):
                 return torch.uint8
             return None
 
@@ -194,7 +200,7 @@ class Model:
                    cfg["head_dim"], cfg["n_experts"], cfg["top_k"], cfg["d_ff"], cfg["vocab"],
                    cfg["canvas"], DG_BF16 if cfg["dtype"] == "bf16" else DG_F32,
                    int(cfg["rope_on"]), float(cfg["rope_theta"]), float(cfg["rms_eps"]),
-                   DG_FP8_E4M3 if fp8 else 0)
+                   DG_FP8_E4M3 if fp8 else (DG_MXFP4 if fp4 else 0))
         self._cfg_struct = c
         layer_arr = (LayerWeights * cfg["n_layers"])()
         for i, d in enumerate(self.lw):
@@ -203,6 +209,9 @@ class Model:
                 setattr(layer_arr[i], k, d[k].data_ptr())
             if fp8:
                 for k in ("s_gate", "s_up", "s_down"):
+                    setattr(layer_arr[i], k, d[k].data_ptr())
+            if fp4:
+                for k in ("x_gate", "x_up", "x_down"):
                     setattr(layer_arr[i], k, d[k].data_ptr())
         self._layer_arr = layer_arr
         self.w["embed_t"] = torch.empty((cfg["d_model"], cfg["vocab"]), dtype=self.dtype,
@@ -416,6 +425,17 @@ def quantize_fp8(src, q, scale, stream=None):
     rows = src.numel() // cols
     dt = DG_BF16 if src.dtype == torch.bfloat16 else DG_F32
     _check(lib().dg_quantize_fp8(_ptr(src), dt, rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def quantize_mxfp4(src, codes, scales, stream=None):
+    """dg_quantize_mxfp4: src [..., cols] (f32 or bf16, cols % 64 == 0) ->
+    codes (uint8 [..., cols/2], two per byte) and scales (uint8, rows * cols/32,
+    laid out [cols/64][rows][2])."""
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    dt = DG_BF16 if src.dtype == torch.bfloat16 else DG_F32
+    _check(lib().dg_quantize_mxfp4(_ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales),
+                                   _stream(stream)))
 
 
 def timer_enable(names) -> None:

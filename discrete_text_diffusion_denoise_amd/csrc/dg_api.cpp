@@ -452,6 +452,11 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
         a.s_gate = L.s_gate;
         a.s_up = L.s_up;
         a.s_down = L.s_down;
+    } else if (c.expert_dtype == DG_MXFP4) {
+        a.f4 = 1;
+        a.x_gate = L.x_gate;
+        a.x_up = L.x_up;
+        a.x_down = L.x_down;
     }
     a.perm_tok = s.perm_tok;
     a.slot_of = s.slot_of;
@@ -698,8 +703,24 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
         if (!L.wq || !L.wk || !L.wv || !L.wo || !L.w_router || !L.w_gate || !L.w_up || !L.w_down)
             return fail(DG_ERR_ARG, "missing weights in layer %d", l);
     }
-    if (c.expert_dtype != 0 && c.expert_dtype != c.dtype && c.expert_dtype != DG_FP8_E4M3)
+    if (c.expert_dtype != 0 && c.expert_dtype != c.dtype && c.expert_dtype != DG_FP8_E4M3 &&
+        c.expert_dtype != DG_MXFP4)
         return fail(DG_ERR_DTYPE, "expert_dtype %d", c.expert_dtype);
+    if (c.expert_dtype == DG_MXFP4) {
+        // the MXFP4 experts run on the direct-to-LDS ring kernels only
+        dg::MoeArgs probe;
+        probe.d = c.d_model;
+        probe.F = c.d_ff;
+        probe.f4 = 1;
+        if (c.dtype != DG_BF16 || !dg::expert_dma_ok(probe))
+            return fail(DG_ERR_UNSUPPORTED,
+                        "MXFP4 experts need a bf16 model with d_model and d_ff multiples of 256");
+        for (int l = 0; l < c.n_layers; ++l) {
+            const dg_layer_weights& L = w->layers[l];
+            if (!L.x_gate || !L.x_up || !L.x_down)
+                return fail(DG_ERR_ARG, "MXFP4 experts need x_gate, x_up and x_down (layer %d)", l);
+        }
+    }
     if (c.expert_dtype == DG_FP8_E4M3) {
         // the 8-bit experts run on the direct-to-LDS ring kernels only
         dg::MoeArgs probe;
@@ -740,6 +761,22 @@ dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, in
     else if (src_dtype == DG_F32)
         DG_HIP(dg::quantize_fp8<float>((const float*)d_src, (long)rows, cols, (uint8_t*)d_q,
                                        d_scale, as_stream(stream)));
+    else
+        return fail(DG_ERR_DTYPE, "src_dtype %d", src_dtype);
+    return DG_OK;
+}
+
+dg_status dg_quantize_mxfp4(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
+                            void* d_codes, uint8_t* d_scales, void* stream) {
+    if (!d_src || !d_codes || !d_scales) return fail(DG_ERR_ARG, "NULL pointer");
+    if (rows < 1 || cols < 64 || cols % 64 || rows > 0x7FFFFFFF)
+        return fail(DG_ERR_ARG, "bad sizes (cols a multiple of 64)");
+    if (src_dtype == DG_BF16)
+        DG_HIP(dg::quantize_mxfp4<bf16_t>((const bf16_t*)d_src, (long)rows, cols,
+                                          (uint8_t*)d_codes, d_scales, as_stream(stream)));
+    else if (src_dtype == DG_F32)
+        DG_HIP(dg::quantize_mxfp4<float>((const float*)d_src, (long)rows, cols, (uint8_t*)d_codes,
+                                         d_scales, as_stream(stream)));
     else
         return fail(DG_ERR_DTYPE, "src_dtype %d", src_dtype);
     return DG_OK;

@@ -173,6 +173,14 @@ struct MoeArgs {
     const float* s_gate = nullptr;
     const float* s_up = nullptr;
     const float* s_down = nullptr;
+    // MXFP4 experts: w_gate / w_up / w_down hold packed E2M1 codes [E][R][K/2]
+    // (the even k in the low nibble); x_* the E8M0 scale codes of each 32-k
+    // block, laid out [K/64][E*R][2] (the two blocks of a 64-k stage of a row
+    // adjacent, the rows of one stage contiguous)
+    int f4 = 0;
+    const uint8_t* x_gate = nullptr;
+    const uint8_t* x_up = nullptr;
+    const uint8_t* x_down = nullptr;
 };
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);
@@ -191,6 +199,13 @@ bool expert_dma_ok(const MoeArgs& a);
 template <typename T>
 hipError_t quantize_fp8(const T* src, long rows, int cols, uint8_t* q, float* scale,
                         hipStream_t st);
+
+// MXFP4 codes and scale codes of src [rows][cols] (cols % 64 == 0), in the
+// expert kernels' layout (MoeArgs::f4): codes [rows][cols/2], scale codes
+// [cols/64][rows][2]
+template <typename T>
+hipError_t quantize_mxfp4(const T* src, long rows, int cols, uint8_t* q, uint8_t* scale,
+                          hipStream_t st);
 
 // ------------------------------------------------------------------ sampler
 struct SampleArgs {

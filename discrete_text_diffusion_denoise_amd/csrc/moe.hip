@@ -324,6 +324,8 @@ struct XdCtx {
     int lane, wave, r16, g4, ct, mp, lr, lc;
     const char* wsrc[2];     // byte addresses of this lane's weight chunks at k = 0
     const bf16_t* X;
+    const uint8_t* ssrc;     // MXFP4: this lane's 16 scale bytes of stage 0
+    long sstride;            // MXFP4: scale bytes from one stage to the next
 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -337,18 +339,34 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     return u32x4{pack_bf2(a.x, a.y), pack_bf2(b.x, b.y), pack_bf2(c.x, c.y), pack_bf2(d.x, d.y)};
 }
 
+// 8 E2M1 codes (a word, the even k in the low nibble of each byte) times a
+// power-of-two scale -> 8 bf16 values, exact (every such product is a bf16
+// value): gfx950 converts the two codes of a selected byte per instruction,
+// low nibble first (checked on all 256 bytes and several scales)
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t w, float scale) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
+}
+
 // XOR swizzle of the four 16-byte chunks of a 64-byte LDS row
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int MODE, int G, bool F8>
+// FMT: 0 bf16 weights, 1 E4M3 codes with per-row scales, 2 MXFP4 (E2M1 codes,
+// an E8M0 scale per 32 k)
+template <int MODE, int G, int FMT>
 __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, unsigned char* w0,
                                               unsigned char* w1, unsigned char* w2, unsigned char* w3,
                                               unsigned char* x0, unsigned char* x1, unsigned char* x2,
-                                              unsigned char* x3) {
+                                              unsigned char* x3, unsigned char* s0, unsigned char* s1,
+                                              unsigned char* s2, unsigned char* s3) {
+    constexpr bool F8 = FMT == 1, F4 = FMT == 2;
     constexpr int WQ = 2;                              // weight DMAs per wave per stage
-    constexpr int PER = WQ + G;                        // DMAs per wave per stage
-    constexpr int WSTAGE = F8 ? 64 : 128;              // weight bytes per row and stage
-    constexpr int J = F8 ? 2 : 1;                      // 16-column tiles per half and wave
+    constexpr int SQ = F4 ? 1 : 0;                     // scale DMAs per wave per stage
+    constexpr int PER = WQ + G + SQ;                   // DMAs per wave per stage
+    constexpr int WSTAGE = F4 ? 32 : (F8 ? 64 : 128);  // weight bytes per row and stage
+    constexpr int J = F4 ? 4 : (F8 ? 2 : 1);           // 16-column tiles per half and wave
     constexpr int HALF = 32 * J;                       // columns per half of the block
     const int n = c.n, rot = c.rot, mp = c.mp, ct = c.ct, r16 = c.r16, g4 = c.g4;
     const int wblk = c.wave * WQ * 1024;
@@ -396,7 +414,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             tv[q] = mg + 16 * (mp + 2 * q) < c.cnt;
         }
 
-#define XD_ISSUE(ST, WB, XB)                                                                      \
+#define XD_ISSUE(ST, WB, XB, SB)                                                                  \
         {                                                                                         \
             int sr_ = (ST) + rot;                                                                 \
             if (sr_ >= n) sr_ -= n;                                                               \
@@ -407,6 +425,9 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             _Pragma("unroll") for (int q = 0; q < G; ++q)                                         \
                 __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
                                                  (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
+            if (F4 && c.lane < 8)                                                                 \
+                __builtin_amdgcn_global_load_lds((glb_void*)(c.ssrc + (long)sr_ * c.sstride),     \
+                                                 (lds_void*)((SB) + c.wave * 128), 16, 0, 0);     \
         }
         // fragments: token rows 16*(mp + 2q) + r16; weight rows (ct + 2j)*16
         // + r16 of each half.  bf16 weights: k-step s of a lane is chunk
@@ -414,14 +435,72 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
         // chunk g4 of the 64-byte row (k 16*g4 .. 16*g4+15), so its token
         // chunks are 2*g4 (k-step 0) and 2*g4 + 1 (k-step 1): every k of the
         // stage is in exactly one k-step of one lane group, as the sum needs
-#define XD_COMPUTE(WB, XB)                                                                        \
+#define XD_COMPUTE(WB, XB, SB)                                                                    \
         {                                                                                         \
             u32x4 fga[J], fgb[J], fua[J], fub[J], fxa[G], fxb[G];                                 \
             const uint32_t xa = lds_addr(XB) + (16 * mp) * 128 + roff;                            \
             const int xs = r16 & 7;                                                               \
-            const uint32_t sa = F8 ? ((2 * g4) ^ xs) << 4 : (g4 ^ xs) << 4;                       \
-            const uint32_t sb = F8 ? ((2 * g4 + 1) ^ xs) << 4 : ((4 + g4) ^ xs) << 4;             \
-            if (F8) {                                                                             \
+            const uint32_t sa = (F8 || F4) ? ((2 * g4) ^ xs) << 4 : (g4 ^ xs) << 4;               \
+            const uint32_t sb = (F8 || F4) ? ((2 * g4 + 1) ^ xs) << 4 : ((4 + g4) ^ xs) << 4;     \
+            if (F4) {                                                                             \
+                /* weight row (ct + 2j)*16 + r16 of each half (32 bytes a row,  */                \
+                /* 16-byte chunk c in slot c ^ bit 3 of the row): the lane's 8  */                \
+                /* bytes are codes k 16*g4 .. 16*g4+15 of the stage, one MX     */                \
+                /* block, whose scale byte sits at half*256 + row*2 + g4/2      */                \
+                const int wr0 = ct * 16 + r16;                                                    \
+                const uint32_t wq_ = lds_addr(WB) + wr0 * 32 +                                    \
+                                     ((((g4 >> 1) ^ ((r16 >> 3) & 1))) << 4) + ((g4 & 1) << 3);   \
+                const uint32_t sq_ = lds_addr(SB) + wr0 * 2 + (g4 >> 1);                          \
+                uint2 cw[2 * J];                                                                  \
+                uint32_t cs[2 * J];                                                               \
+                if (G == 1) {                                                                     \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %18\n ds_read_b128 %1, %19\n"                            \
+                        "ds_read_b64 %2, %20 offset:0\n ds_read_b64 %3, %20 offset:1024\n"        \
+                        "ds_read_b64 %4, %20 offset:2048\n ds_read_b64 %5, %20 offset:3072\n"     \
+                        "ds_read_b64 %6, %20 offset:4096\n ds_read_b64 %7, %20 offset:5120\n"     \
+                        "ds_read_b64 %8, %20 offset:6144\n ds_read_b64 %9, %20 offset:7168\n"     \
+                        "ds_read_u8 %10, %21 offset:0\n ds_read_u8 %11, %21 offset:64\n"          \
+                        "ds_read_u8 %12, %21 offset:128\n ds_read_u8 %13, %21 offset:192\n"       \
+                        "ds_read_u8 %14, %21 offset:256\n ds_read_u8 %15, %21 offset:320\n"       \
+                        "ds_read_u8 %16, %21 offset:384\n ds_read_u8 %17, %21 offset:448\n"       \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]),   \
+                          "=&v"(cw[3]), "=&v"(cw[4]), "=&v"(cw[5]), "=&v"(cw[6]), "=&v"(cw[7]),     \
+                          "=&v"(cs[0]), "=&v"(cs[1]), "=&v"(cs[2]), "=&v"(cs[3]), "=&v"(cs[4]),     \
+                          "=&v"(cs[5]), "=&v"(cs[6]), "=&v"(cs[7])                                \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(wq_), "v"(sq_)                          \
+                        : "memory");                                                              \
+                } else {                                                                          \
+                    asm volatile(                                                                 \
+                        "ds_read_b128 %0, %20\n ds_read_b128 %1, %21\n"                            \
+                        "ds_read_b128 %2, %20 offset:4096\n ds_read_b128 %3, %21 offset:4096\n"   \
+                        "ds_read_b64 %4, %22 offset:0\n ds_read_b64 %5, %22 offset:1024\n"        \
+                        "ds_read_b64 %6, %22 offset:2048\n ds_read_b64 %7, %22 offset:3072\n"     \
+                        "ds_read_b64 %8, %22 offset:4096\n ds_read_b64 %9, %22 offset:5120\n"     \
+                        "ds_read_b64 %10, %22 offset:6144\n ds_read_b64 %11, %22 offset:7168\n"   \
+                        "ds_read_u8 %12, %23 offset:0\n ds_read_u8 %13, %23 offset:64\n"          \
+                        "ds_read_u8 %14, %23 offset:128\n ds_read_u8 %15, %23 offset:192\n"       \
+                        "ds_read_u8 %16, %23 offset:256\n ds_read_u8 %17, %23 offset:320\n"       \
+                        "ds_read_u8 %18, %23 offset:384\n ds_read_u8 %19, %23 offset:448\n"       \
+                        "s_waitcnt lgkmcnt(0)"                                                     \
+                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
+                          "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(cw[4]),     \
+                          "=&v"(cw[5]), "=&v"(cw[6]), "=&v"(cw[7]), "=&v"(cs[0]), "=&v"(cs[1]),     \
+                          "=&v"(cs[2]), "=&v"(cs[3]), "=&v"(cs[4]), "=&v"(cs[5]), "=&v"(cs[6]),     \
+                          "=&v"(cs[7])                                                            \
+                        : "v"(xa + sa), "v"(xa + sb), "v"(wq_), "v"(sq_)                          \
+                        : "memory");                                                              \
+                }                                                                                 \
+                _Pragma("unroll") for (int j = 0; j < J; ++j) {                                   \
+                    const float fg_ = __builtin_amdgcn_ldexpf(1.0f, (int)cs[j] - 127);            \
+                    const float fu_ = __builtin_amdgcn_ldexpf(1.0f, (int)cs[J + j] - 127);        \
+                    fga[j] = e2m1x8_to_bf16(cw[j].x, fg_);                                        \
+                    fgb[j] = e2m1x8_to_bf16(cw[j].y, fg_);                                        \
+                    fua[j] = e2m1x8_to_bf16(cw[J + j].x, fu_);                                    \
+                    fub[j] = e2m1x8_to_bf16(cw[J + j].y, fu_);                                    \
+                }                                                                                 \
+            } else if (F8) {                                                                             \
                 const int wr0 = ct * 16 + r16, wr1 = wr0 + 32;                                    \
                 const uint32_t wb_ = lds_addr(WB);                                                \
                 const uint32_t g0_ = wb_ + wr0 * 64 + ((g4 ^ swz4(wr0)) << 4);                    \
@@ -501,7 +580,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                 }                                                                                 \
             }                                                                                     \
         }
-#define XD_STAGE(t, CW, CX, NW, NX)                          \
+#define XD_STAGE(t, CW, CX, CS, NW, NX, NS)                  \
         {                                                    \
             if ((t) + 2 < n)                                 \
                 DG_WAIT_VM(2 * PER);                         \
@@ -510,17 +589,17 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             else                                             \
                 DG_WAIT_VM(0);                               \
             barrier_lds();                                   \
-            if ((t) + 3 < n) XD_ISSUE((t) + 3, NW, NX);      \
-            XD_COMPUTE(CW, CX);                              \
+            if ((t) + 3 < n) XD_ISSUE((t) + 3, NW, NX, NS);  \
+            XD_COMPUTE(CW, CX, CS);                          \
         }
-        XD_ISSUE(0, w0, x0);
-        XD_ISSUE(1, w1, x1);
-        XD_ISSUE(2, w2, x2);
+        XD_ISSUE(0, w0, x0, s0);
+        XD_ISSUE(1, w1, x1, s1);
+        XD_ISSUE(2, w2, x2, s2);
         for (int t = 0; t < n; t += 4) {
-            XD_STAGE(t, w0, x0, w3, x3);
-            XD_STAGE(t + 1, w1, x1, w0, x0);
-            XD_STAGE(t + 2, w2, x2, w1, x1);
-            XD_STAGE(t + 3, w3, x3, w2, x2);
+            XD_STAGE(t, w0, x0, s0, w3, x3, s3);
+            XD_STAGE(t + 1, w1, x1, s1, w0, x0, s0);
+            XD_STAGE(t + 2, w2, x2, s2, w1, x1, s1);
+            XD_STAGE(t + 3, w3, x3, s3, w2, x2, s2);
         }
 #undef XD_STAGE
 #undef XD_COMPUTE
@@ -563,14 +642,18 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
 // set.  An expert with at most 32 tokens (most of them: a 256-token canvas
 // makes 2048 assignments over 128 experts) runs groups of 32, a busier one
 // groups of 64, so its weights are streamed fewer times.
-template <int MODE, bool F8>
+template <int MODE, int FMT>
 __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.halt && *a.halt) return;
+    constexpr bool F8 = FMT == 1, F4 = FMT == 2;
     __shared__ __align__(1024) unsigned char w0[64 * 128], x0[8192];
     __shared__ __align__(1024) unsigned char w1[64 * 128], x1[8192];
     __shared__ __align__(1024) unsigned char w2[64 * 128], x2[8192];
     __shared__ __align__(1024) unsigned char w3[64 * 128], x3[8192];
-    constexpr int HALF = F8 ? 64 : 32;                 // columns per half of a block
+    // MXFP4 scale bytes of a stage: 256 rows x 2 blocks
+    __shared__ __align__(16) unsigned char s0[F4 ? 512 : 16], s1[F4 ? 512 : 16];
+    __shared__ __align__(16) unsigned char s2[F4 ? 512 : 16], s3[F4 ? 512 : 16];
+    constexpr int HALF = F4 ? 128 : (F8 ? 64 : 32);    // columns per half of a block
 
     XdCtx c;
     // the busiest experts first, so their longer blocks do not form the tail
@@ -601,7 +684,16 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     c.lc = ((c.lane & 7) ^ c.lr) * 8;                 // element offset (rows are 8-aligned)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        if (F8) {
+        if (F4) {
+            // weight DMA lanes: an instruction fills 32 rows x 32 bytes; lane
+            // l takes row l / 2 and global chunk (l % 2) ^ (bit 3 of the row)
+            const int r = (c.wave * 2 + q) * 32 + (c.lane >> 1);   // row within the block
+            const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
+            const int col = min(c.c0 + rr, c.NOUT - 1);
+            const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
+            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * (c.K / 2) +
+                        (((c.lane & 1) ^ ((r >> 3) & 1)) << 4);
+        } else if (F8) {
             // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
             // takes row l / 4 and global chunk (l % 4) ^ swz4(row)
             const int r = (c.wave * 2 + q) * 16 + (c.lane >> 2);   // row within the block
@@ -617,10 +709,20 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
             c.wsrc[q] = base + (((long)c.e * c.NOUT + col) * c.K + c.lc) * 2;
         }
     }
+    c.ssrc = nullptr;
+    c.sstride = 0;
+    if (F4) {
+        // scale DMA lanes 0..7 of wave w: bytes [128 w, 128 w + 128) of the
+        // stage's 512 (gate rows c0.. then up rows c0.., or down rows c0..)
+        const uint8_t* X = MODE == 0 ? (c.wave < 2 ? a.x_gate : a.x_up) : a.x_down;
+        const int piece = MODE == 0 ? (c.wave & 1) : c.wave;
+        c.ssrc = X + ((long)c.e * c.NOUT + c.c0) * 2 + piece * 128 + (c.lane & 7) * 16;
+        c.sstride = (long)a.E * c.NOUT * 2;
+    }
     if (__builtin_amdgcn_readfirstlane(c.cnt) <= 32)
-        expert_groups<MODE, 1, F8>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
+        expert_groups<MODE, 1, FMT>(a, c, w0, w1, w2, w3, x0, x1, x2, x3, s0, s1, s2, s3);
     else
-        expert_groups<MODE, 2, F8>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
+        expert_groups<MODE, 2, FMT>(a, c, w0, w1, w2, w3, x0, x1, x2, x3, s0, s1, s2, s3);
 }
 
 // Counts, offsets and the stable placement in one workgroup.  The
@@ -774,17 +876,20 @@ bool expert_dma_ok(const MoeArgs& a) {
     }
     // DG_DMA=0 (sweeps) turns off the bf16 ring only: 8-bit experts run on
     // the ring alone
-    return (enabled || a.f8) && a.d % 256 == 0 && a.F % 256 == 0;
+    return (enabled || a.f8 || a.f4) && a.d % 256 == 0 && a.F % 256 == 0;
 }
 
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.f8) {
+    if (a.f4) {
+        if (sizeof(T) != 2 || !expert_dma_ok(a) || !a.x_gate || !a.x_up) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((expert_dma_kernel<0, 2>), dim3(cdiv(a.F, 128), a.E), dim3(256), 0, st, a);
+    } else if (a.f8) {
         if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<0, true>), dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<0, 1>), dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
     } else if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<0, false>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<0, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -793,11 +898,14 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.f8) {
+    if (a.f4) {
+        if (sizeof(T) != 2 || !expert_dma_ok(a) || !a.x_down) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((expert_dma_kernel<1, 2>), dim3(cdiv(a.d, 256), a.E), dim3(256), 0, st, a);
+    } else if (a.f8) {
         if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<1, true>), dim3(cdiv(a.d, 128), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<1, 1>), dim3(cdiv(a.d, 128), a.E), dim3(256), 0, st, a);
     } else if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<1, false>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<1, 0>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();

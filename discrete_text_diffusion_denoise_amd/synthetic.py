@@ -31,6 +31,10 @@ SHAPES = {
     "layer_fp8": dict(n_layers=1, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                       n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
                       expert_dtype="fp8", prompt=2048, batch=1, max_steps=48),
+    # the same layer with MXFP4 expert weights
+    "layer_mxfp4": dict(n_layers=1, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+                        n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
+                        expert_dtype="mxfp4", prompt=2048, batch=1, max_steps=48),
     # 30 such layers, prompt 4096
     "stack": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                   n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",

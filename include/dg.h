@@ -61,7 +61,9 @@ typedef enum {
 typedef enum {
     DG_F32 = 0,
     DG_BF16 = 1,
-    DG_FP8_E4M3 = 2   /* OCP 8-bit float E4M3 ("e4m3fn"), expert weights only */
+    DG_FP8_E4M3 = 2,  /* OCP 8-bit float E4M3 ("e4m3fn"), expert weights only */
+    DG_MXFP4 = 3      /* OCP MXFP4: E2M1 codes with an E8M0 scale per 32,       */
+                      /* expert weights only                                     */
 } dg_dtype;
 
 typedef enum {
@@ -85,8 +87,10 @@ typedef struct {
     float rope_theta;       /* RoPE base                                      */
     float rms_eps;          /* RMSNorm epsilon                                */
     int32_t expert_dtype;   /* 0: experts in `dtype`; DG_FP8_E4M3: expert     */
-                            /* weights as E4M3 codes with per-row fp32 scales */
-                            /* (bf16 models, d_model and d_ff multiples of 256) */
+                            /* weights as E4M3 codes with per-row fp32 scales; */
+                            /* DG_MXFP4: packed E2M1 codes with block scales   */
+                            /* (both: bf16 models, d_model and d_ff multiples  */
+                            /* of 256)                                         */
 } dg_config;
 
 typedef struct {
@@ -105,6 +109,14 @@ typedef struct {
     const float* s_gate;     /* [E][F]              */
     const float* s_up;       /* [E][F]              */
     const float* s_down;     /* [E][d]              */
+    /* MXFP4 experts only (else NULL): w_gate / w_up / w_down hold E2M1 codes  */
+    /* packed two per byte ([E][R][K/2], the even k in the low nibble), and    */
+    /* these hold the E8M0 scale code of every 32-k block, laid out            */
+    /* [K/64][E*R][2] (dg_quantize_mxfp4), so that weight[e][r][k] =           */
+    /* decode(code) * 2^(scale - 127)                                          */
+    const uint8_t* x_gate;   /* [d/64][E*F][2]      */
+    const uint8_t* x_up;     /* [d/64][E*F][2]      */
+    const uint8_t* x_down;   /* [F/64][E*d][2]      */
 } dg_layer_weights;
 
 typedef struct {
@@ -198,6 +210,20 @@ dg_status dg_kv_set_length(dg_kv* kv, int32_t len);
  * non-positive sizes, DG_ERR_DTYPE on another src_dtype. */
 dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
                           void* d_q, float* d_scale, void* stream);
+/* 4-bit expert weights in the OCP microscaling format MXFP4 (same passage;
+ * the closest CDNA4 format to the pages' 4-bit one; gfx950 converts it in
+ * hardware).  Quantises d_src [rows][cols] (src_dtype DG_F32 or DG_BF16,
+ * cols % 64 == 0) in blocks of 32 consecutive elements of a row: X =
+ * 2^(floor(log2(max |x|)) - 2), the exponent clamped to [-127, 127] (an
+ * all-zero block takes 2^-127); code = E2M1 of x / X, round to nearest with
+ * ties to the even code, magnitudes above 6 giving 6.  Writes d_codes
+ * [rows][cols/2] (two codes per byte, the even element in the low nibble)
+ * and d_scales [cols/64][rows][2] (the E8M0 codes 127 + log2 X of the two
+ * blocks of each 64-column stage, adjacent).  An expert matrix [E][R][K] is
+ * rows = E*R, cols = K.  DG_ERR_ARG on NULL or bad sizes, DG_ERR_DTYPE on
+ * another src_dtype. */
+dg_status dg_quantize_mxfp4(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
+                            void* d_codes, uint8_t* d_scales, void* stream);
 
 /* ---------------------------------------------------------------- workspace */
 /* Bytes of scratch for every model call with up to `batch` sequences.

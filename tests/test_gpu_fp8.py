@@ -68,3 +68,60 @@ def test_quantize_fp8_expert_shape():
     rq, rs = oq.quantize_rows(w.reshape(-1, 512))
     assert (q.cpu().numpy().reshape(-1, 512) == rq).all()
     assert (s.cpu().numpy().reshape(-1) == rs).all()
+
+
+# ------------------------------------------------------------------ MXFP4
+
+
+def mx_library_layout(scales_nat: np.ndarray) -> np.ndarray:
+    """Scale codes [rows][cols/32] -> the library's [cols/64][rows][2]."""
+    R, nb = scales_nat.shape
+    return np.ascontiguousarray(scales_nat.reshape(R, nb // 2, 2).transpose(1, 0, 2))
+
+
+def mx_tie_rows(K: int) -> np.ndarray:
+    """Blocks whose amax is 6 * 2^j: the scale is 2^(j) * 2^... exactly and
+    every quotient sits on or halfway between E2M1 values (ties to even,
+    saturation of 7 * 2^j against a 4 * 2^j amax, signed zeros)."""
+    vals = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, -5.0, 0.0, -0.0, 0.1,
+                     5.9, 4.4, 2.9], dtype=np.float32)
+    rows = []
+    for j in (-9, -4, 0, 3):
+        rows.append(np.resize(vals, K) * np.float32(2.0 ** j))
+    sat = np.resize(np.array([4.0, 7.9, -7.0, 6.5, 1.0], np.float32), K)   # amax 7.9: X = 1
+    rows.append(sat)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_quantize_mxfp4_bit_exact(src):
+    rng = np.random.default_rng(11)
+    R, K = 300, 768
+    w = (rng.standard_normal((R, K)) * 0.02).astype(np.float32)
+    w[5] = 0.0                                     # all-zero blocks: scale code 0
+    w[7] *= 1e6
+    w[8:13] = mx_tie_rows(K)
+    w[20, :32] = 0.0                               # one zero block inside a row
+    if src == "bf16":
+        w = synthetic.round_bf16(w)
+        d = to_dev(w, torch.bfloat16)
+    else:
+        d = to_dev(w)
+    q = torch.empty((R, K // 2), dtype=torch.uint8, device=DEV)
+    s = torch.empty(R * K // 32, dtype=torch.uint8, device=DEV)
+    binding.quantize_mxfp4(d, q, s)
+    torch.cuda.synchronize()
+    codes, sc = oq.mx_quantize_rows(w)
+    assert np.array_equal(s.cpu().numpy().reshape(K // 64, R, 2), mx_library_layout(sc))
+    gq = q.cpu().numpy()
+    rq = oq.mx_pack(codes)
+    bad = np.argwhere(gq != rq)
+    assert len(bad) == 0, [(int(r), int(c), int(gq[r, c]), int(rq[r, c])) for r, c in bad[:5]]
+
+
+def test_quantize_mxfp4_rejects_ragged_columns():
+    d = torch.zeros((4, 96), dtype=torch.float32, device=DEV)
+    q = torch.empty((4, 48), dtype=torch.uint8, device=DEV)
+    s = torch.empty(12, dtype=torch.uint8, device=DEV)
+    with pytest.raises(binding.DGError):
+        binding.quantize_mxfp4(d, q, s)

@@ -37,15 +37,30 @@ VOCAB_RAGGED = dict(VOCAB_BF16, vocab=32768 + 96, canvas=200)
 # the bf16 model with 8-bit (E4M3, per-row scale) expert weights; the oracle
 # runs the dequantised weights
 SMALL_FP8 = dict(SMALL_BF16, expert_dtype="fp8")
+# ... and with MXFP4 expert weights (E2M1 codes, an E8M0 scale per 32)
+SMALL_MXFP4 = dict(SMALL_BF16, expert_dtype="mxfp4")
 
 MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
-          "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8}
+          "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8, "small_mxfp4": SMALL_MXFP4}
 
 
 def device_form(cfg, W):
-    """(weights for the library, weights for the oracle).  8-bit experts: the
-    oracle's quantiser gives the codes and scales the library runs on, and
-    the oracle runs their dequantised values."""
+    """(weights for the library, weights for the oracle).  8-bit and MXFP4
+    experts: the oracle's quantiser gives the codes and scales the library
+    runs on, and the oracle runs their dequantised values."""
+    if cfg.get("expert_dtype") == "mxfp4":
+        Wg = dict(W, layers=[dict(lw) for lw in W["layers"]])
+        Wo = dict(W, layers=[dict(lw) for lw in W["layers"]])
+        for lg, lo in zip(Wg["layers"], Wo["layers"]):
+            for k, xk in (("w_gate", "x_gate"), ("w_up", "x_up"), ("w_down", "x_down")):
+                w = lg[k]
+                K = w.shape[-1]
+                codes, sc = oq.mx_quantize_rows(w.reshape(-1, K))
+                lg[k] = oq.mx_pack(codes).reshape(w.shape[:-1] + (K // 2,))
+                R = codes.shape[0]
+                lg[xk] = np.ascontiguousarray(sc.reshape(R, K // 64, 2).transpose(1, 0, 2))
+                lo[k] = oq.mx_dequantize_rows(codes, sc).reshape(w.shape)
+        return Wg, Wo
     if cfg.get("expert_dtype") != "fp8":
         return W, W
     Wg = dict(W, layers=[dict(lw) for lw in W["layers"]])
@@ -104,7 +119,7 @@ def oracle_encode_with_gaps(prompt, W64, cfg, gap):
 
 
 @pytest.mark.parametrize("name,P,B", [("tiny", 32, 1), ("small_bf16", 300, 2), ("f32_gqa", 77, 2),
-                                      ("small_fp8", 300, 2)])
+                                      ("small_fp8", 300, 2), ("small_mxfp4", 300, 2)])
 def test_encode_prompt_kv_cache(name, P, B):
     print(f"encode {name} P={P} B={B}", flush=True)
     cfg, W, m = setup(name, P, batch=B)
@@ -145,6 +160,7 @@ def test_encode_prompt_kv_cache(name, P, B):
                                                              ("f32_gqa", 64, 2, True, 2, 0),
                                                              ("f32_gqa", 64, 1, False, 3, 0),
                                                              ("small_fp8", 200, 2, True, 1, 0),
+                                                             ("small_mxfp4", 200, 2, True, 1, 0),
                                                              ("tiny", 32, 1, True, 1, 64),
                                                              ("small_bf16", 200, 2, True, 1, 8)])
 def test_denoise_step(name, P, B, selfcond, layers, top_k):
@@ -230,7 +246,8 @@ def test_stage_attention_on_synthetic_cache(name, causal):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 256), ("small_bf16", 512), ("small_bf16", 37),
-                                    ("f32_gqa", 1000), ("small_fp8", 512), ("small_fp8", 37)])
+                                    ("f32_gqa", 1000), ("small_fp8", 512), ("small_fp8", 37),
+                                    ("small_mxfp4", 512), ("small_mxfp4", 37)])
 def test_stage_moe(name, T):
     cfg, W, m = setup(name, 0)
     rng = np.random.default_rng(11)
@@ -329,6 +346,7 @@ def test_commit_equals_encode_of_concatenation():
                                                          ("small_bf16", 2, True, False, 0),
                                                          ("vocab_bf16", 1, True, False, 0),
                                                          ("small_fp8", 2, True, False, 0),
+                                                         ("small_mxfp4", 2, True, False, 0),
                                                          ("small_bf16", 2, False, False, 0),
                                                          ("small_bf16", 2, True, True, 0),
                                                          ("tiny", 1, True, False, 16),
