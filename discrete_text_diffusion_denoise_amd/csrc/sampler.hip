@@ -964,25 +964,15 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
             }
         }
         if (tid == 0) {
-            // the sorted keys carry H in their high word; 16 keys are read
-            // before the running sum walks them (the LDS reads overlap)
             float acc = 0.0f;
-            bool go = true;
-            for (int n0 = 0; n0 < N && go; n0 += 16) {
-                uint64_t kv[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) kv[u] = keys[min(n0 + u, npow - 1)];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    if (go && n0 + u < N) {
-                        const float H = __uint_as_float((uint32_t)(kv[u] >> 32));
-                        if (acc + H <= a.theta) {
-                            lk[(uint32_t)kv[u]] = 1;
-                            acc = acc + H;
-                        } else {
-                            go = false;
-                        }
-                    }
+            for (int n = 0; n < N; ++n) {
+                const int i = (int)(uint32_t)keys[n];
+                const float H = Hs[i];
+                if (acc + H <= a.theta) {
+                    lk[i] = 1;
+                    acc = acc + H;
+                } else {
+                    break;
                 }
             }
         }
@@ -998,16 +988,8 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
     }
     const int stable = __syncthreads_and(same) && a.step > 0;
     if (tid == 0) {
-        // sequential sum in position order, 16 values read ahead at a time
         float sumH = 0.0f;
-        for (int i0 = 0; i0 < N; i0 += 16) {
-            float hv[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) hv[u] = Hs[min(i0 + u, N - 1)];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (i0 + u < N) sumH = sumH + hv[u];
-        }
+        for (int i = 0; i < N; ++i) sumH = sumH + Hs[i];
         const float meanH = sumH / (float)N;
         int st = (meanH < a.tau) && (!a.require_stable || stable);
         if (a.step + 1 >= a.max_steps) st = 1;
