@@ -281,7 +281,7 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
     int splits = 1;
     static const int target = [] {
         const char* e = getenv("DG_ATTN_WG");   // sweeps: workgroups to aim for
-        return e ? std::max(1, atoi(e)) : 640;
+        return e ? std::max(1, atoi(e)) : 2048;
     }();
     if (!causal && kv_len > 256) {
         splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(target, (int)base)));

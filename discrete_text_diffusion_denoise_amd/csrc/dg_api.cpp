@@ -212,7 +212,8 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.qkv = cv.take<float>(T * qkvw);
     s.q = cv.take_bytes(T * c.n_heads * c.head_dim * es);
     s.ao = cv.take_bytes(T * c.n_heads * c.head_dim * es);
-    const size_t prow = std::max<size_t>(kAttnPartRows, Tc);
+    // split-KV partials: up to eight splits of every canvas row
+    const size_t prow = std::max<size_t>(kAttnPartRows, 8 * Tc);
     s.part_o = cv.take<float>(prow * c.n_heads * c.head_dim);
     s.part_ml = cv.take<float>(prow * c.n_heads * 2);
     s.z = cv.take<float>(T * c.n_experts);
@@ -410,7 +411,7 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     a.halt = s.halt;
     // the split merge handles heads of 64 or more dimensions
     const int max_splits =
-        dh < 64 ? 1 : std::max(1, std::max(kAttnPartRows, B * c.canvas) / Tn);
+        dh < 64 ? 1 : std::max(1, std::max(kAttnPartRows, 8 * B * c.canvas) / Tn);
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len);
     DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
