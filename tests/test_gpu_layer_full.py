@@ -76,3 +76,71 @@ def test_full_layer_selfcond_step_sampled_rows(layer_run):
     print(f"sampled-row normwise error {err:.3e}; near-tie rows {amb.sum()}", flush=True)
     assert err <= TOL_BF16
     assert np.isfinite(r["logits"]).all()
+
+
+def gpu_weights(cfg, seed):
+    """Random-init N(0, 0.02^2) bf16 weights drawn on the GPU (the block loop
+    is compared with its own composition here, so no oracle needs them)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    d, V, E, F = cfg["d_model"], cfg["vocab"], cfg["n_experts"], cfg["d_ff"]
+    Hq, Hkv, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+
+    def draw(*shape):
+        return (torch.randn(shape, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+
+    ones = lambda: torch.ones(d, device=DEV)  # noqa: E731
+    lw = {"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
+          "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
+          "w_router": draw(E, d), "w_gate": draw(E, F, d), "w_up": draw(E, F, d),
+          "w_down": draw(E, d, F)}
+    return {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": [lw]}
+
+
+@pytest.mark.parametrize("top_k", [0, 64])
+def test_full_layer_generate_block_is_its_composition(top_k):
+    """The benchmark's block (full-size layer, the pages' sampler defaults, 48
+    self-conditioned rounds) equals its call-by-call composition bit for bit:
+    block, round counts and the committed cache."""
+    cfg = synthetic.model_config("layer")
+    P, N, V = synthetic.SHAPES["layer"]["prompt"], cfg["canvas"], cfg["vocab"]
+    print(f"full-size block loop, top_k={top_k}", flush=True)
+    W = gpu_weights(cfg, 3)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4)
+    prompt = torch.randint(0, V, (1, P), generator=g, device=DEV, dtype=torch.int32)
+    params = synthetic.default_sampler_params(max_steps=48, seed=7, selfcond_on=1, top_k=top_k)
+    mg = binding.Model(cfg, W, batch=1, capacity=P + 2 * N, generate_ws=True)
+    mg.encode_prompt(prompt)
+    block = torch.zeros((1, N), dtype=torch.int32, device=DEV)
+    steps = mg.generate_block(params, 0, block)
+    torch.cuda.synchronize()
+    K1 = [t.clone() for t in mg.kv_tensors()]
+    del mg
+    mc = binding.Model(cfg, W, batch=1, capacity=P + 2 * N)
+    mc.encode_prompt(prompt)
+    canvas = torch.zeros((1, N), dtype=torch.int32, device=DEV)
+    binding.canvas_init(params["seed"], 0, canvas, V)
+    argmax = torch.zeros((1, N), dtype=torch.int32, device=DEV)
+    lock = torch.zeros((1, N), dtype=torch.uint8, device=DEV)
+    stop = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lg = [torch.empty((1, N, V), dtype=torch.float32, device=DEV) for _ in range(2)]
+    st = [torch.empty((1, N, 4), dtype=torch.float32, device=DEV) for _ in range(2)]
+    ws = binding.sampler_workspace(1, N)
+    prev = prev_st = None
+    my_steps = 0
+    for t in range(params["max_steps"]):
+        mc.denoise_step(canvas, lg[t % 2], prev, prev_st, top_k=top_k if prev is not None else 0)
+        binding.sample_update(params, t, lg[t % 2], canvas, argmax, lock, st[t % 2], stop, ws)
+        if stop.item():
+            my_steps = t + 1
+            break
+        prev, prev_st = lg[t % 2], st[t % 2]
+    mc.commit_block(argmax)
+    torch.cuda.synchronize()
+    assert steps == [my_steps] == [48]
+    assert torch.equal(block, argmax)
+    K2 = mc.kv_tensors()
+    L = P + N
+    assert torch.equal(K1[0][..., :L, :], K2[0][..., :L, :])
+    assert torch.equal(K1[1][..., :L, :], K2[1][..., :L, :])
