@@ -568,7 +568,8 @@ def main():
     m.encode_prompt(prompt)
     params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1,
                                               top_k=args.top_k,
-                                              stop_tau=shape.get("stop_tau", 0.005))
+                                              stop_tau=shape.get("stop_tau", 0.005),
+                                              **shape.get("sampler", {}))
     block = torch.zeros((B, N), dtype=torch.int32, device="cuda")
 
     names = list(binding.TIMERS)
@@ -671,7 +672,10 @@ def main():
                                 f"block (<=48 self-conditioned rounds + commit)"),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
                    "rounds_per_block": float(np.mean(rounds)) if rounds else None,
-                   "sampler": (f"cumulative-entropy lock 0.1, T 0.8->0.4, stop "
+                   "sampler": ((f"cumulative-entropy lock {params['lock_theta']:g}"
+                                if params["lock_rule"] == 1 else
+                                f"lock where max-probability > {params['lock_theta']:g}")
+                               + f", T {params['temp_start']:g}->{params['temp_end']:g}, stop "
                                f"{params['stop_tau']:g} + stable"
                                + (f", top-{args.top_k} truncation" if args.top_k else ""))},
         "denoise_step_ms": round(step_ms, 4),

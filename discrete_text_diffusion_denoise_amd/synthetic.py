@@ -36,9 +36,11 @@ SHAPES = {
                         n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
                         expert_dtype="mxfp4", prompt=2048, batch=1, max_steps=48),
     # 30 such layers, prompt 4096
+    # (its sampler: temperature 1, lock where the max-probability exceeds 0.9)
     "stack": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                   n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",
-                  prompt=4096, batch=1, max_steps=48),
+                  prompt=4096, batch=1, max_steps=48,
+                  sampler=dict(lock_rule=0, lock_theta=0.9, temp_start=1.0, temp_end=1.0)),
     # 8 canvases with 8192-token prompts each
     "batched": dict(n_layers=30, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                     n_experts=128, top_k=8, d_ff=768, vocab=262144, canvas=256, dtype="bf16",

@@ -90,26 +90,30 @@ def gpu_weights(cfg, seed):
         return (torch.randn(shape, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
 
     ones = lambda: torch.ones(d, device=DEV)  # noqa: E731
-    lw = {"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
-          "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
-          "w_router": draw(E, d), "w_gate": draw(E, F, d), "w_up": draw(E, F, d),
-          "w_down": draw(E, d, F)}
-    return {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": [lw]}
+    layers = [{"attn_norm": ones(), "wq": draw(Hq * dh, d), "wk": draw(Hkv * dh, d),
+               "wv": draw(Hkv * dh, d), "wo": draw(d, Hq * dh), "moe_norm": ones(),
+               "w_router": draw(E, d), "w_gate": draw(E, F, d), "w_up": draw(E, F, d),
+               "w_down": draw(E, d, F)} for _ in range(cfg["n_layers"])]
+    return {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": layers}
 
 
-@pytest.mark.parametrize("top_k", [0, 64])
-def test_full_layer_generate_block_is_its_composition(top_k):
-    """The benchmark's block (full-size layer, the pages' sampler defaults, 48
-    self-conditioned rounds) equals its call-by-call composition bit for bit:
-    block, round counts and the committed cache."""
-    cfg = synthetic.model_config("layer")
-    P, N, V = synthetic.SHAPES["layer"]["prompt"], cfg["canvas"], cfg["vocab"]
-    print(f"full-size block loop, top_k={top_k}", flush=True)
+@pytest.mark.parametrize("config,top_k", [("layer", 0), ("layer", 64), ("stack", 0)])
+def test_full_layer_generate_block_is_its_composition(config, top_k):
+    """The benchmark's block at full size (the single layer with the pages'
+    sampler defaults; the 30-layer stack with a 4096-token prompt and its
+    sampler, temperature 1 and max-probability locking at 0.9; 48
+    self-conditioned rounds) equals its call-by-call composition bit for
+    bit: block, round counts and the committed cache."""
+    shape = synthetic.SHAPES[config]
+    cfg = synthetic.model_config(config)
+    P, N, V = shape["prompt"], cfg["canvas"], cfg["vocab"]
+    print(f"full-size block loop, {config}, top_k={top_k}", flush=True)
     W = gpu_weights(cfg, 3)
     g = torch.Generator(device=DEV)
     g.manual_seed(4)
     prompt = torch.randint(0, V, (1, P), generator=g, device=DEV, dtype=torch.int32)
-    params = synthetic.default_sampler_params(max_steps=48, seed=7, selfcond_on=1, top_k=top_k)
+    params = synthetic.default_sampler_params(max_steps=48, seed=7, selfcond_on=1, top_k=top_k,
+                                              **shape.get("sampler", {}))
     mg = binding.Model(cfg, W, batch=1, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(prompt)
     block = torch.zeros((1, N), dtype=torch.int32, device=DEV)
@@ -144,3 +148,4 @@ def test_full_layer_generate_block_is_its_composition(top_k):
     L = P + N
     assert torch.equal(K1[0][..., :L, :], K2[0][..., :L, :])
     assert torch.equal(K1[1][..., :L, :], K2[1][..., :L, :])
+    assert torch.isfinite(lg[(my_steps - 1) % 2]).all()
