@@ -14,7 +14,7 @@ tokens / wall time); ms_per_step = one block.  With random-init weights the
 entropy stop never fires, so each block runs the full 48 rounds.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--config layer|layer_fp8|layer_mxfp4|stack|batched] [--layers L] [--top-k K]
+                  [--config layer|layer_fp8|layer_mxfp4|stack|batched|long] [--layers L] [--top-k K]
   python bench.py --mode train [--rate r] [--config ...]
       the training-side forward: value = canvas tokens/s through corruption,
       the denoiser forward and the cross-entropy at the clean tokens
@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="layer",
-                    choices=["layer", "layer_fp8", "layer_mxfp4", "stack", "batched"])
+                    choices=["layer", "layer_fp8", "layer_mxfp4", "stack", "batched", "long"])
     ap.add_argument("--layers", type=int, default=None,
                     help="override the configuration's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -559,9 +559,12 @@ def main():
     cfg["sampler_alu"] = args.top_k == 0
     cfg["sampler_probs"] = args.top_k == 0 and cfg["dtype"] == "bf16"
     B, N, V, P = shape["batch"], cfg["canvas"], cfg["vocab"], shape["prompt"]
+    # consecutive blocks per step, each committed before the next (the cache
+    # is rewound to the prompt after the last)
+    nb = shape.get("blocks", 1)
     torch.cuda.init()
     W = device_weights(cfg, args.seed, torch)
-    m = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
+    m = binding.Model(cfg, W, batch=B, capacity=P + (nb + 1) * N, generate_ws=True)
     g = torch.Generator(device="cuda")
     g.manual_seed(args.seed + 1)
     prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
@@ -576,7 +579,8 @@ def main():
     # warmup, with every kernel timer on: picks the dominant kernel
     binding.timer_enable(names)
     for w in range(args.warmup):
-        m.generate_block(params, w, block)
+        for k in range(nb):
+            m.generate_block(params, w * nb + k, block)
         m.set_kv_length(P)
     torch.cuda.synchronize()
     warm = {n: binding.timer_read(n) for n in names}
@@ -591,7 +595,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        rounds += m.generate_block(params, args.warmup + s, block)
+        for k in range(nb):
+            rounds += m.generate_block(params, (args.warmup + s) * nb + k, block)
         m.set_kv_length(P)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -649,7 +654,7 @@ def main():
                                       if kern[n]["launches"] else {}))
                   for n in names}
 
-    value = B * N * args.steps / wall
+    value = B * N * args.steps * nb / wall
     out = {
         "metric": "canvas tokens/s at 1 MI355X",
         "value": round(value, 2),
@@ -669,7 +674,9 @@ def main():
                                 f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}"
                                 f"{ {'fp8': ' (E4M3 weights, per-row scales)', 'mxfp4': ' (MXFP4 weights)'}.get(cfg.get('expert_dtype'), '')}, "
                                 f"vocab {V}, prompt {P}, canvas {N}, batch {B}; one step = one "
-                                f"block (<=48 self-conditioned rounds + commit)"),
+                                f"block (<=48 self-conditioned rounds + commit)"
+                                + (f"; here one step = {nb} consecutive blocks, each committed "
+                                   f"(context {P} .. {P + (nb - 1) * N})" if nb > 1 else "")),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
                    "rounds_per_block": float(np.mean(rounds)) if rounds else None,
                    "sampler": ((f"cumulative-entropy lock {params['lock_theta']:g}"
