@@ -97,55 +97,64 @@ def gpu_weights(cfg, seed):
     return {"embed": draw(V, d), "w_sc": draw(d, d), "final_norm": ones(), "layers": layers}
 
 
-@pytest.mark.parametrize("config,top_k", [("layer", 0), ("layer", 64), ("stack", 0)])
+@pytest.mark.parametrize("config,top_k", [("layer", 0), ("layer", 64), ("stack", 0),
+                                          ("batched", 64)])
 def test_full_layer_generate_block_is_its_composition(config, top_k):
-    """The benchmark's block at full size (the single layer with the pages'
-    sampler defaults; the 30-layer stack with a 4096-token prompt and its
-    sampler, temperature 1 and max-probability locking at 0.9; 48
-    self-conditioned rounds) equals its call-by-call composition bit for
-    bit: block, round counts and the committed cache."""
+    """The benchmark's block at full size equals its call-by-call composition
+    bit for bit: block, round counts and the committed cache.  The single
+    layer with the pages' sampler defaults; the 30-layer stack with a
+    4096-token prompt and its sampler (temperature 1, max-probability locking
+    at 0.9); eight canvases over 8192-token prompts through the 30-layer
+    stack with the top-64 sampler; 48 self-conditioned rounds."""
     shape = synthetic.SHAPES[config]
     cfg = synthetic.model_config(config)
-    P, N, V = shape["prompt"], cfg["canvas"], cfg["vocab"]
+    B, P, N, V = shape["batch"], shape["prompt"], cfg["canvas"], cfg["vocab"]
     print(f"full-size block loop, {config}, top_k={top_k}", flush=True)
     W = gpu_weights(cfg, 3)
     g = torch.Generator(device=DEV)
     g.manual_seed(4)
-    prompt = torch.randint(0, V, (1, P), generator=g, device=DEV, dtype=torch.int32)
+    prompt = torch.randint(0, V, (B, P), generator=g, device=DEV, dtype=torch.int32)
     params = synthetic.default_sampler_params(max_steps=48, seed=7, selfcond_on=1, top_k=top_k,
+                                              stop_tau=shape.get("stop_tau", 0.005),
                                               **shape.get("sampler", {}))
-    mg = binding.Model(cfg, W, batch=1, capacity=P + 2 * N, generate_ws=True)
+    mg = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(prompt)
-    block = torch.zeros((1, N), dtype=torch.int32, device=DEV)
+    block = torch.zeros((B, N), dtype=torch.int32, device=DEV)
     steps = mg.generate_block(params, 0, block)
     torch.cuda.synchronize()
     K1 = [t.clone() for t in mg.kv_tensors()]
     del mg
-    mc = binding.Model(cfg, W, batch=1, capacity=P + 2 * N)
+    torch.cuda.empty_cache()
+    mc = binding.Model(cfg, W, batch=B, capacity=P + 2 * N)
     mc.encode_prompt(prompt)
-    canvas = torch.zeros((1, N), dtype=torch.int32, device=DEV)
+    canvas = torch.zeros((B, N), dtype=torch.int32, device=DEV)
     binding.canvas_init(params["seed"], 0, canvas, V)
-    argmax = torch.zeros((1, N), dtype=torch.int32, device=DEV)
-    lock = torch.zeros((1, N), dtype=torch.uint8, device=DEV)
-    stop = torch.zeros(1, dtype=torch.int32, device=DEV)
-    lg = [torch.empty((1, N, V), dtype=torch.float32, device=DEV) for _ in range(2)]
-    st = [torch.empty((1, N, 4), dtype=torch.float32, device=DEV) for _ in range(2)]
-    ws = binding.sampler_workspace(1, N)
+    argmax = torch.zeros((B, N), dtype=torch.int32, device=DEV)
+    lock = torch.zeros((B, N), dtype=torch.uint8, device=DEV)
+    stop = torch.zeros(B, dtype=torch.int32, device=DEV)
+    lg = [torch.empty((B, N, V), dtype=torch.float32, device=DEV) for _ in range(2)]
+    st = [torch.empty((B, N, 4), dtype=torch.float32, device=DEV) for _ in range(2)]
+    ws = binding.sampler_workspace(B, N)
     prev = prev_st = None
-    my_steps = 0
+    my_steps = [0] * B
+    last = 0
     for t in range(params["max_steps"]):
         mc.denoise_step(canvas, lg[t % 2], prev, prev_st, top_k=top_k if prev is not None else 0)
         binding.sample_update(params, t, lg[t % 2], canvas, argmax, lock, st[t % 2], stop, ws)
-        if stop.item():
-            my_steps = t + 1
+        last = t
+        s_ = stop.cpu().tolist()
+        for b in range(B):
+            if my_steps[b] == 0 and s_[b]:
+                my_steps[b] = t + 1
+        if all(s_):
             break
         prev, prev_st = lg[t % 2], st[t % 2]
     mc.commit_block(argmax)
     torch.cuda.synchronize()
-    assert steps == [my_steps] == [48]
+    assert steps == my_steps == [48] * B
     assert torch.equal(block, argmax)
     K2 = mc.kv_tensors()
     L = P + N
     assert torch.equal(K1[0][..., :L, :], K2[0][..., :L, :])
     assert torch.equal(K1[1][..., :L, :], K2[1][..., :L, :])
-    assert torch.isfinite(lg[(my_steps - 1) % 2]).all()
+    assert torch.isfinite(lg[last % 2]).all()
