@@ -196,15 +196,16 @@ KERNEL_SOURCE = {"head_gemm": "gemm_dma.hip", "selfcond_gemm": "gemm_dma.hip",
                  "sampler": "sampler.hip"}
 
 
-def measured_traffic(name, config):
+def measured_traffic(name, config, source=None):
     """HBM bytes per launch of `name` from the committed counter summary
     profiles/traffic_<name>_<config>.txt (FETCH_SIZE and WRITE_SIZE runs,
     each scaled by the same counter on a 1 GiB copy), or None when there is
-    no summary or the kernel's source has changed since it was taken."""
+    no summary or the kernel's source (`source`, else the timer's usual
+    file) has changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{name}_{config}.txt")
     src = os.path.join(ROOT, "discrete_text_diffusion_denoise_amd", "csrc",
-                       KERNEL_SOURCE.get(name, ""))
+                       source or KERNEL_SOURCE.get(name, ""))
     if not os.path.exists(path) or not os.path.isfile(src):
         return None, None
     vals = {}
@@ -216,6 +217,17 @@ def measured_traffic(name, config):
     if vals.get("source_sha256") != digest or "traffic_bytes" not in vals:
         return None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
     return float(vals["traffic_bytes"]), os.path.relpath(path, ROOT)
+
+
+def copy_probe(torch):
+    """Two 1 GiB device-to-device copies: the calibration of the HBM byte
+    counters (a copy's bytes are known)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(cfg, W, prompt, canvas, params, torch):
@@ -371,7 +383,12 @@ def bench_ar(args):
     P_mean = P - 1 + n_new // 2
     roof = roofline(dominant, dom_ms / dom_n, acfg, B, P_mean, 1)
     roof["timed_launches"] = dom_n
-    roof["traffic"], roof["traffic_source"] = None, None
+    # up to 16 new tokens the head runs as the few-row decode kernel
+    if dominant == "head_gemm" and B <= 16:
+        roof["traffic"], roof["traffic_source"] = measured_traffic(
+            dominant, f"ar_b{B}_{args.config}", source="gemm_decode.hip")
+    else:
+        roof["traffic"], roof["traffic_source"] = None, None
     per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], acfg, B,
                                                                   P_mean, 1).items()
                                        if k in ("bound", "achieved", "unit", "frac")}
@@ -401,6 +418,8 @@ def bench_ar(args):
         "kernels": per_kernel,
         "roofline": roof,
     }
+    if args.copy_probe:
+        copy_probe(torch)
     oracle_fits = cfg["n_layers"] == 1 and P <= 4096
     if args.no_cpu_baseline or not oracle_fits:
         out_json["cpu_baseline"] = None
@@ -690,12 +709,7 @@ def main():
         "roofline": roof,
     }
     if args.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch)
     oracle_fits = cfg["n_layers"] == 1 and B == 1 and P <= 4096
     if not args.no_cpu_baseline and not oracle_fits:
         # the float64 oracle's prompt encode alone would run for many minutes

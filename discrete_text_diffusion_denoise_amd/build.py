@@ -20,8 +20,8 @@ LIB = os.path.join(PKG, "libdg.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "gemm_dma.hip", "gemm_stream.hip", "attention.hip", "moe.hip", "elementwise.hip",
-           "sampler.hip", "quant.hip", "dg_api.cpp"]
+SOURCES = ["gemm.hip", "gemm_dma.hip", "gemm_decode.hip", "gemm_stream.hip", "attention.hip",
+           "moe.hip", "elementwise.hip", "sampler.hip", "quant.hip", "dg_api.cpp"]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",

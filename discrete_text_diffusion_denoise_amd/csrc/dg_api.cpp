@@ -593,6 +593,8 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     if (sizeof(T) == 2 && use_stream_wide() && !g.a_tiled)
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
                      [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));
+    else if (g.a_tiled && dg::gemm_decode_ok(g) && env_flag("DG_DECODE_HEAD", 1))
+        DG_HIP(timed(DG_TIMER_HEAD_GEMM, st, [&] { return dg::gemm_decode(g, st); }));
     else
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
                      [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_STORE_F32, 1, st); }));

@@ -26,39 +26,17 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_ring.h"
 
 namespace dg {
 
 namespace {
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 32;                 // bf16 per row per stage (64 bytes)
 constexpr int WAVES = 8;               // arranged 2 (rows) x 4 (columns)
 constexpr int STAGE_BYTES = BM * BK * 2;   // one operand's stage: 16 KiB
-
-// chunk slot of (row r, chunk c) within its 64-byte LDS row
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// vmcnt(n): wait until at most n vector-memory operations of this wave are
-// outstanding; lgkm and exp counters are left alone.
-#define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
-
-// Barrier that only waits for this wave's LDS traffic: the direct-to-LDS
-// loads of later stages stay in flight across it.
-__device__ __forceinline__ void barrier_lds() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-}
 
 // BPOL: cache-policy bits of the B operand's loads (2 = non-temporal)
 template <int EPI, int TA, int TB, int BPOL = 0>

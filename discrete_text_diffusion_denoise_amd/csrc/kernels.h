@@ -77,6 +77,10 @@ hipError_t gemm_tn(const GemmArgs& g, int amode, int epi, int splits, hipStream_
 // four-stage ring (256 x 256 tiles).  gemm_dma_ok says whether the operands
 // meet its conditions: K and k_split multiples of 128, 16-byte aligned rows,
 // no row gather.
+// Decode-step head: M <= 16 rows (A and B blocked, K <= 2048, N % 256 == 0),
+// EPI_STORE_F32, optional 64-column slab maxima (rowmax)
+bool gemm_decode_ok(const GemmArgs& g);
+hipError_t gemm_decode(const GemmArgs& g, hipStream_t st);
 bool gemm_dma_ok(const GemmArgs& g, int epi);
 hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st);
 // Skinny ring kernel (256 x 64 tiles, row-major bf16 operands, segmented B

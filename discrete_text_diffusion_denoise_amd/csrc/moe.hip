@@ -11,6 +11,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_ring.h"
 
 namespace dg {
 
@@ -299,18 +300,6 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
 // slot c ^ (r & 7), which keeps the fragment reads free of bank conflicts.
 // Fragment reads are one asm block per stage ending in its own
 // lgkmcnt(0) (the ring order already guarantees their loads have landed).
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
-#define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
-__device__ __forceinline__ void barrier_lds() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-}
 
 // One expert's token groups against one block of weight rows: a four-stage
 // ring of direct-to-LDS loads (8 KiB of weight rows x 64 k and 32 * G token
@@ -349,9 +338,6 @@ __device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t w, float scale) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
 }
-
-// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // FMT: 0 bf16 weights, 1 E4M3 codes with per-row scales, 2 MXFP4 (E2M1 codes,
 // an E8M0 scale per 32 k)
@@ -503,10 +489,10 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             } else if (F8) {                                                                             \
                 const int wr0 = ct * 16 + r16, wr1 = wr0 + 32;                                    \
                 const uint32_t wb_ = lds_addr(WB);                                                \
-                const uint32_t g0_ = wb_ + wr0 * 64 + ((g4 ^ swz4(wr0)) << 4);                    \
-                const uint32_t g1_ = wb_ + wr1 * 64 + ((g4 ^ swz4(wr1)) << 4);                    \
-                const uint32_t u0_ = wb_ + (wr0 + 64) * 64 + ((g4 ^ swz4(wr0 + 64)) << 4);        \
-                const uint32_t u1_ = wb_ + (wr1 + 64) * 64 + ((g4 ^ swz4(wr1 + 64)) << 4);        \
+                const uint32_t g0_ = wb_ + wr0 * 64 + ((g4 ^ swz(wr0)) << 4);                    \
+                const uint32_t g1_ = wb_ + wr1 * 64 + ((g4 ^ swz(wr1)) << 4);                    \
+                const uint32_t u0_ = wb_ + (wr0 + 64) * 64 + ((g4 ^ swz(wr0 + 64)) << 4);        \
+                const uint32_t u1_ = wb_ + (wr1 + 64) * 64 + ((g4 ^ swz(wr1 + 64)) << 4);        \
                 u32x4 cg0, cg1, cu0, cu1;                                                         \
                 if (G == 1) {                                                                     \
                     asm volatile(                                                                 \
@@ -695,12 +681,12 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
                         (((c.lane & 1) ^ ((r >> 3) & 1)) << 4);
         } else if (F8) {
             // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
-            // takes row l / 4 and global chunk (l % 4) ^ swz4(row)
+            // takes row l / 4 and global chunk (l % 4) ^ swz(row)
             const int r = (c.wave * 2 + q) * 16 + (c.lane >> 2);   // row within the block
             const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
             const int col = min(c.c0 + rr, c.NOUT - 1);
             const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
-            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz4(r)) << 4);
+            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz(r)) << 4);
         } else {
             const int r = (c.wave * 2 + q) * 8 + c.lr;             // row within the block
             const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
