@@ -28,8 +28,10 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // XOR swizzle of the four 16-byte chunks of a 64-byte LDS row: chunk c of
-// row r sits in slot c ^ swz(r), so that a fragment read (16 rows, one
-// chunk per group of 16 lanes) touches distinct banks
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// row r sits in slot c ^ swz(r).  A fragment read (ds_read_b128; lane l
+// reads row l % 16, chunk l / 16) then runs at the rate of a linear 1 KiB
+// read: measured on gfx950, 4.5 LDS cycles per instruction and CU against
+// 8.4 unswizzled, and 8.4 as well with (r >> 3) also folded in.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
 }  // namespace dg
