@@ -201,7 +201,8 @@ def measured_traffic(name, config, source=None):
     profiles/traffic_<name>_<config>.txt (FETCH_SIZE and WRITE_SIZE runs,
     each scaled by the same counter on a 1 GiB copy), or None when there is
     no summary or the kernel's source (`source`, else the timer's usual
-    file) has changed since it was taken."""
+    file, and the header the summary names) has changed since it was
+    taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{name}_{config}.txt")
     src = os.path.join(ROOT, "discrete_text_diffusion_denoise_amd", "csrc",
@@ -214,7 +215,13 @@ def measured_traffic(name, config, source=None):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if vals.get("source_sha256") != digest or "traffic_bytes" not in vals:
+    stale = vals.get("source_sha256") != digest or "traffic_bytes" not in vals
+    if "header" in vals:
+        # a header the kernel's code comes from (the LDS ring helpers)
+        hdr = os.path.join(ROOT, vals["header"])
+        stale = stale or not os.path.isfile(hdr) or \
+            hashlib.sha256(open(hdr, "rb").read()).hexdigest() != vals.get("header_sha256")
+    if stale:
         return None, os.path.relpath(path, ROOT) + " (stale: kernel source changed)"
     return float(vals["traffic_bytes"]), os.path.relpath(path, ROOT)
 
