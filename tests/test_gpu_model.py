@@ -324,6 +324,27 @@ def test_stage_head_rowmax(T):
         mr.stage_head_rowmax(h[:200].contiguous(), lr, rr)
 
 
+@pytest.mark.parametrize("T", [1, 7, 16, 17, 130, 256, 300, 700])
+def test_blocked_head_row_counts(T):
+    """The blocked head at the row counts that pick its kernels: the few-row
+    decode-step kernel (T <= 16) and the persistent kernel with one, two and
+    three row tiles, ragged ones included.  Logits against the float64
+    oracle; slab maxima exactly the maxima of the returned logits."""
+    print(f"blocked head T={T}", flush=True)
+    # a 700-token canvas: the stage calls' workspace (one canvas) holds 768
+    # blocked rows
+    cfg, W, m = setup("vocab_bf16", 0, canvas=700)
+    V, d = cfg["vocab"], cfg["d_model"]
+    h = np.random.default_rng(100 + T).standard_normal((T, d)).astype(np.float32)
+    logits = torch.full((T, V), float("nan"), dtype=torch.float32, device=DEV)
+    rowmax = torch.full((T, V // 64), float("nan"), dtype=torch.float32, device=DEV)
+    m.stage_head_rowmax(to_dev(h), logits, rowmax)
+    torch.cuda.synchronize()
+    ref = om.head(h.astype(np.float64), synthetic.to_float64(W), cfg)
+    assert normwise(logits.cpu().numpy(), ref) <= tol_for(cfg)
+    assert torch.equal(rowmax, logits.view(T, V // 64, 64).amax(dim=-1))
+
+
 def test_commit_equals_encode_of_concatenation():
     cfg, W, m1 = setup("small_bf16", 50, batch=1)
     N, V = cfg["canvas"], cfg["vocab"]
