@@ -229,8 +229,20 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, const 
     const long total = (long)g.M * g.N;
     if (idx >= total) return;
     const int row = (int)(idx / g.N), col = (int)(idx % g.N);
+    // the partials are summed in split order; eight loads go out before
+    // their adds so that the sum waits for one load latency per eight splits
+    const float* pp = part + (long)row * g.N + col;
+    const long zs = (long)g.M * g.N;
     float v = 0.f;
-    for (int z = 0; z < splits; ++z) v += part[((long)z * g.M + row) * g.N + col];
+    int z = 0;
+    for (; z + 8 <= splits; z += 8) {
+        float p[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) p[q] = pp[(z + q) * zs];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v += p[q];
+    }
+    for (; z < splits; ++z) v += pp[z * zs];
     float* C = reinterpret_cast<float*>(g.C) + (long)row * g.ldc + col;
     if (epi == EPI_STORE_F32) {
         *C = v;
