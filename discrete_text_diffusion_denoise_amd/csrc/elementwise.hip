@@ -58,8 +58,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             const float* __restrict__ row_stats) {
     long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
+    // summed in split order, eight loads in flight before their adds
     float s = 0.f;
-    for (int z = 0; z < splits; ++z) s += part[(long)z * total + i];
+    int z = 0;
+    for (; z + 8 <= splits; z += 8) {
+        float p[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) p[q] = part[(long)(z + q) * total + i];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += p[q];
+    }
+    for (; z < splits; ++z) s += part[(long)z * total + i];
     if (row_stats) s = s * (1.0f / row_stats[(i / cols) * 4 + 1]);
     out[i] = Elt<T>::from_f(s);
 }
