@@ -1121,7 +1121,17 @@ __global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restri
     const float* rm = rowmax + row * (long)nslab;
     float bv = -INFINITY;
     int bs = 0x7FFFFFFF;
-    for (int sl = threadIdx.x; sl < nslab; sl += 256) amax_take(rm[sl], sl, bv, bs);
+    // eight slab maxima in flight per thread before they are compared (the
+    // (value, lowest index) maximum does not depend on the visiting order)
+    int sl = threadIdx.x;
+    for (; sl + 7 * 256 < nslab; sl += 8 * 256) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = rm[sl + q * 256];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) amax_take(v[q], sl + q * 256, bv, bs);
+    }
+    for (; sl < nslab; sl += 256) amax_take(rm[sl], sl, bv, bs);
     amax_block<256>(bv, bs);
     if (threadIdx.x < 64) {
         int idx = 0;
