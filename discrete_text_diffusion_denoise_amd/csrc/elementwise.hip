@@ -48,7 +48,17 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E,
     const long b = row / n, i = row % n;
     const int id = min(max(tok[b * ld + i], 0), V - 1);   // ids outside [0, V) never index past E
     const T* e = E + (long)id * d;
-    for (int i = threadIdx.x; i < d; i += 256) h[row * d + i] = Elt<T>::to_f(e[i]);
+    float* o = h + row * d;
+    // eight loads in flight before their stores
+    int k = threadIdx.x;
+    for (; k + 7 * 256 < d; k += 8 * 256) {
+        T v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = e[k + q * 256];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[k + q * 256] = Elt<T>::to_f(v[q]);
+    }
+    for (; k < d; k += 256) o[k] = Elt<T>::to_f(e[k]);
 }
 
 template <typename T>
