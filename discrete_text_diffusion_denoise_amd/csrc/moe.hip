@@ -837,6 +837,37 @@ __global__ __launch_bounds__(256) void combine_kernel(MoeArgs a) {
     }
 }
 
+// The same with the number of experts per token known at compile time: the
+// K expert rows' loads go out together, then the adds run in the same order
+// as above.
+template <int K>
+__global__ __launch_bounds__(256) void combine_k_kernel(MoeArgs a) {
+    const long t = blockIdx.x;
+    float gt[K];
+    long yo[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        gt[j] = a.gates[t * K + j];
+        yo[j] = (long)a.slot_of[t * K + j] * a.d;
+    }
+    float* hr = a.h + t * a.d;
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < min(a.d, (int)(blockIdx.y + 1) * 1024);
+         c += 1024) {
+        float4 y[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) y[j] = *reinterpret_cast<const float4*>(a.y + yo[j] + c);
+        float4 acc = *reinterpret_cast<const float4*>(hr + c);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            acc.x += gt[j] * y[j].x;
+            acc.y += gt[j] * y[j].y;
+            acc.z += gt[j] * y[j].z;
+            acc.w += gt[j] * y[j].w;
+        }
+        *reinterpret_cast<float4*>(hr + c) = acc;
+    }
+}
+
 }  // namespace
 
 hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
@@ -899,7 +930,15 @@ hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
 
 hipError_t moe_combine(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(a.T, cdiv(a.d, 1024)), dim3(256), 0, st, a);
+    const dim3 grid(a.T, cdiv(a.d, 1024));
+    if (a.k == 8)
+        hipLaunchKernelGGL(combine_k_kernel<8>, grid, dim3(256), 0, st, a);
+    else if (a.k == 4)
+        hipLaunchKernelGGL(combine_k_kernel<4>, grid, dim3(256), 0, st, a);
+    else if (a.k == 2)
+        hipLaunchKernelGGL(combine_k_kernel<2>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
