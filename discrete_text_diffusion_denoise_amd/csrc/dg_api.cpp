@@ -270,30 +270,6 @@ dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_
     return DG_OK;
 }
 
-// Integer environment knob (read once per name) for tile and schedule sweeps.
-int env_flag(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
-
-// DG_FUSE_PROBS=0 (for comparisons) keeps the separate probability pass in
-// the block loop.
-bool fuse_probs() {
-    static const int v = env_flag("DG_FUSE_PROBS", 1);
-    return v != 0;
-}
-
-// The vocabulary-sized products use the LDS-tiled GEMM unless DG_WIDE_TILE
-// selects one of the streaming shapes (values 0-4, for tile sweeps).
-bool use_stream_wide() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("DG_WIDE_TILE");
-        v = (e && atoi(e) <= 4) ? 1 : 0;
-    }
-    return v == 1;
-}
-
 // C (epi)= x W^T for x [M][K] (model dtype, or fp32 when T = float) and
 // W [N][K]: C fp32 [M][ldc].  bf16 uses the streaming GEMM, fp32 the LDS-tiled
 // one.  When the output has too few tiles to fill the chip, K is split and a
@@ -334,10 +310,7 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
     if (bf) {
         // canvas-size bf16 projection: skinny ring kernel over 256 x 64 tiles,
         // split over K into 128-multiples, then the ordered split-K pass
-        static const int target = [] {
-            const char* e = getenv("DG_SKINNY_WG");   // sweeps: workgroups to aim for
-            return e ? std::max(1, atoi(e)) : 192;
-        }();
+        constexpr int target = 192;   // workgroups to aim for
         dg::GemmArgs p = g;
         const long stiles = (long)cdiv(N, 64) * cdiv(M, 256);
         int sp = (int)std::min<long>(std::max<long>(1, cdiv(target, (int)stiles)),
@@ -468,7 +441,7 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.act = s.act;
     a.y = s.y;
     a.h = h;
-    a.k_rotate = env_flag("DG_KROT", 1);
+    a.k_rotate = 1;
     a.halt = s.halt;
     DG_HIP(dg::moe_route(a, st));
     DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
@@ -543,14 +516,10 @@ dg_status stage_input(dg_model* m, int B, const int32_t* canvas, const float* pr
         g.a_tiled = s.probs_tiled ? 2 : 0;
         g.b_tiled = m->blocked ? 1 : 0;
         g.xcd_group = (used % 8 == 0 && cdiv(c.d_model, 256) > 1) ? 1 : 0;
-        g.k_rotate = env_flag("DG_KROT", 1);
+        g.k_rotate = 1;
         g.halt = s.halt;
-        if (use_stream_wide() && !g.a_tiled)
-            DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
-                         [&] { return dg::gemm_stream(g, dg::EPI_SPLITK, 4, used, st); }));
-        else
-            DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
-                         [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_SPLITK, used, st); }));
+        DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
+                     [&] { return dg::gemm_tn<T>(g, 0, dg::EPI_SPLITK, used, st); }));
     } else {
         DG_HIP(timed(DG_TIMER_SELFCOND_GEMM, st,
                      [&] { return dg::gemm_tn<T>(g, 1, dg::EPI_SPLITK, used, st); }));
@@ -575,7 +544,7 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
     g.C = logits;
     g.ldc = c.vocab;
     g.k_split = c.d_model;
-    g.k_rotate = env_flag("DG_KROT", 1);
+    g.k_rotate = 1;
     g.halt = s.halt;
     if (m->blocked && m->embed_head && Tn <= s.ut_rows) {
         // both operands in the blocked layout: each stage of a tile is one
@@ -590,10 +559,7 @@ dg_status stage_head(dg_model* m, int Tn, const float* h, float* logits, Scratch
         g.A = s.u;
         g.lda = c.d_model;
     }
-    if (sizeof(T) == 2 && use_stream_wide() && !g.a_tiled)
-        DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
-                     [&] { return dg::gemm_stream(g, dg::EPI_STORE_F32, 4, 1, st); }));
-    else if (g.a_tiled && dg::gemm_decode_ok(g) && env_flag("DG_DECODE_HEAD", 1))
+    if (g.a_tiled && dg::gemm_decode_ok(g))
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st, [&] { return dg::gemm_decode(g, st); }));
     else
         DG_HIP(timed(DG_TIMER_HEAD_GEMM, st,
@@ -1269,7 +1235,7 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     // of round t while it reads round t's logits (the head GEMM supplies the
     // row maxima), so round t+1 skips the separate probability pass.  The
     // values are the same bits that pass would write.
-    s.fuse = p->selfcond_on && p->top_k == 0 && m->blocked && m->embed_head && fuse_probs();
+    s.fuse = p->selfcond_on && p->top_k == 0 && m->blocked && m->embed_head;
     s.topk = p->selfcond_on ? p->top_k : 0;
     s.want_rowmax = (s.fuse || p->top_k > 0) && m->blocked && m->embed_head;
     const float* prev = nullptr;

@@ -248,15 +248,6 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
-int wide_choice() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("DG_WIDE_TILE");
-        v = e ? atoi(e) : 6;
-    }
-    return v;
-}
-
 template <typename T, int AMODE, int EPI>
 hipError_t launch_sized(const GemmArgs& g, int splits, hipStream_t st) {
     // Pick the largest tile that still gives the chip enough workgroups.
@@ -269,9 +260,7 @@ hipError_t launch_sized(const GemmArgs& g, int splits, hipStream_t st) {
     }
     if (big >= 240) {
         // 256 x 256: eight waves of 128 x 64 (measured faster than four waves of
-        // 128 x 128, which halve LDS reads but have half the loads in flight);
-        // DG_WIDE_TILE=5 selects the four-wave shape for sweeps
-        if (wide_choice() == 5) return launch_cfg<T, 256, 256, 2, 2, AMODE, EPI>(g, splits, st);
+        // 128 x 128, which halve LDS reads but have half the loads in flight)
         return launch_cfg<T, 256, 256, 2, 4, AMODE, EPI>(g, splits, st);
     }
     if (med >= 200) return launch_cfg<T, 128, 128, 2, 2, AMODE, EPI>(g, splits, st);

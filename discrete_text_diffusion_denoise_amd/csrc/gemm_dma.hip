@@ -501,14 +501,6 @@ __global__ __launch_bounds__(256) void gemm_dma_skinny_kernel(GemmArgs g) {
 }  // namespace
 
 bool gemm_dma_ok(const GemmArgs& g, int epi) {
-    static int enabled = -1;
-    if (enabled < 0) {
-        const char* e = getenv("DG_DMA");
-        enabled = e ? atoi(e) : 1;
-    }
-    // DG_DMA=0 (sweeps) only turns the ring off for row-major operands:
-    // blocked operands exist for this kernel alone
-    if (!enabled && !g.a_tiled && !g.b_tiled) return false;
     if (epi != EPI_STORE_F32 && epi != EPI_SPLITK) return false;
     if (g.a_rows || g.M <= 0 || g.N <= 0) return false;
     if (g.rowmax && (epi != EPI_STORE_F32 || g.N % 64)) return false;
@@ -540,8 +532,7 @@ int cu_count() {
 
 hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st) {
     if (!gemm_dma_ok(g, epi)) return hipErrorInvalidValue;
-    static const int persist = getenv("DG_HEAD_PERSIST") ? atoi(getenv("DG_HEAD_PERSIST")) : 1;
-    if (persist && epi == EPI_STORE_F32 && g.a_tiled == 1 && g.b_tiled == 1 && splits == 1 &&
+    if (epi == EPI_STORE_F32 && g.a_tiled == 1 && g.b_tiled == 1 && splits == 1 &&
         g.N % BN == 0 && g.k_split >= g.K) {
         // one workgroup per CU (the ring fills 128 KiB of LDS), a whole
         // number per XCD, the row tiles of a column tile on one XCD
@@ -581,12 +572,7 @@ hipError_t gemm_dma_bf16(const GemmArgs& g, int epi, int splits, hipStream_t st)
 }
 
 bool gemm_skinny_ok(const GemmArgs& g) {
-    static int enabled = -1;
-    if (enabled < 0) {
-        const char* e = getenv("DG_DMA");
-        enabled = e ? atoi(e) : 1;
-    }
-    if (!enabled || g.a_rows || g.M <= 0 || g.N <= 0 || g.a_tiled || g.b_tiled) return false;
+    if (g.a_rows || g.M <= 0 || g.N <= 0 || g.a_tiled || g.b_tiled) return false;
     if (g.K % (4 * BK) || g.k_split % (4 * BK)) return false;
     if (g.lda % 8 || g.ldb % 8 || g.N % 4 || g.ldc % 4) return false;
     if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return false;

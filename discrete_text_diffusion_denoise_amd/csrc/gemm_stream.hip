@@ -184,27 +184,11 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Wide tile used for 256-row, many-column products (the head and the
-// self-conditioning product); DG_WIDE_TILE selects among the candidates.
-int wide_tile_choice() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("DG_WIDE_TILE");
-        v = e ? atoi(e) : 0;
-    }
-    return v;
-}
-
 template <int TM, int TN, int EPI>
 hipError_t launch(const GemmArgs& g, int splits, hipStream_t st) {
     if constexpr (TM == 16 && TN == 4) {
-        switch (wide_tile_choice()) {
-            case 1: return launch_cfg<16, 2, 2, 1, EPI>(g, splits, st);   // 256 x 128, 4 waves
-            case 2: return launch_cfg<8, 4, 2, 1, EPI>(g, splits, st);    // 128 x 256, 4 waves
-            case 3: return launch_cfg<8, 2, 2, 2, EPI>(g, splits, st);    // 256 x 128, 8 waves
-            case 4: return launch_cfg<16, 2, 1, 1, EPI>(g, splits, st);   // 256 x 128, k32 stages
-            default: return launch_cfg<8, 4, 2, 2, EPI>(g, splits, st);   // 256 x 256, 8 waves
-        }
+        // wide tile of 256-row, many-column products: 256 x 256, 8 waves
+        return launch_cfg<8, 4, 2, 2, EPI>(g, splits, st);
     } else {
         return launch_cfg<TM, TN, 2, 1, EPI>(g, splits, st);
     }

@@ -886,14 +886,7 @@ hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
 
 // the ring kernel needs whole rings of four 64-wide stages in both products
 bool expert_dma_ok(const MoeArgs& a) {
-    static int enabled = -1;
-    if (enabled < 0) {
-        const char* e = getenv("DG_DMA");
-        enabled = e ? atoi(e) : 1;
-    }
-    // DG_DMA=0 (sweeps) turns off the bf16 ring only: 8-bit experts run on
-    // the ring alone
-    return (enabled || a.f8 || a.f4) && a.d % 256 == 0 && a.F % 256 == 0;
+    return a.d % 256 == 0 && a.F % 256 == 0;
 }
 
 template <typename T>

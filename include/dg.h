@@ -168,8 +168,10 @@ void dg_model_destroy(dg_model* m);
  * 32 values; one stage of one tile (256 x 32 values, 16 KiB) is contiguous,
  * element (r, k) at ((r/256 * K/32 + k/32) * 256 + r%256) * 32 + k%32, with R
  * padded to a multiple of 256.  The vocabulary products stream their weight
- * one contiguous block per stage (youleyou.com article, "Deployment": the
- * step is bound by memory traffic, not arithmetic).
+ * one contiguous block per stage: at one canvas per call they are bound by
+ * that weight stream (this implementation's own measurement of the head: HBM
+ * traffic 1.03 x the algorithmic bytes, at AI 205 FLOP/B below the bf16
+ * ridge), so whole 1 KiB runs per wave instruction matter.
  *
  * Writes the self-conditioning operand E^T [d][V] from d_embed [V][d]: in the
  * blocked layout for blocked models, else row-major.  d_out holds
