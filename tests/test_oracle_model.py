@@ -282,3 +282,76 @@ def test_block_driver_random_model_runs_full_budget():
     block, steps = driver.generate_block(W, cfg, cache, p, block_index=0, B=2)
     assert steps.tolist() == [3, 3]
     assert cache.length == 5 + cfg["canvas"]
+
+
+def test_block_driver_one_canvas_stops_the_other_continues():
+    # Canvas 0 gets logits certain of a fixed sequence (round 0 locks it,
+    # round 1 finds the same most likely sequence and stops); canvas 1 gets
+    # flat-ish random logits and never stops.  Each canvas stops on its own
+    # (report-summary page, section 4), and a stopped canvas is left as it is.
+    cfg = tiny_cfg()
+    W = tiny_weights(cfg)
+    cache = model.KVCache(cfg, 2)
+    model.encode(synthetic.make_tokens(cfg["vocab"], (2, 5)), W, cfg, cache)
+    N, V = cfg["canvas"], cfg["vocab"]
+    target = synthetic.make_tokens(V, (N,), seed=43)
+    rng = np.random.default_rng(44)
+    seen = []
+
+    def hook(t, logits):
+        out = rng.standard_normal(logits.shape) * 0.3
+        out[0] = -50.0
+        out[0, np.arange(N), target] = 50.0
+        return out
+
+    def rec(t, canvas, argmax, lock, stats, stop):
+        seen.append((t, canvas.copy(), argmax.copy(), lock.copy(), stop.copy()))
+
+    p = synthetic.default_sampler_params(max_steps=6)
+    block, steps = driver.generate_block(W, cfg, cache, p, block_index=0, B=2, logits_hook=hook,
+                                         round_hook=rec)
+    assert steps.tolist() == [2, 6]
+    assert [s[0] for s in seen] == list(range(6))
+    assert (block[0] == target).all()
+    # canvas 0: every position locked to the certain token in rounds 0 and 1
+    assert seen[0][3][0].all() and (seen[0][1][0] == target).all()
+    # canvas 1: flat logits give no lock under the 0.1 entropy budget
+    assert not seen[0][3][1].any()
+    # after its stop (round 1) canvas 0 is frozen while canvas 1 moves on
+    for t in range(2, 6):
+        assert (seen[t][1][0] == seen[1][1][0]).all() and (seen[t][2][0] == seen[1][2][0]).all()
+        assert not (seen[t][1][1] == seen[t - 1][1][1]).all()
+    assert seen[1][4].tolist() == [1, 0] and seen[5][4].tolist() == [1, 1]
+    assert (block[1] == seen[5][2][1]).all()
+
+
+def test_block_driver_top1_selfcond_is_the_argmax_embedding():
+    # With top-k truncation at K = 1 the truncated distribution of a position
+    # is certain of its largest logit, so the next round's self-conditioning
+    # input must equal the full-distribution path fed with logits certain of
+    # that token (exp(-1e4) is exactly 0 in float64).
+    cfg = tiny_cfg(n_layers=1)
+    W = tiny_weights(cfg)
+    cache = model.KVCache(cfg, 1)
+    model.encode(synthetic.make_tokens(cfg["vocab"], (1, 5)), W, cfg, cache)
+    seen = {}
+
+    def hook(t, logits):
+        seen[t] = logits.copy()
+        return logits
+
+    def rec(t, canvas, argmax, lock, stats, stop):
+        seen[("canvas", t)] = canvas.copy()
+
+    p = synthetic.default_sampler_params(max_steps=2, top_k=1, require_stable=1)
+    driver.generate_block(W, cfg, cache.copy(), p, block_index=0, B=1, logits_hook=hook,
+                          round_hook=rec)
+    am0 = np.argmax(seen[0].astype(np.float32), axis=-1)
+    onehot = np.full(seen[0].shape, -1e4)
+    np.put_along_axis(onehot, am0[..., None], 0.0, axis=-1)
+    ref = model.denoise_step(seen[("canvas", 0)], W, cfg, cache, onehot, top_k=0)
+    assert np.allclose(seen[1], ref, rtol=0, atol=1e-12)
+    # and it is not the full distribution's self-conditioning
+    full = model.denoise_step(seen[("canvas", 0)], W, cfg, cache, seen[0].astype(np.float32)
+                              .astype(np.float64), top_k=0)
+    assert not np.allclose(seen[1], full, rtol=0, atol=1e-6)
