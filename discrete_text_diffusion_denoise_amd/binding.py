@@ -97,6 +97,7 @@ _SIGS = {
     "dg_generate_workspace_bytes": (_I, [_P, _I, _P]),
     "dg_generate_block": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     "dg_stage_input": (_I, [_P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_stage_input_topk": (_I, [_P, _I, _P, _P, _I, _P, _P, _SZ, _P]),
     "dg_stage_attention": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "dg_stage_moe": (_I, [_P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_stage_head": (_I, [_P, _I, _P, _P, _P, _SZ, _P]),
@@ -339,6 +340,12 @@ class Model:
         _check(lib().dg_stage_input(self.handle, canvas.shape[0], _ptr(canvas),
                                     _ptr(prev_logits), _ptr(prev_stats), _ptr(h), _ptr(self.ws),
                                     self.ws.numel(), _stream(stream)))
+
+    def stage_input_topk(self, canvas, h, prev_logits, top_k: int, stream=None):
+        """dg_stage_input_topk: the input stage with top_k-truncated self-conditioning."""
+        _check(lib().dg_stage_input_topk(self.handle, canvas.shape[0], _ptr(canvas),
+                                         _ptr(prev_logits), int(top_k), _ptr(h), _ptr(self.ws),
+                                         self.ws.numel(), _stream(stream)))
 
     def stage_attention(self, layer, h, n, causal, stream=None):
         _check(lib().dg_stage_attention(self.handle, self.kv, int(layer), self.batch, int(n),

@@ -1294,6 +1294,24 @@ dg_status dg_stage_input(dg_model* m, int32_t batch, const int32_t* d_canvas,
                               as_stream(stream));
 }
 
+dg_status dg_stage_input_topk(dg_model* m, int32_t batch, const int32_t* d_canvas,
+                              const float* d_prev_logits, int32_t top_k, float* d_h, void* d_ws,
+                              size_t ws_bytes, void* stream) {
+    DG_TRY(check_model(m));
+    if (!d_canvas || !d_h || !d_prev_logits || batch < 1) return fail(DG_ERR_ARG, "bad arguments");
+    if (top_k < 1 || top_k > dg::kTopKMax || top_k > m->c.vocab)
+        return fail(DG_ERR_ARG, "top_k %d outside [1, min(64, vocab)]", top_k);
+    Carver cv(d_ws, ws_bytes);
+    Scratch s;
+    DG_TRY(check_ws(m, batch, d_ws, ws_bytes, s, cv));
+    s.topk = top_k;
+    if (m->c.dtype == DG_BF16)
+        return stage_input<bf16_t>(m, batch, d_canvas, d_prev_logits, nullptr, d_h, s,
+                                   as_stream(stream));
+    return stage_input<float>(m, batch, d_canvas, d_prev_logits, nullptr, d_h, s,
+                              as_stream(stream));
+}
+
 dg_status dg_stage_attention(dg_model* m, dg_kv* kv, int32_t layer, int32_t batch, int32_t n,
                              int32_t causal, float* d_h, void* d_ws, size_t ws_bytes,
                              void* stream) {
@@ -1340,10 +1358,11 @@ dg_status dg_stage_head_rowmax(dg_model* m, int32_t T, const float* d_h, float* 
     if (!d_h || !d_logits || !d_rowmax || T < 1) return fail(DG_ERR_ARG, "bad arguments");
     if (!m->blocked || !m->embed_head)
         return fail(DG_ERR_UNSUPPORTED, "row maxima come from the blocked head (embed_head)");
+    const int nb = std::max(1, cdiv(T, m->c.canvas));
     Carver cv(d_ws, ws_bytes);
     Scratch s;
-    DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
-    if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
+    DG_TRY(check_ws(m, nb, d_ws, ws_bytes, s, cv));
+    if (T > token_budget(m, nb)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
     if (T > s.ut_rows) return fail(DG_ERR_CAPACITY, "T exceeds the head's blocked row budget %d", s.ut_rows);
     s.want_rowmax = true;
     s.tmax = d_rowmax;
@@ -1354,10 +1373,11 @@ dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logit
                         size_t ws_bytes, void* stream) {
     DG_TRY(check_model(m));
     if (!d_h || !d_logits || T < 1) return fail(DG_ERR_ARG, "bad arguments");
+    const int nb = std::max(1, cdiv(T, m->c.canvas));
     Carver cv(d_ws, ws_bytes);
     Scratch s;
-    DG_TRY(check_ws(m, 1, d_ws, ws_bytes, s, cv));
-    if (T > token_budget(m, 1)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
+    DG_TRY(check_ws(m, nb, d_ws, ws_bytes, s, cv));
+    if (T > token_budget(m, nb)) return fail(DG_ERR_CAPACITY, "T exceeds the workspace token budget");
     if (m->c.dtype == DG_BF16)
         return stage_head<bf16_t>(m, T, d_h, d_logits, s, as_stream(stream));
     return stage_head<float>(m, T, d_h, d_logits, s, as_stream(stream));

@@ -426,6 +426,13 @@ dg_status dg_train_forward(dg_model* m, dg_kv* kv, int32_t batch, const int32_t*
 dg_status dg_stage_input(dg_model* m, int32_t batch, const int32_t* d_canvas,
                          const float* d_prev_logits, const float* d_prev_stats, float* d_h,
                          void* d_ws, size_t ws_bytes, void* stream);
+/* dg_stage_input with the self-conditioning truncated to each position's
+ * top_k previous logits, as dg_denoise_step_topk computes it (report-summary
+ * page, section 9: top-k truncation): s = sum_i p_i E[c_i] over the top_k
+ * candidates.  1 <= top_k <= min(64, vocab) (DG_ERR_ARG otherwise). */
+dg_status dg_stage_input_topk(dg_model* m, int32_t batch, const int32_t* d_canvas,
+                              const float* d_prev_logits, int32_t top_k, float* d_h, void* d_ws,
+                              size_t ws_bytes, void* stream);
 /* Attention half-block of `layer` for n new tokens per sequence at positions
  * [len, len+n): RMSNorm, Q/K/V, RoPE, K/V written to cache slots [len, len+n),
  * attention (causal != 0: each query sees keys <= its position; causal == 0:
@@ -440,14 +447,16 @@ dg_status dg_stage_attention(dg_model* m, dg_kv* kv, int32_t layer, int32_t batc
  * d_gates [T][top_k] the gates. */
 dg_status dg_stage_moe(dg_model* m, int32_t layer, int32_t T, float* d_h, int32_t* d_route,
                        float* d_gates, void* d_ws, size_t ws_bytes, void* stream);
-/* Head: d_logits [T][V] = RMSNorm(d_h) E^T (fp32). */
+/* Head: d_logits [T][V] = RMSNorm(d_h) E^T (fp32), in the launch configuration
+ * a step over ceil(T / N) canvases uses; d_ws needs
+ * dg_workspace_bytes(ceil(T / N)) (DG_ERR_CAPACITY otherwise). */
 dg_status dg_stage_head(dg_model* m, int32_t T, const float* d_h, float* d_logits, void* d_ws,
                         size_t ws_bytes, void* stream);
 /* The head as the block loop runs it: dg_stage_head, and d_rowmax [T][V/64]
  * = the largest logit of each row in each 64-column slab, taken from the
  * product's registers before the logits are read again.  Blocked models with
- * weights.embed_head only (DG_ERR_UNSUPPORTED otherwise); T up to the canvas
- * tokens of the workspace's batch rounded up to 256 (DG_ERR_CAPACITY). */
+ * weights.embed_head only (DG_ERR_UNSUPPORTED otherwise); d_ws needs
+ * dg_workspace_bytes(ceil(T / N)) (DG_ERR_CAPACITY otherwise). */
 dg_status dg_stage_head_rowmax(dg_model* m, int32_t T, const float* d_h, float* d_logits,
                                float* d_rowmax, void* d_ws, size_t ws_bytes, void* stream);
 

@@ -1,10 +1,11 @@
 """Retained autoregressive mode on the GPU through the C ABI: the greedy
 choice bit-exact against numpy's argmax (ties to the lower index); decode
-steps after a prompt encode against the float64 oracle (logits and the KV
-cache, fp32 1e-4, bf16 2e-2; steps whose routing is within the GPU's
-precision of a tie are not compared); greedy generation bitwise equal to its
-own composition of decode steps and greedy choices; one decode step of the
-full-size layer (vocabulary 262144, prompt 2048) against the oracle."""
+steps after a prompt encode against the float64 oracle stage by stage on the
+GPU's own inputs (the MoE with the GPU's route set; fp32 1e-4, bf16 2e-2),
+every sequence, and for fp32 models also end to end against the oracle's own
+encode and decode; greedy generation bitwise equal to its own composition of
+decode steps and greedy choices; one decode step of the full-size layer
+(vocabulary 262144, prompt 2048) against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +13,8 @@ import torch
 from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import model as om
 
-from helpers import DEV, TOL_BF16, normwise, route_ambiguous, to_dev, tol_for
+import chain
+from helpers import DEV, TOL_BF16, TOL_F32, normwise, route_ambiguous, to_dev, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -88,15 +90,50 @@ def oracle_decode_with_gaps(tokens, W, cfg, cache, gap):
     return om.ar_decode_step(tokens, W, cfg, cache), amb
 
 
-# bf16 models decode through one layer here: with more, a prompt token whose
-# route the GPU's rounding flips (a near-tie) changes its later layers' K/V,
-# which every decoded token then reads; the last layer's K/V never depend on
-# a route.  Deeper bf16 stacks are covered by generate == composition.
-@pytest.mark.parametrize("name,P,B,layers", [("tiny", 20, 2, 2), ("small_bf16", 150, 3, 1),
-                                             ("f32_gqa", 33, 3, 2), ("small_fp8", 150, 3, 1),
+def decode_chain_check(m, cfg, W, tok, logits, tol, label):
+    """The decode step just taken (logits of tokens tok [B] at position L0 =
+    len - 1) run again as a chain of stage calls over the same cache, each
+    stage against the oracle on the GPU's own input to it (the MoE with the
+    GPU's route set); the chain's logits equal the step's bit for bit."""
+    L0 = m.kv_length - 1
+    m.set_kv_length(L0)
+    h = to_dev(np.asarray(W["embed"], np.float32)[tok])
+    for l, lw in enumerate(W["layers"]):
+        lw = chain.layer64(lw)
+        chain.check_attention(m, cfg, lw, l, h, 1, True, tol, label=label)
+        chain.check_moe(m, cfg, lw, l, h, tol, label=label)
+    Wh = {"embed": W["embed"], "final_norm": np.asarray(W["final_norm"], np.float64)}
+    lc = chain.check_head(m, cfg, Wh, h, tol, label=label)
+    assert torch.equal(lc, logits)
+    m.set_kv_length(L0 + 1)
+
+
+@pytest.mark.parametrize("name,P,B,layers", [("tiny", 20, 2, 2), ("small_bf16", 150, 3, 2),
+                                             ("f32_gqa", 33, 3, 2), ("small_fp8", 150, 3, 2),
                                              ("vocab_bf16", 64, 2, 1)])
 def test_ar_decode_steps_match_oracle(name, P, B, layers):
+    """Five decode steps after a prompt encode; each step against the oracle
+    stage by stage on the GPU's own inputs, every sequence."""
     print(f"ar decode {name} P={P} B={B} layers={layers}", flush=True)
+    steps = 5
+    cfg, W, m = setup(name, P + steps, B, n_layers=layers)
+    V = cfg["vocab"]
+    toks = synthetic.make_tokens(V, (B, P + steps - 1), seed=11)
+    m.encode_prompt(to_dev(toks[:, :P - 1]))
+    logits = torch.empty((B, V), dtype=torch.float32, device=DEV)
+    for t in range(steps):
+        tok = toks[:, P - 1 + t].copy()
+        m.ar_decode_step(to_dev(tok), logits)
+        torch.cuda.synchronize()
+        decode_chain_check(m, cfg, W, tok, logits, tol_for(cfg), f"ar {name} step {t}")
+    assert m.kv_length == P - 1 + steps
+
+
+@pytest.mark.parametrize("name,P,B,layers", [("tiny", 20, 2, 2), ("f32_gqa", 33, 3, 2)])
+def test_ar_decode_end_to_end_fp32(name, P, B, layers):
+    """fp32 models: decode steps and the cache against the oracle's own
+    encode and decode (its own routes); a decoded token within 1e-4 of a
+    router tie is not compared."""
     steps = 5
     cfg, W, m = setup(name, P + steps, B, n_layers=layers)
     W = synthetic.to_float64(W)
@@ -105,29 +142,24 @@ def test_ar_decode_steps_match_oracle(name, P, B, layers):
     m.encode_prompt(to_dev(toks[:, :P - 1]))
     cache = om.KVCache(cfg, B)
     om.encode(toks[:, :P - 1], W, cfg, cache)
-    gap = route_gap(cfg, chained=True)
     logits = torch.empty((B, V), dtype=torch.float32, device=DEV)
-    checked = 0
+    skipped = 0
     for t in range(steps):
         tok = toks[:, P - 1 + t].copy()
         m.ar_decode_step(to_dev(tok), logits)
-        # a token whose route is within the GPU's precision of a tie is not
-        # compared (with one layer its route feeds no K/V)
-        ref, amb = oracle_decode_with_gaps(tok, W, cfg, cache, gap)
+        ref, amb = oracle_decode_with_gaps(tok, W, cfg, cache, route_gap(cfg))
         got = logits.cpu().numpy()
+        skipped += int(amb.sum())
         for b in np.flatnonzero(~amb):
             err = normwise(got[b], ref[b])
-            assert err <= tol_for(cfg), f"step {t} seq {b}: {err:.3e}"
-            checked += 1
-    print(f"compared {checked} of {steps * B} decoded tokens", flush=True)
-    assert checked >= (steps * B) // 4
-    # the cache holds every decoded token's K/V
+            assert err <= TOL_F32, f"step {t} seq {b}: {err:.3e}"
+    assert skipped <= 1
     K, Vc = m.kv_tensors()
     L = P - 1 + steps
     for li in range(layers):
         for b in range(B):
-            assert normwise(K[li, b, :, :L].float().cpu().numpy(), cache.k[li][b]) <= tol_for(cfg)
-            assert normwise(Vc[li, b, :, :L].float().cpu().numpy(), cache.v[li][b]) <= tol_for(cfg)
+            assert normwise(K[li, b, :, :L].float().cpu().numpy(), cache.k[li][b]) <= TOL_F32
+            assert normwise(Vc[li, b, :, :L].float().cpu().numpy(), cache.v[li][b]) <= TOL_F32
 
 
 def test_ar_decode_rejects_full_cache():
@@ -180,6 +212,9 @@ def test_ar_generate_equals_composition(name, P, B, n_new):
 
 
 def test_ar_decode_full_layer():
+    """One decode step of four sequences through the full-size layer
+    (vocabulary 262144, prompt 2048), each stage against the oracle on the
+    GPU's own inputs, every sequence and logit."""
     cfg = synthetic.model_config("layer")
     P, V = synthetic.SHAPES["layer"]["prompt"], cfg["vocab"]
     B = 4
@@ -191,20 +226,4 @@ def test_ar_decode_full_layer():
     logits = torch.empty((B, V), dtype=torch.float32, device=DEV)
     m.ar_decode_step(to_dev(toks[:, P].copy()), logits)
     torch.cuda.synchronize()
-    got = logits.cpu().numpy()
-    del m
-    torch.cuda.empty_cache()
-    print("oracle encode + decode", flush=True)
-    lw = {k: np.asarray(v, dtype=np.float64) if k.endswith("norm") or k in ("wq", "wk", "wv", "wo")
-          else v for k, v in W["layers"][0].items()}
-    Wk = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"], "layers": [lw]}
-    cache = om.KVCache(cfg, B)
-    om.encode(toks[:, :P], Wk, cfg, cache)
-    ref, amb = oracle_decode_with_gaps(toks[:, P].copy(), Wk, cfg, cache,
-                                       route_gap(cfg, chained=True))
-    # a token whose route is within bf16 precision of a tie is not compared
-    assert (~amb).any()
-    for b in np.flatnonzero(~amb):
-        err = normwise(got[b], ref[b])
-        print(f"full-layer decode, sequence {b}: normwise error {err:.3e}", flush=True)
-        assert err <= TOL_BF16
+    decode_chain_check(m, cfg, W, toks[:, P].copy(), logits, TOL_BF16, "ar full layer")

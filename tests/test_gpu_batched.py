@@ -3,10 +3,14 @@ prompts each through one full-size denoiser layer (d 2048, 16 query / 4 KV
 heads x 128, 128 experts top-8, d_ff 768, vocabulary 262144, bf16), with the
 self-conditioning truncated to each position's 64 largest previous logits
 (the high-batch sampler setting), in the launch configuration the benchmark's
-batched workload times.  Two canvases, one at each end of the batch, are
-checked against the float64 oracle: their slices of the KV cache, and the
-logits of sampled positions.  Every canvas of the batch runs in the same
-launches, so a canvas that reads another's rows or cache would show here."""
+batched workload times.  The step runs as a chain of its stage calls (equal
+to dg_denoise_step_topk bit for bit) and the oracle recomputes each stage
+from the GPU's own input to it: the attention of all eight canvases, the MoE
+of all 2048 tokens with the GPU's route set, and the input and the head of
+the canvases at both ends of the batch, every position and logit.  Their
+prompt KV caches are compared with the oracle's own encode.  Every canvas of
+the batch runs in the same launches, so a canvas that reads another's rows or
+cache would show here."""
 import numpy as np
 import pytest
 import torch
@@ -14,14 +18,13 @@ import torch
 from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import model as om
 
-from helpers import DEV, TOL_BF16, normwise, route_ambiguous, to_dev
+import chain
+from helpers import DEV, TOL_BF16, normwise, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-CHECKED = (0, 7)       # canvases compared with the oracle
-SAMPLE_ROWS = 16       # positions per checked canvas
+CHECKED = (0, 7)       # canvases whose input and head are compared with the oracle
 TOP_K = 64
-ROUTE_GAP = 3e-2       # see route_gap() in test_gpu_model.py
 
 
 @pytest.fixture(scope="module")
@@ -46,52 +49,45 @@ def batched_run():
     m.denoise_step(to_dev(canvas), logits, prev, None, top_k=TOP_K)
     torch.cuda.synchronize()
     K, Vc = m.kv_tensors()
-    out = dict(cfg=cfg, W=W, prompt=prompt, canvas=canvas, prev=prev_host, P=P,
-               logits={b: logits[b].cpu().numpy() for b in CHECKED},
+    lw = chain.layer64(W["layers"][0])
+    Wk = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"], "layers": [lw]}
+    out = dict(cfg=cfg, W=W, Wk=Wk, m=m, prompt=prompt, canvas=canvas, prev=prev,
+               prev_host=prev_host, P=P, logits=logits,
                K={b: K[0, b, :, :P].float().cpu().numpy() for b in CHECKED},
-               V={b: Vc[0, b, :, :P].float().cpu().numpy() for b in CHECKED},
-               finite=bool(torch.isfinite(logits).all().item()))
-    del m, logits, prev
+               V={b: Vc[0, b, :, :P].float().cpu().numpy() for b in CHECKED})
+    yield out
+    del out["m"], out["logits"], out["prev"]
     torch.cuda.empty_cache()
-    lw = {k: np.asarray(v, dtype=np.float64) if k.endswith("norm") or k in ("wq", "wk", "wv", "wo")
-          else v for k, v in W["layers"][0].items()}
-    out["Wk"] = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"],
-                 "layers": [lw]}
-    out["cache"] = {}
-    for b in CHECKED:
-        print(f"oracle encode of canvas {b}'s prompt", flush=True)
-        cache = om.KVCache(cfg, 1)
-        om.encode(prompt[b:b + 1], out["Wk"], cfg, cache)
-        out["cache"][b] = cache
-    return out
 
 
 @pytest.mark.parametrize("b", CHECKED)
 def test_batched_prompt_kv(batched_run, b):
+    """Layer 0's K/V depend on no route: every prompt position is compared."""
     r = batched_run
-    c = r["cache"][b]
-    assert normwise(r["K"][b], c.k[0][0]) <= TOL_BF16
-    assert normwise(r["V"][b], c.v[0][0]) <= TOL_BF16
+    print(f"oracle encode of canvas {b}'s prompt", flush=True)
+    cache = om.KVCache(r["cfg"], 1)
+    om.encode(r["prompt"][b:b + 1], r["Wk"], r["cfg"], cache)
+    assert normwise(r["K"][b], cache.k[0][0]) <= TOL_BF16
+    assert normwise(r["V"][b], cache.v[0][0]) <= TOL_BF16
 
 
-@pytest.mark.parametrize("b", CHECKED)
-def test_batched_topk_selfcond_step_sampled_rows(batched_run, b):
+def test_batched_topk_selfcond_stage_chain(batched_run):
     r = batched_run
-    assert r["finite"]
-    cfg, Wk, cache = r["cfg"], r["Wk"], r["cache"][b]
-    P = cache.length
-    print(f"oracle step, canvas {b}", flush=True)
-    h = om.denoiser_input(r["canvas"][b], Wk, r["prev"][b], TOP_K)
+    cfg, Wk, m = r["cfg"], r["Wk"], r["m"]
+    B, N, d = m.batch, cfg["canvas"], cfg["d_model"]
+    h = torch.empty((B * N, d), dtype=torch.float32, device=DEV)
+    m.stage_input_topk(to_dev(r["canvas"]), h, r["prev"], TOP_K)
+    torch.cuda.synchronize()
+    hh = h.cpu().numpy()
+    for b in CHECKED:
+        print(f"oracle top-{TOP_K} input, canvas {b}", flush=True)
+        ref = om.denoiser_input(r["canvas"][b], Wk, r["prev_host"][b], TOP_K)
+        err = normwise(hh[b * N:(b + 1) * N], ref)
+        print(f"input canvas {b}: {err:.3e}", flush=True)
+        assert err <= TOL_BF16
     lw = Wk["layers"][0]
-    h, _, _ = om.attn_half(h, lw, cfg, cache.k[0][0], cache.v[0][0], P, causal=False)
-    u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
-    amb = route_ambiguous(u @ np.asarray(lw["w_router"], np.float64).T, cfg["top_k"], ROUTE_GAP)
-    h, _, _, _ = om.moe_half(h, lw, cfg)
-    rows = np.flatnonzero(~amb)
-    rows = rows[np.linspace(0, rows.size - 1, SAMPLE_ROWS).astype(int)]
-    ref = om.head(h[rows], Wk, cfg)
-    got = r["logits"][b][rows]
-    err = normwise(got, ref)
-    print(f"canvas {b}: sampled-row normwise error {err:.3e}; near-tie rows {amb.sum()}",
-          flush=True)
-    assert err <= TOL_BF16
+    chain.check_attention(m, cfg, lw, 0, h, N, False, TOL_BF16, label="batched")
+    chain.check_moe(m, cfg, lw, 0, h, TOL_BF16, label="batched")
+    rows = np.concatenate([np.arange(b * N, (b + 1) * N) for b in CHECKED])
+    lc = chain.check_head(m, cfg, Wk, h, TOL_BF16, label="batched", rows=rows)
+    assert torch.equal(lc.view(B, N, -1), r["logits"])

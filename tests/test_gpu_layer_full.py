@@ -1,8 +1,11 @@
 """Full-size single denoiser layer (d 2048, 16 query / 4 KV heads x 128, 128
 experts top-8, d_ff 768, vocabulary 262144, prompt 2048, canvas 256, bf16) in
 the same launch configuration the benchmark times, against the float64
-oracle on sampled canvas positions: KV cache of the prompt encode, and the
-logits of a self-conditioned denoising step."""
+oracle: the KV cache of the prompt encode at every position, and a
+self-conditioned denoising step as a chain of its stages (the oracle fed the
+GPU's own input to each stage and its route set), every position and every
+logit; the chain equals dg_denoise_step bit for bit.  Also the block loop at
+full size against its call-by-call composition."""
 import numpy as np
 import pytest
 import torch
@@ -11,12 +14,10 @@ from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import model as om
 from oracle import sampler as osampler
 
-from helpers import DEV, TOL_BF16, normwise, route_ambiguous, to_dev
+import chain
+from helpers import DEV, TOL_BF16, normwise, to_dev
 
 pytestmark = pytest.mark.gpu
-
-SAMPLE_ROWS = 24
-ROUTE_GAP = 3e-2   # see route_gap() in test_gpu_model.py
 
 
 @pytest.fixture(scope="module")
@@ -35,47 +36,45 @@ def layer_run():
     m.denoise_step(to_dev(canvas), logits, to_dev(prev), to_dev(stats))
     torch.cuda.synchronize()
     K, Vc = m.kv_tensors()
-    out = dict(cfg=cfg, W=W, prompt=prompt, canvas=canvas, prev=prev,
-               logits=logits.cpu().numpy()[0], K=K[0, 0, :, :P].float().cpu().numpy(),
+    out = dict(cfg=cfg, W=W, m=m, prompt=prompt, canvas=canvas, prev=prev, stats=stats,
+               logits=logits, K=K[0, 0, :, :P].float().cpu().numpy(),
                V=Vc[0, 0, :, :P].float().cpu().numpy())
-    del m, logits
-    torch.cuda.empty_cache()
     print("oracle encode", flush=True)
-    lw = {k: np.asarray(v, dtype=np.float64) if k.endswith("norm") or k in ("wq", "wk", "wv", "wo")
-          else v for k, v in W["layers"][0].items()}
-    cache = om.KVCache(cfg, 1)
+    lw = chain.layer64(W["layers"][0])
     Wk = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"], "layers": [lw]}
+    cache = om.KVCache(cfg, 1)
     om.encode(prompt, Wk, cfg, cache)
     out["cache"] = cache
     out["Wk"] = Wk
-    return out
+    yield out
+    del out["m"], out["logits"]
+    torch.cuda.empty_cache()
 
 
 def test_full_layer_prompt_kv(layer_run):
+    """Layer 0's K/V depend on no route: every prompt position is compared."""
     r = layer_run
     assert normwise(r["K"], r["cache"].k[0][0]) <= TOL_BF16
     assert normwise(r["V"], r["cache"].v[0][0]) <= TOL_BF16
 
 
-def test_full_layer_selfcond_step_sampled_rows(layer_run):
+def test_full_layer_stage_chain(layer_run):
     r = layer_run
-    cfg, Wk, cache = r["cfg"], r["Wk"], r["cache"]
-    P = cache.length
-    print("oracle step", flush=True)
-    h = om.denoiser_input(r["canvas"][0], Wk, r["prev"][0])
-    lw = Wk["layers"][0]
-    h, _, _ = om.attn_half(h, lw, cfg, cache.k[0][0], cache.v[0][0], P, causal=False)
-    u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
-    amb = route_ambiguous(u @ np.asarray(lw["w_router"], np.float64).T, cfg["top_k"], ROUTE_GAP)
-    h, _, _, _ = om.moe_half(h, lw, cfg)
-    rows = np.flatnonzero(~amb)
-    rows = rows[np.linspace(0, rows.size - 1, SAMPLE_ROWS).astype(int)]
-    ref = om.head(h[rows], Wk, cfg)
-    got = r["logits"][rows]
-    err = normwise(got, ref)
-    print(f"sampled-row normwise error {err:.3e}; near-tie rows {amb.sum()}", flush=True)
+    cfg, Wk, m = r["cfg"], r["Wk"], r["m"]
+    N, d = cfg["canvas"], cfg["d_model"]
+    h = torch.empty((N, d), dtype=torch.float32, device=DEV)
+    m.stage_input(to_dev(r["canvas"]), h, to_dev(r["prev"]), to_dev(r["stats"]))
+    torch.cuda.synchronize()
+    print("oracle input", flush=True)
+    ref_in = om.denoiser_input(r["canvas"][0], Wk, r["prev"][0])
+    err = normwise(h.cpu().numpy(), ref_in)
+    print(f"input: {err:.3e}", flush=True)
     assert err <= TOL_BF16
-    assert np.isfinite(r["logits"]).all()
+    lw = Wk["layers"][0]
+    chain.check_attention(m, cfg, lw, 0, h, N, False, TOL_BF16, label="layer")
+    chain.check_moe(m, cfg, lw, 0, h, TOL_BF16, label="layer")
+    lc = chain.check_head(m, cfg, Wk, h, TOL_BF16, label="layer")
+    assert torch.equal(lc.view(1, N, -1), r["logits"])
 
 
 def gpu_weights(cfg, seed):
