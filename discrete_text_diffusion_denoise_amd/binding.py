@@ -82,6 +82,7 @@ _SIGS = {
     "dg_denoise_step": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_denoise_step_topk": (_I, [_P, _P, _I, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "dg_sample_update": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_sample_update_static": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "dg_sample_update_probs": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                     _SZ, _P]),
     "dg_stage_probs": (_I, [_I, _I, _I, _P, _P, _P, _P]),
@@ -384,6 +385,17 @@ def sample_update(params: dict, step: int, logits, canvas, argmax, lock, stats, 
     _check(lib().dg_sample_update(ctypes.byref(sp), int(step), B, N, V, _ptr(logits),
                                   _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats), _ptr(stop),
                                   _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def sample_update_static(params: dict, step: int, logits, canvas, argmax, lock, stats, stop,
+                         stream=None):
+    """dg_sample_update_static: sample_update with the library's static scratch
+    (no workspace; batch * canvas <= 65536)."""
+    B, N, V = logits.shape
+    sp = sampler_params(params)
+    _check(lib().dg_sample_update_static(ctypes.byref(sp), int(step), B, N, V, _ptr(logits),
+                                         _ptr(canvas), _ptr(argmax), _ptr(lock), _ptr(stats),
+                                         _ptr(stop), _stream(stream)))
 
 
 def sample_update_probs(params: dict, step: int, logits, canvas, argmax, lock, stats, stop,

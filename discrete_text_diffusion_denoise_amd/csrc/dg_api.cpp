@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -624,6 +625,44 @@ hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 }  // namespace
 
+// ---- dg_sample_update_static: the sampler's scratch in a static device array
+//
+// For callers that cannot allocate device memory.  The scratch of
+// dg_sample_update (drawn tokens, renoise tokens and the new argmax, one
+// int32 each per row, every one written by the row pass before the canvas
+// pass reads it, so nothing needs clearing) lives in `scratch`, one copy per
+// GPU for the life of the process.  Host code never passes `scratch` itself
+// (that is a host-side stand-in, not a device address): the device address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address goes to the kernels.
+constexpr int kStaticSamplerRows = 65536;   // batch * canvas at most
+constexpr size_t kStaticSamplerBytes =
+    3 * (((size_t)kStaticSamplerRows * 4 + 255) & ~(size_t)255) + 256;
+static __device__ __align__(256) unsigned char scratch[kStaticSamplerBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's `scratch` (looked up on first use).
+dg_status static_scratch(void** out) {
+    int dev = 0;
+    DG_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        DG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(DG_ERR_HIP, "no device address for the sampler scratch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DG_OK;
+}
+}  // namespace
+
 // ======================================================================= API
 
 extern "C" {
@@ -1032,7 +1071,7 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              int32_t* halt = nullptr, const float* rowmax = nullptr,
                              void* probs = nullptr, int probs_tiled = 1,
                              int32_t* host_stop = nullptr, int32_t* tk_idx = nullptr,
-                             float* tk_p = nullptr) {
+                             float* tk_p = nullptr, bool untimed = false) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
@@ -1096,8 +1135,24 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
         a.tk_idx = tk_idx;
         a.tk_p = tk_p;
     }
-    DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
+    if (untimed) DG_HIP(dg::sample_update(a, st));
+    else DG_HIP(timed(DG_TIMER_SAMPLER, st, [&] { return dg::sample_update(a, st); }));
     return DG_OK;
+}
+
+dg_status dg_sample_update_static(const dg_sampler_params* p, int32_t step, int32_t batch,
+                                  int32_t canvas, int32_t vocab, const float* d_logits,
+                                  int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                                  float* d_stats, int32_t* d_stop, void* stream) {
+    if (batch < 1 || canvas < 1) return fail(DG_ERR_SHAPE, "need batch >= 1 and canvas >= 1");
+    if ((long)batch * canvas > kStaticSamplerRows)
+        return fail(DG_ERR_CAPACITY, "batch * canvas = %ld exceeds the static scratch's %d rows",
+                    (long)batch * canvas, kStaticSamplerRows);
+    void* ws = nullptr;
+    DG_TRY(static_scratch(&ws));
+    return sample_impl(p, step, batch, canvas, vocab, d_logits, d_canvas, d_argmax, d_lock,
+                       d_stats, d_stop, ws, kStaticSamplerBytes, as_stream(stream), nullptr,
+                       nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, true);
 }
 
 dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t batch,

@@ -293,6 +293,21 @@ dg_status dg_sample_update(const dg_sampler_params* p, int32_t step, int32_t bat
                            float* d_stats, int32_t* d_stop, void* d_ws, size_t ws_bytes,
                            void* stream);
 
+/* dg_sample_update for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same update with the same results, bit for bit, but no workspace
+ * argument.  Its scratch (three int32 per row) is a static device array
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing.  Limit: batch * canvas <= 65536 rows (DG_ERR_CAPACITY
+ * otherwise, nothing launched).  The stream must belong to the calling
+ * thread's current device.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams or threads)
+ * race and must not be issued; calls in one stream's order are safe. */
+dg_status dg_sample_update_static(const dg_sampler_params* p, int32_t step, int32_t batch,
+                                  int32_t canvas, int32_t vocab, const float* d_logits,
+                                  int32_t* d_canvas, int32_t* d_argmax, uint8_t* d_lock,
+                                  float* d_stats, int32_t* d_stop, void* stream);
+
 /* dg_sample_update that also writes the next round's self-conditioning
  * operand (report-summary page, section 2: the model sees its previous
  * round's prediction; section 5: that costs a pass over the full
