@@ -21,6 +21,10 @@ entropy stop never fires, so each block runs the full 48 rounds.
   python bench.py --mode ar [--ar-tokens n] [--ar-batch B] [--config ...]
       the retained autoregressive mode: value = decoded tokens/s (greedy
       decoding of n tokens per sequence after the prompt, B sequences)
+  python bench.py --mode attn [--config ...]
+      the attention block alone (dg_stage_attention) of the configuration's
+      canvases over a synthetic cache of its context length: value =
+      attention TFLOP/s (the kernel and its split merge, library timer)
 """
 from __future__ import annotations
 
@@ -57,12 +61,17 @@ def parse():
     ap.add_argument("--layers", type=int, default=None,
                     help="override the configuration's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="layer workload: skip the 30-layer stack measurement that the default "
+                         "run adds under the key \"stack\"")
+    ap.add_argument("--stack-steps", type=int, default=2,
+                    help="timed blocks of the 30-layer stack measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the measurement, two 1 GiB device copies (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--top-k", type=int, default=0,
                     help="sampler top-k truncation (0: the full distribution)")
-    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar", "train"],
+    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar", "train", "attn"],
                     help="ar: the retained autoregressive mode (greedy decoding); one step "
                          "= --ar-tokens tokens per sequence after the prompt.  train: the "
                          "training-side forward; one step = corruption + denoiser forward + "
@@ -137,8 +146,9 @@ def kernel_work(name, cfg, B, P, sc_splits):
     Hq, Hkv, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     E, k, F = cfg["n_experts"], cfg["top_k"], cfg["d_ff"]
     T = B * N
-    # expected number of experts that receive at least one of T*k assignments
-    hit = E * (1.0 - (1.0 - k / E) ** T)
+    # experts that receive at least one of the T*k assignments: measured from
+    # the routes when the caller has them, else the uniform-routing estimate
+    hit = cfg.get("experts_hit") or E * (1.0 - (1.0 - k / E) ** T)
     if name == "head_gemm":
         return 2.0 * T * V * d, V * d * es + T * d * es + T * V * 4.0
     if name == "selfcond_gemm":
@@ -500,6 +510,8 @@ def bench_train(args):
     warm = {n: binding.timer_read(n) for n in names}
     binding.timer_enable([])
     dominant = max(names, key=lambda n: warm[n][0]) if args.warmup else "head_gemm"
+    hits = expert_hits(m, cfg, x, torch)
+    cfg["experts_hit"] = float(np.mean(hits))
     binding.timer_enable([dominant])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -545,6 +557,8 @@ def bench_train(args):
                                 f"+ cross-entropy at the clean tokens"),
                    "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)",
                    "mean_loss": float(mean.cpu().numpy()[0])},
+        "experts_hit_per_layer": {"min": min(hits), "mean": round(float(np.mean(hits)), 2),
+                                  "max": max(hits), "of": cfg["n_experts"]},
         "kernels": per_kernel,
         "roofline": roof,
     }
@@ -555,6 +569,77 @@ def bench_train(args):
         out["cpu_baseline"] = cpu_baseline_train(
             cfg, W, prompt.cpu().numpy().astype(np.int64), clean.cpu().numpy().astype(np.int32),
             np.full(B, args.rate, np.float32), args.seed)
+    print(json.dumps(out), flush=True)
+
+
+def bench_attn(args):
+    """The attention block alone: dg_stage_attention of the configuration's B
+    canvases of N tokens over a synthetic cache of P context keys per
+    sequence (N(0, 4) keys, N(0, 1) values, bf16), one layer of the
+    configuration's attention shape.  value = algorithmic FLOP/s of the
+    attention kernel and its split merge (4 B N (P + N) Hq dh per launch),
+    timed by the library's HIP events on the launch stream."""
+    import torch
+
+    from discrete_text_diffusion_denoise_amd import binding, synthetic
+
+    shape = synthetic.SHAPES[args.config]
+    # the attention block's shapes; a small vocabulary and expert set (unused)
+    cfg = synthetic.model_config(args.config, n_layers=1, vocab=1024, n_experts=8, top_k=2,
+                                 expert_dtype=None)
+    B, P, N = shape["batch"], shape["prompt"], cfg["canvas"]
+    Hq, dh, d = cfg["n_heads"], cfg["head_dim"], cfg["d_model"]
+    torch.cuda.init()
+    W = device_weights(cfg, args.seed, torch)
+    m = binding.Model(cfg, W, batch=B, capacity=P + N)
+    K, V = m.kv_tensors()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    K[0, :, :, :P] = (2.0 * torch.randn(K[0, :, :, :P].shape, generator=g, device="cuda")).to(K.dtype)
+    V[0, :, :, :P] = torch.randn(V[0, :, :, :P].shape, generator=g, device="cuda").to(V.dtype)
+    m.set_kv_length(P)
+    h0 = torch.randn((B * N, d), generator=g, device="cuda", dtype=torch.float32)
+    h = h0.clone()
+    for _ in range(args.warmup):
+        h.copy_(h0)
+        m.stage_attention(0, h, N, False)
+    torch.cuda.synchronize()
+    binding.timer_enable(["attention"])
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h.copy_(h0)
+        m.stage_attention(0, h, N, False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms, n = binding.timer_read("attention")
+    binding.timer_enable([])
+    flops = 4.0 * B * N * (P + N) * Hq * dh
+    avg = ms / n
+    ach = flops / (avg * 1e-3) / 1e12
+    roof = roofline("attention", avg, cfg, B, P, 1)
+    roof["timed_launches"] = n
+    out = {
+        "metric": "attention TFLOP/s at 1 MI355X",
+        "value": round(ach, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (N(0,4) keys, N(0,1) values, N(0,1) residual rows, random-init weights)",
+        "config": {"workload": (f"attn-{args.config}: attention block of {B} canvas(es) of {N} "
+                                f"tokens over {P} cached keys each, {Hq}q/{cfg['n_kv_heads']}kv "
+                                f"x{dh}, d {d}; one step = one dg_stage_attention (projections, "
+                                f"RoPE, attention, output projection)"),
+                   "global_batch": B, "seq_len": P + N, "parallelism": "none (1 GPU)"},
+        "attention_avg_ms": round(avg, 5),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 
@@ -570,14 +655,51 @@ def main():
     if args.mode == "train":
         bench_train(args)
         return
+    if args.mode == "attn":
+        bench_attn(args)
+        return
+    out = bench_diffusion(args, args.config, args.layers, args.steps, args.warmup,
+                          not args.no_cpu_baseline)
+    if args.config == "layer" and not args.layers and not args.no_stack:
+        # the full denoise step's 30-layer stack, timed in the same run (its
+        # own line's essentials under one key)
+        st = bench_diffusion(args, "stack", None, args.stack_steps, 1, False)
+        out["stack"] = {k: st[k] for k in ("metric", "value", "unit", "ms_per_step",
+                                           "denoise_step_ms", "kernels", "roofline",
+                                           "experts_hit_per_layer", "fraction_check")}
+        out["stack"]["steps"] = args.stack_steps
+        out["stack"]["workload"] = st["config"]["workload"]
+        out["stack"]["rounds_per_block"] = st["config"]["rounds_per_block"]
+        out["stack"]["sampler"] = st["config"]["sampler"]
+    print(json.dumps(out), flush=True)
+
+
+def expert_hits(m, cfg, canvas, torch):
+    """Distinct experts that receive at least one token, per layer, in one
+    denoising round of `canvas` without self-conditioning (run as the chain
+    of its stage calls, which is the step's own computation)."""
+    B, N = canvas.shape
+    h = torch.empty((B * N, cfg["d_model"]), dtype=torch.float32, device="cuda")
+    route = torch.empty((B * N, cfg["top_k"]), dtype=torch.int32, device="cuda")
+    m.stage_input(canvas, h)
+    hits = []
+    for l in range(cfg["n_layers"]):
+        m.stage_attention(l, h, N, False)
+        m.stage_moe(l, h, route)
+        hits.append(int(torch.unique(route).numel()))
+    return hits
+
+
+def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
+    """One configuration of the block loop: returns the JSON dict."""
     import numpy as np
     import torch
 
     from discrete_text_diffusion_denoise_amd import binding, synthetic
 
-    shape = synthetic.SHAPES[args.config]
-    over = {"n_layers": args.layers} if args.layers else {}
-    cfg = synthetic.model_config(args.config, **over)
+    shape = synthetic.SHAPES[config]
+    over = {"n_layers": layers} if layers else {}
+    cfg = synthetic.model_config(config, **over)
     cfg["sampler_top_k"] = args.top_k
     # the full-distribution sampler is bound by its binary32 arithmetic; in
     # the block loop of bf16 models it also writes the next round's
@@ -604,14 +726,23 @@ def main():
     names = list(binding.TIMERS)
     # warmup, with every kernel timer on: picks the dominant kernel
     binding.timer_enable(names)
-    for w in range(args.warmup):
+    for w in range(warmup):
         for k in range(nb):
             m.generate_block(params, w * nb + k, block)
         m.set_kv_length(P)
     torch.cuda.synchronize()
     warm = {n: binding.timer_read(n) for n in names}
     binding.timer_enable([])
-    dominant = max(names, key=lambda n: warm[n][0]) if args.warmup else "head_gemm"
+    dominant = max(names, key=lambda n: warm[n][0]) if warmup else "head_gemm"
+    # experts that receive tokens, per layer, in the first round of a block
+    # (its starting canvas): the expert kernels' algorithmic bytes count the
+    # weights of every hit expert once (routing of the random-init stack is
+    # far from uniform, so a uniform-routing estimate would overstate them)
+    start = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+    binding.canvas_init(params["seed"], 0, start, V)
+    hits = expert_hits(m, cfg, start, torch)
+    m.set_kv_length(P)
+    cfg["experts_hit"] = float(np.mean(hits))
 
     # timed blocks: only the dominant kernel is bracketed by the library's
     # HIP events (on the stream it runs on); every other timer is off, since
@@ -620,9 +751,9 @@ def main():
     rounds = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         for k in range(nb):
-            rounds += m.generate_block(params, (args.warmup + s) * nb + k, block)
+            rounds += m.generate_block(params, (warmup + s) * nb + k, block)
         m.set_kv_length(P)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -632,7 +763,7 @@ def main():
 
     # per-kernel breakdown: one more block with every timer on
     binding.timer_enable(names)
-    m.generate_block(params, args.warmup + args.steps, block)
+    m.generate_block(params, warmup + steps, block)
     m.set_kv_length(P)
     torch.cuda.synchronize()
     kern = {}
@@ -673,29 +804,35 @@ def main():
     sc_splits = -(-V // k_split)
     roof = roofline(dominant, dom_ms / dom_n, cfg, B, P, sc_splits)
     roof["timed_launches"] = dom_n
-    roof["traffic"], roof["traffic_source"] = measured_traffic(dominant, args.config)
+    roof["traffic"], roof["traffic_source"] = measured_traffic(dominant, config)
     per_kernel = {n: dict(kern[n], **({k: v for k, v in roofline(n, kern[n]["avg_ms"], cfg, B, P,
                                                                   sc_splits).items()
                                        if k in ("bound", "achieved", "unit", "frac")}
                                       if kern[n]["launches"] else {}))
                   for n in names}
 
-    value = B * N * args.steps * nb / wall
+    value = B * N * steps * nb / wall
+    fracs = {n: v["frac"] for n, v in per_kernel.items() if "frac" in v}
+    fracs["roofline"] = roof["frac"]
+    over1 = sorted(n for n, f in fracs.items() if f > 1.0)
+    if over1:
+        print(f"bench.py: fraction of peak above 1 for {over1}: the byte or flop model is wrong",
+              file=sys.stderr)
     out = {
         "metric": "canvas tokens/s at 1 MI355X",
         "value": round(value, 2),
         "unit": "canvas tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg["dtype"] + {"fp8": "+fp8-experts", "mxfp4": "+mxfp4-experts"}.get(
             cfg.get("expert_dtype"), ""),
         "data": "synthetic (random-init N(0,0.02) weights, uniform random prompt tokens)",
-        "config": {"workload": (f"{args.config}: {cfg['n_layers']} denoiser layer(s) d{cfg['d_model']} "
+        "config": {"workload": (f"{config}: {cfg['n_layers']} denoiser layer(s) d{cfg['d_model']} "
                                 f"{cfg['n_heads']}q/{cfg['n_kv_heads']}kv x{cfg['head_dim']}, "
                                 f"{cfg['n_experts']} experts top-{cfg['top_k']} d_ff {cfg['d_ff']}"
                                 f"{ {'fp8': ' (E4M3 weights, per-row scales)', 'mxfp4': ' (MXFP4 weights)'}.get(cfg.get('expert_dtype'), '')}, "
@@ -714,22 +851,29 @@ def main():
         "denoise_step_ms": round(step_ms, 4),
         "kernels": per_kernel,
         "roofline": roof,
+        "experts_hit_per_layer": {"min": min(hits), "mean": round(float(np.mean(hits)), 2),
+                                  "max": max(hits), "of": cfg["n_experts"],
+                                  "layers": len(hits)},
+        "fraction_check": ("ok: every fraction of peak <= 1" if not over1 else
+                           f"FAILED: above 1 for {over1}"),
     }
-    if args.copy_probe:
+    if args.copy_probe and config == args.config:
         copy_probe(torch)
     oracle_fits = cfg["n_layers"] == 1 and B == 1 and P <= 4096
-    if not args.no_cpu_baseline and not oracle_fits:
+    if want_cpu and not oracle_fits:
         # the float64 oracle's prompt encode alone would run for many minutes
         out["cpu_baseline"] = None
         out["cpu_baseline_note"] = ("skipped: the oracle sample is defined for the one-layer, "
                                     "one-canvas workload")
-    elif not args.no_cpu_baseline:
+    elif want_cpu:
         cpu_canvas = np.asarray(canvas.cpu().numpy(), dtype=np.int64)
         out["cpu_baseline"] = cpu_baseline(cfg, W, prompt.cpu().numpy().astype(np.int64),
                                            cpu_canvas, params, torch)
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    del m, W, logits, stats
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -4,6 +4,10 @@
         per-kernel table (calls, total, average, min, max) from the
         --kernel-trace CSV in DIR (markdown)
 
+    python -m discrete_text_diffusion_denoise_amd.profiling counters KERNEL DIR [DIR ...]
+        every PMC counter found in the --pmc runs in DIR..., averaged per
+        dispatch of KERNEL (one line per counter)
+
     python -m discrete_text_diffusion_denoise_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL
         HBM traffic of KERNEL per dispatch from a FETCH_SIZE run and a
         WRITE_SIZE run, each scaled by what the same counter reads for the
@@ -65,6 +69,17 @@ def counter_per_dispatch(d: str, counter: str, kernel: str):
     return sum(kv) / len(kv), len(kv), (sum(cp) / len(cp) if cp else None), len(cp)
 
 
+def counters(kernel: str, dirs) -> dict:
+    """{counter: (average per dispatch of `kernel`, dispatches)} over every
+    counter recorded in the --pmc runs under `dirs`."""
+    acc: dict[str, list[float]] = {}
+    for d in dirs:
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            if kernel in r["Kernel_Name"]:
+                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in sorted(acc.items())}
+
+
 def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
     f, nf, fc, nfc = counter_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
     w, nw, wc, nwc = counter_per_dispatch(write_dir, "WRITE_SIZE", kernel)
@@ -87,6 +102,10 @@ def main(argv):
         print("|---:|---:|---:|---:|---:|---:|---|")
         for k, n, tot, avg, mn, mx, pct in kernel_table(argv[1]):
             print(f"| {tot / 1e3:.3f} | {pct:.1f} | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | `{k}` |")
+        return 0
+    if len(argv) >= 3 and argv[0] == "counters":
+        for k, (v, n) in counters(argv[1], argv[2:]).items():
+            print(f"{k}: {v:.6g}  ({n} dispatches)")
         return 0
     if len(argv) >= 4 and argv[0] == "traffic":
         t = traffic(argv[1], argv[2], argv[3])
