@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_ring.h"
 
 namespace dg {
 
@@ -243,6 +244,306 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------
+// bf16, head dim 128: the same attention as attn_kernel, organised so that
+// the matrix cores rather than the softmax bookkeeping set the pace.
+//
+//   * A wave owns 16 queries of HPW query heads of one KV group, so every
+//     K or V fragment it reads from LDS feeds HPW MFMAs.
+//   * K and V tiles of 32 keys arrive by direct-to-LDS loads
+//     (global_load_lds, no register staging) in a ring of four slots, three
+//     tiles in flight while the fourth is multiplied; the barrier waits for
+//     LDS traffic only.
+//   * Each 256-byte key row keeps its sixteen 16-byte chunks XOR-swizzled
+//     (chunk c of row r in slot c ^ sw2(r)): the K fragment reads (16 rows,
+//     one chunk each) and the transposing V reads (4 rows x 32 bytes per
+//     16 lanes) both touch distinct banks.
+//   * Q is scaled by log2(e)/sqrt(dh) once, when its fragments are loaded,
+//     so a score is already the exponent of 2 the softmax needs.
+//   * The running maximum moves only when a tile's maximum exceeds it by
+//     more than RESCALE_T (2^8 in the weights): O and the sums are then
+//     rescaled; otherwise probabilities are taken against the stale maximum,
+//     which changes no result (every partial is a consistent (o, m, l)
+//     triple) but takes the rescale and the cross-lane maximum off the
+//     common path.
+//   * Key masks run only on the tiles that need them (the last partial
+//     tile; causal tiles that reach past the wave's first query).
+constexpr int KT2 = 32;              // keys per tile
+constexpr int RING2 = 4;             // LDS slots per operand
+constexpr int ROW2 = 256;            // bytes per key row (128 bf16)
+constexpr int TILE2 = KT2 * ROW2;    // 8 KiB per K (or V) tile
+constexpr int SLOT2 = 2 * TILE2;     // K then V
+constexpr float RESCALE_T = 8.0f;
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sw2(int r) {
+    r &= 15;
+    return (2 * r + (r >> 3)) & 15;
+}
+
+// vmcnt(n) for n in {0, 4, 8}: the loads of later tiles stay in flight
+__device__ __forceinline__ void attn2_wait(int n) {
+    if (n >= 8)
+        __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));
+    else if (n >= 4)
+        __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
+    else
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t scale_bf2(uint32_t w, float c) {
+    const float lo = __uint_as_float(w << 16) * c;
+    const float hi = __uint_as_float(w & 0xFFFF0000u) * c;
+    return pack_bf2(lo, hi);
+}
+
+template <int HPW>
+__global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
+    if (a.halt && *a.halt) return;
+    constexpr int DH = 128;
+    __shared__ __align__(1024) unsigned char ring[RING2 * SLOT2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int G = a.Hq / a.Hkv;
+    const int hg = G / HPW;                  // head groups of one KV head
+    const int nqt = cdiv(a.n, 16);
+    const int units = nqt * hg;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
+    const int unit = blockIdx.x * 4 + wave;
+    const bool wvalid = unit < units;
+    const int qt = wvalid ? unit / hg : 0;
+    const int h0 = kvh * G + (wvalid ? (unit % hg) * HPW : 0);
+    const int qi = qt * 16 + r16;
+    const bool qvalid = wvalid && qi < a.n;
+    const long qrow = (long)b * a.n + (qvalid ? qi : 0);
+    const int qpos = a.pos0 + qi;
+    const int qpos_first = a.pos0 + qt * 16;
+
+    int kb = split * a.split_len;
+    int ke = min(a.kv_len, kb + a.split_len);
+    if (a.causal) {
+        const int last_unit = min(blockIdx.x * 4 + 3, units - 1);
+        const int last_q = min(a.n - 1, (last_unit / hg) * 16 + 15);
+        ke = min(ke, a.pos0 + last_q + 1);
+    }
+    const int ntiles = ke > kb ? cdiv(ke - kb, KT2) : 0;
+
+    // Q fragments, scaled so that a score is log2-e based
+    const float qscale = LOG2E / sqrtf((float)DH);
+    u32x4_t qf[HPW][4];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + qrow * (long)a.Hq * DH +
+                          (long)(h0 + hh) * DH;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qvalid) v = *reinterpret_cast<const uint4*>(Q + s * 32 + g4 * 8);
+            qf[hh][s] = u32x4_t{scale_bf2(v.x, qscale), scale_bf2(v.y, qscale),
+                                scale_bf2(v.z, qscale), scale_bf2(v.w, qscale)};
+        }
+    }
+    // the Q loads are waited for here, before any K/V load is in flight
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bf16_t* Kc = reinterpret_cast<const bf16_t*>(a.kc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
+    const bf16_t* Vc = reinterpret_cast<const bf16_t*>(a.vc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
+
+    // direct-to-LDS fill: wave w writes 1 KiB blocks 2w and 2w+1 of each
+    // tile; lane l of block q lands in row 4q + l/16, slot l%16, which holds
+    // global chunk (l%16) ^ sw2(row)
+    int fill_row[2], fill_chunk[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        fill_row[i] = 4 * (2 * wave + i) + (lane >> 4);
+        fill_chunk[i] = (lane & 15) ^ sw2(fill_row[i]);
+    }
+    const uint32_t ring0 = lds_addr(ring);
+#define ATT2_ISSUE(t)                                                                          \
+    {                                                                                          \
+        const int k0_ = kb + (t) * KT2;                                                        \
+        unsigned char* sl_ = ring + ((t) % RING2) * SLOT2;                                     \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                        \
+            const long key_ = min(k0_ + fill_row[i], ke - 1);                                  \
+            const long off_ = key_ * DH + fill_chunk[i] * 8;                                   \
+            __builtin_amdgcn_global_load_lds((glb_void*)(Kc + off_),                           \
+                                             (lds_void*)(sl_ + (2 * wave + i) * 1024), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds((glb_void*)(Vc + off_),                           \
+                                             (lds_void*)(sl_ + TILE2 + (2 * wave + i) * 1024), 16, 0, 0); \
+        }                                                                                      \
+    }
+
+    // fragment addresses within a slot (bytes): K for k-step s (subtile 1 at
+    // +4096), V for dh tile dt (keys 16.. at +4096)
+    uint32_t ka[4], va[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[s] = r16 * ROW2 + (((4 * s + g4) ^ sw2(r16)) << 4);
+    {
+        const int rv = 4 * g4 + (r16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            va[dt] = TILE2 + rv * ROW2 + (((2 * dt + ((r16 & 3) >> 1)) ^ sw2(rv)) << 4) +
+                     8 * (r16 & 1);
+    }
+
+    f32x4_t o[HPW][8];
+    float m_run[HPW], l_run[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        m_run[hh] = -1e30f;
+        l_run[hh] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[hh][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+#pragma unroll
+    for (int j = 0; j < RING2 - 1; ++j)
+        if (j < ntiles) ATT2_ISSUE(j);
+
+    for (int t = 0; t < ntiles; ++t) {
+        // tile t has landed for this wave (later tiles may stay in flight),
+        // then for every wave; the slot of tile t - 1 is free for t + 3
+        attn2_wait(4 * (min(ntiles - 1, t + RING2 - 2) - t));
+        attn_barrier();
+        if (t + RING2 - 1 < ntiles) ATT2_ISSUE(t + RING2 - 1);
+        const int k0 = kb + t * KT2;
+        const uint32_t sb = ring0 + (t % RING2) * SLOT2;
+
+        // K fragments: one asm block, so the compiler does not wait for the
+        // direct-to-LDS loads of later slots before reading this one
+        u32x4_t kf0, kf1, kf2, kf3, kf4, kf5, kf6, kf7;
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:0\n ds_read_b128 %1, %9 offset:0\n"
+            "ds_read_b128 %2, %10 offset:0\n ds_read_b128 %3, %11 offset:0\n"
+            "ds_read_b128 %4, %8 offset:4096\n ds_read_b128 %5, %9 offset:4096\n"
+            "ds_read_b128 %6, %10 offset:4096\n ds_read_b128 %7, %11 offset:4096\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kf0), "=&v"(kf1), "=&v"(kf2), "=&v"(kf3), "=&v"(kf4), "=&v"(kf5), "=&v"(kf6),
+              "=&v"(kf7)
+            : "v"(sb + ka[0]), "v"(sb + ka[1]), "v"(sb + ka[2]), "v"(sb + ka[3])
+            : "memory");
+        const u32x4_t kf[2][4] = {{kf0, kf1, kf2, kf3}, {kf4, kf5, kf6, kf7}};
+        f32x4_t sc[HPW][2];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                sc[hh][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    sc[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, kf[kt][s]),
+                        __builtin_bit_cast(bf16x8_t, qf[hh][s]), sc[hh][kt], 0, 0, 0);
+            }
+
+        // V^T fragments by transposing reads (keys 4*g4 + 0..3 and +16)
+        u32x2_t v0, v1, v2, v3, v4, v5, v6, v7, w0, w1, w2, w3, w4, w5, w6, w7;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16 offset:0\n ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+            "ds_read_b64_tr_b16 %2, %17 offset:0\n ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+            "ds_read_b64_tr_b16 %4, %18 offset:0\n ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+            "ds_read_b64_tr_b16 %6, %19 offset:0\n ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+            "ds_read_b64_tr_b16 %8, %20 offset:0\n ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+            "ds_read_b64_tr_b16 %10, %21 offset:0\n ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+            "ds_read_b64_tr_b16 %12, %22 offset:0\n ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+            "ds_read_b64_tr_b16 %14, %23 offset:0\n ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v0), "=&v"(w0), "=&v"(v1), "=&v"(w1), "=&v"(v2), "=&v"(w2), "=&v"(v3), "=&v"(w3),
+              "=&v"(v4), "=&v"(w4), "=&v"(v5), "=&v"(w5), "=&v"(v6), "=&v"(w6), "=&v"(v7), "=&v"(w7)
+            : "v"(sb + va[0]), "v"(sb + va[1]), "v"(sb + va[2]), "v"(sb + va[3]), "v"(sb + va[4]),
+              "v"(sb + va[5]), "v"(sb + va[6]), "v"(sb + va[7])
+            : "memory");
+        const u32x2_t vlo[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+        const u32x2_t vhi[8] = {w0, w1, w2, w3, w4, w5, w6, w7};
+
+        // masks only where a key can be out of range for this wave
+        const bool mask = (k0 + KT2 > ke) || (a.causal && k0 + KT2 - 1 > qpos_first);
+        u32x4_t pf[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            float x[8];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[kt * 4 + e] = sc[hh][kt][e];
+            if (mask) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = k0 + kt * 16 + 4 * g4 + e;
+                        const bool ok = key < ke && (!a.causal || key <= qpos);
+                        if (!ok) x[kt * 4 + e] = -INFINITY;
+                    }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            if (__ballot(mx > m_run[hh] + RESCALE_T)) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mn = fmaxf(m_run[hh], mx);
+                const float corr = __builtin_amdgcn_exp2f(m_run[hh] - mn);
+                l_run[hh] *= corr;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[hh][dt][e] *= corr;
+                m_run[hh] = mn;
+            }
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_run[hh]);
+            l_run[hh] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            pf[hh] = u32x4_t{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
+                             pack_bf2(p[6], p[7])};
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const u32x4_t vf = u32x4_t{vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y};
+#pragma unroll
+            for (int hh = 0; hh < HPW; ++hh)
+                o[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, vf), __builtin_bit_cast(bf16x8_t, pf[hh]),
+                    o[hh][dt], 0, 0, 0);
+        }
+    }
+#undef ATT2_ISSUE
+
+    // lane holds O^T[d = dt*16 + 4*g4 + e][query r16]
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        float l_tot = l_run[hh] + __shfl_xor(l_run[hh], 16, 64);
+        l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
+        if (!qvalid) continue;
+        const int h = h0 + hh;
+        if (a.splits == 1) {
+            bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + qrow * (long)a.Hq * DH + (long)h * DH;
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                uint2 w;
+                w.x = pack_bf2(o[hh][dt][0] * inv, o[hh][dt][1] * inv);
+                w.y = pack_bf2(o[hh][dt][2] * inv, o[hh][dt][3] * inv);
+                *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g4) = w;
+            }
+        } else {
+            const long base = ((long)split * a.B * a.n + qrow) * a.Hq + h;
+            float* po = a.part_o + base * DH;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<f32x4_t*>(po + dt * 16 + 4 * g4) = o[hh][dt];
+            if (g4 == 0) {
+                a.part_ml[base * 2 + 0] = m_run[hh];
+                a.part_ml[base * 2 + 1] = l_tot;
+            }
+        }
+    }
+}
+
 // Merge of split partials: one workgroup of DH threads per (token, head).
 template <typename T>
 __global__ void attn_merge_kernel(AttnArgs a) {
@@ -274,13 +575,21 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
+// The bf16 head-dim-128 kernel (attn2_kernel) takes the shape: heads per
+// wave 2 when the KV group has an even number of query heads, else 1.
+bool attn2_takes(int dh, bool bf16) { return bf16 && dh == 128; }
+int attn2_hpw(int G) { return G % 2 == 0 ? 2 : 1; }
+
 int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int max_splits,
-                     int* split_len) {
+                     int* split_len, int dh, bool bf16) {
     const int G = Hq / Hkv;
-    const long base = (long)cdiv(G * cdiv(n, 16), 4) * Hkv * B;
+    // workgroups of one key range, and the number to aim for: attn_kernel
+    // runs eight small workgroups per CU, attn2_kernel two large ones
+    const bool v2 = attn2_takes(dh, bf16);
+    const long base = v2 ? (long)cdiv(cdiv(n, 16) * (G / attn2_hpw(G)), 4) * Hkv * B
+                         : (long)cdiv(G * cdiv(n, 16), 4) * Hkv * B;
+    const int target = v2 ? 1024 : 2048;
     int splits = 1;
-    // workgroups to aim for (eight per CU)
-    constexpr int target = 2048;
     if (!causal && kv_len > 256) {
         splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(target, (int)base)));
         splits = std::min(splits, std::min(32, std::max(1, max_splits)));
@@ -304,6 +613,12 @@ hipError_t attention(const AttnArgs& a, hipStream_t st) {
     // the merge keeps the split weights in one wave
     if (a.splits > 1 && (a.splits > 32 || a.dh < 64)) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
+    if (attn2_takes(a.dh, sizeof(T) == 2)) {
+        const int hpw = attn2_hpw(G);
+        dim3 grid2(cdiv(cdiv(a.n, 16) * (G / hpw), 4), a.Hkv, a.B * a.splits);
+        if (hpw == 2) hipLaunchKernelGGL(attn2_kernel<2>, grid2, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(attn2_kernel<1>, grid2, dim3(256), 0, st, a);
+    } else {
     dim3 grid(cdiv(G * cdiv(a.n, 16), 4), a.Hkv, a.B * a.splits);
     switch (a.dh) {
         case 64: hipLaunchKernelGGL((attn_kernel<T, 64>), grid, dim3(256), 0, st, a); break;
@@ -315,6 +630,7 @@ hipError_t attention(const AttnArgs& a, hipStream_t st) {
             }
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
+    }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;

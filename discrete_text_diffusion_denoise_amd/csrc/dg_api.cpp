@@ -387,7 +387,7 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     const int max_splits =
         dh < 64 ? 1 : std::max(1, std::max(kAttnPartRows, 8 * B * c.canvas) / Tn);
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
-                                    &a.split_len);
+                                    &a.split_len, dh, sizeof(T) == 2);
     DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
     DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, s, st));
     return DG_OK;

@@ -149,7 +149,7 @@ template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t st);
 // Number of key splits the launcher would use for this shape.
 int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int max_splits,
-                     int* split_len);
+                     int* split_len, int dh, bool bf16);
 
 // ------------------------------------------------------------------ MoE
 struct MoeArgs {

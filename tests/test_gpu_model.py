@@ -41,8 +41,15 @@ SMALL_FP8 = dict(SMALL_BF16, expert_dtype="fp8")
 # ... and with MXFP4 expert weights (E2M1 codes, an E8M0 scale per 32)
 SMALL_MXFP4 = dict(SMALL_BF16, expert_dtype="mxfp4")
 
+# bf16 with 128-wide heads (the attention kernel of the full-size layer) at
+# query-head groups of 1, 2 and 4 per KV head
+ATT128 = dict(n_layers=1, d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, n_experts=8, top_k=2,
+              d_ff=256, vocab=2048, canvas=256, dtype="bf16")
+
 MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
-          "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8, "small_mxfp4": SMALL_MXFP4}
+          "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8, "small_mxfp4": SMALL_MXFP4,
+          "att128_g4": ATT128, "att128_g2": dict(ATT128, n_heads=4),
+          "att128_g1": dict(ATT128, n_heads=4, n_kv_heads=4)}
 
 
 def device_form(cfg, W):
@@ -276,15 +283,27 @@ def test_denoise_step_end_to_end_fp32(name, P, B, selfcond, layers, top_k):
     assert np.isfinite(got).all()
 
 
-@pytest.mark.parametrize("name,causal", [("tiny", False), ("tiny", True), ("small_bf16", False),
-                                         ("small_bf16", True), ("f32_gqa", False)])
-def test_stage_attention_on_synthetic_cache(name, causal):
+@pytest.mark.parametrize("name,causal,P,N", [("tiny", False, 333, 256), ("tiny", True, 333, 256),
+                                             ("small_bf16", False, 333, 256),
+                                             ("small_bf16", True, 333, 256),
+                                             ("f32_gqa", False, 333, 100),
+                                             ("att128_g4", False, 333, 256),
+                                             ("att128_g4", True, 333, 256),
+                                             ("att128_g4", False, 40, 100),
+                                             ("att128_g4", True, 0, 300),
+                                             ("att128_g2", False, 1000, 256),
+                                             ("att128_g2", True, 77, 33),
+                                             ("att128_g1", False, 333, 256),
+                                             ("att128_g1", True, 5, 1)])
+def test_stage_attention_on_synthetic_cache(name, causal, P, N):
     """Attention half-block with the cache filled directly from synthetic
-    values (no encode), so attention is checked on its own."""
-    B, P = 2, 333
-    cfg, W, m = setup(name, P, batch=B, std=0.05)
-    N, d = cfg["canvas"], cfg["d_model"]
-    Hkv, dh = cfg["n_kv_heads"], cfg["head_dim"]
+    values (no encode), so attention is checked on its own: key ranges with
+    partial tiles and several splits, causal masks on and off the diagonal,
+    ragged and single-token canvases, one, two and four query heads per KV
+    head."""
+    B = 2
+    cfg, W, m = setup(name, P, batch=B, std=0.05, canvas=N)
+    d, Hkv, dh = cfg["d_model"], cfg["n_kv_heads"], cfg["head_dim"]
     rng = np.random.default_rng(10)
     kctx = round_model_dtype(cfg, rng.standard_normal((B, Hkv, P, dh)).astype(np.float32))
     vctx = round_model_dtype(cfg, rng.standard_normal((B, Hkv, P, dh)).astype(np.float32))
@@ -292,22 +311,10 @@ def test_stage_attention_on_synthetic_cache(name, causal):
     K[0, :, :, :P] = to_dev(kctx, m.dtype)
     V[0, :, :, :P] = to_dev(vctx, m.dtype)
     m.set_kv_length(P)
-    h = rng.standard_normal((B * N, d)).astype(np.float32)
-    hd = to_dev(h)
-    m.stage_attention(0, hd, N, causal)
+    h = to_dev(rng.standard_normal((B * N, d)).astype(np.float32))
     torch.cuda.synchronize()
-    W64 = synthetic.to_float64(W)
-    lw = W64["layers"][0]
-    tol = tol_for(cfg)
-    for b in range(B):
-        ref, kn, vn = om.attn_half(h[b * N:(b + 1) * N].astype(np.float64), lw, cfg,
-                                   kctx[b].astype(np.float64), vctx[b].astype(np.float64), P,
-                                   causal=causal)
-        err = normwise(hd[b * N:(b + 1) * N].cpu().numpy(), ref)
-        assert err <= tol, (b, err)
-        # the new K/V were written to slots [P, P+N)
-        assert normwise(K[0, b, :, P:P + N].float().cpu().numpy(), kn) <= tol
-        assert normwise(V[0, b, :, P:P + N].float().cpu().numpy(), vn) <= tol
+    chain.check_attention(m, cfg, chain.layer64(W["layers"][0]), 0, h, N, causal, tol_for(cfg),
+                          label=f"{name} P={P} N={N} causal={causal}")
 
 
 @pytest.mark.parametrize("name,T,top_k", [("tiny", 256, None), ("small_bf16", 512, None),
