@@ -248,11 +248,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // bf16, head dim 128: the same attention as attn_kernel, organised so that
 // the matrix cores rather than the softmax bookkeeping set the pace.
 //
-//   * A wave owns 16 queries of HPW query heads of one KV group, so every
-//     K or V fragment it reads from LDS feeds HPW MFMAs.
+//   * A wave owns 16 queries of HPW query heads of one KV group (HPW = 1:
+//     four workgroups of 128 registers per wave fit on a CU, and that
+//     occupancy hides the LDS and barrier latency better than two heads per
+//     wave at half the occupancy; measured 0.107 against 0.121-0.127 ms at
+//     33 024 keys).
 //   * K and V tiles of 32 keys arrive by direct-to-LDS loads
-//     (global_load_lds, no register staging) in a ring of four slots, three
-//     tiles in flight while the fourth is multiplied; the barrier waits for
+//     (global_load_lds, no register staging) in a ring of two slots: the
+//     next tile loads while this one is multiplied; the barrier waits for
 //     LDS traffic only.
 //   * Each 256-byte key row keeps its sixteen 16-byte chunks XOR-swizzled
 //     (chunk c of row r in slot c ^ sw2(r)): the K fragment reads (16 rows,
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 //   * Key masks run only on the tiles that need them (the last partial
 //     tile; causal tiles that reach past the wave's first query).
 constexpr int KT2 = 32;              // keys per tile
-constexpr int RING2 = 4;             // LDS slots per operand
+constexpr int RING2 = 2;             // LDS slots (K and V tile each)
 constexpr int ROW2 = 256;            // bytes per key row (128 bf16)
 constexpr int TILE2 = KT2 * ROW2;    // 8 KiB per K (or V) tile
 constexpr int SLOT2 = 2 * TILE2;     // K then V
@@ -283,15 +286,6 @@ __device__ __forceinline__ int sw2(int r) {
     return (2 * r + (r >> 3)) & 15;
 }
 
-// vmcnt(n) for n in {0, 4, 8}: the loads of later tiles stay in flight
-__device__ __forceinline__ void attn2_wait(int n) {
-    if (n >= 8)
-        __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8));
-    else if (n >= 4)
-        __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
-    else
-        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-}
 
 __device__ __forceinline__ uint32_t scale_bf2(uint32_t w, float c) {
     const float lo = __uint_as_float(w << 16) * c;
@@ -300,7 +294,7 @@ __device__ __forceinline__ uint32_t scale_bf2(uint32_t w, float c) {
 }
 
 template <int HPW>
-__global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 4) void attn2_kernel(AttnArgs a) {
     if (a.halt && *a.halt) return;
     constexpr int DH = 128;
     __shared__ __align__(1024) unsigned char ring[RING2 * SLOT2];
@@ -311,9 +305,24 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
     const int hg = G / HPW;                  // head groups of one KV head
     const int nqt = cdiv(a.n, 16);
     const int units = nqt * hg;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
-    const int unit = blockIdx.x * 4 + wave;
+    // block -> (key range group, workgroup in it).  Blocks go to the eight
+    // XCDs in turn; when the groups (KV head, sequence, key range) come in
+    // eights, the workgroups of one group all land on one XCD, so each K/V
+    // tile is fetched into one L2 and read from there by all of them.
+    const int nx = cdiv(units, 4);
+    const int ngroups = a.Hkv * a.B * a.splits;
+    int bx, grp;
+    if (ngroups % 8 == 0) {
+        const int slot = blockIdx.x >> 3;
+        bx = slot % nx;
+        grp = (slot / nx) * 8 + (blockIdx.x & 7);
+    } else {
+        bx = blockIdx.x % nx;
+        grp = blockIdx.x / nx;
+    }
+    const int kvh = grp % a.Hkv;
+    const int b = (grp / a.Hkv) / a.splits, split = (grp / a.Hkv) % a.splits;
+    const int unit = bx * 4 + wave;
     const bool wvalid = unit < units;
     const int qt = wvalid ? unit / hg : 0;
     const int h0 = kvh * G + (wvalid ? (unit % hg) * HPW : 0);
@@ -326,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
     int kb = split * a.split_len;
     int ke = min(a.kv_len, kb + a.split_len);
     if (a.causal) {
-        const int last_unit = min(blockIdx.x * 4 + 3, units - 1);
+        const int last_unit = min(bx * 4 + 3, units - 1);
         const int last_q = min(a.n - 1, (last_unit / hg) * 16 + 15);
         ke = min(ke, a.pos0 + last_q + 1);
     }
@@ -347,35 +356,44 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
                                 scale_bf2(v.z, qscale), scale_bf2(v.w, qscale)};
         }
     }
-    // the Q loads are waited for here, before any K/V load is in flight
-    __builtin_amdgcn_sched_barrier(0);
 
     const bf16_t* Kc = reinterpret_cast<const bf16_t*>(a.kc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
     const bf16_t* Vc = reinterpret_cast<const bf16_t*>(a.vc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
 
     // direct-to-LDS fill: wave w writes 1 KiB blocks 2w and 2w+1 of each
     // tile; lane l of block q lands in row 4q + l/16, slot l%16, which holds
-    // global chunk (l%16) ^ sw2(row)
-    int fill_row[2], fill_chunk[2];
+    // global chunk (l%16) ^ sw2(row).  foff: that chunk's byte offset in a
+    // full tile; a partial last tile clamps the row to the last valid key.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int frow[2];
+    uint32_t foff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        fill_row[i] = 4 * (2 * wave + i) + (lane >> 4);
-        fill_chunk[i] = (lane & 15) ^ sw2(fill_row[i]);
+        frow[i] = 4 * (2 * wv + i) + (lane >> 4);
+        foff[i] = frow[i] * ROW2 + (((lane & 15) ^ sw2(frow[i])) << 4);
     }
-    const uint32_t ring0 = lds_addr(ring);
-#define ATT2_ISSUE(t)                                                                          \
-    {                                                                                          \
-        const int k0_ = kb + (t) * KT2;                                                        \
-        unsigned char* sl_ = ring + ((t) % RING2) * SLOT2;                                     \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                        \
-            const long key_ = min(k0_ + fill_row[i], ke - 1);                                  \
-            const long off_ = key_ * DH + fill_chunk[i] * 8;                                   \
-            __builtin_amdgcn_global_load_lds((glb_void*)(Kc + off_),                           \
-                                             (lds_void*)(sl_ + (2 * wave + i) * 1024), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds((glb_void*)(Vc + off_),                           \
-                                             (lds_void*)(sl_ + TILE2 + (2 * wave + i) * 1024), 16, 0, 0); \
-        }                                                                                      \
-    }
+    const char* Kb = reinterpret_cast<const char*>(Kc);
+    const char* Vb = reinterpret_cast<const char*>(Vc);
+    auto issue = [&](int t) {
+        const int k0_ = kb + t * KT2;
+        unsigned char* sl_ = ring + (t % RING2) * SLOT2 + 2 * wv * 1024;
+        const char* kt_ = Kb + (long)k0_ * ROW2;
+        const char* vt_ = Vb + (long)k0_ * ROW2;
+        if (k0_ + KT2 <= ke) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_global_load_lds((glb_void*)(kt_ + foff[i]), (lds_void*)(sl_ + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_void*)(vt_ + foff[i]), (lds_void*)(sl_ + TILE2 + i * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t o_ = min(frow[i], ke - 1 - k0_) * ROW2 + (foff[i] & (ROW2 - 1));
+                __builtin_amdgcn_global_load_lds((glb_void*)(kt_ + o_), (lds_void*)(sl_ + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_void*)(vt_ + o_), (lds_void*)(sl_ + TILE2 + i * 1024), 16, 0, 0);
+            }
+        }
+    };
 
     // fragment addresses within a slot (bytes): K for k-step s (subtile 1 at
     // +4096), V for dh tile dt (keys 16.. at +4096)
@@ -389,32 +407,12 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
             va[dt] = TILE2 + rv * ROW2 + (((2 * dt + ((r16 & 3) >> 1)) ^ sw2(rv)) << 4) +
                      8 * (r16 & 1);
     }
+    const uint32_t ring0 = lds_addr(ring);
 
-    f32x4_t o[HPW][8];
-    float m_run[HPW], l_run[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-        m_run[hh] = -1e30f;
-        l_run[hh] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[hh][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-#pragma unroll
-    for (int j = 0; j < RING2 - 1; ++j)
-        if (j < ntiles) ATT2_ISSUE(j);
-
-    for (int t = 0; t < ntiles; ++t) {
-        // tile t has landed for this wave (later tiles may stay in flight),
-        // then for every wave; the slot of tile t - 1 is free for t + 3
-        attn2_wait(4 * (min(ntiles - 1, t + RING2 - 2) - t));
-        attn_barrier();
-        if (t + RING2 - 1 < ntiles) ATT2_ISSUE(t + RING2 - 1);
-        const int k0 = kb + t * KT2;
-        const uint32_t sb = ring0 + (t % RING2) * SLOT2;
-
-        // K fragments: one asm block, so the compiler does not wait for the
-        // direct-to-LDS loads of later slots before reading this one
+    // S^T = K Q^T of the tile in slot `sb`: lane holds keys kt*16 + 4*g4 + e
+    // of query r16.  The K fragments are one asm block, so the compiler does
+    // not wait for the direct-to-LDS loads of other slots before it.
+    auto qk = [&](uint32_t sb, f32x4_t (&sc)[HPW][2]) {
         u32x4_t kf0, kf1, kf2, kf3, kf4, kf5, kf6, kf7;
         asm volatile(
             "ds_read_b128 %0, %8 offset:0\n ds_read_b128 %1, %9 offset:0\n"
@@ -427,7 +425,6 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
             : "v"(sb + ka[0]), "v"(sb + ka[1]), "v"(sb + ka[2]), "v"(sb + ka[3])
             : "memory");
         const u32x4_t kf[2][4] = {{kf0, kf1, kf2, kf3}, {kf4, kf5, kf6, kf7}};
-        f32x4_t sc[HPW][2];
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -439,28 +436,23 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
                         __builtin_bit_cast(bf16x8_t, kf[kt][s]),
                         __builtin_bit_cast(bf16x8_t, qf[hh][s]), sc[hh][kt], 0, 0, 0);
             }
+    };
 
-        // V^T fragments by transposing reads (keys 4*g4 + 0..3 and +16)
-        u32x2_t v0, v1, v2, v3, v4, v5, v6, v7, w0, w1, w2, w3, w4, w5, w6, w7;
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %16 offset:0\n ds_read_b64_tr_b16 %1, %16 offset:4096\n"
-            "ds_read_b64_tr_b16 %2, %17 offset:0\n ds_read_b64_tr_b16 %3, %17 offset:4096\n"
-            "ds_read_b64_tr_b16 %4, %18 offset:0\n ds_read_b64_tr_b16 %5, %18 offset:4096\n"
-            "ds_read_b64_tr_b16 %6, %19 offset:0\n ds_read_b64_tr_b16 %7, %19 offset:4096\n"
-            "ds_read_b64_tr_b16 %8, %20 offset:0\n ds_read_b64_tr_b16 %9, %20 offset:4096\n"
-            "ds_read_b64_tr_b16 %10, %21 offset:0\n ds_read_b64_tr_b16 %11, %21 offset:4096\n"
-            "ds_read_b64_tr_b16 %12, %22 offset:0\n ds_read_b64_tr_b16 %13, %22 offset:4096\n"
-            "ds_read_b64_tr_b16 %14, %23 offset:0\n ds_read_b64_tr_b16 %15, %23 offset:4096\n"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(v0), "=&v"(w0), "=&v"(v1), "=&v"(w1), "=&v"(v2), "=&v"(w2), "=&v"(v3), "=&v"(w3),
-              "=&v"(v4), "=&v"(w4), "=&v"(v5), "=&v"(w5), "=&v"(v6), "=&v"(w6), "=&v"(v7), "=&v"(w7)
-            : "v"(sb + va[0]), "v"(sb + va[1]), "v"(sb + va[2]), "v"(sb + va[3]), "v"(sb + va[4]),
-              "v"(sb + va[5]), "v"(sb + va[6]), "v"(sb + va[7])
-            : "memory");
-        const u32x2_t vlo[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
-        const u32x2_t vhi[8] = {w0, w1, w2, w3, w4, w5, w6, w7};
+    f32x4_t o[HPW][8];
+    float m_run[HPW], l_run[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        m_run[hh] = -1e30f;
+        l_run[hh] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[hh][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
-        // masks only where a key can be out of range for this wave
+    // softmax of the scores of the tile at keys k0.. (against the running
+    // maximum, moved only past RESCALE_T) into bf16 probabilities, then
+    // O^T += V^T P^T from the tile in slot `sb` (transposing V reads: keys
+    // 4*g4 + 0..3 and +16)
+    auto soft_pv = [&](uint32_t sb, int k0, f32x4_t (&sc)[HPW][2]) {
         const bool mask = (k0 + KT2 > ke) || (a.causal && k0 + KT2 - 1 > qpos_first);
         u32x4_t pf[HPW];
 #pragma unroll
@@ -471,11 +463,12 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[kt * 4 + e] = sc[hh][kt][e];
             if (mask) {
+                const int key0 = k0 + 4 * g4;
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int key = k0 + kt * 16 + 4 * g4 + e;
+                        const int key = key0 + kt * 16 + e;
                         const bool ok = key < ke && (!a.causal || key <= qpos);
                         if (!ok) x[kt * 4 + e] = -INFINITY;
                     }
@@ -501,6 +494,24 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
             pf[hh] = u32x4_t{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]), pack_bf2(p[4], p[5]),
                              pack_bf2(p[6], p[7])};
         }
+        u32x2_t v0, v1, v2, v3, v4, v5, v6, v7, w0, w1, w2, w3, w4, w5, w6, w7;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16 offset:0\n ds_read_b64_tr_b16 %1, %16 offset:4096\n"
+            "ds_read_b64_tr_b16 %2, %17 offset:0\n ds_read_b64_tr_b16 %3, %17 offset:4096\n"
+            "ds_read_b64_tr_b16 %4, %18 offset:0\n ds_read_b64_tr_b16 %5, %18 offset:4096\n"
+            "ds_read_b64_tr_b16 %6, %19 offset:0\n ds_read_b64_tr_b16 %7, %19 offset:4096\n"
+            "ds_read_b64_tr_b16 %8, %20 offset:0\n ds_read_b64_tr_b16 %9, %20 offset:4096\n"
+            "ds_read_b64_tr_b16 %10, %21 offset:0\n ds_read_b64_tr_b16 %11, %21 offset:4096\n"
+            "ds_read_b64_tr_b16 %12, %22 offset:0\n ds_read_b64_tr_b16 %13, %22 offset:4096\n"
+            "ds_read_b64_tr_b16 %14, %23 offset:0\n ds_read_b64_tr_b16 %15, %23 offset:4096\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v0), "=&v"(w0), "=&v"(v1), "=&v"(w1), "=&v"(v2), "=&v"(w2), "=&v"(v3), "=&v"(w3),
+              "=&v"(v4), "=&v"(w4), "=&v"(v5), "=&v"(w5), "=&v"(v6), "=&v"(w6), "=&v"(v7), "=&v"(w7)
+            : "v"(sb + va[0]), "v"(sb + va[1]), "v"(sb + va[2]), "v"(sb + va[3]), "v"(sb + va[4]),
+              "v"(sb + va[5]), "v"(sb + va[6]), "v"(sb + va[7])
+            : "memory");
+        const u32x2_t vlo[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+        const u32x2_t vhi[8] = {w0, w1, w2, w3, w4, w5, w6, w7};
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const u32x4_t vf = u32x4_t{vlo[dt].x, vlo[dt].y, vhi[dt].x, vhi[dt].y};
@@ -510,8 +521,21 @@ __global__ __launch_bounds__(256, 2) void attn2_kernel(AttnArgs a) {
                     __builtin_bit_cast(bf16x8_t, vf), __builtin_bit_cast(bf16x8_t, pf[hh]),
                     o[hh][dt], 0, 0, 0);
         }
+    };
+
+    // Tile 0 goes out first; iteration t waits for tile t (this wave's
+    // loads, then every wave's at the barrier, after which tile t - 1's slot
+    // is free), refills that slot with tile t + 1 and multiplies tile t.
+    if (ntiles > 0) issue(0);
+    f32x4_t sc[HPW][2];
+    for (int t = 0; t < ntiles; ++t) {
+        DG_WAIT_VM(0);
+        attn_barrier();
+        if (t + 1 < ntiles) issue(t + 1);
+        const uint32_t sb = ring0 + (t % RING2) * SLOT2;
+        qk(sb, sc);
+        soft_pv(sb, kb + t * KT2, sc);
     }
-#undef ATT2_ISSUE
 
     // lane holds O^T[d = dt*16 + 4*g4 + e][query r16]
 #pragma unroll
@@ -575,10 +599,10 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
-// The bf16 head-dim-128 kernel (attn2_kernel) takes the shape: heads per
-// wave 2 when the KV group has an even number of query heads, else 1.
+// The bf16 head-dim-128 kernel (attn2_kernel) takes the shape, one query
+// head per wave.
 bool attn2_takes(int dh, bool bf16) { return bf16 && dh == 128; }
-int attn2_hpw(int G) { return G % 2 == 0 ? 2 : 1; }
+int attn2_hpw(int) { return 1; }
 
 int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int max_splits,
                      int* split_len, int dh, bool bf16) {
@@ -601,6 +625,16 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
         splits = (int)std::min<long>(cdiv(kv_len, 2 * KT), std::max<long>(1, cdiv(target, (int)base)));
         splits = std::min(splits, std::min(32, std::max(1, max_splits)));
     }
+    if (v2 && splits > 1) {
+        // round to a count that makes (KV heads x sequences x splits) a
+        // multiple of 8, so that attn2_kernel can keep each key range on one XCD
+        int g = Hkv * B, m = 8;
+        while (m > 1 && g % 2 == 0) {
+            g /= 2;
+            m /= 2;
+        }
+        if (splits >= m) splits = (splits / m) * m;
+    }
     int len = cdiv(cdiv(kv_len, splits), KT) * KT;
     if (len <= 0) len = KT;
     *split_len = len;
@@ -615,9 +649,8 @@ hipError_t attention(const AttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
     if (attn2_takes(a.dh, sizeof(T) == 2)) {
         const int hpw = attn2_hpw(G);
-        dim3 grid2(cdiv(cdiv(a.n, 16) * (G / hpw), 4), a.Hkv, a.B * a.splits);
-        if (hpw == 2) hipLaunchKernelGGL(attn2_kernel<2>, grid2, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL(attn2_kernel<1>, grid2, dim3(256), 0, st, a);
+        dim3 grid2(cdiv(cdiv(a.n, 16) * (G / hpw), 4) * a.Hkv * a.B * a.splits);
+        hipLaunchKernelGGL(attn2_kernel<1>, grid2, dim3(256), 0, st, a);
     } else {
     dim3 grid(cdiv(G * cdiv(a.n, 16), 4), a.Hkv, a.B * a.splits);
     switch (a.dh) {
