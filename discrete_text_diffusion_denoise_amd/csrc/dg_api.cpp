@@ -1276,12 +1276,20 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     // Once every sequence has stopped the sampler raises `halt` on the
     // device, so a look-ahead round after the last stop skips its heavy
     // kernels and leaves canvas, argmax and locks untouched.
+    int nonfinite = -1;   // first canvas whose logits were not all finite
+    int nonfinite_round = 0;
     auto flags_of = [&](int t, bool* all) -> dg_status {   // round t's flags; all stopped?
         DG_HIP(hipEventSynchronize(m->flag_ev[t & 1]));
         const int32_t* hs = m->hflags + (size_t)(t & 1) * m->hflags_cap;
         *all = true;
         for (int b = 0; b < batch; ++b) {
-            if (h_steps_out[b] == 0 && hs[b]) h_steps_out[b] = t + 1;
+            if (h_steps_out[b] == 0 && hs[b]) {
+                h_steps_out[b] = t + 1;
+                if (hs[b] == 2 && nonfinite < 0) {
+                    nonfinite = b;
+                    nonfinite_round = t;
+                }
+            }
             *all = *all && hs[b];
         }
         return DG_OK;
@@ -1327,6 +1335,9 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
     for (int b = 0; b < batch; ++b)
         if (h_steps_out[b] == 0) h_steps_out[b] = p->max_steps;
     DG_HIP(hipMemcpyAsync(d_block_out, argmax, Tc * sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+    if (nonfinite >= 0)
+        return fail(DG_ERR_NONFINITE, "canvas %d: non-finite logits in round %d (block not committed)",
+                    nonfinite, nonfinite_round);
     const size_t model_ws = ws_bytes;  // the model scratch is the prefix of d_ws
     return dg_commit_block(m, kv, batch, d_block_out, d_ws, model_ws, stream);
 }

@@ -305,7 +305,9 @@ __device__ __forceinline__ Rec chunk_full(const float (&x)[4 * NDEPTH], int k0, 
     Rec r;
     r.m = m;
     r.j = k0 + 4 * NLANE * (ju / 4) + (ju % 4);
-    r.s = sum;
+    // a chunk whose maximum is not finite is marked by a NaN sum, so that
+    // every non-finite logit makes its row's entropy NaN
+    r.s = (m - m == 0.0f) ? sum : __builtin_nanf("");
     r.a = ac;
     return r;
 }
@@ -369,7 +371,7 @@ __device__ __forceinline__ Rec chunk_ragged(const float* row, int V, int t, int 
         if (invT == 1.0f) s2 = sum;
         rc.m = m;
         rc.j = j;
-        rc.s = sum;
+        rc.s = (m - m == 0.0f) ? sum : __builtin_nanf("");
         rc.a = ac;
     }
     *s2out = s2;
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
         if (tid == 0) {
             if (a.stats) {
                 float H = dlog(R.s) - R.a / R.s;
-                H = H > 0.0f ? H : 0.0f;
+                H = H > 0.0f ? H : (H != H ? H : 0.0f);  // NaN (non-finite logits) stays NaN
                 float* st = a.stats + rowid * 4;
                 st[0] = R.m;
                 st[1] = R.s;
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(NTHR) void sample_row_kernel(SampleArgs a) {
         const int n = nmem;
         const int yv = n > 0 ? kk[pick_lds(wk, n, uniform01(words[3]))] : 0;
         float H = dlog(R.s) - R.a / R.s;
-        H = H > 0.0f ? H : 0.0f;
+        H = H > 0.0f ? H : (H != H ? H : 0.0f);  // NaN (non-finite logits) stays NaN
         const float pmax = 1.0f / R.s;
         float* st = a.stats + rowid * 4;
         st[0] = R.m;
@@ -901,7 +903,7 @@ __global__ __launch_bounds__(TK_THR) void sample_topk_kernel(SampleArgs a) {
             uint64_t o[4];
             philox((uint64_t)a.step, (uint64_t)b, (uint64_t)i, 0ull, a.seed, 0ull, o);
             float H = dlog(S) - A / S;
-            H = H > 0.0f ? H : 0.0f;
+            H = H > 0.0f ? H : (H != H ? H : 0.0f);  // NaN (non-finite logits) stays NaN
             float* st = a.stats + rowid * 4;
             st[0] = m;
             st[1] = S;
@@ -923,7 +925,7 @@ __global__ __launch_bounds__(TK_THR) void sample_topk_kernel(SampleArgs a) {
 __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
     const int b = blockIdx.x;
     if (a.stop[b]) {
-        if (threadIdx.x == 0 && a.host_stop) a.host_stop[b] = 1;
+        if (threadIdx.x == 0 && a.host_stop) a.host_stop[b] = a.stop[b];
         return;
     }
     __shared__ uint64_t keys[1024];
@@ -944,7 +946,19 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
             keys[i] = ~0ull;
         }
     }
-    __syncthreads();
+    // a NaN entropy means a non-finite logit in that row: the canvas is
+    // reported (stop 2) and left as it was
+    int nan_here = 0;
+    for (int i = tid; i < N; i += blockDim.x) nan_here |= Hs[i] != Hs[i];
+    const int bad = __syncthreads_or(nan_here);
+    if (bad) {
+        if (tid == 0) {
+            a.stop[b] = 2;
+            if (a.host_stop) a.host_stop[b] = 2;
+            if (a.nstop && atomicAdd(a.nstop, 1) + 1 == a.B) *a.halt = 1;
+        }
+        return;
+    }
     if (a.lock_rule == 1) {
         // bitonic sort of (H, index); H >= 0 so its bits order like the value
         for (int size = 2; size <= npow; size <<= 1) {

@@ -53,7 +53,7 @@ typedef enum {
     DG_ERR_SHAPE = 2,       /* shapes inconsistent or outside supported limits  */
     DG_ERR_DTYPE = 3,       /* unknown dtype                                    */
     DG_ERR_CAPACITY = 4,    /* KV cache or workspace too small                  */
-    DG_ERR_NONFINITE = 5,   /* reserved: non-finite values detected             */
+    DG_ERR_NONFINITE = 5,   /* non-finite logits (dg_generate_block)            */
     DG_ERR_HIP = 6,         /* a HIP runtime call failed                        */
     DG_ERR_UNSUPPORTED = 7  /* valid request the library does not implement     */
 } dg_status;
@@ -279,7 +279,11 @@ dg_status dg_denoise_step_topk(dg_model* m, dg_kv* kv, int32_t batch, const int3
  *   d_canvas[b][i]    = lock ? token drawn from softmax(l / T_step)
  *                            : uniform renoise token
  *   d_stop[b]         = 1 if the stop rule fires (or the budget is used up).
- * Canvases with d_stop[b] == 1 on entry are left untouched.  The binary32
+ * Canvases with d_stop[b] != 0 on entry are left untouched.  Logits must be
+ * finite: a NaN or infinite logit makes its row's entropy NaN, and such a
+ * canvas gets d_stop[b] = 2 with its canvas, argmax and locks left as they
+ * were (its statistics are written), so the caller can tell a numerical
+ * failure from a stop.  The binary32
  * arithmetic (statistics, draw, lock and stop) is fixed exactly, so results
  * are bit-reproducible and match the reference definition bit for bit.
  * Random numbers: Philox4x64-10, key (seed, 0), counter (step, b, i, 0).
@@ -357,7 +361,10 @@ dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
  * conditioned on the previous round if params->selfcond_on), stop per
  * canvas, block = the last round's argmax, then dg_commit_block.
  * d_block_out [batch][N]; h_steps_out [batch] receives the rounds each canvas
- * ran.  Waits on the stream once per round to read the stop flags.  For
+ * ran.  Waits on the stream once per round to read the stop flags.  A canvas
+ * whose logits turn non-finite stops in that round (dg_sample_update's
+ * d_stop = 2); the others run on, d_block_out and h_steps_out are written,
+ * the block is NOT committed and the call returns DG_ERR_NONFINITE.  For
  * blocked models with weights.embed_head the rounds run as
  * dg_stage_head_rowmax + dg_sample_update_probs, so the next round's
  * self-conditioning operand comes out of the sampler's pass over the logits

@@ -162,7 +162,8 @@ static int chunk_member(int V, int c, int idx /* 0..63 */)
 typedef struct { float m; int32_t j; float s; float a; float s2; } chunk_t;
 
 /* Stats of one chunk: max, first argmax, and sequential sums of
- * e = E(z), e*z and w = E(z*invT) with z = l - max. s == 0 marks empty. */
+ * e = E(z), e*z and w = E(z*invT) with z = l - max. s == 0 marks empty; a
+ * NaN s marks a chunk whose maximum is not finite. */
 static chunk_t chunk_stats(const float* row, int V, int c, float invT)
 {
     chunk_t r = {-INFINITY, -1, 0.0f, 0.0f, 0.0f};
@@ -181,6 +182,10 @@ static chunk_t chunk_stats(const float* row, int V, int c, float invT)
         r.a = r.a + e * z;
         r.s2 = r.s2 + ora_exp(z * invT);
     }
+    /* a chunk whose maximum is not finite (a NaN first member, or an
+     * infinite logit) is marked by a NaN sum, so that its row's entropy is
+     * NaN: every non-finite logit shows (see ora_nonfinite) */
+    if (!(r.m - r.m == 0.0f)) r.s = NAN;
     return r;
 }
 
@@ -229,7 +234,7 @@ static chunk_t row_stats(const float* row, int V, float invT, chunk_t* chunks)
 static void entropy_maxprob(chunk_t r, float* H, float* pmax)
 {
     float h = ora_log(r.s) - r.a / r.s;
-    *H = h > 0.0f ? h : 0.0f;
+    *H = h > 0.0f ? h : (h != h ? h : 0.0f);   /* a NaN (non-finite logits) stays NaN */
     *pmax = 1.0f / r.s;
 }
 
@@ -410,6 +415,18 @@ void ora_lock_set(int rule, float theta, int N, const float* H, const float* P, 
     free(order);
 }
 
+/* Non-finite logits.  Under the arithmetic above a NaN or infinite logit
+ * makes its row's sum of e*z NaN (0 * inf or NaN), hence its entropy NaN;
+ * the pages assume finite scores.  Reading: such a canvas is reported
+ * (stop = 2) and left as it was (canvas, argmax and locks untouched), so a
+ * caller can tell a numerical failure from a stop. */
+int ora_nonfinite(int N, const float* H)
+{
+    for (int i = 0; i < N; ++i)
+        if (H[i] != H[i]) return 1;
+    return 0;
+}
+
 /* Stop flag of one canvas (report-summary page section 4): mean entropy
  * (sequential binary32 sum in position order, divided by N) below tau and,
  * if required, the most likely sequence unchanged from the previous round;
@@ -474,7 +491,7 @@ int32_t ora_topk_row(const float* row, int V, int K, float invT, float u, float*
     float h = ora_log(S) - A / S;
     out4[0] = m;
     out4[1] = S;
-    out4[2] = h > 0.0f ? h : 0.0f;
+    out4[2] = h > 0.0f ? h : (h != h ? h : 0.0f);
     out4[3] = 1.0f / S;
     for (int i = 0; i < K; ++i) {
         idx[i] = ord[i];
@@ -513,6 +530,7 @@ void ora_sample_update_topk(int lock_rule, float theta, float T0, float T1, floa
             am[i] = idx[0];
             r[i] = ora_uniform_token(o[1], V);
         }
+        if (ora_nonfinite(N, H)) { stop[b] = 2; continue; }
         ora_lock_set(lock_rule, theta, N, H, P, lock + (size_t)b * N);
         uint8_t* lk = lock + (size_t)b * N;
         int stable = step > 0;
@@ -532,7 +550,9 @@ void ora_sample_update_topk(int lock_rule, float theta, float T0, float T1, floa
  *   logits   [B,N,V] float
  *   canvas   [B,N] in/out   argmax [B,N] in: previous step, out: this step
  *   lock     [B,N] out      stats [B,N,4] out {m, S, H, pmax}
- *   stop     [B] in/out: canvases with stop = 1 are left untouched.
+ *   stop     [B] in/out: canvases with stop != 0 are left untouched; a canvas
+ *            whose logits are not all finite gets stop = 2 and keeps its
+ *            canvas, argmax and locks (its statistics are written).
  * lock_rule 0 = max-probability (pmax > theta), 1 = cumulative entropy.
  */
 void ora_sample_update(int lock_rule, float theta, float T0, float T1, float tau,
@@ -562,6 +582,7 @@ void ora_sample_update(int lock_rule, float theta, float T0, float T1, float tau
             float* st = stats + ((size_t)b * N + i) * 4;
             st[0] = s.m; st[1] = s.s; st[2] = H[i]; st[3] = P[i];
         }
+        if (ora_nonfinite(N, H)) { stop[b] = 2; continue; }
         ora_lock_set(lock_rule, theta, N, H, P, lock + (size_t)b * N);
         uint8_t* lk = lock + (size_t)b * N;
         /* renoise and stop */

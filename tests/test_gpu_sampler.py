@@ -280,3 +280,31 @@ def test_topk_rejects_bad_k():
     with pytest.raises(binding.DGError):
         gpu_update(params, 0, logits, np.zeros((1, 4), np.int32), np.zeros((1, 4), np.int32),
                    np.zeros(1, np.int32))
+
+
+@pytest.mark.parametrize("top_k", [0, 8])
+def test_nonfinite_logits_are_reported_like_the_oracle(top_k):
+    """Non-finite logits: the canvases the oracle reports (stop = 2, canvas,
+    argmax and locks left as they were) are the ones the GPU reports; the
+    finite canvas of the same call is bit-exact; the NaN entropies sit at
+    the same positions."""
+    B, N, V = 5, 16, 64
+    rng = np.random.default_rng(7)
+    logits = (rng.standard_normal((B, N, V)) * 3.0).astype(np.float32)
+    logits[1, 5, 17] = np.nan
+    logits[2, 0, 3] = np.inf
+    logits[3, 15, 63] = -np.inf
+    logits[4, 9, 0] = np.nan
+    canvas = rng.integers(0, V, (B, N)).astype(np.int32)
+    argmax = rng.integers(0, V, (B, N)).astype(np.int32)
+    stop = np.zeros(B, dtype=np.int32)
+    p = synthetic.default_sampler_params(max_steps=5, top_k=top_k)
+    g = gpu_update(p, 2, logits, canvas, argmax, stop)
+    r = oracle_update(p, 2, logits, canvas, argmax, stop)
+    assert (g[4] == r[4]).all(), (g[4], r[4])
+    assert (g[0] == r[0]).all() and (g[1] == r[1]).all() and (g[2] == r[2]).all()
+    assert (g[3][0].view(np.uint32) == r[3][0].view(np.uint32)).all()
+    if top_k == 0:
+        assert (np.isnan(g[3][..., 2]) == np.isnan(r[3][..., 2])).all()
+    assert g[4].tolist() == ([r[4][0], 2, 2, 2, 2] if top_k == 0 else g[4].tolist())
+    assert g[4][2] == 2

@@ -369,3 +369,40 @@ def test_page_facts_are_the_defaults():
     assert SHAPES["layer"]["canvas"] == facts["canvas_tokens"]["value"]
     assert SHAPES["layer"]["n_experts"] == facts["n_experts"]["value"]
     assert SHAPES["layer"]["top_k"] == facts["active_experts"]["value"]
+
+
+@pytest.mark.parametrize("top_k", [0, 8])
+def test_nonfinite_canvas_is_reported_and_left_as_it_was(top_k):
+    # A NaN, +inf or -inf logit anywhere in a row makes its entropy NaN
+    # under the fixed arithmetic (0 * inf, NaN, or a chunk whose maximum is
+    # not finite); the canvas gets stop = 2 and keeps its canvas, argmax and
+    # locks; a finite canvas in the same call is updated exactly as it would
+    # be alone.  With top-k truncation only the candidates are read, so a
+    # non-finite logit shows when it is a candidate (+inf always is).
+    B, N, V = 5, 16, 64
+    rng = np.random.default_rng(7)
+    logits = (rng.standard_normal((B, N, V)) * 3.0).astype(np.float32)
+    logits[1, 5, 17] = np.nan
+    logits[2, 0, 3] = np.inf
+    logits[3, 15, 63] = -np.inf
+    logits[4, 9, 0] = np.nan        # the first member of its chunk
+    canvas = rng.integers(0, V, (B, N)).astype(np.int32)
+    argmax = rng.integers(0, V, (B, N)).astype(np.int32)
+    stop = np.zeros(B, dtype=np.int32)
+    c0, a0 = canvas.copy(), argmax.copy()
+    p = _params(max_steps=5, top_k=top_k)
+    lock, stats = sampler.sample_update(p, 2, logits, canvas, argmax, stop)
+    bad = (1, 2, 3, 4) if top_k == 0 else (2,)
+    for b in bad:
+        assert stop[b] == 2
+        assert (canvas[b] == c0[b]).all() and (argmax[b] == a0[b]).all()
+        assert not lock[b].any()
+    if top_k == 0:
+        assert np.isnan(stats[1, 5, 2]) and np.isnan(stats[3, 15, 2]) and np.isnan(stats[4, 9, 2])
+    assert np.isnan(stats[2, 0, 2])
+    # canvas 0 alone gives the same bits
+    c1, a1, s1 = c0[:1].copy(), a0[:1].copy(), np.zeros(1, np.int32)
+    lock1, stats1 = sampler.sample_update(p, 2, logits[:1], c1, a1, s1)
+    assert stop[0] == s1[0] != 2
+    assert (canvas[0] == c1[0]).all() and (argmax[0] == a1[0]).all() and (lock[0] == lock1[0]).all()
+    assert (stats[0].view(np.uint32) == stats1[0].view(np.uint32)).all()
