@@ -1,10 +1,10 @@
 """Training-side forward on the GPU through the C ABI: the multinomial
 corruption and the binary32 cross-entropy bit-exact against the C oracle on
 identical seeded inputs; the whole forward (corrupt, denoise, cross-entropy)
-against the float64 oracle (fp32 1e-4, bf16 2e-2 on positions whose routes
-are not within the GPU's precision of a tie) and bitwise equal to its own
-composition of calls; a full-size layer (vocabulary 262144, prompt 2048) on
-sampled positions."""
+against the float64 oracle stage by stage on the GPU's own inputs (fp32
+1e-4, bf16 2e-2, every position) and bitwise equal to its own composition of
+calls; a full-size layer (vocabulary 262144, prompt 2048) at every
+position."""
 import numpy as np
 import pytest
 import torch
@@ -13,6 +13,7 @@ from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import model as om
 from oracle import sampler as osampler
 
+import chain
 from helpers import DEV, TOL_BF16, normwise, route_ambiguous, to_dev, tol_for
 
 pytestmark = pytest.mark.gpu
@@ -73,15 +74,19 @@ def test_xent_target_outside_vocab_is_nan():
     assert np.isnan(got[1]) and np.isnan(got[2])
 
 
-# bf16 end to end on one layer, as the denoising-step tests: with more, a
-# prompt token whose route the GPU's rounding flips changes its later
-# layers' K/V, which every canvas position reads
-@pytest.mark.parametrize("name,P,B,layers", [("tiny", 40, 2, 2), ("small_bf16", 120, 2, 1),
-                                             ("f32_gqa", 33, 2, 2), ("small_fp8", 120, 1, 1)])
+@pytest.mark.parametrize("name,P,B,layers", [("tiny", 40, 2, 2), ("small_bf16", 120, 2, 2),
+                                             ("f32_gqa", 33, 2, 2), ("small_fp8", 120, 1, 2)])
 def test_train_forward_matches_oracle(name, P, B, layers):
+    """The corrupted canvas bit-exact against the oracle; the cross-entropy
+    bit-exact against the oracle's on the GPU's own logits, every row; the
+    mean the sequential binary32 mean; the logits as a chain of the
+    forward's stages, each against the oracle on the GPU's own input (the
+    MoE with the GPU's route set), every position, equal to the forward's
+    bit for bit; fp32 models also end to end against the oracle's own
+    forward (positions within 1e-4 of a router tie, at most 1 %, skipped)."""
     print(f"train forward {name} P={P} B={B} layers={layers}", flush=True)
     cfg, W, m = setup(name, P, batch=B, n_layers=layers)
-    N, V = cfg["canvas"], cfg["vocab"]
+    N, V, d = cfg["canvas"], cfg["vocab"], cfg["d_model"]
     prompt = synthetic.make_tokens(V, (B, P), seed=21)
     clean = synthetic.make_tokens(V, (B, N), seed=22)
     rate = np.linspace(0.2, 0.9, B).astype(np.float32)
@@ -93,33 +98,42 @@ def test_train_forward_matches_oracle(name, P, B, layers):
     m.train_forward(to_dev(clean), to_dev(rate), 31, 4, x, logits, loss, mean)
     torch.cuda.synchronize()
     assert m.kv_length == P
-    W64 = synthetic.to_float64(W)
-    cache = om.KVCache(cfg, B)
-    om.encode(prompt, W64, cfg, cache)
-    xr, lr, ref_loss, ref_mean = om.train_forward(clean, rate, 31, 4, W64, cfg, cache)
-    assert np.array_equal(x.cpu().numpy(), xr)
-    # positions whose route is ambiguous at the GPU's precision are not compared
-    keep = np.ones((B, N), dtype=bool)
-    for b in range(B):
-        h = om.embed(xr[b], W64)
-        for li, lw in enumerate(W64["layers"]):
-            h, _, _ = om.attn_half(h, lw, cfg, cache.k[li][b], cache.v[li][b], P, causal=False)
-            u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
-            keep[b] &= ~route_ambiguous(u @ lw["w_router"].T, cfg["top_k"],
-                                        route_gap(cfg, chained=True))
-            h, _, _, _ = om.moe_half(h, lw, cfg)
-    assert keep.mean() > 0.5
-    tol = tol_for(cfg)
-    got_l = logits.cpu().numpy()
-    assert normwise(got_l[keep], lr[keep]) <= tol
+    xg = x.cpu().numpy()
+    assert np.array_equal(xg, osampler.corrupt(31, 4, V, rate, clean))
     got_loss = loss.cpu().numpy()
-    assert normwise(got_loss[keep], ref_loss[keep]) <= tol
-    assert abs(float(mean.cpu().numpy()[0]) - ref_mean) <= tol * abs(ref_mean)
-    # the GPU mean is the sequential binary32 mean of its own losses
+    ref_ce, _ = osampler.xent(logits.cpu().numpy().reshape(B * N, V), clean.reshape(-1))
+    assert np.array_equal(got_loss.reshape(-1).view(np.uint32), ref_ce.view(np.uint32))
     acc = np.float32(0.0)
     for v in got_loss.reshape(-1):
         acc = np.float32(acc + v)
     assert mean.cpu().numpy()[0] == np.float32(acc / np.float32(B * N))
+    # the forward's stages on the corrupted canvas
+    tol = tol_for(cfg)
+    W64 = synthetic.to_float64(W)
+    h = torch.empty((B * N, d), dtype=torch.float32, device=DEV)
+    m.stage_input(x, h)
+    for l, lw in enumerate(W["layers"]):
+        lw = chain.layer64(lw)
+        chain.check_attention(m, cfg, lw, l, h, N, False, tol, label=f"train {name}")
+        chain.check_moe(m, cfg, lw, l, h, tol, label=f"train {name}")
+    lc = chain.check_head(m, cfg, W64, h, tol, label=f"train {name}")
+    assert torch.equal(lc.view(B, N, V), logits)
+    if cfg["dtype"] != "f32":
+        return
+    cache = om.KVCache(cfg, B)
+    om.encode(prompt, W64, cfg, cache)
+    xr, lr, ref_loss, ref_mean = om.train_forward(clean, rate, 31, 4, W64, cfg, cache)
+    keep = np.ones((B, N), dtype=bool)
+    for b in range(B):
+        hh = om.embed(xr[b], W64)
+        for li, lw in enumerate(W64["layers"]):
+            hh, _, _ = om.attn_half(hh, lw, cfg, cache.k[li][b], cache.v[li][b], P, causal=False)
+            u = om.rmsnorm(hh, lw["moe_norm"], cfg["rms_eps"])
+            keep[b] &= ~route_ambiguous(u @ lw["w_router"].T, cfg["top_k"], route_gap(cfg))
+            hh, _, _, _ = om.moe_half(hh, lw, cfg)
+    assert keep.mean() >= 0.99
+    assert normwise(logits.cpu().numpy()[keep], lr[keep]) <= tol
+    assert normwise(got_loss[keep], ref_loss[keep]) <= tol
 
 
 def test_train_forward_equals_composition():
@@ -144,7 +158,7 @@ def test_train_forward_equals_composition():
     assert torch.equal(loss, loss2)
 
 
-def test_train_forward_full_layer_sampled_rows():
+def test_train_forward_full_layer():
     cfg = synthetic.model_config("layer")
     P, N, V = synthetic.SHAPES["layer"]["prompt"], cfg["canvas"], cfg["vocab"]
     print("generating full-size layer weights", flush=True)
@@ -163,30 +177,25 @@ def test_train_forward_full_layer_sampled_rows():
     xg = x.cpu().numpy()
     assert np.array_equal(xg, osampler.corrupt(3, 0, V, rate, clean))
     got_loss = loss.cpu().numpy()[0]
-    got_rows = logits[0].cpu().numpy()
-    del m, logits
-    torch.cuda.empty_cache()
-    # the GPU's cross-entropy of its own logits, bit-exact, on sampled rows
-    rows = np.arange(0, N, 16)
-    ref_ce, _ = osampler.xent(got_rows[rows], clean[0, rows])
-    assert np.array_equal(got_loss[rows], ref_ce)
-    print("oracle encode + step", flush=True)
-    SAMPLE = 16
-    lw = {k: np.asarray(v, dtype=np.float64) if k.endswith("norm") or k in ("wq", "wk", "wv", "wo")
-          else v for k, v in W["layers"][0].items()}
+    # the GPU's cross-entropy of its own logits, bit-exact, at every row
+    ref_ce, _ = osampler.xent(logits[0].cpu().numpy(), clean[0])
+    assert np.array_equal(got_loss, ref_ce)
+    # the forward as a chain of its stages on the corrupted canvas, each
+    # against the oracle on the GPU's own input (the MoE with the GPU's
+    # route set), every position; the chain equals the forward bit for bit
+    print("stage chain against the oracle", flush=True)
+    lw = chain.layer64(W["layers"][0])
     Wk = {"embed": W["embed"], "w_sc": W["w_sc"], "final_norm": W["final_norm"], "layers": [lw]}
-    cache = om.KVCache(cfg, 1)
-    om.encode(prompt, Wk, cfg, cache)
-    h = om.embed(xg[0], Wk)
-    h, _, _ = om.attn_half(h, lw, cfg, cache.k[0][0], cache.v[0][0], P, causal=False)
-    u = om.rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
-    amb = route_ambiguous(u @ np.asarray(lw["w_router"], np.float64).T, cfg["top_k"], 3e-2)
-    h, _, _, _ = om.moe_half(h, lw, cfg)
-    # sampled among the positions whose route is not within bf16 precision
-    # of a tie
-    ok = np.flatnonzero(~amb)
-    keep = ok[np.linspace(0, ok.size - 1, SAMPLE).astype(int)]
-    ref = om.xent_rows(om.head(h[keep], Wk, cfg), clean[0, keep])
-    err = normwise(got_loss[keep], ref)
-    print(f"full-layer loss normwise error {err:.3e} over {keep.size} rows", flush=True)
+    h = torch.empty((N, cfg["d_model"]), dtype=torch.float32, device=DEV)
+    m.stage_input(x, h)
+    torch.cuda.synchronize()
+    assert normwise(h.cpu().numpy(), om.embed(xg[0], Wk)) == 0.0
+    chain.check_attention(m, cfg, lw, 0, h, N, False, TOL_BF16, label="train")
+    chain.check_moe(m, cfg, lw, 0, h, TOL_BF16, label="train")
+    lc = chain.check_head(m, cfg, Wk, h, TOL_BF16, label="train")
+    assert torch.equal(lc.view(1, N, V), logits)
+    # the oracle's loss on the chain's final hidden state, every position
+    ref = om.xent_rows(om.head(h.cpu().numpy().astype(np.float64), Wk, cfg), clean[0])
+    err = normwise(got_loss, ref)
+    print(f"full-layer loss normwise error {err:.3e} over {N} rows", flush=True)
     assert err <= TOL_BF16
