@@ -24,6 +24,12 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Maximum under which a NaN ranks above every number (a NaN operand wins).
+// The slab maxima that steer the sampler's top-k candidate search use it, so
+// that a NaN or an infinite logit always reaches the candidates and its row's
+// statistics turn NaN (the row is then reported as non-finite).
+__device__ __forceinline__ float max_nan(float a, float b) { return (a != a || a > b) ? a : b; }
+
 // Element-type traits: loading/storing 8 consecutive k-values of a fragment.
 template <typename T> struct Elt;
 

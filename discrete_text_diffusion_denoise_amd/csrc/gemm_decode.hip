@@ -143,9 +143,9 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) mx = fmaxf(mx, acc[j][q]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            for (int q = 0; q < 4; ++q) mx = max_nan(mx, acc[j][q]);
+        mx = max_nan(mx, __shfl_xor(mx, 16, 64));
+        mx = max_nan(mx, __shfl_xor(mx, 32, 64));
         const int nslab = g.N >> 6;
         if (g4 == 0 && row < g.M) g.rowmax[(long)row * nslab + nt * 4 + wave] = mx;
     }

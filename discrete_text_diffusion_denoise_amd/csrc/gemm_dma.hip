@@ -242,9 +242,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) mx = fmaxf(mx, acc[i][j][q]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                for (int q = 0; q < 4; ++q) mx = max_nan(mx, acc[i][j][q]);
+            mx = max_nan(mx, __shfl_xor(mx, 16, 64));
+            mx = max_nan(mx, __shfl_xor(mx, 32, 64));
             const int row = m0 + wm * 128 + 16 * i + r16;
             if (g4 == 0 && row < g.M && slab < nslab) g.rowmax[(long)row * nslab + slab] = mx;
         }
@@ -355,9 +355,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_head_kernel(GemmArgs g, int r
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, acc[i][j][q]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    for (int q = 0; q < 4; ++q) mx = max_nan(mx, acc[i][j][q]);
+                mx = max_nan(mx, __shfl_xor(mx, 16, 64));
+                mx = max_nan(mx, __shfl_xor(mx, 32, 64));
                 if (g4 == 0 && row < g.M) g.rowmax[(long)row * nslab + c_nt * 4 + wn] = mx;
             }
 #pragma unroll

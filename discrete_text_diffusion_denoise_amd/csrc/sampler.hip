@@ -671,9 +671,12 @@ __global__ __launch_bounds__(256) void selfcond_probs_kernel(const float* __rest
 constexpr int TK_THR = 256;
 constexpr int TK_KEYS = 8192;      // >= (2 * kTopKMax - 1) * 64, a power of two
 
-// Order-preserving unsigned key of a finite float (-0 taken as +0, so keys
-// are equal exactly when the values compare equal).
+// Order-preserving unsigned key of a float (-0 taken as +0, so keys of
+// numbers are equal exactly when the values compare equal); every NaN takes
+// the largest key, above +inf, so NaN ranks above every number and NaNs tie
+// (then the lower index first).
 __device__ __forceinline__ uint32_t okey(float v) {
+    if (v != v) return 0xFFFFFFFFu;
     const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(TK_THR) void sample_topk_kernel(SampleArgs a) {
         for (int sl = tid; sl < nslab; sl += TK_THR) {
             const int k0 = sl * 64, k1 = min(a.V, k0 + 64);
             float mx = row[k0];
-            for (int k = k0 + 1; k < k1; ++k) mx = fmaxf(mx, row[k]);
+            for (int k = k0 + 1; k < k1; ++k) mx = max_nan(mx, row[k]);
             const uint32_t k = okey(mx);
             skey[sl] = k;
             lmin = min(lmin, k);
@@ -1054,11 +1057,15 @@ __global__ __launch_bounds__(64) void mean_seq_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------- greedy (AR mode)
 // Greedy decoding takes each row's largest logit, ties to the lower index.
-// A candidate (v, i) beats (bv, bi) when v > bv, or v == bv and i < bi; NaN
-// entries never win (a row of NaNs gives 0).
+// A NaN ranks above every number (the first NaN of a row is its choice, as
+// numpy's argmax has it), so a non-finite row shows in the decoded token
+// stream instead of being skipped.
 
+// (value, index) maximum: (v, i) beats (bv, bi) when v > bv, or when v is
+// NaN and bv is not, or when they are equal (or both NaN) and i < bi.
 __device__ __forceinline__ void amax_take(float v, int i, float& bv, int& bi) {
-    if (v > bv || (v == bv && i < bi)) {
+    const bool vn = v != v, bn = bv != bv;
+    if ((vn && !bn) || v > bv || ((v == bv || (vn && bn)) && i < bi)) {
         bv = v;
         bi = i;
     }
@@ -1122,9 +1129,9 @@ __global__ __launch_bounds__(AM_THR) void argmax_rows_kernel(const float* __rest
     if (threadIdx.x == 0) out[row * out_stride] = bi == 0x7FFFFFFF ? 0 : bi;
 }
 
-// From the head's 64-column slab maxima (V % 64 == 0): the first slab whose
-// maximum is the row's largest, then the first entry of that slab equal to
-// it.  Every earlier slab's maximum is smaller, so this is the first index
+// From the head's 64-column slab maxima (V % 64 == 0, a NaN member makes its
+// slab's maximum NaN): the first slab whose maximum is the row's largest,
+// then the first entry of that slab equal to it (a NaN, if it is NaN).  Every earlier slab's maximum is smaller, so this is the first index
 // of the row's maximum.
 __global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ rowmax, int V,
@@ -1151,7 +1158,7 @@ __global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restri
         int idx = 0;
         if (bs != 0x7FFFFFFF) {
             const float v = x[row * (long)V + (long)bs * 64 + threadIdx.x];
-            const uint64_t hit = __ballot(v == bv);
+            const uint64_t hit = __ballot(v == bv || (v != v && bv != bv));
             idx = bs * 64 + (hit ? __builtin_ctzll(hit) : 0);
         }
         if (threadIdx.x == 0) out[row * out_stride] = idx;

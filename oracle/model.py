@@ -35,6 +35,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import quant
+
 
 # ---------------------------------------------------------------- primitives
 
@@ -99,11 +101,16 @@ def route(z: np.ndarray, top_k: int):
     return idx, g
 
 
-def moe(u: np.ndarray, lw: dict, top_k: int, idx: np.ndarray | None = None):
+def moe(u: np.ndarray, lw: dict, top_k: int, idx: np.ndarray | None = None,
+        act_mx8: bool = False):
     """Sparse MoE of normalised tokens u [T, d]: router logits z = u W_r^T,
     top-k routing, y_t = sum_e g_e * W_down,e (silu(W_gate,e u) * (W_up,e u)).
     If idx is given it replaces the router's choice (gates still softmax of
-    the chosen logits).  Returns (y [T, d], idx, gates, z)."""
+    the chosen logits).  act_mx8 (the quantised experts): each expert
+    product's input is rounded to MXFP8 along its features first -- u for
+    gate and up (the router still sees u itself), silu(gate) * up for down,
+    before the routing weight (oracle.quant.mx8_round).  Returns (y [T, d],
+    idx, gates, z)."""
     z = u @ lw["w_router"].T
     if idx is None:
         idx, g = route(z, top_k)
@@ -113,12 +120,21 @@ def moe(u: np.ndarray, lw: dict, top_k: int, idx: np.ndarray | None = None):
         g = g / g.sum(axis=1, keepdims=True)
     T, d = u.shape
     y = np.zeros((T, d), dtype=np.float64)
+    xin = quant.mx8_round(u) if act_mx8 else u
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)
-        x = u[rows]
+        x = xin[rows]
         a = silu(x @ lw["w_gate"][e].T) * (x @ lw["w_up"][e].T)
+        if act_mx8:
+            a = quant.mx8_round(a)
         y[rows] += g[rows, slots][:, None] * (a @ lw["w_down"][e].T)
     return y, idx, g, z
+
+
+def act_mx8(cfg: dict) -> bool:
+    """Whether the model's expert products take MXFP8 activations: the
+    quantised expert formats (E4M3 per-row and MXFP4 weights)."""
+    return cfg.get("expert_dtype") in ("fp8", "mxfp4")
 
 
 # ---------------------------------------------------------------- KV cache
@@ -175,7 +191,7 @@ def attn_half(h: np.ndarray, lw: dict, cfg: dict, k_ctx: np.ndarray, v_ctx: np.n
 def moe_half(h: np.ndarray, lw: dict, cfg: dict, idx: np.ndarray | None = None):
     """MoE half-block: h + MoE(RMSNorm(h)).  Returns (h', idx, gates, z)."""
     u = rmsnorm(h, lw["moe_norm"], cfg["rms_eps"])
-    y, idx, g, z = moe(u, lw, cfg["top_k"], idx)
+    y, idx, g, z = moe(u, lw, cfg["top_k"], idx, act_mx8(cfg))
     return h + y, idx, g, z
 
 
@@ -188,9 +204,11 @@ def embed(tokens: np.ndarray, W: dict) -> np.ndarray:
 
 def topk_candidates(row: np.ndarray, K: int) -> np.ndarray:
     """Indices of the K largest entries of a logit row, by value descending,
-    ties to the lower index (the sampler's top-k truncation)."""
+    ties to the lower index (the sampler's top-k truncation); a NaN ranks
+    above every number and NaNs tie among themselves."""
     row = np.asarray(row, dtype=np.float64)
-    order = np.lexsort((np.arange(row.size), -row))
+    nan = np.isnan(row)
+    order = np.lexsort((np.arange(row.size), -np.where(nan, 0.0, row), ~nan))
     return order[:min(K, row.size)]
 
 
@@ -304,7 +322,8 @@ def ar_decode_step(tokens: np.ndarray, W: dict, cfg: dict, cache: KVCache) -> np
 
 def greedy_token(logits: np.ndarray) -> np.ndarray:
     """Greedy choice per row: the index of the largest logit, ties to the
-    lower index."""
+    lower index; a NaN ranks above every number (numpy's argmax returns the
+    first NaN of a row)."""
     return np.argmax(np.asarray(logits), axis=-1).astype(np.int32)
 
 

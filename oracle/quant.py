@@ -37,6 +37,18 @@ value with ties to the even code, magnitudes above 6 clamped to 6.  Readings
 of this library: an all-zero block takes code 0 (X = 2^-127) and zero
 elements; the scale exponent is clamped to [-127, 127]; two elements per byte,
 the even-indexed one in the low nibble.
+
+MXFP8 activations (same specification, element type E4M3, emax = 8 since
+448 = 1.75 * 2^8): the quantised experts multiply 8-bit operands on both
+sides, so the activations entering each expert product are rounded to MXFP8
+first: per token, blocks of 32 consecutive features share the E8M0 scale
+X = 2^(floor(log2(max |v|)) - 8) (clamped to [-127, 127], an all-zero block
+taking -127), and each element is v / X rounded to the nearest E4M3 value
+(ties to the even code), magnitudes at or above 448 giving 448.  Reading:
+the pages name only the 4-bit weight format; the activation format, and that
+it applies to both the gate/up input (the normalised token) and the down
+input (silu(gate) * up, before the routing weight), is this library's
+choice, the plainest one that lets both MFMA operands be 8-bit or narrower.
 """
 from __future__ import annotations
 
@@ -160,12 +172,12 @@ def fp4_encode_array(x: np.ndarray) -> np.ndarray:
     return (c | np.where(neg, 8, 0)).astype(np.uint8)
 
 
-def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
-    """floor(log2(amax)) - 2 per block, clamped to [-127, 127]; -127 for an
-    all-zero block."""
+def mx_scale_exponent(amax: np.ndarray, emax: int = 2) -> np.ndarray:
+    """floor(log2(amax)) - emax per block (emax 2 for E2M1, 8 for E4M3),
+    clamped to [-127, 127]; -127 for an all-zero block."""
     amax = np.asarray(amax, dtype=np.float64)
     m, e = np.frexp(amax)                  # amax = m 2^e, m in [0.5, 1)
-    ex = (e - 1) - 2
+    ex = (e - 1) - emax
     ex = np.where(amax > 0, ex, -127)
     return np.clip(ex, -127, 127).astype(np.int64)
 
@@ -204,3 +216,57 @@ def mx_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     R, K = codes.shape
     x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
     return (table[codes].reshape(R, K // MX_BLOCK, MX_BLOCK) * x[..., None]).reshape(R, K)
+
+
+# ---------------------------------------------------------------- MXFP8
+
+MX8_EMAX = 8
+
+
+def mx8_quantize_rows(x: np.ndarray):
+    """Rows of x [R, K] (K % 32 == 0; float64 or float32 values) -> (E4M3
+    codes uint8 [R, K], E8M0 scale codes uint8 [R, K/32]) by the MXFP8 rule
+    in the module docstring.  The quotient v / X is exact (X is a power of
+    two) and is rounded once, to E4M3."""
+    x = np.asarray(x, dtype=np.float64)
+    R, K = x.shape
+    blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    ex = mx_scale_exponent(np.abs(blocks).max(axis=2), MX8_EMAX)
+    quo = blocks * np.ldexp(1.0, -ex)[..., None]
+    codes = _e4m3_nearest(quo).reshape(R, K)
+    return codes, (ex + 127).astype(np.uint8)
+
+
+def _e4m3_nearest(a: np.ndarray) -> np.ndarray:
+    """E4M3 code of the nearest value to each float64 entry (ties to the even
+    code, saturating at 448, sign kept): the table-neighbour rule of
+    e4m3_encode_array without its binary32 rounding of the input."""
+    a = np.asarray(a, dtype=np.float64)
+    neg = np.signbit(a)
+    m = np.abs(a)
+    hi = np.clip(np.searchsorted(_POS, m), 0, len(_POS) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS) - 1)
+    d_lo = m - _POS[lo]
+    d_hi = _POS[hi] - m
+    c = np.where(d_hi < d_lo, hi, lo)
+    c = np.where(d_hi == d_lo, np.where(lo % 2 == 0, lo, hi), c)
+    c = np.where(m >= E4M3_MAX, 0x7E, c)
+    return (c | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def mx8_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """decode(code) * 2^(scale - 127) per element, in float64 (exact)."""
+    table = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, K = codes.shape
+    X = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (table[codes].reshape(R, K // MX_BLOCK, MX_BLOCK) * X[..., None]).reshape(R, K)
+
+
+def mx8_round(x: np.ndarray) -> np.ndarray:
+    """x [..., K] rounded to MXFP8 along its last axis (quantise, then
+    dequantise), float64."""
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1, x.shape[-1])
+    c, sc = mx8_quantize_rows(flat)
+    return mx8_dequantize_rows(c, sc).reshape(x.shape)

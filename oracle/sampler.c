@@ -448,7 +448,11 @@ int ora_stop_flag(int N, const float* H, int stable, float tau, int require_stab
 /* throughput optimisation).  With K > 0 a position's statistics, draw  */
 /* and self-conditioning use only its K largest logits.                 */
 /*   candidates c_0..c_{K-1}: the K largest entries, ordered by value    */
-/*     descending, ties to the lower index (a total order);             */
+/*     descending, ties to the lower index (a total order); a NaN ranks */
+/*     above every number, NaNs tie among themselves (reading: the pages */
+/*     assume finite scores; this order, that of a positive NaN in IEEE  */
+/*     754 totalOrder, puts any NaN or +inf among the candidates, so the */
+/*     row's statistics turn NaN and its canvas is reported);           */
 /*   m = l[c_0] (the argmax); z_i = l[c_i] - m; e_i = ora_exp(z_i);      */
 /*   S = e_0 + e_1 + ... (in candidate order), A likewise of e_i * z_i;  */
 /*   H = max(0, ora_log(S) - A / S), pmax = 1 / S;                       */
@@ -461,6 +465,8 @@ static int cmp_desc(const void* pa, const void* pb)
 {
     int a = *(const int*)pa, b = *(const int*)pb;
     float x = g_row[a], y = g_row[b];
+    int xn = x != x, yn = y != y;
+    if (xn != yn) return xn ? -1 : 1;
     if (x > y) return -1;
     if (x < y) return 1;
     return a < b ? -1 : (a > b ? 1 : 0);

@@ -100,7 +100,7 @@ def check_moe(m, cfg, lw, layer, h, tol, label=""):
     idx, _ = om.route(z, k)
     same = (np.sort(r, axis=1) == np.sort(idx, axis=1)).all(axis=1)
     assert same[~amb].all(), (label, layer, "route set differs off near ties")
-    y, _, gref, _ = om.moe(u, lw, k, idx=r)
+    y, _, gref, _ = om.moe(u, lw, k, idx=r, act_mx8=om.act_mx8(cfg))
     err = normwise(d_got, y)
     eg = normwise(g, gref)
     print(f"{label} MoE layer {layer}: output {err:.3e}, gates {eg:.3e}, near ties "

@@ -47,6 +47,12 @@ def argmax_case(kind, R, V, seed):
         x[0, :] = -np.inf
         x[1, :] = 0.0
         x[1, ::2] = -0.0
+    elif kind == "nan":
+        # NaN ranks above every number: the first NaN of a row is its choice
+        x[0, 5] = x[0, 3000 % V] = np.nan
+        x[1, V - 1] = np.nan
+        x[1, 0] = np.inf
+        x[2, :] = np.nan
     elif kind == "edges":
         x[0, 0] = 50.0
         x[1, V - 1] = 50.0
@@ -55,7 +61,8 @@ def argmax_case(kind, R, V, seed):
 
 
 ARGMAX_CASES = [("normal", 4, 262144), ("ties", 5, 262144), ("flat", 3, 4096),
-                ("edges", 3, 1001), ("ties", 3, 4099), ("normal", 1, 1)]
+                ("edges", 3, 1001), ("ties", 3, 4099), ("normal", 1, 1),
+                ("nan", 3, 262144), ("nan", 3, 4099)]
 
 
 @pytest.mark.parametrize("kind,R,V", ARGMAX_CASES)

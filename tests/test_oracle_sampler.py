@@ -377,8 +377,9 @@ def test_nonfinite_canvas_is_reported_and_left_as_it_was(top_k):
     # under the fixed arithmetic (0 * inf, NaN, or a chunk whose maximum is
     # not finite); the canvas gets stop = 2 and keeps its canvas, argmax and
     # locks; a finite canvas in the same call is updated exactly as it would
-    # be alone.  With top-k truncation only the candidates are read, so a
-    # non-finite logit shows when it is a candidate (+inf always is).
+    # be alone.  With top-k truncation only the candidates are read; a NaN
+    # ranks above every number, so a NaN or +inf always is a candidate and
+    # shows, while a -inf below K finite logits is no candidate.
     B, N, V = 5, 16, 64
     rng = np.random.default_rng(7)
     logits = (rng.standard_normal((B, N, V)) * 3.0).astype(np.float32)
@@ -392,7 +393,7 @@ def test_nonfinite_canvas_is_reported_and_left_as_it_was(top_k):
     c0, a0 = canvas.copy(), argmax.copy()
     p = _params(max_steps=5, top_k=top_k)
     lock, stats = sampler.sample_update(p, 2, logits, canvas, argmax, stop)
-    bad = (1, 2, 3, 4) if top_k == 0 else (2,)
+    bad = (1, 2, 3, 4) if top_k == 0 else (1, 2, 4)
     for b in bad:
         assert stop[b] == 2
         assert (canvas[b] == c0[b]).all() and (argmax[b] == a0[b]).all()
@@ -400,6 +401,9 @@ def test_nonfinite_canvas_is_reported_and_left_as_it_was(top_k):
     if top_k == 0:
         assert np.isnan(stats[1, 5, 2]) and np.isnan(stats[3, 15, 2]) and np.isnan(stats[4, 9, 2])
     assert np.isnan(stats[2, 0, 2])
+    if top_k:
+        assert np.isnan(stats[1, 5, 2]) and np.isnan(stats[4, 9, 2])
+        assert np.isfinite(stats[3]).all() and stop[3] != 2
     # canvas 0 alone gives the same bits
     c1, a1, s1 = c0[:1].copy(), a0[:1].copy(), np.zeros(1, np.int32)
     lock1, stats1 = sampler.sample_update(p, 2, logits[:1], c1, a1, s1)

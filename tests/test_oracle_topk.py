@@ -103,3 +103,46 @@ def test_update_is_the_rows_composed():
             st, idx, p, y = osampler.topk_row(logits[b, i], K, invT, osampler.uniform(o[0]))
             assert (st == stats[b, i]).all() and argmax[b, i] == idx[0]
             assert canvas[b, i] == (y if lock[b, i] else osampler.uniform_token(o[1], V))
+
+
+def _brute_order(row):
+    """Descending order with NaN above every number, ties (NaNs among
+    themselves, -0 and +0) to the lower index: Python's stable sort on a
+    two-part key."""
+    return sorted(range(len(row)), key=lambda i: (0 if np.isnan(row[i]) else 1,
+                                                  0.0 if np.isnan(row[i]) else -float(row[i])))
+
+
+@pytest.mark.parametrize("K", [1, 3, 8, 40])
+def test_topk_candidates_with_nan_and_inf(K):
+    rng = np.random.default_rng(K)
+    row = rng.standard_normal(40).astype(np.float32)
+    row[[7, 3, 30]] = np.nan
+    row[11] = np.inf
+    row[12] = -np.inf
+    row[5] = -0.0
+    row[6] = 0.0
+    st, idx, p, y = osampler.topk_row(row, K, 1.0, 0.5)
+    assert idx.tolist() == _brute_order(row)[:K]
+    assert idx[0] == 3                       # the first NaN of the row
+    assert np.isnan(st[0]) and np.isnan(st[2])
+    # the model's candidate helper (self-conditioning) takes the same order
+    assert om.topk_candidates(row, K).tolist() == idx.tolist()
+
+
+def test_topk_plus_inf_first_without_nan():
+    row = np.linspace(-3, 3, 50).astype(np.float32)
+    row[20] = np.inf
+    row[21] = -np.inf
+    st, idx, p, y = osampler.topk_row(row, 4, 1.0, 0.5)
+    assert idx.tolist() == [20, 49, 48, 47]
+    assert st[0] == np.inf and np.isnan(st[2])
+    # -inf is no candidate here: the row is finite over its candidates
+    st, idx, p, y = osampler.topk_row(np.delete(row, 20), 4, 1.0, 0.5)
+    assert np.isfinite(st).all()
+
+
+def test_greedy_token_takes_first_nan():
+    x = np.array([[1.0, np.nan, 5.0, np.nan], [np.inf, 2.0, np.inf, -1.0],
+                  [-np.inf, -np.inf, -np.inf, -np.inf]], dtype=np.float32)
+    assert om.greedy_token(x).tolist() == [1, 0, 0]
