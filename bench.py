@@ -21,6 +21,9 @@ entropy stop never fires, so each block runs the full 48 rounds.
   python bench.py --mode ar [--ar-tokens n] [--ar-batch B] [--config ...]
       the retained autoregressive mode: value = decoded tokens/s (greedy
       decoding of n tokens per sequence after the prompt, B sequences)
+  python bench.py --mode moe [--config ...]
+      the mixture-of-experts half alone: value = HBM GB/s of the two expert
+      products (dg_stage_moe of the configuration's canvases)
   python bench.py --mode attn [--config ...]
       the attention block alone (dg_stage_attention) of the configuration's
       canvases over a synthetic cache of its context length: value =
@@ -71,7 +74,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--top-k", type=int, default=0,
                     help="sampler top-k truncation (0: the full distribution)")
-    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar", "train", "attn"],
+    ap.add_argument("--mode", default="diffusion", choices=["diffusion", "ar", "train", "attn", "moe"],
                     help="ar: the retained autoregressive mode (greedy decoding); one step "
                          "= --ar-tokens tokens per sequence after the prompt.  train: the "
                          "training-side forward; one step = corruption + denoiser forward + "
@@ -154,12 +157,15 @@ def kernel_work(name, cfg, B, P, sc_splits):
     if name == "selfcond_gemm":
         # bf16 models read the softmax probabilities in bf16 (written by a pre-pass)
         return 2.0 * T * d * V, T * V * es + d * V * es + sc_splits * T * d * 4.0
+    # quantised experts take MXFP8 activations: a code byte per element and a
+    # scale byte per 32
+    ea = 1.0 + 1.0 / 32 if (fp8 or fp4) else es
     if name == "moe_gateup":
         return (2.0 * T * k * 2 * F * d,
-                hit * 2 * F * (d * ew + (4 if fp8 else 0)) + T * d * es + T * k * F * es)
+                hit * 2 * F * (d * ew + (4 if fp8 else 0)) + T * d * ea + T * k * F * ea)
     if name == "moe_down":
         return (2.0 * T * k * F * d,
-                hit * d * (F * ew + (4 if fp8 else 0)) + T * k * F * es + T * k * d * 4.0)
+                hit * d * (F * ew + (4 if fp8 else 0)) + T * k * F * ea + T * k * d * 4.0)
     if name == "attention":
         L = P + N
         return (4.0 * T * L * Hq * dh,
@@ -266,23 +272,30 @@ def cpu_baseline(cfg, W, prompt, canvas, params, torch):
         hl = {k: v.float().cpu().numpy() for k, v in lw.items()
               if not k.startswith("s_") and not k.startswith("x_")}
         if cfg.get("expert_dtype") == "mxfp4":
-            # the oracle's experts are the dequantised MXFP4 weights
+            # the oracle's experts are the dequantised MXFP4 weights, read
+            # back out of the library's tiled layout (16-row tiles of
+            # 128-column steps; chunk 16 g + r = row r's 32-column block g)
             from oracle import quant as oq
             for k, xk in (("w_gate", "x_gate"), ("w_up", "x_up"), ("w_down", "x_down")):
                 q = lw[k].cpu().numpy()
                 K = 2 * q.shape[-1]
                 R = q.size // q.shape[-1]
-                codes = oq.mx_unpack(q.reshape(R, K // 2))
-                sc = lw[xk].cpu().numpy().reshape(K // 64, R, 2).transpose(1, 0, 2).reshape(R, K // 32)
-                hl[k] = oq.mx_dequantize_rows(codes, sc).reshape(q.shape[:-1] + (K,))
+                S = K // 128
+                packed = q.reshape(R // 16, S, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(R, K // 2)
+                sc = lw[xk].cpu().numpy().reshape(R // 16, S, 4, 16).transpose(0, 3, 1, 2).reshape(
+                    R, K // 32)
+                hl[k] = oq.mx_dequantize_rows(oq.mx_unpack(packed), sc).reshape(q.shape[:-1] + (K,))
         if cfg.get("expert_dtype") == "fp8":
-            # the oracle's experts are the dequantised codes
+            # the oracle's experts are the dequantised codes, read back out of
+            # the tiled layout (two 64-column halves a step, chunk 16 g + r)
             from oracle import quant as oq
             for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
                 q = lw[k].cpu().numpy()
+                K = q.shape[-1]
+                R = q.size // K
+                rows = q.reshape(R // 16, K // 128, 2, 4, 16, 16).transpose(0, 4, 1, 2, 3, 5).reshape(R, K)
                 sc = lw[sk].cpu().numpy()
-                hl[k] = oq.dequantize_rows(q.reshape(-1, q.shape[-1]),
-                                           sc.reshape(-1)).reshape(q.shape)
+                hl[k] = oq.dequantize_rows(rows, sc.reshape(-1)).reshape(q.shape)
         host["layers"].append(hl)
     B, N, V = canvas.shape[0], cfg["canvas"], cfg["vocab"]
     P = prompt.shape[1]
@@ -643,6 +656,86 @@ def bench_attn(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_moe(args):
+    """The mixture-of-experts half alone: dg_stage_moe of the configuration's
+    B canvases of N tokens (N(0, 1) residual rows) through one layer of its
+    expert shape, weights drawn and quantised as in the full bench.  value =
+    algorithmic HBM GB/s of the two expert products together (the weights of
+    every expert the routes hit, read once, plus the activations), timed by
+    the library's HIP events on the launch stream."""
+    import torch
+
+    from discrete_text_diffusion_denoise_amd import binding, synthetic
+
+    shape = synthetic.SHAPES[args.config]
+    cfg = synthetic.model_config(args.config, n_layers=1, vocab=1024)
+    B, N, d = shape["batch"], cfg["canvas"], cfg["d_model"]
+    torch.cuda.init()
+    W = device_weights(cfg, args.seed, torch)
+    m = binding.Model(cfg, W, batch=B, capacity=N + 16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    T = B * N
+    h0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+    h = h0.clone()
+    route = torch.zeros((T, cfg["top_k"]), dtype=torch.int32, device="cuda")
+    gates = torch.zeros((T, cfg["top_k"]), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        h.copy_(h0)
+        m.stage_moe(0, h, route, gates)
+    torch.cuda.synchronize()
+    hit = int(torch.unique(route).numel())
+    cfg["experts_hit"] = hit
+    binding.timer_enable(["moe_gateup", "moe_down"])
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h.copy_(h0)
+        m.stage_moe(0, h, route, gates)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernels, total_bytes, total_ms = {}, 0.0, 0.0
+    for name in ("moe_gateup", "moe_down"):
+        ms, n = binding.timer_read(name)
+        avg = ms / n
+        r = roofline(name, avg, cfg, B, 0, 1)
+        kernels[name] = {"avg_ms": round(avg, 5), "launches": n, "achieved": r["achieved"],
+                         "unit": r["unit"], "frac": r["frac"], "bytes_per_launch": r["bytes_per_launch"]}
+        total_bytes += r["bytes_per_launch"]
+        total_ms += avg
+    binding.timer_enable([])
+    ach = total_bytes / (total_ms * 1e-3) / 1e9
+    fmt = {"fp8": "E4M3 weights, per-row scales", "mxfp4": "MXFP4 weights"}.get(
+        cfg.get("expert_dtype"), cfg["dtype"] + " weights")
+    out = {
+        "metric": "MoE expert GEMM GB/s at 1 MI355X",
+        "value": round(ach, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"] + {"fp8": "+fp8-experts", "mxfp4": "+mxfp4-experts"}.get(
+            cfg.get("expert_dtype"), ""),
+        "data": "synthetic (N(0,1) residual rows, random-init N(0,0.02) weights)",
+        "config": {"workload": (f"moe-{args.config}: MoE half of {B} canvas(es) of {N} tokens, "
+                                f"d {d}, {cfg['n_experts']} experts top-{cfg['top_k']}, d_ff "
+                                f"{cfg['d_ff']} ({fmt}); one step = one dg_stage_moe (RMSNorm, "
+                                f"router, routing, both expert products, combine)"),
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "experts_hit": hit,
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_gateup+moe_down", "bytes_per_launch": total_bytes,
+                     "avg_launch_ms": round(total_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -651,6 +744,9 @@ def main():
         sys.exit(2)
     if args.mode == "ar":
         bench_ar(args)
+        return
+    if args.mode == "moe":
+        bench_moe(args)
         return
     if args.mode == "train":
         bench_train(args)

@@ -438,8 +438,9 @@ def stage_probs(logits, stats, probs, blocked: bool, stream=None):
 
 
 def quantize_fp8(src, q, scale, stream=None):
-    """dg_quantize_fp8: src [..., cols] (f32 or bf16) -> q (uint8, same shape)
-    and scale (f32, one per row)."""
+    """dg_quantize_fp8: src [..., cols] (f32 or bf16; rows % 16 == 0, cols %
+    128 == 0) -> q (uint8, rows * cols bytes in the tiled layout of
+    include/dg.h) and scale (f32, one per row)."""
     cols = src.shape[-1]
     rows = src.numel() // cols
     dt = DG_BF16 if src.dtype == torch.bfloat16 else DG_F32
@@ -447,9 +448,9 @@ def quantize_fp8(src, q, scale, stream=None):
 
 
 def quantize_mxfp4(src, codes, scales, stream=None):
-    """dg_quantize_mxfp4: src [..., cols] (f32 or bf16, cols % 64 == 0) ->
-    codes (uint8 [..., cols/2], two per byte) and scales (uint8, rows * cols/32,
-    laid out [cols/64][rows][2])."""
+    """dg_quantize_mxfp4: src [..., cols] (f32 or bf16; rows % 16 == 0, cols %
+    128 == 0) -> codes (uint8, rows * cols/2 bytes, two codes a byte) and
+    scales (uint8, rows * cols/32), both in the tiled layout of include/dg.h."""
     cols = src.shape[-1]
     rows = src.numel() // cols
     dt = DG_BF16 if src.dtype == torch.bfloat16 else DG_F32

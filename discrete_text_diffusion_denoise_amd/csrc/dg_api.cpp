@@ -166,6 +166,13 @@ struct Scratch {
     int ut_rows = 0;  // rows `ut` holds (the canvas tokens, padded to 256)
     int probs_tiled = 0;  // `probs` in the 64-wide blocked layout (else row-major)
     float* u32;       // bf16 models: fp32 normalised activations for the router
+    // quantised experts: MXFP8 codes and scale codes of the normalised tokens
+    // and of the gate/up output
+    uint8_t* u8 = nullptr;
+    uint8_t* u8s = nullptr;
+    uint8_t* act8 = nullptr;
+    uint8_t* act8s = nullptr;
+    int32_t* work = nullptr;  // expert chunk prefix over the busiest-first order
     float* tmax;      // blocked models: head GEMM row maxima per 64-column slab
     // set by the block loop (not carved): the head GEMM writes its slab
     // maxima (fuse), and the probabilities of the previous round's logits are
@@ -239,6 +246,13 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.tok = cv.take<int32_t>(T);
     const bool wide = c.dtype == DG_BF16;
     s.u32 = wide ? cv.take<float>(T * c.d_model) : nullptr;
+    if (c.expert_dtype == DG_FP8_E4M3 || c.expert_dtype == DG_MXFP4) {
+        s.u8 = cv.take<uint8_t>(T * c.d_model);
+        s.u8s = cv.take<uint8_t>(T * c.d_model / 32);
+        s.act8 = cv.take<uint8_t>(T * c.top_k * c.d_ff);
+        s.act8s = cv.take<uint8_t>(T * c.top_k * c.d_ff / 32);
+        s.work = cv.take<int32_t>(c.n_experts + 1);
+    }
     s.tmax = m->blocked ? cv.take<float>(Tc * (size_t)(c.vocab / 64)) : nullptr;
     s.tk_idx = cv.take<int32_t>(Tc * dg::kTopKMax);
     s.tk_p = cv.take<float>(Tc * dg::kTopKMax);
@@ -402,7 +416,8 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
         // them from the fp32 normalised activations (written by the same
         // kernel as the bf16 ones) and the bf16 router weights widened to
         // fp32 on load, so bf16 rounding of the activations cannot flip it.
-        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32));
+        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32, s.u8,
+                              s.u8s));
         DG_TRY(linear<float>(s.u32, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
                              dg::EPI_STORE_F32, s, st, nullptr, nullptr, 0, 1));
     } else {
@@ -440,6 +455,11 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.w_up = L.w_up;
     a.w_down = L.w_down;
     a.act = s.act;
+    a.u8 = s.u8;
+    a.u8s = s.u8s;
+    a.act8 = s.act8;
+    a.act8s = s.act8s;
+    a.work = s.work;
     a.y = s.y;
     a.h = h;
     a.k_rotate = 1;
@@ -714,15 +734,13 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
     if (c.expert_dtype != 0 && c.expert_dtype != c.dtype && c.expert_dtype != DG_FP8_E4M3 &&
         c.expert_dtype != DG_MXFP4)
         return fail(DG_ERR_DTYPE, "expert_dtype %d", c.expert_dtype);
+    const bool quantised_experts = c.expert_dtype == DG_MXFP4 || c.expert_dtype == DG_FP8_E4M3;
+    if (quantised_experts && (c.dtype != DG_BF16 || c.d_model % 128 || c.d_ff % 128))
+        // the block-scaled MFMA kernels take 128 k per step, 64 gate/up
+        // features and 128 down rows per workgroup
+        return fail(DG_ERR_UNSUPPORTED,
+                    "quantised experts need a bf16 model with d_model and d_ff multiples of 128");
     if (c.expert_dtype == DG_MXFP4) {
-        // the MXFP4 experts run on the direct-to-LDS ring kernels only
-        dg::MoeArgs probe;
-        probe.d = c.d_model;
-        probe.F = c.d_ff;
-        probe.f4 = 1;
-        if (c.dtype != DG_BF16 || !dg::expert_dma_ok(probe))
-            return fail(DG_ERR_UNSUPPORTED,
-                        "MXFP4 experts need a bf16 model with d_model and d_ff multiples of 256");
         for (int l = 0; l < c.n_layers; ++l) {
             const dg_layer_weights& L = w->layers[l];
             if (!L.x_gate || !L.x_up || !L.x_down)
@@ -730,14 +748,6 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
         }
     }
     if (c.expert_dtype == DG_FP8_E4M3) {
-        // the 8-bit experts run on the direct-to-LDS ring kernels only
-        dg::MoeArgs probe;
-        probe.d = c.d_model;
-        probe.F = c.d_ff;
-        probe.f8 = 1;
-        if (c.dtype != DG_BF16 || !dg::expert_dma_ok(probe))
-            return fail(DG_ERR_UNSUPPORTED,
-                        "FP8 experts need a bf16 model with d_model and d_ff multiples of 256");
         for (int l = 0; l < c.n_layers; ++l) {
             const dg_layer_weights& L = w->layers[l];
             if (!L.s_gate || !L.s_up || !L.s_down)
@@ -762,7 +772,8 @@ void dg_model_destroy(dg_model* m) { delete m; }
 dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
                           void* d_q, float* d_scale, void* stream) {
     if (!d_src || !d_q || !d_scale) return fail(DG_ERR_ARG, "NULL pointer");
-    if (rows < 1 || cols < 1 || rows > 0x7FFFFFFF) return fail(DG_ERR_ARG, "bad sizes");
+    if (rows < 16 || cols < 128 || rows % 16 || cols % 128 || rows > 0x7FFFFFFF)
+        return fail(DG_ERR_ARG, "bad sizes (rows a multiple of 16, cols of 128)");
     if (src_dtype == DG_BF16)
         DG_HIP(dg::quantize_fp8<bf16_t>((const bf16_t*)d_src, (long)rows, cols, (uint8_t*)d_q,
                                         d_scale, as_stream(stream)));
@@ -777,8 +788,8 @@ dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, in
 dg_status dg_quantize_mxfp4(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
                             void* d_codes, uint8_t* d_scales, void* stream) {
     if (!d_src || !d_codes || !d_scales) return fail(DG_ERR_ARG, "NULL pointer");
-    if (rows < 1 || cols < 64 || cols % 64 || rows > 0x7FFFFFFF)
-        return fail(DG_ERR_ARG, "bad sizes (cols a multiple of 64)");
+    if (rows < 16 || cols < 128 || rows % 16 || cols % 128 || rows > 0x7FFFFFFF)
+        return fail(DG_ERR_ARG, "bad sizes (rows a multiple of 16, cols of 128)");
     if (src_dtype == DG_BF16)
         DG_HIP(dg::quantize_mxfp4<bf16_t>((const bf16_t*)d_src, (long)rows, cols,
                                           (uint8_t*)d_codes, d_scales, as_stream(stream)));

@@ -2,17 +2,23 @@
 // reduction, transpose, and RoPE with the KV-cache write.
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace dg {
 
 namespace {
 
-// One workgroup per row: sum of squares in fp32, then scale.
+// One workgroup per row: sum of squares in fp32, then scale.  With q8 set,
+// the fp32 result is also written as MXFP8 (d % 32 == 0): E4M3 codes into
+// q8 [rows][d] and the E8M0 scale code of each 32-element block into q8s
+// [rows][d / 32]; a block is the 4 values of 8 consecutive threads.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h,
                                                       const float* __restrict__ w,
                                                       T* __restrict__ u, int d, float eps,
-                                                      float* __restrict__ u32) {
+                                                      float* __restrict__ u32,
+                                                      uint8_t* __restrict__ q8,
+                                                      uint8_t* __restrict__ q8s) {
     const long row = blockIdx.x;
     const float* x = h + row * d;
     float ss = 0.f;
@@ -37,6 +43,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
         o[i + 2] = Elt<T>::from_f(r.z);
         o[i + 3] = Elt<T>::from_f(r.w);
         if (u32) *reinterpret_cast<float4*>(u32 + row * d + i) = r;
+        if (q8) {
+            // the 8 threads of a block hold the same loop trip count (d % 32 == 0)
+            float m = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
+            m = fmaxf(m, __shfl_xor(m, 1, 64));
+            m = fmaxf(m, __shfl_xor(m, 2, 64));
+            m = fmaxf(m, __shfl_xor(m, 4, 64));
+            const int ex = mx8_exponent(m);
+            const float inv = __builtin_amdgcn_ldexpf(1.0f, -ex);   // exact: a power of two
+            const uint32_t code = e4m3_act(r.x * inv) | (e4m3_act(r.y * inv) << 8) |
+                                  (e4m3_act(r.z * inv) << 16) | (e4m3_act(r.w * inv) << 24);
+            *reinterpret_cast<uint32_t*>(q8 + row * d + i) = code;
+            if ((threadIdx.x & 7) == 0) q8s[row * (d / 32) + i / 32] = (uint8_t)(ex + 127);
+        }
     }
 }
 
@@ -270,9 +289,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
 
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
-                   hipStream_t st, float* u32) {
+                   hipStream_t st, float* u32, uint8_t* q8, uint8_t* q8s) {
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, st, h, w, u, d, eps, u32);
+    if (q8 && (d % 32 || !q8s)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, st, h, w, u, d, eps, u32, q8,
+                       q8s);
     return hipGetLastError();
 }
 
@@ -360,7 +381,7 @@ hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int p
 
 #define DG_INST(T)                                                                        \
     template hipError_t rmsnorm<T>(const float*, const float*, T*, int, int, float,        \
-                                   hipStream_t, float*);                                   \
+                                   hipStream_t, float*, uint8_t*, uint8_t*);               \
     template hipError_t embed_rows<T>(const T*, int, const int32_t*, int, int, int, float*, int, \
                                       hipStream_t);                                        \
     template hipError_t splitk_reduce<T>(const float*, T*, int, int, int, hipStream_t,     \

@@ -106,10 +106,12 @@ hipError_t rmsnorm_tiled(const float* h, const float* w, uint16_t* u, int rows, 
 // 256, K = d) or of E^T (transpose 1: rows d, K = V; d % 256 == 0, V % 32 == 0)
 hipError_t embed_tile(const uint16_t* E, int V, int d, int transpose, uint16_t* out,
                       hipStream_t st);
-// u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T; also fp32 into u32 if set)
+// u[t] = h[t] / sqrt(mean(h[t]^2) + eps) * w   (u in T; also fp32 into u32 if
+// set, and MXFP8 codes / scale codes into q8 [rows][d] / q8s [rows][d/32] if set)
 template <typename T>
 hipError_t rmsnorm(const float* h, const float* w, T* u, int rows, int d, float eps,
-                   hipStream_t st, float* u32 = nullptr);
+                   hipStream_t st, float* u32 = nullptr, uint8_t* q8 = nullptr,
+                   uint8_t* q8s = nullptr);
 // h[b*n + i] = E[tok[b*ld + i]] (fp32), b < B, i < n; E has V rows
 template <typename T>
 hipError_t embed_rows(const T* E, int V, const int32_t* tok, int ld, int n, int B, float* h, int d,
@@ -171,21 +173,34 @@ struct MoeArgs {
     float* h = nullptr;              // residual [T][d]
     int k_rotate = 0;                // rotate each block's starting k-stage
     const int32_t* halt = nullptr;   // expert kernels: skip all work when *halt != 0
-    // 8-bit experts: w_gate / w_up / w_down hold E4M3 codes, one fp32 scale
-    // per weight row (s_gate, s_up [E][F]; s_down [E][d])
+    // 8-bit experts: w_gate / w_up / w_down hold E4M3 codes in the tiled
+    // layout of quantize_fp8, one fp32 scale per weight row (s_gate, s_up
+    // [E][F]; s_down [E][d])
     int f8 = 0;
     const float* s_gate = nullptr;
     const float* s_up = nullptr;
     const float* s_down = nullptr;
-    // MXFP4 experts: w_gate / w_up / w_down hold packed E2M1 codes [E][R][K/2]
-    // (the even k in the low nibble); x_* the E8M0 scale codes of each 32-k
-    // block, laid out [K/64][E*R][2] (the two blocks of a 64-k stage of a row
-    // adjacent, the rows of one stage contiguous)
+    // MXFP4 experts: w_gate / w_up / w_down hold packed E2M1 codes and x_*
+    // the E8M0 scale codes of each 32-k block, both in the tiled layout of
+    // quantize_mxfp4 (rows E*R, columns K)
     int f4 = 0;
     const uint8_t* x_gate = nullptr;
     const uint8_t* x_up = nullptr;
     const uint8_t* x_down = nullptr;
+    // quantised experts take MXFP8 activations (E4M3 codes, an E8M0 scale
+    // code per 32 features): the normalised tokens u8 [T][d] / u8s [T][d/32]
+    // (written by the RMSNorm) and the gate/up output act8 [T*k][F] / act8s
+    // [T*k][F/32] (written by the gate/up epilogue)
+    const uint8_t* u8 = nullptr;
+    const uint8_t* u8s = nullptr;
+    uint8_t* act8 = nullptr;
+    uint8_t* act8s = nullptr;
+    // optional [E+1]: exclusive prefix, over the experts in `order`, of their
+    // chunks of kMoeChunk tokens (written with `order` by moe_route): the
+    // work items (expert, chunk) of the block-scaled expert kernels
+    int32_t* work = nullptr;
 };
+constexpr int kMoeChunk = 32;
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);
 template <typename T>
@@ -193,20 +208,30 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st);
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st);
 hipError_t moe_combine(const MoeArgs& a, hipStream_t st);
-// the ring kernels' shape limits (d and F multiples of 256); 8-bit experts
-// run on them only
+// the bf16 ring kernels' shape limits (d and F multiples of 256)
 bool expert_dma_ok(const MoeArgs& a);
+// quantised experts (f4 or f8) on the block-scaled MFMA: d and F multiples of
+// 128, MXFP8 activations in u8 / u8s, act8 / act8s written by the gate/up
+// product and read by the down product
+bool expert_mx_ok(const MoeArgs& a);
+hipError_t moe_gateup_mx(const MoeArgs& a, hipStream_t st);
+hipError_t moe_down_mx(const MoeArgs& a, hipStream_t st);
 
-// E4M3 codes and per-row scales of src [rows][cols] (T = float or bf16_t):
-// scale = max|x| / 448 (1 for a zero row), code = round-to-nearest-even of
-// x / scale, saturating at 448
+// E4M3 codes and per-row scales of src [rows][cols] (T = float or bf16_t;
+// rows % 16 == 0, cols % 128 == 0): scale = max|x| / 448 (1 for a zero row),
+// code = round-to-nearest-even of x / scale, saturating at 448.  Codes in the
+// expert kernels' tiled layout: per 16-row tile and 128-column step, two
+// 1-KiB halves (columns 0..63, 64..127), chunk 16 g + r of half h holding
+// row r's columns 64 h + 16 g .. +15; the tile's steps follow one another
 template <typename T>
 hipError_t quantize_fp8(const T* src, long rows, int cols, uint8_t* q, float* scale,
                         hipStream_t st);
 
-// MXFP4 codes and scale codes of src [rows][cols] (cols % 64 == 0), in the
-// expert kernels' layout (MoeArgs::f4): codes [rows][cols/2], scale codes
-// [cols/64][rows][2]
+// MXFP4 codes and scale codes of src [rows][cols] (rows % 16 == 0, cols % 128
+// == 0), in the expert kernels' tiled layout: per 16-row tile and 128-column
+// step, 1 KiB of codes (chunk 16 g + r: row r's 32-column block g, two codes
+// a byte, the even column low) and 64 scale codes (byte 16 g + r); the tile's
+// steps follow one another, then the next tile
 template <typename T>
 hipError_t quantize_mxfp4(const T* src, long rows, int cols, uint8_t* q, uint8_t* scale,
                           hipStream_t st);

@@ -84,17 +84,50 @@ __global__ __launch_bounds__(256) void count_kernel(MoeArgs a) {
     if (threadIdx.x == 0) a.counts[e] = part[0];
 }
 
-// Experts by falling count (ties: lower id) from the counts.
-__global__ __launch_bounds__(256) void order_kernel(MoeArgs a) {
-    const int e = threadIdx.x;
-    if (e >= a.E) return;
-    const int me = a.counts[e];
-    int rank = 0;
-    for (int e2 = 0; e2 < a.E; ++e2) {
-        const int o = a.counts[e2];
-        rank += (o > me) || (o == me && e2 < e);
+// work[r] for r = 0 .. E: exclusive prefix of ch[0 .. E) (chunks of the
+// expert of rank r, in LDS), by threads 0..63 of the block, four each.
+__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) {
+    const int tid = threadIdx.x;
+    if (tid >= 64) return;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = tid * 4 + q < E ? ch[tid * 4 + q] : 0;
+        sum += v[q];
     }
-    a.order[rank] = e;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += y;
+    }
+    int ex = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (tid * 4 + q < E) work[tid * 4 + q] = ex;
+        ex += v[q];
+    }
+    if (tid == 63) work[E] = incl;
+}
+
+// Experts by falling count (ties: lower id) from the counts, and the chunk
+// prefix over that order.
+__global__ __launch_bounds__(256) void order_kernel(MoeArgs a) {
+    __shared__ int ch[256];
+    const int e = threadIdx.x;
+    if (e < a.E) {
+        const int me = a.counts[e];
+        int rank = 0;
+        for (int e2 = 0; e2 < a.E; ++e2) {
+            const int o = a.counts[e2];
+            rank += (o > me) || (o == me && e2 < e);
+        }
+        a.order[rank] = e;
+        ch[rank] = cdiv(me, kMoeChunk);
+    }
+    if (!a.work) return;
+    __syncthreads();
+    write_work(ch, a.E, a.work);
 }
 
 // One wave per expert: exclusive prefix of counts, then a stable, ordered
@@ -304,55 +337,24 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
 // One expert's token groups against one block of weight rows: a four-stage
 // ring of direct-to-LDS loads (8 KiB of weight rows x 64 k and 32 * G token
 // rows x 64 k per stage), G = 1 or 2 groups of 32 tokens per pass over the
-// weights.  bf16 weights: 64 rows (two halves of 32 columns) per block.
-// F8: 128 rows of E4M3 codes (two halves of 64 columns; 64 bytes per row and
-// stage), widened to bf16 in registers (exactly: E4M3 values are bf16
-// values) and scaled per output column after the sum.
+// weights: 64 rows (two halves of 32 columns) per block.  (Quantised
+// experts run on the block-scaled MFMA kernels of moe_mx.hip.)
 struct XdCtx {
     int e, off, cnt, K, NOUT, c0, n, rot;
     int lane, wave, r16, g4, ct, mp, lr, lc;
     const char* wsrc[2];     // byte addresses of this lane's weight chunks at k = 0
     const bf16_t* X;
-    const uint8_t* ssrc;     // MXFP4: this lane's 16 scale bytes of stage 0
-    long sstride;            // MXFP4: scale bytes from one stage to the next
 };
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// 8 E4M3 codes (two words, increasing k) -> 8 bf16 values
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    return u32x4{pack_bf2(a.x, a.y), pack_bf2(b.x, b.y), pack_bf2(c.x, c.y), pack_bf2(d.x, d.y)};
-}
-
-// 8 E2M1 codes (a word, the even k in the low nibble of each byte) times a
-// power-of-two scale -> 8 bf16 values, exact (every such product is a bf16
-// value): gfx950 converts the two codes of a selected byte per instruction,
-// low nibble first (checked on all 256 bytes and several scales)
-__device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t w, float scale) {
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
-}
-
-// FMT: 0 bf16 weights, 1 E4M3 codes with per-row scales, 2 MXFP4 (E2M1 codes,
-// an E8M0 scale per 32 k)
-template <int MODE, int G, int FMT>
+template <int MODE, int G>
 __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, unsigned char* w0,
                                               unsigned char* w1, unsigned char* w2, unsigned char* w3,
                                               unsigned char* x0, unsigned char* x1, unsigned char* x2,
-                                              unsigned char* x3, unsigned char* s0, unsigned char* s1,
-                                              unsigned char* s2, unsigned char* s3) {
-    constexpr bool F8 = FMT == 1, F4 = FMT == 2;
+                                              unsigned char* x3) {
     constexpr int WQ = 2;                              // weight DMAs per wave per stage
-    constexpr int SQ = F4 ? 1 : 0;                     // scale DMAs per wave per stage
-    constexpr int PER = WQ + G + SQ;                   // DMAs per wave per stage
-    constexpr int WSTAGE = F4 ? 32 : (F8 ? 64 : 128);  // weight bytes per row and stage
-    constexpr int J = F4 ? 4 : (F8 ? 2 : 1);           // 16-column tiles per half and wave
+    constexpr int PER = WQ + G;                        // DMAs per wave per stage
+    constexpr int WSTAGE = 128;                        // weight bytes per row and stage
+    constexpr int J = 1;                               // 16-column tiles per half and wave
     constexpr int HALF = 32 * J;                       // columns per half of the block
     const int n = c.n, rot = c.rot, mp = c.mp, ct = c.ct, r16 = c.r16, g4 = c.g4;
     const int wblk = c.wave * WQ * 1024;
@@ -360,24 +362,9 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
     const int roff = r16 * 128;
     // output columns of the lane (tile ct + 2j of the first half; the
     // second half is the up projection, or the down columns HALF later)
-    // and, for 8-bit weights, their scales
     int col[J];
-    float sc0[J], sc1[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        col[j] = c.c0 + (ct + 2 * j) * 16 + r16;
-        sc0[j] = 1.0f;
-        sc1[j] = 1.0f;
-        if (F8 && col[j] < c.NOUT) {
-            if (MODE == 0) {
-                sc0[j] = a.s_gate[(long)c.e * c.NOUT + col[j]];
-                sc1[j] = a.s_up[(long)c.e * c.NOUT + col[j]];
-            } else {
-                sc0[j] = a.s_down[(long)c.e * c.NOUT + col[j]];
-                sc1[j] = col[j] + HALF < c.NOUT ? a.s_down[(long)c.e * c.NOUT + col[j] + HALF] : 1.0f;
-            }
-        }
-    }
+    for (int j = 0; j < J; ++j) col[j] = c.c0 + (ct + 2 * j) * 16 + r16;
     for (int mg = 0; mg < c.cnt; mg += 32 * G) {
         const bf16_t* xsrc[G];
 #pragma unroll
@@ -400,7 +387,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             tv[q] = mg + 16 * (mp + 2 * q) < c.cnt;
         }
 
-#define XD_ISSUE(ST, WB, XB, SB)                                                                  \
+#define XD_ISSUE(ST, WB, XB)                                                                      \
         {                                                                                         \
             int sr_ = (ST) + rot;                                                                 \
             if (sr_ >= n) sr_ -= n;                                                               \
@@ -411,120 +398,18 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             _Pragma("unroll") for (int q = 0; q < G; ++q)                                         \
                 __builtin_amdgcn_global_load_lds((glb_void*)(xsrc[q] + k_),                       \
                                                  (lds_void*)((XB) + xblk + q * 1024), 16, 0, 0);  \
-            if (F4 && c.lane < 8)                                                                 \
-                __builtin_amdgcn_global_load_lds((glb_void*)(c.ssrc + (long)sr_ * c.sstride),     \
-                                                 (lds_void*)((SB) + c.wave * 128), 16, 0, 0);     \
         }
         // fragments: token rows 16*(mp + 2q) + r16; weight rows (ct + 2j)*16
-        // + r16 of each half.  bf16 weights: k-step s of a lane is chunk
-        // 4*s + g4 of both operands; 8-bit weights: the lane's 16 codes are
-        // chunk g4 of the 64-byte row (k 16*g4 .. 16*g4+15), so its token
-        // chunks are 2*g4 (k-step 0) and 2*g4 + 1 (k-step 1): every k of the
-        // stage is in exactly one k-step of one lane group, as the sum needs
-#define XD_COMPUTE(WB, XB, SB)                                                                    \
+        // + r16 of each half; k-step s of a lane is chunk 4*s + g4 of both
+        // operands
+#define XD_COMPUTE(WB, XB)                                                                        \
         {                                                                                         \
             u32x4 fga[J], fgb[J], fua[J], fub[J], fxa[G], fxb[G];                                 \
             const uint32_t xa = lds_addr(XB) + (16 * mp) * 128 + roff;                            \
             const int xs = r16 & 7;                                                               \
-            const uint32_t sa = (F8 || F4) ? ((2 * g4) ^ xs) << 4 : (g4 ^ xs) << 4;               \
-            const uint32_t sb = (F8 || F4) ? ((2 * g4 + 1) ^ xs) << 4 : ((4 + g4) ^ xs) << 4;     \
-            if (F4) {                                                                             \
-                /* weight row (ct + 2j)*16 + r16 of each half (32 bytes a row,  */                \
-                /* 16-byte chunk c in slot c ^ bit 3 of the row): the lane's 8  */                \
-                /* bytes are codes k 16*g4 .. 16*g4+15 of the stage, one MX     */                \
-                /* block, whose scale byte sits at half*256 + row*2 + g4/2      */                \
-                const int wr0 = ct * 16 + r16;                                                    \
-                const uint32_t wq_ = lds_addr(WB) + wr0 * 32 +                                    \
-                                     ((((g4 >> 1) ^ ((r16 >> 3) & 1))) << 4) + ((g4 & 1) << 3);   \
-                const uint32_t sq_ = lds_addr(SB) + wr0 * 2 + (g4 >> 1);                          \
-                uint2 cw[2 * J];                                                                  \
-                uint32_t cs[2 * J];                                                               \
-                if (G == 1) {                                                                     \
-                    asm volatile(                                                                 \
-                        "ds_read_b128 %0, %18\n ds_read_b128 %1, %19\n"                            \
-                        "ds_read_b64 %2, %20 offset:0\n ds_read_b64 %3, %20 offset:1024\n"        \
-                        "ds_read_b64 %4, %20 offset:2048\n ds_read_b64 %5, %20 offset:3072\n"     \
-                        "ds_read_b64 %6, %20 offset:4096\n ds_read_b64 %7, %20 offset:5120\n"     \
-                        "ds_read_b64 %8, %20 offset:6144\n ds_read_b64 %9, %20 offset:7168\n"     \
-                        "ds_read_u8 %10, %21 offset:0\n ds_read_u8 %11, %21 offset:64\n"          \
-                        "ds_read_u8 %12, %21 offset:128\n ds_read_u8 %13, %21 offset:192\n"       \
-                        "ds_read_u8 %14, %21 offset:256\n ds_read_u8 %15, %21 offset:320\n"       \
-                        "ds_read_u8 %16, %21 offset:384\n ds_read_u8 %17, %21 offset:448\n"       \
-                        "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]),   \
-                          "=&v"(cw[3]), "=&v"(cw[4]), "=&v"(cw[5]), "=&v"(cw[6]), "=&v"(cw[7]),     \
-                          "=&v"(cs[0]), "=&v"(cs[1]), "=&v"(cs[2]), "=&v"(cs[3]), "=&v"(cs[4]),     \
-                          "=&v"(cs[5]), "=&v"(cs[6]), "=&v"(cs[7])                                \
-                        : "v"(xa + sa), "v"(xa + sb), "v"(wq_), "v"(sq_)                          \
-                        : "memory");                                                              \
-                } else {                                                                          \
-                    asm volatile(                                                                 \
-                        "ds_read_b128 %0, %20\n ds_read_b128 %1, %21\n"                            \
-                        "ds_read_b128 %2, %20 offset:4096\n ds_read_b128 %3, %21 offset:4096\n"   \
-                        "ds_read_b64 %4, %22 offset:0\n ds_read_b64 %5, %22 offset:1024\n"        \
-                        "ds_read_b64 %6, %22 offset:2048\n ds_read_b64 %7, %22 offset:3072\n"     \
-                        "ds_read_b64 %8, %22 offset:4096\n ds_read_b64 %9, %22 offset:5120\n"     \
-                        "ds_read_b64 %10, %22 offset:6144\n ds_read_b64 %11, %22 offset:7168\n"   \
-                        "ds_read_u8 %12, %23 offset:0\n ds_read_u8 %13, %23 offset:64\n"          \
-                        "ds_read_u8 %14, %23 offset:128\n ds_read_u8 %15, %23 offset:192\n"       \
-                        "ds_read_u8 %16, %23 offset:256\n ds_read_u8 %17, %23 offset:320\n"       \
-                        "ds_read_u8 %18, %23 offset:384\n ds_read_u8 %19, %23 offset:448\n"       \
-                        "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
-                          "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(cw[4]),     \
-                          "=&v"(cw[5]), "=&v"(cw[6]), "=&v"(cw[7]), "=&v"(cs[0]), "=&v"(cs[1]),     \
-                          "=&v"(cs[2]), "=&v"(cs[3]), "=&v"(cs[4]), "=&v"(cs[5]), "=&v"(cs[6]),     \
-                          "=&v"(cs[7])                                                            \
-                        : "v"(xa + sa), "v"(xa + sb), "v"(wq_), "v"(sq_)                          \
-                        : "memory");                                                              \
-                }                                                                                 \
-                _Pragma("unroll") for (int j = 0; j < J; ++j) {                                   \
-                    const float fg_ = __builtin_amdgcn_ldexpf(1.0f, (int)cs[j] - 127);            \
-                    const float fu_ = __builtin_amdgcn_ldexpf(1.0f, (int)cs[J + j] - 127);        \
-                    fga[j] = e2m1x8_to_bf16(cw[j].x, fg_);                                        \
-                    fgb[j] = e2m1x8_to_bf16(cw[j].y, fg_);                                        \
-                    fua[j] = e2m1x8_to_bf16(cw[J + j].x, fu_);                                    \
-                    fub[j] = e2m1x8_to_bf16(cw[J + j].y, fu_);                                    \
-                }                                                                                 \
-            } else if (F8) {                                                                             \
-                const int wr0 = ct * 16 + r16, wr1 = wr0 + 32;                                    \
-                const uint32_t wb_ = lds_addr(WB);                                                \
-                const uint32_t g0_ = wb_ + wr0 * 64 + ((g4 ^ swz(wr0)) << 4);                    \
-                const uint32_t g1_ = wb_ + wr1 * 64 + ((g4 ^ swz(wr1)) << 4);                    \
-                const uint32_t u0_ = wb_ + (wr0 + 64) * 64 + ((g4 ^ swz(wr0 + 64)) << 4);        \
-                const uint32_t u1_ = wb_ + (wr1 + 64) * 64 + ((g4 ^ swz(wr1 + 64)) << 4);        \
-                u32x4 cg0, cg1, cu0, cu1;                                                         \
-                if (G == 1) {                                                                     \
-                    asm volatile(                                                                 \
-                        "ds_read_b128 %0, %6\n ds_read_b128 %1, %7\n"                              \
-                        "ds_read_b128 %2, %8\n ds_read_b128 %3, %9\n"                              \
-                        "ds_read_b128 %4, %10\n ds_read_b128 %5, %11\n"                            \
-                        "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(cg0), "=&v"(cg1), "=&v"(cu0), "=&v"(cu1) \
-                        : "v"(xa + sa), "v"(xa + sb), "v"(g0_), "v"(g1_), "v"(u0_), "v"(u1_)      \
-                        : "memory");                                                              \
-                } else {                                                                          \
-                    asm volatile(                                                                 \
-                        "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n"                              \
-                        "ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"                            \
-                        "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n"                            \
-                        "ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"                            \
-                        "s_waitcnt lgkmcnt(0)"                                                     \
-                        : "=&v"(fxa[0]), "=&v"(fxb[0]), "=&v"(fxa[G - 1]), "=&v"(fxb[G - 1]),      \
-                          "=&v"(cg0), "=&v"(cg1), "=&v"(cu0), "=&v"(cu1)                          \
-                        : "v"(xa + sa), "v"(xa + sb), "v"(xa + 32 * 128 + sa),                    \
-                          "v"(xa + 32 * 128 + sb), "v"(g0_), "v"(g1_), "v"(u0_), "v"(u1_)         \
-                        : "memory");                                                              \
-                }                                                                                 \
-                fga[0] = e4m3x8_to_bf16(cg0[0], cg0[1]);                                          \
-                fgb[0] = e4m3x8_to_bf16(cg0[2], cg0[3]);                                          \
-                fua[0] = e4m3x8_to_bf16(cu0[0], cu0[1]);                                          \
-                fub[0] = e4m3x8_to_bf16(cu0[2], cu0[3]);                                          \
-                fga[J - 1] = e4m3x8_to_bf16(cg1[0], cg1[1]);                                      \
-                fgb[J - 1] = e4m3x8_to_bf16(cg1[2], cg1[3]);                                      \
-                fua[J - 1] = e4m3x8_to_bf16(cu1[0], cu1[1]);                                      \
-                fub[J - 1] = e4m3x8_to_bf16(cu1[2], cu1[3]);                                      \
-            } else {                                                                              \
+            const uint32_t sa = (g4 ^ xs) << 4;                                                   \
+            const uint32_t sb = ((4 + g4) ^ xs) << 4;                                             \
+            {                                                                                     \
                 const uint32_t wa = lds_addr(WB) + (ct * 16) * 128 + roff;                        \
                 if (G == 1) {                                                                     \
                     asm volatile(                                                                 \
@@ -566,7 +451,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                 }                                                                                 \
             }                                                                                     \
         }
-#define XD_STAGE(t, CW, CX, CS, NW, NX, NS)                  \
+#define XD_STAGE(t, CW, CX, NW, NX)                          \
         {                                                    \
             if ((t) + 2 < n)                                 \
                 DG_WAIT_VM(2 * PER);                         \
@@ -575,17 +460,17 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
             else                                             \
                 DG_WAIT_VM(0);                               \
             barrier_lds();                                   \
-            if ((t) + 3 < n) XD_ISSUE((t) + 3, NW, NX, NS);  \
-            XD_COMPUTE(CW, CX, CS);                          \
+            if ((t) + 3 < n) XD_ISSUE((t) + 3, NW, NX);      \
+            XD_COMPUTE(CW, CX);                              \
         }
-        XD_ISSUE(0, w0, x0, s0);
-        XD_ISSUE(1, w1, x1, s1);
-        XD_ISSUE(2, w2, x2, s2);
+        XD_ISSUE(0, w0, x0);
+        XD_ISSUE(1, w1, x1);
+        XD_ISSUE(2, w2, x2);
         for (int t = 0; t < n; t += 4) {
-            XD_STAGE(t, w0, x0, s0, w3, x3, s3);
-            XD_STAGE(t + 1, w1, x1, s1, w0, x0, s0);
-            XD_STAGE(t + 2, w2, x2, s2, w1, x1, s1);
-            XD_STAGE(t + 3, w3, x3, s3, w2, x2, s2);
+            XD_STAGE(t, w0, x0, w3, x3);
+            XD_STAGE(t + 1, w1, x1, w0, x0);
+            XD_STAGE(t + 2, w2, x2, w1, x1);
+            XD_STAGE(t + 3, w3, x3, w2, x2);
         }
 #undef XD_STAGE
 #undef XD_COMPUTE
@@ -603,16 +488,15 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
                     const int row = mg + 16 * (mp + 2 * q) + 4 * g4 + i;
                     if (row >= c.cnt) continue;
                     if constexpr (MODE == 0) {
-                        const float gv = F8 ? ag[q][j][i] * sc0[j] : ag[q][j][i];
-                        const float uv = F8 ? au[q][j][i] * sc1[j] : au[q][j][i];
+                        const float gv = ag[q][j][i];
+                        const float uv = au[q][j][i];
                         const float sv = gv / (1.0f + __expf(-gv));
                         reinterpret_cast<bf16_t*>(a.act)[(long)(c.off + row) * a.F + col[j]] =
                             f2bf(sv * uv);
                     } else {
-                        a.y[(long)(c.off + row) * a.d + col[j]] = F8 ? ag[q][j][i] * sc0[j] : ag[q][j][i];
+                        a.y[(long)(c.off + row) * a.d + col[j]] = ag[q][j][i];
                         if (col[j] + HALF < c.NOUT)
-                            a.y[(long)(c.off + row) * a.d + col[j] + HALF] =
-                                F8 ? au[q][j][i] * sc1[j] : au[q][j][i];
+                            a.y[(long)(c.off + row) * a.d + col[j] + HALF] = au[q][j][i];
                     }
                 }
             }
@@ -622,24 +506,19 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
     }
 }
 
-// Blocks of weight rows (bf16: 64 rows = gate and up rows of 32 columns
-// (MODE 0) or 64 columns of the down projection (MODE 1); 8-bit: 128 rows,
-// twice the columns); blockIdx.y walks the experts in `order` when it is
-// set.  An expert with at most 32 tokens (most of them: a 256-token canvas
+// Blocks of 64 weight rows (gate and up rows of 32 columns (MODE 0) or 64
+// columns of the down projection (MODE 1)); blockIdx.y walks the experts in
+// `order` when it is set.  An expert with at most 32 tokens (most of them: a 256-token canvas
 // makes 2048 assignments over 128 experts) runs groups of 32, a busier one
 // groups of 64, so its weights are streamed fewer times.
-template <int MODE, int FMT>
+template <int MODE>
 __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.halt && *a.halt) return;
-    constexpr bool F8 = FMT == 1, F4 = FMT == 2;
     __shared__ __align__(1024) unsigned char w0[64 * 128], x0[8192];
     __shared__ __align__(1024) unsigned char w1[64 * 128], x1[8192];
     __shared__ __align__(1024) unsigned char w2[64 * 128], x2[8192];
     __shared__ __align__(1024) unsigned char w3[64 * 128], x3[8192];
-    // MXFP4 scale bytes of a stage: 256 rows x 2 blocks
-    __shared__ __align__(16) unsigned char s0[F4 ? 512 : 16], s1[F4 ? 512 : 16];
-    __shared__ __align__(16) unsigned char s2[F4 ? 512 : 16], s3[F4 ? 512 : 16];
-    constexpr int HALF = F4 ? 128 : (F8 ? 64 : 32);    // columns per half of a block
+    constexpr int HALF = 32;                           // columns per half of a block
 
     XdCtx c;
     // the busiest experts first, so their longer blocks do not form the tail
@@ -670,24 +549,7 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     c.lc = ((c.lane & 7) ^ c.lr) * 8;                 // element offset (rows are 8-aligned)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        if (F4) {
-            // weight DMA lanes: an instruction fills 32 rows x 32 bytes; lane
-            // l takes row l / 2 and global chunk (l % 2) ^ (bit 3 of the row)
-            const int r = (c.wave * 2 + q) * 32 + (c.lane >> 1);   // row within the block
-            const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
-            const int col = min(c.c0 + rr, c.NOUT - 1);
-            const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
-            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * (c.K / 2) +
-                        (((c.lane & 1) ^ ((r >> 3) & 1)) << 4);
-        } else if (F8) {
-            // weight DMA lanes: an instruction fills 16 rows x 64 bytes; lane l
-            // takes row l / 4 and global chunk (l % 4) ^ swz(row)
-            const int r = (c.wave * 2 + q) * 16 + (c.lane >> 2);   // row within the block
-            const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
-            const int col = min(c.c0 + rr, c.NOUT - 1);
-            const char* base = (MODE == 0 && r >= HALF) ? Wu : Wg;
-            c.wsrc[q] = base + ((long)c.e * c.NOUT + col) * c.K + (((c.lane & 3) ^ swz(r)) << 4);
-        } else {
+        {
             const int r = (c.wave * 2 + q) * 8 + c.lr;             // row within the block
             const int rr = MODE == 0 ? (r & (HALF - 1)) : r;
             const int col = min(c.c0 + rr, c.NOUT - 1);
@@ -695,20 +557,10 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
             c.wsrc[q] = base + (((long)c.e * c.NOUT + col) * c.K + c.lc) * 2;
         }
     }
-    c.ssrc = nullptr;
-    c.sstride = 0;
-    if (F4) {
-        // scale DMA lanes 0..7 of wave w: bytes [128 w, 128 w + 128) of the
-        // stage's 512 (gate rows c0.. then up rows c0.., or down rows c0..)
-        const uint8_t* X = MODE == 0 ? (c.wave < 2 ? a.x_gate : a.x_up) : a.x_down;
-        const int piece = MODE == 0 ? (c.wave & 1) : c.wave;
-        c.ssrc = X + ((long)c.e * c.NOUT + c.c0) * 2 + piece * 128 + (c.lane & 7) * 16;
-        c.sstride = (long)a.E * c.NOUT * 2;
-    }
     if (__builtin_amdgcn_readfirstlane(c.cnt) <= 32)
-        expert_groups<MODE, 1, FMT>(a, c, w0, w1, w2, w3, x0, x1, x2, x3, s0, s1, s2, s3);
+        expert_groups<MODE, 1>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
     else
-        expert_groups<MODE, 2, FMT>(a, c, w0, w1, w2, w3, x0, x1, x2, x3, s0, s1, s2, s3);
+        expert_groups<MODE, 2>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
 }
 
 // Counts, offsets and the stable placement in one workgroup.  The
@@ -725,6 +577,7 @@ constexpr int PW = 16;             // waves of the placement workgroup
 __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
     __shared__ int cw[PW][256];    // per-range counts, then per-range running offsets
     __shared__ int tot[256];       // per-expert totals, then expert offsets
+    __shared__ int ch[256];        // chunks of the expert of each rank
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int total = a.T * a.k;
     const int per = cdiv(cdiv(total, 64), PW) * 64;    // assignments per range
@@ -747,8 +600,10 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
             rank += (o > me) || (o == me && e2 < tid);
         }
         a.order[rank] = tid;
+        ch[rank] = cdiv(me, kMoeChunk);
     }
     __syncthreads();
+    if (a.order && a.work) write_work(ch, a.E, a.work);
     if (tid < 64) {                                    // exclusive scan of the totals
         int v[4], sum = 0;
 #pragma unroll
@@ -892,14 +747,12 @@ bool expert_dma_ok(const MoeArgs& a) {
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.f4) {
-        if (sizeof(T) != 2 || !expert_dma_ok(a) || !a.x_gate || !a.x_up) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<0, 2>), dim3(cdiv(a.F, 128), a.E), dim3(256), 0, st, a);
-    } else if (a.f8) {
-        if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<0, 1>), dim3(cdiv(a.F, 64), a.E), dim3(256), 0, st, a);
-    } else if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<0, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+    if (a.f4 || a.f8) {
+        if (sizeof(T) != 2) return hipErrorInvalidValue;
+        return moe_gateup_mx(a, st);
+    }
+    if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL((expert_dma_kernel<0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -908,14 +761,12 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.f4) {
-        if (sizeof(T) != 2 || !expert_dma_ok(a) || !a.x_down) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<1, 2>), dim3(cdiv(a.d, 256), a.E), dim3(256), 0, st, a);
-    } else if (a.f8) {
-        if (sizeof(T) != 2 || !expert_dma_ok(a)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((expert_dma_kernel<1, 1>), dim3(cdiv(a.d, 128), a.E), dim3(256), 0, st, a);
-    } else if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<1, 0>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+    if (a.f4 || a.f8) {
+        if (sizeof(T) != 2) return hipErrorInvalidValue;
+        return moe_down_mx(a, st);
+    }
+    if (sizeof(T) == 2 && expert_dma_ok(a))
+        hipLaunchKernelGGL((expert_dma_kernel<1>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();

@@ -12,37 +12,24 @@
 // ties to the even code, magnitudes at or above 448 giving 448.
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace dg {
 
 namespace {
 
-// E4M3 code of a finite binary32 value: sign kept; below 2^-6 the
-// subnormal steps of 2^-9 (round half to even on the step count, 8 steps
-// being the smallest normal code 0x08); above, the binary32 mantissa rounded
-// to 3 bits (half to even, a carry moving into the exponent); saturating at
-// 448 (code 0x7E).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    uint32_t c;
-    if (!(a < 448.0f)) {
-        c = 0x7Eu;
-    } else if (a < 0.015625f) {
-        c = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        const uint32_t b = __float_as_uint(a);
-        const uint32_t e = (b >> 23) - 127u + 7u;     // 1 .. 15
-        const uint32_t m = b & 0x7FFFFFu;
-        c = (e << 3) | (m >> 20);
-        const uint32_t rem = m & 0xFFFFFu;
-        if (rem > 0x80000u || (rem == 0x80000u && (c & 1u))) c += 1u;
-        c = c > 0x7Eu ? 0x7Eu : c;
-    }
-    return sign | c;
+// Tiled layout of the codes (the block-scaled expert kernels' operand order):
+// 16-row tiles, each a run of 128-column steps; a tile-step is two 1-KiB
+// halves (columns 0..63 and 64..127 of the step), and in half h the 16-byte
+// chunk 16 g + r holds row r's columns 64 h + 16 g .. +15.
+__device__ __forceinline__ long fp8_tiled_index(long row, int col, int cols) {
+    const long tile = row >> 4;
+    const int r = (int)(row & 15), s = col >> 7, kk = col & 127;
+    const int h = kk >> 6, g = (kk >> 4) & 3, p = kk & 15;
+    return ((tile * (cols >> 7) + s) * 2 + h) * 1024 + (16 * g + r) * 16 + p;
 }
 
-// One workgroup per row: the row's amax, then four codes per thread step.
+// One workgroup per row: the row's amax, then one code per thread step.
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__ src, int cols,
                                                            uint8_t* __restrict__ q,
@@ -58,8 +45,8 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
     amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
     const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
     if (threadIdx.x == 0) scale[row] = s;
-    uint8_t* out = q + row * cols;
-    for (int i = threadIdx.x; i < cols; i += 256) out[i] = (uint8_t)e4m3_code(Elt<T>::to_f(x[i]) / s);
+    for (int i = threadIdx.x; i < cols; i += 256)
+        q[fp8_tiled_index(row, i, cols)] = (uint8_t)e4m3_code(Elt<T>::to_f(x[i]) / s);
 }
 
 // ------------------------------------------------------------------ MXFP4
@@ -88,10 +75,11 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 }
 
 // One thread per 32-element block: the block's scale code, then its 16
-// bytes of codes (two per byte, the even element in the low nibble).  Scale
-// codes go to scale[(b / 2) * rows * 2 + row * 2 + b % 2] for block b of a
-// row: the two blocks of each 64-element stage of every row are adjacent
-// and the rows of one stage contiguous.
+// bytes of codes (two per byte, the even element in the low nibble).  Tiled
+// layout (the block-scaled expert kernels' operand order): 16-row tiles, each
+// a run of 128-column steps; in a tile-step the 16 code bytes of block g of
+// row r are chunk 16 g + r of 1 KiB, and its scale code is byte 16 g + r of
+// 64.
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const T* __restrict__ src, long rows,
                                                              int cols, uint8_t* __restrict__ q,
@@ -120,8 +108,10 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const T* __restrict
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_code(v[i] * inv) << (4 * (i & 7));
-    *reinterpret_cast<uint4*>(q + row * (cols / 2) + (long)b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    scale[(long)(b >> 1) * rows * 2 + row * 2 + (b & 1)] = (uint8_t)(ex + 127);
+    const long ts = (row >> 4) * (cols >> 7) + (b >> 2);        // tile-step
+    const int lane = 16 * (b & 3) + (int)(row & 15);
+    *reinterpret_cast<uint4*>(q + ts * 1024 + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    scale[ts * 64 + lane] = (uint8_t)(ex + 127);
 }
 
 }  // namespace
@@ -130,7 +120,7 @@ template <typename T>
 hipError_t quantize_mxfp4(const T* src, long rows, int cols, uint8_t* q, uint8_t* scale,
                           hipStream_t st) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
-    if (cols % 64) return hipErrorInvalidValue;
+    if (cols % 128 || rows % 16) return hipErrorInvalidValue;
     const long blocks = rows * (cols / 32);
     if (blocks / 256 + 1 > 0x7FFFFFFFL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quantize_mxfp4_kernel<T>, dim3((unsigned)((blocks + 255) / 256)), dim3(256),
@@ -146,7 +136,7 @@ template <typename T>
 hipError_t quantize_fp8(const T* src, long rows, int cols, uint8_t* q, float* scale,
                         hipStream_t st) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
-    if (rows > 0x7FFFFFFFL) return hipErrorInvalidValue;
+    if (rows > 0x7FFFFFFFL || cols % 128 || rows % 16) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quantize_fp8_kernel<T>, dim3((unsigned)rows), dim3(256), 0, st, src, cols, q,
                        scale);
     return hipGetLastError();

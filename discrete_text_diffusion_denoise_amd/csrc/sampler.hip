@@ -1111,10 +1111,11 @@ __global__ __launch_bounds__(AM_THR) void argmax_rows_kernel(const float* __rest
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + u * AM_THR;
-                v[u] = j < n4 ? r4[j] : make_float4(NAN, NAN, NAN, NAN);
+                v[u] = j < n4 ? r4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
+                if (j0 + u * AM_THR >= n4) continue;    // past the row: no candidate
                 const int i = 4 * (j0 + u * AM_THR);
                 amax_take(v[u].x, i, bv, bi);
                 amax_take(v[u].y, i + 1, bv, bi);
@@ -1131,8 +1132,9 @@ __global__ __launch_bounds__(AM_THR) void argmax_rows_kernel(const float* __rest
 
 // From the head's 64-column slab maxima (V % 64 == 0, a NaN member makes its
 // slab's maximum NaN): the first slab whose maximum is the row's largest,
-// then the first entry of that slab equal to it (a NaN, if it is NaN).  Every earlier slab's maximum is smaller, so this is the first index
-// of the row's maximum.
+// then the first entry of that slab equal to it (a NaN, if it is NaN).
+// Every earlier slab's maximum is smaller, so this is the first index of the
+// row's maximum.
 __global__ __launch_bounds__(256) void argmax_slabs_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ rowmax, int V,
                                                            int32_t* __restrict__ out,

@@ -104,19 +104,19 @@ typedef struct {
     const void* w_gate;      /* [E][F][d]           */
     const void* w_up;        /* [E][F][d]           */
     const void* w_down;      /* [E][d][F]           */
-    /* FP8 experts only (else NULL): one fp32 scale per weight row, so that   */
-    /* weight[e][r][k] = decode(w[e][r][k]) * s[e][r] (dg_quantize_fp8)        */
+    /* FP8 experts only (else NULL): w_gate / w_up / w_down hold E4M3 codes   */
+    /* in the tiled layout of dg_quantize_fp8 (rows E*R, columns K), and these */
+    /* one fp32 scale per weight row: weight[e][r][k] = decode(code) * s[e][r] */
     const float* s_gate;     /* [E][F]              */
     const float* s_up;       /* [E][F]              */
     const float* s_down;     /* [E][d]              */
     /* MXFP4 experts only (else NULL): w_gate / w_up / w_down hold E2M1 codes  */
-    /* packed two per byte ([E][R][K/2], the even k in the low nibble), and    */
-    /* these hold the E8M0 scale code of every 32-k block, laid out            */
-    /* [K/64][E*R][2] (dg_quantize_mxfp4), so that weight[e][r][k] =           */
-    /* decode(code) * 2^(scale - 127)                                          */
-    const uint8_t* x_gate;   /* [d/64][E*F][2]      */
-    const uint8_t* x_up;     /* [d/64][E*F][2]      */
-    const uint8_t* x_down;   /* [F/64][E*d][2]      */
+    /* and these the E8M0 scale code of every 32-k block, both in the tiled    */
+    /* layout of dg_quantize_mxfp4 (rows E*R, columns K), so that               */
+    /* weight[e][r][k] = decode(code) * 2^(scale - 127)                        */
+    const uint8_t* x_gate;   /* E*F*d/32 bytes      */
+    const uint8_t* x_up;     /* E*F*d/32 bytes      */
+    const uint8_t* x_down;   /* E*d*F/32 bytes      */
 } dg_layer_weights;
 
 typedef struct {
@@ -206,24 +206,33 @@ dg_status dg_kv_set_length(dg_kv* kv, int32_t len);
  * OCP E4M3 with one scale per row).  Quantises d_src [rows][cols] (src_dtype
  * DG_F32 or DG_BF16) row by row: amax = max |x|, scale = amax / 448 in fp32
  * (1 for an all-zero row), code = E4M3 of the fp32 quotient x / scale, round
- * to nearest with ties to the even code, saturating at 448.  Writes d_q
- * [rows][cols] (one byte per code) and d_scale [rows] (fp32).  An expert
- * matrix [E][R][K] is rows = E*R, cols = K.  DG_ERR_ARG on NULL or
- * non-positive sizes, DG_ERR_DTYPE on another src_dtype. */
+ * to nearest with ties to the even code, saturating at 448.  Writes d_scale
+ * [rows] (fp32) and the rows*cols code bytes of d_q tiled in the order the
+ * block-scaled expert kernels read their MFMA operands (rows % 16 == 0, cols %
+ * 128 == 0): 16-row tiles, one after another; in a tile its 128-column steps,
+ * one after another; a step is two 1-KiB halves (columns 0..63 and 64..127 of
+ * the step), and in half h the 16 bytes at 16 * (16 g + r) are row r's
+ * columns 64 h + 16 g .. +15.  An expert matrix [E][R][K] is rows = E*R,
+ * cols = K.  DG_ERR_ARG on NULL or bad sizes, DG_ERR_DTYPE on another
+ * src_dtype. */
 dg_status dg_quantize_fp8(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
                           void* d_q, float* d_scale, void* stream);
 /* 4-bit expert weights in the OCP microscaling format MXFP4 (same passage;
- * the closest CDNA4 format to the pages' 4-bit one; gfx950 converts it in
- * hardware).  Quantises d_src [rows][cols] (src_dtype DG_F32 or DG_BF16,
- * cols % 64 == 0) in blocks of 32 consecutive elements of a row: X =
- * 2^(floor(log2(max |x|)) - 2), the exponent clamped to [-127, 127] (an
- * all-zero block takes 2^-127); code = E2M1 of x / X, round to nearest with
- * ties to the even code, magnitudes above 6 giving 6.  Writes d_codes
- * [rows][cols/2] (two codes per byte, the even element in the low nibble)
- * and d_scales [cols/64][rows][2] (the E8M0 codes 127 + log2 X of the two
- * blocks of each 64-column stage, adjacent).  An expert matrix [E][R][K] is
- * rows = E*R, cols = K.  DG_ERR_ARG on NULL or bad sizes, DG_ERR_DTYPE on
- * another src_dtype. */
+ * the closest CDNA4 format to the pages' 4-bit one; gfx950's block-scaled
+ * matrix cores take it as stored).  Quantises d_src [rows][cols] (src_dtype
+ * DG_F32 or DG_BF16, rows % 16 == 0, cols % 128 == 0) in blocks of 32
+ * consecutive elements of a row: X = 2^(floor(log2(max |x|)) - 2), the
+ * exponent clamped to [-127, 127] (an all-zero block takes 2^-127); code =
+ * E2M1 of x / X, round to nearest with ties to the even code, magnitudes
+ * above 6 giving 6.  Writes rows*cols/2 code bytes to d_codes (two codes a
+ * byte, the even column in the low nibble) and rows*cols/32 E8M0 scale codes
+ * (127 + log2 X) to d_scales, both tiled in the order the block-scaled expert
+ * kernels read their MFMA operands: 16-row tiles, one after another; in a
+ * tile its 128-column steps, one after another; a tile-step is 1 KiB of
+ * codes, the 16 bytes at 16 * (16 g + r) holding row r's 32-column block g
+ * of the step, and 64 scale codes, byte 16 g + r that block's.  An expert
+ * matrix [E][R][K] is rows = E*R, cols = K.  DG_ERR_ARG on NULL or bad sizes,
+ * DG_ERR_DTYPE on another src_dtype. */
 dg_status dg_quantize_mxfp4(const void* d_src, int32_t src_dtype, int64_t rows, int32_t cols,
                             void* d_codes, uint8_t* d_scales, void* stream);
 

@@ -1,8 +1,10 @@
-"""8-bit expert weights: the library's quantiser (dg_quantize_fp8) against
-the oracle's (oracle/quant.py), bit for bit, on fp32 and bf16 sources,
-including exact ties, subnormal codes, saturation and an all-zero row.  The
-expert kernels on 8-bit weights are checked against the oracle in
-test_gpu_model.py (small_fp8)."""
+"""Quantised expert weights: the library's quantisers (dg_quantize_fp8,
+dg_quantize_mxfp4) against the oracle's (oracle/quant.py), bit for bit, on
+fp32 and bf16 sources, including exact ties, subnormal codes, saturation and
+all-zero rows and blocks; the library writes its tiled layout, compared
+through the layout's index permutation (helpers.tile_*).  The expert kernels
+on these weights are checked against the oracle in test_gpu_model.py
+(small_fp8, small_mxfp4) and test_gpu_mx_experts.py (full size)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ import torch
 from discrete_text_diffusion_denoise_amd import binding, synthetic
 from oracle import quant as oq
 
-from helpers import DEV, to_dev
+from helpers import DEV, tile_e4m3, tile_mxfp4, to_dev, untile_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +34,7 @@ def tie_rows(K: int) -> np.ndarray:
 @pytest.mark.parametrize("src", ["f32", "bf16"])
 def test_quantize_fp8_bit_exact(src):
     rng = np.random.default_rng(7)
-    R, K = 300, 777
+    R, K = 304, 768
     w = (rng.standard_normal((R, K)) * 0.02).astype(np.float32)
     w[5] = 0.0                                     # scale 1, all codes zero
     w[6] *= 1e-30                                  # tiny row: subnormal binary32 inputs
@@ -50,10 +52,11 @@ def test_quantize_fp8_bit_exact(src):
     rq, rs = oq.quantize_rows(w)
     gs = s.cpu().numpy()
     assert (gs.view(np.uint32) == rs.view(np.uint32)).all(), np.argwhere(gs != rs)[:5]
-    gq = q.cpu().numpy()
+    gq = untile_e4m3(q.cpu().numpy().reshape(-1), R, K)
     bad = np.argwhere(gq != rq)
     assert len(bad) == 0, [(int(r), int(c), int(gq[r, c]), int(rq[r, c]), float(w[r, c]))
                            for r, c in bad[:5]]
+    assert np.array_equal(q.cpu().numpy().reshape(-1), tile_e4m3(rq))
 
 
 def test_quantize_fp8_expert_shape():
@@ -66,17 +69,11 @@ def test_quantize_fp8_expert_shape():
     binding.quantize_fp8(d, q, s)
     torch.cuda.synchronize()
     rq, rs = oq.quantize_rows(w.reshape(-1, 512))
-    assert (q.cpu().numpy().reshape(-1, 512) == rq).all()
+    assert (q.cpu().numpy().reshape(-1) == tile_e4m3(rq)).all()
     assert (s.cpu().numpy().reshape(-1) == rs).all()
 
 
 # ------------------------------------------------------------------ MXFP4
-
-
-def mx_library_layout(scales_nat: np.ndarray) -> np.ndarray:
-    """Scale codes [rows][cols/32] -> the library's [cols/64][rows][2]."""
-    R, nb = scales_nat.shape
-    return np.ascontiguousarray(scales_nat.reshape(R, nb // 2, 2).transpose(1, 0, 2))
 
 
 def mx_tie_rows(K: int) -> np.ndarray:
@@ -96,7 +93,7 @@ def mx_tie_rows(K: int) -> np.ndarray:
 @pytest.mark.parametrize("src", ["f32", "bf16"])
 def test_quantize_mxfp4_bit_exact(src):
     rng = np.random.default_rng(11)
-    R, K = 300, 768
+    R, K = 304, 768
     w = (rng.standard_normal((R, K)) * 0.02).astype(np.float32)
     w[5] = 0.0                                     # all-zero blocks: scale code 0
     w[7] *= 1e6
@@ -112,16 +109,22 @@ def test_quantize_mxfp4_bit_exact(src):
     binding.quantize_mxfp4(d, q, s)
     torch.cuda.synchronize()
     codes, sc = oq.mx_quantize_rows(w)
-    assert np.array_equal(s.cpu().numpy().reshape(K // 64, R, 2), mx_library_layout(sc))
-    gq = q.cpu().numpy()
-    rq = oq.mx_pack(codes)
-    bad = np.argwhere(gq != rq)
-    assert len(bad) == 0, [(int(r), int(c), int(gq[r, c]), int(rq[r, c])) for r, c in bad[:5]]
+    tq, ts = tile_mxfp4(oq.mx_pack(codes), sc)
+    assert np.array_equal(s.cpu().numpy(), ts)
+    gq = q.cpu().numpy().reshape(-1)
+    bad = np.flatnonzero(gq != tq)
+    assert len(bad) == 0, [(int(i), int(gq[i]), int(tq[i])) for i in bad[:5]]
 
 
-def test_quantize_mxfp4_rejects_ragged_columns():
-    d = torch.zeros((4, 96), dtype=torch.float32, device=DEV)
-    q = torch.empty((4, 48), dtype=torch.uint8, device=DEV)
-    s = torch.empty(12, dtype=torch.uint8, device=DEV)
+@pytest.mark.parametrize("rows,cols", [(4, 96), (16, 192), (8, 128), (24, 256)])
+def test_quantizers_reject_untileable_shapes(rows, cols):
+    """The tiled layout needs rows % 16 == 0 and cols % 128 == 0."""
+    d = torch.zeros((rows, cols), dtype=torch.float32, device=DEV)
+    q4 = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    s4 = torch.empty(rows * cols // 32, dtype=torch.uint8, device=DEV)
     with pytest.raises(binding.DGError):
-        binding.quantize_mxfp4(d, q, s)
+        binding.quantize_mxfp4(d, q4, s4)
+    q8 = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    s8 = torch.empty(rows, dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.DGError):
+        binding.quantize_fp8(d, q8, s8)

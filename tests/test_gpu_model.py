@@ -14,7 +14,7 @@ from oracle import sampler as osampler
 
 import chain
 from helpers import (DEV, TOL_F32, normwise, round_model_dtype, route_ambiguous, route_is_valid,
-                     to_dev, tol_for)
+                     tile_e4m3, tile_mxfp4, to_dev, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,9 +64,7 @@ def device_form(cfg, W):
                 w = lg[k]
                 K = w.shape[-1]
                 codes, sc = oq.mx_quantize_rows(w.reshape(-1, K))
-                lg[k] = oq.mx_pack(codes).reshape(w.shape[:-1] + (K // 2,))
-                R = codes.shape[0]
-                lg[xk] = np.ascontiguousarray(sc.reshape(R, K // 64, 2).transpose(1, 0, 2))
+                lg[k], lg[xk] = tile_mxfp4(oq.mx_pack(codes), sc)
                 lo[k] = oq.mx_dequantize_rows(codes, sc).reshape(w.shape)
         return Wg, Wo
     if cfg.get("expert_dtype") != "fp8":
@@ -77,7 +75,7 @@ def device_form(cfg, W):
         for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
             w = lg[k]
             q, sc = oq.quantize_rows(w.reshape(-1, w.shape[-1]))
-            lg[k] = q.reshape(w.shape)
+            lg[k] = tile_e4m3(q)
             lg[sk] = sc.reshape(w.shape[:-1])
             lo[k] = oq.dequantize_rows(q, sc).reshape(w.shape)
     return Wg, Wo
