@@ -703,6 +703,8 @@ def bench_moe(args):
         total_bytes += r["bytes_per_launch"]
         total_ms += avg
     binding.timer_enable([])
+    if args.copy_probe:
+        copy_probe(torch)
     ach = total_bytes / (total_ms * 1e-3) / 1e9
     fmt = {"fp8": "E4M3 weights, per-row scales", "mxfp4": "MXFP4 weights"}.get(
         cfg.get("expert_dtype"), cfg["dtype"] + " weights")

@@ -230,7 +230,9 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
     s.counts = cv.take<int32_t>(c.n_experts);
     s.order = cv.take<int32_t>(c.n_experts);
     s.offsets = cv.take<int32_t>(c.n_experts + 1);
-    s.perm_tok = cv.take<int32_t>(T * c.top_k);
+    // (16 entries of padding: the block-scaled expert kernels read a wave's
+    // 16 sorted slots with scalar loads, up to 15 past an expert's last slot)
+    s.perm_tok = cv.take<int32_t>(T * c.top_k + 16);
     s.slot_of = cv.take<int32_t>(T * c.top_k);
     s.act = cv.take_bytes(T * c.top_k * c.d_ff * es);
     s.y = cv.take<float>(T * c.top_k * c.d_model);

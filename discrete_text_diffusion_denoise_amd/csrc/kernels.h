@@ -200,7 +200,9 @@ struct MoeArgs {
     // work items (expert, chunk) of the block-scaled expert kernels
     int32_t* work = nullptr;
 };
-constexpr int kMoeChunk = 32;
+constexpr int kMoeChunk = 64;
+// compute units of the current device (cached per device)
+int cu_count();
 // routing, counts and the stable permutation
 hipError_t moe_route(const MoeArgs& a, hipStream_t st);
 template <typename T>

@@ -6,10 +6,11 @@ tiled layout and dequantised for the oracle.  The MoE stage (dg_stage_moe) runs 
 the oracle's MoE fed the GPU's route set, with its expert inputs rounded to
 MXFP8 (oracle.model.moe, act_mx8) -- every token and feature.
 
-Router cases: uniform (about 16 tokens per expert: 16- and 32-token chunks),
-48 of the tokens pushed towards eight experts (those take 33 to 64 tokens:
-the 64-token chunk), and 160 pushed (more than 64: several chunks, the last
-one ragged)."""
+Router cases: uniform (about 16 tokens per expert: chunks of one or two
+16-token tiles), 48 of the tokens pushed towards eight experts (those take 33
+to 64 tokens: chunks of three or four tiles, whose rows 32..63 take the
+second token load), and 160 pushed (more than 64: several 64-token chunks,
+the last one ragged)."""
 import numpy as np
 import pytest
 import torch
