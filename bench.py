@@ -705,6 +705,15 @@ def bench_moe(args):
     binding.timer_enable([])
     if args.copy_probe:
         copy_probe(torch)
+    # measured HBM bytes per launch, from the committed counter summaries of
+    # this workload (null when absent or taken on an older kernel source)
+    src = "moe_mx.hip" if cfg.get("expert_dtype") in ("fp8", "mxfp4") else "moe.hip"
+    traffic = 0.0
+    for name in kernels:
+        t, where = measured_traffic(name, "moe_" + args.config, source=src)
+        kernels[name]["traffic"] = round(t) if t is not None else None
+        kernels[name]["traffic_source"] = where
+        traffic = traffic + t if (t is not None and traffic is not None) else None
     ach = total_bytes / (total_ms * 1e-3) / 1e9
     fmt = {"fp8": "E4M3 weights, per-row scales", "mxfp4": "MXFP4 weights"}.get(
         cfg.get("expert_dtype"), cfg["dtype"] + " weights")
@@ -730,7 +739,8 @@ def bench_moe(args):
         "experts_hit": hit,
         "kernels": kernels,
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": round(traffic) if traffic else None,
                      "kernel": "moe_gateup+moe_down", "bytes_per_launch": total_bytes,
                      "avg_launch_ms": round(total_ms, 5)},
         "cpu_baseline": None,
