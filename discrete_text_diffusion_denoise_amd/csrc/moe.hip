@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void count_kernel(MoeArgs a) {
 }
 
 // work[r] for r = 0 .. E: exclusive prefix of ch[0 .. E) (chunks of the
-// expert of rank r, in LDS), by threads 0..63 of the block, four each.
-__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) {
+// expert of rank r, in LDS), by threads 0..63 of the block, four each; and,
+// when `rank` is set, rank[i] = r for the items i of rank r.
+__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work, int32_t* rank) {
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     int v[4], sum = 0;
@@ -104,10 +105,29 @@ __device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) 
     int ex = incl - sum;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (tid * 4 + q < E) work[tid * 4 + q] = ex;
+        if (tid * 4 + q < E) {
+            work[tid * 4 + q] = ex;
+            if (rank)
+                for (int i = 0; i < v[q]; ++i) rank[ex + i] = tid * 4 + q;
+        }
         ex += v[q];
     }
     if (tid == 63) work[E] = incl;
+}
+
+// The rank of work item w's expert: work_rank when the routing wrote it,
+// else a binary search of work[] (work[r] <= w < work[r + 1]).
+__device__ __forceinline__ int item_rank(const MoeArgs& a, int w) {
+    if (a.work_rank) return a.work_rank[w];
+    int lo = 0, hi = a.E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.work[mid] <= w)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
 }
 
 // Experts by falling count (ties: lower id) from the counts, and the chunk
@@ -127,7 +147,7 @@ __global__ __launch_bounds__(256) void order_kernel(MoeArgs a) {
     }
     if (!a.work) return;
     __syncthreads();
-    write_work(ch, a.E, a.work);
+    write_work(ch, a.E, a.work, a.work_rank);
 }
 
 // One wave per expert: exclusive prefix of counts, then a stable, ordered
@@ -341,6 +361,7 @@ __global__ __launch_bounds__(256) void expert_kernel(MoeArgs a) {
 // experts run on the block-scaled MFMA kernels of moe_mx.hip.)
 struct XdCtx {
     int e, off, cnt, K, NOUT, c0, n, rot;
+    int m0, m1;              // the token range [m0, m1) of the expert this block runs
     int lane, wave, r16, g4, ct, mp, lr, lc;
     const char* wsrc[2];     // byte addresses of this lane's weight chunks at k = 0
     const bf16_t* X;
@@ -365,7 +386,7 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
     int col[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) col[j] = c.c0 + (ct + 2 * j) * 16 + r16;
-    for (int mg = 0; mg < c.cnt; mg += 32 * G) {
+    for (int mg = c.m0; mg < c.m1; mg += 32 * G) {
         const bf16_t* xsrc[G];
 #pragma unroll
         for (int q = 0; q < G; ++q) {
@@ -507,10 +528,14 @@ __device__ __forceinline__ void expert_groups(const MoeArgs& a, const XdCtx& c, 
 }
 
 // Blocks of 64 weight rows (gate and up rows of 32 columns (MODE 0) or 64
-// columns of the down projection (MODE 1)); blockIdx.y walks the experts in
-// `order` when it is set.  An expert with at most 32 tokens (most of them: a 256-token canvas
-// makes 2048 assignments over 128 experts) runs groups of 32, a busier one
-// groups of 64, so its weights are streamed fewer times.
+// columns of the down projection (MODE 1)).  With the routing's work items
+// (`work`), blockIdx.y is one item: a chunk of up to 64 tokens of one expert,
+// the busiest experts' chunks first, so the chunks of a busy expert run side
+// by side instead of one block walking them in turn (under collapsed
+// routing one expert takes hundreds of tokens).  Without them, blockIdx.y is
+// an expert (in `order` when set) and the block walks all its tokens.  A
+// chunk of at most 32 tokens runs one 32-token group, a larger one one group
+// of 64.
 template <int MODE>
 __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.halt && *a.halt) return;
@@ -521,10 +546,23 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     constexpr int HALF = 32;                           // columns per half of a block
 
     XdCtx c;
-    // the busiest experts first, so their longer blocks do not form the tail
-    c.e = a.order ? a.order[blockIdx.y] : (int)blockIdx.y;
-    c.off = a.offsets[c.e];
-    c.cnt = a.offsets[c.e + 1] - c.off;
+    if (a.work && a.order) {
+        const int w = blockIdx.y;
+        if (w >= a.work[a.E]) return;
+        const int lo = item_rank(a, w);
+        c.e = a.order[lo];
+        c.off = a.offsets[c.e];
+        c.cnt = a.offsets[c.e + 1] - c.off;
+        c.m0 = (w - a.work[lo]) * kMoeChunk;
+        c.m1 = min(c.cnt, c.m0 + kMoeChunk);
+    } else {
+        // the busiest experts first, so their longer blocks do not form the tail
+        c.e = a.order ? a.order[blockIdx.y] : (int)blockIdx.y;
+        c.off = a.offsets[c.e];
+        c.cnt = a.offsets[c.e + 1] - c.off;
+        c.m0 = 0;
+        c.m1 = c.cnt;
+    }
     if (c.cnt == 0) return;
     const int tid = threadIdx.x;
     c.lane = tid & 63;
@@ -557,7 +595,7 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
             c.wsrc[q] = base + (((long)c.e * c.NOUT + col) * c.K + c.lc) * 2;
         }
     }
-    if (__builtin_amdgcn_readfirstlane(c.cnt) <= 32)
+    if (__builtin_amdgcn_readfirstlane(c.m1 - c.m0) <= 32)
         expert_groups<MODE, 1>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
     else
         expert_groups<MODE, 2>(a, c, w0, w1, w2, w3, x0, x1, x2, x3);
@@ -603,7 +641,7 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
         ch[rank] = cdiv(me, kMoeChunk);
     }
     __syncthreads();
-    if (a.order && a.work) write_work(ch, a.E, a.work);
+    if (a.order && a.work) write_work(ch, a.E, a.work, a.work_rank);
     if (tid < 64) {                                    // exclusive scan of the totals
         int v[4], sum = 0;
 #pragma unroll
@@ -744,6 +782,12 @@ bool expert_dma_ok(const MoeArgs& a) {
     return a.d % 256 == 0 && a.F % 256 == 0;
 }
 
+// blockIdx.y of the ring kernels: the most work items there can be (every
+// expert's last chunk partial), or the experts
+static int dma_rows(const MoeArgs& a) {
+    return a.work && a.order ? cdiv(a.T * a.k, kMoeChunk) + std::min(a.E, a.T * a.k) : a.E;
+}
+
 template <typename T>
 hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
@@ -752,7 +796,7 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st) {
         return moe_gateup_mx(a, st);
     }
     if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<0>), dim3(cdiv(a.F, 32), dma_rows(a)), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 0>), dim3(cdiv(a.F, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -766,7 +810,7 @@ hipError_t moe_down(const MoeArgs& a, hipStream_t st) {
         return moe_down_mx(a, st);
     }
     if (sizeof(T) == 2 && expert_dma_ok(a))
-        hipLaunchKernelGGL((expert_dma_kernel<1>), dim3(cdiv(a.d, 64), a.E), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((expert_dma_kernel<1>), dim3(cdiv(a.d, 64), dma_rows(a)), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((expert_kernel<T, 1>), dim3(cdiv(a.d, 32), a.E), dim3(256), 0, st, a);
     return hipGetLastError();

@@ -100,14 +100,20 @@ struct MxTask {
 template <int MODE>
 __device__ __forceinline__ MxTask mx_task(const MoeArgs& a, int t, int NX, int wave) {
     const int w = t / NX, bx = t - w * NX;
-    // the rank r of the item's expert: work[r] <= w < work[r + 1]
-    int lo = 0, hi = a.E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sload(a.work + mid) <= w)
-            lo = mid;
-        else
-            hi = mid - 1;
+    // the rank r of the item's expert (work[r] <= w < work[r + 1])
+    int lo;
+    if (a.work_rank) {
+        lo = sload(a.work_rank + w);
+    } else {
+        lo = 0;
+        int hi = a.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sload(a.work + mid) <= w)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
     }
     MxTask k;
     k.e = sload(a.order + lo);

@@ -320,13 +320,16 @@ def test_stage_attention_on_synthetic_cache(name, causal, P, N):
                                          ("small_fp8", 512, None), ("small_fp8", 37, None),
                                          ("small_mxfp4", 512, None), ("small_mxfp4", 37, None),
                                          ("small_bf16", 512, 4), ("small_bf16", 300, 3),
-                                         ("small_bf16", 129, 1), ("small_bf16", 256, 16)])
+                                         ("small_bf16", 129, 1), ("small_bf16", 256, 16),
+                                         ("small_mxfp4", 300, 3), ("small_fp8", 129, 1),
+                                         ("small_mxfp4", 256, 16)])
 def test_stage_moe(name, T, top_k):
     """The MoE stage on identical synthetic inputs: the route is a valid top-k
     (the oracle's own set off near ties, at most 1 % of tokens within 1e-4
     of a tie) and the output matches the oracle fed the GPU's route set at
     every token.  top_k 1, 3, 4 and 16 run the combine kernels other than
-    the 2- and 8-expert ones."""
+    the 2- and 8-expert ones (with quantised experts too: work items and
+    token chunks of other sizes)."""
     over = {} if top_k is None else {"top_k": top_k}
     cfg, W, m = setup(name, 0, **over)
     rng = np.random.default_rng(11)
