@@ -81,6 +81,10 @@ def parse():
                          "cross-entropy of every canvas")
     ap.add_argument("--rate", type=float, default=0.5,
                     help="train: corruption rate of every canvas")
+    ap.add_argument("--router-skew", action="store_true",
+                    help="--mode moe: inject the router logits N(0,1) + 0.5 on 13 hot experts "
+                         "(the batched workload's expert skew) instead of computing them from "
+                         "random router weights; reports the measured max/mean expert load")
     ap.add_argument("--ar-tokens", type=int, default=64)
     ap.add_argument("--ar-batch", type=int, default=1)
     return ap.parse_args()
@@ -662,7 +666,13 @@ def bench_moe(args):
     expert shape, weights drawn and quantised as in the full bench.  value =
     algorithmic HBM GB/s of the two expert products together (the weights of
     every expert the routes hit, read once, plus the activations), timed by
-    the library's HIP events on the launch stream."""
+    the library's HIP events on the launch stream.
+
+    --router-skew injects the router logits z = N(0, 1) + 0.5 on a seeded set
+    of 13 hot experts (about 10 % of 128): the router rows are the first E unit
+    vectors, and a token's first E features are its z (the rest N(0, 1)), so
+    its logits after the RMSNorm are z / rms(row) -- a positive scale that
+    keeps the token's top-k exactly that of z."""
     import torch
 
     from discrete_text_diffusion_denoise_amd import binding, synthetic
@@ -672,11 +682,18 @@ def bench_moe(args):
     B, N, d = shape["batch"], cfg["canvas"], cfg["d_model"]
     torch.cuda.init()
     W = device_weights(cfg, args.seed, torch)
+    E = cfg["n_experts"]
+    hot = None
+    if args.router_skew:
+        W["layers"][0]["w_router"] = torch.eye(E, d, device="cuda").to(W["layers"][0]["w_router"].dtype)
+        hot = torch.randperm(E, generator=torch.Generator().manual_seed(args.seed + 7))[:13]
     m = binding.Model(cfg, W, batch=B, capacity=N + 16)
     g = torch.Generator(device="cuda")
     g.manual_seed(args.seed + 1)
     T = B * N
     h0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+    if hot is not None:
+        h0[:, hot.to("cuda")] += 0.5
     h = h0.clone()
     route = torch.zeros((T, cfg["top_k"]), dtype=torch.int32, device="cuda")
     gates = torch.zeros((T, cfg["top_k"]), dtype=torch.float32, device="cuda")
@@ -686,6 +703,12 @@ def bench_moe(args):
     torch.cuda.synchronize()
     hit = int(torch.unique(route).numel())
     cfg["experts_hit"] = hit
+    load = torch.bincount(route.reshape(-1).long(), minlength=E).float()
+    load_stats = {"max": int(load.max()), "mean": round(float(load.mean()), 2),
+                  "max_over_mean": round(float(load.max() / load.mean()), 3),
+                  "hot_mean": round(float(load[hot].mean()), 2) if hot is not None else None,
+                  "cold_mean": (round(float(load[[e for e in range(E) if e not in set(hot.tolist())]].mean()), 2)
+                                if hot is not None else None)}
     binding.timer_enable(["moe_gateup", "moe_down"])
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -710,7 +733,8 @@ def bench_moe(args):
     src = "moe_mx.hip" if cfg.get("expert_dtype") in ("fp8", "mxfp4") else "moe.hip"
     traffic = 0.0
     for name in kernels:
-        t, where = measured_traffic(name, "moe_" + args.config, source=src)
+        t, where = measured_traffic(name, "moe_" + args.config + ("_skew" if hot is not None else ""),
+                                    source=src)
         kernels[name]["traffic"] = round(t) if t is not None else None
         kernels[name]["traffic_source"] = where
         traffic = traffic + t if (t is not None and traffic is not None) else None
@@ -731,12 +755,16 @@ def bench_moe(args):
         "dtype": cfg["dtype"] + {"fp8": "+fp8-experts", "mxfp4": "+mxfp4-experts"}.get(
             cfg.get("expert_dtype"), ""),
         "data": "synthetic (N(0,1) residual rows, random-init N(0,0.02) weights)",
-        "config": {"workload": (f"moe-{args.config}: MoE half of {B} canvas(es) of {N} tokens, "
+        "config": {"workload": (f"moe-{args.config}{'-skew' if hot is not None else ''}: MoE half of "
+                                f"{B} canvas(es) of {N} tokens, "
                                 f"d {d}, {cfg['n_experts']} experts top-{cfg['top_k']}, d_ff "
                                 f"{cfg['d_ff']} ({fmt}); one step = one dg_stage_moe (RMSNorm, "
                                 f"router, routing, both expert products, combine)"),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "experts_hit": hit,
+        "expert_load": load_stats,
+        "router": ("injected logits N(0,1) + 0.5 on 13 hot experts" if hot is not None
+                   else "random router weights, N(0,1) rows"),
         "kernels": kernels,
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
