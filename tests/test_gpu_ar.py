@@ -117,7 +117,7 @@ def decode_chain_check(m, cfg, W, tok, logits, tol, label):
 
 @pytest.mark.parametrize("name,P,B,layers", [("tiny", 20, 2, 2), ("small_bf16", 150, 3, 2),
                                              ("f32_gqa", 33, 3, 2), ("small_fp8", 150, 3, 2),
-                                             ("vocab_bf16", 64, 2, 1)])
+                                             ("small_mxfp4", 150, 3, 2), ("vocab_bf16", 64, 2, 1)])
 def test_ar_decode_steps_match_oracle(name, P, B, layers):
     """Five decode steps after a prompt encode; each step against the oracle
     stage by stage on the GPU's own inputs, every sequence."""
@@ -182,7 +182,8 @@ def test_ar_decode_rejects_full_cache():
 
 
 @pytest.mark.parametrize("name,P,B,n_new", [("tiny", 12, 2, 6), ("small_bf16", 100, 2, 5),
-                                            ("vocab_bf16", 40, 1, 4), ("small_fp8", 100, 1, 4)])
+                                            ("vocab_bf16", 40, 1, 4), ("small_fp8", 100, 1, 4),
+                                            ("small_mxfp4", 100, 2, 4)])
 def test_ar_generate_equals_composition(name, P, B, n_new):
     print(f"ar generate {name} P={P} B={B} n={n_new}", flush=True)
     cfg, W, m1 = setup(name, P + n_new, B)

@@ -75,7 +75,8 @@ def test_xent_target_outside_vocab_is_nan():
 
 
 @pytest.mark.parametrize("name,P,B,layers", [("tiny", 40, 2, 2), ("small_bf16", 120, 2, 2),
-                                             ("f32_gqa", 33, 2, 2), ("small_fp8", 120, 1, 2)])
+                                             ("f32_gqa", 33, 2, 2), ("small_fp8", 120, 1, 2),
+                                             ("small_mxfp4", 120, 1, 2)])
 def test_train_forward_matches_oracle(name, P, B, layers):
     """The corrupted canvas bit-exact against the oracle; the cross-entropy
     bit-exact against the oracle's on the GPU's own logits, every row; the
