@@ -69,6 +69,9 @@ def parse():
                          "run adds under the key \"stack\"")
     ap.add_argument("--stack-steps", type=int, default=2,
                     help="timed blocks of the 30-layer stack measurement")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the microbenchmark peaks (HBM read and copy, bf16 matrix "
+                         "product) reported beside the published ones")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the measurement, two 1 GiB device copies (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
@@ -255,6 +258,49 @@ def copy_probe(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+
+
+def measured_peaks(torch):
+    """Microbenchmark peaks of this GPU, reported beside the published ones
+    (8 TB/s, 2.5 PFLOP/s bf16 dense): the library's probe kernels
+    (dg_measure_peaks: a read-only stream over 4 GiB, independent bf16
+    MFMAs at eight waves a SIMD), plus a 2 GiB device-to-device copy (read +
+    write bytes) and a bf16 8192^3 torch.matmul (the vendor GEMM library) for
+    context.  Calibration runs outside the timed region, not steps of the
+    path."""
+    from discrete_text_diffusion_denoise_amd import binding
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1e-3
+
+    buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    read_gbs, mfma_tf = binding.measure_peaks(buf)
+    y = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+    t_copy = timed(lambda: y.copy_(buf[: 1 << 29]), 10)
+    del buf, y
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    t_mm = timed(lambda: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(read_gbs, 1),
+            "bf16_mfma_tflops": round(mfma_tf, 1),
+            "hbm_copy_gbs": round(2.0 * 4.0 * (1 << 29) / t_copy / 1e9, 1),
+            "torch_matmul_bf16_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1),
+            "method": "dg_measure_peaks (read-only stream over 4 GiB; independent "
+                      "v_mfma_f32_16x16x32_bf16, eight waves a SIMD); 2 GiB device copy "
+                      "(read + write bytes); bf16 8192^3 torch.matmul; outside the timed "
+                      "region"}
 
 
 def cpu_baseline(cfg, W, prompt, canvas, params, torch):
@@ -995,6 +1041,12 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
     }
     if args.copy_probe and config == args.config:
         copy_probe(torch)
+    if config == args.config and not args.no_peaks:
+        pk = measured_peaks(torch)
+        out["measured_peaks"] = pk
+        ref = {"hbm": pk["hbm_read_gbs"], "mfma": pk["bf16_mfma_tflops"]}.get(roof["bound"])
+        if ref:
+            roof["frac_of_measured_peak"] = round(roof["achieved"] / ref, 4)
     oracle_fits = cfg["n_layers"] == 1 and B == 1 and P <= 4096
     if want_cpu and not oracle_fits:
         # the float64 oracle's prompt encode alone would run for many minutes

@@ -105,6 +105,7 @@ _SIGS = {
     "dg_stage_head_rowmax": (_I, [_P, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_timer_enable": (_I, [ctypes.c_uint32]),
     "dg_timer_read": (_I, [_I, _P, _P]),
+    "dg_measure_peaks": (_I, [_P, _SZ, _P, _P, _P]),
 }
 
 TIMERS = {"head_gemm": 0, "selfcond_gemm": 1, "moe_gateup": 2, "moe_down": 3, "attention": 4,
@@ -472,6 +473,16 @@ def timer_read(name: str):
     n = ctypes.c_int64()
     _check(lib().dg_timer_read(TIMERS[name], ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def measure_peaks(buf, stream=None):
+    """(HBM read GB/s, bf16 MFMA TFLOP/s) measured by the library's probe
+    kernels on a device buffer of at least 256 MiB (a calibration aid)."""
+    gbs = ctypes.c_double()
+    tf = ctypes.c_double()
+    _check(lib().dg_measure_peaks(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream),
+                                  ctypes.byref(gbs), ctypes.byref(tf)))
+    return gbs.value, tf.value
 
 
 def canvas_init(seed: int, block_index: int, canvas, vocab: int, stream=None):

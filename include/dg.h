@@ -511,6 +511,21 @@ dg_status dg_timer_enable(uint32_t mask);
  * duration (ms) and number of launches since the last dg_timer_enable. */
 dg_status dg_timer_read(int32_t id, double* total_ms, int64_t* launches);
 
+/* ------------------------------------------------------- calibration */
+/* Microbenchmark peaks of the current device, for reporting beside the
+ * published ones; no step of the denoising path uses them.  Runs two probe
+ * kernels on `stream` and waits for them:
+ *   *hbm_read_gbs     = bytes per second of a read-only stream over d_buf
+ *                       (non-temporal 16-byte loads, 8 workgroups a CU,
+ *                       5 passes timed after one untimed);
+ *   *mfma_bf16_tflops = FLOP/s of independent v_mfma_f32_16x16x32_bf16
+ *                       (four accumulators a wave, eight waves a SIMD).
+ * d_buf is caller-owned device memory of buf_bytes >= 256 MiB plus a few MB
+ * (DG_ERR_CAPACITY otherwise); its contents are overwritten.  DG_ERR_HIP if
+ * a launch or event call fails. */
+dg_status dg_measure_peaks(void* d_buf, size_t buf_bytes, void* stream, double* hbm_read_gbs,
+                           double* mfma_bf16_tflops);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,3 +136,10 @@ def test_sampler_argument_errors(L):
     assert L.dg_sample_update(ctypes.byref(p), 0, 1, 256, 1024, P, P, P, P, P, P, P, 8,
                               None) == 4
     assert L.dg_status_string(4) == b"capacity exceeded"
+
+
+def test_measure_peaks_argument_errors(L):
+    # argument checks come before any device call
+    d = ctypes.c_double()
+    assert L.dg_measure_peaks(None, 1 << 30, None, ctypes.byref(d), ctypes.byref(d)) == 1
+    assert L.dg_measure_peaks(ctypes.c_void_p(16), 1 << 30, None, None, ctypes.byref(d)) == 1
