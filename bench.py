@@ -847,7 +847,8 @@ def main():
         # own line's essentials under one key)
         st = bench_diffusion(args, "stack", None, args.stack_steps, 1, False)
         out["stack"] = {k: st[k] for k in ("metric", "value", "unit", "ms_per_step",
-                                           "denoise_step_ms", "kernels", "roofline",
+                                           "denoise_step_ms", "canvas_tokens_per_s_at_12_rounds",
+                                           "kernels", "roofline",
                                            "experts_hit_per_layer", "fraction_check")}
         out["stack"]["steps"] = args.stack_steps
         out["stack"]["workload"] = st["config"]["workload"]
@@ -966,8 +967,8 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
     sws = binding.sampler_workspace(B, N)
     m.denoise_step(canvas, logits[0])
     binding.sample_update(params, 0, logits[0], canvas, argmax, lock, stats[0], stop, sws)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = 10
+    reps = 11
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
     for j in range(1, reps + 1):
         stop.zero_()
@@ -975,9 +976,10 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
                        top_k=args.top_k)
         binding.sample_update(params, j, logits[j % 2], canvas, argmax, lock, stats[j % 2], stop,
                               sws)
-    ev[1].record()
+        ev[j].record()
     torch.cuda.synchronize()
-    step_ms = ev[0].elapsed_time(ev[1]) / reps
+    # median over the steps (each timed between consecutive events)
+    step_ms = float(np.median([ev[j - 1].elapsed_time(ev[j]) for j in range(1, reps + 1)]))
 
     sc_tiles = -(-B * N // 256) * -(-cfg["d_model"] // 256)
     sc_splits = max(1, min(64, 256 // max(sc_tiles, 1)))
@@ -1030,7 +1032,13 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
                                + f", T {params['temp_start']:g}->{params['temp_end']:g}, stop "
                                f"{params['stop_tau']:g} + stable"
                                + (f", top-{args.top_k} truncation" if args.top_k else ""))},
+        "weights_cache": ("cold: a round streams both vocabulary products' E (2 x "
+                          f"{2 * V * cfg['d_model'] / 1e9:.2f} GB) and every hit expert, far "
+                          "more than the 256 MB last-level cache, so no weight is cache-warm "
+                          "from one round to the next"),
         "denoise_step_ms": round(step_ms, 4),
+        "canvas_tokens_per_s_at_12_rounds": (
+            round(value * float(np.mean(rounds)) / 12.0, 1) if rounds else None),
         "kernels": per_kernel,
         "roofline": roof,
         "experts_hit_per_layer": {"min": min(hits), "mean": round(float(np.mean(hits)), 2),
