@@ -848,6 +848,7 @@ def main():
         st = bench_diffusion(args, "stack", None, args.stack_steps, 1, False)
         out["stack"] = {k: st[k] for k in ("metric", "value", "unit", "ms_per_step",
                                            "denoise_step_ms", "canvas_tokens_per_s_at_12_rounds",
+                                           "prefill",
                                            "kernels", "roofline",
                                            "experts_hit_per_layer", "fraction_check")}
         out["stack"]["steps"] = args.stack_steps
@@ -899,7 +900,18 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
     g = torch.Generator(device="cuda")
     g.manual_seed(args.seed + 1)
     prompt = torch.randint(0, V, (B, P), generator=g, device="cuda", dtype=torch.int32)
+    # the prompt encode (causal prefill of B x P tokens through every layer),
+    # timed on its own (the second of two identical encodes, the cache rewound
+    # between them): not part of a step
     m.encode_prompt(prompt)
+    m.set_kv_length(0)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    pe[0].record()
+    m.encode_prompt(prompt)
+    pe[1].record()
+    torch.cuda.synchronize()
+    prefill_ms = pe[0].elapsed_time(pe[1])
     params = synthetic.default_sampler_params(max_steps=48, seed=args.seed, selfcond_on=1,
                                               top_k=args.top_k,
                                               stop_tau=shape.get("stop_tau", 0.005),
@@ -1036,6 +1048,9 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
                           f"{2 * V * cfg['d_model'] / 1e9:.2f} GB) and every hit expert, far "
                           "more than the 256 MB last-level cache, so no weight is cache-warm "
                           "from one round to the next"),
+        "prefill": {"ms": round(prefill_ms, 3), "tokens": B * P,
+                    "note": "one causal prompt encode (the second of two), not part of the "
+                            "timed steps"},
         "denoise_step_ms": round(step_ms, 4),
         "canvas_tokens_per_s_at_12_rounds": (
             round(value * float(np.mean(rounds)) / 12.0, 1) if rounds else None),
