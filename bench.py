@@ -848,7 +848,7 @@ def main():
         st = bench_diffusion(args, "stack", None, args.stack_steps, 1, False)
         out["stack"] = {k: st[k] for k in ("metric", "value", "unit", "ms_per_step",
                                            "denoise_step_ms", "canvas_tokens_per_s_at_12_rounds",
-                                           "prefill",
+                                           "prefill", "trajectory",
                                            "kernels", "roofline",
                                            "experts_hit_per_layer", "fraction_check")}
         out["stack"]["steps"] = args.stack_steps
@@ -956,11 +956,16 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
     dom_ms, dom_n = binding.timer_read(dominant)
     binding.timer_enable([])
 
-    # per-kernel breakdown: one more block with every timer on
+    # per-kernel breakdown: one more block with every timer on, recording the
+    # rounds' mean entropy and locked count (dg_generate_block_trace)
     binding.timer_enable(names)
-    m.generate_block(params, warmup + steps, block)
+    trace = torch.full((params["max_steps"], B, 2), float("nan"), dtype=torch.float32,
+                       device="cuda")
+    tr_steps = m.generate_block(params, warmup + steps, block, trace=trace)
     m.set_kv_length(P)
     torch.cuda.synchronize()
+    tr = trace.cpu().numpy()
+    pick = [t for t in (0, 1, 2, 4, 8, 16, 32, params["max_steps"] - 1) if t < tr_steps[0]]
     kern = {}
     for n in names:
         ms, cnt = binding.timer_read(n)
@@ -1051,6 +1056,11 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
         "prefill": {"ms": round(prefill_ms, 3), "tokens": B * P,
                     "note": "one causal prompt encode (the second of two), not part of the "
                             "timed steps"},
+        "trajectory": {"canvas": 0, "rounds": pick,
+                       "mean_entropy_nats": [round(float(tr[t, 0, 0]), 4) for t in pick],
+                       "locked_fraction": [round(float(tr[t, 0, 1]) / N, 4) for t in pick],
+                       "tokens_per_forward": round(N / float(np.mean(rounds)), 3) if rounds
+                       else None},
         "denoise_step_ms": round(step_ms, 4),
         "canvas_tokens_per_s_at_12_rounds": (
             round(value * float(np.mean(rounds)) / 12.0, 1) if rounds else None),

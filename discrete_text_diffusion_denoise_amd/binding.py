@@ -97,6 +97,7 @@ _SIGS = {
                               _P]),
     "dg_generate_workspace_bytes": (_I, [_P, _I, _P]),
     "dg_generate_block": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    "dg_generate_block_trace": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "dg_stage_input": (_I, [_P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_stage_input_topk": (_I, [_P, _I, _P, _P, _I, _P, _P, _SZ, _P]),
     "dg_stage_attention": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _SZ, _P]),
@@ -329,12 +330,25 @@ class Model:
         _check(lib().dg_commit_block(self.handle, self.kv, block.shape[0], _ptr(block),
                                      _ptr(self.ws), self.ws.numel(), _stream(stream)))
 
-    def generate_block(self, params: dict, block_index: int, block_out, stream=None):
+    def generate_block(self, params: dict, block_index: int, block_out, stream=None,
+                       trace=None):
+        """dg_generate_block; with `trace` (float32 [max_steps, batch, 2] on
+        the device) dg_generate_block_trace, which also records each round's
+        mean entropy and locked count per canvas."""
         steps = (ctypes.c_int32 * self.batch)()
         sp = sampler_params(params)
-        _check(lib().dg_generate_block(self.handle, self.kv, self.batch, ctypes.byref(sp),
-                                       int(block_index), _ptr(block_out), steps, _ptr(self.ws),
-                                       self.ws.numel(), _stream(stream)))
+        if trace is None:
+            _check(lib().dg_generate_block(self.handle, self.kv, self.batch, ctypes.byref(sp),
+                                           int(block_index), _ptr(block_out), steps,
+                                           _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        else:
+            if tuple(trace.shape) != (int(params["max_steps"]), self.batch, 2) or \
+                    trace.dtype != torch.float32:
+                raise ValueError("trace must be float32 [max_steps, batch, 2]")
+            _check(lib().dg_generate_block_trace(self.handle, self.kv, self.batch,
+                                                 ctypes.byref(sp), int(block_index),
+                                                 _ptr(block_out), steps, _ptr(trace),
+                                                 _ptr(self.ws), self.ws.numel(), _stream(stream)))
         return list(steps)
 
     # ---- stages

@@ -1089,7 +1089,8 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
                              int32_t* halt = nullptr, const float* rowmax = nullptr,
                              void* probs = nullptr, int probs_tiled = 1,
                              int32_t* host_stop = nullptr, int32_t* tk_idx = nullptr,
-                             float* tk_p = nullptr, bool untimed = false) {
+                             float* tk_p = nullptr, bool untimed = false,
+                             float* trace = nullptr) {
     if (!p || !d_logits || !d_canvas || !d_argmax || !d_lock || !d_stats || !d_stop || !d_ws)
         return fail(DG_ERR_ARG, "NULL argument");
     if (batch < 1 || canvas < 1 || canvas > 1024 || vocab < 1 || vocab > 524288)
@@ -1135,6 +1136,7 @@ static dg_status sample_impl(const dg_sampler_params* p, int32_t step, int32_t b
     a.nstop = nstop;
     a.halt = halt;
     a.host_stop = host_stop;
+    a.trace = trace;
     if (probs) {
         // also write the next round's self-conditioning operand
         if (!rowmax || vocab % 128) return fail(DG_ERR_SHAPE, "probabilities need row maxima and vocab %% 128 == 0");
@@ -1258,9 +1260,10 @@ static dg_status ensure_host_flags(dg_model* m, int batch) {
     return DG_OK;
 }
 
-dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
-                            int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
-                            void* d_ws, size_t ws_bytes, void* stream) {
+static dg_status generate_block_impl(dg_model* m, dg_kv* kv, int32_t batch,
+                                     const dg_sampler_params* p, int32_t block_index,
+                                     int32_t* d_block_out, int32_t* h_steps_out, float* d_trace,
+                                     void* d_ws, size_t ws_bytes, void* stream) {
     DG_TRY(check_model(m));
     if (!kv || !p || !d_block_out || !h_steps_out || !d_ws) return fail(DG_ERR_ARG, "NULL argument");
     if (batch != kv->B) return fail(DG_ERR_SHAPE, "batch %d != cache batch %d", batch, kv->B);
@@ -1336,7 +1339,8 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
                            stop, sws, sws_bytes, st, nstop, halt,
                            s.want_rowmax ? s.tmax : nullptr, s.fuse ? s.probs : nullptr,
                            s.probs_tiled, m->hflags + (size_t)(t & 1) * m->hflags_cap,
-                           s.topk > 0 ? s.tk_idx : nullptr, s.topk > 0 ? s.tk_p : nullptr));
+                           s.topk > 0 ? s.tk_idx : nullptr, s.topk > 0 ? s.tk_p : nullptr,
+                           false, d_trace ? d_trace + (size_t)t * batch * 2 : nullptr));
         DG_HIP(hipEventRecord(m->flag_ev[t & 1], st));
         if (t > 0) DG_TRY(flags_of(t - 1, &done));
         if (p->selfcond_on) {
@@ -1358,6 +1362,22 @@ dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_samp
                     nonfinite, nonfinite_round);
     const size_t model_ws = ws_bytes;  // the model scratch is the prefix of d_ws
     return dg_commit_block(m, kv, batch, d_block_out, d_ws, model_ws, stream);
+}
+
+dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
+                            int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
+                            void* d_ws, size_t ws_bytes, void* stream) {
+    return generate_block_impl(m, kv, batch, p, block_index, d_block_out, h_steps_out, nullptr,
+                               d_ws, ws_bytes, stream);
+}
+
+dg_status dg_generate_block_trace(dg_model* m, dg_kv* kv, int32_t batch,
+                                  const dg_sampler_params* p, int32_t block_index,
+                                  int32_t* d_block_out, int32_t* h_steps_out, float* d_trace,
+                                  void* d_ws, size_t ws_bytes, void* stream) {
+    if (!d_trace) return fail(DG_ERR_ARG, "NULL trace");
+    return generate_block_impl(m, kv, batch, p, block_index, d_block_out, h_steps_out, d_trace,
+                               d_ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ stages

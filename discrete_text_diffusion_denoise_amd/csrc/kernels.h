@@ -261,6 +261,10 @@ struct SampleArgs {
     int32_t* nstop = nullptr;        // optional: count of stopped sequences
     int32_t* halt = nullptr;         // optional: set to 1 once all B have stopped
     int32_t* host_stop = nullptr;    // optional: the stop flags also go here (pinned host memory)
+    // optional [B][2]: a running canvas's mean entropy (the value the stop
+    // rule tests) and its count of locked positions after this step; NaN and
+    // 0 for a canvas reported non-finite; stopped canvases are not written
+    float* trace = nullptr;
     // optional (V % 128 == 0): also write the self-conditioning weights of
     // the logits (selfcond_probs) as bf16 [B*N][V], 64-wide blocked
     // (probs_tiled, tiled64_index) or row-major, the operand of the next

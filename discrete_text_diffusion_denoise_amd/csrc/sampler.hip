@@ -958,6 +958,10 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
         if (tid == 0) {
             a.stop[b] = 2;
             if (a.host_stop) a.host_stop[b] = 2;
+            if (a.trace) {
+                a.trace[2 * b] = __builtin_nanf("");
+                a.trace[2 * b + 1] = 0.0f;
+            }
             if (a.nstop && atomicAdd(a.nstop, 1) + 1 == a.B) *a.halt = 1;
         }
         return;
@@ -1008,6 +1012,12 @@ __global__ __launch_bounds__(1024) void sample_canvas_kernel(SampleArgs a) {
         float sumH = 0.0f;
         for (int i = 0; i < N; ++i) sumH = sumH + Hs[i];
         const float meanH = sumH / (float)N;
+        if (a.trace) {
+            int nl = 0;
+            for (int i = 0; i < N; ++i) nl += lk[i];
+            a.trace[2 * b] = meanH;
+            a.trace[2 * b + 1] = (float)nl;
+        }
         int st = (meanH < a.tau) && (!a.require_stable || stable);
         if (a.step + 1 >= a.max_steps) st = 1;
         a.stop[b] = st;

@@ -383,6 +383,19 @@ dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* 
 dg_status dg_generate_block(dg_model* m, dg_kv* kv, int32_t batch, const dg_sampler_params* p,
                             int32_t block_index, int32_t* d_block_out, int32_t* h_steps_out,
                             void* d_ws, size_t ws_bytes, void* stream);
+/* dg_generate_block that also records the per-round quantities the
+ * report-summary page's section 4 describes the loop by (the mean-entropy
+ * trajectory that the stop rule watches, and how many positions are locked):
+ * d_trace [params->max_steps][batch][2] float, caller-owned device memory;
+ * entry [t][b] = (mean entropy of canvas b's round-t logits, i.e. the value
+ * the stop rule tests, and the number of its positions locked after round t)
+ * for every round t < h_steps_out[b] that the canvas ran; (NaN, 0) for the
+ * round in which a canvas's logits turned non-finite; entries of rounds a
+ * canvas did not run are not written.  NULL d_trace is DG_ERR_ARG. */
+dg_status dg_generate_block_trace(dg_model* m, dg_kv* kv, int32_t batch,
+                                  const dg_sampler_params* p, int32_t block_index,
+                                  int32_t* d_block_out, int32_t* h_steps_out, float* d_trace,
+                                  void* d_ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- retained AR mode */
 /* Report-summary page, section 7: the diffusion model keeps its

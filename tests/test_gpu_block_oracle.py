@@ -12,7 +12,8 @@ device flag once every canvas has stopped, so the round it has already
 queued does nothing.  Its rounds are not observable from outside, so the
 test runs three things on identical seeded inputs:
 
-  1. dg_generate_block (block, round counts, committed cache);
+  1. dg_generate_block, as dg_generate_block_trace (block, round counts,
+     committed cache, and each round's mean entropy and locked count);
   2. the same rounds call by call on the GPU (dg_denoise_step +
      dg_sample_update), recording every round's logits and sampler outputs;
   3. the oracle's loop with its model logits replaced by the GPU's of the
@@ -138,9 +139,11 @@ def test_generate_block_against_oracle_loop(name, scale, variant, over):
     mg = binding.Model(cfg, W, batch=B, capacity=P + 2 * N, generate_ws=True)
     mg.encode_prompt(to_dev(prompt))
     block = torch.zeros((B, N), dtype=torch.int32, device=DEV)
-    steps_g = mg.generate_block(params, 0, block)
+    trace = torch.full((params["max_steps"], B, 2), -7.0, dtype=torch.float32, device=DEV)
+    steps_g = mg.generate_block(params, 0, block, trace=trace)
     torch.cuda.synchronize()
     block_g = block.cpu().numpy()
+    trace = trace.cpu().numpy()
     Kg, Vg = [t[0].float().cpu().numpy() for t in mg.kv_tensors()]
     assert steps_g == steps_c
     assert (block_g == recs[-1]["argmax"]).all()
@@ -191,12 +194,21 @@ def test_generate_block_against_oracle_loop(name, scale, variant, over):
         assert (lock[act] == r["lock"][act]).all(), f"round {t}: locks"
         assert (stats[act].view(np.uint32) == r["stats"][act].view(np.uint32)).all(), \
             f"round {t}: statistics"
+        # dg_generate_block_trace: the mean entropy the stop rule tested and the
+        # locked count, for every canvas that ran this round (bit for bit)
+        for b in np.flatnonzero(act):
+            assert np.float32(trace[t, b, 0]) == np.float32(mean_entropy(stats[b])), \
+                f"round {t} canvas {b}: traced mean entropy"
+            assert trace[t, b, 1] == float(lock[b].sum()), f"round {t} canvas {b}: locked count"
         seen.append(dict(canvas=canvas.copy()))
 
     block_o, steps_o = driver.generate_block(W64, cfg, cache, params, 0, B, selfcond=True,
                                              logits_hook=hook, round_hook=on_round)
     assert len(seen) == len(recs)
     assert steps_o.tolist() == steps_g
+    # rounds a canvas did not run are not written
+    for b in range(B):
+        assert (trace[steps_g[b]:, b] == -7.0).all()
     assert (block_o == block_g).all()
     # the committed block: the oracle's float64 encode against the GPU's cache
     assert cache.length == P + N
