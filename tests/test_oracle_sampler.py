@@ -410,3 +410,35 @@ def test_nonfinite_canvas_is_reported_and_left_as_it_was(top_k):
     assert stop[0] == s1[0] != 2
     assert (canvas[0] == c1[0]).all() and (argmax[0] == a1[0]).all() and (lock[0] == lock1[0]).all()
     assert (stats[0].view(np.uint32) == stats1[0].view(np.uint32)).all()
+
+
+def test_locked_token_can_change_later():
+    # Report-summary page, section 1 (multinomial rather than masked
+    # diffusion, so any position can still be replaced), and the youleyou.com
+    # article, "How discrete text diffusion works" (self-correction: when the
+    # confidence at a position drops in a later pass, the sampler renoises
+    # and replaces it): a lock is decided anew every round, so a token locked
+    # in one round is re-drawn, or renoised, when a later round is no longer
+    # confident about it.  Round 0: every position of canvas 0 is
+    # one-hot on token a (all lock to a); round 1: positions 0..127 are
+    # one-hot on another token b (they re-lock to b), positions 128..255 are
+    # flat (they unlock and are renoised, so they leave a almost surely).
+    B, N, V = 1, 256, 1024
+    a, b = 17, 900
+    p = _params(lock_rule=1, lock_theta=0.1, require_stable=0, stop_tau=-1.0, max_steps=48)
+    canvas = np.zeros((B, N), dtype=np.int32)
+    argmax = np.zeros((B, N), dtype=np.int32)
+    stop = np.zeros(B, dtype=np.int32)
+    l0 = np.full((B, N, V), -60.0, dtype=np.float32)
+    l0[..., a] = 40.0
+    lock, _ = sampler.sample_update(p, 0, l0, canvas, argmax, stop)
+    assert (lock == 1).all() and (canvas == a).all()
+    l1 = np.zeros((B, N, V), dtype=np.float32)
+    l1[:, :128, :] = -60.0
+    l1[:, :128, b] = 40.0
+    lock, stats = sampler.sample_update(p, 1, l1, canvas, argmax, stop)
+    assert stop[0] == 0
+    assert (lock[0, :128] == 1).all() and (canvas[0, :128] == b).all()
+    assert (lock[0, 128:] == 0).all()
+    assert (canvas[0, 128:] != a).mean() > 0.95
+    assert (argmax[0, :128] == b).all()
