@@ -313,3 +313,33 @@ def test_nonfinite_logits_are_reported_like_the_oracle(top_k):
     assert g[4].tolist() == expect
     if top_k:
         assert r[4][3] != 2
+
+
+def test_locked_tokens_are_re_decided_bit_exact():
+    # A lock is decided anew every round (report-summary page, section 1;
+    # youleyou.com article, "How discrete text diffusion works"): round 0
+    # locks every position on token a, round 1 re-locks half of them on
+    # token b and leaves the other half flat, which unlocks and renoises
+    # them.  GPU and oracle agree bit for bit in both rounds.
+    B, N, V = 2, 256, 4096
+    a_tok, b_tok = 17, 3900
+    params = synthetic.default_sampler_params(lock_rule=1, lock_theta=0.1, require_stable=0,
+                                              stop_tau=-1.0, max_steps=48, seed=9)
+    l0 = np.full((B, N, V), -60.0, dtype=np.float32)
+    l0[..., a_tok] = 40.0
+    l1 = np.zeros((B, N, V), dtype=np.float32)
+    l1[:, :128, :] = -60.0
+    l1[:, :128, b_tok] = 40.0
+    canvas = np.zeros((B, N), dtype=np.int32)
+    argmax = np.zeros((B, N), dtype=np.int32)
+    stop = np.zeros(B, dtype=np.int32)
+    for t, lg in enumerate((l0, l1)):
+        g = gpu_update(params, t, lg, canvas, argmax, stop)
+        r = oracle_update(params, t, lg, canvas, argmax, stop)
+        assert_same(g, r, f"round {t}")
+        canvas, argmax, lock, _, stop = r
+        if t == 0:
+            assert (lock == 1).all() and (canvas == a_tok).all()
+        else:
+            assert (lock[:, :128] == 1).all() and (canvas[:, :128] == b_tok).all()
+            assert (lock[:, 128:] == 0).all() and (canvas[:, 128:] != a_tok).mean() > 0.95
