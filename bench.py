@@ -1074,7 +1074,9 @@ def bench_diffusion(args, config, layers, steps, warmup, want_cpu):
     }
     if args.copy_probe and config == args.config:
         copy_probe(torch)
-    if config == args.config and not args.no_peaks:
+    # (not with --copy-probe: the calibration's own device copy would join the
+    # copies the HBM counters are calibrated on)
+    if config == args.config and not args.no_peaks and not args.copy_probe:
         pk = measured_peaks(torch)
         out["measured_peaks"] = pk
         ref = {"hbm": pk["hbm_read_gbs"], "mfma": pk["bf16_mfma_tflops"]}.get(roof["bound"])
