@@ -5,8 +5,12 @@
 // position (causal).  Report-summary page (animattoys.com), section 2;
 // youleyou.com article, "Architecture basis".
 //
-// A wave owns 16 queries of one query head; the four waves of a workgroup
-// share one KV head, so each K/V tile staged in LDS serves all of them.
+// Three kernels: attn3_kernel (bf16, head dim 128, the canvas: 32 queries a
+// wave on the 32x32x16 MFMA), attn2_kernel (bf16, head dim 128, causal: the
+// prompt encode and decode steps) and attn_kernel (other shapes, fp32).
+// In attn_kernel and attn2_kernel a wave owns 16 queries of one query head;
+// the four waves of a workgroup share one KV head, so each K/V tile staged
+// in LDS serves all of them.
 // Scores are computed transposed, S^T = K Q^T, so that a lane holds 8 keys of
 // ONE query: the online-softmax state (max, sum, rescale) is lane-local
 // except for one max across the 4 lanes of a query, and the probabilities
@@ -283,6 +287,7 @@ constexpr float RESCALE_T = 8.0f;
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int sw2(int r) {
     r &= 15;
@@ -573,6 +578,265 @@ __global__ __launch_bounds__(256, 4) void attn2_kernel(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------
+// bf16, head dim 128, canvas (no mask but the key range): 32 queries of one
+// query head per wave on the 32x32x16 MFMA, so every K and V fragment read
+// from LDS serves twice the queries of attn2_kernel.
+//   * S^T = K Q^T per 32-key tile: A = K (32 keys x 16 dh), B = Q^T; a lane
+//     holds 16 keys (8(i/4) + 4g + i%4, g = lane/32) of query lane%32.
+//   * The PV product takes the 32 keys as two halves of 16; with the
+//     k-index of half h mapped to key 16h + 8(j/4) + 4g + j%4, lane l's B
+//     operand is its own probabilities 8h..8h+7, and the A operand (V^T,
+//     32 dh x 16 keys) is two transposing reads of 4 keys each.
+//   * K rows: chunk c of row r in slot c ^ (r % 16); V rows: slot
+//     c ^ 4(r % 4), so the 32 lanes of half a transposing read (4 rows x 4
+//     chunks) touch 16 distinct slots, and rows 4 apart share a swizzle (the
+//     second read of a fragment and the second key half are immediate
+//     offsets).
+constexpr int KT3 = 32;
+constexpr int SLOT3 = 2 * TILE2;
+
+__device__ __forceinline__ int swv3(int r) { return 4 * (r & 3); }
+
+__global__ __launch_bounds__(256, 3) void attn3_kernel(AttnArgs a) {
+    if (a.halt && *a.halt) return;
+    constexpr int DH = 128;
+    __shared__ __align__(1024) unsigned char ring[RING2 * SLOT3];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q32 = lane & 31, g = lane >> 5;
+    const int G = a.Hq / a.Hkv;
+    const int nqt = cdiv(a.n, 32);
+    const int units = nqt * G;
+    const int nx = cdiv(units, 4);
+    const int ngroups = a.Hkv * a.B * a.splits;
+    int bx, grp;
+    if (ngroups % 8 == 0) {
+        const int slot = blockIdx.x >> 3;
+        bx = slot % nx;
+        grp = (slot / nx) * 8 + (blockIdx.x & 7);
+    } else {
+        bx = blockIdx.x % nx;
+        grp = blockIdx.x / nx;
+    }
+    const int kvh = grp % a.Hkv;
+    const int b = (grp / a.Hkv) / a.splits, split = (grp / a.Hkv) % a.splits;
+    const int unit = bx * 4 + wave;
+    const bool wvalid = unit < units;
+    const int qt = wvalid ? unit / G : 0;
+    const int h = kvh * G + (wvalid ? unit % G : 0);
+    const int qi = qt * 32 + q32;
+    const bool qvalid = wvalid && qi < a.n;
+    const long qrow = (long)b * a.n + (qvalid ? qi : 0);
+
+    const int kb = split * a.split_len;
+    const int ke = min(a.kv_len, kb + a.split_len);
+    const int ntiles = ke > kb ? cdiv(ke - kb, KT3) : 0;
+
+    // Q^T fragments (B operand): query q32, dh 16s + 8g .. +7, scaled so
+    // that a score is log2-e based
+    const float qscale = LOG2E / sqrtf((float)DH);
+    u32x4_t qf[8];
+    {
+        const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + qrow * (long)a.Hq * DH + (long)h * DH;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qvalid) v = *reinterpret_cast<const uint4*>(Q + 16 * s + 8 * g);
+            qf[s] = u32x4_t{scale_bf2(v.x, qscale), scale_bf2(v.y, qscale), scale_bf2(v.z, qscale),
+                            scale_bf2(v.w, qscale)};
+        }
+    }
+
+    const bf16_t* Kc = reinterpret_cast<const bf16_t*>(a.kc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
+    const bf16_t* Vc = reinterpret_cast<const bf16_t*>(a.vc) + ((long)b * a.Hkv + kvh) * (long)a.cap * DH;
+
+    // direct-to-LDS fill: wave w writes 1 KiB blocks 2w and 2w+1 of each
+    // tile; lane l of block q lands in row 4q + l/16, slot l%16
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int frow[2];
+    uint32_t kof[2], vof[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        frow[i] = 4 * (2 * wv + i) + (lane >> 4);
+        kof[i] = frow[i] * ROW2 + (((lane & 15) ^ (frow[i] & 15)) << 4);
+        vof[i] = frow[i] * ROW2 + (((lane & 15) ^ swv3(frow[i])) << 4);
+    }
+    const char* Kb = reinterpret_cast<const char*>(Kc);
+    const char* Vb = reinterpret_cast<const char*>(Vc);
+    auto issue = [&](int t) {
+        const int k0_ = kb + t * KT3;
+        unsigned char* sl_ = ring + (t % RING2) * SLOT3 + 2 * wv * 1024;
+        const char* kt_ = Kb + (long)k0_ * ROW2;
+        const char* vt_ = Vb + (long)k0_ * ROW2;
+        if (k0_ + KT3 <= ke) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_global_load_lds((glb_void*)(kt_ + kof[i]), (lds_void*)(sl_ + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_void*)(vt_ + vof[i]), (lds_void*)(sl_ + TILE2 + i * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t r_ = min(frow[i], ke - 1 - k0_) * ROW2;
+                __builtin_amdgcn_global_load_lds((glb_void*)(kt_ + r_ + (kof[i] & (ROW2 - 1))), (lds_void*)(sl_ + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_void*)(vt_ + r_ + (vof[i] & (ROW2 - 1))), (lds_void*)(sl_ + TILE2 + i * 1024), 16, 0, 0);
+            }
+        }
+    };
+
+    // K fragment of dh slice s (A operand): row q32 (key), chunk 2s + g, in
+    // slot (2s + g) ^ (q32 % 16): address ka0 ^ 32 s
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t ka0 = q32 * ROW2 + ((g ^ (q32 & 1)) << 4) + (((q32 & 15) >> 1) << 5);
+    // V^T fragment of dh block blk (A operand), first read of key half 0: the
+    // 16-lane group q = lane/16 reads keys 4g + (lane%16)/4 (+0..3 after the
+    // transpose), dh 32 blk + 16 (q % 2) + 4 (lane % 4) .. +3; the second read
+    // is 8 keys on (+2048), key half 1 is 16 keys on (+4096)
+    uint32_t va[4];
+    {
+        const int rv = 4 * g + ((lane & 15) >> 2);
+        const int qh = (lane >> 4) & 1;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+            va[blk] = TILE2 + rv * ROW2 + (((4 * blk + 2 * qh + ((lane & 3) >> 1)) ^ swv3(rv)) << 4) +
+                      8 * (lane & 1);
+    }
+
+    f32x16_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+    float m_run = -1e30f, l_run = 0.f;
+
+    if (ntiles > 0) issue(0);
+    for (int t = 0; t < ntiles; ++t) {
+        DG_WAIT_VM(0);
+        attn_barrier();
+        if (t + 1 < ntiles) issue(t + 1);
+        const uint32_t sb = ring0 + (t % RING2) * SLOT3;
+        const int k0 = kb + t * KT3;
+
+        // S^T - tile: two reads of four K slices each
+        f32x16_t sc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            u32x4_t k0f, k1f, k2f, k3f;
+            const uint32_t base = sb + ka0;
+            asm volatile(
+                "ds_read_b128 %0, %4\n ds_read_b128 %1, %5\n"
+                "ds_read_b128 %2, %6\n ds_read_b128 %3, %7\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(k0f), "=&v"(k1f), "=&v"(k2f), "=&v"(k3f)
+                : "v"(base ^ (uint32_t)(32 * (4 * part + 0))), "v"(base ^ (uint32_t)(32 * (4 * part + 1))),
+                  "v"(base ^ (uint32_t)(32 * (4 * part + 2))), "v"(base ^ (uint32_t)(32 * (4 * part + 3)))
+                : "memory");
+            const u32x4_t kf[4] = {k0f, k1f, k2f, k3f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[s]),
+                                                             __builtin_bit_cast(bf16x8_t, qf[4 * part + s]),
+                                                             sc, 0, 0, 0);
+        }
+
+        // softmax of the lane's 16 keys against the running maximum
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = sc[i];
+        if (k0 + KT3 > ke) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (key >= ke) x[i] = -INFINITY;
+            }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+        if (__ballot(mx > m_run + RESCALE_T)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m_run, mx);
+            const float corr = __builtin_amdgcn_exp2f(m_run - mn);
+            l_run *= corr;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[blk][e] *= corr;
+            m_run = mn;
+        }
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ls += p[i];
+        l_run += ls;
+        u32x4_t pf[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            pf[hh] = u32x4_t{pack_bf2(p[8 * hh + 0], p[8 * hh + 1]), pack_bf2(p[8 * hh + 2], p[8 * hh + 3]),
+                             pack_bf2(p[8 * hh + 4], p[8 * hh + 5]), pack_bf2(p[8 * hh + 6], p[8 * hh + 7])};
+
+        // O^T += V^T P^T: per pair of dh blocks, both key halves
+#pragma unroll
+        for (int bp = 0; bp < 2; ++bp) {
+            u32x2_t a0, a1, a2, a3, b0, b1, b2, b3;
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %8 offset:0\n ds_read_b64_tr_b16 %1, %8 offset:2048\n"
+                "ds_read_b64_tr_b16 %2, %8 offset:4096\n ds_read_b64_tr_b16 %3, %8 offset:6144\n"
+                "ds_read_b64_tr_b16 %4, %9 offset:0\n ds_read_b64_tr_b16 %5, %9 offset:2048\n"
+                "ds_read_b64_tr_b16 %6, %9 offset:4096\n ds_read_b64_tr_b16 %7, %9 offset:6144\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+                : "v"(sb + va[2 * bp]), "v"(sb + va[2 * bp + 1])
+                : "memory");
+            const u32x4_t v00 = u32x4_t{a0.x, a0.y, a1.x, a1.y}, v01 = u32x4_t{a2.x, a2.y, a3.x, a3.y};
+            const u32x4_t v10 = u32x4_t{b0.x, b0.y, b1.x, b1.y}, v11 = u32x4_t{b2.x, b2.y, b3.x, b3.y};
+            o[2 * bp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v00),
+                                                                __builtin_bit_cast(bf16x8_t, pf[0]), o[2 * bp], 0, 0, 0);
+            o[2 * bp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v01),
+                                                                __builtin_bit_cast(bf16x8_t, pf[1]), o[2 * bp], 0, 0, 0);
+            o[2 * bp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v10),
+                                                                    __builtin_bit_cast(bf16x8_t, pf[0]), o[2 * bp + 1], 0, 0, 0);
+            o[2 * bp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v11),
+                                                                    __builtin_bit_cast(bf16x8_t, pf[1]), o[2 * bp + 1], 0, 0, 0);
+        }
+    }
+
+    // lane holds O^T[dh = 32 blk + 8 (i/4) + 4 g + i%4][query q32]
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!qvalid) return;
+    if (a.splits == 1) {
+        bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + qrow * (long)a.Hq * DH + (long)h * DH;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint2 w;
+                w.x = pack_bf2(o[blk][4 * r + 0] * inv, o[blk][4 * r + 1] * inv);
+                w.y = pack_bf2(o[blk][4 * r + 2] * inv, o[blk][4 * r + 3] * inv);
+                *reinterpret_cast<uint2*>(out + 32 * blk + 8 * r + 4 * g) = w;
+            }
+    } else {
+        const long base = ((long)split * a.B * a.n + qrow) * a.Hq + h;
+        float* po = a.part_o + base * DH;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<f32x4_t*>(po + 32 * blk + 8 * r + 4 * g) =
+                    f32x4_t{o[blk][4 * r + 0], o[blk][4 * r + 1], o[blk][4 * r + 2], o[blk][4 * r + 3]};
+        if (g == 0) {
+            a.part_ml[base * 2 + 0] = m_run;
+            a.part_ml[base * 2 + 1] = l_tot;
+        }
+    }
+}
+
 // Merge of split partials: one workgroup of DH threads per (token, head).
 template <typename T>
 __global__ void attn_merge_kernel(AttnArgs a) {
@@ -604,8 +868,8 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 
 }  // namespace
 
-// The bf16 head-dim-128 kernel (attn2_kernel) takes the shape, one query
-// head per wave.
+// bf16 with head dim 128 goes to attn3_kernel (canvas, no mask) or
+// attn2_kernel (causal, one query head per wave).
 bool attn2_takes(int dh, bool bf16) { return bf16 && dh == 128; }
 int attn2_hpw(int) { return 1; }
 
@@ -613,11 +877,14 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
                      int* split_len, int dh, bool bf16) {
     const int G = Hq / Hkv;
     // workgroups of one key range, and the number to aim for: attn_kernel
-    // runs eight small workgroups per CU, attn2_kernel two large ones
+    // runs eight small workgroups per CU, attn2_kernel four, attn3_kernel
+    // three
     const bool v2 = attn2_takes(dh, bf16);
-    const long base = v2 ? (long)cdiv(cdiv(n, 16) * (G / attn2_hpw(G)), 4) * Hkv * B
+    const bool v3 = v2 && !causal;
+    const long base = v3 ? (long)cdiv(cdiv(n, 32) * G, 4) * Hkv * B
+                    : v2 ? (long)cdiv(cdiv(n, 16) * (G / attn2_hpw(G)), 4) * Hkv * B
                          : (long)cdiv(G * cdiv(n, 16), 4) * Hkv * B;
-    const int target = v2 ? 1024 : 2048;
+    const int target = v3 ? 768 : v2 ? 1024 : 2048;
     int splits = 1;
     if (!causal && kv_len > 256) {
         splits = (int)std::min<long>(cdiv(kv_len, 256), std::max<long>(1, cdiv(target, (int)base)));
@@ -632,7 +899,8 @@ int attention_splits(int B, int n, int Hq, int Hkv, int kv_len, int causal, int 
     }
     if (v2 && splits > 1) {
         // round to a count that makes (KV heads x sequences x splits) a
-        // multiple of 8, so that attn2_kernel can keep each key range on one XCD
+        // multiple of 8, so that attn2_kernel and attn3_kernel can keep each
+        // key range on one XCD
         int g = Hkv * B, m = 8;
         while (m > 1 && g % 2 == 0) {
             g /= 2;
@@ -652,7 +920,10 @@ hipError_t attention(const AttnArgs& a, hipStream_t st) {
     // the merge keeps the split weights in one wave
     if (a.splits > 1 && (a.splits > 32 || a.dh < 64)) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
-    if (attn2_takes(a.dh, sizeof(T) == 2)) {
+    if (attn2_takes(a.dh, sizeof(T) == 2) && !a.causal) {
+        dim3 grid3(cdiv(cdiv(a.n, 32) * G, 4) * a.Hkv * a.B * a.splits);
+        hipLaunchKernelGGL(attn3_kernel, grid3, dim3(256), 0, st, a);
+    } else if (attn2_takes(a.dh, sizeof(T) == 2)) {
         const int hpw = attn2_hpw(G);
         dim3 grid2(cdiv(cdiv(a.n, 16) * (G / hpw), 4) * a.Hkv * a.B * a.splits);
         hipLaunchKernelGGL(attn2_kernel<1>, grid2, dim3(256), 0, st, a);
