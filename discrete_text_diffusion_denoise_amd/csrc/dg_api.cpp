@@ -173,7 +173,7 @@ struct Scratch {
     uint8_t* act8 = nullptr;
     uint8_t* act8s = nullptr;
     int32_t* work = nullptr;  // expert chunk prefix over the busiest-first order
-    int32_t* work_rank = nullptr;  // the expert rank of each work item
+    int32_t* items = nullptr;      // the work items' records (4 words each)
     float* tmax;      // blocked models: head GEMM row maxima per 64-column slab
     // set by the block loop (not carved): the head GEMM writes its slab
     // maxima (fuse), and the probabilities of the previous round's logits are
@@ -256,9 +256,9 @@ bool carve_scratch(Carver& cv, const dg_model* m, int B, Scratch& s) {
         s.act8s = cv.take<uint8_t>(T * c.top_k * c.d_ff / 32);
     }
     // the expert kernels' work items (chunks of up to 64 tokens of an expert)
-    // and the rank of each item's expert
+    // and their records
     s.work = cv.take<int32_t>(c.n_experts + 1);
-    s.work_rank = cv.take<int32_t>((T * c.top_k + dg::kMoeChunk - 1) / dg::kMoeChunk + c.n_experts);
+    s.items = cv.take<int32_t>(4 * ((T * c.top_k + dg::kMoeChunk - 1) / dg::kMoeChunk + c.n_experts));
     s.tmax = m->blocked ? cv.take<float>(Tc * (size_t)(c.vocab / 64)) : nullptr;
     s.tk_idx = cv.take<int32_t>(Tc * dg::kTopKMax);
     s.tk_p = cv.take<float>(Tc * dg::kTopKMax);
@@ -466,7 +466,7 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.act8 = s.act8;
     a.act8s = s.act8s;
     a.work = s.work;
-    a.work_rank = s.work_rank;
+    a.items = s.items;
     a.y = s.y;
     a.h = h;
     a.k_rotate = 1;

@@ -199,10 +199,11 @@ struct MoeArgs {
     // chunks of kMoeChunk tokens (written with `order` by moe_route): the
     // work items (expert, chunk) of the block-scaled expert kernels
     int32_t* work = nullptr;
-    // optional [cdiv(T*k, kMoeChunk) + E]: the rank (in `order`) of each work
-    // item's expert, written with `work`, so a block finds its item's expert
-    // with one load
-    int32_t* work_rank = nullptr;
+    // optional [cdiv(T*k, kMoeChunk) + E][4] (16-byte aligned): per work
+    // item, written with `work` once the offsets are known, (its expert, the
+    // expert's first routed row, the item's first row within the expert, the
+    // expert's row count), so a block finds its item with one load
+    int32_t* items = nullptr;
 };
 constexpr int kMoeChunk = 64;
 // compute units of the current device (cached per device)

@@ -85,9 +85,8 @@ __global__ __launch_bounds__(256) void count_kernel(MoeArgs a) {
 }
 
 // work[r] for r = 0 .. E: exclusive prefix of ch[0 .. E) (chunks of the
-// expert of rank r, in LDS), by threads 0..63 of the block, four each; and,
-// when `rank` is set, rank[i] = r for the items i of rank r.
-__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work, int32_t* rank) {
+// expert of rank r, in LDS), by threads 0..63 of the block, four each.
+__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) {
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     int v[4], sum = 0;
@@ -105,20 +104,28 @@ __device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work, 
     int ex = incl - sum;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (tid * 4 + q < E) {
-            work[tid * 4 + q] = ex;
-            if (rank)
-                for (int i = 0; i < v[q]; ++i) rank[ex + i] = tid * 4 + q;
-        }
+        if (tid * 4 + q < E) work[tid * 4 + q] = ex;
         ex += v[q];
     }
     if (tid == 63) work[E] = incl;
 }
 
-// The rank of work item w's expert: work_rank when the routing wrote it,
-// else a binary search of work[] (work[r] <= w < work[r + 1]).
+// The work items' records (a.items), from order, offsets and work once
+// this workgroup (or an earlier kernel) has written them: the threads take
+// the ranks in turn and write one record per chunk of the rank's expert.
+__device__ __forceinline__ void write_items(const MoeArgs& a) {
+    for (int r = threadIdx.x; r < a.E; r += blockDim.x) {
+        const int e = a.order[r];
+        const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
+        const int first = a.work[r];
+        for (int i = 0; i * kMoeChunk < cnt; ++i)
+            reinterpret_cast<int4*>(a.items)[first + i] = make_int4(e, off, i * kMoeChunk, cnt);
+    }
+}
+
+// The rank of work item w's expert when no records were written: a binary
+// search of work[] (work[r] <= w < work[r + 1]).
 __device__ __forceinline__ int item_rank(const MoeArgs& a, int w) {
-    if (a.work_rank) return a.work_rank[w];
     int lo = 0, hi = a.E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -147,7 +154,10 @@ __global__ __launch_bounds__(256) void order_kernel(MoeArgs a) {
     }
     if (!a.work) return;
     __syncthreads();
-    write_work(ch, a.E, a.work, a.work_rank);
+    write_work(ch, a.E, a.work);
+    if (!a.items) return;
+    __syncthreads();
+    write_items(a);
 }
 
 // One wave per expert: exclusive prefix of counts, then a stable, ordered
@@ -549,11 +559,19 @@ __global__ __launch_bounds__(256) void expert_dma_kernel(MoeArgs a) {
     if (a.work && a.order) {
         const int w = blockIdx.y;
         if (w >= a.work[a.E]) return;
-        const int lo = item_rank(a, w);
-        c.e = a.order[lo];
-        c.off = a.offsets[c.e];
-        c.cnt = a.offsets[c.e + 1] - c.off;
-        c.m0 = (w - a.work[lo]) * kMoeChunk;
+        if (a.items) {
+            const int4 it = reinterpret_cast<const int4*>(a.items)[w];
+            c.e = it.x;
+            c.off = it.y;
+            c.m0 = it.z;
+            c.cnt = it.w;
+        } else {
+            const int lo = item_rank(a, w);
+            c.e = a.order[lo];
+            c.off = a.offsets[c.e];
+            c.cnt = a.offsets[c.e + 1] - c.off;
+            c.m0 = (w - a.work[lo]) * kMoeChunk;
+        }
         c.m1 = min(c.cnt, c.m0 + kMoeChunk);
     } else {
         // the busiest experts first, so their longer blocks do not form the tail
@@ -641,7 +659,7 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
         ch[rank] = cdiv(me, kMoeChunk);
     }
     __syncthreads();
-    if (a.order && a.work) write_work(ch, a.E, a.work, a.work_rank);
+    if (a.order && a.work) write_work(ch, a.E, a.work);
     if (tid < 64) {                                    // exclusive scan of the totals
         int v[4], sum = 0;
 #pragma unroll
@@ -669,6 +687,7 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
         if (tid == 63) a.offsets[a.E] = incl;
     }
     __syncthreads();
+    if (a.order && a.work && a.items) write_items(a);
     if (tid < 256) {                                   // range offsets: expert offset + earlier ranges
         int run = tot[tid];
         for (int w = 0; w < PW; ++w) {

@@ -100,13 +100,17 @@ struct MxTask {
 template <int MODE>
 __device__ __forceinline__ MxTask mx_task(const MoeArgs& a, int t, int NX, int wave) {
     const int w = t / NX, bx = t - w * NX;
-    // the rank r of the item's expert (work[r] <= w < work[r + 1])
-    int lo;
-    if (a.work_rank) {
-        lo = sload(a.work_rank + w);
+    MxTask k;
+    if (a.items) {
+        // the item's record: one scalar load of four words
+        const int32_t* rec = a.items + 4 * w;
+        k.e = sload(rec);
+        k.off = sload(rec + 1);
+        k.c0 = sload(rec + 2);
+        k.cnt = sload(rec + 3);
     } else {
-        lo = 0;
-        int hi = a.E - 1;
+        // the rank r of the item's expert (work[r] <= w < work[r + 1])
+        int lo = 0, hi = a.E - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (sload(a.work + mid) <= w)
@@ -114,12 +118,11 @@ __device__ __forceinline__ MxTask mx_task(const MoeArgs& a, int t, int NX, int w
             else
                 hi = mid - 1;
         }
+        k.e = sload(a.order + lo);
+        k.off = sload(a.offsets + k.e);
+        k.cnt = sload(a.offsets + k.e + 1) - k.off;
+        k.c0 = (w - sload(a.work + lo)) * kMoeChunk;
     }
-    MxTask k;
-    k.e = sload(a.order + lo);
-    k.off = sload(a.offsets + k.e);
-    k.cnt = sload(a.offsets + k.e + 1) - k.off;
-    k.c0 = (w - sload(a.work + lo)) * kMoeChunk;
     k.f0 = MODE == 0 ? bx * (32 * MX_TPW) + 16 * (MX_TPW / 2) * wave
                      : bx * (64 * MX_TPW) + 16 * MX_TPW * wave;
     return k;
