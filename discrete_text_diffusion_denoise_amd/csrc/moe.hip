@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void count_kernel(MoeArgs a) {
 }
 
 // work[r] for r = 0 .. E: exclusive prefix of ch[0 .. E) (chunks of the
-// expert of rank r, in LDS), by threads 0..63 of the block, four each.
-__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) {
+// expert of rank r, in LDS), by threads 0..63 of the block, four each; also
+// into the LDS array lw[0 .. E) when it is given.
+__device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work, int* lw = nullptr) {
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     int v[4], sum = 0;
@@ -104,22 +105,30 @@ __device__ __forceinline__ void write_work(const int* ch, int E, int32_t* work) 
     int ex = incl - sum;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (tid * 4 + q < E) work[tid * 4 + q] = ex;
+        if (tid * 4 + q < E) {
+            work[tid * 4 + q] = ex;
+            if (lw) lw[tid * 4 + q] = ex;
+        }
         ex += v[q];
     }
     if (tid == 63) work[E] = incl;
 }
 
-// The work items' records (a.items), from order, offsets and work once
-// this workgroup (or an earlier kernel) has written them: the threads take
-// the ranks in turn and write one record per chunk of the rank's expert.
+// The records of rank r's work items: expert e, its first routed row off
+// and row count cnt, its first item `first`; one record per chunk.
+__device__ __forceinline__ void write_rank_items(const MoeArgs& a, int e, int off, int cnt, int first) {
+    for (int i = 0; i * kMoeChunk < cnt; ++i)
+        reinterpret_cast<int4*>(a.items)[first + i] = make_int4(e, off, i * kMoeChunk, cnt);
+}
+
+// The work items' records (a.items), from order, offsets and work once an
+// earlier kernel, or this workgroup before a barrier, has written them: the
+// threads take the ranks in turn.
 __device__ __forceinline__ void write_items(const MoeArgs& a) {
     for (int r = threadIdx.x; r < a.E; r += blockDim.x) {
         const int e = a.order[r];
-        const int off = a.offsets[e], cnt = a.offsets[e + 1] - off;
-        const int first = a.work[r];
-        for (int i = 0; i * kMoeChunk < cnt; ++i)
-            reinterpret_cast<int4*>(a.items)[first + i] = make_int4(e, off, i * kMoeChunk, cnt);
+        const int off = a.offsets[e];
+        write_rank_items(a, e, off, a.offsets[e + 1] - off, a.work[r]);
     }
 }
 
@@ -634,6 +643,9 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
     __shared__ int cw[PW][256];    // per-range counts, then per-range running offsets
     __shared__ int tot[256];       // per-expert totals, then expert offsets
     __shared__ int ch[256];        // chunks of the expert of each rank
+    __shared__ int ord[256];       // the expert of each rank
+    __shared__ int wk[256];        // the first work item of each rank
+    __shared__ int cnt[256];       // per-expert totals, kept through the scan
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int total = a.T * a.k;
     const int per = cdiv(cdiv(total, 64), PW) * 64;    // assignments per range
@@ -656,10 +668,11 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
             rank += (o > me) || (o == me && e2 < tid);
         }
         a.order[rank] = tid;
+        ord[rank] = tid;
         ch[rank] = cdiv(me, kMoeChunk);
     }
     __syncthreads();
-    if (a.order && a.work) write_work(ch, a.E, a.work);
+    if (a.order && a.work) write_work(ch, a.E, a.work, wk);
     if (tid < 64) {                                    // exclusive scan of the totals
         int v[4], sum = 0;
 #pragma unroll
@@ -682,12 +695,17 @@ __global__ __launch_bounds__(64 * PW) void place_all_kernel(MoeArgs a) {
                 a.counts[e] = v[q];
             }
             tot[e] = ex;
+            cnt[e] = v[q];
             ex += v[q];
         }
         if (tid == 63) a.offsets[a.E] = incl;
     }
     __syncthreads();
-    if (a.order && a.work && a.items) write_items(a);
+    if (a.order && a.work && a.items)                  // the records, from LDS
+        for (int r = tid; r < a.E; r += 64 * PW) {
+            const int e = ord[r];
+            write_rank_items(a, e, tot[e], cnt[e], wk[r]);
+        }
     if (tid < 256) {                                   // range offsets: expert offset + earlier ranges
         int run = tot[tid];
         for (int w = 0; w < PW; ++w) {
