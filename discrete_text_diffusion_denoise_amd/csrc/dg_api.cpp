@@ -119,7 +119,7 @@ struct dg_model {
     std::vector<dg_layer_weights> layers;
     // block loop: pinned host memory that the sampler's canvas kernel writes
     // the stop flags of two rounds into, and the events that say they have
-    // arrived (created on first use)
+    // arrived (created with the model)
     int32_t* hflags = nullptr;
     int hflags_cap = 0;
     hipEvent_t flag_ev[2] = {nullptr, nullptr};
@@ -770,6 +770,22 @@ dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** 
     m->w_sc = w->w_sc;
     m->final_norm = w->final_norm;
     m->layers.assign(w->layers, w->layers + c.n_layers);
+    // the block loop's stop-flag slots and their events, freed with the
+    // model.  Without a usable device they stay absent: creation still
+    // succeeds (validation needs no GPU) and the block loop reports it.
+    bool loop_ok = true;
+    for (hipEvent_t& e : m->flag_ev)
+        if (loop_ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            e = nullptr;
+            loop_ok = false;
+        }
+    if (loop_ok &&
+        hipHostMalloc((void**)&m->hflags, 2 * (size_t)DG_MAX_LOOP_BATCH * sizeof(int32_t)) ==
+            hipSuccess)
+        m->hflags_cap = DG_MAX_LOOP_BATCH;
+    else
+        m->hflags = nullptr;
+    (void)hipGetLastError();   // a failure here is reported by the block loop
     *out = m;
     return DG_OK;
 }
@@ -1247,16 +1263,14 @@ dg_status dg_generate_workspace_bytes(const dg_model* m, int32_t batch, size_t* 
     return DG_OK;
 }
 
-static dg_status ensure_host_flags(dg_model* m, int batch) {
-    if (!m->flag_ev[0]) {
-        for (hipEvent_t& e : m->flag_ev) DG_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-    }
-    if (m->hflags_cap < batch) {
-        if (m->hflags) DG_HIP(hipHostFree(m->hflags));
-        m->hflags = nullptr;
-        DG_HIP(hipHostMalloc((void**)&m->hflags, 2 * (size_t)batch * sizeof(int32_t)));
-        m->hflags_cap = batch;
-    }
+// The block loop reads each round's stop flags from pinned host memory:
+// two slots (one per round parity) of up to DG_MAX_LOOP_BATCH flags, allocated
+// with the model so that no call of the loop allocates.
+static dg_status check_loop_batch(const dg_model* m, int batch) {
+    if (!m->hflags || !m->flag_ev[0] || !m->flag_ev[1])
+        return fail(DG_ERR_HIP, "the model's stop-flag buffers were not allocated at creation");
+    if (batch > m->hflags_cap)
+        return fail(DG_ERR_CAPACITY, "block loop batch %d > %d", batch, m->hflags_cap);
     return DG_OK;
 }
 
@@ -1283,7 +1297,7 @@ static dg_status generate_block_impl(dg_model* m, dg_kv* kv, int32_t batch,
                             ws_bytes, cv.off);
     hipStream_t st = as_stream(stream);
     const size_t Tc = (size_t)batch * c.canvas;
-    DG_TRY(ensure_host_flags(m, batch));
+    DG_TRY(check_loop_batch(m, batch));
     DG_HIP(dg::canvas_init(p->seed, block_index, batch, c.canvas, c.vocab, canvas, st));
     DG_HIP(dg::fill_i32(argmax, 0, (long)Tc, st));
     DG_HIP(dg::fill_i32(stop, 0, batch + 2, st));

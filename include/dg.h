@@ -155,7 +155,15 @@ const char* dg_status_string(dg_status s);
 const char* dg_last_error(void);
 
 /* ---------------------------------------------------------------- model */
-/* Validates the configuration and copies the weight pointer table.
+/* Most canvases one dg_generate_block call runs (its stop-flag slots are
+ * allocated with the model). */
+#define DG_MAX_LOOP_BATCH 4096
+
+/* Validates the configuration and copies the weight pointer table.  Also
+ * allocates the block loop's only host resources, once: two events and
+ * 2 x DG_MAX_LOOP_BATCH int32 stop flags in pinned host memory (hipHostMalloc),
+ * freed by dg_model_destroy; dg_generate_block reports DG_ERR_HIP when they
+ * could not be allocated (no usable device at creation).
  * DG_ERR_SHAPE on unsupported shapes (limits listed in dg_config);
  * DG_ERR_DTYPE on an unknown dtype or expert_dtype, DG_ERR_UNSUPPORTED for
  * FP8 experts outside their limits, DG_ERR_ARG when their scales are
@@ -373,7 +381,8 @@ dg_status dg_commit_block(dg_model* m, dg_kv* kv, int32_t batch, const int32_t* 
  * ran.  Waits on the stream once per round to read the stop flags.  A canvas
  * whose logits turn non-finite stops in that round (dg_sample_update's
  * d_stop = 2); the others run on, d_block_out and h_steps_out are written,
- * the block is NOT committed and the call returns DG_ERR_NONFINITE.  For
+ * the block is NOT committed and the call returns DG_ERR_NONFINITE.
+ * DG_ERR_CAPACITY if batch > DG_MAX_LOOP_BATCH.  The call allocates nothing.  For
  * blocked models with weights.embed_head the rounds run as
  * dg_stage_head_rowmax + dg_sample_update_probs, so the next round's
  * self-conditioning operand comes out of the sampler's pass over the logits
