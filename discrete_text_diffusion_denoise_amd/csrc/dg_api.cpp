@@ -417,6 +417,8 @@ template <typename T>
 dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
+    // canvas-sized batches: the router product runs inside the routing kernel
+    const bool fused_router = sizeof(T) == 2 && dg::router_fused_ok(Tn, c.d_model, c.n_experts);
     if (sizeof(T) == 2) {
         // The route is an integer decision taken from float logits: compute
         // them from the fp32 normalised activations (written by the same
@@ -424,8 +426,9 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
         // fp32 on load, so bf16 rounding of the activations cannot flip it.
         DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32, s.u8,
                               s.u8s));
-        DG_TRY(linear<float>(s.u32, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
-                             dg::EPI_STORE_F32, s, st, nullptr, nullptr, 0, 1));
+        if (!fused_router)
+            DG_TRY(linear<float>(s.u32, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
+                                 dg::EPI_STORE_F32, s, st, nullptr, nullptr, 0, 1));
     } else {
         DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
         DG_TRY(linear<T>(s.u, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
@@ -471,6 +474,10 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     a.h = h;
     a.k_rotate = 1;
     a.halt = s.halt;
+    if (fused_router) {
+        a.router_u = s.u32;
+        a.router_w = L.w_router;
+    }
     DG_HIP(dg::moe_route(a, st));
     DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
     DG_HIP(timed(DG_TIMER_MOE_DOWN, st, [&] { return dg::moe_down<T>(a, st); }));

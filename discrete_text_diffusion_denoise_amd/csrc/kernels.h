@@ -204,8 +204,18 @@ struct MoeArgs {
     // expert's first routed row, the item's first row within the expert, the
     // expert's row count), so a block finds its item with one load
     int32_t* items = nullptr;
+    // optional: router logits computed inside the routing (moe_route) from
+    // the fp32 normalised tokens router_u [T][d] and the bf16 router rows
+    // router_w [E][d], instead of reading z; used where router_fused_ok
+    const float* router_u = nullptr;
+    const void* router_w = nullptr;
 };
 constexpr int kMoeChunk = 64;
+// shapes the fused router + top-k kernel takes: few tokens (one workgroup
+// each), d of 512, 1024 or 2048, at most 256 experts
+inline bool router_fused_ok(int T, int d, int E) {
+    return T >= 1 && T <= 512 && (d == 512 || d == 1024 || d == 2048) && E >= 1 && E <= 256;
+}
 // compute units of the current device (cached per device)
 int cu_count();
 // routing, counts and the stable permutation

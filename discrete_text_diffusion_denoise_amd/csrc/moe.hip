@@ -22,12 +22,10 @@ __device__ __forceinline__ uint32_t orderable(float z) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave per token: k rounds of a wave-wide max over (logit, -index).
-__global__ __launch_bounds__(256) void route_kernel(MoeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.T) return;
-    const float* z = a.z + t * a.E;
+// Top-k of token t's E logits z (global or LDS) by one wave: k rounds of a
+// wave-wide max over (logit, -index); gates = softmax over the selected
+// logits in selection order.
+__device__ __forceinline__ void route_select(const MoeArgs& a, long t, const float* z, int lane) {
     uint64_t key[4];
     float zv[4];
 #pragma unroll
@@ -58,7 +56,6 @@ __global__ __launch_bounds__(256) void route_kernel(MoeArgs a) {
             mye = e;
         }
     }
-    // gates = softmax over the selected logits (selection order)
     const float z0 = __shfl(myz, 0, 64);
     const float ex = lane < a.k ? expf(myz - z0) : 0.f;
     const float s = wave_sum(ex);
@@ -66,6 +63,126 @@ __global__ __launch_bounds__(256) void route_kernel(MoeArgs a) {
         a.route[t * a.k + lane] = mye;
         a.gates[t * a.k + lane] = ex / s;
     }
+}
+
+// One wave per token, logits z [T][E] from the router product.
+__global__ __launch_bounds__(256) void route_kernel(MoeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    route_select(a, t, a.z + t * a.E, lane);
+}
+
+// Router logits and top-k of one token per workgroup, for canvas-sized
+// batches, where a split-K router product, its epilogue and route_kernel
+// are three launches of a few microseconds each.  z[e] = sum_k u[k] W[e][k]
+// in fp32 (u the fp32 normalised token, W the bf16 router rows widened on
+// load): lane l owns the 8-wide pieces k = 512 c + 8 l (c < NCH = d / 512)
+// and keeps the token's pieces in registers.  Wave w of 8 takes the groups
+// of 4 experts w, w + 8, ... (in a rotated order), each group's weights loaded
+// while the previous group is multiplied; a fixed butterfly sums each
+// expert's 64 lane partials, so the order of the groups changes no bit.  Every workgroup reads all E x d router weights, which stay in
+// L2.
+template <int NCH>
+struct RouterGroup {
+    uint4 w[4][NCH];
+};
+
+template <int NCH>
+__device__ __forceinline__ void router_load(RouterGroup<NCH>& g, const uint16_t* wr, int grp, int E,
+                                            int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = min(4 * grp + i, E - 1);   // rows past E repeat the last (unused)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            g.w[i][c] = *reinterpret_cast<const uint4*>(wr + (long)e * (NCH * 512) + 512 * c + 8 * lane);
+    }
+}
+
+// the group's four logits: lane l's partials, then lanes l ^ 32 and l ^ 16
+// swap halves so that lane l keeps expert 2 (l / 32) + (l / 16) mod 2, then
+// sums over l ^ 8, ^ 4, ^ 2, ^ 1; lanes 0, 16, 32, 48 write experts 0..3
+template <int NCH>
+__device__ __forceinline__ void router_group(const RouterGroup<NCH>& g, const float (&u)[NCH][8],
+                                             int grp, int E, int lane, float* zs) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint32_t q[4] = {g.w[i][c].x, g.w[i][c].y, g.w[i][c].z, g.w[i][c].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = __builtin_fmaf(u[c][2 * j], __uint_as_float(q[j] << 16), acc);
+                acc = __builtin_fmaf(u[c][2 * j + 1], __uint_as_float(q[j] & 0xFFFF0000u), acc);
+            }
+        }
+        p[i] = acc;
+    }
+    const bool hi32 = lane & 32, hi16 = lane & 16;
+    // lanes below 32 keep experts 0, 1 and send 2, 3; the others the reverse
+    const float s0 = hi32 ? p[0] : p[2], s1 = hi32 ? p[1] : p[3];
+    const float r0 = __shfl_xor(s0, 32, 64), r1 = __shfl_xor(s1, 32, 64);
+    const float k0 = (hi32 ? p[2] : p[0]) + r0, k1 = (hi32 ? p[3] : p[1]) + r1;
+    const float s = hi16 ? k0 : k1;
+    const float r = __shfl_xor(s, 16, 64);
+    float v = (hi16 ? k1 : k0) + r;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = v + __shfl_xor(v, o, 64);
+    const int e = 4 * grp + 2 * (hi32 ? 1 : 0) + (hi16 ? 1 : 0);
+    if ((lane & 15) == 0 && e < E) zs[e] = v;
+}
+
+constexpr int kRouterWaves = 8;
+
+template <int NCH>
+__global__ __launch_bounds__(64 * kRouterWaves) void router_route_kernel(MoeArgs a) {
+    __shared__ float zs[256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long t = blockIdx.x;
+    const float* ur = a.router_u + t * (NCH * 512);
+    const uint16_t* wr = static_cast<const uint16_t*>(a.router_w);
+    float u[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const float4 x0 = *reinterpret_cast<const float4*>(ur + 512 * c + 8 * lane);
+        const float4 x1 = *reinterpret_cast<const float4*>(ur + 512 * c + 8 * lane + 4);
+        u[c][0] = x0.x;
+        u[c][1] = x0.y;
+        u[c][2] = x0.z;
+        u[c][3] = x0.w;
+        u[c][4] = x1.x;
+        u[c][5] = x1.y;
+        u[c][6] = x1.z;
+        u[c][7] = x1.w;
+    }
+    // wave w owns groups w + W j (j < nj, W waves); workgroup t starts at
+    // j = t mod nj, so that the workgroups of an XCD, which run side by side,
+    // read different weight rows at a time rather than the same lines in
+    // lockstep
+    constexpr int W = kRouterWaves;
+    const int ngroups = cdiv(a.E, 4);
+    const int nj = wave < ngroups ? cdiv(ngroups - wave, W) : 0;
+    const int rot = nj ? (int)(t % nj) : 0;
+    auto grp = [&](int jj) { return wave + W * ((jj + rot) % nj); };
+    RouterGroup<NCH> ga, gb;
+    int jj = 0;
+    if (jj < nj) router_load(ga, wr, grp(jj), a.E, lane);
+    // two groups a trip: the next group's loads go out before this one's
+    // products
+    while (jj < nj) {
+        if (jj + 1 < nj) router_load(gb, wr, grp(jj + 1), a.E, lane);
+        router_group(ga, u, grp(jj), a.E, lane, zs);
+        ++jj;
+        if (jj >= nj) break;
+        if (jj + 1 < nj) router_load(ga, wr, grp(jj + 1), a.E, lane);
+        router_group(gb, u, grp(jj), a.E, lane, zs);
+        ++jj;
+    }
+    __syncthreads();
+    if (wave == 0) route_select(a, t, zs, lane);
 }
 
 // counts[e] = number of (token, slot) pairs routed to e.
@@ -802,7 +919,17 @@ __global__ __launch_bounds__(256) void combine_k_kernel(MoeArgs a) {
 
 hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(route_kernel, dim3(cdiv(a.T, 4)), dim3(256), 0, st, a);
+    if (a.router_w) {
+        if (!a.router_u || !router_fused_ok(a.T, a.d, a.E)) return hipErrorInvalidValue;
+        switch (a.d / 512) {
+            case 1: hipLaunchKernelGGL(router_route_kernel<1>, dim3(a.T), dim3(64 * kRouterWaves), 0, st, a); break;
+            case 2: hipLaunchKernelGGL(router_route_kernel<2>, dim3(a.T), dim3(64 * kRouterWaves), 0, st, a); break;
+            case 4: hipLaunchKernelGGL(router_route_kernel<4>, dim3(a.T), dim3(64 * kRouterWaves), 0, st, a); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        hipLaunchKernelGGL(route_kernel, dim3(cdiv(a.T, 4)), dim3(256), 0, st, a);
+    }
     if ((long)a.T * a.k <= 8192) {
         // few assignments (a canvas): one workgroup places them all
         hipLaunchKernelGGL(place_all_kernel, dim3(1), dim3(64 * PW), 0, st, a);
