@@ -113,3 +113,64 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Sum of a split-K product's partials for one output, in split order:
+// pp points at the element in split 0, splits are zs floats apart; eight
+// loads go out before their adds.  Every epilogue that reduces partials
+// uses it, so they give the same bits.
+__device__ __forceinline__ float splitk_sum(const float* pp, long zs, int splits) {
+    float v = 0.f;
+    int z = 0;
+    for (; z + 8 <= splits; z += 8) {
+        float p[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) p[q] = pp[(z + q) * zs];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v += p[q];
+    }
+    for (; z < splits; ++z) v += pp[z * zs];
+    return v;
+}
+
+// RMSNorm arithmetic shared by every kernel that normalises rows of d fp32
+// values with 256 threads (thread t takes the float4 at 4t + 1024 i), so that
+// they give the same bits: the sum of squares in fixed fma order, the block
+// total over the four waves in wave order, the scale and the scaled value.
+__device__ __forceinline__ float rms_accum(float ss, float4 v) {
+    ss = __builtin_fmaf(v.x, v.x, ss);
+    ss = __builtin_fmaf(v.y, v.y, ss);
+    ss = __builtin_fmaf(v.z, v.z, ss);
+    return __builtin_fmaf(v.w, v.w, ss);
+}
+// the row's scale 1 / sqrt(mean square + eps); part: 4 floats of LDS
+__device__ __forceinline__ float rms_block_scale(float ss, float* part, int d, float eps) {
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    return 1.0f / sqrtf(tot / (float)d + eps);
+}
+__device__ __forceinline__ float4 rms_apply(float4 v, float scale, const float* w, int i) {
+    const float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+    return make_float4(v.x * scale * s.x, v.y * scale * s.y, v.z * scale * s.z, v.w * scale * s.w);
+}
+
+// RoPE rotation of pair j (of dh / 2) at position pos: angle pos * theta^(-2j/dh)
+// in double, cos and sin rounded to float, then (x1, x2) -> (x1 c - x2 s, x2 c + x1 s)
+__device__ __forceinline__ void rope_cs(long pos, int j, int dh, int rope_on, double log_theta,
+                                        float& c, float& s) {
+    c = 1.f;
+    s = 0.f;
+    if (rope_on) {
+        const double inv_freq = exp(-2.0 * (double)j / (double)dh * log_theta);
+        const double ang = (double)pos * inv_freq;
+        c = (float)cos(ang);
+        s = (float)sin(ang);
+    }
+}
+__device__ __forceinline__ float rope_first(float x1, float x2, float c, float s) {
+    return x1 * c - x2 * s;
+}
+__device__ __forceinline__ float rope_second(float x1, float x2, float c, float s) {
+    return x2 * c + x1 * s;
+}

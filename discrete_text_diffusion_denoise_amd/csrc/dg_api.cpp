@@ -291,6 +291,16 @@ dg_status gemm(const dg::GemmArgs& g, int amode, int epi, int splits, hipStream_
     return DG_OK;
 }
 
+// Optional epilogue of the stacked Q/K/V product: RoPE and the KV-cache write
+// straight from the split-K partials, taken when the product runs split over
+// K on the skinny kernel (`done` tells the caller; otherwise C holds q|k|v).
+struct RopeEpi {
+    void *q, *kc, *vc;
+    int B, n, pos0, cap, Hq, Hkv, dh, rope_on;
+    float theta;
+    bool done;
+};
+
 // C (epi)= x W^T for x [M][K] (model dtype, or fp32 when T = float) and
 // W [N][K]: C fp32 [M][ldc].  bf16 uses the streaming GEMM, fp32 the LDS-tiled
 // one.  When the output has too few tiles to fill the chip, K is split and a
@@ -299,7 +309,8 @@ template <typename T>
 dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, long ldc, int epi,
                  Scratch& s, hipStream_t st, const void* E = nullptr,
                  const int32_t* tokens = nullptr, int vocab = 0, int b_bf16 = 0,
-                 const void* B2 = nullptr, int n_b2 = 0, const void* B3 = nullptr, int n_b3 = 0) {
+                 const void* B2 = nullptr, int n_b2 = 0, const void* B3 = nullptr, int n_b3 = 0,
+                 RopeEpi* rope = nullptr) {
     dg::GemmArgs g;
     g.M = M;
     g.N = N;
@@ -346,7 +357,14 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
         p.ldc = N;
         if ((size_t)used * M * N <= kSplitPartFloats && dg::gemm_skinny_ok(p)) {
             DG_HIP(dg::gemm_skinny_splitk(p, used, st));
-            DG_HIP(dg::splitk_epilogue(g, s.gp, used, epi, st));
+            if (rope) {
+                DG_HIP(dg::splitk_rope_kv<T>(s.gp, used, (T*)rope->q, (T*)rope->kc, (T*)rope->vc,
+                                             rope->B, rope->n, rope->pos0, rope->cap, rope->Hq,
+                                             rope->Hkv, rope->dh, rope->rope_on, rope->theta, st));
+                rope->done = true;
+            } else {
+                DG_HIP(dg::splitk_epilogue(g, s.gp, used, epi, st));
+            }
             return DG_OK;
         }
     }
@@ -369,23 +387,34 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
     return DG_OK;
 }
 
+// attention RMSNorm weight of the layer after l (nullptr after the last)
+static const float* next_attn_norm(const dg_model* m, int l) {
+    return l + 1 < m->c.n_layers ? m->layers[l + 1].attn_norm : nullptr;
+}
+
 // ---- attention half-block: n new tokens per sequence at [pos0, pos0+n)
 template <typename T>
 dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, int causal,
-                    float* h, Scratch& s, hipStream_t st) {
+                    float* h, Scratch& s, hipStream_t st, bool normed = false) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
     const int Tn = B * n;
     const int d = c.d_model, dh = c.head_dim;
     const int qkvw = (c.n_heads + 2 * c.n_kv_heads) * dh;
-    DG_HIP(dg::rmsnorm<T>(h, L.attn_norm, (T*)s.u, Tn, d, c.rms_eps, st));
-    // q, k and v in one product: the columns of W_k and W_v follow those of W_q
-    DG_TRY(linear<T>(s.u, Tn, d, L.wq, qkvw, s.qkv, qkvw, dg::EPI_STORE_F32, s, st, nullptr,
-                     nullptr, 0, 0, L.wk, c.n_heads * dh, L.wv, (c.n_heads + c.n_kv_heads) * dh));
+    // (normed: the previous MoE half's combine has already written s.u)
+    if (!normed) DG_HIP(dg::rmsnorm<T>(h, L.attn_norm, (T*)s.u, Tn, d, c.rms_eps, st));
     void *kc, *vc;
     kv_layer(m, kv, layer, &kc, &vc);
-    DG_HIP(dg::rope_kv<T>(s.qkv, (T*)s.q, (T*)kc, (T*)vc, B, n, pos0, kv->cap, c.n_heads,
-                          c.n_kv_heads, dh, c.rope_on, c.rope_theta, st));
+    // q, k and v in one product: the columns of W_k and W_v follow those of W_q;
+    // RoPE and the cache write run in its split-K epilogue when it has one
+    RopeEpi re{s.q, kc, vc, B, n, pos0, kv->cap, c.n_heads, c.n_kv_heads, dh, c.rope_on,
+               c.rope_theta, false};
+    DG_TRY(linear<T>(s.u, Tn, d, L.wq, qkvw, s.qkv, qkvw, dg::EPI_STORE_F32, s, st, nullptr,
+                     nullptr, 0, 0, L.wk, c.n_heads * dh, L.wv, (c.n_heads + c.n_kv_heads) * dh,
+                     &re));
+    if (!re.done)
+        DG_HIP(dg::rope_kv<T>(s.qkv, (T*)s.q, (T*)kc, (T*)vc, B, n, pos0, kv->cap, c.n_heads,
+                              c.n_kv_heads, dh, c.rope_on, c.rope_theta, st));
     dg::AttnArgs a;
     a.q = s.q;
     a.kc = kc;
@@ -413,8 +442,11 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     return DG_OK;
 }
 
+// next_norm: the next layer's attention RMSNorm weight, to fuse that norm into
+// the combine (then *normed is set and s.u holds its output)
 template <typename T>
-dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st) {
+dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st,
+                   const float* next_norm = nullptr, bool* normed = nullptr) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
     // canvas-sized batches: the router product runs inside the routing kernel
@@ -481,7 +513,13 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
     DG_HIP(dg::moe_route(a, st));
     DG_HIP(timed(DG_TIMER_MOE_GATEUP, st, [&] { return dg::moe_gateup<T>(a, st); }));
     DG_HIP(timed(DG_TIMER_MOE_DOWN, st, [&] { return dg::moe_down<T>(a, st); }));
-    DG_HIP(dg::moe_combine(a, st));
+    if (normed) *normed = false;
+    if (next_norm && dg::moe_combine_norm_ok(c.top_k)) {
+        DG_HIP(dg::moe_combine_norm<T>(a, next_norm, (T*)s.u, c.rms_eps, st));
+        if (normed) *normed = true;
+    } else {
+        DG_HIP(dg::moe_combine(a, st));
+    }
     return DG_OK;
 }
 
@@ -608,9 +646,10 @@ dg_status denoise(dg_model* m, dg_kv* kv, int B, const int32_t* canvas, const fl
     const dg_config& c = m->c;
     const int Tn = B * c.canvas;
     DG_TRY(stage_input<T>(m, B, canvas, prev, prev_stats, s.h, s, st));
+    bool normed = false;
     for (int l = 0; l < c.n_layers; ++l) {
-        DG_TRY(attn_half<T>(m, kv, l, B, c.canvas, kv->len, 0, s.h, s, st));
-        DG_TRY(moe_half<T>(m, l, Tn, s.h, s, st));
+        DG_TRY(attn_half<T>(m, kv, l, B, c.canvas, kv->len, 0, s.h, s, st, normed));
+        DG_TRY(moe_half<T>(m, l, Tn, s.h, s, st, next_attn_norm(m, l), &normed));
     }
     return stage_head<T>(m, Tn, s.h, logits, s, st);
 }
@@ -624,9 +663,11 @@ dg_status encode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int P, Sc
         const int n = std::min(chunk, P - c0);
         const int pos0 = kv->len + c0;
         DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens + c0, P, n, B, s.h, c.d_model, st));
+        bool normed = false;
         for (int l = 0; l < c.n_layers; ++l) {
-            DG_TRY(attn_half<T>(m, kv, l, B, n, pos0, 1, s.h, s, st));
-            if (l + 1 < c.n_layers) DG_TRY(moe_half<T>(m, l, B * n, s.h, s, st));
+            DG_TRY(attn_half<T>(m, kv, l, B, n, pos0, 1, s.h, s, st, normed));
+            if (l + 1 < c.n_layers)
+                DG_TRY(moe_half<T>(m, l, B * n, s.h, s, st, next_attn_norm(m, l), &normed));
         }
     }
     kv->len += P;
@@ -642,9 +683,10 @@ dg_status ar_decode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int ld
     const dg_config& c = m->c;
     const int pos0 = kv->len;
     DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens, ld, 1, B, s.h, c.d_model, st));
+    bool normed = false;
     for (int l = 0; l < c.n_layers; ++l) {
-        DG_TRY(attn_half<T>(m, kv, l, B, 1, pos0, 1, s.h, s, st));
-        DG_TRY(moe_half<T>(m, l, B, s.h, s, st));
+        DG_TRY(attn_half<T>(m, kv, l, B, 1, pos0, 1, s.h, s, st, normed));
+        DG_TRY(moe_half<T>(m, l, B, s.h, s, st, next_attn_norm(m, l), &normed));
     }
     kv->len += 1;
     return stage_head<T>(m, B, s.h, logits, s, st);

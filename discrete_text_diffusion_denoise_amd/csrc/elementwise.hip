@@ -22,22 +22,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     const long row = blockIdx.x;
     const float* x = h + row * d;
     float ss = 0.f;
-    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-        float4 v = *reinterpret_cast<const float4*>(x + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = wave_sum(ss);
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4)
+        ss = rms_accum(ss, *reinterpret_cast<const float4*>(x + i));
     __shared__ float part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = part[0] + part[1] + part[2] + part[3];
-    const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+    const float scale = rms_block_scale(ss, part, d, eps);
     T* o = u + row * d;
     for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-        float4 v = *reinterpret_cast<const float4*>(x + i);
-        float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
-        const float4 r = make_float4(v.x * scale * s.x, v.y * scale * s.y, v.z * scale * s.z,
-                                     v.w * scale * s.w);
+        const float4 r = rms_apply(*reinterpret_cast<const float4*>(x + i), scale, w, i);
         o[i + 0] = Elt<T>::from_f(r.x);
         o[i + 1] = Elt<T>::from_f(r.y);
         o[i + 2] = Elt<T>::from_f(r.z);
@@ -159,22 +150,14 @@ __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float* __restr
     const long row = blockIdx.x;
     const float* x = h + row * d;
     float ss = 0.f;
-    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-        float4 v = *reinterpret_cast<const float4*>(x + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = wave_sum(ss);
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4)
+        ss = rms_accum(ss, *reinterpret_cast<const float4*>(x + i));
     __shared__ float part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = part[0] + part[1] + part[2] + part[3];
-    const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+    const float scale = rms_block_scale(ss, part, d, eps);
     for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-        float4 v = *reinterpret_cast<const float4*>(x + i);
-        float4 s = w ? *reinterpret_cast<const float4*>(w + i) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float4 r = rms_apply(*reinterpret_cast<const float4*>(x + i), scale, w, i);
         *reinterpret_cast<uint2*>(u + tiled_index(row, i, d)) =
-            make_uint2(pack_bf2(v.x * scale * s.x, v.y * scale * s.y),
-                       pack_bf2(v.z * scale * s.z, v.w * scale * s.w));
+            make_uint2(pack_bf2(r.x, r.y), pack_bf2(r.z, r.w));
     }
 }
 
@@ -258,30 +241,75 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     const long t = r / (Hq + Hkv);      // token index b*n + i
     const int b = (int)(t / n), i = (int)(t % n);
     const long pos = pos0 + i;
-    float c = 1.f, s = 0.f;
-    if (rope_on) {
-        double inv_freq = exp(-2.0 * (double)j / (double)dh * log_theta);
-        double ang = (double)pos * inv_freq;
-        c = (float)cos(ang);
-        s = (float)sin(ang);
-    }
+    float c, s;
+    rope_cs(pos, j, dh, rope_on, log_theta, c, s);
     const int width = (Hq + 2 * Hkv) * dh;
     const float* row = qkv + t * width;
     if (hh < Hq) {
         const float x1 = row[hh * dh + j], x2 = row[hh * dh + j + half];
         T* o = q_out + t * (long)Hq * dh + (long)hh * dh;
-        o[j] = Elt<T>::from_f(x1 * c - x2 * s);
-        o[j + half] = Elt<T>::from_f(x2 * c + x1 * s);
+        o[j] = Elt<T>::from_f(rope_first(x1, x2, c, s));
+        o[j + half] = Elt<T>::from_f(rope_second(x1, x2, c, s));
     } else {
         const int h = hh - Hq;
         const float* kr = row + (Hq + h) * dh;
         const float* vr = row + (Hq + Hkv + h) * dh;
         const long slot = (((long)b * Hkv + h) * cap + pos) * dh;
         const float x1 = kr[j], x2 = kr[j + half];
-        kc[slot + j] = Elt<T>::from_f(x1 * c - x2 * s);
-        kc[slot + j + half] = Elt<T>::from_f(x2 * c + x1 * s);
+        kc[slot + j] = Elt<T>::from_f(rope_first(x1, x2, c, s));
+        kc[slot + j + half] = Elt<T>::from_f(rope_second(x1, x2, c, s));
         vc[slot + j] = Elt<T>::from_f(vr[j]);
         vc[slot + j + half] = Elt<T>::from_f(vr[j + half]);
+    }
+}
+
+// The same with the stacked Q/K/V product still in split-K partials
+// part [splits][rows][width]: each value is first summed over the splits
+// exactly as the generic split-K epilogue sums it, so the result equals
+// that epilogue followed by rope_kv_kernel, without the fp32 round trip
+// and the extra launch.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_rope_kv_kernel(const float* __restrict__ part,
+                                                             int splits, long rows,
+                                                             T* __restrict__ q_out,
+                                                             T* __restrict__ kc,
+                                                             T* __restrict__ vc, int n, int pos0,
+                                                             int cap, int Hq, int Hkv, int dh,
+                                                             int rope_on, double log_theta,
+                                                             long total) {
+    long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int half = dh / 2;
+    const int j = (int)(idx % half);
+    const long r = idx / half;
+    const int hh = (int)(r % (Hq + Hkv));
+    const long t = r / (Hq + Hkv);
+    const int b = (int)(t / n), i = (int)(t % n);
+    const long pos = pos0 + i;
+    float c, s;
+    rope_cs(pos, j, dh, rope_on, log_theta, c, s);
+    const int width = (Hq + 2 * Hkv) * dh;
+    const long zs = rows * width;
+    const float* row = part + t * width;
+    if (hh < Hq) {
+        const float x1 = splitk_sum(row + hh * dh + j, zs, splits);
+        const float x2 = splitk_sum(row + hh * dh + j + half, zs, splits);
+        T* o = q_out + t * (long)Hq * dh + (long)hh * dh;
+        o[j] = Elt<T>::from_f(rope_first(x1, x2, c, s));
+        o[j + half] = Elt<T>::from_f(rope_second(x1, x2, c, s));
+    } else {
+        const int h = hh - Hq;
+        const float* kr = row + (Hq + h) * dh;
+        const float* vr = row + (Hq + Hkv + h) * dh;
+        const long slot = (((long)b * Hkv + h) * cap + pos) * dh;
+        const float x1 = splitk_sum(kr + j, zs, splits);
+        const float x2 = splitk_sum(kr + j + half, zs, splits);
+        const float v1 = splitk_sum(vr + j, zs, splits);
+        const float v2 = splitk_sum(vr + j + half, zs, splits);
+        kc[slot + j] = Elt<T>::from_f(rope_first(x1, x2, c, s));
+        kc[slot + j + half] = Elt<T>::from_f(rope_second(x1, x2, c, s));
+        vc[slot + j] = Elt<T>::from_f(v1);
+        vc[slot + j + half] = Elt<T>::from_f(v2);
     }
 }
 
@@ -379,6 +407,18 @@ hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int p
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t splitk_rope_kv(const float* part, int splits, T* q_out, T* kc, T* vc, int B, int n,
+                          int pos0, int cap, int Hq, int Hkv, int dh, int rope_on, float theta,
+                          hipStream_t st) {
+    long total = (long)B * n * (Hq + Hkv) * (dh / 2);
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(splitk_rope_kv_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, st, part, splits, (long)B * n, q_out, kc, vc, n, pos0, cap, Hq, Hkv, dh,
+                       rope_on, log((double)theta), total);
+    return hipGetLastError();
+}
+
 #define DG_INST(T)                                                                        \
     template hipError_t rmsnorm<T>(const float*, const float*, T*, int, int, float,        \
                                    hipStream_t, float*, uint8_t*, uint8_t*);               \
@@ -388,7 +428,9 @@ hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int p
                                          const float*);                                    \
     template hipError_t transpose<T>(const T*, T*, int, int, hipStream_t);                 \
     template hipError_t rope_kv<T>(const float*, T*, T*, T*, int, int, int, int, int, int, \
-                                   int, int, float, hipStream_t);
+                                   int, int, float, hipStream_t);                          \
+    template hipError_t splitk_rope_kv<T>(const float*, int, T*, T*, T*, int, int, int, int, \
+                                          int, int, int, int, float, hipStream_t);
 DG_INST(bf16_t)
 DG_INST(float)
 #undef DG_INST

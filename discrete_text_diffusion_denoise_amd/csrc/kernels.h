@@ -131,6 +131,12 @@ hipError_t transpose(const T* in, T* out, int rows, int cols, hipStream_t st);
 template <typename T>
 hipError_t rope_kv(const float* qkv, T* q_out, T* kc, T* vc, int B, int n, int pos0, int cap,
                    int Hq, int Hkv, int dh, int rope_on, float theta, hipStream_t st);
+// rope_kv from the stacked Q/K/V product's split-K partials [splits][B*n][width]
+// (summed as splitk_epilogue sums them)
+template <typename T>
+hipError_t splitk_rope_kv(const float* part, int splits, T* q_out, T* kc, T* vc, int B, int n,
+                          int pos0, int cap, int Hq, int Hkv, int dh, int rope_on, float theta,
+                          hipStream_t st);
 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
@@ -225,6 +231,11 @@ hipError_t moe_gateup(const MoeArgs& a, hipStream_t st);
 template <typename T>
 hipError_t moe_down(const MoeArgs& a, hipStream_t st);
 hipError_t moe_combine(const MoeArgs& a, hipStream_t st);
+// moe_combine that also writes u = RMSNorm(new h rows, weight nw) (T), with
+// the bits of moe_combine followed by rmsnorm; for k in {2, 4, 8}
+bool moe_combine_norm_ok(int k);
+template <typename T>
+hipError_t moe_combine_norm(const MoeArgs& a, const float* nw, T* u, float eps, hipStream_t st);
 // the bf16 ring kernels' shape limits (d and F multiples of 256)
 bool expert_dma_ok(const MoeArgs& a);
 // quantised experts (f4 or f8) on the block-scaled MFMA: d and F multiples of

@@ -915,7 +915,73 @@ __global__ __launch_bounds__(256) void combine_k_kernel(MoeArgs a) {
     }
 }
 
+// The combine, with the next layer's attention RMSNorm of the new rows
+// fused: one workgroup a token takes the whole row (thread t the float4 at
+// 4t + 1024 i, the layout of rmsnorm_kernel), adds the K expert rows in the
+// order combine_k_kernel adds them, writes h and normalises it with the
+// shared RMSNorm arithmetic, so both h and u have the bits of the two
+// separate kernels.
+template <int K, typename T>
+__global__ __launch_bounds__(256) void combine_norm_k_kernel(MoeArgs a, const float* __restrict__ nw,
+                                                             T* __restrict__ u, float eps) {
+    const long t = blockIdx.x;
+    float gt[K];
+    long yo[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        gt[j] = a.gates[t * K + j];
+        yo[j] = (long)a.slot_of[t * K + j] * a.d;
+    }
+    float* hr = a.h + t * a.d;
+    float ss = 0.f;
+    for (int c = threadIdx.x * 4; c < a.d; c += 1024) {
+        float4 y[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) y[j] = *reinterpret_cast<const float4*>(a.y + yo[j] + c);
+        float4 acc = *reinterpret_cast<const float4*>(hr + c);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            acc.x += gt[j] * y[j].x;
+            acc.y += gt[j] * y[j].y;
+            acc.z += gt[j] * y[j].z;
+            acc.w += gt[j] * y[j].w;
+        }
+        *reinterpret_cast<float4*>(hr + c) = acc;
+        ss = rms_accum(ss, acc);
+    }
+    __shared__ float part[4];
+    const float scale = rms_block_scale(ss, part, a.d, eps);
+    T* o = u + t * a.d;
+    for (int c = threadIdx.x * 4; c < a.d; c += 1024) {
+        const float4 r = rms_apply(*reinterpret_cast<const float4*>(hr + c), scale, nw, c);
+        o[c + 0] = Elt<T>::from_f(r.x);
+        o[c + 1] = Elt<T>::from_f(r.y);
+        o[c + 2] = Elt<T>::from_f(r.z);
+        o[c + 3] = Elt<T>::from_f(r.w);
+    }
+}
+
 }  // namespace
+
+bool moe_combine_norm_ok(int k) { return k == 2 || k == 4 || k == 8; }
+
+template <typename T>
+hipError_t moe_combine_norm(const MoeArgs& a, const float* nw, T* u, float eps, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
+    if (a.d % 4) return hipErrorInvalidValue;
+    const dim3 grid(a.T);
+    if (a.k == 8)
+        hipLaunchKernelGGL((combine_norm_k_kernel<8, T>), grid, dim3(256), 0, st, a, nw, u, eps);
+    else if (a.k == 4)
+        hipLaunchKernelGGL((combine_norm_k_kernel<4, T>), grid, dim3(256), 0, st, a, nw, u, eps);
+    else if (a.k == 2)
+        hipLaunchKernelGGL((combine_norm_k_kernel<2, T>), grid, dim3(256), 0, st, a, nw, u, eps);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+template hipError_t moe_combine_norm<bf16_t>(const MoeArgs&, const float*, bf16_t*, float, hipStream_t);
+template hipError_t moe_combine_norm<float>(const MoeArgs&, const float*, float*, float, hipStream_t);
 
 hipError_t moe_route(const MoeArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
