@@ -115,20 +115,20 @@ __device__ __forceinline__ float wave_max(float v) {
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Sum of a split-K product's partials for one output, in split order:
-// pp points at the element in split 0, splits are zs floats apart; eight
-// loads go out before their adds.  Every epilogue that reduces partials
-// uses it, so they give the same bits.
+// pp points at the element in split 0, splits are zs floats apart; up to
+// eight loads go out before their adds (a short last group is predicated,
+// not a loop of dependent loads).  Every epilogue that reduces partials uses
+// it, so they give the same bits.
 __device__ __forceinline__ float splitk_sum(const float* pp, long zs, int splits) {
     float v = 0.f;
-    int z = 0;
-    for (; z + 8 <= splits; z += 8) {
+    for (int z = 0; z < splits; z += 8) {
         float p[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) p[q] = pp[(z + q) * zs];
+        for (int q = 0; q < 8; ++q) p[q] = z + q < splits ? pp[(z + q) * zs] : 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v += p[q];
+        for (int q = 0; q < 8; ++q)
+            if (z + q < splits) v += p[q];
     }
-    for (; z < splits; ++z) v += pp[z * zs];
     return v;
 }
 
