@@ -132,6 +132,28 @@ __device__ __forceinline__ float splitk_sum(const float* pp, long zs, int splits
     return v;
 }
 
+// splitk_sum of four adjacent outputs (pp 16-byte aligned, zs a multiple of
+// 4): each component summed in the same order as splitk_sum sums it
+__device__ __forceinline__ float4 splitk_sum4(const float* pp, long zs, int splits) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < splits; z += 8) {
+        float4 p[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            p[q] = z + q < splits ? *reinterpret_cast<const float4*>(pp + (z + q) * zs)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (z + q < splits) {
+                v.x += p[q].x;
+                v.y += p[q].y;
+                v.z += p[q].z;
+                v.w += p[q].w;
+            }
+    }
+    return v;
+}
+
 // RMSNorm arithmetic shared by every kernel that normalises rows of d fp32
 // values with 256 threads (thread t takes the float4 at 4t + 1024 i), so that
 // they give the same bits: the sum of squares in fixed fma order, the block

@@ -301,6 +301,18 @@ struct RopeEpi {
     bool done;
 };
 
+// Optional epilogue of the O projection: the residual add and the MoE half's
+// RMSNorm of the new rows in one pass over the split-K partials (same
+// outputs as rmsnorm), taken like RopeEpi.
+struct AddNormEpi {
+    const float* w;
+    void* u;
+    float* u32;
+    uint8_t *q8, *q8s;
+    float eps;
+    bool done;
+};
+
 // C (epi)= x W^T for x [M][K] (model dtype, or fp32 when T = float) and
 // W [N][K]: C fp32 [M][ldc].  bf16 uses the streaming GEMM, fp32 the LDS-tiled
 // one.  When the output has too few tiles to fill the chip, K is split and a
@@ -310,7 +322,7 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
                  Scratch& s, hipStream_t st, const void* E = nullptr,
                  const int32_t* tokens = nullptr, int vocab = 0, int b_bf16 = 0,
                  const void* B2 = nullptr, int n_b2 = 0, const void* B3 = nullptr, int n_b3 = 0,
-                 RopeEpi* rope = nullptr) {
+                 RopeEpi* rope = nullptr, AddNormEpi* addnorm = nullptr) {
     dg::GemmArgs g;
     g.M = M;
     g.N = N;
@@ -362,6 +374,11 @@ dg_status linear(const void* x, int M, int K, const void* W, int N, float* C, lo
                                              rope->B, rope->n, rope->pos0, rope->cap, rope->Hq,
                                              rope->Hkv, rope->dh, rope->rope_on, rope->theta, st));
                 rope->done = true;
+            } else if (addnorm && epi == dg::EPI_ADD_F32 && ldc == N) {
+                DG_HIP(dg::splitk_add_norm<T>(s.gp, used, C, M, N, addnorm->w, (T*)addnorm->u,
+                                              addnorm->eps, st, addnorm->u32, addnorm->q8,
+                                              addnorm->q8s));
+                addnorm->done = true;
             } else {
                 DG_HIP(dg::splitk_epilogue(g, s.gp, used, epi, st));
             }
@@ -395,7 +412,8 @@ static const float* next_attn_norm(const dg_model* m, int l) {
 // ---- attention half-block: n new tokens per sequence at [pos0, pos0+n)
 template <typename T>
 dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, int causal,
-                    float* h, Scratch& s, hipStream_t st, bool normed = false) {
+                    float* h, Scratch& s, hipStream_t st, bool normed = false,
+                    AddNormEpi* moe_norm = nullptr) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
     const int Tn = B * n;
@@ -438,15 +456,26 @@ dg_status attn_half(dg_model* m, dg_kv* kv, int layer, int B, int n, int pos0, i
     a.splits = dg::attention_splits(B, n, c.n_heads, c.n_kv_heads, a.kv_len, causal, max_splits,
                                     &a.split_len, dh, sizeof(T) == 2);
     DG_HIP(timed(DG_TIMER_ATTENTION, st, [&] { return dg::attention<T>(a, st); }));
-    DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, s, st));
+    // (moe_norm: the MoE half's RMSNorm runs in this product's epilogue when it can)
+    DG_TRY(linear<T>(s.ao, Tn, c.n_heads * dh, L.wo, d, h, d, dg::EPI_ADD_F32, s, st, nullptr,
+                     nullptr, 0, 0, nullptr, 0, nullptr, 0, nullptr, moe_norm));
     return DG_OK;
+}
+
+// the MoE half's RMSNorm outputs, as moe_half's own rmsnorm call writes them
+template <typename T>
+AddNormEpi moe_norm_epi(const dg_model* m, int layer, const Scratch& s) {
+    const bool b = sizeof(T) == 2;
+    return AddNormEpi{m->layers[layer].moe_norm, s.u, b ? s.u32 : nullptr, b ? s.u8 : nullptr,
+                      b ? s.u8s : nullptr, m->c.rms_eps, false};
 }
 
 // next_norm: the next layer's attention RMSNorm weight, to fuse that norm into
 // the combine (then *normed is set and s.u holds its output)
 template <typename T>
 dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStream_t st,
-                   const float* next_norm = nullptr, bool* normed = nullptr) {
+                   const float* next_norm = nullptr, bool* normed = nullptr,
+                   bool moe_normed = false) {
     const dg_config& c = m->c;
     const dg_layer_weights& L = m->layers[layer];
     // canvas-sized batches: the router product runs inside the routing kernel
@@ -456,13 +485,14 @@ dg_status moe_half(dg_model* m, int layer, int Tn, float* h, Scratch& s, hipStre
         // them from the fp32 normalised activations (written by the same
         // kernel as the bf16 ones) and the bf16 router weights widened to
         // fp32 on load, so bf16 rounding of the activations cannot flip it.
-        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32, s.u8,
-                              s.u8s));
+        if (!moe_normed)
+            DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st, s.u32,
+                                  s.u8, s.u8s));
         if (!fused_router)
             DG_TRY(linear<float>(s.u32, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
                                  dg::EPI_STORE_F32, s, st, nullptr, nullptr, 0, 1));
     } else {
-        DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
+        if (!moe_normed) DG_HIP(dg::rmsnorm<T>(h, L.moe_norm, (T*)s.u, Tn, c.d_model, c.rms_eps, st));
         DG_TRY(linear<T>(s.u, Tn, c.d_model, L.w_router, c.n_experts, s.z, c.n_experts,
                          dg::EPI_STORE_F32, s, st));
     }
@@ -648,8 +678,9 @@ dg_status denoise(dg_model* m, dg_kv* kv, int B, const int32_t* canvas, const fl
     DG_TRY(stage_input<T>(m, B, canvas, prev, prev_stats, s.h, s, st));
     bool normed = false;
     for (int l = 0; l < c.n_layers; ++l) {
-        DG_TRY(attn_half<T>(m, kv, l, B, c.canvas, kv->len, 0, s.h, s, st, normed));
-        DG_TRY(moe_half<T>(m, l, Tn, s.h, s, st, next_attn_norm(m, l), &normed));
+        AddNormEpi mn = moe_norm_epi<T>(m, l, s);
+        DG_TRY(attn_half<T>(m, kv, l, B, c.canvas, kv->len, 0, s.h, s, st, normed, &mn));
+        DG_TRY(moe_half<T>(m, l, Tn, s.h, s, st, next_attn_norm(m, l), &normed, mn.done));
     }
     return stage_head<T>(m, Tn, s.h, logits, s, st);
 }
@@ -665,9 +696,12 @@ dg_status encode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int P, Sc
         DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens + c0, P, n, B, s.h, c.d_model, st));
         bool normed = false;
         for (int l = 0; l < c.n_layers; ++l) {
-            DG_TRY(attn_half<T>(m, kv, l, B, n, pos0, 1, s.h, s, st, normed));
-            if (l + 1 < c.n_layers)
-                DG_TRY(moe_half<T>(m, l, B * n, s.h, s, st, next_attn_norm(m, l), &normed));
+            const bool last = l + 1 == c.n_layers;   // its MoE half is not needed
+            AddNormEpi mn = moe_norm_epi<T>(m, l, s);
+            DG_TRY(attn_half<T>(m, kv, l, B, n, pos0, 1, s.h, s, st, normed, last ? nullptr : &mn));
+            if (!last)
+                DG_TRY(moe_half<T>(m, l, B * n, s.h, s, st, next_attn_norm(m, l), &normed,
+                                   mn.done));
         }
     }
     kv->len += P;
@@ -685,8 +719,9 @@ dg_status ar_decode(dg_model* m, dg_kv* kv, int B, const int32_t* tokens, int ld
     DG_HIP(dg::embed_rows<T>((const T*)m->embed, c.vocab, tokens, ld, 1, B, s.h, c.d_model, st));
     bool normed = false;
     for (int l = 0; l < c.n_layers; ++l) {
-        DG_TRY(attn_half<T>(m, kv, l, B, 1, pos0, 1, s.h, s, st, normed));
-        DG_TRY(moe_half<T>(m, l, B, s.h, s, st, next_attn_norm(m, l), &normed));
+        AddNormEpi mn = moe_norm_epi<T>(m, l, s);
+        DG_TRY(attn_half<T>(m, kv, l, B, 1, pos0, 1, s.h, s, st, normed, &mn));
+        DG_TRY(moe_half<T>(m, l, B, s.h, s, st, next_attn_norm(m, l), &normed, mn.done));
     }
     kv->len += 1;
     return stage_head<T>(m, B, s.h, logits, s, st);

@@ -8,6 +8,33 @@ namespace dg {
 
 namespace {
 
+// The outputs of a normalised float4 r at column i of row `row`: u (T),
+// optionally u32 (fp32) and the MXFP8 codes q8 / scale codes q8s (d % 32 == 0;
+// a 32-column block is the float4s of 8 consecutive threads).
+template <typename T>
+__device__ __forceinline__ void rms_write(const float4 r, long row, int i, int d, T* o,
+                                          float* __restrict__ u32, uint8_t* __restrict__ q8,
+                                          uint8_t* __restrict__ q8s) {
+    o[i + 0] = Elt<T>::from_f(r.x);
+    o[i + 1] = Elt<T>::from_f(r.y);
+    o[i + 2] = Elt<T>::from_f(r.z);
+    o[i + 3] = Elt<T>::from_f(r.w);
+    if (u32) *reinterpret_cast<float4*>(u32 + row * d + i) = r;
+    if (q8) {
+        // the 8 threads of a block hold the same loop trip count (d % 32 == 0)
+        float m = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        const int ex = mx8_exponent(m);
+        const float inv = __builtin_amdgcn_ldexpf(1.0f, -ex);   // exact: a power of two
+        const uint32_t code = e4m3_act(r.x * inv) | (e4m3_act(r.y * inv) << 8) |
+                              (e4m3_act(r.z * inv) << 16) | (e4m3_act(r.w * inv) << 24);
+        *reinterpret_cast<uint32_t*>(q8 + row * d + i) = code;
+        if ((threadIdx.x & 7) == 0) q8s[row * (d / 32) + i / 32] = (uint8_t)(ex + 127);
+    }
+}
+
 // One workgroup per row: sum of squares in fp32, then scale.  With q8 set,
 // the fp32 result is also written as MXFP8 (d % 32 == 0): E4M3 codes into
 // q8 [rows][d] and the E8M0 scale code of each 32-element block into q8s
@@ -29,24 +56,45 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     T* o = u + row * d;
     for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
         const float4 r = rms_apply(*reinterpret_cast<const float4*>(x + i), scale, w, i);
-        o[i + 0] = Elt<T>::from_f(r.x);
-        o[i + 1] = Elt<T>::from_f(r.y);
-        o[i + 2] = Elt<T>::from_f(r.z);
-        o[i + 3] = Elt<T>::from_f(r.w);
-        if (u32) *reinterpret_cast<float4*>(u32 + row * d + i) = r;
-        if (q8) {
-            // the 8 threads of a block hold the same loop trip count (d % 32 == 0)
-            float m = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            m = fmaxf(m, __shfl_xor(m, 2, 64));
-            m = fmaxf(m, __shfl_xor(m, 4, 64));
-            const int ex = mx8_exponent(m);
-            const float inv = __builtin_amdgcn_ldexpf(1.0f, -ex);   // exact: a power of two
-            const uint32_t code = e4m3_act(r.x * inv) | (e4m3_act(r.y * inv) << 8) |
-                                  (e4m3_act(r.z * inv) << 16) | (e4m3_act(r.w * inv) << 24);
-            *reinterpret_cast<uint32_t*>(q8 + row * d + i) = code;
-            if ((threadIdx.x & 7) == 0) q8s[row * (d / 32) + i / 32] = (uint8_t)(ex + 127);
-        }
+        rms_write(r, row, i, d, o, u32, q8, q8s);
+    }
+}
+
+
+// The residual add of a split-K product (h += sum over the splits of part
+// [splits][rows][d], in split order) with the RMSNorm of the new rows fused:
+// one workgroup a row in rmsnorm_kernel's layout, the same outputs and bits
+// as splitk_epilogue (EPI_ADD_F32) followed by rmsnorm.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_add_norm_kernel(const float* __restrict__ part,
+                                                              int splits, long rows,
+                                                              float* __restrict__ h,
+                                                              const float* __restrict__ w,
+                                                              T* __restrict__ u, int d, float eps,
+                                                              float* __restrict__ u32,
+                                                              uint8_t* __restrict__ q8,
+                                                              uint8_t* __restrict__ q8s) {
+    const long row = blockIdx.x;
+    float* x = h + row * d;
+    const float* pr = part + row * d;
+    const long zs = rows * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        const float4 v = splitk_sum4(pr + i, zs, splits);
+        float4 hv = *reinterpret_cast<const float4*>(x + i);
+        hv.x = hv.x + v.x;
+        hv.y = hv.y + v.y;
+        hv.z = hv.z + v.z;
+        hv.w = hv.w + v.w;
+        *reinterpret_cast<float4*>(x + i) = hv;
+        ss = rms_accum(ss, hv);
+    }
+    __shared__ float pt[4];
+    const float scale = rms_block_scale(ss, pt, d, eps);
+    T* o = u + row * d;
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        const float4 r = rms_apply(*reinterpret_cast<const float4*>(x + i), scale, w, i);
+        rms_write(r, row, i, d, o, u32, q8, q8s);
     }
 }
 
@@ -419,6 +467,17 @@ hipError_t splitk_rope_kv(const float* part, int splits, T* q_out, T* kc, T* vc,
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t splitk_add_norm(const float* part, int splits, float* h, int rows, int d,
+                           const float* w, T* u, float eps, hipStream_t st, float* u32,
+                           uint8_t* q8, uint8_t* q8s) {
+    if (rows <= 0) return hipSuccess;
+    if (d % 4 || (q8 && (d % 32 || !q8s))) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_add_norm_kernel<T>, dim3(rows), dim3(256), 0, st, part, splits,
+                       (long)rows, h, w, u, d, eps, u32, q8, q8s);
+    return hipGetLastError();
+}
+
 #define DG_INST(T)                                                                        \
     template hipError_t rmsnorm<T>(const float*, const float*, T*, int, int, float,        \
                                    hipStream_t, float*, uint8_t*, uint8_t*);               \
@@ -430,7 +489,9 @@ hipError_t splitk_rope_kv(const float* part, int splits, T* q_out, T* kc, T* vc,
     template hipError_t rope_kv<T>(const float*, T*, T*, T*, int, int, int, int, int, int, \
                                    int, int, float, hipStream_t);                          \
     template hipError_t splitk_rope_kv<T>(const float*, int, T*, T*, T*, int, int, int, int, \
-                                          int, int, int, int, float, hipStream_t);
+                                          int, int, int, int, float, hipStream_t); \
+    template hipError_t splitk_add_norm<T>(const float*, int, float*, int, int, const float*, \
+                                           T*, float, hipStream_t, float*, uint8_t*, uint8_t*);
 DG_INST(bf16_t)
 DG_INST(float)
 #undef DG_INST

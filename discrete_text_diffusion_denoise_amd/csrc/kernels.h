@@ -137,6 +137,12 @@ template <typename T>
 hipError_t splitk_rope_kv(const float* part, int splits, T* q_out, T* kc, T* vc, int B, int n,
                           int pos0, int cap, int Hq, int Hkv, int dh, int rope_on, float theta,
                           hipStream_t st);
+// h [rows][d] += the split-K partials part [splits][rows][d] (summed as
+// splitk_epilogue sums them), then rmsnorm of the new rows with its outputs
+template <typename T>
+hipError_t splitk_add_norm(const float* part, int splits, float* h, int rows, int d,
+                           const float* w, T* u, float eps, hipStream_t st, float* u32,
+                           uint8_t* q8, uint8_t* q8s);
 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
