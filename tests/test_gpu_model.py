@@ -46,7 +46,12 @@ SMALL_MXFP4 = dict(SMALL_BF16, expert_dtype="mxfp4")
 ATT128 = dict(n_layers=1, d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, n_experts=8, top_k=2,
               d_ff=256, vocab=2048, canvas=256, dtype="bf16")
 
-MODELS = {"tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
+# the bf16 model with 30 experts (not a multiple of the fused router's groups
+# of four) and 3 per token (no fused combine and norm: the separate kernels
+# run inside the production step)
+SMALL_E30 = dict(SMALL_BF16, n_experts=30, top_k=3)
+
+MODELS = {"small_e30": SMALL_E30, "tiny": TINY, "small_bf16": SMALL_BF16, "f32_gqa": F32_GQA, "vocab_bf16": VOCAB_BF16,
           "vocab_ragged": VOCAB_RAGGED, "small_fp8": SMALL_FP8, "small_mxfp4": SMALL_MXFP4,
           "att128_g4": ATT128, "att128_g2": dict(ATT128, n_heads=4),
           "att128_g1": dict(ATT128, n_heads=4, n_kv_heads=4)}
@@ -183,7 +188,8 @@ STEP_CASES = [("tiny", 32, 1, False, 1, 0), ("tiny", 32, 1, True, 1, 0),
               ("f32_gqa", 64, 2, True, 2, 0), ("f32_gqa", 64, 1, False, 3, 0),
               ("small_fp8", 200, 2, True, 2, 0), ("small_mxfp4", 200, 2, True, 2, 0),
               ("tiny", 32, 1, True, 1, 64), ("small_bf16", 200, 2, True, 2, 8),
-              ("vocab_bf16", 100, 1, True, 1, 0), ("vocab_ragged", 100, 1, True, 1, 0)]
+              ("vocab_bf16", 100, 1, True, 1, 0), ("vocab_ragged", 100, 1, True, 1, 0),
+              ("small_e30", 200, 2, True, 2, 0)]
 
 
 def prev_and_stats(B, N, V, seed=4):
@@ -322,7 +328,8 @@ def test_stage_attention_on_synthetic_cache(name, causal, P, N):
                                          ("small_bf16", 512, 4), ("small_bf16", 300, 3),
                                          ("small_bf16", 129, 1), ("small_bf16", 256, 16),
                                          ("small_mxfp4", 300, 3), ("small_fp8", 129, 1),
-                                         ("small_mxfp4", 256, 16)])
+                                         ("small_mxfp4", 256, 16), ("small_e30", 512, None),
+                                         ("small_e30", 77, None)])
 def test_stage_moe(name, T, top_k):
     """The MoE stage on identical synthetic inputs: the route is a valid top-k
     (the oracle's own set off near ties, at most 1 % of tokens within 1e-4
